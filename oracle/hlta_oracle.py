@@ -1,0 +1,292 @@
+"""Float64 CPU oracle of Hybrid Linear Temporal Attention (HLTA).
+
+TEST INFRASTRUCTURE ONLY. Only tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py may import this module. The GPU library never
+calls it and shares no code with it; the only common module is the seeded
+input generator (hybrid_linear_temporal_amd/inputs.py).
+
+Plain and slow on purpose: every function is the plain definition of what it
+computes, in float64, one (batch, head) at a time.
+
+What HLTA is (Kairos abstract on chatpaper.ai, point (2); Kairos summary page
+on researchpapers.dev, section on how the hybrid linear temporal attention
+limits drift): three temporal branches over latent-video tokens, namely
+sliding-window softmax attention for local dynamics, dilated sliding windows for
+mid-range dependencies, and gated linear attention with a delta update rule as
+the persistent global memory.
+
+Readings taken where the pages are silent (each is listed in the design doc):
+  * tokens are frame-major, t = f*P + p; frame(t) = t // P;
+  * the softmax branches are frame-block causal: a query of frame f sees every
+    token of each frame in its frame set, bidirectional inside a frame;
+  * SWA frame set {f - j : 0 <= j < W}: W counts the current frame;
+  * DSWA frame set {f - dil*r : 1 <= r <= taps}; frames below 0 are skipped;
+    a query with an empty frame set outputs zeros;
+  * softmax scale 1/sqrt(d) unless given; no bias, no positional term;
+  * the memory follows the gated delta rule, one token at a time in token order
+    (raster inside a frame), with per-token per-head gates a (decay) and b
+    (write strength) used as given, in-op L2 normalisation of q and k with
+    eps = 1e-6 inside the square root, and the read o_t = S_t q_t taken after
+    the token's own update;
+  * the three outputs are combined as o_mix = w0*o_swa + w1*o_dswa + w2*o_gdn
+    with caller weights w[h, :] and nothing else.
+"""
+from __future__ import annotations
+
+import numpy as np
+from scipy.linalg import solve_triangular
+
+L2_EPS = 1e-6
+LOG_A_FLOOR = -80.0   # log of the decay gate is floored here (a = 0 stays finite)
+
+
+# ---------------------------------------------------------------------------
+# token / frame indexing
+# ---------------------------------------------------------------------------
+
+def swa_frames(f: int, W: int) -> list[int]:
+    """Frames a query frame f reads in the sliding-window branch: the current
+    frame and the W-1 before it (Kairos abstract, point (2): sliding-window
+    attention for local dynamics)."""
+    return [f - j for j in range(W) if f - j >= 0]
+
+
+def dswa_frames(f: int, dil: int, taps: int) -> list[int]:
+    """Frames a query frame f reads in the dilated branch: f - dil*r for
+    r = 1..taps (Kairos abstract, point (2): dilated sliding windows for
+    mid-range dependencies)."""
+    return [f - dil * r for r in range(1, taps + 1) if f - dil * r >= 0]
+
+
+# ---------------------------------------------------------------------------
+# softmax branches
+# ---------------------------------------------------------------------------
+
+def frame_softmax_attention(q, k, v, T, P, frames_of, scale=None):
+    """Exact softmax attention of each query frame over the keys of its frame set.
+
+    q, k, v: [T*P, d] float64 of one (batch, head). frames_of(f) -> list of key
+    frames. Every legal (query, key) pair is used, as exact attention does
+    (long-context page, section 03 on FlashAttention: tiling changes memory
+    traffic, not the set of pairs or the result). Rows with no key frame are 0.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    d = q.shape[1]
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    out = np.zeros((T * P, v.shape[1]))
+    for f in range(T):
+        frames = frames_of(f)
+        if not frames:
+            continue
+        idx = np.concatenate([np.arange(g * P, (g + 1) * P) for g in frames])
+        z = scale * (q[f * P:(f + 1) * P] @ k[idx].T)
+        z -= z.max(axis=1, keepdims=True)
+        e = np.exp(z)
+        out[f * P:(f + 1) * P] = (e @ v[idx]) / e.sum(axis=1, keepdims=True)
+    return out
+
+
+def swa(q, k, v, T, P, W, scale=None):
+    return frame_softmax_attention(q, k, v, T, P, lambda f: swa_frames(f, W), scale)
+
+
+def dswa(q, k, v, T, P, dil, taps, scale=None):
+    return frame_softmax_attention(q, k, v, T, P, lambda f: dswa_frames(f, dil, taps), scale)
+
+
+# ---------------------------------------------------------------------------
+# gated delta rule memory
+# ---------------------------------------------------------------------------
+
+def l2norm_rows(x, eps=L2_EPS):
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt((x * x).sum(axis=-1, keepdims=True) + eps)
+
+
+def gdn_recurrent(q, k, v, a, b, S0=None, l2norm=True):
+    """Gated delta rule, one token at a time (the reference of record).
+
+    S_t = a_t * S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,  o_t = S_t q_t.
+
+    Decay first, then correct: the state is scaled by the gate a_t (the decay
+    gate alpha_t of the recurrence quoted on the Kairos related-work page,
+    row A), and the association stored under k_t is erased before v_t is
+    written (long-context page, section 06: the delta rule and its gated
+    form). S is [d_v, d_k]; q, k: [L, d_k]; v: [L, d_v]; a, b: [L].
+    Returns (o [L, d_v], S_L).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    if l2norm:
+        q, k = l2norm_rows(q), l2norm_rows(k)
+    L, dk = k.shape
+    dv = v.shape[1]
+    S = np.zeros((dv, dk)) if S0 is None else np.array(S0, np.float64)
+    o = np.empty((L, dv))
+    for t in range(L):
+        kt = k[t]
+        erase = np.outer(S @ kt, kt)                 # what S currently stores under k_t
+        S = a[t] * (S - b[t] * erase) + b[t] * np.outer(v[t], kt)
+        o[t] = S @ q[t]
+    return o, S
+
+
+def gdn_chunked(q, k, v, a, b, C, S0=None, l2norm=True):
+    """Gated delta rule in chunked (UT / WY) form; equals gdn_recurrent.
+
+    Derivation (our own, from the recurrence above; the long-context page,
+    sections 02 and 06, says chunkwise-parallel and recurrent forms of such a
+    state are equivalent algorithms). Inside one chunk of n tokens with start
+    state S0, write S_i = a_i S_{i-1} + u_i k_i^T with
+    u_i = b_i (v_i - a_i S_{i-1} k_i), and let g_i = sum_{j<=i} log a_j,
+    gamma_i = exp(g_i). Unrolling gives
+        (I + A) U = diag(b) V - diag(b gamma) K S0^T,
+        A_ij = b_i exp(g_i - g_j) (k_i . k_j)   for j < i,
+    so with T = (I + A)^-1, W = T diag(b gamma) K and U' = T diag(b) V:
+        U   = U' - W S0^T
+        O   = diag(gamma) Q S0^T + (exp(g_i - g_j) q_i . k_j)_{j<=i} U
+        S_n = gamma_n S0 + U^T diag(gamma_n / gamma) K.
+    Chunks start at token 0 of the call; the last one may be shorter.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    if l2norm:
+        q, k = l2norm_rows(q), l2norm_rows(k)
+    L, dk = k.shape
+    dv = v.shape[1]
+    S = np.zeros((dv, dk)) if S0 is None else np.array(S0, np.float64)
+    o = np.empty((L, dv))
+    with np.errstate(divide="ignore"):
+        loga = np.maximum(np.log(a), LOG_A_FLOOR)
+    for s in range(0, L, C):
+        e = min(s + C, L)
+        n = e - s
+        K, Q, V, bc = k[s:e], q[s:e], v[s:e], b[s:e]
+        g = np.cumsum(loga[s:e])
+        gam = np.exp(g)
+        lower = np.tril(np.ones((n, n), bool))
+        ratio = np.where(lower, np.exp(np.where(lower, g[:, None] - g[None, :], 0.0)), 0.0)
+        A = np.tril(bc[:, None] * ratio * (K @ K.T), -1)
+        IA = np.eye(n) + A
+        Wm = solve_triangular(IA, (bc * gam)[:, None] * K, lower=True, unit_diagonal=True)
+        Up = solve_triangular(IA, bc[:, None] * V, lower=True, unit_diagonal=True)
+        U = Up - Wm @ S.T
+        Aqk = ratio * (Q @ K.T)
+        o[s:e] = gam[:, None] * (Q @ S.T) + Aqk @ U
+        S = gam[-1] * S + U.T @ (np.exp(g[-1] - g)[:, None] * K)
+    return o, S
+
+
+# ---------------------------------------------------------------------------
+# whole operator
+# ---------------------------------------------------------------------------
+
+def hlta_head(q, k, v, a, b, w3, T, P, W, dil, taps, C, scale=None, S0=None, gdn="chunked"):
+    """HLTA forward of one (batch, head): returns o_swa, o_dswa, o_gdn, o_mix, S_out."""
+    o_swa = swa(q, k, v, T, P, W, scale)
+    o_dswa = dswa(q, k, v, T, P, dil, taps, scale)
+    if gdn == "chunked":
+        o_gdn, S = gdn_chunked(q, k, v, a, b, C, S0)
+    else:
+        o_gdn, S = gdn_recurrent(q, k, v, a, b, S0)
+    w3 = np.asarray(w3, np.float64)
+    o_mix = w3[0] * o_swa + w3[1] * o_dswa + w3[2] * o_gdn
+    return o_swa, o_dswa, o_gdn, o_mix, S
+
+
+def hlta_forward(q, k, v, a, b, w, T, P, W, dil, taps, C, scale=None, S0=None, gdn="chunked",
+                 heads=None):
+    """HLTA forward over [B, L, H, d] inputs; returns float64 arrays in the same
+    layout (o_* [B, L, H, d], S_out [B, H, d_v, d_k]). heads: optional list of
+    (b, h) to compute (others stay zero)."""
+    B, L, H, d = np.shape(q)
+    dv = np.shape(v)[3]
+    outs = [np.zeros((B, L, H, dv)) for _ in range(4)]
+    S_out = np.zeros((B, H, dv, d))
+    todo = heads if heads is not None else [(bi, hi) for bi in range(B) for hi in range(H)]
+    for bi, hi in todo:
+        s0 = None if S0 is None else S0[bi, hi]
+        res = hlta_head(q[bi, :, hi], k[bi, :, hi], v[bi, :, hi], a[bi, :, hi], b[bi, :, hi],
+                        w[hi], T, P, W, dil, taps, C, scale, s0, gdn)
+        for o, r in zip(outs, res[:4]):
+            o[bi, :, hi] = r
+        S_out[bi, hi] = res[4]
+    return (*outs, S_out)
+
+
+# ---------------------------------------------------------------------------
+# streaming: one latent frame at a time
+# ---------------------------------------------------------------------------
+
+class StreamHead:
+    """Streaming HLTA of one (rollout, head): keeps the state S and the K/V of
+    past frames, and appends one latent frame per step without recomputing the
+    clip (Kairos article on zhichai.net, section 2.3: streaming tokens for
+    incremental generation; long-context page, section 02: a recurrent twin of
+    the parallel form for decoding)."""
+
+    def __init__(self, P, W, dil, taps, C, scale=None, S0=None):
+        self.P, self.W, self.dil, self.taps, self.C = P, W, dil, taps, C
+        self.scale = scale
+        self.S0 = None if S0 is None else np.array(S0, np.float64)
+        self.k = {}
+        self.v = {}
+        self.f = 0
+
+    def load_prefix(self, k, v, frames, S):
+        for j in range(frames):
+            self.k[j] = np.asarray(k[j * self.P:(j + 1) * self.P], np.float64)
+            self.v[j] = np.asarray(v[j * self.P:(j + 1) * self.P], np.float64)
+        self.f = frames
+        self.S0 = np.array(S, np.float64)
+
+    def step(self, q, k, v, a, b, w3, commit=True):
+        P, f = self.P, self.f
+        q = np.asarray(q, np.float64)
+        kf = np.asarray(k, np.float64)
+        vf = np.asarray(v, np.float64)
+        scale = 1.0 / np.sqrt(q.shape[1]) if self.scale is None else self.scale
+
+        def attend(frames):
+            if not frames:
+                return np.zeros((P, vf.shape[1]))
+            ks = np.concatenate([kf if g == f else self.k[g] for g in frames])
+            vs = np.concatenate([vf if g == f else self.v[g] for g in frames])
+            z = scale * (q @ ks.T)
+            z -= z.max(axis=1, keepdims=True)
+            e = np.exp(z)
+            return (e @ vs) / e.sum(axis=1, keepdims=True)
+
+        o_swa = attend(swa_frames(f, self.W))
+        o_dswa = attend(dswa_frames(f, self.dil, self.taps))
+        o_gdn, S = gdn_chunked(q, kf, vf, a, b, self.C, self.S0)
+        w3 = np.asarray(w3, np.float64)
+        o_mix = w3[0] * o_swa + w3[1] * o_dswa + w3[2] * o_gdn
+        if commit:
+            self.k[f], self.v[f] = kf, vf
+            self.S0 = S
+            self.f = f + 1
+        return o_swa, o_dswa, o_gdn, o_mix
+
+
+# ---------------------------------------------------------------------------
+# comparison
+# ---------------------------------------------------------------------------
+
+def rel_l2(x, ref):
+    """||x - ref||_2 / ||ref||_2 in float64 (0 when both are zero)."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    num = np.linalg.norm((x - ref).ravel())
+    den = np.linalg.norm(ref.ravel())
+    if den == 0.0:
+        return 0.0 if num == 0.0 else float("inf")
+    return float(num / den)

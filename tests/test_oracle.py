@@ -1,0 +1,376 @@
+"""Pins of the float64 oracle to things other than itself (CPU only).
+
+Each test checks the oracle against a brute-force enumeration, a closed form
+derived by hand, a textbook special case computed by a library routine, or an
+invariant the pages state. A plausible mistake in the oracle (a dropped term, a
+wrong sign, a transposed operand, an off-by-one frame) fails at least one.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import hlta_oracle as O
+from hybrid_linear_temporal_amd import inputs as I
+
+pytestmark = pytest.mark.filterwarnings("ignore::DeprecationWarning")
+
+
+def _rand(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _unit(x):
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+# ---------------------------------------------------------------------------
+# frame sets vs a per-pair brute-force mask
+# ---------------------------------------------------------------------------
+
+def _pair_mask(T, P, rule):
+    """Boolean [L, L] mask built pair by pair from the frame offset."""
+    L = T * P
+    m = np.zeros((L, L), bool)
+    for i in range(L):
+        for j in range(L):
+            m[i, j] = rule(i // P - j // P)
+    return m
+
+
+def _swa_rule(W):
+    return lambda off: 0 <= off <= W - 1
+
+
+def _dswa_rule(dil, taps):
+    return lambda off: off > 0 and off % dil == 0 and off // dil <= taps
+
+
+def _mask_from_frames(T, P, frames_of):
+    L = T * P
+    m = np.zeros((L, L), bool)
+    for f in range(T):
+        for g in frames_of(f):
+            m[f * P:(f + 1) * P, g * P:(g + 1) * P] = True
+    return m
+
+
+@pytest.mark.parametrize("T,P,W,dil,taps", [(8, 3, 2, 2, 2), (9, 2, 3, 4, 4), (5, 4, 1, 1, 3),
+                                             (6, 2, 7, 3, 0), (17, 1, 3, 4, 4)])
+def test_frame_sets_match_pairwise_rule(T, P, W, dil, taps):
+    np.testing.assert_array_equal(_mask_from_frames(T, P, lambda f: O.swa_frames(f, W)),
+                                  _pair_mask(T, P, _swa_rule(W)))
+    np.testing.assert_array_equal(_mask_from_frames(T, P, lambda f: O.dswa_frames(f, dil, taps)),
+                                  _pair_mask(T, P, _dswa_rule(dil, taps)))
+
+
+def test_swa_dswa_disjoint_on_workloads():
+    # with W counting the current frame and taps starting at r=1 the two
+    # branches read disjoint frame offsets on every workload
+    for wl in I.WORKLOADS.values():
+        s = set(range(wl.swa_frames))
+        dsw = {wl.dswa_dilation * r for r in range(1, wl.dswa_taps + 1)}
+        assert not (s & dsw), wl.name
+
+
+# ---------------------------------------------------------------------------
+# softmax branches vs dense brute force and textbook cases
+# ---------------------------------------------------------------------------
+
+def _dense_masked_softmax(q, k, v, mask, scale):
+    """Dense [L, L] masked softmax attention, looping over query rows."""
+    L = q.shape[0]
+    out = np.zeros((L, v.shape[1]))
+    for i in range(L):
+        js = np.nonzero(mask[i])[0]
+        if len(js) == 0:
+            continue
+        z = np.array([scale * float(np.dot(q[i], k[j])) for j in js])
+        p = np.exp(z - z.max())
+        p /= p.sum()
+        out[i] = (p[:, None] * v[js]).sum(0)
+    return out
+
+
+@pytest.mark.parametrize("qscale", [1.0, 20.0])
+def test_branches_vs_dense_bruteforce(qscale):
+    T, P, d, W, dil, taps = 8, 16, 32, 2, 2, 2
+    q = _unit(_rand(1, T * P, d)) * qscale
+    k = _unit(_rand(2, T * P, d))
+    v = _rand(3, T * P, d)
+    sc = 1 / math.sqrt(d)
+    ref_swa = _dense_masked_softmax(q, k, v, _pair_mask(T, P, _swa_rule(W)), sc)
+    ref_dswa = _dense_masked_softmax(q, k, v, _pair_mask(T, P, _dswa_rule(dil, taps)), sc)
+    np.testing.assert_allclose(O.swa(q, k, v, T, P, W), ref_swa, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(O.dswa(q, k, v, T, P, dil, taps), ref_dswa, rtol=1e-12, atol=1e-13)
+    # DSWA rows of frames 0..dil-1 have no key frame -> zeros
+    assert np.all(O.dswa(q, k, v, T, P, dil, taps)[:dil * P] == 0)
+
+
+def test_window_covering_all_frames_is_frame_causal_attention():
+    T, P, d = 6, 5, 16
+    q, k, v = _rand(4, T * P, d), _rand(5, T * P, d), _rand(6, T * P, d)
+    causal = np.zeros((T * P, T * P), bool)
+    for i in range(T * P):
+        causal[i, :(i // P + 1) * P] = True
+    ref = _dense_masked_softmax(q, k, v, causal, 0.3)
+    for W in (T, T + 3):
+        np.testing.assert_allclose(O.swa(q, k, v, T, P, W, scale=0.3), ref, rtol=1e-12, atol=1e-13)
+
+
+def test_single_frame_equals_library_sdpa():
+    P, d = 37, 32
+    q, k, v = _rand(7, P, d), _rand(8, P, d), _rand(9, P, d)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None])[0].numpy()
+    np.testing.assert_allclose(O.swa(q, k, v, 1, P, 3), ref, rtol=1e-12, atol=1e-13)
+
+
+def test_softmax_branch_invariants():
+    T, P, d = 5, 7, 8
+    q, k, v, v2 = _rand(10, T * P, d), _rand(11, T * P, d), _rand(12, T * P, d), _rand(13, T * P, d)
+    # constant values -> that constant
+    c = np.tile(np.arange(d, dtype=float), (T * P, 1))
+    np.testing.assert_allclose(O.swa(q, k, c, T, P, 2), c, rtol=1e-13)
+    # linear in v
+    np.testing.assert_allclose(O.dswa(q, k, 2 * v - 3 * v2, T, P, 2, 2),
+                               2 * O.dswa(q, k, v, T, P, 2, 2) - 3 * O.dswa(q, k, v2, T, P, 2, 2),
+                               rtol=1e-11, atol=1e-12)
+    # permuting tokens (keys with their values) inside a key frame changes nothing
+    perm = np.arange(T * P)
+    perm[P:2 * P] = P + np.random.default_rng(0).permutation(P)
+    base = O.swa(q, k, v, T, P, 2)
+    moved = O.swa(q, k[perm], v[perm], T, P, 2)
+    np.testing.assert_allclose(moved[2 * P:], base[2 * P:], rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# gated delta rule: closed forms and invariants
+# ---------------------------------------------------------------------------
+
+def _gdn_case(seed, L, d, a_range=(0.9, 0.999)):
+    r = np.random.default_rng(seed)
+    q = _unit(r.standard_normal((L, d)))
+    k = _unit(r.standard_normal((L, d)))
+    v = r.standard_normal((L, d))
+    a = r.uniform(*a_range, L)
+    b = 1 / (1 + np.exp(-r.standard_normal(L)))
+    return q, k, v, a, b
+
+
+def test_gdn_write_gate_zero_only_decays():
+    L, d = 40, 8
+    q, k, v, a, _ = _gdn_case(20, L, d)
+    S0 = _rand(21, d, d)
+    o, S = O.gdn_recurrent(q, k, v, a, np.zeros(L), S0)
+    cum = np.cumprod(a)
+    qn = q / np.sqrt((q * q).sum(1, keepdims=True) + 1e-6)
+    np.testing.assert_allclose(S, cum[-1] * S0, rtol=1e-12)
+    np.testing.assert_allclose(o, cum[:, None] * (qn @ S0.T), rtol=1e-11, atol=1e-13)
+
+
+def test_gdn_single_key_closed_form():
+    # every token writes under the same unit key k; with S0 = 0 the state stays
+    # x_t k^T and the hand-derived recurrence is x_t = a_t (1 - b_t) x_{t-1} + b_t v_t
+    L, d = 30, 6
+    r = np.random.default_rng(22)
+    key = _unit(r.standard_normal(d))
+    k = np.tile(key, (L, 1))
+    q = np.tile(key, (L, 1))
+    v = r.standard_normal((L, d))
+    a = r.uniform(0.5, 1.0, L)
+    b = r.uniform(0.0, 1.0, L)
+    o, S = O.gdn_recurrent(q, k, v, a, b, l2norm=False)
+    x = np.zeros(d)
+    for t in range(L):
+        x = a[t] * (1 - b[t]) * x + b[t] * v[t]
+        np.testing.assert_allclose(o[t], x, rtol=1e-12, atol=1e-14)   # o_t read after the write
+    np.testing.assert_allclose(S, np.outer(x, key), rtol=1e-12, atol=1e-14)
+
+
+def test_gdn_orthonormal_recall_and_overwrite():
+    d, m = 16, 10
+    keys = np.linalg.qr(_rand(23, d, d))[0][:, :m].T          # m orthonormal rows
+    vals = _rand(24, m, d)
+    vals2 = _rand(25, m, d)
+    # write every key once, then overwrite key 3, then read all keys (b = 0 reads)
+    k = np.concatenate([keys, keys[3:4], keys])
+    v = np.concatenate([vals, vals2[3:4], np.zeros((m, d))])
+    a = np.ones(len(k))
+    b = np.concatenate([np.ones(m + 1), np.zeros(m)])
+    o, S = O.gdn_recurrent(k, k, v, a, b, l2norm=False)
+    want = vals.copy()
+    want[3] = vals2[3]
+    np.testing.assert_allclose(o[m + 1:], want, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S @ keys[3], vals2[3], rtol=1e-12, atol=1e-12)
+
+
+def test_gdn_contraction_ratio_bounded_by_decay():
+    L, d = 200, 8
+    q, k, v, a, b = _gdn_case(26, L, d)
+    S0, S1 = _rand(27, d, d), _rand(28, d, d)
+    Sa, Sb = S0.copy(), S1.copy()
+    for t in range(L):
+        na, _ = O.gdn_recurrent(q[t:t + 1], k[t:t + 1], v[t:t + 1], a[t:t + 1], b[t:t + 1], Sa)[1], None
+        nb = O.gdn_recurrent(q[t:t + 1], k[t:t + 1], v[t:t + 1], a[t:t + 1], b[t:t + 1], Sb)[1]
+        ratio = np.linalg.norm(na - nb) / np.linalg.norm(Sa - Sb)
+        assert ratio <= a[t] * (1 + 1e-12)
+        Sa, Sb = na, nb
+
+
+def test_gdn_bounded_error_under_perturbation():
+    # with a perturbation of norm <= xi injected every step, the state error
+    # stays below xi / (1 - max a)
+    L, d, xi = 300, 8, 1e-3
+    q, k, v, a, b = _gdn_case(29, L, d, a_range=(0.8, 0.95))
+    rho = a.max()
+    r = np.random.default_rng(30)
+    S, Sp = np.zeros((d, d)), np.zeros((d, d))
+    worst = 0.0
+    for t in range(L):
+        sl = slice(t, t + 1)
+        S = O.gdn_recurrent(q[sl], k[sl], v[sl], a[sl], b[sl], S)[1]
+        Sp = O.gdn_recurrent(q[sl], k[sl], v[sl], a[sl], b[sl], Sp)[1]
+        e = r.standard_normal((d, d))
+        Sp = Sp + xi * e / np.linalg.norm(e)
+        worst = max(worst, np.linalg.norm(S - Sp))
+    assert worst <= xi / (1 - rho)
+    assert worst > 0.5 * xi       # the bound is not vacuous here
+
+
+def test_gdn_linear_in_values_and_start_state():
+    L, d = 50, 8
+    q, k, v, a, b = _gdn_case(31, L, d)
+    v2 = _rand(32, L, d)
+    S0, S1 = _rand(33, d, d), _rand(34, d, d)
+    o1, s1 = O.gdn_recurrent(q, k, v, a, b, S0)
+    o2, s2 = O.gdn_recurrent(q, k, v2, a, b, S1)
+    o3, s3 = O.gdn_recurrent(q, k, 2 * v - v2, a, b, 2 * S0 - S1)
+    np.testing.assert_allclose(o3, 2 * o1 - o2, rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(s3, 2 * s1 - s2, rtol=1e-10, atol=1e-11)
+
+
+def test_gdn_l2norm_in_op():
+    # scaling q or k by a positive factor changes nothing (up to the eps term)
+    L, d = 20, 8
+    q, k, v, a, b = _gdn_case(35, L, d)
+    o1, _ = O.gdn_recurrent(q, k, v, a, b)
+    o2, _ = O.gdn_recurrent(3 * q, 5 * k, v, a, b)
+    np.testing.assert_allclose(o1, o2, rtol=2e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("C", [1, 4, 16, 64])
+@pytest.mark.parametrize("L", [1, 63, 64, 65, 130, 200])
+def test_gdn_chunked_equals_recurrent(C, L):
+    d = 16
+    q, k, v, a, b = _gdn_case(40 + L, L, d)
+    S0 = 0.3 * _rand(41, d, d)
+    o_ref, S_ref = O.gdn_recurrent(q, k, v, a, b, S0)
+    o, S = O.gdn_chunked(q, k, v, a, b, C, S0)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(S, S_ref, rtol=1e-11, atol=1e-12)
+
+
+def test_gdn_chunked_every_tail():
+    d, C = 8, 16
+    for L in range(1, 2 * C + 1):
+        q, k, v, a, b = _gdn_case(100 + L, L, d)
+        o_ref, S_ref = O.gdn_recurrent(q, k, v, a, b)
+        o, S = O.gdn_chunked(q, k, v, a, b, C)
+        np.testing.assert_allclose(o, o_ref, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(S, S_ref, rtol=1e-11, atol=1e-12)
+
+
+def test_gdn_chunked_extreme_gates():
+    # a = 1, b = 1, a = 0 (floored log) and b = 0 tokens mixed in
+    L, d = 70, 8
+    q, k, v, a, b = _gdn_case(50, L, d)
+    a[5] = 1.0
+    a[20] = 0.0
+    b[7] = 0.0
+    b[9] = 1.0
+    o_ref, S_ref = O.gdn_recurrent(q, k, v, a, b)
+    o, S = O.gdn_chunked(q, k, v, a, b, 16)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(S, S_ref, rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# whole operator and streaming
+# ---------------------------------------------------------------------------
+
+def test_mix_selects_branches():
+    wl = I.TINY_F32
+    x = I.make_clip(wl)
+    args = (x["q"][0, :, 0], x["k"][0, :, 0], x["v"][0, :, 0], x["a"][0, :, 0], x["b"][0, :, 0])
+    cfg = (wl.T, wl.P, wl.swa_frames, wl.dswa_dilation, wl.dswa_taps, wl.gdn_chunk)
+    for i in range(3):
+        w3 = np.zeros(3)
+        w3[i] = 1.0
+        res = O.hlta_head(*args, w3, *cfg)
+        np.testing.assert_array_equal(res[3], res[i])
+
+
+def test_forward_gdn_forms_agree_on_tiny():
+    wl = I.TINY_F32
+    x = I.make_clip(wl)
+    cfg = (wl.T, wl.P, wl.swa_frames, wl.dswa_dilation, wl.dswa_taps, wl.gdn_chunk)
+    r1 = O.hlta_forward(x["q"], x["k"], x["v"], x["a"], x["b"], x["w"], *cfg, gdn="chunked")
+    r2 = O.hlta_forward(x["q"], x["k"], x["v"], x["a"], x["b"], x["w"], *cfg, gdn="recurrent")
+    for u, w in zip(r1, r2):
+        np.testing.assert_allclose(u, w, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("commit_every", [True, False])
+def test_streaming_equals_full_forward(commit_every):
+    T, P, d, W, dil, taps, C = 12, 6, 8, 3, 2, 3, 4
+    q, k, v, a, b = _gdn_case(60, T * P, d)
+    w3 = np.array([0.3, 0.5, 0.7])
+    full = O.hlta_head(q, k, v, a, b, w3, T, P, W, dil, taps, C)
+    prefix = 5
+    # the prefix state comes from the full recurrence over the prefix frames
+    _, Sp = O.gdn_recurrent(q[:prefix * P], k[:prefix * P], v[:prefix * P], a[:prefix * P], b[:prefix * P])
+    st = O.StreamHead(P, W, dil, taps, C)
+    st.load_prefix(k, v, prefix, Sp)
+    for f in range(prefix, T):
+        sl = slice(f * P, (f + 1) * P)
+        if not commit_every:
+            # an uncommitted evaluation first must leave the state untouched
+            st.step(q[sl] * 2, k[sl], v[sl] * 3, a[sl], b[sl], w3, commit=False)
+        outs = st.step(q[sl], k[sl], v[sl], a[sl], b[sl], w3)
+        for got, ref in zip(outs, full[:4]):
+            np.testing.assert_allclose(got, ref[sl], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(st.S0, full[4], rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# input recipe helpers
+# ---------------------------------------------------------------------------
+
+def test_round_to_bf16_matches_torch_on_f32_values():
+    r = np.random.default_rng(70)
+    x = np.concatenate([r.standard_normal(20000).astype(np.float32),
+                        (r.standard_normal(2000) * 1e-39).astype(np.float32),
+                        np.array([0.0, -0.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 2.0 ** -130], np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(I.round_to_bf16(x.astype(np.float64)), ref)
+
+
+def test_round_to_bf16_single_rounding_from_f64():
+    # 1 + 2^-8 + 2^-40 lies just above the tie: rounds up directly from f64;
+    # going through f32 first would make it a tie and round down to even
+    x = 1.0 + 2.0 ** -8 + 2.0 ** -40
+    assert I.round_to_bf16(np.array([x]))[0] == np.float32(1.0 + 2.0 ** -7)
+    assert I.round_to_bf16(np.array([1.0 + 2.0 ** -8]))[0] == np.float32(1.0)
+
+
+def test_inputs_recipe():
+    wl = I.TINY_F32
+    x = I.make_clip(wl)
+    assert x["q"].shape == (1, 128, 2, 32) and x["a"].shape == (1, 128, 2)
+    np.testing.assert_allclose(np.linalg.norm(x["k"], axis=-1), 1.0, rtol=1e-6)
+    assert x["a"].min() >= 0.9 and x["a"].max() <= 0.999
+    assert 0 < x["b"].min() and x["b"].max() < 1
+    y = I.make_clip(wl)
+    np.testing.assert_array_equal(x["q"], y["q"])   # seeded
