@@ -1,0 +1,238 @@
+// C-ABI entry points that launch work: hlta_fwd, hlta_stream_load_prefix,
+// hlta_step_frame. Validation happens on the host before any launch; the
+// library allocates nothing (scratch is the caller's workspace).
+#include <string>
+
+#include "hlta_device.h"
+#include "hlta_internal.h"
+#include "hlta_launch.h"
+
+using namespace hlta;
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+hlta_status hip_fail(hipError_t e, const char* what) {
+  return fail(HLTA_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+hlta_status need(const void* p, const char* name) {
+  if (!p) return fail(HLTA_E_NULL, std::string(name) + " is NULL");
+  if (!aligned16(p)) return fail(HLTA_E_ALIGN, std::string(name) + " is not 16-byte aligned");
+  return HLTA_OK;
+}
+
+hlta_status maybe(const void* p, const char* name) {
+  if (p && !aligned16(p)) return fail(HLTA_E_ALIGN, std::string(name) + " is not 16-byte aligned");
+  return HLTA_OK;
+}
+
+#define HLTA_TRY(x)                  \
+  do {                               \
+    hlta_status s_ = (x);            \
+    if (s_ != HLTA_OK) return s_;    \
+  } while (0)
+
+hlta_status check_outputs(const float* a, const float* b, const float* mix_w, void* o_swa, void* o_dswa,
+                          void* o_gdn, void* o_mix) {
+  HLTA_TRY(need(a, "a"));
+  HLTA_TRY(need(b, "b"));
+  HLTA_TRY(need(mix_w, "mix_w"));
+  HLTA_TRY(need(o_swa, "o_swa"));
+  HLTA_TRY(need(o_dswa, "o_dswa"));
+  HLTA_TRY(need(o_gdn, "o_gdn"));
+  HLTA_TRY(need(o_mix, "o_mix"));
+  return HLTA_OK;
+}
+
+// GDN over L tokens per row, then SWA/DSWA + mix. attn.* query fields set by caller.
+hlta_status run_layer(const hlta_config* cfg, const Plan& plan, const void* q, const void* k, const void* v,
+                      const float* a, const float* b, const float* S0, float* S_out, void* o_gdn,
+                      void* workspace, AttnParams attn, hipStream_t st) {
+  GdnParams g{};
+  g.q = q;
+  g.k = k;
+  g.v = v;
+  g.a = a;
+  g.b = b;
+  g.S0 = S0;
+  g.S_out = S_out;
+  g.o = o_gdn;
+  g.ws = static_cast<unsigned char*>(workspace);
+  g.rec_bytes = plan.gdn == Impl::Mfma ? gdn_mfma_record_bytes(cfg->gdn_chunk, cfg->d)
+                                       : gdn_generic_record_bytes(cfg->gdn_chunk, cfg->d);
+  g.B = cfg->B;
+  g.H = cfg->H;
+  g.L = plan.L;
+  g.n_chunks = int(plan.n_chunks);
+  g.l2norm = cfg->gdn_l2norm_qk;
+  hipError_t e = plan.gdn == Impl::Mfma
+                     ? launch_gdn_mfma(g, cfg->out_dtype, st)
+                     : launch_gdn_generic(g, cfg->d, cfg->gdn_chunk, cfg->in_dtype, cfg->out_dtype, st);
+  if (e != hipSuccess) return hip_fail(e, "gated delta rule launch");
+
+  attn.o_gdn = o_gdn;
+  attn.scale_log2 = plan.scale * kLog2e;
+  e = plan.attn == Impl::Mfma ? launch_attn_mfma(attn, cfg->out_dtype, st)
+                              : launch_attn_generic(attn, cfg->d, cfg->in_dtype, cfg->out_dtype, st);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return HLTA_OK;
+}
+
+size_t state_bytes(const hlta_config* cfg) { return size_t(cfg->B) * cfg->H * cfg->d * cfg->d * sizeof(float); }
+
+}  // namespace
+
+extern "C" {
+
+hlta_status hlta_fwd(const hlta_config* cfg, const void* q, const void* k, const void* v, const float* a,
+                     const float* b, const float* mix_w, const float* S0, void* o_swa, void* o_dswa,
+                     void* o_gdn, void* o_mix, float* S_out, void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  Plan plan;
+  HLTA_TRY(check_config(cfg));
+  HLTA_TRY(make_plan(cfg, int64_t(cfg->T) * cfg->P, &plan));
+  HLTA_TRY(maybe(S0, "S0"));
+  HLTA_TRY(maybe(S_out, "S_out"));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (plan.L == 0) {
+    // empty clip: the state passes through unchanged
+    if (S_out && S_out != S0) {
+      hipError_t e = S0 ? hipMemcpyAsync(S_out, S0, state_bytes(cfg), hipMemcpyDeviceToDevice, st)
+                        : hipMemsetAsync(S_out, 0, state_bytes(cfg), st);
+      if (e != hipSuccess) return hip_fail(e, "state copy");
+    }
+    return HLTA_OK;
+  }
+  HLTA_TRY(need(q, "q"));
+  HLTA_TRY(need(k, "k"));
+  HLTA_TRY(need(v, "v"));
+  HLTA_TRY(check_outputs(a, b, mix_w, o_swa, o_dswa, o_gdn, o_mix));
+  if (plan.ws_total > 0) {
+    HLTA_TRY(need(workspace, "workspace"));
+    if (ws_bytes < plan.ws_total)
+      return fail(HLTA_E_WORKSPACE, "workspace has " + std::to_string(ws_bytes) + " bytes, needs " +
+                                        std::to_string(plan.ws_total));
+  }
+  AttnParams at{};
+  at.q = q;
+  at.k = k;
+  at.v = v;
+  at.o_swa = o_swa;
+  at.o_dswa = o_dswa;
+  at.o_mix = o_mix;
+  at.mix_w = mix_w;
+  at.B = cfg->B;
+  at.H = cfg->H;
+  at.T = cfg->T;
+  at.P = cfg->P;
+  at.W = cfg->swa_frames;
+  at.dil = cfg->dswa_dilation;
+  at.taps = cfg->dswa_taps;
+  at.R = 0;
+  at.f0 = 0;
+  return run_layer(cfg, plan, q, k, v, a, b, S0, S_out, o_gdn, workspace, at, st);
+}
+
+static hlta_status check_stream(const hlta_config* cfg, const hlta_stream_state* st) {
+  if (!st) return fail(HLTA_E_NULL, "stream state is NULL");
+  HLTA_TRY(need(st->S, "state S"));
+  HLTA_TRY(need(st->ring_k, "ring_k"));
+  HLTA_TRY(need(st->ring_v, "ring_v"));
+  const long long need_frames = cfg->swa_frames - 1 > (long long)cfg->dswa_dilation * cfg->dswa_taps
+                                    ? cfg->swa_frames - 1
+                                    : (long long)cfg->dswa_dilation * cfg->dswa_taps;
+  if (st->ring_frames < 1 || st->ring_frames < need_frames)
+    return fail(HLTA_E_STATE, "ring_frames must be >= max(1, W-1, dil*taps) = " +
+                                  std::to_string(need_frames < 1 ? 1 : need_frames));
+  if (st->frames_done < 0) return fail(HLTA_E_STATE, "frames_done is negative");
+  return HLTA_OK;
+}
+
+hlta_status hlta_stream_load_prefix(const hlta_config* cfg, hlta_stream_state* st, const void* k_prefix,
+                                    const void* v_prefix, int32_t prefix_frames, const float* S_prefix,
+                                    void* stream) {
+  clear_error();
+  HLTA_TRY(check_config(cfg));
+  HLTA_TRY(check_stream(cfg, st));
+  if (prefix_frames < 0) return fail(HLTA_E_SHAPE, "prefix_frames must be >= 0");
+  if (prefix_frames > 0) {
+    HLTA_TRY(need(k_prefix, "k_prefix"));
+    HLTA_TRY(need(v_prefix, "v_prefix"));
+  }
+  HLTA_TRY(maybe(S_prefix, "S_prefix"));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const long long keep = prefix_frames < st->ring_frames ? prefix_frames : st->ring_frames;
+  const long long first = prefix_frames - keep;
+  const long long frame_elems = (long long)cfg->P * cfg->H * cfg->d;
+  const int elem = int(dtype_bytes(cfg->in_dtype));
+  hipError_t e = launch_ring_store(k_prefix, prefix_frames, 0, st->ring_k, st->ring_frames, first, keep, cfg->B,
+                                   frame_elems, elem, s);
+  if (e == hipSuccess)
+    e = launch_ring_store(v_prefix, prefix_frames, 0, st->ring_v, st->ring_frames, first, keep, cfg->B,
+                          frame_elems, elem, s);
+  if (e != hipSuccess) return hip_fail(e, "ring store");
+  e = S_prefix ? (S_prefix == st->S ? hipSuccess
+                                    : hipMemcpyAsync(st->S, S_prefix, state_bytes(cfg), hipMemcpyDeviceToDevice, s))
+               : hipMemsetAsync(st->S, 0, state_bytes(cfg), s);
+  if (e != hipSuccess) return hip_fail(e, "state copy");
+  st->frames_done = prefix_frames;
+  return HLTA_OK;
+}
+
+hlta_status hlta_step_frame(const hlta_config* cfg, hlta_stream_state* st, const void* q_f, const void* k_f,
+                            const void* v_f, const float* a_f, const float* b_f, const float* mix_w, void* o_swa,
+                            void* o_dswa, void* o_gdn, void* o_mix, int32_t commit, void* workspace,
+                            size_t ws_bytes, void* stream) {
+  clear_error();
+  HLTA_TRY(check_config(cfg));
+  HLTA_TRY(check_stream(cfg, st));
+  Plan plan;
+  HLTA_TRY(make_plan(cfg, cfg->P, &plan));
+  HLTA_TRY(need(q_f, "q_f"));
+  HLTA_TRY(need(k_f, "k_f"));
+  HLTA_TRY(need(v_f, "v_f"));
+  HLTA_TRY(check_outputs(a_f, b_f, mix_w, o_swa, o_dswa, o_gdn, o_mix));
+  if (plan.ws_total > 0) {
+    HLTA_TRY(need(workspace, "workspace"));
+    if (ws_bytes < plan.ws_total)
+      return fail(HLTA_E_WORKSPACE, "workspace has " + std::to_string(ws_bytes) + " bytes, needs " +
+                                        std::to_string(plan.ws_total));
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const long long f = st->frames_done;
+  AttnParams at{};
+  at.q = q_f;
+  at.k = k_f;
+  at.v = v_f;
+  at.ring_k = st->ring_k;
+  at.ring_v = st->ring_v;
+  at.o_swa = o_swa;
+  at.o_dswa = o_dswa;
+  at.o_mix = o_mix;
+  at.mix_w = mix_w;
+  at.B = cfg->B;
+  at.H = cfg->H;
+  at.T = 1;
+  at.P = cfg->P;
+  at.W = cfg->swa_frames;
+  at.dil = cfg->dswa_dilation;
+  at.taps = cfg->dswa_taps;
+  at.R = st->ring_frames;
+  at.f0 = f;
+  HLTA_TRY(run_layer(cfg, plan, q_f, k_f, v_f, a_f, b_f, st->S, commit ? st->S : nullptr, o_gdn, workspace,
+                     at, s));
+  if (commit) {
+    const long long frame_elems = (long long)cfg->P * cfg->H * cfg->d;
+    const int elem = int(dtype_bytes(cfg->in_dtype));
+    hipError_t e = launch_ring_store(k_f, 1, f, st->ring_k, st->ring_frames, f, 1, cfg->B, frame_elems, elem, s);
+    if (e == hipSuccess)
+      e = launch_ring_store(v_f, 1, f, st->ring_v, st->ring_frames, f, 1, cfg->B, frame_elems, elem, s);
+    if (e != hipSuccess) return hip_fail(e, "ring store");
+    st->frames_done = f + 1;
+  }
+  return HLTA_OK;
+}
+
+}  // extern "C"

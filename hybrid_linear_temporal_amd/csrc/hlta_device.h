@@ -1,0 +1,90 @@
+// Device-side helpers and kernel parameter blocks of the HLTA library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace hlta {
+
+using bf16 = __bf16;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+// round-to-nearest-even (gfx950 converts with v_cvt_pk_bf16_f32)
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
+
+// Value of x after a round trip through T (what a store of x leaves in memory).
+template <typename T> __device__ __forceinline__ float stored_value(float x) {
+  return to_f32(from_f32<T>(x));
+}
+
+// Parameters of the softmax branches (SWA + DSWA + fused mix epilogue).
+// Full mode (R == 0): queries and keys come from q, k, v of T frames.
+// Stream mode (R > 0): the call's single query frame is absolute frame f0;
+// its own K/V come from k, v; earlier frames g from ring slot g mod R.
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* ring_k;
+  const void* ring_v;
+  const void* o_gdn;     // read by the mix epilogue (out dtype)
+  void* o_swa;
+  void* o_dswa;
+  void* o_mix;
+  const float* mix_w;    // [H, 3]
+  int B, H, T, P;        // T = query frames of this call
+  int W, dil, taps;
+  int R;                 // ring frames (stream mode) or 0
+  long long f0;          // absolute index of query frame 0
+  float scale_log2;      // softmax scale * log2(e)
+};
+
+// Key frame g (absolute index) of batch row b, head h: pointer to its token 0.
+// Tokens of a frame are H*D elements apart.
+template <typename T, int D>
+__device__ __forceinline__ const T* key_frame_ptr(const T* main, const T* ring, const AttnParams& p,
+                                                  int b, int h, long long g) {
+  if (p.R == 0)
+    return main + ((size_t(b) * p.T * p.P + size_t(g) * p.P) * p.H + h) * D;
+  if (g == p.f0)
+    return main + (size_t(b) * p.P * p.H + h) * D;
+  const long long slot = g % p.R;
+  return ring + ((size_t(b) * p.R + slot) * p.P * p.H + h) * D;
+}
+
+// Frame sets of query frame f (absolute): SWA reads frames f-nswa+1 .. f,
+// DSWA reads f - dil*(s+1) for s < ndswa.
+__device__ __forceinline__ int swa_count(long long f, int W) {
+  return int(f + 1 < W ? f + 1 : W);
+}
+__device__ __forceinline__ int dswa_count(long long f, int dil, int taps) {
+  const long long n = f / dil;
+  return int(n < taps ? n : taps);
+}
+__device__ __forceinline__ long long branch_frame(int branch, long long f, int nswa, int dil, int s) {
+  return branch == 0 ? f - nswa + 1 + s : f - (long long)dil * (s + 1);
+}
+
+// Parameters of the gated delta rule kernels.
+struct GdnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* a;
+  const float* b;
+  const float* S0;       // [B, H, D, D] or null
+  float* S_out;          // [B, H, D, D] or null (may alias S0)
+  void* o;               // [B, L, H, D]
+  unsigned char* ws;     // per-chunk records
+  size_t rec_bytes;
+  int B, H;
+  long long L;
+  int n_chunks;
+  int l2norm;
+};
+
+}  // namespace hlta

@@ -1,0 +1,164 @@
+// HIP-free host layer of the HLTA library: status strings, the thread-local
+// error message, config validation, kernel selection and workspace sizing.
+// Built into libhlta.so and, with g++, into a CPU test binary.
+#include <cmath>
+#include <cstdio>
+#include <limits>
+#include <string>
+
+#include "hlta_internal.h"
+
+namespace hlta {
+
+static thread_local std::string g_last_error;
+
+hlta_status fail(hlta_status s, const std::string& msg) {
+  g_last_error = std::string(hlta_status_string(s)) + ": " + msg;
+  return s;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+static bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > std::numeric_limits<int64_t>::max() / a) return false;
+  *out = a * b;
+  return true;
+}
+
+hlta_status check_config(const hlta_config* cfg) {
+  if (!cfg) return fail(HLTA_E_NULL, "config is NULL");
+  if (cfg->B < 1) return fail(HLTA_E_SHAPE, "B must be >= 1");
+  if (cfg->H < 1) return fail(HLTA_E_SHAPE, "H must be >= 1");
+  if (cfg->T < 0) return fail(HLTA_E_SHAPE, "T must be >= 0");
+  if (cfg->P < 1) return fail(HLTA_E_SHAPE, "P must be >= 1");
+  if (cfg->d != 32 && cfg->d != 64 && cfg->d != 128)
+    return fail(HLTA_E_UNSUPPORTED, "d must be 32, 64 or 128 (got " + std::to_string(cfg->d) + ")");
+  if (cfg->swa_frames < 0) return fail(HLTA_E_SHAPE, "swa_frames must be >= 0");
+  if (cfg->dswa_dilation < 1) return fail(HLTA_E_SHAPE, "dswa_dilation must be >= 1");
+  if (cfg->dswa_taps < 0) return fail(HLTA_E_SHAPE, "dswa_taps must be >= 0");
+  if (cfg->gdn_chunk != 16 && cfg->gdn_chunk != 32 && cfg->gdn_chunk != 64)
+    return fail(HLTA_E_UNSUPPORTED, "gdn_chunk must be 16, 32 or 64");
+  if (!std::isfinite(cfg->softmax_scale)) return fail(HLTA_E_SHAPE, "softmax_scale is not finite");
+  if (cfg->gdn_l2norm_qk != 0 && cfg->gdn_l2norm_qk != 1)
+    return fail(HLTA_E_SHAPE, "gdn_l2norm_qk must be 0 or 1");
+  const bool in_ok = cfg->in_dtype == HLTA_F32 || cfg->in_dtype == HLTA_BF16;
+  const bool out_ok = cfg->out_dtype == HLTA_F32 || cfg->out_dtype == HLTA_BF16;
+  if (!in_ok || !out_ok) return fail(HLTA_E_DTYPE, "dtype must be HLTA_F32 or HLTA_BF16");
+  if (cfg->in_dtype == HLTA_F32 && cfg->out_dtype != HLTA_F32)
+    return fail(HLTA_E_DTYPE, "float32 inputs need float32 outputs");
+  if (cfg->impl != HLTA_IMPL_AUTO && cfg->impl != HLTA_IMPL_GENERIC && cfg->impl != HLTA_IMPL_MFMA)
+    return fail(HLTA_E_SHAPE, "impl must be HLTA_IMPL_AUTO, _GENERIC or _MFMA");
+  // every element offset must fit in int64, and token counts in int32 grids
+  int64_t L, n;
+  if (!mul_ok(cfg->T, cfg->P, &L) || !mul_ok(L, cfg->B, &n) || !mul_ok(n, cfg->H, &n) ||
+      !mul_ok(n, cfg->d, &n))
+    return fail(HLTA_E_SHAPE, "B*T*P*H*d overflows int64");
+  if (L > (int64_t(1) << 31) - 1) return fail(HLTA_E_SHAPE, "T*P must be < 2^31");
+  return HLTA_OK;
+}
+
+bool mfma_attn_supported(const hlta_config* cfg) {
+  return false && cfg->in_dtype == HLTA_BF16 && cfg->d == 128;
+}
+
+bool mfma_gdn_supported(const hlta_config* cfg) {
+  return false && cfg->in_dtype == HLTA_BF16 && cfg->d == 128 && cfg->gdn_chunk == 64;
+}
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// generic record: W, U', Q*gamma, K*gamma_C/gamma [C x d] + Aqk [C x C] + gamma_C, fp32
+size_t gdn_generic_record_bytes(int C, int d) {
+  return align_up(sizeof(float) * (4 * size_t(C) * d + size_t(C) * C + 1), 256);
+}
+
+// MFMA record: W, U' [C x d] bf16 + Aqk [C x C] bf16 + per-token gamma, gamma_C/gamma,
+// inverse norms of q and k (fp32)
+size_t gdn_mfma_record_bytes(int C, int d) {
+  return align_up(2 * (2 * size_t(C) * d + size_t(C) * C) + sizeof(float) * (4 * size_t(C) + 4), 256);
+}
+
+hlta_status make_plan(const hlta_config* cfg, int64_t L, Plan* plan) {
+  hlta_status s = check_config(cfg);
+  if (s != HLTA_OK) return s;
+  Plan p;
+  p.L = L;
+  p.n_chunks = (L + cfg->gdn_chunk - 1) / cfg->gdn_chunk;
+  p.scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / std::sqrt(float(cfg->d));
+  const bool ma = mfma_attn_supported(cfg), mg = mfma_gdn_supported(cfg);
+  switch (cfg->impl) {
+    case HLTA_IMPL_GENERIC:
+      p.attn = p.gdn = Impl::Generic;
+      break;
+    case HLTA_IMPL_MFMA:
+      if (!ma || !mg)
+        return fail(HLTA_E_UNSUPPORTED,
+                    "MFMA kernels need bf16 inputs, d = 128 and gdn_chunk = 64");
+      p.attn = p.gdn = Impl::Mfma;
+      break;
+    default:
+      p.attn = ma ? Impl::Mfma : Impl::Generic;
+      p.gdn = mg ? Impl::Mfma : Impl::Generic;
+  }
+  const size_t rec = p.gdn == Impl::Mfma ? gdn_mfma_record_bytes(cfg->gdn_chunk, cfg->d)
+                                         : gdn_generic_record_bytes(cfg->gdn_chunk, cfg->d);
+  int64_t nrec = 0;
+  if (!mul_ok(int64_t(cfg->B) * cfg->H, p.n_chunks, &nrec)) return fail(HLTA_E_SHAPE, "workspace overflow");
+  p.ws_gdn = size_t(nrec) * rec;
+  p.ws_total = p.ws_gdn;
+  *plan = p;
+  return HLTA_OK;
+}
+
+}  // namespace hlta
+
+using namespace hlta;
+
+extern "C" {
+
+int32_t hlta_abi_version(void) { return HLTA_ABI_VERSION; }
+
+const char* hlta_status_string(int32_t s) {
+  switch (s) {
+    case HLTA_OK: return "HLTA_OK";
+    case HLTA_E_NULL: return "HLTA_E_NULL";
+    case HLTA_E_SHAPE: return "HLTA_E_SHAPE";
+    case HLTA_E_DTYPE: return "HLTA_E_DTYPE";
+    case HLTA_E_UNSUPPORTED: return "HLTA_E_UNSUPPORTED";
+    case HLTA_E_WORKSPACE: return "HLTA_E_WORKSPACE";
+    case HLTA_E_ALIGN: return "HLTA_E_ALIGN";
+    case HLTA_E_STATE: return "HLTA_E_STATE";
+    case HLTA_E_HIP: return "HLTA_E_HIP";
+    default: return "HLTA_E_UNKNOWN";
+  }
+}
+
+const char* hlta_last_error(void) { return g_last_error.c_str(); }
+
+hlta_status hlta_validate_config(const hlta_config* cfg) {
+  clear_error();
+  return check_config(cfg);
+}
+
+size_t hlta_fwd_workspace_bytes(const hlta_config* cfg) {
+  clear_error();
+  Plan p;
+  if (!cfg || make_plan(cfg, int64_t(cfg->T) * cfg->P, &p) != HLTA_OK) return 0;
+  return p.ws_total;
+}
+
+size_t hlta_step_workspace_bytes(const hlta_config* cfg) {
+  clear_error();
+  Plan p;
+  if (!cfg || make_plan(cfg, cfg->P, &p) != HLTA_OK) return 0;
+  return p.ws_total;
+}
+
+size_t hlta_stream_ring_bytes(const hlta_config* cfg, int32_t ring_frames) {
+  clear_error();
+  if (check_config(cfg) != HLTA_OK || ring_frames < 1) return 0;
+  return size_t(cfg->B) * ring_frames * cfg->P * cfg->H * cfg->d * dtype_bytes(cfg->in_dtype);
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Internal host-side declarations shared by the HIP-free host layer
+// (hlta_host.cpp) and the launch layer (hlta_api.hip). No HIP types here, so
+// the host layer also builds with plain g++ into a CPU test binary.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../include/hlta.h"
+
+namespace hlta {
+
+// Which kernel family runs each branch.
+enum class Impl : int { Generic = 1, Mfma = 2 };
+
+struct Plan {
+  Impl attn = Impl::Generic;
+  Impl gdn = Impl::Generic;
+  int64_t L = 0;            // tokens per batch row in this call
+  int64_t n_chunks = 0;     // ceil(L / C)
+  size_t ws_gdn = 0;        // bytes of GDN scratch
+  size_t ws_total = 0;      // bytes the caller must supply
+  float scale = 0.f;        // resolved softmax scale
+};
+
+// Record a failure message for hlta_last_error() and return the status.
+hlta_status fail(hlta_status s, const std::string& msg);
+void clear_error();
+
+// Config checks that need no GPU. Returns HLTA_OK or an error (message set).
+hlta_status check_config(const hlta_config* cfg);
+
+// Kernel selection and workspace layout for a call over L tokens per row.
+hlta_status make_plan(const hlta_config* cfg, int64_t L, Plan* plan);
+
+// Is there an MFMA kernel for this shape?
+bool mfma_attn_supported(const hlta_config* cfg);
+bool mfma_gdn_supported(const hlta_config* cfg);
+
+// Per-chunk record sizes of the GDN scratch (in bytes).
+size_t gdn_generic_record_bytes(int C, int d);
+size_t gdn_mfma_record_bytes(int C, int d);
+
+// 16-byte alignment check of a device pointer (NULL passes; checked elsewhere).
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline size_t dtype_bytes(int32_t dt) { return dt == HLTA_BF16 ? 2 : 4; }
+
+}  // namespace hlta

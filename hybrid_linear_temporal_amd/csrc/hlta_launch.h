@@ -1,0 +1,27 @@
+// Kernel launchers of the HLTA library (one per kernel family).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/hlta.h"
+#include "hlta_device.h"
+
+namespace hlta {
+
+// SWA + DSWA + mix, fp32 arithmetic, any supported d and dtype.
+hipError_t launch_attn_generic(const AttnParams& p, int d, int in_dt, int out_dt, hipStream_t st);
+// SWA + DSWA + mix with bf16 MFMA (bf16 inputs, d = 128).
+hipError_t launch_attn_mfma(const AttnParams& p, int out_dt, hipStream_t st);
+
+// Gated delta rule, chunked form, fp32 arithmetic (any supported d, C, dtype).
+hipError_t launch_gdn_generic(const GdnParams& p, int d, int C, int in_dt, int out_dt, hipStream_t st);
+// Gated delta rule, chunked form with bf16 MFMA (bf16 inputs, d = 128, C = 64).
+hipError_t launch_gdn_mfma(const GdnParams& p, int out_dt, hipStream_t st);
+
+// Copy n_frames latent frames [B, frames, P, H, d] from src (frames src_f0..)
+// into ring slots (frame g -> slot g mod R). elem = element bytes.
+hipError_t launch_ring_store(const void* src, long long src_frames, long long src_f0, void* ring,
+                             int R, long long first_frame, long long n_frames, int B, long long frame_elems,
+                             int elem, hipStream_t st);
+
+}  // namespace hlta

@@ -1,0 +1,208 @@
+"""Python binding of libhlta.so (ctypes): argument marshalling only.
+
+Each function has the name of the C entry point it calls (include/hlta.h).
+PyTorch supplies device memory and the current HIP stream; every step of the
+operator runs in the library's HIP kernels. There is no fallback: if the
+library is not built, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import inputs as _inputs
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhlta.so")
+
+HLTA_OK = 0
+HLTA_F32, HLTA_BF16 = 0, 1
+HLTA_IMPL_AUTO, HLTA_IMPL_GENERIC, HLTA_IMPL_MFMA = 0, 1, 2
+STATUS = {0: "HLTA_OK", 1: "HLTA_E_NULL", 2: "HLTA_E_SHAPE", 3: "HLTA_E_DTYPE", 4: "HLTA_E_UNSUPPORTED",
+          5: "HLTA_E_WORKSPACE", 6: "HLTA_E_ALIGN", 7: "HLTA_E_STATE", 8: "HLTA_E_HIP"}
+
+# every symbol include/hlta.h declares
+EXPORTS = ("hlta_abi_version", "hlta_status_string", "hlta_last_error", "hlta_validate_config",
+           "hlta_fwd_workspace_bytes", "hlta_fwd", "hlta_stream_ring_bytes", "hlta_stream_load_prefix",
+           "hlta_step_workspace_bytes", "hlta_step_frame")
+
+
+class hlta_config(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32), ("P", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("swa_frames", ctypes.c_int32), ("dswa_dilation", ctypes.c_int32),
+                ("dswa_taps", ctypes.c_int32), ("gdn_chunk", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("gdn_l2norm_qk", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("impl", ctypes.c_int32)]
+
+
+class hlta_stream_state(ctypes.Structure):
+    _fields_ = [("S", ctypes.c_void_p), ("ring_k", ctypes.c_void_p), ("ring_v", ctypes.c_void_p),
+                ("ring_frames", ctypes.c_int32), ("frames_done", ctypes.c_int64)]
+
+
+class HLTAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libhlta.so once and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build() or "
+                          "python -m hybrid_linear_temporal_amd.build")
+    lib = ctypes.CDLL(path)
+    P, S, I32, I64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+    cfgp = ctypes.POINTER(hlta_config)
+    stp = ctypes.POINTER(hlta_stream_state)
+    sig = {
+        "hlta_abi_version": (I32, []),
+        "hlta_status_string": (ctypes.c_char_p, [I32]),
+        "hlta_last_error": (ctypes.c_char_p, []),
+        "hlta_validate_config": (I32, [cfgp]),
+        "hlta_fwd_workspace_bytes": (S, [cfgp]),
+        "hlta_fwd": (I32, [cfgp, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]),
+        "hlta_stream_ring_bytes": (S, [cfgp, I32]),
+        "hlta_stream_load_prefix": (I32, [cfgp, stp, P, P, I32, P, P]),
+        "hlta_step_workspace_bytes": (S, [cfgp]),
+        "hlta_step_frame": (I32, [cfgp, stp, P, P, P, P, P, P, P, P, P, P, I32, P, S, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != HLTA_OK:
+        raise HLTAError(status, load_library().hlta_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _tdtype(dt: int):
+    return torch.bfloat16 if dt == HLTA_BF16 else torch.float32
+
+
+def make_config(wl: _inputs.Workload | None = None, *, impl: int = HLTA_IMPL_AUTO, out_dtype: str | None = None,
+                softmax_scale: float = 0.0, l2norm: bool = True, **over) -> hlta_config:
+    """hlta_config from a Workload (fields can be overridden by keyword)."""
+    f = dict(B=wl.B, H=wl.H, T=wl.T, P=wl.P, d=wl.d, swa_frames=wl.swa_frames, dswa_dilation=wl.dswa_dilation,
+             dswa_taps=wl.dswa_taps, gdn_chunk=wl.gdn_chunk, dtype=wl.dtype) if wl is not None else {}
+    f.update(over)
+    in_dt = HLTA_BF16 if f["dtype"] == "bf16" else HLTA_F32
+    out_dt = in_dt if out_dtype is None else (HLTA_BF16 if out_dtype == "bf16" else HLTA_F32)
+    return hlta_config(f["B"], f["H"], f["T"], f["P"], f["d"], f["swa_frames"], f["dswa_dilation"],
+                       f["dswa_taps"], f["gdn_chunk"], softmax_scale, int(l2norm), in_dt, out_dt, impl)
+
+
+def hlta_validate_config(cfg: hlta_config) -> None:
+    _check(load_library().hlta_validate_config(ctypes.byref(cfg)))
+
+
+def hlta_fwd_workspace_bytes(cfg: hlta_config) -> int:
+    return int(load_library().hlta_fwd_workspace_bytes(ctypes.byref(cfg)))
+
+
+def hlta_step_workspace_bytes(cfg: hlta_config) -> int:
+    return int(load_library().hlta_step_workspace_bytes(ctypes.byref(cfg)))
+
+
+def hlta_stream_ring_bytes(cfg: hlta_config, ring_frames: int) -> int:
+    return int(load_library().hlta_stream_ring_bytes(ctypes.byref(cfg), ring_frames))
+
+
+def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def alloc_outputs(cfg: hlta_config, tokens: int, device="cuda") -> dict:
+    shape = (cfg.B, tokens, cfg.H, cfg.d)
+    dt = _tdtype(cfg.out_dtype)
+    return {n: torch.empty(shape, dtype=dt, device=device) for n in ("o_swa", "o_dswa", "o_gdn", "o_mix")}
+
+
+def hlta_fwd(cfg: hlta_config, q, k, v, a, b, mix_w, S0=None, out=None, S_out=None, workspace=None,
+             stream=None) -> dict:
+    """HLTA forward (C: hlta_fwd). Tensors on the GPU, [B, L, H, d] / [B, L, H] / [H, 3].
+
+    Returns dict of the four outputs (allocated when out is None) and S_out.
+    """
+    lib = load_library()
+    L = cfg.T * cfg.P
+    if out is None:
+        out = alloc_outputs(cfg, L, q.device)
+    if workspace is None:
+        workspace = alloc_workspace(hlta_fwd_workspace_bytes(cfg), q.device)
+    _check(lib.hlta_fwd(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(mix_w), _ptr(S0),
+                        _ptr(out["o_swa"]), _ptr(out["o_dswa"]), _ptr(out["o_gdn"]), _ptr(out["o_mix"]),
+                        _ptr(S_out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    res = dict(out)
+    res["S_out"] = S_out
+    return res
+
+
+class Stream:
+    """Device buffers of one stream (state S and the K/V rings) plus the C state struct."""
+
+    def __init__(self, cfg: hlta_config, ring_frames: int, device="cuda"):
+        self.cfg = cfg
+        dt = _tdtype(cfg.in_dtype)
+        self.S = torch.zeros((cfg.B, cfg.H, cfg.d, cfg.d), dtype=torch.float32, device=device)
+        shape = (cfg.B, ring_frames, cfg.P, cfg.H, cfg.d)
+        self.ring_k = torch.zeros(shape, dtype=dt, device=device)
+        self.ring_v = torch.zeros(shape, dtype=dt, device=device)
+        self.state = hlta_stream_state(self.S.data_ptr(), self.ring_k.data_ptr(), self.ring_v.data_ptr(),
+                                       ring_frames, 0)
+        self.workspace = alloc_workspace(hlta_step_workspace_bytes(cfg), device)
+
+    @property
+    def frames_done(self) -> int:
+        return int(self.state.frames_done)
+
+
+def hlta_stream_load_prefix(st: Stream, k_prefix, v_prefix, prefix_frames: int, S_prefix=None, stream=None):
+    _check(load_library().hlta_stream_load_prefix(ctypes.byref(st.cfg), ctypes.byref(st.state), _ptr(k_prefix),
+                                                  _ptr(v_prefix), prefix_frames, _ptr(S_prefix), _stream(stream)))
+
+
+def hlta_step_frame(st: Stream, q_f, k_f, v_f, a_f, b_f, mix_w, out=None, commit: bool = True,
+                    stream=None) -> dict:
+    """Append one latent frame to every rollout (C: hlta_step_frame)."""
+    cfg = st.cfg
+    if out is None:
+        out = alloc_outputs(cfg, cfg.P, q_f.device)
+    _check(load_library().hlta_step_frame(
+        ctypes.byref(cfg), ctypes.byref(st.state), _ptr(q_f), _ptr(k_f), _ptr(v_f), _ptr(a_f), _ptr(b_f),
+        _ptr(mix_w), _ptr(out["o_swa"]), _ptr(out["o_dswa"]), _ptr(out["o_gdn"]), _ptr(out["o_mix"]),
+        int(bool(commit)), _ptr(st.workspace), st.workspace.numel(), _stream(stream)))
+    return out
+
+
+def to_device(x: dict, dtype: str, device="cuda") -> dict:
+    """Move generator output (float32 numpy holding dtype values) to the GPU:
+    q, k, v in the workload dtype (exact conversion), gates and weights float32."""
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = {}
+    for n, arr in x.items():
+        t = torch.from_numpy(arr)
+        out[n] = t.to(device=device, dtype=tdt if n in ("q", "k", "v") else torch.float32).contiguous()
+    return out

@@ -1,0 +1,196 @@
+/*
+ * hlta.h - C ABI of the MI355X (gfx950) Hybrid Linear Temporal Attention library.
+ *
+ * HLTA (Kairos abstract on chatpaper.ai, point (2); Kairos summary page on
+ * researchpapers.dev, section on how the hybrid linear temporal attention limits
+ * drift) mixes three temporal branches over latent-video tokens:
+ *   - SWA:  sliding-window softmax attention over whole latent frames (local dynamics);
+ *   - DSWA: softmax attention over dilated past frames (mid-range dependencies);
+ *   - GDN:  gated linear attention with the delta update rule, a fixed-size
+ *           state S per head that is the persistent global memory
+ *           (Kairos related-work page, row A; long-context page, section 06):
+ *             S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,  o_t = S_t q_t.
+ * Each call returns the three branch outputs separately and their weighted sum.
+ *
+ * Conventions shared by every entry point
+ *   Layout.   Tokens are frame-major: token t = f*P + p of latent frame f.
+ *             q, k, v, outputs: [B, L, H, d] row-major (heads interleaved per
+ *             token, as a fused QKV projection emits them), L = T*P.
+ *             a, b (gates): [B, L, H] float32. mix_w: [H, 3] float32
+ *             (weights of SWA, DSWA, GDN). States S: [B, H, d, d] float32,
+ *             S[b][h][i][j] = row i (value dim) , column j (key dim).
+ *   Memory.   Every pointer is a device pointer owned by the caller, 16-byte
+ *             aligned. The library allocates nothing and keeps no per-call
+ *             state; scratch memory is the caller's workspace.
+ *   Streams.  `stream` is a hipStream_t (NULL = the default stream). Work is
+ *             enqueued asynchronously; outputs are valid after the caller
+ *             synchronises the stream. Calls on one stream run in order.
+ *   Errors.   Arguments are validated on the host before anything is launched;
+ *             a failed check returns a non-zero hlta_status, launches nothing
+ *             and leaves a message in hlta_last_error(). A launch failure
+ *             returns HLTA_E_HIP. Faults inside kernels surface at the caller's
+ *             synchronisation. Gate values are not checked: a in (0, 1] and
+ *             b in [0, 1] give the contractive memory; a = 0 is accepted (its
+ *             logarithm is floored at -80).
+ */
+#ifndef HLTA_H
+#define HLTA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HLTA_ABI_VERSION 1
+
+typedef enum {
+  HLTA_OK = 0,
+  HLTA_E_NULL = 1,        /* a required pointer is NULL */
+  HLTA_E_SHAPE = 2,       /* a size is out of range */
+  HLTA_E_DTYPE = 3,       /* unsupported dtype pair */
+  HLTA_E_UNSUPPORTED = 4, /* valid but not implemented (e.g. d = 96) */
+  HLTA_E_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+  HLTA_E_ALIGN = 6,       /* a pointer is not 16-byte aligned */
+  HLTA_E_STATE = 7,       /* streaming state inconsistent with the config */
+  HLTA_E_HIP = 8          /* a HIP runtime call or launch failed */
+} hlta_status;
+
+typedef enum { HLTA_F32 = 0, HLTA_BF16 = 1 } hlta_dtype;
+
+typedef enum {
+  HLTA_IMPL_AUTO = 0,     /* MFMA kernels where the shape has them, else generic */
+  HLTA_IMPL_GENERIC = 1,  /* plain fp32-arithmetic kernels, any supported shape */
+  HLTA_IMPL_MFMA = 2      /* bf16 MFMA kernels; HLTA_E_UNSUPPORTED where absent */
+} hlta_impl;
+
+/* Sizes and options of one HLTA layer. */
+typedef struct {
+  int32_t B;              /* batch (independent clips or rollouts), >= 1 */
+  int32_t H;              /* heads, >= 1 */
+  int32_t T;              /* latent frames, >= 0 (0 = empty call, returns HLTA_OK) */
+  int32_t P;              /* tokens per latent frame, >= 1 */
+  int32_t d;              /* head dim, d_k = d_v = d, one of 32, 64, 128 */
+  int32_t swa_frames;     /* W >= 0: SWA reads frames f-W+1 .. f (W counts the current frame) */
+  int32_t dswa_dilation;  /* dil >= 1 */
+  int32_t dswa_taps;      /* taps >= 0: DSWA reads frames f - dil*r, r = 1..taps */
+  int32_t gdn_chunk;      /* C: chunk length of the chunked delta rule, 16, 32 or 64 */
+  float softmax_scale;    /* logit scale; <= 0 selects 1/sqrt(d) */
+  int32_t gdn_l2norm_qk;  /* 1: GDN L2-normalises q and k per token (eps 1e-6 in the sqrt) */
+  int32_t in_dtype;       /* hlta_dtype of q, k, v and of the ring buffers */
+  int32_t out_dtype;      /* hlta_dtype of every output: (f32,f32), (bf16,bf16), (bf16,f32) */
+  int32_t impl;           /* hlta_impl */
+} hlta_config;
+
+/* ABI version of the loaded library (HLTA_ABI_VERSION). */
+int32_t hlta_abi_version(void);
+
+/* Static string for a status code. */
+const char* hlta_status_string(int32_t status);
+
+/* Detail of the last failed call on this thread ("" if none). */
+const char* hlta_last_error(void);
+
+/* Host-only check of a config (no GPU needed). */
+hlta_status hlta_validate_config(const hlta_config* cfg);
+
+/* Bytes of device workspace hlta_fwd needs for cfg (0 on an invalid config). */
+size_t hlta_fwd_workspace_bytes(const hlta_config* cfg);
+
+/*
+ * hlta_fwd - HLTA forward over whole clips.
+ *
+ * Per batch row b, head h and latent frame f:
+ *   o_swa  = softmax attention of the queries of frame f over every key of
+ *            frames max(0, f-W+1) .. f (bidirectional inside a frame, causal
+ *            across frames), logits scaled by softmax_scale;
+ *   o_dswa = the same over frames f - dil*r, r = 1..taps, f - dil*r >= 0;
+ *            rows of a frame with no such frame are 0;
+ *   o_gdn  = the gated delta rule run over the tokens in order from S0
+ *            (computed in chunks of C tokens; equal to the token recurrence);
+ *   o_mix  = w[h,0]*o_swa + w[h,1]*o_dswa + w[h,2]*o_gdn, evaluated in fp32
+ *            from the three outputs as stored, rounded once to out_dtype.
+ * The memory and its contraction: Kairos related-work page (row A, and the
+ * delta section on contraction rho < 1); long-context page, section 06.
+ *
+ * q, k, v   [B, L, H, d] in_dtype (read only)
+ * a, b      [B, L, H] float32 decay and write gates (read only)
+ * mix_w     [H, 3] float32 (read only)
+ * S0        [B, H, d, d] float32 start state, or NULL for zero
+ * o_swa, o_dswa, o_gdn, o_mix   [B, L, H, d] out_dtype (written; no aliasing)
+ * S_out     [B, H, d, d] float32 final state, or NULL; may equal S0
+ * workspace device buffer of at least hlta_fwd_workspace_bytes(cfg) bytes
+ */
+hlta_status hlta_fwd(const hlta_config* cfg,
+                     const void* q, const void* k, const void* v,
+                     const float* a, const float* b, const float* mix_w,
+                     const float* S0,
+                     void* o_swa, void* o_dswa, void* o_gdn, void* o_mix,
+                     float* S_out,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Streaming (Kairos article on zhichai.net, section 2.3: streaming tokens so
+ * generation proceeds incrementally without recomputing the sequence).
+ *
+ * A stream holds, per rollout b: the GDN state S [B, H, d, d] float32 and a
+ * ring of the K and V of the last ring_frames frames, [B, R, P, H, d]
+ * in_dtype each; frame j lives in slot j mod R. frames_done counts the frames
+ * appended so far (all B rollouts advance together). The caller allocates the
+ * three buffers (hlta_stream_ring_bytes gives the size of each ring) and owns
+ * the struct; saving and restoring (S, rings, frames_done) resumes a stream.
+ * R must be at least max(W - 1, dil * taps) so that every frame a step reads
+ * is still in the ring. cfg->T is ignored by the streaming calls.
+ */
+typedef struct {
+  float* S;               /* [B, H, d, d] float32 */
+  void* ring_k;           /* [B, R, P, H, d] in_dtype */
+  void* ring_v;           /* [B, R, P, H, d] in_dtype */
+  int32_t ring_frames;    /* R */
+  int64_t frames_done;    /* frames appended so far */
+} hlta_stream_state;
+
+/* Bytes of one ring buffer (K or V) for R frames (0 on an invalid config). */
+size_t hlta_stream_ring_bytes(const hlta_config* cfg, int32_t ring_frames);
+
+/*
+ * Start a stream from a prefix of prefix_frames frames: copies the K and V of
+ * the last min(prefix_frames, R) prefix frames into their ring slots, copies
+ * S_prefix (or zeros when NULL) into st->S and sets frames_done = prefix_frames.
+ * k_prefix, v_prefix: [B, prefix_frames*P, H, d] in_dtype (may be NULL only
+ * when prefix_frames == 0). S_prefix is typically the S_out of hlta_fwd over
+ * the prefix.
+ */
+hlta_status hlta_stream_load_prefix(const hlta_config* cfg, hlta_stream_state* st,
+                                    const void* k_prefix, const void* v_prefix,
+                                    int32_t prefix_frames, const float* S_prefix,
+                                    void* stream);
+
+/* Bytes of device workspace hlta_step_frame needs (0 on an invalid config). */
+size_t hlta_step_workspace_bytes(const hlta_config* cfg);
+
+/*
+ * hlta_step_frame - append frame f = st->frames_done to every rollout.
+ *
+ * Outputs equal rows [f*P, (f+1)*P) of hlta_fwd over frames 0..f of the same
+ * rollout: SWA reads frames f-W+1 .. f-1 from the ring and frame f from the
+ * inputs; DSWA reads frames f - dil*r from the ring; GDN runs the frame's P
+ * tokens from st->S. With commit != 0 the call then updates st->S in place,
+ * writes k_f, v_f to ring slot f mod R and increments st->frames_done; with
+ * commit == 0 the stream is left unchanged (several evaluations of one frame).
+ *
+ * q_f, k_f, v_f [B, P, H, d] in_dtype; a_f, b_f [B, P, H] float32;
+ * mix_w [H, 3]; o_* [B, P, H, d] out_dtype.
+ */
+hlta_status hlta_step_frame(const hlta_config* cfg, hlta_stream_state* st,
+                            const void* q_f, const void* k_f, const void* v_f,
+                            const float* a_f, const float* b_f, const float* mix_w,
+                            void* o_swa, void* o_dswa, void* o_gdn, void* o_mix,
+                            int32_t commit, void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HLTA_H */

@@ -1,0 +1,73 @@
+"""Shared helpers of the GPU parity tests: run the library through the C ABI and
+the float64 oracle on the same seeded inputs, and compare per branch."""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+from hybrid_linear_temporal_amd import hlta as H
+from hybrid_linear_temporal_amd import inputs as I
+from oracle import hlta_oracle as O
+
+BRANCHES = ("o_swa", "o_dswa", "o_gdn", "o_mix")
+# tolerances on relative L2 per branch: float32 inputs / bf16 inputs with fp32 accumulation
+TOL = {"f32": 1e-4, "bf16": 1e-2}
+
+
+def small(name, **kw) -> I.Workload:
+    base = dict(B=1, H=2, T=8, P=16, d=32, swa_frames=2, dswa_dilation=2, dswa_taps=2, gdn_chunk=16,
+                dtype="f32", seed=2000)
+    base.update(kw)
+    return I.Workload(name, **base)
+
+
+def run_gpu(wl: I.Workload, x: dict, impl=H.HLTA_IMPL_AUTO, out_dtype=None, S0=None, want_state=True,
+            **cfg_over):
+    cfg = H.make_config(wl, impl=impl, out_dtype=out_dtype, **cfg_over)
+    dev = H.to_device(x, wl.dtype)
+    S_out = torch.empty((cfg.B, cfg.H, cfg.d, cfg.d), dtype=torch.float32, device="cuda") if want_state else None
+    S0_t = None if S0 is None else torch.from_numpy(np.asarray(S0, np.float32)).cuda()
+    res = H.hlta_fwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], S0=S0_t, S_out=S_out)
+    torch.cuda.synchronize()
+    return res
+
+
+def to64(t) -> np.ndarray:
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def run_oracle(wl: I.Workload, x: dict, S0=None, heads=None, gdn="chunked", **over):
+    T = over.get("T", wl.T)
+    return O.hlta_forward(x["q"], x["k"], x["v"], x["a"], x["b"], x["w"], T, wl.P,
+                          over.get("swa_frames", wl.swa_frames), over.get("dswa_dilation", wl.dswa_dilation),
+                          over.get("dswa_taps", wl.dswa_taps), over.get("gdn_chunk", wl.gdn_chunk),
+                          S0=S0, gdn=gdn, heads=heads)
+
+
+def compare(gpu: dict, ref, tol: float, heads=None, label=""):
+    """rel-L2 per branch (and state) over the given heads; asserts <= tol."""
+    errs = {}
+    for i, n in enumerate(BRANCHES):
+        g = to64(gpu[n])
+        r = ref[i]
+        if heads is not None:
+            g = np.stack([g[b, :, h] for b, h in heads])
+            r = np.stack([r[b, :, h] for b, h in heads])
+        errs[n] = O.rel_l2(g, r)
+    if gpu.get("S_out") is not None:
+        g = to64(gpu["S_out"])
+        r = ref[4]
+        if heads is not None:
+            g = np.stack([g[b, h] for b, h in heads])
+            r = np.stack([r[b, h] for b, h in heads])
+        errs["S_out"] = O.rel_l2(g, r)
+    print(label, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for n, e in errs.items():
+        assert e <= tol, f"{label} {n}: rel-L2 {e:.3e} > {tol:.0e}"
+    return errs
+
+
+def replace(wl, **kw):
+    return dataclasses.replace(wl, **kw)

@@ -1,0 +1,135 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and validates arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from hybrid_linear_temporal_amd import hlta as H
+from hybrid_linear_temporal_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "hlta.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hlta_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(H.LIB_PATH):
+        pytest.fail("libhlta.so is not built (run __graft_entry__.build())")
+    return H.load_library()
+
+
+def test_library_exports_every_header_symbol(lib):
+    names = _header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(H.EXPORTS)
+    assert lib.hlta_abi_version() == 1
+
+
+def test_struct_layout_matches_header():
+    # 13 int32 fields + 1 float = 56 bytes; stream state: 3 pointers, int32, int64
+    assert ctypes.sizeof(H.hlta_config) == 14 * 4
+    assert ctypes.sizeof(H.hlta_stream_state) == 8 * 3 + 8 + 8
+
+
+def _cfg(**kw):
+    return H.make_config(I.P480_T31, **kw)
+
+
+def test_valid_configs(lib):
+    for wl in I.WORKLOADS.values():
+        H.hlta_validate_config(H.make_config(wl))
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("B", 0, 2), ("H", 0, 2), ("T", -1, 2), ("P", 0, 2), ("d", 96, 4), ("swa_frames", -1, 2),
+    ("dswa_dilation", 0, 2), ("dswa_taps", -2, 2), ("gdn_chunk", 48, 4), ("in_dtype", 7, 3),
+    ("impl", 9, 2), ("softmax_scale", float("inf"), 2), ("gdn_l2norm_qk", 2, 2)])
+def test_invalid_config_codes(lib, field, value, status):
+    cfg = _cfg()
+    setattr(cfg, field, value)
+    with pytest.raises(H.HLTAError) as e:
+        H.hlta_validate_config(cfg)
+    assert e.value.status == status
+    assert field.split("_")[0].lower() in str(e.value).lower() or str(e.value)
+
+
+def test_f32_in_bf16_out_rejected(lib):
+    cfg = H.make_config(I.TINY_F32, out_dtype="bf16")
+    with pytest.raises(H.HLTAError) as e:
+        H.hlta_validate_config(cfg)
+    assert e.value.status == 3
+
+
+def test_overflow_rejected(lib):
+    cfg = _cfg(T=1 << 20, P=1 << 12)
+    with pytest.raises(H.HLTAError):
+        H.hlta_validate_config(cfg)
+
+
+def test_workspace_sizes(lib):
+    cfg = _cfg()
+    ws = H.hlta_fwd_workspace_bytes(cfg)
+    assert ws > 0
+    chunks = -(-cfg.T * cfg.P // cfg.gdn_chunk)
+    assert ws % (cfg.B * cfg.H * chunks) == 0
+    bad = _cfg(d=96)
+    assert H.hlta_fwd_workspace_bytes(bad) == 0
+    assert H.hlta_step_workspace_bytes(cfg) > 0
+    assert H.hlta_stream_ring_bytes(cfg, 16) == cfg.B * 16 * cfg.P * cfg.H * cfg.d * 2
+    assert H.hlta_stream_ring_bytes(cfg, 0) == 0
+
+
+def test_mfma_impl_needs_supported_shape(lib):
+    cfg = H.make_config(I.TINY_F32, impl=H.HLTA_IMPL_MFMA)
+    assert H.hlta_fwd_workspace_bytes(cfg) == 0
+    assert b"MFMA" in lib.hlta_last_error()
+
+
+def test_fwd_argument_errors_before_launch(lib):
+    cfg = _cfg()
+    ws = H.hlta_fwd_workspace_bytes(cfg)
+    # pointers are never dereferenced on the host; validation fails first
+    fake = ctypes.c_void_p(1 << 20)
+    mis = ctypes.c_void_p((1 << 20) + 8)
+    args = [fake] * 6 + [None] + [fake] * 4 + [None, fake]
+    # NULL q
+    a2 = list(args)
+    a2[0] = None
+    assert lib.hlta_fwd(ctypes.byref(cfg), *a2, ws, None) == 1
+    # misaligned k
+    a2 = list(args)
+    a2[1] = mis
+    assert lib.hlta_fwd(ctypes.byref(cfg), *a2, ws, None) == 6
+    # small workspace
+    assert lib.hlta_fwd(ctypes.byref(cfg), *args, ws - 1, None) == 5
+    # NULL workspace
+    a2 = list(args)
+    a2[12] = None
+    assert lib.hlta_fwd(ctypes.byref(cfg), *a2, ws, None) == 1
+    # NULL config
+    assert lib.hlta_fwd(None, *args, ws, None) == 1
+    assert b"NULL" in lib.hlta_last_error()
+
+
+def test_stream_argument_errors(lib):
+    cfg = H.make_config(I.STREAM_P480)
+    fake = 1 << 20
+    st = H.hlta_stream_state(fake, fake, fake, 8, 0)       # ring too short for dil*taps = 16
+    assert lib.hlta_stream_load_prefix(ctypes.byref(cfg), ctypes.byref(st), None, None, 0, None, None) == 7
+    st = H.hlta_stream_state(None, fake, fake, 16, 0)
+    assert lib.hlta_stream_load_prefix(ctypes.byref(cfg), ctypes.byref(st), None, None, 0, None, None) == 1
+    st = H.hlta_stream_state(fake, fake, fake, 16, -1)
+    p = ctypes.c_void_p(fake)
+    assert lib.hlta_step_frame(ctypes.byref(cfg), ctypes.byref(st), p, p, p, p, p, p, p, p, p, p, 1, p,
+                               1 << 40, None) == 7
+    st = H.hlta_stream_state(fake, fake, fake, 16, 0)
+    assert lib.hlta_stream_load_prefix(ctypes.byref(cfg), ctypes.byref(st), None, None, 3, None, None) == 1

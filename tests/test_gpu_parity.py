@@ -1,0 +1,132 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle, per
+branch, on seeded inputs. Tolerances on relative L2 error: 1e-4 for float32
+inputs, 1e-2 for bf16 inputs with fp32 accumulation."""
+import numpy as np
+import pytest
+import torch
+
+from hybrid_linear_temporal_amd import hlta as H
+from hybrid_linear_temporal_amd import inputs as I
+from oracle import hlta_oracle as O
+from tests.helpers import TOL, compare, run_gpu, run_oracle, small, to64, replace
+
+pytestmark = pytest.mark.gpu
+
+IMPLS = [H.HLTA_IMPL_GENERIC, H.HLTA_IMPL_AUTO]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    H.load_library()
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_tiny_f32(impl):
+    wl = I.TINY_F32
+    x = I.make_clip(wl)
+    S0 = 0.1 * np.random.default_rng(5).standard_normal((wl.B, wl.H, wl.d, wl.d))
+    S0 = S0.astype(np.float32)
+    ref = run_oracle(wl, x, S0=S0, gdn="recurrent")
+    got = run_gpu(wl, x, impl=impl, S0=S0)
+    compare(got, ref, TOL["f32"], label=f"tiny impl={impl}")
+
+
+F32_CASES = [
+    small("f32_d64_c32", H=3, T=10, P=50, d=64, swa_frames=3, dswa_dilation=3, dswa_taps=2, gdn_chunk=32),
+    small("f32_d128_c64", B=2, H=1, T=7, P=37, d=128, swa_frames=2, dswa_dilation=2, dswa_taps=3, gdn_chunk=64),
+    small("f32_P1", H=2, T=40, P=1, d=32, swa_frames=5, dswa_dilation=4, dswa_taps=4, gdn_chunk=16),
+    small("f32_noswa_notaps", T=6, P=20, swa_frames=0, dswa_taps=0),
+    small("f32_W_gt_T", T=5, P=24, swa_frames=9, dswa_dilation=1, dswa_taps=7),
+]
+
+
+@pytest.mark.parametrize("wl", F32_CASES, ids=lambda w: w.name)
+def test_f32_shapes(wl):
+    x = I.make_clip(wl)
+    ref = run_oracle(wl, x, gdn="recurrent")
+    got = run_gpu(wl, x)
+    compare(got, ref, TOL["f32"], label=wl.name)
+
+
+BF16_CASES = [
+    small("bf16_d128_c64", B=2, H=3, T=18, P=70, d=128, swa_frames=3, dswa_dilation=4, dswa_taps=4,
+          gdn_chunk=64, dtype="bf16", seed=2100),
+    small("bf16_d128_c64_P130", B=1, H=2, T=9, P=130, d=128, swa_frames=3, dswa_dilation=2, dswa_taps=4,
+          gdn_chunk=64, dtype="bf16", seed=2101),
+    small("bf16_d64_c32", B=1, H=2, T=12, P=33, d=64, swa_frames=2, dswa_dilation=3, dswa_taps=3,
+          gdn_chunk=32, dtype="bf16", seed=2102),
+    small("bf16_d128_c16", B=1, H=2, T=6, P=64, d=128, swa_frames=3, dswa_dilation=2, dswa_taps=2,
+          gdn_chunk=16, dtype="bf16", seed=2103),
+]
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+@pytest.mark.parametrize("wl", BF16_CASES, ids=lambda w: w.name)
+def test_bf16_shapes(wl, impl):
+    x = I.make_clip(wl)
+    ref = run_oracle(wl, x)
+    got = run_gpu(wl, x, impl=impl)
+    compare(got, ref, TOL["bf16"], label=f"{wl.name} impl={impl}")
+
+
+def test_bf16_in_f32_out():
+    wl = BF16_CASES[0]
+    x = I.make_clip(wl)
+    ref = run_oracle(wl, x)
+    got = run_gpu(wl, x, out_dtype="f32")
+    assert got["o_swa"].dtype == torch.float32
+    compare(got, ref, TOL["bf16"], label="bf16->f32")
+
+
+def test_peaked_attention_and_long_memory():
+    # q scaled x20 makes the softmax peaked (exercises the running max);
+    # a close to 1 stresses the state carried across many chunks
+    wl = BF16_CASES[0]
+    x = I.make_clip(wl, q_scale=20.0, a_range=(0.999, 1.0))
+    ref = run_oracle(wl, x)
+    got = run_gpu(wl, x)
+    compare(got, ref, TOL["bf16"], label="peaked")
+
+
+def test_mix_is_weighted_sum_of_stored_branches():
+    wl = BF16_CASES[1]
+    x = I.make_clip(wl)
+    got = run_gpu(wl, x)
+    w = x["w"].astype(np.float64)
+    mix = (w[None, None, :, 0, None] * to64(got["o_swa"]) + w[None, None, :, 1, None] * to64(got["o_dswa"])
+           + w[None, None, :, 2, None] * to64(got["o_gdn"]))
+    g = to64(got["o_mix"])
+    # one bf16 rounding of an fp32 sum
+    assert np.all(np.abs(g - mix) <= 2.0 ** -8 * np.abs(mix) + 1e-6)
+
+
+def test_deterministic():
+    wl = BF16_CASES[0]
+    x = I.make_clip(wl)
+    r1 = run_gpu(wl, x)
+    r2 = run_gpu(wl, x)
+    for n in ("o_swa", "o_dswa", "o_gdn", "o_mix", "S_out"):
+        assert torch.equal(r1[n], r2[n]), n
+
+
+def test_empty_clip_passes_state_through():
+    wl = replace(BF16_CASES[0], T=0)
+    cfg = H.make_config(wl)
+    S0 = torch.randn((wl.B, wl.H, wl.d, wl.d), device="cuda")
+    S_out = torch.full_like(S0, 7.0)
+    e = torch.empty((1,), device="cuda")
+    z = torch.empty((wl.B, 0, wl.H, wl.d), dtype=torch.bfloat16, device="cuda")
+    out = {n: z for n in ("o_swa", "o_dswa", "o_gdn", "o_mix")}
+    H.hlta_fwd(cfg, z, z, z, e, e, e, S0=S0, out=out, S_out=S_out)
+    torch.cuda.synchronize()
+    assert torch.equal(S_out, S0)
+
+
+def test_chunk_size_invariance():
+    # the chunked form gives the token recurrence for every chunk length
+    wl = small("f32_chunks", H=2, T=6, P=45, d=64, swa_frames=2, dswa_dilation=2, dswa_taps=2, gdn_chunk=16)
+    x = I.make_clip(wl)
+    outs = [to64(run_gpu(wl, x, gdn_chunk=c)["o_gdn"]) for c in (16, 32, 64)]
+    for o in outs[1:]:
+        assert O.rel_l2(o, outs[0]) < 1e-5
