@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""HLTA forward throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one whole HLTA forward (gated-delta-rule memory, SWA, DSWA and the
+mix) over one synthetic clip that is already resident in HBM. Prints one JSON
+line: tokens/s over the timed steps, the roofline of the dominant kernel (the
+softmax-branch kernel, priced against the bf16 MFMA peak) measured with HIP
+events on the stream the library launches on, and the float64 CPU oracle timed
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "HLTA fwd tokens/s at 480P 31 latent frames (1 MI355X); % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def valid_pairs(T, P, W, dil, taps):
+    """(SWA pairs, DSWA pairs) per (batch row, head): queries x keys of the frame sets."""
+    swa = dsw = 0
+    for f in range(T):
+        swa += min(W, f + 1) * P * P
+        dsw += min(taps, f // dil) * P * P
+    return swa, dsw
+
+
+def work(wl):
+    """Algorithmic work of one forward: flops of the softmax branches (4*d per
+    valid query-key pair: QK^T and PV), and compulsory HBM bytes of the memory
+    branch (q, k, v read, a and b read, o_gdn written, per token-head, plus S out)."""
+    swa, dsw = valid_pairs(wl.T, wl.P, wl.swa_frames, wl.dswa_dilation, wl.dswa_taps)
+    heads = wl.B * wl.H
+    attn_flops = 4 * wl.d * (swa + dsw) * heads
+    el = 2 if wl.dtype == "bf16" else 4
+    per_token_head = 3 * wl.d * el + 8 + wl.d * el
+    gdn_bytes = per_token_head * wl.L * heads + heads * wl.d * wl.d * 4
+    return attn_flops, gdn_bytes, per_token_head
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "hybrid_linear_temporal_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_file, digest):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", kernel_file)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != digest or "bytes_per_launch" not in kv:
+        return None
+    return float(kv["bytes_per_launch"])
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The float64 oracle (as it stands) on whole heads of the same workload,
+    until the time budget is spent; scaled to whole-workload tokens/s."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from hybrid_linear_temporal_amd import inputs as I
+    from oracle import hlta_oracle as O
+
+    w = I.mix_weights(wl.seed, wl.H)
+    done = []
+    t_total = 0.0
+    for b in range(wl.B):
+        for h in range(wl.H):
+            q, k, v = I.head_qkv(wl.seed, I.S_CLIP, b, h, wl.L, wl.d, wl.dtype)
+            a, bb = I.head_gates(wl.seed, I.S_CLIP, b, h, wl.L)
+            t0 = time.perf_counter()
+            O.hlta_head(q, k, v, a, bb, w[h], wl.T, wl.P, wl.swa_frames, wl.dswa_dilation, wl.dswa_taps,
+                        wl.gdn_chunk)
+            t_total += time.perf_counter() - t0
+            done.append((b, h))
+            if t_total >= budget_s:
+                break
+        if t_total >= budget_s:
+            break
+    frac = len(done) / (wl.B * wl.H)
+    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    return {"value": wl.B * wl.L * frac / t_total, "unit": "tokens/s", "cores": int(max(blas) if blas else 1),
+            "kind": "oracle",
+            "sample": f"float64 oracle (SWA, DSWA, chunked GDN, mix) on {len(done)} of {wl.B * wl.H} "
+                      f"(batch, head) pairs of {wl.name}, {t_total:.1f} s; tokens/s scaled by that fraction; "
+                      f"host CPUs available: {len(os.sched_getaffinity(0))}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="p480_T31_bf16")
+    ap.add_argument("--impl", type=int, default=0, help="0 auto, 1 generic, 2 mfma")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    from hybrid_linear_temporal_amd import hlta as H
+    from hybrid_linear_temporal_amd import inputs as I
+
+    wl = I.WORKLOADS[args.workload]
+    if wl.rollouts:
+        raise SystemExit("use a whole-clip workload (the streaming workload has its own driver)")
+    torch.cuda.set_device(0)
+    H.load_library()
+    print(f"# generating {wl.name} inputs", file=sys.stderr, flush=True)
+    x = I.make_clip(wl, threads=16)
+    dev = H.to_device(x, wl.dtype)
+    del x
+    cfg = H.make_config(wl, impl=args.impl)
+    out = H.alloc_outputs(cfg, wl.L)
+    ws = H.alloc_workspace(H.hlta_fwd_workspace_bytes(cfg))
+    S_out = torch.empty((wl.B, wl.H, wl.d, wl.d), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        H.hlta_gdn_fwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], out["o_gdn"], S_out=S_out,
+                       workspace=ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        H.hlta_attn_fwd(cfg, dev["q"], dev["k"], dev["v"], dev["w"], out["o_gdn"], out, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    print(f"# warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    print(f"# timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    gdn_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ms = elapsed * 1e3 / args.steps
+    tokens = wl.B * wl.L
+    attn_flops, gdn_bytes, per_th = work(wl)
+    attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+    gdn_gbs = gdn_bytes / (gdn_ms * 1e-3) / 1e9
+    mfma = cfg.impl != H.HLTA_IMPL_GENERIC and wl.dtype == "bf16" and wl.d == 128
+    attn_src = "attn_mfma.hip" if mfma else "attn_generic.hip"
+    traffic = read_traffic(f"traffic_{attn_src.split('.')[0]}_{wl.name}.txt", source_digest(attn_src))
+    res = {
+        "metric": METRIC, "value": tokens * args.steps / elapsed, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "P": wl.P, "d": wl.d,
+                   "swa_frames": wl.swa_frames, "dswa_dilation": wl.dswa_dilation, "dswa_taps": wl.dswa_taps,
+                   "gdn_chunk": wl.gdn_chunk, "tokens": tokens, "impl": ["auto", "generic", "mfma"][args.impl]},
+        "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "kernel": attn_src.split(".")[0], "flops_per_launch": attn_flops,
+                     "avg_launch_ms": attn_ms},
+        "gdn_roofline": {"bound": "hbm", "achieved": gdn_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gdn_gbs / PEAK_HBM_GBS, "bytes_per_launch": gdn_bytes,
+                         "bytes_per_token_head": per_th, "avg_ms": gdn_ms},
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (float64 oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

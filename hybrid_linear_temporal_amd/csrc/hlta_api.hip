@@ -1,5 +1,5 @@
-// C-ABI entry points that launch work: hlta_fwd, hlta_stream_load_prefix,
-// hlta_step_frame. Validation happens on the host before any launch; the
+// C-ABI entry points that launch work: hlta_fwd, hlta_gdn_fwd, hlta_attn_fwd,
+// hlta_stream_load_prefix, hlta_step_frame. Validation happens on the host before any launch; the
 // library allocates nothing (scratch is the caller's workspace).
 #include <string>
 
@@ -46,10 +46,9 @@ hlta_status check_outputs(const float* a, const float* b, const float* mix_w, vo
   return HLTA_OK;
 }
 
-// GDN over L tokens per row, then SWA/DSWA + mix. attn.* query fields set by caller.
-hlta_status run_layer(const hlta_config* cfg, const Plan& plan, const void* q, const void* k, const void* v,
-                      const float* a, const float* b, const float* S0, float* S_out, void* o_gdn,
-                      void* workspace, AttnParams attn, hipStream_t st) {
+hlta_status run_gdn(const hlta_config* cfg, const Plan& plan, const void* q, const void* k, const void* v,
+                    const float* a, const float* b, const float* S0, float* S_out, void* o_gdn, void* workspace,
+                    hipStream_t st) {
   GdnParams g{};
   g.q = q;
   g.k = k;
@@ -71,12 +70,57 @@ hlta_status run_layer(const hlta_config* cfg, const Plan& plan, const void* q, c
                      ? launch_gdn_mfma(g, cfg->out_dtype, st)
                      : launch_gdn_generic(g, cfg->d, cfg->gdn_chunk, cfg->in_dtype, cfg->out_dtype, st);
   if (e != hipSuccess) return hip_fail(e, "gated delta rule launch");
+  return HLTA_OK;
+}
 
+hlta_status run_attn(const hlta_config* cfg, const Plan& plan, const void* o_gdn, AttnParams attn,
+                     hipStream_t st) {
   attn.o_gdn = o_gdn;
   attn.scale_log2 = plan.scale * kLog2e;
-  e = plan.attn == Impl::Mfma ? launch_attn_mfma(attn, cfg->out_dtype, st)
-                              : launch_attn_generic(attn, cfg->d, cfg->in_dtype, cfg->out_dtype, st);
+  hipError_t e = plan.attn == Impl::Mfma
+                     ? launch_attn_mfma(attn, cfg->out_dtype, st)
+                     : launch_attn_generic(attn, cfg->d, cfg->in_dtype, cfg->out_dtype, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return HLTA_OK;
+}
+
+// GDN over L tokens per row, then SWA/DSWA + mix. attn.* query fields set by caller.
+hlta_status run_layer(const hlta_config* cfg, const Plan& plan, const void* q, const void* k, const void* v,
+                      const float* a, const float* b, const float* S0, float* S_out, void* o_gdn,
+                      void* workspace, AttnParams attn, hipStream_t st) {
+  HLTA_TRY(run_gdn(cfg, plan, q, k, v, a, b, S0, S_out, o_gdn, workspace, st));
+  return run_attn(cfg, plan, o_gdn, attn, st);
+}
+
+AttnParams full_attn_params(const hlta_config* cfg, const void* q, const void* k, const void* v,
+                            const float* mix_w, void* o_swa, void* o_dswa, void* o_mix) {
+  AttnParams at{};
+  at.q = q;
+  at.k = k;
+  at.v = v;
+  at.o_swa = o_swa;
+  at.o_dswa = o_dswa;
+  at.o_mix = o_mix;
+  at.mix_w = mix_w;
+  at.B = cfg->B;
+  at.H = cfg->H;
+  at.T = cfg->T;
+  at.P = cfg->P;
+  at.W = cfg->swa_frames;
+  at.dil = cfg->dswa_dilation;
+  at.taps = cfg->dswa_taps;
+  at.R = 0;
+  at.f0 = 0;
+  return at;
+}
+
+hlta_status check_workspace(const Plan& plan, const void* workspace, size_t ws_bytes) {
+  if (plan.ws_total > 0) {
+    HLTA_TRY(need(workspace, "workspace"));
+    if (ws_bytes < plan.ws_total)
+      return fail(HLTA_E_WORKSPACE, "workspace has " + std::to_string(ws_bytes) + " bytes, needs " +
+                                        std::to_string(plan.ws_total));
+  }
   return HLTA_OK;
 }
 
@@ -109,30 +153,57 @@ hlta_status hlta_fwd(const hlta_config* cfg, const void* q, const void* k, const
   HLTA_TRY(need(k, "k"));
   HLTA_TRY(need(v, "v"));
   HLTA_TRY(check_outputs(a, b, mix_w, o_swa, o_dswa, o_gdn, o_mix));
-  if (plan.ws_total > 0) {
-    HLTA_TRY(need(workspace, "workspace"));
-    if (ws_bytes < plan.ws_total)
-      return fail(HLTA_E_WORKSPACE, "workspace has " + std::to_string(ws_bytes) + " bytes, needs " +
-                                        std::to_string(plan.ws_total));
-  }
-  AttnParams at{};
-  at.q = q;
-  at.k = k;
-  at.v = v;
-  at.o_swa = o_swa;
-  at.o_dswa = o_dswa;
-  at.o_mix = o_mix;
-  at.mix_w = mix_w;
-  at.B = cfg->B;
-  at.H = cfg->H;
-  at.T = cfg->T;
-  at.P = cfg->P;
-  at.W = cfg->swa_frames;
-  at.dil = cfg->dswa_dilation;
-  at.taps = cfg->dswa_taps;
-  at.R = 0;
-  at.f0 = 0;
+  HLTA_TRY(check_workspace(plan, workspace, ws_bytes));
+  AttnParams at = full_attn_params(cfg, q, k, v, mix_w, o_swa, o_dswa, o_mix);
   return run_layer(cfg, plan, q, k, v, a, b, S0, S_out, o_gdn, workspace, at, st);
+}
+
+hlta_status hlta_gdn_fwd(const hlta_config* cfg, const void* q, const void* k, const void* v, const float* a,
+                         const float* b, const float* S0, void* o_gdn, float* S_out, void* workspace,
+                         size_t ws_bytes, void* stream) {
+  clear_error();
+  Plan plan;
+  HLTA_TRY(check_config(cfg));
+  HLTA_TRY(make_plan(cfg, int64_t(cfg->T) * cfg->P, &plan));
+  HLTA_TRY(maybe(S0, "S0"));
+  HLTA_TRY(maybe(S_out, "S_out"));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (plan.L == 0) {
+    if (S_out && S_out != S0) {
+      hipError_t e = S0 ? hipMemcpyAsync(S_out, S0, state_bytes(cfg), hipMemcpyDeviceToDevice, st)
+                        : hipMemsetAsync(S_out, 0, state_bytes(cfg), st);
+      if (e != hipSuccess) return hip_fail(e, "state copy");
+    }
+    return HLTA_OK;
+  }
+  HLTA_TRY(need(q, "q"));
+  HLTA_TRY(need(k, "k"));
+  HLTA_TRY(need(v, "v"));
+  HLTA_TRY(need(a, "a"));
+  HLTA_TRY(need(b, "b"));
+  HLTA_TRY(need(o_gdn, "o_gdn"));
+  HLTA_TRY(check_workspace(plan, workspace, ws_bytes));
+  return run_gdn(cfg, plan, q, k, v, a, b, S0, S_out, o_gdn, workspace, st);
+}
+
+hlta_status hlta_attn_fwd(const hlta_config* cfg, const void* q, const void* k, const void* v,
+                          const float* mix_w, const void* o_gdn, void* o_swa, void* o_dswa, void* o_mix,
+                          void* stream) {
+  clear_error();
+  Plan plan;
+  HLTA_TRY(check_config(cfg));
+  HLTA_TRY(make_plan(cfg, int64_t(cfg->T) * cfg->P, &plan));
+  if (plan.L == 0) return HLTA_OK;
+  HLTA_TRY(need(q, "q"));
+  HLTA_TRY(need(k, "k"));
+  HLTA_TRY(need(v, "v"));
+  HLTA_TRY(need(mix_w, "mix_w"));
+  HLTA_TRY(need(o_gdn, "o_gdn"));
+  HLTA_TRY(need(o_swa, "o_swa"));
+  HLTA_TRY(need(o_dswa, "o_dswa"));
+  HLTA_TRY(need(o_mix, "o_mix"));
+  AttnParams at = full_attn_params(cfg, q, k, v, mix_w, o_swa, o_dswa, o_mix);
+  return run_attn(cfg, plan, o_gdn, at, static_cast<hipStream_t>(stream));
 }
 
 static hlta_status check_stream(const hlta_config* cfg, const hlta_stream_state* st) {
@@ -194,12 +265,7 @@ hlta_status hlta_step_frame(const hlta_config* cfg, hlta_stream_state* st, const
   HLTA_TRY(need(k_f, "k_f"));
   HLTA_TRY(need(v_f, "v_f"));
   HLTA_TRY(check_outputs(a_f, b_f, mix_w, o_swa, o_dswa, o_gdn, o_mix));
-  if (plan.ws_total > 0) {
-    HLTA_TRY(need(workspace, "workspace"));
-    if (ws_bytes < plan.ws_total)
-      return fail(HLTA_E_WORKSPACE, "workspace has " + std::to_string(ws_bytes) + " bytes, needs " +
-                                        std::to_string(plan.ws_total));
-  }
+  HLTA_TRY(check_workspace(plan, workspace, ws_bytes));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const long long f = st->frames_done;
   AttnParams at{};

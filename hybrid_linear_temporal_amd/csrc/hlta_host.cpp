@@ -58,8 +58,9 @@ hlta_status check_config(const hlta_config* cfg) {
   return HLTA_OK;
 }
 
+// the MFMA attention kernel addresses a 64-key tile from at most two frames
 bool mfma_attn_supported(const hlta_config* cfg) {
-  return false && cfg->in_dtype == HLTA_BF16 && cfg->d == 128;
+  return cfg->in_dtype == HLTA_BF16 && cfg->d == 128 && cfg->P >= 64;
 }
 
 bool mfma_gdn_supported(const hlta_config* cfg) {
@@ -92,10 +93,10 @@ hlta_status make_plan(const hlta_config* cfg, int64_t L, Plan* plan) {
       p.attn = p.gdn = Impl::Generic;
       break;
     case HLTA_IMPL_MFMA:
-      if (!ma || !mg)
-        return fail(HLTA_E_UNSUPPORTED,
-                    "MFMA kernels need bf16 inputs, d = 128 and gdn_chunk = 64");
-      p.attn = p.gdn = Impl::Mfma;
+      if (!ma)
+        return fail(HLTA_E_UNSUPPORTED, "MFMA kernels need bf16 inputs and d = 128");
+      p.attn = Impl::Mfma;
+      p.gdn = mg ? Impl::Mfma : Impl::Generic;
       break;
     default:
       p.attn = ma ? Impl::Mfma : Impl::Generic;

@@ -25,8 +25,8 @@ STATUS = {0: "HLTA_OK", 1: "HLTA_E_NULL", 2: "HLTA_E_SHAPE", 3: "HLTA_E_DTYPE", 
 
 # every symbol include/hlta.h declares
 EXPORTS = ("hlta_abi_version", "hlta_status_string", "hlta_last_error", "hlta_validate_config",
-           "hlta_fwd_workspace_bytes", "hlta_fwd", "hlta_stream_ring_bytes", "hlta_stream_load_prefix",
-           "hlta_step_workspace_bytes", "hlta_step_frame")
+           "hlta_fwd_workspace_bytes", "hlta_fwd", "hlta_gdn_fwd", "hlta_attn_fwd", "hlta_stream_ring_bytes",
+           "hlta_stream_load_prefix", "hlta_step_workspace_bytes", "hlta_step_frame")
 
 
 class hlta_config(ctypes.Structure):
@@ -70,6 +70,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "hlta_validate_config": (I32, [cfgp]),
         "hlta_fwd_workspace_bytes": (S, [cfgp]),
         "hlta_fwd": (I32, [cfgp, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]),
+        "hlta_gdn_fwd": (I32, [cfgp, P, P, P, P, P, P, P, P, P, S, P]),
+        "hlta_attn_fwd": (I32, [cfgp, P, P, P, P, P, P, P, P, P]),
         "hlta_stream_ring_bytes": (S, [cfgp, I32]),
         "hlta_stream_load_prefix": (I32, [cfgp, stp, P, P, I32, P, P]),
         "hlta_step_workspace_bytes": (S, [cfgp]),
@@ -158,6 +160,22 @@ def hlta_fwd(cfg: hlta_config, q, k, v, a, b, mix_w, S0=None, out=None, S_out=No
     res = dict(out)
     res["S_out"] = S_out
     return res
+
+
+def hlta_gdn_fwd(cfg: hlta_config, q, k, v, a, b, o_gdn, S0=None, S_out=None, workspace=None, stream=None):
+    """Memory branch alone (C: hlta_gdn_fwd)."""
+    if workspace is None:
+        workspace = alloc_workspace(hlta_fwd_workspace_bytes(cfg), q.device)
+    _check(load_library().hlta_gdn_fwd(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(S0),
+                                       _ptr(o_gdn), _ptr(S_out), _ptr(workspace), workspace.numel(),
+                                       _stream(stream)))
+
+
+def hlta_attn_fwd(cfg: hlta_config, q, k, v, mix_w, o_gdn, out: dict, stream=None):
+    """Softmax branches and the mix (C: hlta_attn_fwd); out holds o_swa, o_dswa, o_mix."""
+    _check(load_library().hlta_attn_fwd(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(mix_w), _ptr(o_gdn),
+                                        _ptr(out["o_swa"]), _ptr(out["o_dswa"]), _ptr(out["o_mix"]),
+                                        _stream(stream)))
 
 
 class Stream:

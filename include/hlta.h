@@ -131,6 +131,30 @@ hlta_status hlta_fwd(const hlta_config* cfg,
                      void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * hlta_gdn_fwd - the memory branch alone: o_gdn and S_out exactly as hlta_fwd
+ * computes them (the gated delta rule of the Kairos related-work page, row A,
+ * and of the long-context page, section 06). Arguments as in hlta_fwd.
+ */
+hlta_status hlta_gdn_fwd(const hlta_config* cfg,
+                         const void* q, const void* k, const void* v,
+                         const float* a, const float* b, const float* S0,
+                         void* o_gdn, float* S_out,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * hlta_attn_fwd - the two softmax branches (Kairos abstract, point (2):
+ * sliding windows for local dynamics, dilated windows for mid-range
+ * dependencies) and the mix, exactly as hlta_fwd computes them. o_gdn is read
+ * by the mix (it is the output of a previous hlta_gdn_fwd on the same
+ * stream); hlta_gdn_fwd followed by hlta_attn_fwd equals hlta_fwd. Needs no
+ * workspace. Arguments as in hlta_fwd.
+ */
+hlta_status hlta_attn_fwd(const hlta_config* cfg,
+                          const void* q, const void* k, const void* v,
+                          const float* mix_w, const void* o_gdn,
+                          void* o_swa, void* o_dswa, void* o_mix, void* stream);
+
+/*
  * Streaming (Kairos article on zhichai.net, section 2.3: streaming tokens so
  * generation proceeds incrementally without recomputing the sequence).
  *
