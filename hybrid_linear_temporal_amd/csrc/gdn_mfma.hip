@@ -1,5 +1,489 @@
+// Gated delta rule with bf16 MFMA on gfx950 (bf16 inputs, d = 128, chunk 64).
+//
+// The memory (Kairos related-work page, row A: the GatedDeltaNet state S_t
+// with decay gate alpha_t; long-context page, section 06: erase what the
+// current key stores, then write, under an overall forget gate):
+//   S_t = a_t S_{t-1} (I - b_t k^_t k^_t^T) + b_t v_t k^_t^T,  o_t = S_t q^_t,
+// with q^, k^ the L2-normalised q, k. Chunked form (block-parallel inside a
+// chunk, recurrent across chunks; long-context page, sections 02 and 06): with
+// g_i = sum_{j<=i} log a_j, gamma_i = exp(g_i) inside a chunk,
+//   A_ij = b_i exp(g_i - g_j) k^_i.k^_j (j < i),  T = (I + A)^-1,
+//   W = T diag(b gamma) K^,  U' = T diag(b) V,
+//   U = U' - W S^T,  O = diag(gamma) Q^ S^T + [exp(g_i - g_j) q^_i.k^_j]_{j<=i} U,
+//   S <- gamma_C S + U^T diag(gamma_C / gamma) K^.
+//
+// Kernel 1, gdn_prep_mfma: one workgroup per (chunk, head, batch row), fully
+// parallel. Gram matrices K K^T and Q K^T on raw bf16 inputs (exact products,
+// fp32 sums) with the norms and gates applied in fp32; T by blocked forward
+// substitution in fp32 (16x16 diagonal blocks per wave, then the off-diagonal
+// blocks level by level); W^T and U' on MFMA with the raw K, V read transposed
+// from LDS (ds_read_b64_tr_b16). Writes one record per chunk.
+//
+// Kernel 2, gdn_chain_mfma: one workgroup per (64 value channels, head, batch
+// row), four waves of 16 value channels each, chunks in order. Each wave keeps
+// its slice of S^T (128 x 16, fp32) in MFMA accumulator layout for the whole
+// sequence. Its bf16 copy is the B operand of W S^T and Q S^T directly, because
+// the reduction (d_k) index of an MFMA may be permuted as long as both operands
+// agree; the A operands are read from LDS in that permuted order. The same holds
+// for U (C layout) as B operand of Aqk U and of the state update, so the chain
+// never moves S or U through LDS.
 #include "hlta_device.h"
+#include "hlta_internal.h"
 #include "hlta_launch.h"
+
 namespace hlta {
-hipError_t launch_gdn_mfma(const GdnParams&, int, hipStream_t) { return hipErrorNotSupported; }
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr int D = 128;
+constexpr int C = 64;
+constexpr int NT = 256;
+constexpr int XP = D + 8;   // LDS pitch (bf16) of 64 x 128 tiles
+constexpr int CP = C + 8;   // LDS pitch (bf16) of 64 x 64 / 128 x 64 tiles
+constexpr int FP = C + 4;   // LDS pitch (fp32) of 64 x 64 matrices
+constexpr float kL2Eps = 1e-6f;
+constexpr float kLogAFloor = -80.f;
+using R = GdnMfmaRec;
+static_assert(R::C == C && R::D == D, "record layout");
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+
+__device__ __forceinline__ bf16x8 join(const bf16x4& lo, const bf16x4& hi) {
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Transposed LDS read (gfx950): inside each group of 16 lanes, lane j gets
+// element j%4 of the 4-element rows addressed by lanes 4e + j/4, e = 0..3.
+__device__ __forceinline__ bf16x4 ld_tr(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x4 ld4(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
+
+__device__ __forceinline__ void load_rows(bf16 (*dst)[XP], const bf16* src, size_t row_stride, int n, int tid) {
+  // 64 rows x 16 chunks of 16 B
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (tid >> 4) + 16 * i, c = tid & 15;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < n) v = *reinterpret_cast<const uint4*>(src + size_t(row) * row_stride + c * 8);
+    *reinterpret_cast<uint4*>(&dst[row][c * 8]) = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// kernel 1: per-chunk preparation
+// ---------------------------------------------------------------------------
+
+struct PrepSmem {
+  bf16 K[C][XP];
+  bf16 Q[C][XP];    // after the Gram products: Aqk staging (bf16 [C][CP])
+  bf16 V[C][XP];
+  float A[C][FP];
+  float T[C][FP];
+  float X[4][16][17];
+  float g[C], bb[C], rk[C], rq[C];
+};
+
+// one 16x16 block product on VALU: lane owns row r = lane/4, cols 4*(lane%4)..+3
+__device__ __forceinline__ void blk_acc(float (*M)[FP], int r0, int c0, const float* B, int bpitch,
+                                        int b0r, int b0c, int lane, float out[4]) {
+  // out[c] += sum_k M[r0 + r][c0 + k] * B[(b0r + k) * bpitch + b0c + c]
+  const int r = lane >> 2, cc = (lane & 3) * 4;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const float m = M[r0 + r][c0 + k];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) out[c] += m * B[(b0r + k) * bpitch + b0c + cc + c];
+  }
+}
+
+__global__ void __launch_bounds__(NT, 1)
+gdn_prep_mfma(GdnParams p) {
+  __shared__ __attribute__((aligned(16))) PrepSmem sm;
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const long long t0 = (long long)chunk * C;
+  const int n = int(p.L - t0 < C ? p.L - t0 : C);
+  const size_t HD = size_t(p.H) * D;
+  const size_t base = (size_t(b) * p.L + t0) * HD + size_t(h) * D;
+  const size_t gbase = (size_t(b) * p.L + t0) * p.H + h;
+  unsigned char* rec = p.ws + (size_t(b * p.H + h) * p.n_chunks + chunk) * p.rec_bytes;
+
+  load_rows(sm.K, static_cast<const bf16*>(p.k) + base, HD, n, tid);
+  load_rows(sm.Q, static_cast<const bf16*>(p.q) + base, HD, n, tid);
+  load_rows(sm.V, static_cast<const bf16*>(p.v) + base, HD, n, tid);
+  for (int e = tid; e < C * FP; e += NT) (&sm.T[0][0])[e] = 0.f;
+  if (wave == 0) {
+    // gates: inclusive scan of log a over the chunk (one token per lane)
+    float la = 0.f, bi = 0.f;
+    if (lane < n) {
+      la = fmaxf(logf(p.a[gbase + size_t(lane) * p.H]), kLogAFloor);
+      bi = p.b[gbase + size_t(lane) * p.H];
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(la, off);
+      if (lane >= off) la += y;
+    }
+    sm.g[lane] = la;
+    sm.bb[lane] = bi;
+  }
+  __syncthreads();
+  {
+    // inverse norms: 4 threads per row, 32 elements each
+    const int row = tid >> 2, part = tid & 3;
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float kv = static_cast<float>(sm.K[row][part * 32 + i]);
+      const float qv = static_cast<float>(sm.Q[row][part * 32 + i]);
+      sk += kv * kv;
+      sq += qv * qv;
+    }
+    sk += __shfl_xor(sk, 1, 4);
+    sk += __shfl_xor(sk, 2, 4);
+    sq += __shfl_xor(sq, 1, 4);
+    sq += __shfl_xor(sq, 2, 4);
+    if (part == 0) {
+      sm.rk[row] = p.l2norm ? 1.f / sqrtf(sk + kL2Eps) : 1.f;
+      sm.rq[row] = p.l2norm ? 1.f / sqrtf(sq + kL2Eps) : 1.f;
+    }
+  }
+  __syncthreads();
+
+  // ---- Gram products: wave w owns token rows 16w..16w+15 ----
+  {
+    f32x4 kk[4], qk[4];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) kk[jb] = qk[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&sm.K[16 * wave + l16][32 * ks + 8 * g]);
+      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sm.Q[16 * wave + l16][32 * ks + 8 * g]);
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&sm.K[16 * jb + l16][32 * ks + 8 * g]);
+        kk[jb] = mfma16(ak, bk, kk[jb]);
+        qk[jb] = mfma16(aq, bk, qk[jb]);
+      }
+    }
+    __syncthreads();   // Q is dead from here; its space stages Aqk
+    bf16 (*aqk)[CP] = reinterpret_cast<bf16 (*)[CP]>(&sm.Q[0][0]);
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      const int j = 16 * jb + l16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * wave + 4 * g + e;
+        const float ratio = j <= i ? __expf(sm.g[i] - sm.g[j]) : 0.f;
+        sm.A[i][j] = j < i ? sm.bb[i] * ratio * sm.rk[i] * sm.rk[j] * kk[jb][e] : 0.f;
+        aqk[i][j] = static_cast<bf16>(ratio * sm.rq[i] * sm.rk[j] * qk[jb][e]);
+      }
+    }
+  }
+  __syncthreads();
+  // Aqk to the record (64 rows x 8 chunks of 16 B)
+  {
+    const bf16 (*aqk)[CP] = reinterpret_cast<const bf16 (*)[CP]>(&sm.Q[0][0]);
+    bf16* dst = reinterpret_cast<bf16*>(rec + R::AQK);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid + NT * i, row = e >> 3, c = e & 7;
+      *reinterpret_cast<uint4*>(dst + row * C + c * 8) = *reinterpret_cast<const uint4*>(&aqk[row][c * 8]);
+    }
+  }
+
+  // ---- T = (I + A)^-1: diagonal 16x16 blocks (wave w, lane = column) ----
+  if (l16 == lane) {
+    const int o = 16 * wave, c = lane;
+    float t[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float s = r == c ? 1.f : 0.f;
+      if (r > c) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          if (k >= c && k < r) s -= sm.A[o + r][o + k] * t[k];
+      }
+      t[r] = s;
+      sm.T[o + r][o + c] = s;
+    }
+  }
+  __syncthreads();
+  // off-diagonal blocks, level by level: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
+  for (int level = 1; level < 4; ++level) {
+    const int i = wave, j = wave - level;
+    if (j >= 0) {
+      float x[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int k = j; k < i; ++k) blk_acc(sm.A, 16 * i, 16 * k, &sm.T[0][0], FP, 16 * k, 16 * j, lane, x);
+      const int r = lane >> 2, cc = (lane & 3) * 4;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sm.X[wave][r][cc + c] = x[c];
+    }
+    __syncthreads();
+    if (j >= 0) {
+      float y[4] = {0.f, 0.f, 0.f, 0.f};
+      const int r = lane >> 2, cc = (lane & 3) * 4;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float t = sm.T[16 * i + r][16 * i + k];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) y[c] += t * sm.X[wave][k][cc + c];
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sm.T[16 * i + r][16 * j + cc + c] = -y[c];
+    }
+    __syncthreads();
+  }
+
+  // ---- W^T = K^T T'^T with T' = T diag(b gamma rk): wave w -> d_k blocks 2w, 2w+1 ----
+  {
+    bf16* wn = reinterpret_cast<bf16*>(rec + R::WN);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+      const int mb = 2 * wave + mi;
+      f32x4 acc[4];
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) acc[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int js = 0; js < 2; ++js) {
+        // A = K^T rows d_k = 16mb + l16, slots = tokens 32js + 8g + 0..7 (transposed reads)
+        const int jr = 32 * js + 8 * g;
+        const bf16x4 lo = ld_tr(&sm.K[jr + (l16 >> 2)][16 * mb + 4 * (l16 & 3)]);
+        const bf16x4 hi = ld_tr(&sm.K[jr + 4 + (l16 >> 2)][16 * mb + 4 * (l16 & 3)]);
+        const bf16x8 a = join(lo, hi);
+        float sc[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int j = jr + q;
+          sc[q] = sm.bb[j] * __expf(sm.g[j]) * sm.rk[j];
+        }
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) {
+          // B = T'^T: col = token i = 16ib + l16, slots j = jr + 0..7
+          const int i = 16 * ib + l16;
+          bf16x8 bv;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) bv[q] = static_cast<bf16>(sm.T[i][jr + q] * sc[q]);
+          acc[ib] = mfma16(a, bv, acc[ib]);
+        }
+      }
+      // C layout: col = token i, rows d_k = 16mb + 4g + e -> Wn[i][d_k..d_k+3] = -W
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) {
+        const int i = 16 * ib + l16;
+        const bf16x4 v = {static_cast<bf16>(-acc[ib][0]), static_cast<bf16>(-acc[ib][1]),
+                          static_cast<bf16>(-acc[ib][2]), static_cast<bf16>(-acc[ib][3])};
+        *reinterpret_cast<bf16x4*>(wn + i * D + 16 * mb + 4 * g) = v;
+      }
+    }
+  }
+  // ---- U' = T diag(b) V: wave w -> token rows 16w..16w+15, all 8 d_v blocks ----
+  {
+    bf16* upt = reinterpret_cast<bf16*>(rec + R::UPT);
+    f32x4 acc[8];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int js = 0; js < 2; ++js) {
+      const int jr = 32 * js + 8 * g;
+      const int i = 16 * wave + l16;
+      bf16x8 a;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) a[q] = static_cast<bf16>(sm.T[i][jr + q] * sm.bb[jr + q]);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const bf16x4 lo = ld_tr(&sm.V[jr + (l16 >> 2)][16 * nb + 4 * (l16 & 3)]);
+        const bf16x4 hi = ld_tr(&sm.V[jr + 4 + (l16 >> 2)][16 * nb + 4 * (l16 & 3)]);
+        acc[nb] = mfma16(a, join(lo, hi), acc[nb]);
+      }
+    }
+    // C layout: col = d_v = 16nb + l16, rows = tokens 16w + 4g + e -> UpT[d_v][tok..tok+3]
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const bf16x4 v = {static_cast<bf16>(acc[nb][0]), static_cast<bf16>(acc[nb][1]),
+                        static_cast<bf16>(acc[nb][2]), static_cast<bf16>(acc[nb][3])};
+      *reinterpret_cast<bf16x4*>(upt + (16 * nb + l16) * C + 16 * wave + 4 * g) = v;
+    }
+  }
+  // ---- per-token scalars ----
+  if (tid < C) {
+    const int i = tid;
+    const float gl = sm.g[C - 1];
+    float* sq = reinterpret_cast<float*>(rec + R::SQ);
+    float* skp = reinterpret_cast<float*>(rec + R::SK);
+    sq[i] = i < n ? __expf(sm.g[i]) * sm.rq[i] : 0.f;
+    skp[i] = i < n ? __expf(gl - sm.g[i]) * sm.rk[i] : 0.f;
+    if (i == 0) *reinterpret_cast<float*>(rec + R::GC) = __expf(gl);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// kernel 2: the chunk-to-chunk state pass
+// ---------------------------------------------------------------------------
+
+struct ChainSmem {
+  bf16 Wn[C][XP];
+  bf16 Q[C][XP];
+  bf16 K[C][XP];
+  bf16 Aqk[C][CP];
+  bf16 UpT[64][CP];   // this workgroup's 64 value channels
+  float sq[C], sk[C];
+  float gC;
+};
+
+template <typename Tout>
+__global__ void __launch_bounds__(NT, 1)
+gdn_chain_mfma(GdnParams p) {
+  __shared__ __attribute__((aligned(16))) ChainSmem sm;
+  const int vhalf = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int v0 = 64 * vhalf + 16 * wave;   // this wave's value channels v0 .. v0+15
+  const size_t HD = size_t(p.H) * D;
+  const size_t sbase = (size_t(b) * p.H + h) * D * D;
+  Tout* o = static_cast<Tout*>(p.o);
+
+  // S^T slice in C layout: block mb holds d_k rows 16mb + 4g + e, column d_v = v0 + l16
+  f32x4 st[8];
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) {
+    if (p.S0) {
+      const float4 v = *reinterpret_cast<const float4*>(p.S0 + sbase + size_t(v0 + l16) * D + 16 * mb + 4 * g);
+      st[mb] = f32x4{v.x, v.y, v.z, v.w};
+    } else {
+      st[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  for (int chunk = 0; chunk < p.n_chunks; ++chunk) {
+    const long long t0 = (long long)chunk * C;
+    const int n = int(p.L - t0 < C ? p.L - t0 : C);
+    const unsigned char* rec = p.ws + (size_t(b * p.H + h) * p.n_chunks + chunk) * p.rec_bytes;
+    const size_t base = (size_t(b) * p.L + t0) * HD + size_t(h) * D;
+    __syncthreads();   // previous chunk's LDS reads are done
+    load_rows(sm.Q, static_cast<const bf16*>(p.q) + base, HD, n, tid);
+    load_rows(sm.K, static_cast<const bf16*>(p.k) + base, HD, n, tid);
+    {
+      const bf16* wn = reinterpret_cast<const bf16*>(rec + R::WN);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = (tid >> 4) + 16 * i, c = tid & 15;
+        *reinterpret_cast<uint4*>(&sm.Wn[row][c * 8]) = *reinterpret_cast<const uint4*>(wn + row * D + c * 8);
+      }
+      const bf16* aqk = reinterpret_cast<const bf16*>(rec + R::AQK);
+      const bf16* upt = reinterpret_cast<const bf16*>(rec + R::UPT) + size_t(64 * vhalf) * C;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int e = tid + NT * i, row = e >> 3, c = e & 7;
+        *reinterpret_cast<uint4*>(&sm.Aqk[row][c * 8]) = *reinterpret_cast<const uint4*>(aqk + row * C + c * 8);
+        *reinterpret_cast<uint4*>(&sm.UpT[row][c * 8]) = *reinterpret_cast<const uint4*>(upt + row * C + c * 8);
+      }
+      if (tid < C) {
+        sm.sq[tid] = reinterpret_cast<const float*>(rec + R::SQ)[tid];
+        sm.sk[tid] = reinterpret_cast<const float*>(rec + R::SK)[tid];
+      }
+      if (tid == 0) sm.gC = *reinterpret_cast<const float*>(rec + R::GC);
+    }
+    __syncthreads();
+
+    // bf16 copy of S^T as B operand: K-step ks takes blocks 2ks, 2ks+1 (d_k = 32ks + 16(i/4) + 4g + i%4)
+    bf16x8 sb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sb[ks][e] = static_cast<bf16>(st[2 * ks][e]);
+        sb[ks][4 + e] = static_cast<bf16>(st[2 * ks + 1][e]);
+      }
+
+    // (1) U = U' - W S^T: rows = tokens 16tb + 4g + e, col = d_v
+    f32x4 u[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const bf16x4 up = ld4(&sm.UpT[16 * wave + l16][16 * tb + 4 * g]);
+      u[tb] = f32x4{static_cast<float>(up[0]), static_cast<float>(up[1]), static_cast<float>(up[2]),
+                    static_cast<float>(up[3])};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16* wr = &sm.Wn[16 * tb + l16][32 * ks + 4 * g];
+        u[tb] = mfma16(join(ld4(wr), ld4(wr + 16)), sb[ks], u[tb]);
+      }
+    }
+    // (2) O = diag(sq) (Q S^T) + Aqk U
+    bf16x8 ub[2], usb[2];
+#pragma unroll
+    for (int js = 0; js < 2; ++js)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ta = 32 * js + 4 * g + e, tb2 = 32 * js + 16 + 4 * g + e;
+        ub[js][e] = static_cast<bf16>(u[2 * js][e]);
+        ub[js][4 + e] = static_cast<bf16>(u[2 * js + 1][e]);
+        usb[js][e] = static_cast<bf16>(u[2 * js][e] * sm.sk[ta]);
+        usb[js][4 + e] = static_cast<bf16>(u[2 * js + 1][e] * sm.sk[tb2]);
+      }
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16* qr = &sm.Q[16 * tb + l16][32 * ks + 4 * g];
+        x = mfma16(join(ld4(qr), ld4(qr + 16)), sb[ks], x);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] *= sm.sq[16 * tb + 4 * g + e];
+#pragma unroll
+      for (int js = 0; js < 2; ++js) {
+        const bf16* ar = &sm.Aqk[16 * tb + l16][32 * js + 4 * g];
+        x = mfma16(join(ld4(ar), ld4(ar + 16)), ub[js], x);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tok = 16 * tb + 4 * g + e;
+        if (tok < n) o[(size_t(b) * p.L + t0 + tok) * HD + size_t(h) * D + v0 + l16] = from_f32<Tout>(x[e]);
+      }
+    }
+    // (3) S^T <- gamma_C S^T + K^T diag(sk) U, A = K^T read transposed from LDS
+    const float gc = sm.gC;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st[mb][e] *= gc;
+#pragma unroll
+      for (int js = 0; js < 2; ++js) {
+        const bf16x4 lo = ld_tr(&sm.K[32 * js + 4 * g + (l16 >> 2)][16 * mb + 4 * (l16 & 3)]);
+        const bf16x4 hi = ld_tr(&sm.K[32 * js + 16 + 4 * g + (l16 >> 2)][16 * mb + 4 * (l16 & 3)]);
+        st[mb] = mfma16(join(lo, hi), usb[js], st[mb]);
+      }
+    }
+  }
+  if (p.S_out) {
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+      *reinterpret_cast<float4*>(p.S_out + sbase + size_t(v0 + l16) * D + 16 * mb + 4 * g) =
+          make_float4(st[mb][0], st[mb][1], st[mb][2], st[mb][3]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gdn_mfma(const GdnParams& p, int out_dt, hipStream_t st) {
+  if (p.rec_bytes < R::BYTES) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gdn_prep_mfma, dim3(p.n_chunks, p.H, p.B), dim3(NT), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (out_dt == HLTA_BF16)
+    hipLaunchKernelGGL((gdn_chain_mfma<bf16>), dim3(2, p.H, p.B), dim3(NT), 0, st, p);
+  else
+    hipLaunchKernelGGL((gdn_chain_mfma<float>), dim3(2, p.H, p.B), dim3(NT), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace hlta

@@ -64,7 +64,7 @@ bool mfma_attn_supported(const hlta_config* cfg) {
 }
 
 bool mfma_gdn_supported(const hlta_config* cfg) {
-  return false && cfg->in_dtype == HLTA_BF16 && cfg->d == 128 && cfg->gdn_chunk == 64;
+  return cfg->in_dtype == HLTA_BF16 && cfg->d == 128 && cfg->gdn_chunk == 64;
 }
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -74,10 +74,8 @@ size_t gdn_generic_record_bytes(int C, int d) {
   return align_up(sizeof(float) * (4 * size_t(C) * d + size_t(C) * C + 1), 256);
 }
 
-// MFMA record: W, U' [C x d] bf16 + Aqk [C x C] bf16 + per-token gamma, gamma_C/gamma,
-// inverse norms of q and k (fp32)
 size_t gdn_mfma_record_bytes(int C, int d) {
-  return align_up(2 * (2 * size_t(C) * d + size_t(C) * C) + sizeof(float) * (4 * size_t(C) + 4), 256);
+  return (C == int(GdnMfmaRec::C) && d == int(GdnMfmaRec::D)) ? GdnMfmaRec::BYTES : 0;
 }
 
 hlta_status make_plan(const hlta_config* cfg, int64_t L, Plan* plan) {
@@ -93,10 +91,10 @@ hlta_status make_plan(const hlta_config* cfg, int64_t L, Plan* plan) {
       p.attn = p.gdn = Impl::Generic;
       break;
     case HLTA_IMPL_MFMA:
-      if (!ma)
-        return fail(HLTA_E_UNSUPPORTED, "MFMA kernels need bf16 inputs and d = 128");
-      p.attn = Impl::Mfma;
-      p.gdn = mg ? Impl::Mfma : Impl::Generic;
+      if (!ma || !mg)
+        return fail(HLTA_E_UNSUPPORTED,
+                    "MFMA kernels need bf16 inputs, d = 128, gdn_chunk = 64 and P >= 64");
+      p.attn = p.gdn = Impl::Mfma;
       break;
     default:
       p.attn = ma ? Impl::Mfma : Impl::Generic;

@@ -40,6 +40,24 @@ bool mfma_gdn_supported(const hlta_config* cfg);
 
 // Per-chunk record sizes of the GDN scratch (in bytes).
 size_t gdn_generic_record_bytes(int C, int d);
+
+// Record of one chunk for the MFMA gated-delta-rule kernels (C = 64, d = 128):
+//   Wn   bf16 [C][d]  -W = -T diag(b gamma) K^   (row per token)
+//   UpT  bf16 [d][C]  U'^T = (T diag(b) V)^T     (row per value channel)
+//   Aqk  bf16 [C][C]  exp(g_i - g_j) q^_i.k^_j, j <= i
+//   sq   f32  [C]     gamma_i / ||q_i||          (scales rows of Q S^T)
+//   sk   f32  [C]     gamma_C / (gamma_i ||k_i||) (scales rows of U in the state update)
+//   gC   f32          gamma_C
+struct GdnMfmaRec {
+  static constexpr size_t C = 64, D = 128;
+  static constexpr size_t WN = 0;
+  static constexpr size_t UPT = WN + 2 * C * D;
+  static constexpr size_t AQK = UPT + 2 * D * C;
+  static constexpr size_t SQ = AQK + 2 * C * C;
+  static constexpr size_t SK = SQ + 4 * C;
+  static constexpr size_t GC = SK + 4 * C;
+  static constexpr size_t BYTES = (GC + 16 + 255) / 256 * 256;
+};
 size_t gdn_mfma_record_bytes(int C, int d);
 
 // 16-byte alignment check of a device pointer (NULL passes; checked elsewhere).
