@@ -11,18 +11,26 @@
 //
 // Mapping to CDNA4:
 //  * workgroup = 4 waves = 128 query rows of one frame of one head; each wave
-//    owns 32 query rows and keeps its Q block in registers as MFMA operand;
+//    owns 32 query rows and keeps them in registers as MFMA operands; two
+//    workgroups per CU (two waves per SIMD) so one wave's softmax overlaps the
+//    other's MFMAs and memory waits;
 //  * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    each lane then holds 32 key scores of one query, which is exactly the
 //    B-operand layout of O^T = V^T P^T, so P never goes through LDS;
-//  * K tiles are staged in LDS key-major (16-byte rows reads), V tiles
-//    transposed (d-major) so the A operand of the P.V product is two 8-byte
-//    LDS reads; both are double-buffered with one barrier per tile;
-//  * the softmax runs in the exp2 domain with the scale folded into one FMA;
-//    row sums stay per half-wave until the epilogue;
+//  * K and V tiles sit in LDS key-major, 16-byte chunks XOR-swizzled by row so
+//    column reads of 16 rows hit distinct banks; the V^T operand comes from
+//    ds_read_b64_tr_b16 transposed reads; tiles go global -> LDS by direct
+//    loads (global_load_lds_dwordx4, no staging registers), double-buffered
+//    with one barrier per tile and the next tile in flight during compute;
+//  * the key stream of a branch is walked with wave-uniform (frame, token)
+//    counters, so tile addresses cost no division;
+//  * softmax in the exp2 domain with the scale folded into one FMA; the
+//    running max is only raised (and the accumulators rescaled) when a tile's
+//    max exceeds it by more than 2^8, which leaves the result unchanged
+//    (numerator and denominator share the stale max) and skips most rescales;
 //  * workgroups are ordered so each XCD (blockIdx mod 8) walks a contiguous
-//    range of (head, frame) items, heaviest frames first: the 13 query tiles
-//    of a frame and the neighbouring frames share K/V tiles in that XCD's L2.
+//    range of (head, frame) items, heaviest frames first, so the query tiles of
+//    a frame and the neighbouring frames share K/V tiles in that XCD's L2.
 #include "hlta_device.h"
 #include "hlta_launch.h"
 
@@ -34,114 +42,121 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-constexpr int D = 128;        // head dim
-constexpr int QT = 128;       // query rows per workgroup
-constexpr int KT = 64;        // keys per tile
-constexpr int NT = 256;       // threads
-constexpr int KS = D + 8;     // LDS row pitch of K (bf16), 272 B
-constexpr int VS = KT + 4;    // LDS row pitch of V^T (bf16), 136 B
+constexpr int D = 128;           // head dim
+constexpr int RB = 1;            // 32-row query blocks per wave
+constexpr int QT = 4 * 32 * RB;  // query rows per workgroup (128)
+constexpr int KT = 64;           // keys per tile
+constexpr int NT = 256;          // threads
 constexpr int kXcds = 8;
+constexpr float kLazy = 8.f;     // raise the running max only past this margin (log2 units)
 
+// one K or V tile: 64 rows of 256 B; 16-byte chunk c of row r lives at chunk c ^ (r & 15)
+struct Tile {
+  uint4 row[KT][16];
+};
 struct Smem {
-  bf16 K[2][KT][KS];
-  bf16 Vt[2][D][VS];
+  Tile K[2];
+  Tile V[2];
 };
 
-// Staging registers of one K/V tile: each thread moves 4 K chunks of 16 B and
-// a 4-key x 8-d block of V.
-struct Stage {
-  uint4 k[4];
-  uint4 v[4];
-};
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 15); }
 
-// A tile of 64 consecutive keys of the virtual sequence spans at most two
-// frames (P >= 64) or several (P < 64). Keys are addressed from the frame
-// bases of the tile's first frame onwards; with P >= 64 the two bases are
-// wave-uniform and live in scalar registers.
-struct TileAddr {
-  const bf16* k0;    // K row of the tile's first key
+// Wave-uniform values kept in scalar registers.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+template <typename T>
+__device__ __forceinline__ const T* uni(const T* ptr) {
+  const unsigned long long u = reinterpret_cast<unsigned long long>(ptr);
+  const unsigned lo = __builtin_amdgcn_readfirstlane(unsigned(u));
+  const unsigned hi = __builtin_amdgcn_readfirstlane(unsigned(u >> 32));
+  return reinterpret_cast<const T*>((static_cast<unsigned long long>(hi) << 32) | lo);
+}
+
+// Walks the virtual key sequence of one branch tile by tile. A tile of 64
+// keys spans at most two frames (P >= 64); all fields are wave-uniform.
+struct KeyStream {
+  const AttnParams* p;
+  int b, h, branch, nswa, nframes;
+  long long f;
+  int slot, pk;            // current tile starts at token pk of frame slot `slot`
+  const bf16* k0;          // token 0 of the current frame
   const bf16* v0;
-  const bf16* k1;    // K row 0 of the next frame (if the tile crosses into it)
+  const bf16* k1;          // token 0 of the next frame (the current one if none)
   const bf16* v1;
-  int split;         // keys [0, split) come from the first frame
+
+  __device__ __forceinline__ void frame_bases(int sl, const bf16*& kb, const bf16*& vb) const {
+    const long long g = branch_frame(branch, f, nswa, p->dil, sl);
+    kb = uni(key_frame_ptr<bf16, D>(static_cast<const bf16*>(p->k), static_cast<const bf16*>(p->ring_k), *p, b, h, g));
+    vb = uni(key_frame_ptr<bf16, D>(static_cast<const bf16*>(p->v), static_cast<const bf16*>(p->ring_v), *p, b, h, g));
+  }
+  __device__ __forceinline__ void start() {
+    slot = 0;
+    pk = 0;
+    if (nframes > 0) frame_bases(0, k0, v0);
+    if (nframes > 1) frame_bases(1, k1, v1);
+    else {
+      k1 = k0;
+      v1 = v0;
+    }
+  }
+  __device__ __forceinline__ void advance() {
+    pk += KT;
+    if (pk >= p->P) {
+      pk -= p->P;
+      ++slot;
+      k0 = k1;
+      v0 = v1;
+      if (slot + 1 < nframes) frame_bases(slot + 1, k1, v1);
+    }
+  }
 };
 
-__device__ __forceinline__ TileAddr tile_addr(const AttnParams& p, int b, int h, int branch, long long f,
-                                              int nswa, int nframes, long long t0) {
-  const bf16* km = static_cast<const bf16*>(p.k);
-  const bf16* vm = static_cast<const bf16*>(p.v);
-  const bf16* kr = static_cast<const bf16*>(p.ring_k);
-  const bf16* vr = static_cast<const bf16*>(p.ring_v);
-  const int s = int(t0 / p.P);
-  const int pk = int(t0 - (long long)s * p.P);
-  const long long g0 = branch_frame(branch, f, nswa, p.dil, s);
-  const size_t off = size_t(pk) * p.H * D;
-  TileAddr a;
-  a.k0 = key_frame_ptr<bf16, D>(km, kr, p, b, h, g0) + off;
-  a.v0 = key_frame_ptr<bf16, D>(vm, vr, p, b, h, g0) + off;
-  a.split = p.P - pk;
-  if (s + 1 < nframes) {
-    const long long g1 = branch_frame(branch, f, nswa, p.dil, s + 1);
-    a.k1 = key_frame_ptr<bf16, D>(km, kr, p, b, h, g1);
-    a.v1 = key_frame_ptr<bf16, D>(vm, vr, p, b, h, g1);
-  } else {
-    a.k1 = a.k0;
-    a.v1 = a.v0;
-  }
-  return a;
-}
-
-// row of key kk (0..63) of the tile; P >= KT assumed (at most one frame switch)
-__device__ __forceinline__ const bf16* tile_row(const bf16* base0, const bf16* base1, int split, int kk,
-                                                size_t tok_stride) {
-  return kk < split ? base0 + size_t(kk) * tok_stride : base1 + size_t(kk - split) * tok_stride;
-}
-
-__device__ __forceinline__ void load_tile(Stage& st, const AttnParams& p, int b, int h, int branch, long long f,
-                                          int nswa, int nframes, long long nk, long long t0, int tid) {
-  const TileAddr ta = tile_addr(p, b, h, branch, f, nswa, nframes, t0);
-  const size_t ts = size_t(p.H) * D;
-  const int kleft = int(nk - t0 < KT ? nk - t0 : KT);
-  // K: key = tid/16 + 16*i, 16-byte chunk c = tid%16
-  const int c = tid & 15;
+// Direct global -> LDS copy of the current tile: wave w moves rows 16w .. 16w+15,
+// four rows (1 KB) per instruction; lane i lands at chunk position i%16 of row
+// 16w + 4j + i/16 and so loads the chunk that the swizzle puts there. Rows past
+// the end of the sequence re-read the last valid row (finite data; their scores
+// are masked, so they contribute exactly zero).
+__device__ __forceinline__ void issue_tile(Tile& Kd, Tile& Vd, const KeyStream& ks, int kleft, int wave, int lane) {
+  const size_t ts = size_t(ks.p->H) * D;
+  const int split = ks.p->P - ks.pk;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int kk = (tid >> 4) + 16 * i;
-    if (kk < kleft)
-      st.k[i] = *reinterpret_cast<const uint4*>(tile_row(ta.k0, ta.k1, ta.split, kk, ts) + c * 8);
-    else
-      st.k[i] = make_uint4(0, 0, 0, 0);
-  }
-  // V: keys 4*kg .. 4*kg+3, d = 8*dg .. 8*dg+7 with dg = tid%16, kg = tid/16
-  const int kg = tid >> 4, dg = tid & 15;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int kk = 4 * kg + i;
-    if (kk < kleft)
-      st.v[i] = *reinterpret_cast<const uint4*>(tile_row(ta.v0, ta.v1, ta.split, kk, ts) + dg * 8);
-    else
-      st.v[i] = make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < 4; ++j) {
+    const int r0 = 16 * wave + 4 * j;
+    const int row = r0 + (lane >> 4);
+    const int rr = row < kleft ? row : kleft - 1;
+    const int c = swz(row, lane & 15);
+    const size_t koff = rr < split ? size_t(ks.pk + rr) * ts : size_t(rr - split) * ts;
+    const bf16* ksrc = (rr < split ? ks.k0 : ks.k1) + koff + c * 8;
+    const bf16* vsrc = (rr < split ? ks.v0 : ks.v1) + koff + c * 8;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(ksrc),
+                                     (__attribute__((address_space(3))) void*)(&Kd.row[r0][0]), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vsrc),
+                                     (__attribute__((address_space(3))) void*)(&Vd.row[r0][0]), 16, 0, 0);
   }
 }
 
-__device__ __forceinline__ void store_tile(Smem& sm, int buf, const Stage& st, int tid) {
-  const int c = tid & 15;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<uint4*>(&sm.K[buf][(tid >> 4) + 16 * i][c * 8]) = st.k[i];
-  const int kg = tid >> 4, dg = tid & 15;
-  // transpose the 4 x 8 block: Vt[8dg + e][4kg + i] = V[4kg + i][8dg + e]
-  const unsigned short* v0 = reinterpret_cast<const unsigned short*>(&st.v[0]);
-  const unsigned short* v1 = reinterpret_cast<const unsigned short*>(&st.v[1]);
-  const unsigned short* v2 = reinterpret_cast<const unsigned short*>(&st.v[2]);
-  const unsigned short* v3 = reinterpret_cast<const unsigned short*>(&st.v[3]);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    u16x4 w = {v0[e], v1[e], v2[e], v3[e]};
-    *reinterpret_cast<u16x4*>(&sm.Vt[buf][8 * dg + e][4 * kg]) = w;
-  }
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+// 8 consecutive d values (chunk c) of key row r
+__device__ __forceinline__ bf16x8 ld_chunk(const Tile& t, int r, int c) {
+  const uint4 u = t.row[r][swz(r, c)];
+  return *reinterpret_cast<const bf16x8*>(&u);
+}
+
+// V^T operand of one 32x32x16 MFMA: lane = d row (d0 + l16 inside its 16-lane group),
+// slots 0..3 = keys k0 .. k0+3, slots 4..7 = keys k0+8 .. k0+11, read transposed:
+// lane 4e+q of the group addresses key row k0+e (+8), d columns d0 + 4q .. +3.
+__device__ __forceinline__ bf16x8 ld_vt(const Tile& t, int k0, int d0, int l16) {
+  const int e = l16 >> 2, q = l16 & 3;
+  const int dcol = d0 + 4 * q;
+  const int r0 = k0 + e, r1 = k0 + 8 + e;
+  const char* base = reinterpret_cast<const char*>(&t.row[0][0]);
+  const char* p0 = base + r0 * 256 + swz(r0, dcol >> 3) * 16 + (dcol & 7) * 2;
+  const char* p1 = base + r1 * 256 + swz(r1, dcol >> 3) * 16 + (dcol & 7) * 2;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p1));
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
 __device__ __forceinline__ void store4(bf16* p, const float* v) {
@@ -168,7 +183,7 @@ __global__ void __launch_bounds__(NT, 2)
 attn_mfma_kernel(AttnParams p) {
   __shared__ Smem sm;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int wave = uni(tid >> 6), lane = tid & 63, hl = lane >> 5, l32 = lane & 31, l16 = lane & 15;
 
   // ---- work item (XCD-aware order, heaviest frames first) ----
   const int nqt = (p.P + QT - 1) / QT;
@@ -184,24 +199,22 @@ attn_mfma_kernel(AttnParams p) {
   const long long f = p.f0 + fq;
 
   const size_t HD = size_t(p.H) * D;
-  const int row0 = qt * QT + wave * 32;
-  const bool wave_active = row0 < p.P;
-  const int qrow = row0 + l32;
-  const bool row_ok = qrow < p.P;
-  const size_t qbase = ((size_t(b) * p.T + fq) * p.P + qrow) * HD + size_t(h) * D;
+  const int wrow0 = qt * QT + wave * 32 * RB;   // first query row (in the frame) of this wave
+  const bool wave_active = wrow0 < p.P;
+  const size_t fbase = ((size_t(b) * p.T + fq) * p.P) * HD + size_t(h) * D;
 
-  // Q block as the B operand of S^T = K Q^T: lane holds Q[query l32][ks*16 + hl*8 + 0..7]
-  bf16x8 qv[8];
+  // Q blocks as B operands of S^T = K Q^T: lane holds Q[row l32 of block rb][ks*16 + hl*8 + 0..7]
+  bf16x8 qv[RB][8];
   {
     const bf16* q = static_cast<const bf16*>(p.q);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      if (row_ok) {
-        uint4 u = *reinterpret_cast<const uint4*>(q + qbase + ks * 16 + hl * 8);
-        qv[ks] = *reinterpret_cast<bf16x8*>(&u);
-      } else {
-        uint4 z = make_uint4(0, 0, 0, 0);
-        qv[ks] = *reinterpret_cast<bf16x8*>(&z);
+    for (int rb = 0; rb < RB; ++rb) {
+      const int qrow = wrow0 + rb * 32 + l32;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (qrow < p.P) u = *reinterpret_cast<const uint4*>(q + fbase + size_t(qrow) * HD + ks * 16 + hl * 8);
+        qv[rb][ks] = *reinterpret_cast<bf16x8*>(&u);
       }
     }
   }
@@ -209,42 +222,55 @@ attn_mfma_kernel(AttnParams p) {
   const float c = p.scale_log2;
   const int nswa = swa_count(f, p.W);
   const int ndswa = dswa_count(f, p.dil, p.taps);
-  Stage st;
-
   for (int branch = 0; branch < 2; ++branch) {
     const int nframes = branch == 0 ? nswa : ndswa;
     const long long nk = (long long)nframes * p.P;
     const int ntiles = int((nk + KT - 1) / KT);
-    float m = -INFINITY;   // running max of the scaled (log2-domain) scores
-    float lsum = 0.f;      // running sum over this half-wave's keys
-    f32x16 acc[4];
+    float m[RB], lsum[RB];
+    f32x16 acc[RB][4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int rb = 0; rb < RB; ++rb) {
+      m[rb] = -INFINITY;
+      lsum[rb] = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-
-    __syncthreads();   // the previous branch's last tile is no longer read
-    if (ntiles > 0) {
-      load_tile(st, p, b, h, branch, f, nswa, nframes, nk, 0, tid);
-      store_tile(sm, 0, st, tid);
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[rb][db][r] = 0.f;
     }
+
+    KeyStream ks{&p, b, h, branch, nswa, nframes, f};
+    ks.start();
+    __syncthreads();   // the previous branch's last tile is no longer read
+    if (ntiles > 0) issue_tile(sm.K[0], sm.V[0], ks, int(nk < KT ? nk : KT), wave, lane);
     for (int t = 0; t < ntiles; ++t) {
       const int buf = t & 1;
-      __syncthreads();
-      const bool more = t + 1 < ntiles;
-      if (more) load_tile(st, p, b, h, branch, f, nswa, nframes, nk, (long long)(t + 1) * KT, tid);
+      wait_vmem();
+      __syncthreads();   // tile t is in LDS; nobody reads buffer buf^1 any more
+      if (t + 1 < ntiles) {
+        ks.advance();
+        const long long left = nk - (long long)(t + 1) * KT;
+        issue_tile(sm.K[buf ^ 1], sm.V[buf ^ 1], ks, int(left < KT ? left : KT), wave, lane);
+      }
 
       if (wave_active) {
-        // S^T for 64 keys: two 32x32 blocks (keys kb*32 .. +31) x 32 queries
-        f32x16 s[2];
+        const Tile& Kt = sm.K[buf];
+        const Tile& Vt = sm.V[buf];
+        // S^T: for each key block kb (32 keys) and query block rb
+        f32x16 s[RB][2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int ks = 0; ks < 8; ++ks) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.K[buf][kb * 32 + l32][ks * 16 + hl * 8]);
-            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qv[ks], s[kb], 0, 0, 0);
+            for (int r = 0; r < 16; ++r) s[rb][kb][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            const bf16x8 a = ld_chunk(Kt, kb * 32 + l32, 2 * ks + hl);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              s[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qv[rb][ks], s[rb][kb], 0, 0, 0);
           }
         }
         // mask keys past the end (last tile only); value r of block kb is key
@@ -252,38 +278,47 @@ attn_mfma_kernel(AttnParams p) {
         const long long kleft = nk - (long long)t * KT;
         if (kleft < KT) {
 #pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int key = kb * 32 + (r >> 2) * 8 + 4 * hl + (r & 3);
+                if (key >= kleft) s[rb][kb][r] = -INFINITY;
+              }
+        }
+        bf16x8 pv[RB][2][2];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          float mt = -INFINITY;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[rb][kb][r]);
+          mt = fmaxf(mt, __shfl_xor(mt, 32)) * c;
+          // lazy rescale: only when some lane's tile max passes its running max by kLazy
+          const bool raise = mt > m[rb] + kLazy;
+          if (__ballot(raise) != 0) {
+            const float mnew = raise ? fmaxf(m[rb], mt) : m[rb];
+            const float alpha = __builtin_amdgcn_exp2f(m[rb] - mnew);
+            m[rb] = mnew;
+            lsum[rb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) acc[rb][db][r] *= alpha;
+          }
+          const float mm = m[rb];
+#pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int key = kb * 32 + (r >> 2) * 8 + 4 * hl + (r & 3);
-              if (key >= kleft) s[kb][r] = -INFINITY;
+              const float e = __builtin_amdgcn_exp2f(fmaf(s[rb][kb][r], c, -mm));
+              lsum[rb] += e;
+              pv[rb][kb][r >> 3][r & 7] = static_cast<bf16>(e);
             }
         }
-        float mt = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float mnew = fmaxf(m, mt * c);
-        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-        m = mnew;
-        lsum *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-        // P^T in bf16, directly in B-operand layout: MFMA (kb, m2) takes values r = m2*8 + 0..7
-        bf16x8 pv[2][2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -mnew));
-            lsum += e;
-            pv[kb][r >> 3][r & 7] = static_cast<bf16>(e);
-          }
-        // O^T += V^T P^T: A operand lane = d row (db*32 + l32), keys of slot i:
+        // O^T += V^T P^T: A operand lane = d row db*32 + l32, keys of slot i:
         // kb*32 + 16*m2 + 8*(i/4) + 4*hl + i%4
 #pragma unroll
         for (int db = 0; db < 4; ++db)
@@ -291,45 +326,49 @@ attn_mfma_kernel(AttnParams p) {
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int m2 = 0; m2 < 2; ++m2) {
-              const bf16* vrow = &sm.Vt[buf][db * 32 + l32][kb * 32 + 16 * m2 + 4 * hl];
-              const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow);
-              const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 8);
-              const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-              acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pv[kb][m2], acc[db], 0, 0, 0);
+              const bf16x8 a = ld_vt(Vt, kb * 32 + 16 * m2 + 4 * hl, db * 32 + (l32 & 16), l16);
+#pragma unroll
+              for (int rb = 0; rb < RB; ++rb)
+                acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pv[rb][kb][m2], acc[rb][db], 0, 0, 0);
             }
       }
-      if (more) store_tile(sm, buf ^ 1, st, tid);
     }
 
-    // ---- epilogue of this branch: normalise, store, keep for the mix ----
+    // ---- epilogue of this branch: normalise, store; the mix after DSWA ----
     if (wave_active) {
-      const float ltot = lsum + __shfl_xor(lsum, 32);
-      const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
       Tout* out = static_cast<Tout*>(branch == 0 ? p.o_swa : p.o_dswa);
       const Tout* out_swa = static_cast<const Tout*>(p.o_swa);
       const Tout* og = static_cast<const Tout*>(p.o_gdn);
       Tout* om = static_cast<Tout*>(p.o_mix);
       const float w0 = p.mix_w[h * 3 + 0], w1 = p.mix_w[h * 3 + 1], w2 = p.mix_w[h * 3 + 2];
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int rb = 0; rb < RB; ++rb) {
+        const int qrow = wrow0 + rb * 32 + l32;
+        const bool row_ok = qrow < p.P;
+        const float ltot = lsum[rb] + __shfl_xor(lsum[rb], 32);
+        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+        const size_t qbase = fbase + size_t(qrow) * HD;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int dcol = db * 32 + j * 8 + 4 * hl;   // 4 consecutive d values r = 4j .. 4j+3
-          float o4[4];
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o4[e] = stored_value<Tout>(acc[db][4 * j + e] * inv);
-          if (!row_ok) continue;
-          store4(out + qbase + dcol, o4);
-          if (branch == 1) {
-            // the mix reads back this lane's own SWA store and the GDN output
-            float s4[4], g4[4], m4[4];
-            load4(out_swa + qbase + dcol, s4);
-            load4(og + qbase + dcol, g4);
+          for (int j = 0; j < 4; ++j) {
+            const int dcol = db * 32 + j * 8 + 4 * hl;   // 4 consecutive d values r = 4j .. 4j+3
+            float o4[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) m4[e] = w0 * s4[e] + w1 * o4[e] + w2 * g4[e];
-            store4(om + qbase + dcol, m4);
+            for (int e = 0; e < 4; ++e) o4[e] = stored_value<Tout>(acc[rb][db][4 * j + e] * inv);
+            if (!row_ok) continue;
+            store4(out + qbase + dcol, o4);
+            if (branch == 1) {
+              // the mix reads back this lane's own SWA store and the GDN output
+              float s4[4], g4[4], m4[4];
+              load4(out_swa + qbase + dcol, s4);
+              load4(og + qbase + dcol, g4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) m4[e] = w0 * s4[e] + w1 * o4[e] + w2 * g4[e];
+              store4(om + qbase + dcol, m4);
+            }
           }
-        }
+      }
     }
   }
 }

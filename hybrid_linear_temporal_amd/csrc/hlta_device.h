@@ -52,7 +52,7 @@ __device__ __forceinline__ const T* key_frame_ptr(const T* main, const T* ring, 
     return main + ((size_t(b) * p.T * p.P + size_t(g) * p.P) * p.H + h) * D;
   if (g == p.f0)
     return main + (size_t(b) * p.P * p.H + h) * D;
-  const long long slot = g % p.R;
+  const int slot = int(g % p.R);
   return ring + ((size_t(b) * p.R + slot) * p.P * p.H + h) * D;
 }
 
