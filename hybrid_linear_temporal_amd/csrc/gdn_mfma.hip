@@ -26,7 +26,9 @@
 // the reduction (d_k) index of an MFMA may be permuted as long as both operands
 // agree; the A operands are read from LDS in that permuted order. The same holds
 // for U (C layout) as B operand of Aqk U and of the state update, so the chain
-// never moves S or U through LDS.
+// never moves S or U through LDS. Each chunk's operands (-W, q, k, Aqk, the
+// workgroup's U' rows, per-token scales) stream into a second LDS buffer by
+// direct global -> LDS loads while the current chunk computes.
 #include "hlta_device.h"
 #include "hlta_internal.h"
 #include "hlta_launch.h"
@@ -108,7 +110,9 @@ __device__ __forceinline__ void blk_acc(float (*M)[FP], int r0, int c0, const fl
 __global__ void __launch_bounds__(NT, 1)
 gdn_prep_mfma(GdnParams p) {
   __shared__ __attribute__((aligned(16))) PrepSmem sm;
-  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // last chunk first: when the state pass starts, the records it reads first
+  // are the most recently written ones (still in the last-level cache)
+  const int chunk = p.n_chunks - 1 - int(blockIdx.x), h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const long long t0 = (long long)chunk * C;
   const int n = int(p.L - t0 < C ? p.L - t0 : C);
@@ -330,22 +334,82 @@ gdn_prep_mfma(GdnParams p) {
 // kernel 2: the chunk-to-chunk state pass
 // ---------------------------------------------------------------------------
 
-struct ChainSmem {
-  bf16 Wn[C][XP];
-  bf16 Q[C][XP];
-  bf16 K[C][XP];
-  bf16 Aqk[C][CP];
-  bf16 UpT[64][CP];   // this workgroup's 64 value channels
-  float sq[C], sk[C];
-  float gC;
+// One chunk's operands in LDS. 16-byte chunks are XOR-swizzled by row
+// (c ^ (r & 15) for 256-byte rows, c ^ (r & 7) for 128-byte rows) so that
+// column reads of 16 rows hit distinct banks; tiles arrive by direct
+// global -> LDS loads (lane i of a wave instruction lands at byte 16 i).
+struct ChainBuf {
+  uint4 Wn[C][16];    // -W, row per token
+  uint4 Q[C][16];     // raw q, row per token
+  uint4 K[C][16];     // raw k, row per token
+  uint4 Aqk[C][8];    // row per token
+  uint4 UpT[64][8];   // this workgroup's 64 value channels, row per channel
+  float sc[2 * C + 32];  // sq[C], sk[C], gC
 };
+
+__device__ __forceinline__ int sw16(int r, int c) { return c ^ (r & 15); }
+__device__ __forceinline__ int sw8(int r, int c) { return c ^ (r & 7); }
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
+                                   (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+// 4 consecutive bf16 at (row, col) of a swizzled tile with `cpr` chunks per row
+template <int CPR>
+__device__ __forceinline__ bf16x4 ld4s(const uint4 (*t)[CPR], int row, int col) {
+  const int c = col >> 3;
+  const int pos = CPR == 16 ? sw16(row, c) : sw8(row, c);
+  const char* p = reinterpret_cast<const char*>(&t[row][pos]) + (col & 7) * 2;
+  return *reinterpret_cast<const bf16x4*>(p);
+}
+template <int CPR>
+__device__ __forceinline__ bf16x4 ld4s_tr(const uint4 (*t)[CPR], int row, int col) {
+  const int c = col >> 3;
+  const int pos = CPR == 16 ? sw16(row, c) : sw8(row, c);
+  const char* p = reinterpret_cast<const char*>(&t[row][pos]) + (col & 7) * 2;
+  return ld_tr(reinterpret_cast<const bf16*>(p));
+}
+
+// Issue the direct loads of one chunk into `buf` (all four waves take part).
+__device__ __forceinline__ void issue_chunk(ChainBuf& buf, const GdnParams& p, int b, int h, int vhalf, int chunk,
+                                            int wave, int lane) {
+  const unsigned char* rec = p.ws + (size_t(b * p.H + h) * p.n_chunks + chunk) * p.rec_bytes;
+  const long long t0 = (long long)chunk * C;
+  const int n = int(p.L - t0 < C ? p.L - t0 : C);
+  const size_t HD = size_t(p.H) * D;
+  const bf16* qb = static_cast<const bf16*>(p.q) + (size_t(b) * p.L + t0) * HD + size_t(h) * D;
+  const bf16* kb = static_cast<const bf16*>(p.k) + (size_t(b) * p.L + t0) * HD + size_t(h) * D;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r0 = 16 * wave + 4 * j;
+    const int row = r0 + (lane >> 4);
+    const int c = sw16(row, lane & 15);
+    const int rr = row < n ? row : n - 1;   // rows past the end re-read the last token (weights are zero there)
+    dma16(rec + R::WN + size_t(row) * 256 + c * 16, &buf.Wn[r0][0]);
+    dma16(qb + size_t(rr) * HD + c * 8, &buf.Q[r0][0]);
+    dma16(kb + size_t(rr) * HD + c * 8, &buf.K[r0][0]);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r0 = 16 * wave + 8 * j;
+    const int row = r0 + (lane >> 3);
+    const int c = sw8(row, lane & 7);
+    dma16(rec + R::AQK + size_t(row) * 128 + c * 16, &buf.Aqk[r0][0]);
+    dma16(rec + R::UPT + size_t(64 * vhalf + row) * 128 + c * 16, &buf.UpT[r0][0]);
+  }
+  if (wave == 0 && lane < 33) dma16(rec + R::SQ + 16 * lane, &buf.sc[0]);
+}
 
 template <typename Tout>
 __global__ void __launch_bounds__(NT, 1)
 gdn_chain_mfma(GdnParams p) {
-  __shared__ __attribute__((aligned(16))) ChainSmem sm;
+  __shared__ __attribute__((aligned(16))) ChainBuf sm[2];
   const int vhalf = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int v0 = 64 * vhalf + 16 * wave;   // this wave's value channels v0 .. v0+15
   const size_t HD = size_t(p.H) * D;
   const size_t sbase = (size_t(b) * p.H + h) * D * D;
@@ -363,36 +427,18 @@ gdn_chain_mfma(GdnParams p) {
     }
   }
 
+  issue_chunk(sm[0], p, b, h, vhalf, 0, wave, lane);
   for (int chunk = 0; chunk < p.n_chunks; ++chunk) {
+    const int cur = chunk & 1;
+    wait_vmem();
+    __syncthreads();   // chunk `chunk` is in sm[cur]; nobody reads sm[cur ^ 1] any more
+    if (chunk + 1 < p.n_chunks) issue_chunk(sm[cur ^ 1], p, b, h, vhalf, chunk + 1, wave, lane);
+    const ChainBuf& B = sm[cur];
     const long long t0 = (long long)chunk * C;
     const int n = int(p.L - t0 < C ? p.L - t0 : C);
-    const unsigned char* rec = p.ws + (size_t(b * p.H + h) * p.n_chunks + chunk) * p.rec_bytes;
-    const size_t base = (size_t(b) * p.L + t0) * HD + size_t(h) * D;
-    __syncthreads();   // previous chunk's LDS reads are done
-    load_rows(sm.Q, static_cast<const bf16*>(p.q) + base, HD, n, tid);
-    load_rows(sm.K, static_cast<const bf16*>(p.k) + base, HD, n, tid);
-    {
-      const bf16* wn = reinterpret_cast<const bf16*>(rec + R::WN);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = (tid >> 4) + 16 * i, c = tid & 15;
-        *reinterpret_cast<uint4*>(&sm.Wn[row][c * 8]) = *reinterpret_cast<const uint4*>(wn + row * D + c * 8);
-      }
-      const bf16* aqk = reinterpret_cast<const bf16*>(rec + R::AQK);
-      const bf16* upt = reinterpret_cast<const bf16*>(rec + R::UPT) + size_t(64 * vhalf) * C;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int e = tid + NT * i, row = e >> 3, c = e & 7;
-        *reinterpret_cast<uint4*>(&sm.Aqk[row][c * 8]) = *reinterpret_cast<const uint4*>(aqk + row * C + c * 8);
-        *reinterpret_cast<uint4*>(&sm.UpT[row][c * 8]) = *reinterpret_cast<const uint4*>(upt + row * C + c * 8);
-      }
-      if (tid < C) {
-        sm.sq[tid] = reinterpret_cast<const float*>(rec + R::SQ)[tid];
-        sm.sk[tid] = reinterpret_cast<const float*>(rec + R::SK)[tid];
-      }
-      if (tid == 0) sm.gC = *reinterpret_cast<const float*>(rec + R::GC);
-    }
-    __syncthreads();
+    const float* sq = &B.sc[0];
+    const float* sk = &B.sc[C];
+    const float gc = B.sc[2 * C];
 
     // bf16 copy of S^T as B operand: K-step ks takes blocks 2ks, 2ks+1 (d_k = 32ks + 16(i/4) + 4g + i%4)
     bf16x8 sb[4];
@@ -408,13 +454,14 @@ gdn_chain_mfma(GdnParams p) {
     f32x4 u[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-      const bf16x4 up = ld4(&sm.UpT[16 * wave + l16][16 * tb + 4 * g]);
+      const bf16x4 up = ld4s<8>(B.UpT, 16 * wave + l16, 16 * tb + 4 * g);
       u[tb] = f32x4{static_cast<float>(up[0]), static_cast<float>(up[1]), static_cast<float>(up[2]),
                     static_cast<float>(up[3])};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16* wr = &sm.Wn[16 * tb + l16][32 * ks + 4 * g];
-        u[tb] = mfma16(join(ld4(wr), ld4(wr + 16)), sb[ks], u[tb]);
+        const int row = 16 * tb + l16;
+        u[tb] = mfma16(join(ld4s<16>(B.Wn, row, 32 * ks + 4 * g), ld4s<16>(B.Wn, row, 32 * ks + 16 + 4 * g)),
+                       sb[ks], u[tb]);
       }
     }
     // (2) O = diag(sq) (Q S^T) + Aqk U
@@ -426,24 +473,21 @@ gdn_chain_mfma(GdnParams p) {
         const int ta = 32 * js + 4 * g + e, tb2 = 32 * js + 16 + 4 * g + e;
         ub[js][e] = static_cast<bf16>(u[2 * js][e]);
         ub[js][4 + e] = static_cast<bf16>(u[2 * js + 1][e]);
-        usb[js][e] = static_cast<bf16>(u[2 * js][e] * sm.sk[ta]);
-        usb[js][4 + e] = static_cast<bf16>(u[2 * js + 1][e] * sm.sk[tb2]);
+        usb[js][e] = static_cast<bf16>(u[2 * js][e] * sk[ta]);
+        usb[js][4 + e] = static_cast<bf16>(u[2 * js + 1][e] * sk[tb2]);
       }
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
+      const int row = 16 * tb + l16;
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16* qr = &sm.Q[16 * tb + l16][32 * ks + 4 * g];
-        x = mfma16(join(ld4(qr), ld4(qr + 16)), sb[ks], x);
-      }
+      for (int ks = 0; ks < 4; ++ks)
+        x = mfma16(join(ld4s<16>(B.Q, row, 32 * ks + 4 * g), ld4s<16>(B.Q, row, 32 * ks + 16 + 4 * g)), sb[ks], x);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] *= sm.sq[16 * tb + 4 * g + e];
+      for (int e = 0; e < 4; ++e) x[e] *= sq[16 * tb + 4 * g + e];
 #pragma unroll
-      for (int js = 0; js < 2; ++js) {
-        const bf16* ar = &sm.Aqk[16 * tb + l16][32 * js + 4 * g];
-        x = mfma16(join(ld4(ar), ld4(ar + 16)), ub[js], x);
-      }
+      for (int js = 0; js < 2; ++js)
+        x = mfma16(join(ld4s<8>(B.Aqk, row, 32 * js + 4 * g), ld4s<8>(B.Aqk, row, 32 * js + 16 + 4 * g)), ub[js], x);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int tok = 16 * tb + 4 * g + e;
@@ -451,15 +495,15 @@ gdn_chain_mfma(GdnParams p) {
       }
     }
     // (3) S^T <- gamma_C S^T + K^T diag(sk) U, A = K^T read transposed from LDS
-    const float gc = sm.gC;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) st[mb][e] *= gc;
 #pragma unroll
       for (int js = 0; js < 2; ++js) {
-        const bf16x4 lo = ld_tr(&sm.K[32 * js + 4 * g + (l16 >> 2)][16 * mb + 4 * (l16 & 3)]);
-        const bf16x4 hi = ld_tr(&sm.K[32 * js + 16 + 4 * g + (l16 >> 2)][16 * mb + 4 * (l16 & 3)]);
+        const int col = 16 * mb + 4 * (l16 & 3);
+        const bf16x4 lo = ld4s_tr<16>(B.K, 32 * js + 4 * g + (l16 >> 2), col);
+        const bf16x4 hi = ld4s_tr<16>(B.K, 32 * js + 16 + 4 * g + (l16 >> 2), col);
         st[mb] = mfma16(join(lo, hi), usb[js], st[mb]);
       }
     }
