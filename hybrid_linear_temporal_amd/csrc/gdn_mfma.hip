@@ -19,8 +19,10 @@
 // blocks level by level); W^T and U' on MFMA with the raw K, V read transposed
 // from LDS (ds_read_b64_tr_b16). Writes one record per chunk.
 //
-// Kernel 2, gdn_chain_mfma: one workgroup per (64 value channels, head, batch
-// row), four waves of 16 value channels each, chunks in order. Each wave keeps
+// Kernel 2, gdn_chain_mfma: one single-wave workgroup per (16 value channels,
+// head, batch row), chunks in order; the 8 workgroups of a head sit on one XCD
+// and share its L2 (one wave per CU keeps the per-CU LDS traffic to one copy of
+// the chunk's shared operands). Each wave keeps
 // its slice of S^T (128 x 16, fp32) in MFMA accumulator layout for the whole
 // sequence. Its bf16 copy is the B operand of W S^T and Q S^T directly, because
 // the reduction (d_k) index of an MFMA may be permuted as long as both operands
@@ -334,21 +336,30 @@ gdn_prep_mfma(GdnParams p) {
 // kernel 2: the chunk-to-chunk state pass
 // ---------------------------------------------------------------------------
 
-// One chunk's operands in LDS. 16-byte chunks are XOR-swizzled by row
-// (c ^ (r & 15) for 256-byte rows, c ^ (r & 7) for 128-byte rows) so that
-// column reads of 16 rows hit distinct banks; tiles arrive by direct
-// global -> LDS loads (lane i of a wave instruction lands at byte 16 i).
+// One chunk's operands in LDS, rows padded so that 16 lanes reading one
+// column of 16 rows hit distinct banks: 272-byte rows for -W and q, 288-byte
+// rows for k (read transposed), 144-byte rows for the 64-wide tiles. Tiles
+// arrive by direct global -> LDS loads: a wave instruction writes 1 KB
+// contiguously (lane i at byte 16 i), so padded tiles are filled as runs of
+// 64 chunk slots, each lane loading the chunk its slot holds (pad slots load
+// a harmless in-row chunk).
+constexpr int PW = 17;   // chunk slots per row: -W and q
+constexpr int PK = 18;   // k
+constexpr int PS = 9;    // Aqk, U'^T rows
+constexpr int NV = 16;   // value channels per workgroup (one wave)
+constexpr int kChainXcds = 8;
 struct ChainBuf {
-  uint4 Wn[C][16];    // -W, row per token
-  uint4 Q[C][16];     // raw q, row per token
-  uint4 K[C][16];     // raw k, row per token
-  uint4 Aqk[C][8];    // row per token
-  uint4 UpT[64][8];   // this workgroup's 64 value channels, row per channel
+  uint4 Wn[C * PW];
+  uint4 Q[C * PW];
+  uint4 K[C * PK];
+  uint4 Aqk[C * PS];
+  uint4 UpT[NV * PS];
   float sc[2 * C + 32];  // sq[C], sk[C], gC
 };
-
-__device__ __forceinline__ int sw16(int r, int c) { return c ^ (r & 15); }
-__device__ __forceinline__ int sw8(int r, int c) { return c ^ (r & 7); }
+struct ChainSmem {
+  ChainBuf buf[2];
+  bf16 ostage[C][NV + 8];
+};
 
 __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
@@ -357,62 +368,88 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
-// 4 consecutive bf16 at (row, col) of a swizzled tile with `cpr` chunks per row
-template <int CPR>
-__device__ __forceinline__ bf16x4 ld4s(const uint4 (*t)[CPR], int row, int col) {
-  const int c = col >> 3;
-  const int pos = CPR == 16 ? sw16(row, c) : sw8(row, c);
-  const char* p = reinterpret_cast<const char*>(&t[row][pos]) + (col & 7) * 2;
-  return *reinterpret_cast<const bf16x4*>(p);
-}
-template <int CPR>
-__device__ __forceinline__ bf16x4 ld4s_tr(const uint4 (*t)[CPR], int row, int col) {
-  const int c = col >> 3;
-  const int pos = CPR == 16 ? sw16(row, c) : sw8(row, c);
-  const char* p = reinterpret_cast<const char*>(&t[row][pos]) + (col & 7) * 2;
-  return ld_tr(reinterpret_cast<const bf16*>(p));
+// Source offset of chunk slot P of a padded tile (row P / pitch, chunk P % pitch).
+__device__ __forceinline__ unsigned slot_offset(int P, int pitch_chunks, int src_chunks, int src_row_bytes,
+                                                int clamp_row) {
+  int row = P / pitch_chunks, ch = P - row * pitch_chunks;
+  if (ch >= src_chunks) ch = src_chunks - 1;
+  if (row > clamp_row) row = clamp_row;
+  return unsigned(row) * unsigned(src_row_bytes) + unsigned(ch) * 16u;
 }
 
-// Issue the direct loads of one chunk into `buf` (all four waves take part).
-__device__ __forceinline__ void issue_chunk(ChainBuf& buf, const GdnParams& p, int b, int h, int vhalf, int chunk,
-                                            int wave, int lane) {
-  const unsigned char* rec = p.ws + (size_t(b * p.H + h) * p.n_chunks + chunk) * p.rec_bytes;
-  const long long t0 = (long long)chunk * C;
-  const int n = int(p.L - t0 < C ? p.L - t0 : C);
-  const size_t HD = size_t(p.H) * D;
-  const bf16* qb = static_cast<const bf16*>(p.q) + (size_t(b) * p.L + t0) * HD + size_t(h) * D;
-  const bf16* kb = static_cast<const bf16*>(p.k) + (size_t(b) * p.L + t0) * HD + size_t(h) * D;
+// 4 consecutive bf16 at (row, col) of a padded tile
+template <int PC>
+__device__ __forceinline__ bf16x4 ld4p(const uint4* t, int row, int col) {
+  return *reinterpret_cast<const bf16x4*>(reinterpret_cast<const char*>(t) + row * (PC * 16) + col * 2);
+}
+template <int PC>
+__device__ __forceinline__ bf16x4 ld4p_tr(const uint4* t, int row, int col) {
+  return ld_tr(reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(t) + row * (PC * 16) + col * 2));
+}
+
+// Lane offsets of the direct loads of one chunk (the same for every chunk;
+// q and k rows past the end of the last chunk are clamped separately).
+// Offsets are kept in (row * 256 + chunk * 16) form; q and k rows are tokens
+// of the input tensors, so their offsets are rescaled to the token stride (and
+// clamped to the last token in the ragged last chunk).
+struct DmaPlan {
+  unsigned w[PW], k[PK], aqk[PS], upt[3];
+};
+
+__device__ __forceinline__ void make_plan(DmaPlan& pl, int lane) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r0 = 16 * wave + 4 * j;
-    const int row = r0 + (lane >> 4);
-    const int c = sw16(row, lane & 15);
-    const int rr = row < n ? row : n - 1;   // rows past the end re-read the last token (weights are zero there)
-    dma16(rec + R::WN + size_t(row) * 256 + c * 16, &buf.Wn[r0][0]);
-    dma16(qb + size_t(rr) * HD + c * 8, &buf.Q[r0][0]);
-    dma16(kb + size_t(rr) * HD + c * 8, &buf.K[r0][0]);
+  for (int j = 0; j < PW; ++j) pl.w[j] = slot_offset(64 * j + lane, PW, 16, 256, C - 1);
+#pragma unroll
+  for (int j = 0; j < PK; ++j) pl.k[j] = slot_offset(64 * j + lane, PK, 16, 256, C - 1);
+#pragma unroll
+  for (int j = 0; j < PS; ++j) pl.aqk[j] = slot_offset(64 * j + lane, PS, 8, 128, C - 1);
+#pragma unroll
+  for (int j = 0; j < 3; ++j) pl.upt[j] = slot_offset(64 * j + lane, PS, 8, 128, NV - 1);
+}
+
+__device__ __forceinline__ unsigned tok_offset(unsigned off256, int last_row, unsigned tok_bytes) {
+  unsigned row = off256 >> 8;
+  if (row > unsigned(last_row)) row = unsigned(last_row);
+  return row * tok_bytes + (off256 & 255u);
+}
+
+__device__ __forceinline__ void issue_chunk(ChainBuf& buf, const DmaPlan& pl, const unsigned char* rec,
+                                            const unsigned char* qb, const unsigned char* kb, int vblk, int lane,
+                                            int n, int src_tok_bytes) {
+  const unsigned char* wn = rec + R::WN;
+  const unsigned char* aqk = rec + R::AQK;
+  const unsigned char* upt = rec + R::UPT + size_t(NV * vblk) * 128;
+  const unsigned tb = unsigned(src_tok_bytes);
+#pragma unroll
+  for (int j = 0; j < PW; ++j) {
+    dma16(wn + pl.w[j], &buf.Wn[64 * j]);
+    dma16(qb + tok_offset(pl.w[j], n - 1, tb), &buf.Q[64 * j]);
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r0 = 16 * wave + 8 * j;
-    const int row = r0 + (lane >> 3);
-    const int c = sw8(row, lane & 7);
-    dma16(rec + R::AQK + size_t(row) * 128 + c * 16, &buf.Aqk[r0][0]);
-    dma16(rec + R::UPT + size_t(64 * vhalf + row) * 128 + c * 16, &buf.UpT[r0][0]);
-  }
-  if (wave == 0 && lane < 33) dma16(rec + R::SQ + 16 * lane, &buf.sc[0]);
+  for (int j = 0; j < PK; ++j) dma16(kb + tok_offset(pl.k[j], n - 1, tb), &buf.K[64 * j]);
+#pragma unroll
+  for (int j = 0; j < PS; ++j) dma16(aqk + pl.aqk[j], &buf.Aqk[64 * j]);
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+    if (64 * j + lane < NV * PS) dma16(upt + pl.upt[j], &buf.UpT[64 * j]);
+  if (lane < 33) dma16(rec + R::SQ + 16 * lane, &buf.sc[0]);
 }
 
 template <typename Tout>
-__global__ void __launch_bounds__(NT, 1)
+__global__ void __launch_bounds__(64, 1)
 gdn_chain_mfma(GdnParams p) {
-  __shared__ __attribute__((aligned(16))) ChainBuf sm[2];
-  const int vhalf = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int v0 = 64 * vhalf + 16 * wave;   // this wave's value channels v0 .. v0+15
+  __shared__ __attribute__((aligned(16))) ChainSmem sm;
+  // XCD-aware: the 8 workgroups of a head get blockIdx with the same value mod 8
+  const int xcd = blockIdx.x % kChainXcds, slot = blockIdx.x / kChainXcds;
+  const int vblk = slot % (D / NV);
+  const int bh = (slot / (D / NV)) * kChainXcds + xcd;
+  if (bh >= p.B * p.H) return;
+  const int b = bh / p.H, h = bh % p.H;
+  const int lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
+  const int v0 = NV * vblk;   // this wave's value channels v0 .. v0+15
   const size_t HD = size_t(p.H) * D;
   const size_t sbase = (size_t(b) * p.H + h) * D * D;
+  const int tok_bytes = int(HD * sizeof(bf16));
   Tout* o = static_cast<Tout*>(p.o);
 
   // S^T slice in C layout: block mb holds d_k rows 16mb + 4g + e, column d_v = v0 + l16
@@ -427,18 +464,57 @@ gdn_chain_mfma(GdnParams p) {
     }
   }
 
-  issue_chunk(sm[0], p, b, h, vhalf, 0, wave, lane);
+  DmaPlan plan;
+  make_plan(plan, lane);
+  auto issue = [&](int chunk, ChainBuf& dst) {
+    const unsigned char* rec = p.ws + (size_t(b * p.H + h) * p.n_chunks + chunk) * p.rec_bytes;
+    const long long t0 = (long long)chunk * C;
+    const size_t tb = ((size_t(b) * p.L + t0) * HD + size_t(h) * D) * sizeof(bf16);
+    const int n = int(p.L - t0 < C ? p.L - t0 : C);
+    issue_chunk(dst, plan, rec, static_cast<const unsigned char*>(p.q) + tb,
+                static_cast<const unsigned char*>(p.k) + tb, vblk, lane, n, tok_bytes);
+  };
+
+  issue(0, sm.buf[0]);
   for (int chunk = 0; chunk < p.n_chunks; ++chunk) {
     const int cur = chunk & 1;
-    wait_vmem();
-    __syncthreads();   // chunk `chunk` is in sm[cur]; nobody reads sm[cur ^ 1] any more
-    if (chunk + 1 < p.n_chunks) issue_chunk(sm[cur ^ 1], p, b, h, vhalf, chunk + 1, wave, lane);
-    const ChainBuf& B = sm[cur];
+    wait_vmem();   // this chunk's operands have landed in buf[cur]
+    __builtin_amdgcn_s_barrier();   // single-wave workgroup: orders the LDS writes before the reads below
+    const ChainBuf& B = sm.buf[cur];
     const long long t0 = (long long)chunk * C;
     const int n = int(p.L - t0 < C ? p.L - t0 : C);
-    const float* sq = &B.sc[0];
-    const float* sk = &B.sc[C];
+
+    // per-token scales of this lane's rows: tokens 16tb + 4g + e
+    f32x4 sqv[4], skv[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      sqv[tb] = *reinterpret_cast<const f32x4*>(&B.sc[16 * tb + 4 * g]);
+      skv[tb] = *reinterpret_cast<const f32x4*>(&B.sc[C + 16 * tb + 4 * g]);
+    }
     const float gc = B.sc[2 * C];
+
+    // LDS operands are read in two batches into registers so the reads
+    // pipeline: first those of the state path (-W, k, U'), then (while those
+    // MFMAs run) those of the output (q, Aqk).
+    bf16x8 aw[4][4], ak[8][2];
+    bf16x4 upv[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const int row = 16 * tb + l16;
+      upv[tb] = ld4p<PS>(B.UpT, l16, 16 * tb + 4 * g);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        aw[tb][ks] = join(ld4p<PW>(B.Wn, row, 32 * ks + 4 * g), ld4p<PW>(B.Wn, row, 32 * ks + 16 + 4 * g));
+    }
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int js = 0; js < 2; ++js) {
+        const int col = 16 * mb + 4 * (l16 & 3);
+        ak[mb][js] = join(ld4p_tr<PK>(B.K, 32 * js + 4 * g + (l16 >> 2), col),
+                          ld4p_tr<PK>(B.K, 32 * js + 16 + 4 * g + (l16 >> 2), col));
+      }
+    __builtin_amdgcn_sched_barrier(0);
 
     // bf16 copy of S^T as B operand: K-step ks takes blocks 2ks, 2ks+1 (d_k = 32ks + 16(i/4) + 4g + i%4)
     bf16x8 sb[4];
@@ -454,57 +530,73 @@ gdn_chain_mfma(GdnParams p) {
     f32x4 u[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-      const bf16x4 up = ld4s<8>(B.UpT, 16 * wave + l16, 16 * tb + 4 * g);
-      u[tb] = f32x4{static_cast<float>(up[0]), static_cast<float>(up[1]), static_cast<float>(up[2]),
-                    static_cast<float>(up[3])};
+      u[tb] = f32x4{static_cast<float>(upv[tb][0]), static_cast<float>(upv[tb][1]), static_cast<float>(upv[tb][2]),
+                    static_cast<float>(upv[tb][3])};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int row = 16 * tb + l16;
-        u[tb] = mfma16(join(ld4s<16>(B.Wn, row, 32 * ks + 4 * g), ld4s<16>(B.Wn, row, 32 * ks + 16 + 4 * g)),
-                       sb[ks], u[tb]);
-      }
+      for (int ks = 0; ks < 4; ++ks) u[tb] = mfma16(aw[tb][ks], sb[ks], u[tb]);
     }
-    // (2) O = diag(sq) (Q S^T) + Aqk U
+    bf16x8 aq[4][4], aa[4][2];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const int row = 16 * tb + l16;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        aq[tb][ks] = join(ld4p<PW>(B.Q, row, 32 * ks + 4 * g), ld4p<PW>(B.Q, row, 32 * ks + 16 + 4 * g));
+#pragma unroll
+      for (int js = 0; js < 2; ++js)
+        aa[tb][js] = join(ld4p<PS>(B.Aqk, row, 32 * js + 4 * g), ld4p<PS>(B.Aqk, row, 32 * js + 16 + 4 * g));
+    }
+    // the next chunk's operands stream into the other buffer while this
+    // chunk's MFMAs run (after its own LDS reads, so they do not contend)
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this chunk's LDS operands are in registers
+    __builtin_amdgcn_sched_barrier(0);
+    if (chunk + 1 < p.n_chunks) issue(chunk + 1, sm.buf[cur ^ 1]);
+    __builtin_amdgcn_sched_barrier(0);
     bf16x8 ub[2], usb[2];
 #pragma unroll
     for (int js = 0; js < 2; ++js)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int ta = 32 * js + 4 * g + e, tb2 = 32 * js + 16 + 4 * g + e;
         ub[js][e] = static_cast<bf16>(u[2 * js][e]);
         ub[js][4 + e] = static_cast<bf16>(u[2 * js + 1][e]);
-        usb[js][e] = static_cast<bf16>(u[2 * js][e] * sk[ta]);
-        usb[js][4 + e] = static_cast<bf16>(u[2 * js + 1][e] * sk[tb2]);
+        usb[js][e] = static_cast<bf16>(u[2 * js][e] * skv[2 * js][e]);
+        usb[js][4 + e] = static_cast<bf16>(u[2 * js + 1][e] * skv[2 * js + 1][e]);
       }
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const int row = 16 * tb + l16;
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        x = mfma16(join(ld4s<16>(B.Q, row, 32 * ks + 4 * g), ld4s<16>(B.Q, row, 32 * ks + 16 + 4 * g)), sb[ks], x);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] *= sq[16 * tb + 4 * g + e];
-#pragma unroll
-      for (int js = 0; js < 2; ++js)
-        x = mfma16(join(ld4s<8>(B.Aqk, row, 32 * js + 4 * g), ld4s<8>(B.Aqk, row, 32 * js + 16 + 4 * g)), ub[js], x);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tok = 16 * tb + 4 * g + e;
-        if (tok < n) o[(size_t(b) * p.L + t0 + tok) * HD + size_t(h) * D + v0 + l16] = from_f32<Tout>(x[e]);
-      }
-    }
-    // (3) S^T <- gamma_C S^T + K^T diag(sk) U, A = K^T read transposed from LDS
+    // (3) S^T <- gamma_C S^T + K^T diag(sk) U (the next chunk waits on it)
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) st[mb][e] *= gc;
 #pragma unroll
-      for (int js = 0; js < 2; ++js) {
-        const int col = 16 * mb + 4 * (l16 & 3);
-        const bf16x4 lo = ld4s_tr<16>(B.K, 32 * js + 4 * g + (l16 >> 2), col);
-        const bf16x4 hi = ld4s_tr<16>(B.K, 32 * js + 16 + 4 * g + (l16 >> 2), col);
-        st[mb] = mfma16(join(lo, hi), usb[js], st[mb]);
+      for (int js = 0; js < 2; ++js) st[mb] = mfma16(ak[mb][js], usb[js], st[mb]);
+    }
+    // (2) O = diag(sq) (Q S^T) + Aqk U, staged in LDS for 16-byte stores
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) x = mfma16(aq[tb][ks], sb[ks], x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] *= sqv[tb][e];
+#pragma unroll
+      for (int js = 0; js < 2; ++js) x = mfma16(aa[tb][js], ub[js], x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.ostage[16 * tb + 4 * g + e][l16] = static_cast<bf16>(x[e]);
+    }
+    // the 64 tokens x 16 channels back from LDS (one wave, in order): 2 x 16 B per token
+    if (lane < n) {
+      const bf16x8 lo = *reinterpret_cast<const bf16x8*>(&sm.ostage[lane][0]);
+      const bf16x8 hi = *reinterpret_cast<const bf16x8*>(&sm.ostage[lane][8]);
+      Tout* dst = o + (size_t(b) * p.L + t0 + lane) * HD + size_t(h) * D + v0;
+      if constexpr (sizeof(Tout) == 2) {
+        *reinterpret_cast<bf16x8*>(dst) = lo;
+        *reinterpret_cast<bf16x8*>(dst + 8) = hi;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          dst[q] = static_cast<float>(lo[q]);
+          dst[8 + q] = static_cast<float>(hi[q]);
+        }
       }
     }
   }
@@ -523,10 +615,12 @@ hipError_t launch_gdn_mfma(const GdnParams& p, int out_dt, hipStream_t st) {
   hipLaunchKernelGGL(gdn_prep_mfma, dim3(p.n_chunks, p.H, p.B), dim3(NT), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const int heads_per_xcd = (p.B * p.H + kChainXcds - 1) / kChainXcds;
+  const dim3 grid(unsigned(kChainXcds * heads_per_xcd * (D / NV)));
   if (out_dt == HLTA_BF16)
-    hipLaunchKernelGGL((gdn_chain_mfma<bf16>), dim3(2, p.H, p.B), dim3(NT), 0, st, p);
+    hipLaunchKernelGGL((gdn_chain_mfma<bf16>), grid, dim3(64), 0, st, p);
   else
-    hipLaunchKernelGGL((gdn_chain_mfma<float>), dim3(2, p.H, p.B), dim3(NT), 0, st, p);
+    hipLaunchKernelGGL((gdn_chain_mfma<float>), grid, dim3(64), 0, st, p);
   return hipGetLastError();
 }
 
