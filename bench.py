@@ -106,6 +106,67 @@ def cpu_baseline(wl, budget_s=12.0):
                       f"host CPUs available: {len(os.sched_getaffinity(0))}"}
 
 
+def torch_recipe(shape, dtype, gen, device="cuda"):
+    """q, k, v, a, b drawn on the GPU with the same recipe as the numpy
+    generator (for timing-only runs: L2-normalised q, k; v ~ N(0,1);
+    a ~ U[0.9, 0.999]; b = sigmoid(N(0,1)))."""
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    B, L, Hh, d = shape
+    q = torch.nn.functional.normalize(torch.randn(shape, generator=gen, device=device), dim=-1).to(tdt)
+    k = torch.nn.functional.normalize(torch.randn(shape, generator=gen, device=device), dim=-1).to(tdt)
+    v = torch.randn(shape, generator=gen, device=device).to(tdt)
+    a = torch.rand((B, L, Hh), generator=gen, device=device) * 0.099 + 0.9
+    b = torch.sigmoid(torch.randn((B, L, Hh), generator=gen, device=device))
+    return q, k, v, a, b
+
+
+def stream_leg(steps, warmup=4, distinct=4):
+    """Streaming frame steps on the 8-rollout 480P workload: 16-frame prefix
+    through hlta_fwd, then `steps` timed hlta_step_frame calls (inputs cycle
+    over `distinct` pre-drawn frames). Returns a dict for the JSON line."""
+    import torch
+    from hybrid_linear_temporal_amd import hlta as H
+    from hybrid_linear_temporal_amd import inputs as I
+
+    wl = I.STREAM_P480
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.seed)
+    P, R, prefix = wl.P, wl.ring_frames, wl.prefix_frames
+    w = torch.from_numpy(I.mix_weights(wl.seed, wl.H)).cuda()
+    q, k, v, a, b = torch_recipe((wl.B, prefix * P, wl.H, wl.d), wl.dtype, gen)
+    cfg_pre = H.make_config(wl, T=prefix)
+    S_pre = torch.empty((wl.B, wl.H, wl.d, wl.d), dtype=torch.float32, device="cuda")
+    H.hlta_fwd(cfg_pre, q, k, v, a, b, w, S_out=S_pre)
+    cfg = H.make_config(wl, T=1)
+    st = H.Stream(cfg, R)
+    H.hlta_stream_load_prefix(st, k, v, prefix, S_pre)
+    del q, k, v, a, b
+    frames = [torch_recipe((wl.B, P, wl.H, wl.d), wl.dtype, gen) for _ in range(distinct)]
+    out = H.alloc_outputs(cfg, P)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        fq, fk, fv, fa, fb = frames[i % distinct]
+        H.hlta_step_frame(st, fq, fk, fv, fa, fb, w, out=out, stream=stream)
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record(stream)
+    for i in range(steps):
+        fq, fk, fv, fa, fb = frames[i % distinct]
+        H.hlta_step_frame(st, fq, fk, fv, fa, fb, w, out=out, stream=stream)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    total = sum(per_step)
+    pairs = (wl.swa_frames + wl.dswa_taps) * P * P * wl.B * wl.H   # every tap is valid after the prefix
+    return {"workload": wl.name, "steps": steps, "tokens_per_step": wl.B * P,
+            "tokens_per_s": wl.B * P * steps / (total * 1e-3), "ms_per_step": total / steps,
+            "ms_per_step_first8": sum(per_step[:8]) / min(8, steps),
+            "ms_per_step_last8": sum(per_step[-8:]) / min(8, steps),
+            "attn_tflops_per_step": 4 * wl.d * pairs / 1e12,
+            "inputs": "torch-seeded GPU draws, same recipe; 4 distinct frames cycled"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,6 +175,7 @@ def main():
     ap.add_argument("--workload", default="p480_T31_bf16")
     ap.add_argument("--impl", type=int, default=0, help="0 auto, 1 generic, 2 mfma")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stream-steps", type=int, default=64, help="streaming frame steps to time (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -187,6 +249,11 @@ def main():
                          "bytes_per_token_head": per_th, "avg_ms": gdn_ms},
         "device": torch.cuda.get_device_name(0),
     }
+    if args.stream_steps > 0:
+        del dev, out, ws
+        torch.cuda.empty_cache()
+        print(f"# streaming leg, {args.stream_steps} frame steps", file=sys.stderr, flush=True)
+        res["stream"] = stream_leg(args.stream_steps)
     if not args.no_cpu_baseline:
         print("# cpu baseline (float64 oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl)

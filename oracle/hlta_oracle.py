@@ -71,21 +71,27 @@ def frame_softmax_attention(q, k, v, T, P, frames_of, scale=None):
     traffic, not the set of pairs or the result). Rows with no key frame are 0.
     """
     q = np.asarray(q, np.float64)
-    k = np.asarray(k, np.float64)
-    v = np.asarray(v, np.float64)
-    d = q.shape[1]
-    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
-    out = np.zeros((T * P, v.shape[1]))
+    out = np.zeros((T * P, np.shape(v)[1]))
     for f in range(T):
-        frames = frames_of(f)
-        if not frames:
-            continue
-        idx = np.concatenate([np.arange(g * P, (g + 1) * P) for g in frames])
-        z = scale * (q[f * P:(f + 1) * P] @ k[idx].T)
-        z -= z.max(axis=1, keepdims=True)
-        e = np.exp(z)
-        out[f * P:(f + 1) * P] = (e @ v[idx]) / e.sum(axis=1, keepdims=True)
+        out[f * P:(f + 1) * P] = attend_rows(q[f * P:(f + 1) * P], k, v, P, frames_of(f), scale)
     return out
+
+
+def attend_rows(q_rows, k, v, P, frames, scale=None):
+    """Softmax attention of the given query rows over every key of `frames`
+    (frame g = tokens g*P .. g*P+P-1 of k, v); zeros when `frames` is empty."""
+    q_rows = np.asarray(q_rows, np.float64)
+    d = q_rows.shape[1]
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    if not frames:
+        return np.zeros((q_rows.shape[0], np.shape(v)[1]))
+    idx = np.concatenate([np.arange(g * P, (g + 1) * P) for g in frames])
+    kk = np.asarray(k[idx], np.float64)
+    vv = np.asarray(v[idx], np.float64)
+    z = scale * (q_rows @ kk.T)
+    z -= z.max(axis=1, keepdims=True)
+    e = np.exp(z)
+    return (e @ vv) / e.sum(axis=1, keepdims=True)
 
 
 def swa(q, k, v, T, P, W, scale=None):

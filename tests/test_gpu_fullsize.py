@@ -1,0 +1,100 @@
+"""GPU parity at the full workload sizes, in the launch configuration bench.py
+times (all heads, whole clips), checked on sampled outputs the float64 oracle
+computes one by one: the whole memory branch and final state of sampled heads,
+and the softmax branches and mix on sampled query frames of those heads.
+Tolerance: relative L2 1e-2 (bf16 inputs, fp32 accumulation)."""
+import numpy as np
+import pytest
+import torch
+
+from hybrid_linear_temporal_amd import hlta as H
+from hybrid_linear_temporal_amd import inputs as I
+from oracle import hlta_oracle as O
+from tests.helpers import TOL, to64
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    H.load_library()
+
+
+def _check_head(wl, x, res, b, h, frames, label):
+    q, k, v = x["q"][b, :, h], x["k"][b, :, h], x["v"][b, :, h]
+    o_gdn, S = O.gdn_chunked(q, k, v, x["a"][b, :, h], x["b"][b, :, h], wl.gdn_chunk)
+    e = O.rel_l2(to64(res["o_gdn"][b, :, h]), o_gdn)
+    eS = O.rel_l2(to64(res["S_out"][b, h]), S)
+    print(f"{label} (b={b}, h={h}) o_gdn {e:.2e} S_out {eS:.2e}", flush=True)
+    assert e <= TOL["bf16"] and eS <= TOL["bf16"]
+    w3 = x["w"][h].astype(np.float64)
+    P = wl.P
+    for f in frames:
+        sl = slice(f * P, (f + 1) * P)
+        swa = O.attend_rows(q[sl], k, v, P, O.swa_frames(f, wl.swa_frames))
+        dsw = O.attend_rows(q[sl], k, v, P, O.dswa_frames(f, wl.dswa_dilation, wl.dswa_taps))
+        mix = w3[0] * swa + w3[1] * dsw + w3[2] * o_gdn[sl]
+        for name, ref in (("o_swa", swa), ("o_dswa", dsw), ("o_mix", mix)):
+            got = to64(res[name][b, sl, h])
+            err = O.rel_l2(got, ref)
+            print(f"{label} (b={b}, h={h}) frame {f} {name} {err:.2e}", flush=True)
+            assert err <= TOL["bf16"], f"{label} frame {f} {name}: {err:.3e}"
+
+
+@pytest.mark.parametrize("wl", [I.P480_T31, I.P480_T61, I.P720_T61], ids=lambda w: w.name)
+def test_full_size_sampled(wl):
+    print(f"generating {wl.name}", flush=True)
+    x = I.make_clip(wl, threads=16)
+    dev = H.to_device(x, wl.dtype)
+    cfg = H.make_config(wl)
+    S_out = torch.empty((wl.B, wl.H, wl.d, wl.d), dtype=torch.float32, device="cuda")
+    res = H.hlta_fwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], S_out=S_out)
+    torch.cuda.synchronize()
+    del dev
+    # frames: first (no DSWA key frame), one with a partial DSWA set, middle, last
+    frames = sorted({0, 5, wl.T // 2, wl.T - 1})
+    for b, h in ((0, 0), (wl.B - 1, wl.H - 1)):
+        _check_head(wl, x, res, b, h, frames, wl.name)
+
+
+def test_stream_full_size_sampled():
+    """8 rollouts of 480P frames: a 16-frame prefix through hlta_fwd, then
+    frame steps; sampled (rollout, head) pairs against the streaming oracle."""
+    wl = I.STREAM_P480
+    P, R, prefix, steps = wl.P, wl.ring_frames, wl.prefix_frames, 3
+    pre_wl = I.Workload("stream_prefix", B=wl.B, H=wl.H, T=prefix, P=P, d=wl.d, swa_frames=wl.swa_frames,
+                        dswa_dilation=wl.dswa_dilation, dswa_taps=wl.dswa_taps, gdn_chunk=wl.gdn_chunk,
+                        dtype=wl.dtype, seed=wl.seed)
+    print("generating stream prefix", flush=True)
+    xp = I.make_clip(pre_wl, stream=I.S_PREFIX, threads=16)
+    dev = H.to_device(xp, wl.dtype)
+    cfg_pre = H.make_config(pre_wl)
+    S_pre = torch.empty((wl.B, wl.H, wl.d, wl.d), dtype=torch.float32, device="cuda")
+    H.hlta_fwd(cfg_pre, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], S_out=S_pre)
+    st = H.Stream(H.make_config(wl), R)
+    H.hlta_stream_load_prefix(st, dev["k"], dev["v"], prefix, S_pre)
+    del dev
+    pairs = ((0, 0), (wl.B - 1, wl.H - 1))
+    ost = {}
+    for b, h in pairs:
+        _, Sp = O.gdn_chunked(xp["q"][b, :, h], xp["k"][b, :, h], xp["v"][b, :, h], xp["a"][b, :, h],
+                              xp["b"][b, :, h], wl.gdn_chunk)
+        s = O.StreamHead(P, wl.swa_frames, wl.dswa_dilation, wl.dswa_taps, wl.gdn_chunk)
+        s.load_prefix(xp["k"][b, :, h], xp["v"][b, :, h], prefix, Sp)
+        ost[b, h] = s
+    for s_i in range(steps):
+        xs = I.stream_step_inputs(wl, s_i, threads=16)
+        d = H.to_device(xs, wl.dtype)
+        got = H.hlta_step_frame(st, d["q"], d["k"], d["v"], d["a"], d["b"], d["w"])
+        torch.cuda.synchronize()
+        for b, h in pairs:
+            refs = ost[b, h].step(xs["q"][b, :, h], xs["k"][b, :, h], xs["v"][b, :, h], xs["a"][b, :, h],
+                                  xs["b"][b, :, h], xs["w"][h])
+            for name, ref in zip(("o_swa", "o_dswa", "o_gdn", "o_mix"), refs):
+                err = O.rel_l2(to64(got[name][b, :, h]), ref)
+                print(f"stream step {s_i} (b={b}, h={h}) {name} {err:.2e}", flush=True)
+                assert err <= TOL["bf16"], f"step {s_i} {name}: {err:.3e}"
+    for b, h in pairs:
+        err = O.rel_l2(to64(st.S[b, h]), ost[b, h].S0)
+        assert err <= TOL["bf16"], f"stream state {err:.3e}"
