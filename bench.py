@@ -50,8 +50,9 @@ def work(wl):
 
 
 def source_digest(*names):
+    """Digest of kernel sources (plus the shared device header)."""
     h = hashlib.sha256()
-    for n in names:
+    for n in (*names, "hlta_device.h"):
         with open(os.path.join(ROOT, "hybrid_linear_temporal_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -176,6 +177,9 @@ def main():
     ap.add_argument("--impl", type=int, default=0, help="0 auto, 1 generic, 2 mfma")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stream-steps", type=int, default=64, help="streaming frame steps to time (0: skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB read + 1 GiB write elementwise kernel (3 launches), to scale "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -184,6 +188,16 @@ def main():
     import torch
     from hybrid_linear_temporal_amd import hlta as H
     from hybrid_linear_temporal_amd import inputs as I
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"read_bytes": src.numel() * 4, "write_bytes": dst.numel() * 4,
+                                               "launches": 3}}))
+        return
 
     wl = I.WORKLOADS[args.workload]
     if wl.rollouts:

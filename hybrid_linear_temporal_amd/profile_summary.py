@@ -1,0 +1,41 @@
+"""Summarise a rocprofv3 kernel trace (CSV) of bench.py by kernel and launch grid.
+
+    python -m hybrid_linear_temporal_amd.profile_summary <dir>/<name>_kernel_trace.csv
+
+Prints a markdown table: kernel, grid (workgroups), launches, mean / min / max
+duration in microseconds.
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import sys
+
+
+def summarise(path: str) -> str:
+    agg = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        name = r["Kernel_Name"]
+        if "hlta" not in name:
+            continue
+        short = name
+        for pre in ("hlta::(anonymous namespace)::", "void "):
+            short = short.replace(pre, "")
+        short = short.split("(")[0]
+        for mangled, plain in (("16attn_mfma_kernelIDF16b", "attn_mfma_kernel<bf16>"),
+                               ("16attn_mfma_kernelIf", "attn_mfma_kernel<float>"),
+                               ("14gdn_chain_mfmaIDF16b", "gdn_chain_mfma<bf16>"),
+                               ("14gdn_chain_mfmaIf", "gdn_chain_mfma<float>")):
+            if mangled in short:
+                short = plain
+        wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
+        grid = (int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])) // max(wg, 1)
+        agg[(short, grid)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = ["| kernel | workgroups | launches | mean us | min us | max us |", "|---|---|---|---|---|---|"]
+    for (k, grid), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"| {k} | {grid} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} |")
+    return "\n".join(out)
+
+
+if __name__ == "__main__":
+    print(summarise(sys.argv[1]))
