@@ -47,9 +47,6 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 constexpr int D = 128;
 constexpr int C = 64;
 constexpr int NT = 256;
-constexpr int XP = D + 8;   // LDS pitch (bf16) of 64 x 128 tiles
-constexpr int CP = C + 8;   // LDS pitch (bf16) of 64 x 64 / 128 x 64 tiles
-constexpr int FP = C + 4;   // LDS pitch (fp32) of 64 x 64 matrices
 constexpr float kL2Eps = 1e-6f;
 constexpr float kLogAFloor = -80.f;
 using R = GdnMfmaRec;
@@ -71,62 +68,104 @@ __device__ __forceinline__ bf16x4 ld_tr(const bf16* p) {
 
 __device__ __forceinline__ bf16x4 ld4(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
 
-__device__ __forceinline__ void load_rows(bf16 (*dst)[XP], const bf16* src, size_t row_stride, int n, int tid) {
-  // 64 rows x 16 chunks of 16 B
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (tid >> 4) + 16 * i, c = tid & 15;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row < n) v = *reinterpret_cast<const uint4*>(src + size_t(row) * row_stride + c * 8);
-    *reinterpret_cast<uint4*>(&dst[row][c * 8]) = v;
-  }
+
+// direct global -> LDS loads, padded-tile helpers
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
+                                   (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+// Source offset of chunk slot P of a padded tile (row P / pitch, chunk P % pitch).
+__device__ __forceinline__ unsigned slot_offset(int P, int pitch_chunks, int src_chunks, int src_row_bytes,
+                                                int clamp_row) {
+  int row = P / pitch_chunks, ch = P - row * pitch_chunks;
+  if (ch >= src_chunks) ch = src_chunks - 1;
+  if (row > clamp_row) row = clamp_row;
+  return unsigned(row) * unsigned(src_row_bytes) + unsigned(ch) * 16u;
+}
+
+// 4 consecutive bf16 at (row, col) of a padded tile
+template <int PC>
+__device__ __forceinline__ bf16x4 ld4p(const uint4* t, int row, int col) {
+  return *reinterpret_cast<const bf16x4*>(reinterpret_cast<const char*>(t) + row * (PC * 16) + col * 2);
+}
+template <int PC>
+__device__ __forceinline__ bf16x4 ld4p_tr(const uint4* t, int row, int col) {
+  return ld_tr(reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(t) + row * (PC * 16) + col * 2));
+}
+
+__device__ __forceinline__ unsigned tok_offset(unsigned off256, int last_row, unsigned tok_bytes) {
+  unsigned row = off256 >> 8;
+  if (row > unsigned(last_row)) row = unsigned(last_row);
+  return row * tok_bytes + (off256 & 255u);
 }
 
 // ---------------------------------------------------------------------------
 // kernel 1: per-chunk preparation
 // ---------------------------------------------------------------------------
 
+// LDS of one chunk (76 KB, two workgroups per CU). K, Q, V tiles have 272-byte
+// rows (17 chunk slots, filled by direct loads); the Q tile is reused for A
+// after the Gram products, and the T region first stages Aqk, then holds T,
+// then the bf16 T' = T diag(b gamma / ||k||) and T'' = T diag(b).
+constexpr int PQ = 17;           // chunk slots per K/Q/V row
+constexpr int AP = 68;           // fp32 pitch of A and T
+constexpr int TP = 68;           // bf16 pitch of T' and T''
+constexpr int TILE_BYTES = C * PQ * 16;
+static_assert(C * AP * 4 == TILE_BYTES, "A and T fill one tile region");
 struct PrepSmem {
-  bf16 K[C][XP];
-  bf16 Q[C][XP];    // after the Gram products: Aqk staging (bf16 [C][CP])
-  bf16 V[C][XP];
-  float A[C][FP];
-  float T[C][FP];
-  float X[4][16][17];
-  float g[C], bb[C], rk[C], rq[C];
+  uint4 K[C * PQ];
+  uint4 V[C * PQ];
+  uint4 QA[C * PQ];            // Q tile, then A (fp32 [C][AP])
+  uint4 TT[C * PQ];            // Aqk staging (bf16 [C][72]), then T (fp32 [C][AP]), then T', T''
+  float X[4][16][20];          // per-wave 16x16 scratch
+  float g[C], bb[C], rk[C], rq[C], sc[C];
 };
 
-// one 16x16 block product on VALU: lane owns row r = lane/4, cols 4*(lane%4)..+3
-__device__ __forceinline__ void blk_acc(float (*M)[FP], int r0, int c0, const float* B, int bpitch,
-                                        int b0r, int b0c, int lane, float out[4]) {
-  // out[c] += sum_k M[r0 + r][c0 + k] * B[(b0r + k) * bpitch + b0c + c]
-  const int r = lane >> 2, cc = (lane & 3) * 4;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const float m = M[r0 + r][c0 + k];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) out[c] += m * B[(b0r + k) * bpitch + b0c + cc + c];
-  }
+__device__ __forceinline__ bf16x8 ld8p(const uint4* t, int row, int col) {
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(t) + row * (PQ * 16) + col * 2);
 }
 
-__global__ void __launch_bounds__(NT, 1)
+__global__ void __launch_bounds__(NT, 2)
 gdn_prep_mfma(GdnParams p) {
   __shared__ __attribute__((aligned(16))) PrepSmem sm;
+  float (*A)[AP] = reinterpret_cast<float (*)[AP]>(sm.QA);
+  float (*T)[AP] = reinterpret_cast<float (*)[AP]>(sm.TT);
+  bf16 (*aqk)[72] = reinterpret_cast<bf16 (*)[72]>(sm.TT);
+  bf16 (*t1)[TP] = reinterpret_cast<bf16 (*)[TP]>(sm.TT);
+  bf16 (*t2)[TP] = reinterpret_cast<bf16 (*)[TP]>(reinterpret_cast<unsigned char*>(sm.TT) + C * TP * 2);
+
   // last chunk first: when the state pass starts, the records it reads first
   // are the most recently written ones (still in the last-level cache)
   const int chunk = p.n_chunks - 1 - int(blockIdx.x), h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long long t0 = (long long)chunk * C;
   const int n = int(p.L - t0 < C ? p.L - t0 : C);
   const size_t HD = size_t(p.H) * D;
-  const size_t base = (size_t(b) * p.L + t0) * HD + size_t(h) * D;
+  const unsigned tok_bytes = unsigned(HD * sizeof(bf16));
+  const size_t tbase = ((size_t(b) * p.L + t0) * HD + size_t(h) * D) * sizeof(bf16);
   const size_t gbase = (size_t(b) * p.L + t0) * p.H + h;
   unsigned char* rec = p.ws + (size_t(b * p.H + h) * p.n_chunks + chunk) * p.rec_bytes;
 
-  load_rows(sm.K, static_cast<const bf16*>(p.k) + base, HD, n, tid);
-  load_rows(sm.Q, static_cast<const bf16*>(p.q) + base, HD, n, tid);
-  load_rows(sm.V, static_cast<const bf16*>(p.v) + base, HD, n, tid);
-  for (int e = tid; e < C * FP; e += NT) (&sm.T[0][0])[e] = 0.f;
+  // ---- K, Q, V: direct loads into padded tiles (rows past the end repeat the last token) ----
+  {
+    const unsigned char* kb = static_cast<const unsigned char*>(p.k) + tbase;
+    const unsigned char* qb = static_cast<const unsigned char*>(p.q) + tbase;
+    const unsigned char* vb = static_cast<const unsigned char*>(p.v) + tbase;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const int j = wave + 4 * i;
+      if (j < PQ) {
+        const unsigned off = tok_offset(slot_offset(64 * j + lane, PQ, 16, 256, C - 1), n - 1, tok_bytes);
+        dma16(kb + off, &sm.K[64 * j]);
+        dma16(qb + off, &sm.QA[64 * j]);
+        dma16(vb + off, &sm.V[64 * j]);
+      }
+    }
+  }
   if (wave == 0) {
     // gates: inclusive scan of log a over the chunk (one token per lane)
     float la = 0.f, bi = 0.f;
@@ -142,17 +181,22 @@ gdn_prep_mfma(GdnParams p) {
     sm.g[lane] = la;
     sm.bb[lane] = bi;
   }
+  wait_vmem();
   __syncthreads();
   {
-    // inverse norms: 4 threads per row, 32 elements each
+    // inverse norms: 4 threads per row, 32 elements each (four 16-byte reads per tile)
     const int row = tid >> 2, part = tid & 3;
     float sk = 0.f, sq = 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const float kv = static_cast<float>(sm.K[row][part * 32 + i]);
-      const float qv = static_cast<float>(sm.Q[row][part * 32 + i]);
-      sk += kv * kv;
-      sq += qv * qv;
+    for (int c = 0; c < 4; ++c) {
+      const bf16x8 kv = ld8p(sm.K, row, 32 * part + 8 * c);
+      const bf16x8 qv = ld8p(sm.QA, row, 32 * part + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = static_cast<float>(kv[e]), y = static_cast<float>(qv[e]);
+        sk += x * x;
+        sq += y * y;
+      }
     }
     sk += __shfl_xor(sk, 1, 4);
     sk += __shfl_xor(sk, 2, 4);
@@ -164,41 +208,54 @@ gdn_prep_mfma(GdnParams p) {
     }
   }
   __syncthreads();
+  if (tid < C) sm.sc[tid] = sm.bb[tid] * __expf(sm.g[tid]) * sm.rk[tid];
 
-  // ---- Gram products: wave w owns token rows 16w..16w+15 ----
+  // ---- Gram products on raw bf16: wave w owns token rows 16w..16w+15 ----
   {
-    f32x4 kk[4], qk[4];
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) kk[jb] = qk[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 ak[4], aq[4], bk[4][4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&sm.K[16 * wave + l16][32 * ks + 8 * g]);
-      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sm.Q[16 * wave + l16][32 * ks + 8 * g]);
+      ak[ks] = ld8p(sm.K, 16 * wave + l16, 32 * ks + 8 * g);
+      aq[ks] = ld8p(sm.QA, 16 * wave + l16, 32 * ks + 8 * g);
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
-        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&sm.K[16 * jb + l16][32 * ks + 8 * g]);
-        kk[jb] = mfma16(ak, bk, kk[jb]);
-        qk[jb] = mfma16(aq, bk, qk[jb]);
+      for (int jb = 0; jb < 4; ++jb) bk[jb][ks] = ld8p(sm.K, 16 * jb + l16, 32 * ks + 8 * g);
+    }
+    f32x4 kk[4], qk[4];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      kk[jb] = qk[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        kk[jb] = mfma16(ak[ks], bk[jb][ks], kk[jb]);
+        qk[jb] = mfma16(aq[ks], bk[jb][ks], qk[jb]);
       }
     }
-    __syncthreads();   // Q is dead from here; its space stages Aqk
-    bf16 (*aqk)[CP] = reinterpret_cast<bf16 (*)[CP]>(&sm.Q[0][0]);
+    float gi[4], ri[4], qi[4], bi[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * wave + 4 * g + e;
+      gi[e] = sm.g[i];
+      ri[e] = sm.rk[i];
+      qi[e] = sm.rq[i];
+      bi[e] = sm.bb[i];
+    }
+    __syncthreads();   // every wave is done with the Q tile: it becomes A
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
       const int j = 16 * jb + l16;
+      const float gj = sm.g[j], rj = sm.rk[j];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 16 * wave + 4 * g + e;
-        const float ratio = j <= i ? __expf(sm.g[i] - sm.g[j]) : 0.f;
-        sm.A[i][j] = j < i ? sm.bb[i] * ratio * sm.rk[i] * sm.rk[j] * kk[jb][e] : 0.f;
-        aqk[i][j] = static_cast<bf16>(ratio * sm.rq[i] * sm.rk[j] * qk[jb][e]);
+        const float ratio = j <= i ? __expf(gi[e] - gj) : 0.f;
+        A[i][j] = j < i ? bi[e] * ratio * ri[e] * rj * kk[jb][e] : 0.f;
+        aqk[i][j] = static_cast<bf16>(ratio * qi[e] * rj * qk[jb][e]);
       }
     }
   }
   __syncthreads();
-  // Aqk to the record (64 rows x 8 chunks of 16 B)
   {
-    const bf16 (*aqk)[CP] = reinterpret_cast<const bf16 (*)[CP]>(&sm.Q[0][0]);
+    // Aqk to the record (64 rows x 8 chunks of 16 B)
     bf16* dst = reinterpret_cast<bf16*>(rec + R::AQK);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -206,21 +263,23 @@ gdn_prep_mfma(GdnParams p) {
       *reinterpret_cast<uint4*>(dst + row * C + c * 8) = *reinterpret_cast<const uint4*>(&aqk[row][c * 8]);
     }
   }
+  __syncthreads();   // the staging is dead: the region becomes T
 
-  // ---- T = (I + A)^-1: diagonal 16x16 blocks (wave w, lane = column) ----
-  if (l16 == lane) {
+  // ---- T = (I + A)^-1, diagonal 16x16 blocks: wave w, lane c < 16 computes column c ----
+  if (lane < 16) {
     const int o = 16 * wave, c = lane;
     float t[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float s = r == c ? 1.f : 0.f;
-      if (r > c) {
+      float4 row[4];
 #pragma unroll
-        for (int k = 0; k < 16; ++k)
-          if (k >= c && k < r) s -= sm.A[o + r][o + k] * t[k];
-      }
-      t[r] = s;
-      sm.T[o + r][o + c] = s;
+      for (int q = 0; q < 4; ++q) row[q] = *reinterpret_cast<const float4*>(&A[o + r][o + 4 * q]);
+      const float* a = reinterpret_cast<const float*>(row);
+      float s = r == c ? 1.f : 0.f;
+#pragma unroll
+      for (int k = 0; k < r; ++k) s -= a[k] * t[k];
+      t[r] = r > c ? s : (r == c ? 1.f : 0.f);
+      T[o + r][o + c] = t[r];
     }
   }
   __syncthreads();
@@ -228,95 +287,134 @@ gdn_prep_mfma(GdnParams p) {
   for (int level = 1; level < 4; ++level) {
     const int i = wave, j = wave - level;
     if (j >= 0) {
+      const int r = lane >> 2, cc = (lane & 3) * 4;
       float x[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int k = j; k < i; ++k) blk_acc(sm.A, 16 * i, 16 * k, &sm.T[0][0], FP, 16 * k, 16 * j, lane, x);
-      const int r = lane >> 2, cc = (lane & 3) * 4;
+      for (int k = j; k < i; ++k) {
+        float4 arow[4], tr[16];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) sm.X[wave][r][cc + c] = x[c];
-    }
-    __syncthreads();
-    if (j >= 0) {
-      float y[4] = {0.f, 0.f, 0.f, 0.f};
-      const int r = lane >> 2, cc = (lane & 3) * 4;
+        for (int q = 0; q < 4; ++q) arow[q] = *reinterpret_cast<const float4*>(&A[16 * i + r][16 * k + 4 * q]);
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float t = sm.T[16 * i + r][16 * i + k];
+        for (int kk = 0; kk < 16; ++kk) tr[kk] = *reinterpret_cast<const float4*>(&T[16 * k + kk][16 * j + cc]);
+        const float* a = reinterpret_cast<const float*>(arow);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) y[c] += t * sm.X[wave][k][cc + c];
+        for (int kk = 0; kk < 16; ++kk) {
+          x[0] += a[kk] * tr[kk].x;
+          x[1] += a[kk] * tr[kk].y;
+          x[2] += a[kk] * tr[kk].z;
+          x[3] += a[kk] * tr[kk].w;
+        }
       }
+      *reinterpret_cast<float4*>(&sm.X[wave][r][cc]) = make_float4(x[0], x[1], x[2], x[3]);
+      // X is private to this wave and LDS executes a wave's accesses in order:
+      // only the compiler must not move the reads above the writes
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      float4 trow[4], xr[16];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) sm.T[16 * i + r][16 * j + cc + c] = -y[c];
+      for (int q = 0; q < 4; ++q) trow[q] = *reinterpret_cast<const float4*>(&T[16 * i + r][16 * i + 4 * q]);
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) xr[kk] = *reinterpret_cast<const float4*>(&sm.X[wave][kk][cc]);
+      const float* tt = reinterpret_cast<const float*>(trow);
+      float y[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) {
+        y[0] += tt[kk] * xr[kk].x;
+        y[1] += tt[kk] * xr[kk].y;
+        y[2] += tt[kk] * xr[kk].z;
+        y[3] += tt[kk] * xr[kk].w;
+      }
+      *reinterpret_cast<float4*>(&T[16 * i + r][16 * j + cc]) = make_float4(-y[0], -y[1], -y[2], -y[3]);
     }
     __syncthreads();
   }
 
-  // ---- W^T = K^T T'^T with T' = T diag(b gamma rk): wave w -> d_k blocks 2w, 2w+1 ----
+  // ---- T' = T diag(b gamma / ||k||) and T'' = T diag(b) in bf16 (lower triangle) ----
+  {
+    const int i = tid >> 2, c0 = 16 * (tid & 3);
+    float v1[16], v2[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 tq = *reinterpret_cast<const float4*>(&T[i][c0 + 4 * q]);
+      const float4 sq4 = *reinterpret_cast<const float4*>(&sm.sc[c0 + 4 * q]);
+      const float4 bq4 = *reinterpret_cast<const float4*>(&sm.bb[c0 + 4 * q]);
+      const float tv[4] = {tq.x, tq.y, tq.z, tq.w}, sv[4] = {sq4.x, sq4.y, sq4.z, sq4.w},
+                  bv[4] = {bq4.x, bq4.y, bq4.z, bq4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool lower = c0 + 4 * q + e <= i;
+        v1[4 * q + e] = lower ? tv[e] * sv[e] : 0.f;
+        v2[4 * q + e] = lower ? tv[e] * bv[e] : 0.f;
+      }
+    }
+    __syncthreads();   // T is read: the region becomes T', T''
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bf16x4 w1 = {static_cast<bf16>(v1[4 * q]), static_cast<bf16>(v1[4 * q + 1]),
+                         static_cast<bf16>(v1[4 * q + 2]), static_cast<bf16>(v1[4 * q + 3])};
+      const bf16x4 w2 = {static_cast<bf16>(v2[4 * q]), static_cast<bf16>(v2[4 * q + 1]),
+                         static_cast<bf16>(v2[4 * q + 2]), static_cast<bf16>(v2[4 * q + 3])};
+      *reinterpret_cast<bf16x4*>(&t1[i][c0 + 4 * q]) = w1;
+      *reinterpret_cast<bf16x4*>(&t2[i][c0 + 4 * q]) = w2;
+    }
+  }
+  __syncthreads();
+
+  // ---- W^T = K^T T'^T: wave w -> d_k blocks 2w, 2w+1 (A = K^T read transposed) ----
   {
     bf16* wn = reinterpret_cast<bf16*>(rec + R::WN);
+    bf16x8 ka[2][2], tb8[2][4];
+#pragma unroll
+    for (int js = 0; js < 2; ++js) {
+      const int jr = 32 * js + 8 * g;
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const int col = 16 * (2 * wave + mi) + 4 * (l16 & 3);
+        ka[mi][js] = join(ld4p_tr<PQ>(sm.K, jr + (l16 >> 2), col), ld4p_tr<PQ>(sm.K, jr + 4 + (l16 >> 2), col));
+      }
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) {
+        const bf16* r = &t1[16 * ib + l16][jr];
+        tb8[js][ib] = join(*reinterpret_cast<const bf16x4*>(r), *reinterpret_cast<const bf16x4*>(r + 4));
+      }
+    }
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi) {
       const int mb = 2 * wave + mi;
-      f32x4 acc[4];
-#pragma unroll
-      for (int ib = 0; ib < 4; ++ib) acc[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int js = 0; js < 2; ++js) {
-        // A = K^T rows d_k = 16mb + l16, slots = tokens 32js + 8g + 0..7 (transposed reads)
-        const int jr = 32 * js + 8 * g;
-        const bf16x4 lo = ld_tr(&sm.K[jr + (l16 >> 2)][16 * mb + 4 * (l16 & 3)]);
-        const bf16x4 hi = ld_tr(&sm.K[jr + 4 + (l16 >> 2)][16 * mb + 4 * (l16 & 3)]);
-        const bf16x8 a = join(lo, hi);
-        float sc[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int j = jr + q;
-          sc[q] = sm.bb[j] * __expf(sm.g[j]) * sm.rk[j];
-        }
-#pragma unroll
-        for (int ib = 0; ib < 4; ++ib) {
-          // B = T'^T: col = token i = 16ib + l16, slots j = jr + 0..7
-          const int i = 16 * ib + l16;
-          bf16x8 bv;
-#pragma unroll
-          for (int q = 0; q < 8; ++q) bv[q] = static_cast<bf16>(sm.T[i][jr + q] * sc[q]);
-          acc[ib] = mfma16(a, bv, acc[ib]);
-        }
-      }
-      // C layout: col = token i, rows d_k = 16mb + 4g + e -> Wn[i][d_k..d_k+3] = -W
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int js = 0; js < 2; ++js) acc = mfma16(ka[mi][js], tb8[js][ib], acc);
+        // C layout: col = token i = 16ib + l16, rows d_k = 16mb + 4g + e -> Wn[i][d_k..d_k+3] = -W
         const int i = 16 * ib + l16;
-        const bf16x4 v = {static_cast<bf16>(-acc[ib][0]), static_cast<bf16>(-acc[ib][1]),
-                          static_cast<bf16>(-acc[ib][2]), static_cast<bf16>(-acc[ib][3])};
+        const bf16x4 v = {static_cast<bf16>(-acc[0]), static_cast<bf16>(-acc[1]), static_cast<bf16>(-acc[2]),
+                          static_cast<bf16>(-acc[3])};
         *reinterpret_cast<bf16x4*>(wn + i * D + 16 * mb + 4 * g) = v;
       }
     }
   }
-  // ---- U' = T diag(b) V: wave w -> token rows 16w..16w+15, all 8 d_v blocks ----
+  // ---- U' = T'' V: wave w -> token rows 16w..16w+15, all 8 d_v blocks (B = V read transposed) ----
   {
     bf16* upt = reinterpret_cast<bf16*>(rec + R::UPT);
-    f32x4 acc[8];
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 ta[2];
 #pragma unroll
     for (int js = 0; js < 2; ++js) {
-      const int jr = 32 * js + 8 * g;
-      const int i = 16 * wave + l16;
-      bf16x8 a;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) a[q] = static_cast<bf16>(sm.T[i][jr + q] * sm.bb[jr + q]);
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const bf16x4 lo = ld_tr(&sm.V[jr + (l16 >> 2)][16 * nb + 4 * (l16 & 3)]);
-        const bf16x4 hi = ld_tr(&sm.V[jr + 4 + (l16 >> 2)][16 * nb + 4 * (l16 & 3)]);
-        acc[nb] = mfma16(a, join(lo, hi), acc[nb]);
-      }
+      const bf16* r = &t2[16 * wave + l16][32 * js + 8 * g];
+      ta[js] = join(*reinterpret_cast<const bf16x4*>(r), *reinterpret_cast<const bf16x4*>(r + 4));
     }
-    // C layout: col = d_v = 16nb + l16, rows = tokens 16w + 4g + e -> UpT[d_v][tok..tok+3]
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
-      const bf16x4 v = {static_cast<bf16>(acc[nb][0]), static_cast<bf16>(acc[nb][1]),
-                        static_cast<bf16>(acc[nb][2]), static_cast<bf16>(acc[nb][3])};
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int js = 0; js < 2; ++js) {
+        const int jr = 32 * js + 8 * g, col = 16 * nb + 4 * (l16 & 3);
+        const bf16x8 vb = join(ld4p_tr<PQ>(sm.V, jr + (l16 >> 2), col), ld4p_tr<PQ>(sm.V, jr + 4 + (l16 >> 2), col));
+        acc = mfma16(ta[js], vb, acc);
+      }
+      // C layout: col = d_v = 16nb + l16, rows = tokens 16w + 4g + e -> UpT[d_v][tok..tok+3]
+      const bf16x4 v = {static_cast<bf16>(acc[0]), static_cast<bf16>(acc[1]), static_cast<bf16>(acc[2]),
+                        static_cast<bf16>(acc[3])};
       *reinterpret_cast<bf16x4*>(upt + (16 * nb + l16) * C + 16 * wave + 4 * g) = v;
     }
   }
@@ -324,9 +422,9 @@ gdn_prep_mfma(GdnParams p) {
   if (tid < C) {
     const int i = tid;
     const float gl = sm.g[C - 1];
-    float* sq = reinterpret_cast<float*>(rec + R::SQ);
+    float* sqp = reinterpret_cast<float*>(rec + R::SQ);
     float* skp = reinterpret_cast<float*>(rec + R::SK);
-    sq[i] = i < n ? __expf(sm.g[i]) * sm.rq[i] : 0.f;
+    sqp[i] = i < n ? __expf(sm.g[i]) * sm.rq[i] : 0.f;
     skp[i] = i < n ? __expf(gl - sm.g[i]) * sm.rk[i] : 0.f;
     if (i == 0) *reinterpret_cast<float*>(rec + R::GC) = __expf(gl);
   }
@@ -361,32 +459,6 @@ struct ChainSmem {
   bf16 ostage[C][NV + 8];
 };
 
-__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
-                                   (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
-}
-
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
-
-// Source offset of chunk slot P of a padded tile (row P / pitch, chunk P % pitch).
-__device__ __forceinline__ unsigned slot_offset(int P, int pitch_chunks, int src_chunks, int src_row_bytes,
-                                                int clamp_row) {
-  int row = P / pitch_chunks, ch = P - row * pitch_chunks;
-  if (ch >= src_chunks) ch = src_chunks - 1;
-  if (row > clamp_row) row = clamp_row;
-  return unsigned(row) * unsigned(src_row_bytes) + unsigned(ch) * 16u;
-}
-
-// 4 consecutive bf16 at (row, col) of a padded tile
-template <int PC>
-__device__ __forceinline__ bf16x4 ld4p(const uint4* t, int row, int col) {
-  return *reinterpret_cast<const bf16x4*>(reinterpret_cast<const char*>(t) + row * (PC * 16) + col * 2);
-}
-template <int PC>
-__device__ __forceinline__ bf16x4 ld4p_tr(const uint4* t, int row, int col) {
-  return ld_tr(reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(t) + row * (PC * 16) + col * 2));
-}
-
 // Lane offsets of the direct loads of one chunk (the same for every chunk;
 // q and k rows past the end of the last chunk are clamped separately).
 // Offsets are kept in (row * 256 + chunk * 16) form; q and k rows are tokens
@@ -405,12 +477,6 @@ __device__ __forceinline__ void make_plan(DmaPlan& pl, int lane) {
   for (int j = 0; j < PS; ++j) pl.aqk[j] = slot_offset(64 * j + lane, PS, 8, 128, C - 1);
 #pragma unroll
   for (int j = 0; j < 3; ++j) pl.upt[j] = slot_offset(64 * j + lane, PS, 8, 128, NV - 1);
-}
-
-__device__ __forceinline__ unsigned tok_offset(unsigned off256, int last_row, unsigned tok_bytes) {
-  unsigned row = off256 >> 8;
-  if (row > unsigned(last_row)) row = unsigned(last_row);
-  return row * tok_bytes + (off256 & 255u);
 }
 
 __device__ __forceinline__ void issue_chunk(ChainBuf& buf, const DmaPlan& pl, const unsigned char* rec,
