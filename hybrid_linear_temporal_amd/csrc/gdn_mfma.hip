@@ -457,6 +457,7 @@ struct ChainBuf {
 struct ChainSmem {
   ChainBuf buf[2];
   bf16 ostage[C][NV + 8];
+  unsigned pf_scratch[64];   // target of the L2 prefetch loads (never read)
 };
 
 // Lane offsets of the direct loads of one chunk (the same for every chunk;
@@ -501,8 +502,48 @@ __device__ __forceinline__ void issue_chunk(ChainBuf& buf, const DmaPlan& pl, co
   if (lane < 33) dma16(rec + R::SQ + 16 * lane, &buf.sc[0]);
 }
 
+// Workgroup barrier that orders LDS accesses only: global stores still in
+// flight (the outputs) and L2 prefetches are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// L2 prefetch of one chunk's operands: the record (325 lines of 128 B up to
+// gamma_C) and the q and k rows of its tokens (2 lines each). The 8
+// workgroups of a head split the lines (part = value block); each lane
+// touches one line with a 4-byte direct load into a scratch LDS word.
+constexpr int kRecLines = int((R::GC + 4 + 127) / 128);
+constexpr int kPrefetchLines = kRecLines + 4 * C;
+static_assert(kPrefetchLines <= 2 * 64 * (D / NV), "prefetch lanes");
+__device__ __forceinline__ void prefetch_chunk(const unsigned char* rec, const unsigned char* qb,
+                                               const unsigned char* kb, int part, int lane, int n,
+                                               unsigned tok_bytes, unsigned* scratch) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int idx = part * 128 + 64 * j + lane;
+    const unsigned char* src = rec;
+    if (idx < kRecLines) {
+      src = rec + 128 * idx;
+    } else if (idx < kPrefetchLines) {
+      const int t = idx - kRecLines, which = t >> 7, tok = min((t & 127) >> 1, n - 1);
+      src = (which ? kb : qb) + unsigned(tok) * tok_bytes + 128u * unsigned(t & 1);
+    }
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
+                                     (__attribute__((address_space(3))) void*)(scratch), 4, 0, 0);
+  }
+}
+
+// Three waves per workgroup, on separate SIMDs: wave 0 computes, wave 1 loads
+// the next chunk's operands into the other LDS buffer, wave 2 prefetches
+// chunks kPrefetchAhead ahead into L2. One barrier per chunk hands buffers
+// between the loader and the compute wave.
+constexpr int kChainWaves = 3;
+constexpr int kPrefetchAhead = 4;
+
 template <typename Tout>
-__global__ void __launch_bounds__(64, 1)
+__global__ void __launch_bounds__(64 * kChainWaves, 1)
 gdn_chain_mfma(GdnParams p) {
   __shared__ __attribute__((aligned(16))) ChainSmem sm;
   // XCD-aware: the 8 workgroups of a head get blockIdx with the same value mod 8
@@ -511,13 +552,62 @@ gdn_chain_mfma(GdnParams p) {
   const int bh = (slot / (D / NV)) * kChainXcds + xcd;
   if (bh >= p.B * p.H) return;
   const int b = bh / p.H, h = bh % p.H;
-  const int lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
-  const int v0 = NV * vblk;   // this wave's value channels v0 .. v0+15
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
+  const int v0 = NV * vblk;   // this workgroup's value channels v0 .. v0+15
   const size_t HD = size_t(p.H) * D;
   const size_t sbase = (size_t(b) * p.H + h) * D * D;
   const int tok_bytes = int(HD * sizeof(bf16));
-  Tout* o = static_cast<Tout*>(p.o);
+  auto rec_of = [&](int chunk) {
+    return p.ws + (size_t(b * p.H + h) * p.n_chunks + chunk) * p.rec_bytes;
+  };
+  auto tok_base = [&](int chunk) {
+    return ((size_t(b) * p.L + (long long)chunk * C) * HD + size_t(h) * D) * sizeof(bf16);
+  };
+  auto chunk_len = [&](int chunk) {
+    const long long t0 = (long long)chunk * C;
+    return int(p.L - t0 < C ? p.L - t0 : C);
+  };
 
+  if (wave == 1) {
+    // loader: chunk c + 1 into buf[(c + 1) & 1] while chunk c is computed
+    DmaPlan plan;
+    make_plan(plan, lane);
+    auto issue = [&](int chunk) {
+      const size_t tb = tok_base(chunk);
+      issue_chunk(sm.buf[chunk & 1], plan, rec_of(chunk), static_cast<const unsigned char*>(p.q) + tb,
+                  static_cast<const unsigned char*>(p.k) + tb, vblk, lane, chunk_len(chunk), tok_bytes);
+    };
+    issue(0);
+    wait_vmem();
+    lds_barrier();
+    for (int chunk = 0; chunk < p.n_chunks; ++chunk) {
+      if (chunk + 1 < p.n_chunks) issue(chunk + 1);
+      wait_vmem();
+      lds_barrier();
+    }
+    return;
+  }
+  if (wave == 2) {
+    // L2 prefetcher: never waits for its loads inside the loop
+    auto pf = [&](int chunk) {
+      const size_t tb = tok_base(chunk);
+      prefetch_chunk(rec_of(chunk), static_cast<const unsigned char*>(p.q) + tb,
+                     static_cast<const unsigned char*>(p.k) + tb, vblk, lane, chunk_len(chunk),
+                     unsigned(tok_bytes), sm.pf_scratch);
+    };
+    for (int c = 1; c < kPrefetchAhead && c < p.n_chunks; ++c) pf(c);
+    lds_barrier();
+    for (int chunk = 0; chunk < p.n_chunks; ++chunk) {
+      if (chunk + kPrefetchAhead < p.n_chunks) pf(chunk + kPrefetchAhead);
+      lds_barrier();
+    }
+    wait_vmem();
+    return;
+  }
+
+  // compute wave
+  Tout* o = static_cast<Tout*>(p.o);
   // S^T slice in C layout: block mb holds d_k rows 16mb + 4g + e, column d_v = v0 + l16
   f32x4 st[8];
 #pragma unroll
@@ -529,26 +619,11 @@ gdn_chain_mfma(GdnParams p) {
       st[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
-
-  DmaPlan plan;
-  make_plan(plan, lane);
-  auto issue = [&](int chunk, ChainBuf& dst) {
-    const unsigned char* rec = p.ws + (size_t(b * p.H + h) * p.n_chunks + chunk) * p.rec_bytes;
-    const long long t0 = (long long)chunk * C;
-    const size_t tb = ((size_t(b) * p.L + t0) * HD + size_t(h) * D) * sizeof(bf16);
-    const int n = int(p.L - t0 < C ? p.L - t0 : C);
-    issue_chunk(dst, plan, rec, static_cast<const unsigned char*>(p.q) + tb,
-                static_cast<const unsigned char*>(p.k) + tb, vblk, lane, n, tok_bytes);
-  };
-
-  issue(0, sm.buf[0]);
+  lds_barrier();   // chunk 0 has landed
   for (int chunk = 0; chunk < p.n_chunks; ++chunk) {
-    const int cur = chunk & 1;
-    wait_vmem();   // this chunk's operands have landed in buf[cur]
-    __builtin_amdgcn_s_barrier();   // single-wave workgroup: orders the LDS writes before the reads below
-    const ChainBuf& B = sm.buf[cur];
+    const ChainBuf& B = sm.buf[chunk & 1];
     const long long t0 = (long long)chunk * C;
-    const int n = int(p.L - t0 < C ? p.L - t0 : C);
+    const int n = chunk_len(chunk);
 
     // per-token scales of this lane's rows: tokens 16tb + 4g + e
     f32x4 sqv[4], skv[4];
@@ -612,11 +687,7 @@ gdn_chain_mfma(GdnParams p) {
       for (int js = 0; js < 2; ++js)
         aa[tb][js] = join(ld4p<PS>(B.Aqk, row, 32 * js + 4 * g), ld4p<PS>(B.Aqk, row, 32 * js + 16 + 4 * g));
     }
-    // the next chunk's operands stream into the other buffer while this
-    // chunk's MFMAs run (after its own LDS reads, so they do not contend)
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this chunk's LDS operands are in registers
-    __builtin_amdgcn_sched_barrier(0);
-    if (chunk + 1 < p.n_chunks) issue(chunk + 1, sm.buf[cur ^ 1]);
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 ub[2], usb[2];
 #pragma unroll
@@ -665,6 +736,7 @@ gdn_chain_mfma(GdnParams p) {
         }
       }
     }
+    lds_barrier();   // buf[chunk & 1] is free for the loader; chunk + 1 has landed
   }
   if (p.S_out) {
 #pragma unroll
@@ -684,9 +756,9 @@ hipError_t launch_gdn_mfma(const GdnParams& p, int out_dt, hipStream_t st) {
   const int heads_per_xcd = (p.B * p.H + kChainXcds - 1) / kChainXcds;
   const dim3 grid(unsigned(kChainXcds * heads_per_xcd * (D / NV)));
   if (out_dt == HLTA_BF16)
-    hipLaunchKernelGGL((gdn_chain_mfma<bf16>), grid, dim3(64), 0, st, p);
+    hipLaunchKernelGGL((gdn_chain_mfma<bf16>), grid, dim3(64 * kChainWaves), 0, st, p);
   else
-    hipLaunchKernelGGL((gdn_chain_mfma<float>), grid, dim3(64), 0, st, p);
+    hipLaunchKernelGGL((gdn_chain_mfma<float>), grid, dim3(64 * kChainWaves), 0, st, p);
   return hipGetLastError();
 }
 
