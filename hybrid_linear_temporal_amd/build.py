@@ -23,6 +23,10 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-result",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-file additions. The GDN state pass keeps its fp32 state in MFMA
+# accumulators that VALU code also scales and converts every chunk; the VGPR
+# form of MFMA keeps them out of the AGPR file (no copies back and forth).
+EXTRA = {"gdn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def sources() -> list[str]:
@@ -31,7 +35,7 @@ def sources() -> list[str]:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

@@ -456,50 +456,77 @@ struct ChainBuf {
 };
 struct ChainSmem {
   ChainBuf buf[2];
-  bf16 ostage[C][NV + 8];
+  bf16x8 stage[2][4][64];    // bf16 S^T published by the state wave, per lane, by chunk parity
   unsigned pf_scratch[64];   // target of the L2 prefetch loads (never read)
 };
 
-// Lane offsets of the direct loads of one chunk (the same for every chunk;
-// q and k rows past the end of the last chunk are clamped separately).
-// Offsets are kept in (row * 256 + chunk * 16) form; q and k rows are tokens
-// of the input tensors, so their offsets are rescaled to the token stride (and
-// clamped to the last token in the ragged last chunk).
+// Lane offsets of the direct loads of one chunk (the same for every chunk).
+// Record tiles use (row * 256 + chunk * 16) form; q and k rows are tokens of
+// the input tensors, so their offsets are rescaled to the token stride. Full
+// chunks use the precomputed 32-bit offsets on a scalar base (no per-load
+// vector arithmetic); the ragged last chunk clamps rows to its last token.
 struct DmaPlan {
   unsigned w[PW], k[PK], aqk[PS], upt[3];
+  unsigned qo[PW], ko[PK];
 };
 
-__device__ __forceinline__ void make_plan(DmaPlan& pl, int lane) {
+__device__ __forceinline__ void make_plan(DmaPlan& pl, int lane, unsigned tok_bytes) {
 #pragma unroll
-  for (int j = 0; j < PW; ++j) pl.w[j] = slot_offset(64 * j + lane, PW, 16, 256, C - 1);
+  for (int j = 0; j < PW; ++j) {
+    pl.w[j] = slot_offset(64 * j + lane, PW, 16, 256, C - 1);
+    pl.qo[j] = tok_offset(pl.w[j], C - 1, tok_bytes);
+  }
 #pragma unroll
-  for (int j = 0; j < PK; ++j) pl.k[j] = slot_offset(64 * j + lane, PK, 16, 256, C - 1);
+  for (int j = 0; j < PK; ++j) {
+    pl.k[j] = slot_offset(64 * j + lane, PK, 16, 256, C - 1);
+    pl.ko[j] = tok_offset(pl.k[j], C - 1, tok_bytes);
+  }
 #pragma unroll
   for (int j = 0; j < PS; ++j) pl.aqk[j] = slot_offset(64 * j + lane, PS, 8, 128, C - 1);
 #pragma unroll
   for (int j = 0; j < 3; ++j) pl.upt[j] = slot_offset(64 * j + lane, PS, 8, 128, NV - 1);
 }
 
+// Buffer resource over [base, base + bytes): loads through it take a 32-bit
+// lane offset plus a scalar offset (no per-lane 64-bit address arithmetic),
+// and lanes past the end read zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
+  const unsigned n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : unsigned(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(n), 0x00020000);
+}
+__device__ __forceinline__ void dma16r(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_base), 16, voff, soff, 0,
+                                           0);
+}
+
+// One chunk's operands into buf: the record's -W, Aqk, U' slice and scales,
+// and the q, k rows of its tokens (qk_bytes: bytes of q and k from the
+// chunk's first token to the end of the tensors).
 __device__ __forceinline__ void issue_chunk(ChainBuf& buf, const DmaPlan& pl, const unsigned char* rec,
-                                            const unsigned char* qb, const unsigned char* kb, int vblk, int lane,
-                                            int n, int src_tok_bytes) {
-  const unsigned char* wn = rec + R::WN;
-  const unsigned char* aqk = rec + R::AQK;
-  const unsigned char* upt = rec + R::UPT + size_t(NV * vblk) * 128;
-  const unsigned tb = unsigned(src_tok_bytes);
+                                            size_t rec_bytes, const unsigned char* qb, const unsigned char* kb,
+                                            size_t qk_bytes, int vblk, int lane, int n, unsigned tok_bytes) {
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec, rec_bytes);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, qk_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, qk_bytes);
 #pragma unroll
-  for (int j = 0; j < PW; ++j) {
-    dma16(wn + pl.w[j], &buf.Wn[64 * j]);
-    dma16(qb + tok_offset(pl.w[j], n - 1, tb), &buf.Q[64 * j]);
+  for (int j = 0; j < PW; ++j) dma16r(rr, pl.w[j], unsigned(R::WN), &buf.Wn[64 * j]);
+  if (n == C) {
+#pragma unroll
+    for (int j = 0; j < PW; ++j) dma16r(rq, pl.qo[j], 0u, &buf.Q[64 * j]);
+#pragma unroll
+    for (int j = 0; j < PK; ++j) dma16r(rk, pl.ko[j], 0u, &buf.K[64 * j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < PW; ++j) dma16r(rq, tok_offset(pl.w[j], n - 1, tok_bytes), 0u, &buf.Q[64 * j]);
+#pragma unroll
+    for (int j = 0; j < PK; ++j) dma16r(rk, tok_offset(pl.k[j], n - 1, tok_bytes), 0u, &buf.K[64 * j]);
   }
 #pragma unroll
-  for (int j = 0; j < PK; ++j) dma16(kb + tok_offset(pl.k[j], n - 1, tb), &buf.K[64 * j]);
-#pragma unroll
-  for (int j = 0; j < PS; ++j) dma16(aqk + pl.aqk[j], &buf.Aqk[64 * j]);
+  for (int j = 0; j < PS; ++j) dma16r(rr, pl.aqk[j], unsigned(R::AQK), &buf.Aqk[64 * j]);
 #pragma unroll
   for (int j = 0; j < 3; ++j)
-    if (64 * j + lane < NV * PS) dma16(upt + pl.upt[j], &buf.UpT[64 * j]);
-  if (lane < 33) dma16(rec + R::SQ + 16 * lane, &buf.sc[0]);
+    if (64 * j + lane < NV * PS) dma16r(rr, pl.upt[j], unsigned(R::UPT + size_t(NV * vblk) * 128), &buf.UpT[64 * j]);
+  if (lane < 33) dma16r(rr, 16u * unsigned(lane), unsigned(R::SQ), &buf.sc[0]);
 }
 
 // Workgroup barrier that orders LDS accesses only: global stores still in
@@ -535,12 +562,54 @@ __device__ __forceinline__ void prefetch_chunk(const unsigned char* rec, const u
   }
 }
 
-// Three waves per workgroup, on separate SIMDs: wave 0 computes, wave 1 loads
-// the next chunk's operands into the other LDS buffer, wave 2 prefetches
-// chunks kPrefetchAhead ahead into L2. One barrier per chunk hands buffers
-// between the loader and the compute wave.
-constexpr int kChainWaves = 3;
+// Four waves per workgroup, one per SIMD:
+//   wave 0 (state)   U = U' - W S^T and S <- gamma_C S + K^T diag(sk) U; it
+//                    publishes the bf16 copy of each new S in LDS;
+//   wave 1 (output)  recomputes U from that copy (same operands, same
+//                    products, so the same U) and writes O = diag(sq) Q S^T + Aqk U;
+//   wave 2 (loader)  loads chunk c + 1 into the other LDS buffer;
+//   wave 3           prefetches chunk c + kPrefetchAhead into L2.
+// One barrier per chunk hands the buffers and the published state over.
+constexpr int kChainWaves = 4;
 constexpr int kPrefetchAhead = 4;
+
+// -W tile (A operand of W S^T) and the U' slice (its initial value) of this lane.
+__device__ __forceinline__ void load_u_operands(const ChainBuf& B, int g, int l16, bf16x8 (&aw)[4][4],
+                                                bf16x4 (&upv)[4]) {
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    const int row = 16 * tb + l16;
+    upv[tb] = ld4p<PS>(B.UpT, l16, 16 * tb + 4 * g);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      aw[tb][ks] = join(ld4p<PW>(B.Wn, row, 32 * ks + 4 * g), ld4p<PW>(B.Wn, row, 32 * ks + 16 + 4 * g));
+  }
+}
+
+// U = U' - W S^T in C layout: u[tb] holds tokens 16tb + 4g + e of channel v0 + l16.
+__device__ __forceinline__ void compute_u(const bf16x8 (&aw)[4][4], const bf16x4 (&upv)[4], const bf16x8 (&sb)[4],
+                                          f32x4 (&u)[4]) {
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    u[tb] = f32x4{static_cast<float>(upv[tb][0]), static_cast<float>(upv[tb][1]), static_cast<float>(upv[tb][2]),
+                  static_cast<float>(upv[tb][3])};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) u[tb] = mfma16(aw[tb][ks], sb[ks], u[tb]);
+  }
+}
+
+// bf16 copy of S^T: K-step ks takes blocks 2ks, 2ks+1 (d_k = 32ks + 16(i/4) + 4g + i%4).
+// The 16x16x32 A and B layouts coincide, so it is the B operand of W S^T
+// (S^T, columns d_v) and the A operand of S q^T (S, rows d_v) alike.
+__device__ __forceinline__ void state_bf16(const f32x4 (&st)[8], bf16x8 (&sb)[4]) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sb[ks][e] = static_cast<bf16>(st[2 * ks][e]);
+      sb[ks][4 + e] = static_cast<bf16>(st[2 * ks + 1][e]);
+    }
+}
 
 template <typename Tout>
 __global__ void __launch_bounds__(64 * kChainWaves, 1)
@@ -557,7 +626,7 @@ gdn_chain_mfma(GdnParams p) {
   const int v0 = NV * vblk;   // this workgroup's value channels v0 .. v0+15
   const size_t HD = size_t(p.H) * D;
   const size_t sbase = (size_t(b) * p.H + h) * D * D;
-  const int tok_bytes = int(HD * sizeof(bf16));
+  const unsigned tok_bytes = unsigned(HD * sizeof(bf16));
   auto rec_of = [&](int chunk) {
     return p.ws + (size_t(b * p.H + h) * p.n_chunks + chunk) * p.rec_bytes;
   };
@@ -569,14 +638,16 @@ gdn_chain_mfma(GdnParams p) {
     return int(p.L - t0 < C ? p.L - t0 : C);
   };
 
-  if (wave == 1) {
+  if (wave == 2) {
     // loader: chunk c + 1 into buf[(c + 1) & 1] while chunk c is computed
     DmaPlan plan;
-    make_plan(plan, lane);
+    make_plan(plan, lane, tok_bytes);
+    const size_t qk_total = size_t(p.B) * size_t(p.L) * HD * sizeof(bf16);
     auto issue = [&](int chunk) {
       const size_t tb = tok_base(chunk);
-      issue_chunk(sm.buf[chunk & 1], plan, rec_of(chunk), static_cast<const unsigned char*>(p.q) + tb,
-                  static_cast<const unsigned char*>(p.k) + tb, vblk, lane, chunk_len(chunk), tok_bytes);
+      issue_chunk(sm.buf[chunk & 1], plan, rec_of(chunk), p.rec_bytes, static_cast<const unsigned char*>(p.q) + tb,
+                  static_cast<const unsigned char*>(p.k) + tb, qk_total - tb, vblk, lane, chunk_len(chunk),
+                  tok_bytes);
     };
     issue(0);
     wait_vmem();
@@ -588,13 +659,13 @@ gdn_chain_mfma(GdnParams p) {
     }
     return;
   }
-  if (wave == 2) {
+  if (wave == 3) {
     // L2 prefetcher: never waits for its loads inside the loop
     auto pf = [&](int chunk) {
       const size_t tb = tok_base(chunk);
       prefetch_chunk(rec_of(chunk), static_cast<const unsigned char*>(p.q) + tb,
-                     static_cast<const unsigned char*>(p.k) + tb, vblk, lane, chunk_len(chunk),
-                     unsigned(tok_bytes), sm.pf_scratch);
+                     static_cast<const unsigned char*>(p.k) + tb, vblk, lane, chunk_len(chunk), tok_bytes,
+                     sm.pf_scratch);
     };
     for (int c = 1; c < kPrefetchAhead && c < p.n_chunks; ++c) pf(c);
     lds_barrier();
@@ -606,77 +677,94 @@ gdn_chain_mfma(GdnParams p) {
     return;
   }
 
-  // compute wave
-  Tout* o = static_cast<Tout*>(p.o);
-  // S^T slice in C layout: block mb holds d_k rows 16mb + 4g + e, column d_v = v0 + l16
-  f32x4 st[8];
+  if (wave == 0) {
+    // state wave: S^T slice in C layout, block mb holds d_k rows 16mb + 4g + e, column d_v = v0 + l16
+    f32x4 st[8];
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb) {
-    if (p.S0) {
-      const float4 v = *reinterpret_cast<const float4*>(p.S0 + sbase + size_t(v0 + l16) * D + 16 * mb + 4 * g);
-      st[mb] = f32x4{v.x, v.y, v.z, v.w};
-    } else {
-      st[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < 8; ++mb) {
+      if (p.S0) {
+        const float4 v = *reinterpret_cast<const float4*>(p.S0 + sbase + size_t(v0 + l16) * D + 16 * mb + 4 * g);
+        st[mb] = f32x4{v.x, v.y, v.z, v.w};
+      } else {
+        st[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
+    bf16x8 sb[4];
+    state_bf16(st, sb);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) sm.stage[0][ks][lane] = sb[ks];
+    lds_barrier();   // chunk 0 has landed; the initial state is published
+    for (int chunk = 0; chunk < p.n_chunks; ++chunk) {
+      const ChainBuf& B = sm.buf[chunk & 1];
+      bf16x8 aw[4][4];
+      bf16x4 upv[4];
+      load_u_operands(B, g, l16, aw, upv);
+      f32x4 skv[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) skv[tb] = *reinterpret_cast<const f32x4*>(&B.sc[C + 16 * tb + 4 * g]);
+      const float gc = B.sc[2 * C];
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 u[4];
+      compute_u(aw, upv, sb, u);
+      // k^T (A operand of the state update), read while the U products run
+      bf16x8 ak[8][2];
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int js = 0; js < 2; ++js) {
+          const int col = 16 * mb + 4 * (l16 & 3);
+          ak[mb][js] = join(ld4p_tr<PK>(B.K, 32 * js + 4 * g + (l16 >> 2), col),
+                            ld4p_tr<PK>(B.K, 32 * js + 16 + 4 * g + (l16 >> 2), col));
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 usb[2];
+#pragma unroll
+      for (int js = 0; js < 2; ++js)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          usb[js][e] = static_cast<bf16>(u[2 * js][e] * skv[2 * js][e]);
+          usb[js][4 + e] = static_cast<bf16>(u[2 * js + 1][e] * skv[2 * js + 1][e]);
+        }
+      // S^T <- gamma_C S^T + K^T diag(sk) U
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st[mb][e] *= gc;
+#pragma unroll
+        for (int js = 0; js < 2; ++js) st[mb] = mfma16(ak[mb][js], usb[js], st[mb]);
+      }
+      state_bf16(st, sb);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) sm.stage[(chunk + 1) & 1][ks][lane] = sb[ks];
+      lds_barrier();   // buf[chunk & 1] is free; chunk + 1 has landed; S of chunk + 1 is published
+    }
+    if (p.S_out) {
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+        *reinterpret_cast<float4*>(p.S_out + sbase + size_t(v0 + l16) * D + 16 * mb + 4 * g) =
+            make_float4(st[mb][0], st[mb][1], st[mb][2], st[mb][3]);
+    }
+    return;
   }
-  lds_barrier();   // chunk 0 has landed
+
+  // output wave
+  Tout* o = static_cast<Tout*>(p.o);
+  lds_barrier();
   for (int chunk = 0; chunk < p.n_chunks; ++chunk) {
     const ChainBuf& B = sm.buf[chunk & 1];
     const long long t0 = (long long)chunk * C;
     const int n = chunk_len(chunk);
-
-    // per-token scales of this lane's rows: tokens 16tb + 4g + e
-    f32x4 sqv[4], skv[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      sqv[tb] = *reinterpret_cast<const f32x4*>(&B.sc[16 * tb + 4 * g]);
-      skv[tb] = *reinterpret_cast<const f32x4*>(&B.sc[C + 16 * tb + 4 * g]);
-    }
-    const float gc = B.sc[2 * C];
-
-    // LDS operands are read in two batches into registers so the reads
-    // pipeline: first those of the state path (-W, k, U'), then (while those
-    // MFMAs run) those of the output (q, Aqk).
-    bf16x8 aw[4][4], ak[8][2];
+    bf16x8 sb[4], aw[4][4];
     bf16x4 upv[4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const int row = 16 * tb + l16;
-      upv[tb] = ld4p<PS>(B.UpT, l16, 16 * tb + 4 * g);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        aw[tb][ks] = join(ld4p<PW>(B.Wn, row, 32 * ks + 4 * g), ld4p<PW>(B.Wn, row, 32 * ks + 16 + 4 * g));
-    }
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-      for (int js = 0; js < 2; ++js) {
-        const int col = 16 * mb + 4 * (l16 & 3);
-        ak[mb][js] = join(ld4p_tr<PK>(B.K, 32 * js + 4 * g + (l16 >> 2), col),
-                          ld4p_tr<PK>(B.K, 32 * js + 16 + 4 * g + (l16 >> 2), col));
-      }
+    for (int ks = 0; ks < 4; ++ks) sb[ks] = sm.stage[chunk & 1][ks][lane];
+    load_u_operands(B, g, l16, aw, upv);
     __builtin_amdgcn_sched_barrier(0);
-
-    // bf16 copy of S^T as B operand: K-step ks takes blocks 2ks, 2ks+1 (d_k = 32ks + 16(i/4) + 4g + i%4)
-    bf16x8 sb[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sb[ks][e] = static_cast<bf16>(st[2 * ks][e]);
-        sb[ks][4 + e] = static_cast<bf16>(st[2 * ks + 1][e]);
-      }
-
-    // (1) U = U' - W S^T: rows = tokens 16tb + 4g + e, col = d_v
     f32x4 u[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      u[tb] = f32x4{static_cast<float>(upv[tb][0]), static_cast<float>(upv[tb][1]), static_cast<float>(upv[tb][2]),
-                    static_cast<float>(upv[tb][3])};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) u[tb] = mfma16(aw[tb][ks], sb[ks], u[tb]);
-    }
+    compute_u(aw, upv, sb, u);
+    // q and Aqk rows (B operands of S q^T and U^T Aqk^T) and the query scales
     bf16x8 aq[4][4], aa[4][2];
+    float sqs[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       const int row = 16 * tb + l16;
@@ -686,63 +774,39 @@ gdn_chain_mfma(GdnParams p) {
 #pragma unroll
       for (int js = 0; js < 2; ++js)
         aa[tb][js] = join(ld4p<PS>(B.Aqk, row, 32 * js + 4 * g), ld4p<PS>(B.Aqk, row, 32 * js + 16 + 4 * g));
+      sqs[tb] = B.sc[row];
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this chunk's LDS operands are in registers
     __builtin_amdgcn_sched_barrier(0);
-    bf16x8 ub[2], usb[2];
+    bf16x8 ub[2];
 #pragma unroll
     for (int js = 0; js < 2; ++js)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         ub[js][e] = static_cast<bf16>(u[2 * js][e]);
         ub[js][4 + e] = static_cast<bf16>(u[2 * js + 1][e]);
-        usb[js][e] = static_cast<bf16>(u[2 * js][e] * skv[2 * js][e]);
-        usb[js][4 + e] = static_cast<bf16>(u[2 * js + 1][e] * skv[2 * js + 1][e]);
       }
-    // (3) S^T <- gamma_C S^T + K^T diag(sk) U (the next chunk waits on it)
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) st[mb][e] *= gc;
-#pragma unroll
-      for (int js = 0; js < 2; ++js) st[mb] = mfma16(ak[mb][js], usb[js], st[mb]);
-    }
-    // (2) O = diag(sq) (Q S^T) + Aqk U, staged in LDS for 16-byte stores
+    // O^T = (S q^T) diag(sq) + U^T Aqk^T: lane holds channels v0 + 4g + e of token 16tb + l16
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) x = mfma16(aq[tb][ks], sb[ks], x);
+      for (int ks = 0; ks < 4; ++ks) x = mfma16(sb[ks], aq[tb][ks], x);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] *= sqv[tb][e];
+      for (int e = 0; e < 4; ++e) x[e] *= sqs[tb];
 #pragma unroll
-      for (int js = 0; js < 2; ++js) x = mfma16(aa[tb][js], ub[js], x);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sm.ostage[16 * tb + 4 * g + e][l16] = static_cast<bf16>(x[e]);
-    }
-    // the 64 tokens x 16 channels back from LDS (one wave, in order): 2 x 16 B per token
-    if (lane < n) {
-      const bf16x8 lo = *reinterpret_cast<const bf16x8*>(&sm.ostage[lane][0]);
-      const bf16x8 hi = *reinterpret_cast<const bf16x8*>(&sm.ostage[lane][8]);
-      Tout* dst = o + (size_t(b) * p.L + t0 + lane) * HD + size_t(h) * D + v0;
-      if constexpr (sizeof(Tout) == 2) {
-        *reinterpret_cast<bf16x8*>(dst) = lo;
-        *reinterpret_cast<bf16x8*>(dst + 8) = hi;
-      } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          dst[q] = static_cast<float>(lo[q]);
-          dst[8 + q] = static_cast<float>(hi[q]);
+      for (int js = 0; js < 2; ++js) x = mfma16(ub[js], aa[tb][js], x);
+      const int tok = 16 * tb + l16;
+      if (tok < n) {
+        Tout* dst = o + (size_t(b) * p.L + t0 + tok) * HD + size_t(h) * D + v0 + 4 * g;
+        if constexpr (sizeof(Tout) == 2) {
+          *reinterpret_cast<bf16x4*>(dst) = bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]),
+                                                   static_cast<bf16>(x[2]), static_cast<bf16>(x[3])};
+        } else {
+          *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
         }
       }
     }
-    lds_barrier();   // buf[chunk & 1] is free for the loader; chunk + 1 has landed
-  }
-  if (p.S_out) {
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
-      *reinterpret_cast<float4*>(p.S_out + sbase + size_t(v0 + l16) * D + 16 * mb + 4 * g) =
-          make_float4(st[mb][0], st[mb][1], st[mb][2], st[mb][3]);
+    lds_barrier();
   }
 }
 
