@@ -75,26 +75,49 @@ __device__ __forceinline__ const T* uni(const T* ptr) {
 
 // Walks the virtual key sequence of one branch tile by tile. A tile of 64
 // keys spans at most two frames (P >= 64); all fields are wave-uniform.
+// Frames of a branch are g, g + step, ...: step 1 for SWA (oldest first),
+// -dil for DSWA. In stream mode the call's own frame f0 comes from the main
+// tensors and earlier frames from ring slot g mod R.
+template <bool kRing>
 struct KeyStream {
-  const AttnParams* p;
-  int b, h, branch, nswa, nframes;
-  long long f;
-  int slot, pk;            // current tile starts at token pk of frame slot `slot`
-  const bf16* k0;          // token 0 of the current frame
+  const bf16* kmain;     // token 0 of frame 0 (full mode) or of the call's frame (stream mode), head h
+  const bf16* vmain;
+  const bf16* kring;     // token 0 of ring slot 0, head h (stream mode)
+  const bf16* vring;
+  size_t fstride;        // elements between consecutive frames: P*H*D
+  long long f0;
+  int R;
+  long long g;           // current frame
+  int step, left, P;     // frame step, frames after the current one, tokens per frame
+  int pk;                // current tile starts at token pk of the current frame
+  const bf16* k0;        // token 0 of the current frame
   const bf16* v0;
-  const bf16* k1;          // token 0 of the next frame (the current one if none)
+  const bf16* k1;        // token 0 of the next frame (the current one if none)
   const bf16* v1;
 
-  __device__ __forceinline__ void frame_bases(int sl, const bf16*& kb, const bf16*& vb) const {
-    const long long g = branch_frame(branch, f, nswa, p->dil, sl);
-    kb = uni(key_frame_ptr<bf16, D>(static_cast<const bf16*>(p->k), static_cast<const bf16*>(p->ring_k), *p, b, h, g));
-    vb = uni(key_frame_ptr<bf16, D>(static_cast<const bf16*>(p->v), static_cast<const bf16*>(p->ring_v), *p, b, h, g));
+  __device__ __forceinline__ void frame_ptrs(long long gg, const bf16*& kb, const bf16*& vb) const {
+    if constexpr (!kRing) {
+      const size_t off = size_t(gg) * fstride;
+      kb = uni(kmain + off);
+      vb = uni(vmain + off);
+    } else {
+      if (gg == f0) {
+        kb = kmain;
+        vb = vmain;
+      } else {
+        const size_t off = size_t(unsigned(gg) % unsigned(R)) * fstride;
+        kb = uni(kring + off);
+        vb = uni(vring + off);
+      }
+    }
   }
-  __device__ __forceinline__ void start() {
-    slot = 0;
+  __device__ __forceinline__ void start(long long g_first, int step_, int nframes) {
+    g = g_first;
+    step = step_;
+    left = nframes - 1;
     pk = 0;
-    if (nframes > 0) frame_bases(0, k0, v0);
-    if (nframes > 1) frame_bases(1, k1, v1);
+    if (nframes > 0) frame_ptrs(g, k0, v0);
+    if (nframes > 1) frame_ptrs(g + step, k1, v1);
     else {
       k1 = k0;
       v1 = v0;
@@ -102,24 +125,48 @@ struct KeyStream {
   }
   __device__ __forceinline__ void advance() {
     pk += KT;
-    if (pk >= p->P) {
-      pk -= p->P;
-      ++slot;
+    if (pk >= P) {
+      pk -= P;
+      g += step;
+      --left;
       k0 = k1;
       v0 = v1;
-      if (slot + 1 < nframes) frame_bases(slot + 1, k1, v1);
+      if (left > 0) frame_ptrs(g + step, k1, v1);
     }
   }
 };
 
+// Buffer resource over [base, base + bytes): 32-bit lane offsets on a scalar base.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+
 // Direct global -> LDS copy of the current tile: wave w moves rows 16w .. 16w+15,
 // four rows (1 KB) per instruction; lane i lands at chunk position i%16 of row
-// 16w + 4j + i/16 and so loads the chunk that the swizzle puts there. Rows past
-// the end of the sequence re-read the last valid row (finite data; their scores
-// are masked, so they contribute exactly zero).
-__device__ __forceinline__ void issue_tile(Tile& Kd, Tile& Vd, const KeyStream& ks, int kleft, int wave, int lane) {
-  const size_t ts = size_t(ks.p->H) * D;
-  const int split = ks.p->P - ks.pk;
+// 16w + 4j + i/16 and so loads the chunk that the swizzle puts there. A tile
+// inside one frame (the common case) loads through buffer resources with the
+// precomputed lane offsets `off` (no per-lane address arithmetic); a tile
+// across a frame boundary or past the end of the sequence computes each lane's
+// row, and rows past the end re-read the last valid row (finite data; their
+// scores are masked, so they contribute exactly zero).
+template <bool kRing>
+__device__ __forceinline__ void issue_tile(Tile& Kd, Tile& Vd, const KeyStream<kRing>& ks, int kleft,
+                                           const unsigned (&off)[4], size_t ts, int wave, int lane) {
+  if (ks.pk + KT <= ks.P && kleft >= KT) {
+    const unsigned bytes = unsigned(KT * ts * sizeof(bf16));
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(ks.k0 + size_t(ks.pk) * ts, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(ks.v0 + size_t(ks.pk) * ts, bytes);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r0 = 16 * wave + 4 * j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(&Kd.row[r0][0]), 16,
+                                               off[j], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(&Vd.row[r0][0]), 16,
+                                               off[j], 0, 0, 0);
+    }
+    return;
+  }
+  const int split = ks.P - ks.pk;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r0 = 16 * wave + 4 * j;
@@ -137,7 +184,6 @@ __device__ __forceinline__ void issue_tile(Tile& Kd, Tile& Vd, const KeyStream& 
 }
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
-
 // 8 consecutive d values (chunk c) of key row r
 __device__ __forceinline__ bf16x8 ld_chunk(const Tile& t, int r, int c) {
   const uint4 u = t.row[r][swz(r, c)];
@@ -178,7 +224,7 @@ __device__ __forceinline__ void load4(const float* p, float* v) {
   for (int e = 0; e < 4; ++e) v[e] = x[e];
 }
 
-template <typename Tout>
+template <typename Tout, bool kRing>
 __global__ void __launch_bounds__(NT, 2)
 attn_mfma_kernel(AttnParams p) {
   __shared__ Smem sm;
@@ -219,6 +265,35 @@ attn_mfma_kernel(AttnParams p) {
     }
   }
 
+  // direct-load lane offsets of a tile inside one frame: row 16w + 4j + lane/16,
+  // source chunk (lane%16) ^ (row%16)
+  const size_t ts = HD;   // token stride (elements)
+  unsigned off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 16 * wave + 4 * j + (lane >> 4);
+    off[j] = unsigned(row) * unsigned(ts * sizeof(bf16)) + unsigned(swz(row, lane & 15)) * 16u;
+  }
+  KeyStream<kRing> kst;
+  kst.fstride = size_t(p.P) * HD;
+  kst.f0 = p.f0;
+  kst.R = p.R;
+  kst.P = p.P;
+  if constexpr (!kRing) {
+    const size_t o = size_t(b) * p.T * kst.fstride + size_t(h) * D;
+    kst.kmain = uni(static_cast<const bf16*>(p.k) + o);
+    kst.vmain = uni(static_cast<const bf16*>(p.v) + o);
+    kst.kring = kst.kmain;
+    kst.vring = kst.vmain;
+  } else {
+    const size_t o = size_t(b) * kst.fstride + size_t(h) * D;
+    const size_t orr = size_t(b) * p.R * kst.fstride + size_t(h) * D;
+    kst.kmain = uni(static_cast<const bf16*>(p.k) + o);
+    kst.vmain = uni(static_cast<const bf16*>(p.v) + o);
+    kst.kring = uni(static_cast<const bf16*>(p.ring_k) + orr);
+    kst.vring = uni(static_cast<const bf16*>(p.ring_v) + orr);
+  }
+
   const float c = p.scale_log2;
   const int nswa = swa_count(f, p.W);
   const int ndswa = dswa_count(f, p.dil, p.taps);
@@ -238,18 +313,21 @@ attn_mfma_kernel(AttnParams p) {
         for (int r = 0; r < 16; ++r) acc[rb][db][r] = 0.f;
     }
 
-    KeyStream ks{&p, b, h, branch, nswa, nframes, f};
-    ks.start();
+    KeyStream<kRing> ks = kst;
+    ks.start(branch == 0 ? f - nswa + 1 : f - p.dil, branch == 0 ? 1 : -p.dil, nframes);
     __syncthreads();   // the previous branch's last tile is no longer read
-    if (ntiles > 0) issue_tile(sm.K[0], sm.V[0], ks, int(nk < KT ? nk : KT), wave, lane);
+    auto kleft_of = [&](int t) {
+      const long long left = nk - (long long)t * KT;
+      return int(left < KT ? (left > 0 ? left : 0) : KT);
+    };
+    if (ntiles > 0) issue_tile(sm.K[0], sm.V[0], ks, kleft_of(0), off, ts, wave, lane);
     for (int t = 0; t < ntiles; ++t) {
       const int buf = t & 1;
       wait_vmem();
       __syncthreads();   // tile t is in LDS; nobody reads buffer buf^1 any more
       if (t + 1 < ntiles) {
         ks.advance();
-        const long long left = nk - (long long)(t + 1) * KT;
-        issue_tile(sm.K[buf ^ 1], sm.V[buf ^ 1], ks, int(left < KT ? left : KT), wave, lane);
+        issue_tile(sm.K[buf ^ 1], sm.V[buf ^ 1], ks, kleft_of(t + 1), off, ts, wave, lane);
       }
 
       if (wave_active) {
@@ -380,7 +458,10 @@ hipError_t launch_t(const AttnParams& p, hipStream_t st) {
   const long long grid = (total + kXcds - 1) / kXcds * kXcds;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_mfma_kernel<Tout>), dim3(unsigned(grid)), dim3(NT), 0, st, p);
+  if (p.R == 0)
+    hipLaunchKernelGGL((attn_mfma_kernel<Tout, false>), dim3(unsigned(grid)), dim3(NT), 0, st, p);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<Tout, true>), dim3(unsigned(grid)), dim3(NT), 0, st, p);
   return hipGetLastError();
 }
 
