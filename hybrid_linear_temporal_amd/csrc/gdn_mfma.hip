@@ -13,24 +13,25 @@
 //   S <- gamma_C S + U^T diag(gamma_C / gamma) K^.
 //
 // Kernel 1, gdn_prep_mfma: one workgroup per (chunk, head, batch row), fully
-// parallel. Gram matrices K K^T and Q K^T on raw bf16 inputs (exact products,
-// fp32 sums) with the norms and gates applied in fp32; T by blocked forward
-// substitution in fp32 (16x16 diagonal blocks per wave, then the off-diagonal
-// blocks level by level); W^T and U' on MFMA with the raw K, V read transposed
-// from LDS (ds_read_b64_tr_b16). Writes one record per chunk.
+// parallel, two per CU. Gram matrices K K^T and Q K^T on raw bf16 inputs
+// (exact products, fp32 sums) with the norms and gates applied in fp32; T by
+// blocked forward substitution in fp32 (16x16 diagonal blocks per wave, then
+// the off-diagonal blocks level by level); W^T and U' on MFMA with the raw K,
+// V read transposed from LDS (ds_read_b64_tr_b16). Writes one record per chunk.
 //
-// Kernel 2, gdn_chain_mfma: one single-wave workgroup per (16 value channels,
-// head, batch row), chunks in order; the 8 workgroups of a head sit on one XCD
-// and share its L2 (one wave per CU keeps the per-CU LDS traffic to one copy of
-// the chunk's shared operands). Each wave keeps
-// its slice of S^T (128 x 16, fp32) in MFMA accumulator layout for the whole
-// sequence. Its bf16 copy is the B operand of W S^T and Q S^T directly, because
-// the reduction (d_k) index of an MFMA may be permuted as long as both operands
-// agree; the A operands are read from LDS in that permuted order. The same holds
-// for U (C layout) as B operand of Aqk U and of the state update, so the chain
-// never moves S or U through LDS. Each chunk's operands (-W, q, k, Aqk, the
-// workgroup's U' rows, per-token scales) stream into a second LDS buffer by
-// direct global -> LDS loads while the current chunk computes.
+// Kernel 2, gdn_chain_mfma: one workgroup per (16 value channels, head, batch
+// row), chunks in order; the 8 workgroups of a head sit on one XCD and share
+// its L2. Four waves, one per SIMD: the state wave keeps the slice of S^T
+// (128 x 16, fp32) in MFMA accumulator layout for the whole sequence and runs
+// U = U' - W S^T and the state update; the output wave recomputes U from the
+// same operands and writes O; the loader wave streams the next chunk's
+// operands into the second LDS buffer; the prefetch wave pulls later chunks
+// into L2. The bf16 copy of S^T, published in LDS by the state wave, is the B
+// operand of W S^T and the A operand of S q^T directly, because the 16x16x32
+// A and B layouts coincide and the reduction (d_k) index of an MFMA may be
+// permuted as long as both operands agree; the other operands are read from
+// LDS in that permuted order. The same holds for U (C layout) as operand of
+// the state update and of U^T Aqk^T, so S and U are never transposed.
 #include "hlta_device.h"
 #include "hlta_internal.h"
 #include "hlta_launch.h"
@@ -529,12 +530,16 @@ __device__ __forceinline__ void issue_chunk(ChainBuf& buf, const DmaPlan& pl, co
   if (lane < 33) dma16r(rr, 16u * unsigned(lane), unsigned(R::SQ), &buf.sc[0]);
 }
 
-// Workgroup barrier that orders LDS accesses only: global stores still in
-// flight (the outputs) and L2 prefetches are not waited for.
+// Workgroup barrier for LDS accesses made by the waves' own instructions:
+// they complete (lgkmcnt(0)) before it, and the compiler moves no memory
+// access across it. Direct loads into LDS are waited for explicitly by the
+// loader (a release fence here would also make the prefetch wave wait for its
+// L2 prefetches every chunk), and global stores in flight are not waited for.
 __device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  asm volatile("" ::: "memory");
 }
 
 // L2 prefetch of one chunk's operands: the record (325 lines of 128 B up to

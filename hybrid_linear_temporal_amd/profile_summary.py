@@ -22,12 +22,18 @@ def summarise(path: str) -> str:
         for pre in ("hlta::(anonymous namespace)::", "void "):
             short = short.replace(pre, "")
         short = short.split("(")[0]
-        for mangled, plain in (("16attn_mfma_kernelIDF16b", "attn_mfma_kernel<bf16>"),
+        for mangled, plain in (("16attn_mfma_kernelIDF16bLb1", "attn_mfma_kernel<bf16, ring>"),
+                               ("16attn_mfma_kernelIfLb1", "attn_mfma_kernel<float, ring>"),
+                               ("16attn_mfma_kernelIDF16b", "attn_mfma_kernel<bf16>"),
                                ("16attn_mfma_kernelIf", "attn_mfma_kernel<float>"),
                                ("14gdn_chain_mfmaIDF16b", "gdn_chain_mfma<bf16>"),
                                ("14gdn_chain_mfmaIf", "gdn_chain_mfma<float>")):
             if mangled in short:
                 short = plain
+                break
+        if short.startswith("attn_mfma_kernel<bool"):
+            # rocprofv3 demangles the stream-mode (ring) instantiation this way
+            short = "attn_mfma_kernel<ring>"
         wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
         grid = (int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])) // max(wg, 1)
         agg[(short, grid)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
