@@ -341,29 +341,38 @@ attn_mfma_kernel(AttnParams p) {
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[rb][kb][r] = 0.f;
+        // all 16 K operands are read before the first product so the reads
+        // pipeline (one at a time, each would wait out the LDS latency)
+        bf16x8 ka[8][2];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) ka[ks][kb] = ld_chunk(Kt, kb * 32 + l32, 2 * ks + hl);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
-            const bf16x8 a = ld_chunk(Kt, kb * 32 + l32, 2 * ks + hl);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
-              s[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qv[rb][ks], s[rb][kb], 0, 0, 0);
+              s[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][kb], qv[rb][ks], s[rb][kb], 0, 0, 0);
           }
         }
+
         // mask keys past the end (last tile only); value r of block kb is key
         // kb*32 + (r/4)*8 + 4*hl + r%4 of the tile
         const long long kleft = nk - (long long)t * KT;
         if (kleft < KT) {
+          // compare the lane-independent part of the key index with kleft - 4*hl
+          // (one register, instead of 32 hoisted key indices)
+          const int kthr = int(kleft) - 4 * hl;
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int key = kb * 32 + (r >> 2) * 8 + 4 * hl + (r & 3);
-                if (key >= kleft) s[rb][kb][r] = -INFINITY;
-              }
+              for (int r = 0; r < 16; ++r)
+                if (kb * 32 + (r >> 2) * 8 + (r & 3) >= kthr) s[rb][kb][r] = -INFINITY;
         }
         bf16x8 pv[RB][2][2];
 #pragma unroll
@@ -396,6 +405,15 @@ attn_mfma_kernel(AttnParams p) {
               pv[rb][kb][r >> 3][r & 7] = static_cast<bf16>(e);
             }
         }
+        // V^T operands, all read before the first product
+        bf16x8 va[4][2][2];
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2) va[db][kb][m2] = ld_vt(Vt, kb * 32 + 16 * m2 + 4 * hl, db * 32 + (l32 & 16), l16);
+        __builtin_amdgcn_sched_barrier(0);
         // O^T += V^T P^T: A operand lane = d row db*32 + l32, keys of slot i:
         // kb*32 + 16*m2 + 8*(i/4) + 4*hl + i%4
 #pragma unroll
@@ -404,10 +422,9 @@ attn_mfma_kernel(AttnParams p) {
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int m2 = 0; m2 < 2; ++m2) {
-              const bf16x8 a = ld_vt(Vt, kb * 32 + 16 * m2 + 4 * hl, db * 32 + (l32 & 16), l16);
 #pragma unroll
               for (int rb = 0; rb < RB; ++rb)
-                acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pv[rb][kb][m2], acc[rb][db], 0, 0, 0);
+                acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][kb][m2], pv[rb][kb][m2], acc[rb][db], 0, 0, 0);
             }
       }
     }

@@ -58,6 +58,10 @@ BF16_CASES = [
           gdn_chunk=32, dtype="bf16", seed=2102),
     small("bf16_d128_c16", B=1, H=2, T=6, P=64, d=128, swa_frames=3, dswa_dilation=2, dswa_taps=2,
           gdn_chunk=16, dtype="bf16", seed=2103),
+    # 15 (batch, head) pairs: not a multiple of the 8 XCDs the state pass spreads heads over;
+    # 500 tokens = 7 full chunks and a ragged one
+    small("bf16_d128_c64_bh15", B=3, H=5, T=5, P=100, d=128, swa_frames=2, dswa_dilation=2, dswa_taps=2,
+          gdn_chunk=64, dtype="bf16", seed=2104),
 ]
 
 
