@@ -184,6 +184,29 @@ __device__ __forceinline__ void issue_tile(Tile& Kd, Tile& Vd, const KeyStream<k
 }
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+// Lanes l and l ^ 32 combined without LDS: v_permlane32_swap on two copies of
+// x leaves (x[l], x[l^32]) in lanes below 32 and (x[l^32], x[l]) above (lane
+// layout checked on the GPU). The results are copied out of the returned
+// vector before the bit casts: casting the vector elements in place reads
+// element 0 twice with this compiler.
+__device__ __forceinline__ void pair_xor32(float x, float& a, float& b) {
+  const unsigned xa = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(xa, xa, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  float a, b;
+  pair_xor32(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  float a, b;
+  pair_xor32(x, a, b);
+  return a + b;
+}
+
 // 8 consecutive d values (chunk c) of key row r
 __device__ __forceinline__ bf16x8 ld_chunk(const Tile& t, int r, int c) {
   const uint4 u = t.row[r][swz(r, c)];
@@ -359,6 +382,15 @@ attn_mfma_kernel(AttnParams p) {
           }
         }
 
+        // V^T operands, read now so the softmax below hides their latency
+        bf16x8 va[4][2][2];
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2) va[db][kb][m2] = ld_vt(Vt, kb * 32 + 16 * m2 + 4 * hl, db * 32 + (l32 & 16), l16);
+        __builtin_amdgcn_sched_barrier(0);
         // mask keys past the end (last tile only); value r of block kb is key
         // kb*32 + (r/4)*8 + 4*hl + r%4 of the tile
         const long long kleft = nk - (long long)t * KT;
@@ -382,7 +414,7 @@ attn_mfma_kernel(AttnParams p) {
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[rb][kb][r]);
-          mt = fmaxf(mt, __shfl_xor(mt, 32)) * c;
+          mt = max_xor32(mt) * c;
           // lazy rescale: only when some lane's tile max passes its running max by kLazy
           const bool raise = mt > m[rb] + kLazy;
           if (__ballot(raise) != 0) {
@@ -405,15 +437,6 @@ attn_mfma_kernel(AttnParams p) {
               pv[rb][kb][r >> 3][r & 7] = static_cast<bf16>(e);
             }
         }
-        // V^T operands, all read before the first product
-        bf16x8 va[4][2][2];
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int m2 = 0; m2 < 2; ++m2) va[db][kb][m2] = ld_vt(Vt, kb * 32 + 16 * m2 + 4 * hl, db * 32 + (l32 & 16), l16);
-        __builtin_amdgcn_sched_barrier(0);
         // O^T += V^T P^T: A operand lane = d row db*32 + l32, keys of slot i:
         // kb*32 + 16*m2 + 8*(i/4) + 4*hl + i%4
 #pragma unroll
@@ -440,7 +463,7 @@ attn_mfma_kernel(AttnParams p) {
       for (int rb = 0; rb < RB; ++rb) {
         const int qrow = wrow0 + rb * 32 + l32;
         const bool row_ok = qrow < p.P;
-        const float ltot = lsum[rb] + __shfl_xor(lsum[rb], 32);
+        const float ltot = sum_xor32(lsum[rb]);
         const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
         const size_t qbase = fbase + size_t(qrow) * HD;
 #pragma unroll
