@@ -1,5 +1,5 @@
 // Generic SWA + DSWA softmax-attention kernel (fp32 arithmetic, any d in
-// {32, 64, 128}, float32 or bf16 inputs) with the mix fused in its epilogue.
+// {32, 64, 128}, float32 or bf16 inputs).
 //
 // Exact attention over every legal (query, key) pair, computed tile by tile
 // with a running max and sum so the score matrix never leaves the chip
@@ -50,8 +50,6 @@ attn_generic_kernel(AttnParams p) {
 #pragma unroll
   for (int i = 0; i < DP; ++i) qr[i] = row_ok ? to_f32(q[qoff + i]) * p.scale_log2 : 0.f;
 
-  float swa_r[DP];
-  float dswa_r[DP];
   const int nswa = swa_count(f, p.W);
   const int ndswa = dswa_count(f, p.dil, p.taps);
 
@@ -110,22 +108,10 @@ attn_generic_kernel(AttnParams p) {
 
     const float inv = l > 0.f ? 1.f / l : 0.f;
     Tout* out = static_cast<Tout*>(branch == 0 ? p.o_swa : p.o_dswa);
-    float* keep = branch == 0 ? swa_r : dswa_r;
+    if (row_ok) {
 #pragma unroll
-    for (int i = 0; i < DP; ++i) {
-      const Tout o = from_f32<Tout>(acc[i] * inv);
-      keep[i] = to_f32(o);
-      if (row_ok) out[qoff + i] = o;
+      for (int i = 0; i < DP; ++i) out[qoff + i] = from_f32<Tout>(acc[i] * inv);
     }
-  }
-
-  if (row_ok) {
-    const float w0 = p.mix_w[h * 3 + 0], w1 = p.mix_w[h * 3 + 1], w2 = p.mix_w[h * 3 + 2];
-    const Tout* og = static_cast<const Tout*>(p.o_gdn);
-    Tout* om = static_cast<Tout*>(p.o_mix);
-#pragma unroll
-    for (int i = 0; i < DP; ++i)
-      om[qoff + i] = from_f32<Tout>(w0 * swa_r[i] + w1 * dswa_r[i] + w2 * to_f32(og[qoff + i]));
   }
 }
 

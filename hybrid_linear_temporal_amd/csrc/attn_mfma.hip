@@ -1,5 +1,4 @@
-// SWA + DSWA softmax attention with bf16 MFMA on gfx950 (d = 128), with the
-// mix fused in the epilogue.
+// SWA + DSWA softmax attention with bf16 MFMA on gfx950 (d = 128).
 //
 // What is computed: for every query of latent frame f, exact softmax attention
 // over all keys of its frame set (SWA: frames f-W+1 .. f; DSWA: frames
@@ -252,16 +251,6 @@ __device__ __forceinline__ void store4(float* p, const float* v) {
   f32x4 x = {v[0], v[1], v[2], v[3]};
   *reinterpret_cast<f32x4*>(p) = x;
 }
-__device__ __forceinline__ void load4(const bf16* p, float* v) {
-  const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) v[e] = static_cast<float>(x[e]);
-}
-__device__ __forceinline__ void load4(const float* p, float* v) {
-  const f32x4 x = *reinterpret_cast<const f32x4*>(p);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) v[e] = x[e];
-}
 
 template <typename Tout, bool kRing>
 __global__ void __launch_bounds__(NT, 2)
@@ -476,40 +465,26 @@ attn_mfma_kernel(AttnParams p) {
       if (t + 1 < ntiles) tile(t + 1, sK1, sV1, sK0, sV0);
     }
 
-    // ---- epilogue of this branch: normalise, store; the mix after DSWA ----
+    // ---- epilogue of this branch: normalise, store ----
     if (wave_active) {
       Tout* out = static_cast<Tout*>(branch == 0 ? p.o_swa : p.o_dswa);
-      const Tout* out_swa = static_cast<const Tout*>(p.o_swa);
-      const Tout* og = static_cast<const Tout*>(p.o_gdn);
-      Tout* om = static_cast<Tout*>(p.o_mix);
-      const float w0 = p.mix_w[h * 3 + 0], w1 = p.mix_w[h * 3 + 1], w2 = p.mix_w[h * 3 + 2];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const int qrow = wrow0 + rb * 32 + l32;
-        const bool row_ok = qrow < p.P;
         const float ltot = sum_xor32(lsum[rb]);
         const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-        const size_t qbase = fbase + size_t(qrow) * HD;
+        if (qrow < p.P) {
+          const size_t qbase = fbase + size_t(qrow) * HD;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+          for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int dcol = db * 32 + j * 8 + 4 * hl;   // 4 consecutive d values r = 4j .. 4j+3
-            float o4[4];
+            for (int j = 0; j < 4; ++j) {
+              float o4[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o4[e] = stored_value<Tout>(acc[rb][db][4 * j + e] * inv);
-            if (!row_ok) continue;
-            store4(out + qbase + dcol, o4);
-            if (branch == 1) {
-              // the mix reads back this lane's own SWA store and the GDN output
-              float s4[4], g4[4], m4[4];
-              load4(out_swa + qbase + dcol, s4);
-              load4(og + qbase + dcol, g4);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) m4[e] = w0 * s4[e] + w1 * o4[e] + w2 * g4[e];
-              store4(om + qbase + dcol, m4);
+              for (int e = 0; e < 4; ++e) o4[e] = acc[rb][db][4 * j + e] * inv;
+              store4(out + qbase + db * 32 + j * 8 + 4 * hl, o4);   // 4 consecutive d values r = 4j .. 4j+3
             }
-          }
+        }
       }
     }
   }

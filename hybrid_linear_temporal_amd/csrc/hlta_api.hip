@@ -1,6 +1,6 @@
 // C-ABI entry points that launch work: hlta_fwd, hlta_gdn_fwd, hlta_attn_fwd,
 // hlta_stream_load_prefix, hlta_step_frame. Validation happens on the host before any launch; the
-// library allocates nothing (scratch is the caller's workspace).
+// library allocates no device memory (scratch is the caller's workspace).
 #include <string>
 
 #include "hlta_device.h"
@@ -73,9 +73,7 @@ hlta_status run_gdn(const hlta_config* cfg, const Plan& plan, const void* q, con
   return HLTA_OK;
 }
 
-hlta_status run_attn(const hlta_config* cfg, const Plan& plan, const void* o_gdn, AttnParams attn,
-                     hipStream_t st) {
-  attn.o_gdn = o_gdn;
+hlta_status run_attn(const hlta_config* cfg, const Plan& plan, AttnParams attn, hipStream_t st) {
   attn.scale_log2 = plan.scale * kLog2e;
   hipError_t e = plan.attn == Impl::Mfma
                      ? launch_attn_mfma(attn, cfg->out_dtype, st)
@@ -84,24 +82,35 @@ hlta_status run_attn(const hlta_config* cfg, const Plan& plan, const void* o_gdn
   return HLTA_OK;
 }
 
-// GDN over L tokens per row, then SWA/DSWA + mix. attn.* query fields set by caller.
-hlta_status run_layer(const hlta_config* cfg, const Plan& plan, const void* q, const void* k, const void* v,
-                      const float* a, const float* b, const float* S0, float* S_out, void* o_gdn,
-                      void* workspace, AttnParams attn, hipStream_t st) {
-  HLTA_TRY(run_gdn(cfg, plan, q, k, v, a, b, S0, S_out, o_gdn, workspace, st));
-  return run_attn(cfg, plan, o_gdn, attn, st);
+hlta_status run_mix(const hlta_config* cfg, const Plan& plan, const void* o_swa, const void* o_dswa,
+                    const void* o_gdn, void* o_mix, const float* mix_w, hipStream_t st) {
+  hipError_t e = launch_mix(o_swa, o_dswa, o_gdn, o_mix, mix_w, (long long)cfg->B * plan.L, cfg->H, cfg->d,
+                            cfg->out_dtype, st);
+  if (e != hipSuccess) return hip_fail(e, "mix launch");
+  return HLTA_OK;
 }
 
-AttnParams full_attn_params(const hlta_config* cfg, const void* q, const void* k, const void* v,
-                            const float* mix_w, void* o_swa, void* o_dswa, void* o_mix) {
+// One layer: the memory branch (GDN over L tokens per row), the softmax
+// branches, then the per-head mix of the three stored outputs, in order on st.
+// (Running the memory branch on a second stream gains nothing here: its state
+// pass needs one compute unit per workgroup for its LDS buffers, so it cannot
+// share the chip with the attention branches.) attn.* query fields set by caller.
+hlta_status run_layer(const hlta_config* cfg, const Plan& plan, const void* q, const void* k, const void* v,
+                      const float* a, const float* b, const float* S0, float* S_out, void* o_gdn,
+                      const float* mix_w, void* o_mix, void* workspace, AttnParams attn, hipStream_t st) {
+  HLTA_TRY(run_gdn(cfg, plan, q, k, v, a, b, S0, S_out, o_gdn, workspace, st));
+  HLTA_TRY(run_attn(cfg, plan, attn, st));
+  return run_mix(cfg, plan, attn.o_swa, attn.o_dswa, o_gdn, o_mix, mix_w, st);
+}
+
+AttnParams full_attn_params(const hlta_config* cfg, const void* q, const void* k, const void* v, void* o_swa,
+                            void* o_dswa) {
   AttnParams at{};
   at.q = q;
   at.k = k;
   at.v = v;
   at.o_swa = o_swa;
   at.o_dswa = o_dswa;
-  at.o_mix = o_mix;
-  at.mix_w = mix_w;
   at.B = cfg->B;
   at.H = cfg->H;
   at.T = cfg->T;
@@ -154,8 +163,8 @@ hlta_status hlta_fwd(const hlta_config* cfg, const void* q, const void* k, const
   HLTA_TRY(need(v, "v"));
   HLTA_TRY(check_outputs(a, b, mix_w, o_swa, o_dswa, o_gdn, o_mix));
   HLTA_TRY(check_workspace(plan, workspace, ws_bytes));
-  AttnParams at = full_attn_params(cfg, q, k, v, mix_w, o_swa, o_dswa, o_mix);
-  return run_layer(cfg, plan, q, k, v, a, b, S0, S_out, o_gdn, workspace, at, st);
+  AttnParams at = full_attn_params(cfg, q, k, v, o_swa, o_dswa);
+  return run_layer(cfg, plan, q, k, v, a, b, S0, S_out, o_gdn, mix_w, o_mix, workspace, at, st);
 }
 
 hlta_status hlta_gdn_fwd(const hlta_config* cfg, const void* q, const void* k, const void* v, const float* a,
@@ -202,8 +211,10 @@ hlta_status hlta_attn_fwd(const hlta_config* cfg, const void* q, const void* k, 
   HLTA_TRY(need(o_swa, "o_swa"));
   HLTA_TRY(need(o_dswa, "o_dswa"));
   HLTA_TRY(need(o_mix, "o_mix"));
-  AttnParams at = full_attn_params(cfg, q, k, v, mix_w, o_swa, o_dswa, o_mix);
-  return run_attn(cfg, plan, o_gdn, at, static_cast<hipStream_t>(stream));
+  AttnParams at = full_attn_params(cfg, q, k, v, o_swa, o_dswa);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  HLTA_TRY(run_attn(cfg, plan, at, st));
+  return run_mix(cfg, plan, o_swa, o_dswa, o_gdn, o_mix, mix_w, st);
 }
 
 static hlta_status check_stream(const hlta_config* cfg, const hlta_stream_state* st) {
@@ -276,8 +287,6 @@ hlta_status hlta_step_frame(const hlta_config* cfg, hlta_stream_state* st, const
   at.ring_v = st->ring_v;
   at.o_swa = o_swa;
   at.o_dswa = o_dswa;
-  at.o_mix = o_mix;
-  at.mix_w = mix_w;
   at.B = cfg->B;
   at.H = cfg->H;
   at.T = 1;
@@ -287,8 +296,8 @@ hlta_status hlta_step_frame(const hlta_config* cfg, hlta_stream_state* st, const
   at.taps = cfg->dswa_taps;
   at.R = st->ring_frames;
   at.f0 = f;
-  HLTA_TRY(run_layer(cfg, plan, q_f, k_f, v_f, a_f, b_f, st->S, commit ? st->S : nullptr, o_gdn, workspace,
-                     at, s));
+  HLTA_TRY(run_layer(cfg, plan, q_f, k_f, v_f, a_f, b_f, st->S, commit ? st->S : nullptr, o_gdn, mix_w, o_mix,
+                     workspace, at, s));
   if (commit) {
     const long long frame_elems = (long long)cfg->P * cfg->H * cfg->d;
     const int elem = int(dtype_bytes(cfg->in_dtype));

@@ -21,7 +21,7 @@ template <typename T> __device__ __forceinline__ float stored_value(float x) {
   return to_f32(from_f32<T>(x));
 }
 
-// Parameters of the softmax branches (SWA + DSWA + fused mix epilogue).
+// Parameters of the softmax branches (SWA + DSWA).
 // Full mode (R == 0): queries and keys come from q, k, v of T frames.
 // Stream mode (R > 0): the call's single query frame is absolute frame f0;
 // its own K/V come from k, v; earlier frames g from ring slot g mod R.
@@ -31,11 +31,8 @@ struct AttnParams {
   const void* v;
   const void* ring_k;
   const void* ring_v;
-  const void* o_gdn;     // read by the mix epilogue (out dtype)
   void* o_swa;
   void* o_dswa;
-  void* o_mix;
-  const float* mix_w;    // [H, 3]
   int B, H, T, P;        // T = query frames of this call
   int W, dil, taps;
   int R;                 // ring frames (stream mode) or 0

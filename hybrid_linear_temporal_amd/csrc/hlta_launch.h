@@ -8,10 +8,14 @@
 
 namespace hlta {
 
-// SWA + DSWA + mix, fp32 arithmetic, any supported d and dtype.
+// SWA + DSWA, fp32 arithmetic, any supported d and dtype.
 hipError_t launch_attn_generic(const AttnParams& p, int d, int in_dt, int out_dt, hipStream_t st);
-// SWA + DSWA + mix with bf16 MFMA (bf16 inputs, d = 128).
+// SWA + DSWA with bf16 MFMA (bf16 inputs, d = 128).
 hipError_t launch_attn_mfma(const AttnParams& p, int out_dt, hipStream_t st);
+// o_mix = per-head weighted sum of the three stored branch outputs
+// ([ntok, H, d] each, out dtype), d a multiple of 8.
+hipError_t launch_mix(const void* o_swa, const void* o_dswa, const void* o_gdn, void* o_mix, const float* mix_w,
+                      long long ntok, int H, int d, int out_dt, hipStream_t st);
 
 // Gated delta rule, chunked form, fp32 arithmetic (any supported d, C, dtype).
 hipError_t launch_gdn_generic(const GdnParams& p, int d, int C, int in_dt, int out_dt, hipStream_t st);

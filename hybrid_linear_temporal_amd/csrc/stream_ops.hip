@@ -1,7 +1,8 @@
-// Ring-buffer copies of the streaming path: frame g of every rollout goes to
-// ring slot g mod R, so a step finds the K/V of past frames without the clip
-// being recomputed (Kairos article on zhichai.net, section 2.3, streaming
-// tokens).
+// Elementwise kernels around the branches: the per-head mix of the three
+// branch outputs, and the ring-buffer copies of the streaming path (frame g
+// of every rollout goes to ring slot g mod R, so a step finds the K/V of past
+// frames without the clip being recomputed; Kairos article on zhichai.net,
+// section 2.3, streaming tokens).
 #include "hlta_device.h"
 #include "hlta_launch.h"
 
@@ -25,7 +26,73 @@ ring_store_kernel(const uint4* src, long long src_frames, long long src_f0, uint
     d[i] = s[i];
 }
 
+// o_mix = w[h][0] o_swa + w[h][1] o_dswa + w[h][2] o_gdn, elementwise over the
+// stored branch outputs (Kairos abstract, point (2): the three branches are
+// mixed per head), with one fp32 rounding order for every caller:
+// fma(w2, gdn, fma(w1, dswa, w0 * swa)), then one rounding to the output type.
+// One thread per 8 consecutive values of one (token, head); 16-byte vectors.
+template <typename T>
+struct Vec8;
+template <>
+struct Vec8<bf16> {
+  uint4 u;
+  __device__ __forceinline__ void load(const bf16* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ float get(int i) const {
+    const bf16* e = reinterpret_cast<const bf16*>(&u);
+    return static_cast<float>(e[i]);
+  }
+  __device__ __forceinline__ void set(int i, float x) { reinterpret_cast<bf16*>(&u)[i] = static_cast<bf16>(x); }
+  __device__ __forceinline__ void store(bf16* p) const { *reinterpret_cast<uint4*>(p) = u; }
+};
+template <>
+struct Vec8<float> {
+  uint4 u[2];
+  __device__ __forceinline__ void load(const float* p) {
+    u[0] = reinterpret_cast<const uint4*>(p)[0];
+    u[1] = reinterpret_cast<const uint4*>(p)[1];
+  }
+  __device__ __forceinline__ float get(int i) const { return reinterpret_cast<const float*>(u)[i]; }
+  __device__ __forceinline__ void set(int i, float x) { reinterpret_cast<float*>(u)[i] = x; }
+  __device__ __forceinline__ void store(float* p) const {
+    reinterpret_cast<uint4*>(p)[0] = u[0];
+    reinterpret_cast<uint4*>(p)[1] = u[1];
+  }
+};
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+mix_kernel(const T* swa, const T* dswa, const T* gdn, T* mix, const float* w, long long n8, int H, int d8) {
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < n8; i += (long long)gridDim.x * kThreads) {
+    const int h = int((i / d8) % H);
+    const float w0 = w[3 * h], w1 = w[3 * h + 1], w2 = w[3 * h + 2];
+    Vec8<T> a, b, g, o;
+    a.load(swa + 8 * i);
+    b.load(dswa + 8 * i);
+    g.load(gdn + 8 * i);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o.set(e, fmaf(w2, g.get(e), fmaf(w1, b.get(e), w0 * a.get(e))));
+    o.store(mix + 8 * i);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_mix(const void* o_swa, const void* o_dswa, const void* o_gdn, void* o_mix, const float* mix_w,
+                      long long ntok, int H, int d, int out_dt, hipStream_t st) {
+  const long long n8 = ntok * H * (d / 8);
+  if (n8 <= 0) return hipSuccess;
+  long long blocks = (n8 + kThreads - 1) / kThreads;
+  if (blocks > 8192) blocks = 8192;
+  if (out_dt == HLTA_BF16)
+    hipLaunchKernelGGL(mix_kernel<bf16>, dim3(unsigned(blocks)), dim3(kThreads), 0, st,
+                       static_cast<const bf16*>(o_swa), static_cast<const bf16*>(o_dswa),
+                       static_cast<const bf16*>(o_gdn), static_cast<bf16*>(o_mix), mix_w, n8, H, d / 8);
+  else
+    hipLaunchKernelGGL(mix_kernel<float>, dim3(unsigned(blocks)), dim3(kThreads), 0, st,
+                       static_cast<const float*>(o_swa), static_cast<const float*>(o_dswa),
+                       static_cast<const float*>(o_gdn), static_cast<float*>(o_mix), mix_w, n8, H, d / 8);
+  return hipGetLastError();
+}
 
 hipError_t launch_ring_store(const void* src, long long src_frames, long long src_f0, void* ring, int R,
                              long long first_frame, long long n_frames, int B, long long frame_elems,

@@ -105,6 +105,63 @@ def test_mix_is_weighted_sum_of_stored_branches():
     assert np.all(np.abs(g - mix) <= 2.0 ** -8 * np.abs(mix) + 1e-6)
 
 
+def test_split_calls_equal_fwd():
+    """hlta_gdn_fwd then hlta_attn_fwd on one stream equal hlta_fwd bit for bit."""
+    for wl in (BF16_CASES[0], F32_CASES[0]):
+        x = I.make_clip(wl)
+        ref = run_gpu(wl, x)
+        cfg = H.make_config(wl)
+        dev = H.to_device(x, wl.dtype)
+        out = H.alloc_outputs(cfg, wl.L)
+        S_out = torch.empty((wl.B, wl.H, wl.d, wl.d), device="cuda")
+        ws = H.alloc_workspace(H.hlta_fwd_workspace_bytes(cfg))
+        H.hlta_gdn_fwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], out["o_gdn"], S_out=S_out,
+                       workspace=ws)
+        H.hlta_attn_fwd(cfg, dev["q"], dev["k"], dev["v"], dev["w"], out["o_gdn"], out)
+        torch.cuda.synchronize()
+        for n in ("o_swa", "o_dswa", "o_gdn", "o_mix"):
+            assert torch.equal(out[n], ref[n]), (wl.name, n)
+        assert torch.equal(S_out, ref["S_out"]), wl.name
+
+
+def test_fwd_graph_replays_match_eager():
+    """hlta_fwd captured in a HIP graph: every replay, with eager work and
+    synchronisation in between, equals the eager call bit for bit."""
+    wl = BF16_CASES[0]
+    x = I.make_clip(wl)
+    cfg = H.make_config(wl)
+    dev = H.to_device(x, wl.dtype)
+    ws = H.alloc_workspace(H.hlta_fwd_workspace_bytes(cfg))
+    out = H.alloc_outputs(cfg, wl.L)
+    S_out = torch.empty((wl.B, wl.H, wl.d, wl.d), device="cuda")
+
+    def call():
+        H.hlta_fwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], out=out, S_out=S_out,
+                   workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    ref = {n: t.clone() for n, t in out.items()}
+    ref["S_out"] = S_out.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        for t in out.values():
+            t.fill_(float("nan"))
+        S_out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n, t in out.items():
+            assert torch.equal(t, ref[n]), (rep, n)
+        assert torch.equal(S_out, ref["S_out"]), rep
+
+
 def test_deterministic():
     wl = BF16_CASES[0]
     x = I.make_clip(wl)
