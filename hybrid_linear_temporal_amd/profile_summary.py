@@ -27,7 +27,9 @@ def summarise(path: str) -> str:
                                ("16attn_mfma_kernelIDF16b", "attn_mfma_kernel<bf16>"),
                                ("16attn_mfma_kernelIf", "attn_mfma_kernel<float>"),
                                ("14gdn_chain_mfmaIDF16b", "gdn_chain_mfma<bf16>"),
-                               ("14gdn_chain_mfmaIf", "gdn_chain_mfma<float>")):
+                               ("14gdn_chain_mfmaIf", "gdn_chain_mfma<float>"),
+                               ("10mix_kernelIDF16b", "mix_kernel<bf16>"),
+                               ("10mix_kernelIf", "mix_kernel<float>")):
             if mangled in short:
                 short = plain
                 break
