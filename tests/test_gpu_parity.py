@@ -191,3 +191,32 @@ def test_chunk_size_invariance():
     outs = [to64(run_gpu(wl, x, gdn_chunk=c)["o_gdn"]) for c in (16, 32, 64)]
     for o in outs[1:]:
         assert O.rel_l2(o, outs[0]) < 1e-5
+
+
+def _bf16_exact(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).bfloat16().float().numpy()
+
+
+@pytest.mark.parametrize("side", ["above", "below"])
+def test_scores_far_from_zero(side):
+    """Rows whose largest scaled score lies far above (peaked queries) or far
+    below (every key opposite its query) zero, beyond the range the attention
+    kernels take exponentials over in one pass."""
+    wl = BF16_CASES[1]
+    x = I.make_clip(wl)
+    if side == "above":
+        x["q"] = _bf16_exact(x["q"] * 1000.0)
+    else:
+        rng = np.random.default_rng(77)
+        d = wl.d
+        u = rng.standard_normal((wl.H, d))
+        u /= np.linalg.norm(u, axis=-1, keepdims=True)
+        noise = rng.standard_normal(x["k"].shape)
+        noise /= np.linalg.norm(noise, axis=-1, keepdims=True)
+        kk = -0.9 * u[None, None] + 0.1 * noise
+        kk /= np.linalg.norm(kk, axis=-1, keepdims=True)
+        x["q"] = _bf16_exact(np.broadcast_to(300.0 * u[None, None], x["q"].shape))
+        x["k"] = _bf16_exact(kk)
+    ref = run_oracle(wl, x)
+    got = run_gpu(wl, x)
+    compare(got, ref, TOL["bf16"], label=f"scores {side}")
