@@ -160,12 +160,57 @@ def stream_leg(steps, warmup=4, distinct=4):
     per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
     total = sum(per_step)
     pairs = (wl.swa_frames + wl.dswa_taps) * P * P * wl.B * wl.H   # every tap is valid after the prefix
-    return {"workload": wl.name, "steps": steps, "tokens_per_step": wl.B * P,
-            "tokens_per_s": wl.B * P * steps / (total * 1e-3), "ms_per_step": total / steps,
-            "ms_per_step_first8": sum(per_step[:8]) / min(8, steps),
-            "ms_per_step_last8": sum(per_step[-8:]) / min(8, steps),
-            "attn_tflops_per_step": 4 * wl.d * pairs / 1e12,
-            "inputs": "torch-seeded GPU draws, same recipe; 4 distinct frames cycled"}
+    res = {"workload": wl.name, "steps": steps, "tokens_per_step": wl.B * P,
+           "tokens_per_s": wl.B * P * steps / (total * 1e-3), "ms_per_step": total / steps,
+           "ms_per_step_first8": sum(per_step[:8]) / min(8, steps),
+           "ms_per_step_last8": sum(per_step[-8:]) / min(8, steps),
+           "attn_tflops_per_step": 4 * wl.d * pairs / 1e12,
+           "inputs": "torch-seeded GPU draws, same recipe; 4 distinct frames cycled"}
+    res["rollouts"] = rollouts_leg(H, st, frames, w, out, max(2, steps // 2))
+    return res
+
+
+def rollouts_leg(H, st, frames, w, out, steps):
+    """hlta_step_frame_rollouts on the same stream: first the rollouts are
+    spread out (rollout b ends b frames ahead of rollout 0), then `steps`
+    timed steps with every rollout at its own position, then `steps` with
+    alternate rollouts sitting out (half the tokens per step)."""
+    import numpy as np
+    import torch
+    B, P = st.cfg.B, st.cfg.P
+    pos = np.full(B, st.frames_done, dtype=np.int64)
+    stream = torch.cuda.current_stream()
+    for j in range(B - 1):            # step j advances the rollouts b > j
+        call = np.where(np.arange(B) > j, pos, -1).astype(np.int64)
+        fq, fk, fv, fa, fb = frames[j % len(frames)]
+        H.hlta_step_frame_rollouts(st, call, fq, fk, fv, fa, fb, w, out=out, stream=stream)
+        pos = np.where(call >= 0, call, pos)
+    spread = (pos - pos[0]).tolist()
+
+    def timed(active):
+        nonlocal pos
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        tokens = 0
+        e0.record(stream)
+        for i in range(steps):
+            mask = active(i)
+            call = np.where(mask, pos, -1).astype(np.int64)
+            fq, fk, fv, fa, fb = frames[i % len(frames)]
+            H.hlta_step_frame_rollouts(st, call, fq, fk, fv, fa, fb, w, out=out, stream=stream)
+            pos = np.where(call >= 0, call, pos)
+            tokens += int(mask.sum()) * P
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        return ms / steps, tokens / (ms * 1e-3)
+
+    every = np.ones(B, dtype=bool)
+    ms_all, tps_all = timed(lambda i: every)
+    ms_half, tps_half = timed(lambda i: (np.arange(B) % 2) == (i % 2))
+    return {"steps": steps, "frames_ahead_of_rollout0": spread,
+            "ms_per_step": ms_all, "tokens_per_s": tps_all,
+            "half_sitting_out_ms_per_step": ms_half, "half_sitting_out_tokens_per_s": tps_half}
 
 
 def main():

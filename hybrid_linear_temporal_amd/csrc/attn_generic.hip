@@ -32,11 +32,12 @@ attn_generic_kernel(AttnParams p) {
   const int fq = blockIdx.x / tiles_per_frame;             // query frame within the call
   const int row0 = (blockIdx.x % tiles_per_frame) * kRows;
   const int h = blockIdx.y, b = blockIdx.z;
+  if (skipped(p.ro.skip, b)) return;
   const int tid = threadIdx.x;
   const int r = tid >> 2, c = tid & 3;
   const int prow = row0 + r;                               // token inside the frame
   const bool row_ok = prow < p.P;
-  const long long f = p.f0 + fq;                           // absolute frame
+  const long long f = call_frame(p, b) + fq;               // absolute frame
 
   const Tin* q = static_cast<const Tin*>(p.q);
   const Tin* kmain = static_cast<const Tin*>(p.k);

@@ -275,7 +275,9 @@ attn_mfma_kernel(AttnParams p) {
   const int fq = p.T - 1 - int(rest % p.T);
   const int bh = int(rest / p.T);
   const int b = bh / p.H, h = bh % p.H;
-  const long long f = p.f0 + fq;
+  if (skipped(p.ro.skip, b)) return;
+  const long long f0b = call_frame(p, b);
+  const long long f = f0b + fq;
 
   const size_t HD = size_t(p.H) * D;
   const int wrow0 = qt * QT + wave * 32 * RB;   // first query row (in the frame) of this wave
@@ -309,7 +311,7 @@ attn_mfma_kernel(AttnParams p) {
   }
   KeyStream<kRing> kst;
   kst.fstride = size_t(p.P) * HD;
-  kst.f0 = p.f0;
+  kst.f0 = f0b;
   kst.R = p.R;
   kst.P = p.P;
   if constexpr (!kRing) {

@@ -46,6 +46,7 @@ gdn_prep_generic(GdnParams p) {
   __shared__ float g[C], bb[C], rk[C], rq[C];
 
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  if (skipped(p.skip, b)) return;
   const int tid = threadIdx.x;
   const long long t0 = (long long)chunk * C;
   const int n = int(p.L - t0 < C ? p.L - t0 : C);
@@ -160,6 +161,7 @@ gdn_chain_generic(GdnParams p) {
   using R = Rec<D, C>;
 
   const int v0 = blockIdx.x * NB, h = blockIdx.y, b = blockIdx.z;
+  if (skipped(p.skip, b)) return;
   const int tid = threadIdx.x;
   const size_t sbase = (size_t(b) * p.H + h) * D * D;
   for (int e = tid; e < NB * D; e += kThreads) {

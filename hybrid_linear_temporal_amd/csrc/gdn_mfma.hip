@@ -141,6 +141,7 @@ gdn_prep_mfma(GdnParams p) {
   // last chunk first: when the state pass starts, the records it reads first
   // are the most recently written ones (still in the last-level cache)
   const int chunk = p.n_chunks - 1 - int(blockIdx.x), h = blockIdx.y, b = blockIdx.z;
+  if (skipped(p.skip, b)) return;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long long t0 = (long long)chunk * C;
@@ -626,6 +627,7 @@ gdn_chain_mfma(GdnParams p) {
   const int bh = (slot / (D / NV)) * kChainXcds + xcd;
   if (bh >= p.B * p.H) return;
   const int b = bh / p.H, h = bh % p.H;
+  if (skipped(p.skip, b)) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
   const int v0 = NV * vblk;   // this workgroup's value channels v0 .. v0+15

@@ -48,8 +48,9 @@ hlta_status check_outputs(const float* a, const float* b, const float* mix_w, vo
 
 hlta_status run_gdn(const hlta_config* cfg, const Plan& plan, const void* q, const void* k, const void* v,
                     const float* a, const float* b, const float* S0, float* S_out, void* o_gdn, void* workspace,
-                    hipStream_t st) {
+                    hipStream_t st, unsigned long long skip = 0) {
   GdnParams g{};
+  g.skip = skip;
   g.q = q;
   g.k = k;
   g.v = v;
@@ -83,24 +84,25 @@ hlta_status run_attn(const hlta_config* cfg, const Plan& plan, AttnParams attn, 
 }
 
 hlta_status run_mix(const hlta_config* cfg, const Plan& plan, const void* o_swa, const void* o_dswa,
-                    const void* o_gdn, void* o_mix, const float* mix_w, hipStream_t st) {
+                    const void* o_gdn, void* o_mix, const float* mix_w, hipStream_t st, unsigned long long skip = 0) {
   hipError_t e = launch_mix(o_swa, o_dswa, o_gdn, o_mix, mix_w, (long long)cfg->B * plan.L, cfg->H, cfg->d,
-                            cfg->out_dtype, st);
+                            cfg->out_dtype, st, skip, plan.L);
   if (e != hipSuccess) return hip_fail(e, "mix launch");
   return HLTA_OK;
 }
 
 // One layer: the memory branch (GDN over L tokens per row), the softmax
 // branches, then the per-head mix of the three stored outputs, in order on st.
+// Rollouts in attn.ro.skip are left out of all three.
 // (Running the memory branch on a second stream gains nothing here: its state
 // pass needs one compute unit per workgroup for its LDS buffers, so it cannot
 // share the chip with the attention branches.) attn.* query fields set by caller.
 hlta_status run_layer(const hlta_config* cfg, const Plan& plan, const void* q, const void* k, const void* v,
                       const float* a, const float* b, const float* S0, float* S_out, void* o_gdn,
                       const float* mix_w, void* o_mix, void* workspace, AttnParams attn, hipStream_t st) {
-  HLTA_TRY(run_gdn(cfg, plan, q, k, v, a, b, S0, S_out, o_gdn, workspace, st));
+  HLTA_TRY(run_gdn(cfg, plan, q, k, v, a, b, S0, S_out, o_gdn, workspace, st, attn.ro.skip));
   HLTA_TRY(run_attn(cfg, plan, attn, st));
-  return run_mix(cfg, plan, attn.o_swa, attn.o_dswa, o_gdn, o_mix, mix_w, st);
+  return run_mix(cfg, plan, attn.o_swa, attn.o_dswa, o_gdn, o_mix, mix_w, st, attn.ro.skip);
 }
 
 AttnParams full_attn_params(const hlta_config* cfg, const void* q, const void* k, const void* v, void* o_swa,
@@ -263,10 +265,13 @@ hlta_status hlta_stream_load_prefix(const hlta_config* cfg, hlta_stream_state* s
   return HLTA_OK;
 }
 
-hlta_status hlta_step_frame(const hlta_config* cfg, hlta_stream_state* st, const void* q_f, const void* k_f,
-                            const void* v_f, const float* a_f, const float* b_f, const float* mix_w, void* o_swa,
-                            void* o_dswa, void* o_gdn, void* o_mix, int32_t commit, void* workspace,
-                            size_t ws_bytes, void* stream) {
+// One streaming step. frames == null: every rollout appends frame
+// st->frames_done. Otherwise rollout b appends frame frames[b], or sits the
+// step out when frames[b] == -1.
+static hlta_status step_frame_impl(const hlta_config* cfg, hlta_stream_state* st, int64_t* frames, const void* q_f,
+                                   const void* k_f, const void* v_f, const float* a_f, const float* b_f,
+                                   const float* mix_w, void* o_swa, void* o_dswa, void* o_gdn, void* o_mix,
+                                   int32_t commit, void* workspace, size_t ws_bytes, void* stream) {
   clear_error();
   HLTA_TRY(check_config(cfg));
   HLTA_TRY(check_stream(cfg, st));
@@ -277,9 +282,26 @@ hlta_status hlta_step_frame(const hlta_config* cfg, hlta_stream_state* st, const
   HLTA_TRY(need(v_f, "v_f"));
   HLTA_TRY(check_outputs(a_f, b_f, mix_w, o_swa, o_dswa, o_gdn, o_mix));
   HLTA_TRY(check_workspace(plan, workspace, ws_bytes));
+  AttnParams at{};
+  unsigned long long skip = 0;
+  if (frames) {
+    if (cfg->B > kMaxRollouts)
+      return fail(HLTA_E_UNSUPPORTED, "per-rollout positions support at most " + std::to_string(kMaxRollouts) +
+                                          " rollouts (B = " + std::to_string(cfg->B) + ")");
+    int active = 0;
+    for (int b = 0; b < cfg->B; ++b) {
+      if (frames[b] < -1)
+        return fail(HLTA_E_STATE, "frames[" + std::to_string(b) + "] = " + std::to_string(frames[b]) +
+                                      " (a frame index, or -1 to leave the rollout out)");
+      if (frames[b] == -1) skip |= 1ull << b;
+      else ++active;
+      at.ro.frame[b] = frames[b] < 0 ? 0 : frames[b];
+    }
+    if (active == 0) return HLTA_OK;
+    at.per_rollout = 1;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const long long f = st->frames_done;
-  AttnParams at{};
   at.q = q_f;
   at.k = k_f;
   at.v = v_f;
@@ -296,18 +318,51 @@ hlta_status hlta_step_frame(const hlta_config* cfg, hlta_stream_state* st, const
   at.taps = cfg->dswa_taps;
   at.R = st->ring_frames;
   at.f0 = f;
+  at.ro.skip = skip;
   HLTA_TRY(run_layer(cfg, plan, q_f, k_f, v_f, a_f, b_f, st->S, commit ? st->S : nullptr, o_gdn, mix_w, o_mix,
                      workspace, at, s));
   if (commit) {
     const long long frame_elems = (long long)cfg->P * cfg->H * cfg->d;
     const int elem = int(dtype_bytes(cfg->in_dtype));
-    hipError_t e = launch_ring_store(k_f, 1, f, st->ring_k, st->ring_frames, f, 1, cfg->B, frame_elems, elem, s);
-    if (e == hipSuccess)
-      e = launch_ring_store(v_f, 1, f, st->ring_v, st->ring_frames, f, 1, cfg->B, frame_elems, elem, s);
+    hipError_t e = hipSuccess;
+    if (!frames) {
+      e = launch_ring_store(k_f, 1, f, st->ring_k, st->ring_frames, f, 1, cfg->B, frame_elems, elem, s);
+      if (e == hipSuccess)
+        e = launch_ring_store(v_f, 1, f, st->ring_v, st->ring_frames, f, 1, cfg->B, frame_elems, elem, s);
+    } else {
+      // each rollout that stepped into the slot of its own frame
+      e = launch_ring_store_rollouts(k_f, st->ring_k, st->ring_frames, cfg->B, frame_elems, elem, at.ro, s);
+      if (e == hipSuccess)
+        e = launch_ring_store_rollouts(v_f, st->ring_v, st->ring_frames, cfg->B, frame_elems, elem, at.ro, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "ring store");
-    st->frames_done = f + 1;
+    if (!frames) st->frames_done = f + 1;
+    else
+      for (int b = 0; b < cfg->B; ++b)
+        if (frames[b] >= 0) ++frames[b];
   }
   return HLTA_OK;
+}
+
+hlta_status hlta_step_frame(const hlta_config* cfg, hlta_stream_state* st, const void* q_f, const void* k_f,
+                            const void* v_f, const float* a_f, const float* b_f, const float* mix_w, void* o_swa,
+                            void* o_dswa, void* o_gdn, void* o_mix, int32_t commit, void* workspace,
+                            size_t ws_bytes, void* stream) {
+  return step_frame_impl(cfg, st, nullptr, q_f, k_f, v_f, a_f, b_f, mix_w, o_swa, o_dswa, o_gdn, o_mix, commit,
+                         workspace, ws_bytes, stream);
+}
+
+hlta_status hlta_step_frame_rollouts(const hlta_config* cfg, hlta_stream_state* st, int64_t* frames,
+                                     const void* q_f, const void* k_f, const void* v_f, const float* a_f,
+                                     const float* b_f, const float* mix_w, void* o_swa, void* o_dswa, void* o_gdn,
+                                     void* o_mix, int32_t commit, void* workspace, size_t ws_bytes,
+                                     void* stream) {
+  if (!frames) {
+    clear_error();
+    return fail(HLTA_E_NULL, "frames is NULL");
+  }
+  return step_frame_impl(cfg, st, frames, q_f, k_f, v_f, a_f, b_f, mix_w, o_swa, o_dswa, o_gdn, o_mix, commit,
+                         workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

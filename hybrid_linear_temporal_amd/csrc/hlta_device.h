@@ -25,6 +25,19 @@ template <typename T> __device__ __forceinline__ float stored_value(float x) {
 // Full mode (R == 0): queries and keys come from q, k, v of T frames.
 // Stream mode (R > 0): the call's single query frame is absolute frame f0;
 // its own K/V come from k, v; earlier frames g from ring slot g mod R.
+// Rollouts left out of a launch have their bit set in a skip mask: their
+// workgroups return at once, so nothing of theirs is read or written.
+constexpr int kMaxRollouts = 64;
+__device__ __forceinline__ bool skipped(unsigned long long skip, int b) {
+  return b < kMaxRollouts && ((skip >> b) & 1ull) != 0;
+}
+
+// Frame index per rollout and the rollouts left out (kernel argument).
+struct RolloutFrames {
+  unsigned long long skip;
+  long long frame[kMaxRollouts];
+};
+
 struct AttnParams {
   const void* q;
   const void* k;
@@ -38,7 +51,16 @@ struct AttnParams {
   int R;                 // ring frames (stream mode) or 0
   long long f0;          // absolute index of query frame 0
   float scale_log2;      // softmax scale * log2(e)
+  // Streaming with a position per rollout (T = 1): rollout b's query frame is
+  // ro.frame[b]; rollouts in ro.skip are left out entirely (also without it).
+  int per_rollout;
+  RolloutFrames ro;
 };
+
+// Absolute index of the call's first query frame for rollout b.
+__device__ __forceinline__ long long call_frame(const AttnParams& p, int b) {
+  return p.per_rollout ? p.ro.frame[b] : p.f0;
+}
 
 // Key frame g (absolute index) of batch row b, head h: pointer to its token 0.
 // Tokens of a frame are H*D elements apart.
@@ -47,7 +69,7 @@ __device__ __forceinline__ const T* key_frame_ptr(const T* main, const T* ring, 
                                                   int b, int h, long long g) {
   if (p.R == 0)
     return main + ((size_t(b) * p.T * p.P + size_t(g) * p.P) * p.H + h) * D;
-  if (g == p.f0)
+  if (g == call_frame(p, b))
     return main + (size_t(b) * p.P * p.H + h) * D;
   const int slot = int(g % p.R);
   return ring + ((size_t(b) * p.R + slot) * p.P * p.H + h) * D;
@@ -82,6 +104,7 @@ struct GdnParams {
   long long L;
   int n_chunks;
   int l2norm;
+  unsigned long long skip;   // rollouts left out (bit b)
 };
 
 }  // namespace hlta

@@ -13,9 +13,11 @@ hipError_t launch_attn_generic(const AttnParams& p, int d, int in_dt, int out_dt
 // SWA + DSWA with bf16 MFMA (bf16 inputs, d = 128).
 hipError_t launch_attn_mfma(const AttnParams& p, int out_dt, hipStream_t st);
 // o_mix = per-head weighted sum of the three stored branch outputs
-// ([ntok, H, d] each, out dtype), d a multiple of 8.
+// ([ntok, H, d] each, out dtype), d a multiple of 8; rows of rollouts in
+// skip (rollout_tokens tokens each) are not written.
 hipError_t launch_mix(const void* o_swa, const void* o_dswa, const void* o_gdn, void* o_mix, const float* mix_w,
-                      long long ntok, int H, int d, int out_dt, hipStream_t st);
+                      long long ntok, int H, int d, int out_dt, hipStream_t st, unsigned long long skip = 0,
+                      long long rollout_tokens = 1);
 
 // Gated delta rule, chunked form, fp32 arithmetic (any supported d, C, dtype).
 hipError_t launch_gdn_generic(const GdnParams& p, int d, int C, int in_dt, int out_dt, hipStream_t st);
@@ -27,5 +29,11 @@ hipError_t launch_gdn_mfma(const GdnParams& p, int out_dt, hipStream_t st);
 hipError_t launch_ring_store(const void* src, long long src_frames, long long src_f0, void* ring,
                              int R, long long first_frame, long long n_frames, int B, long long frame_elems,
                              int elem, hipStream_t st);
+
+// Streaming with a position per rollout: src [B, P, H, d] holds one frame per
+// rollout; rollout b's goes to ring slot sel.frame[b] mod R (rollouts in
+// sel.skip are left alone).
+hipError_t launch_ring_store_rollouts(const void* src, void* ring, int R, int B, long long frame_elems, int elem,
+                                      const RolloutFrames& sel, hipStream_t st);
 
 }  // namespace hlta

@@ -26,6 +26,21 @@ ring_store_kernel(const uint4* src, long long src_frames, long long src_f0, uint
     d[i] = s[i];
 }
 
+// One frame per rollout, each into the slot of its own frame: rollout b's
+// frame (src row b) goes to ring slot frame[b] mod R; rollouts in skip are
+// left alone. grid: (blocks, 1, B).
+__global__ void __launch_bounds__(kThreads)
+ring_store_rollouts_kernel(const uint4* src, uint4* ring, int R, long long frame_vec, RolloutFrames sel) {
+  const int b = blockIdx.z;
+  if (skipped(sel.skip, b)) return;
+  const long long slot = sel.frame[b] % R;
+  const uint4* s = src + size_t(b) * frame_vec;
+  uint4* d = ring + (size_t(b) * R + size_t(slot)) * frame_vec;
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < frame_vec;
+       i += (long long)gridDim.x * kThreads)
+    d[i] = s[i];
+}
+
 // o_mix = w[h][0] o_swa + w[h][1] o_dswa + w[h][2] o_gdn, elementwise over the
 // stored branch outputs (Kairos abstract, point (2): the three branches are
 // mixed per head), with one fp32 rounding order for every caller:
@@ -61,8 +76,10 @@ struct Vec8<float> {
 
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
-mix_kernel(const T* swa, const T* dswa, const T* gdn, T* mix, const float* w, long long n8, int H, int d8) {
+mix_kernel(const T* swa, const T* dswa, const T* gdn, T* mix, const float* w, long long n8, int H, int d8,
+           unsigned long long skip, long long row8) {
   for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < n8; i += (long long)gridDim.x * kThreads) {
+    if (skip != 0 && skipped(skip, int(i / row8))) continue;   // rollout left out: its rows stay as they are
     const int h = int((i / d8) % H);
     const float w0 = w[3 * h], w1 = w[3 * h + 1], w2 = w[3 * h + 2];
     Vec8<T> a, b, g, o;
@@ -78,19 +95,31 @@ mix_kernel(const T* swa, const T* dswa, const T* gdn, T* mix, const float* w, lo
 }  // namespace
 
 hipError_t launch_mix(const void* o_swa, const void* o_dswa, const void* o_gdn, void* o_mix, const float* mix_w,
-                      long long ntok, int H, int d, int out_dt, hipStream_t st) {
+                      long long ntok, int H, int d, int out_dt, hipStream_t st, unsigned long long skip,
+                      long long rollout_tokens) {
   const long long n8 = ntok * H * (d / 8);
+  const long long row8 = rollout_tokens * H * (d / 8);
   if (n8 <= 0) return hipSuccess;
   long long blocks = (n8 + kThreads - 1) / kThreads;
   if (blocks > 8192) blocks = 8192;
   if (out_dt == HLTA_BF16)
     hipLaunchKernelGGL(mix_kernel<bf16>, dim3(unsigned(blocks)), dim3(kThreads), 0, st,
                        static_cast<const bf16*>(o_swa), static_cast<const bf16*>(o_dswa),
-                       static_cast<const bf16*>(o_gdn), static_cast<bf16*>(o_mix), mix_w, n8, H, d / 8);
+                       static_cast<const bf16*>(o_gdn), static_cast<bf16*>(o_mix), mix_w, n8, H, d / 8, skip, row8);
   else
     hipLaunchKernelGGL(mix_kernel<float>, dim3(unsigned(blocks)), dim3(kThreads), 0, st,
                        static_cast<const float*>(o_swa), static_cast<const float*>(o_dswa),
-                       static_cast<const float*>(o_gdn), static_cast<float*>(o_mix), mix_w, n8, H, d / 8);
+                       static_cast<const float*>(o_gdn), static_cast<float*>(o_mix), mix_w, n8, H, d / 8, skip, row8);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_store_rollouts(const void* src, void* ring, int R, int B, long long frame_elems, int elem,
+                                     const RolloutFrames& sel, hipStream_t st) {
+  const long long frame_vec = frame_elems * elem / 16;   // frame bytes are a multiple of 16 (d >= 32)
+  long long blocks = (frame_vec + kThreads * 4 - 1) / (kThreads * 4);
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(ring_store_rollouts_kernel, dim3(unsigned(blocks), 1, B), dim3(kThreads), 0, st,
+                     static_cast<const uint4*>(src), static_cast<uint4*>(ring), R, frame_vec, sel);
   return hipGetLastError();
 }
 

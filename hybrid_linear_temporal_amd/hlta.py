@@ -26,7 +26,8 @@ STATUS = {0: "HLTA_OK", 1: "HLTA_E_NULL", 2: "HLTA_E_SHAPE", 3: "HLTA_E_DTYPE", 
 # every symbol include/hlta.h declares
 EXPORTS = ("hlta_abi_version", "hlta_status_string", "hlta_last_error", "hlta_validate_config",
            "hlta_fwd_workspace_bytes", "hlta_fwd", "hlta_gdn_fwd", "hlta_attn_fwd", "hlta_stream_ring_bytes",
-           "hlta_stream_load_prefix", "hlta_step_workspace_bytes", "hlta_step_frame")
+           "hlta_stream_load_prefix", "hlta_step_workspace_bytes", "hlta_step_frame",
+           "hlta_step_frame_rollouts")
 
 
 class hlta_config(ctypes.Structure):
@@ -76,6 +77,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "hlta_stream_load_prefix": (I32, [cfgp, stp, P, P, I32, P, P]),
         "hlta_step_workspace_bytes": (S, [cfgp]),
         "hlta_step_frame": (I32, [cfgp, stp, P, P, P, P, P, P, P, P, P, P, I32, P, S, P]),
+        "hlta_step_frame_rollouts": (I32, [cfgp, stp, ctypes.POINTER(I64), P, P, P, P, P, P, P, P, P, P, I32, P,
+                                           S, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -212,6 +215,26 @@ def hlta_step_frame(st: Stream, q_f, k_f, v_f, a_f, b_f, mix_w, out=None, commit
         ctypes.byref(cfg), ctypes.byref(st.state), _ptr(q_f), _ptr(k_f), _ptr(v_f), _ptr(a_f), _ptr(b_f),
         _ptr(mix_w), _ptr(out["o_swa"]), _ptr(out["o_dswa"]), _ptr(out["o_gdn"]), _ptr(out["o_mix"]),
         int(bool(commit)), _ptr(st.workspace), st.workspace.numel(), _stream(stream)))
+    return out
+
+
+def hlta_step_frame_rollouts(st: Stream, frames, q_f, k_f, v_f, a_f, b_f, mix_w, out=None, commit: bool = True,
+                             stream=None) -> dict:
+    """One step with a position per rollout (C: hlta_step_frame_rollouts).
+    frames: int64 numpy array [B], frame each rollout appends or -1; advanced
+    in place on commit."""
+    import numpy as np
+    cfg = st.cfg
+    if not (isinstance(frames, np.ndarray) and frames.dtype == np.int64 and frames.flags.c_contiguous
+            and frames.shape == (cfg.B,)):
+        raise TypeError("frames must be a contiguous int64 numpy array of B entries")
+    if out is None:
+        out = alloc_outputs(cfg, cfg.P, q_f.device)
+    _check(load_library().hlta_step_frame_rollouts(
+        ctypes.byref(cfg), ctypes.byref(st.state), frames.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        _ptr(q_f), _ptr(k_f), _ptr(v_f), _ptr(a_f), _ptr(b_f), _ptr(mix_w), _ptr(out["o_swa"]),
+        _ptr(out["o_dswa"]), _ptr(out["o_gdn"]), _ptr(out["o_mix"]), int(bool(commit)), _ptr(st.workspace),
+        st.workspace.numel(), _stream(stream)))
     return out
 
 

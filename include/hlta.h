@@ -213,6 +213,28 @@ hlta_status hlta_step_frame(const hlta_config* cfg, hlta_stream_state* st,
                             void* o_swa, void* o_dswa, void* o_gdn, void* o_mix,
                             int32_t commit, void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * hlta_step_frame_rollouts - one streaming step in which every rollout is at
+ * its own position (rollouts started at different times, or advanced by
+ * different numbers of steps, e.g. several streams served together). The
+ * per-rollout counts live in frames, a host array of B entries owned by the
+ * caller (st->frames_done is not used): rollout b appends frame frames[b],
+ * which must equal the number of frames it has appended so far, or sits the
+ * step out when frames[b] == -1 (its output rows are not written and its
+ * state, ring slots and count stay as they are). Outputs of a stepping
+ * rollout equal those of hlta_step_frame on a stream holding that rollout
+ * alone. With commit != 0 each stepping rollout's S and ring slot
+ * frames[b] mod R are updated and frames[b] is incremented.
+ * B <= 64 (HLTA_E_UNSUPPORTED otherwise); an entry below -1 is HLTA_E_STATE,
+ * frames == NULL is HLTA_E_NULL. Other arguments as in hlta_step_frame; rows
+ * of q_f .. b_f belonging to rollouts that sit out are not read.
+ */
+hlta_status hlta_step_frame_rollouts(const hlta_config* cfg, hlta_stream_state* st, int64_t* frames,
+                                     const void* q_f, const void* k_f, const void* v_f,
+                                     const float* a_f, const float* b_f, const float* mix_w,
+                                     void* o_swa, void* o_dswa, void* o_gdn, void* o_mix,
+                                     int32_t commit, void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

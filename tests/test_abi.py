@@ -133,3 +133,30 @@ def test_stream_argument_errors(lib):
                                1 << 40, None) == 7
     st = H.hlta_stream_state(fake, fake, fake, 16, 0)
     assert lib.hlta_stream_load_prefix(ctypes.byref(cfg), ctypes.byref(st), None, None, 3, None, None) == 1
+
+
+def test_step_rollouts_argument_errors(lib):
+    """Per-rollout positions: NULL frames, an entry below -1 and more than 64
+    rollouts fail before any launch; a step every rollout sits out is a no-op."""
+    import numpy as np
+    cfg = H.make_config(I.STREAM_P480)
+    fake = 1 << 20
+    st = H.hlta_stream_state(fake, fake, fake, 16, 0)
+    p = ctypes.c_void_p(fake)
+    ws = 1 << 40
+
+    def call(c, frames):
+        fp = None if frames is None else frames.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        return lib.hlta_step_frame_rollouts(ctypes.byref(c), ctypes.byref(st), fp, p, p, p, p, p, p, p, p, p, p,
+                                            1, p, ws, None)
+
+    assert call(cfg, None) == 1
+    frames = np.full(cfg.B, 20, dtype=np.int64)
+    frames[3] = -2
+    assert call(cfg, frames) == 7
+    assert b"frames[3]" in lib.hlta_last_error()
+    skip_all = np.full(cfg.B, -1, dtype=np.int64)
+    assert call(cfg, skip_all) == 0 and np.all(skip_all == -1)
+    big = H.make_config(I.STREAM_P480)
+    big.B = 65
+    assert call(big, np.zeros(65, dtype=np.int64)) == 4

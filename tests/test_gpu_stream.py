@@ -110,3 +110,85 @@ def test_stream_resume_is_bitwise():
     for n in BRANCHES:
         assert torch.equal(a1[n], b1[n]) and torch.equal(a2[n], b2[n]), n
     assert torch.equal(st.S, st2.S)
+
+
+@pytest.mark.parametrize("wl,prefix,R", STREAM_CASES, ids=lambda c: getattr(c, "name", str(c)))
+def test_rollouts_at_own_positions(wl, prefix, R):
+    """hlta_step_frame_rollouts: three rollouts advanced on different
+    schedules. A stepping rollout's outputs equal the float64 stream of that
+    rollout alone and the rows of hlta_fwd over its clip; a rollout sitting a
+    step out has its output rows and state left alone and its input rows
+    unread (they hold NaN)."""
+    from tests.helpers import replace
+    wl = replace(wl, B=3)
+    x = I.make_clip(wl)
+    P, B = wl.P, wl.B
+    tol = TOL[wl.dtype]
+    dev = H.to_device(x, wl.dtype)
+    full = H.hlta_fwd(H.make_config(wl), dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"])
+    cfg_pre = H.make_config(wl, T=prefix)
+    pre = {n: t[:, :prefix * P].contiguous() if n != "w" else t for n, t in dev.items()}
+    S_pre = torch.empty((B, wl.H, wl.d, wl.d), dtype=torch.float32, device="cuda")
+    H.hlta_fwd(cfg_pre, pre["q"], pre["k"], pre["v"], pre["a"], pre["b"], pre["w"], S_out=S_pre)
+    st = H.Stream(H.make_config(wl, T=1), R)
+    H.hlta_stream_load_prefix(st, pre["k"], pre["v"], prefix, S_pre)
+    heads = [(b, h) for b in range(B) for h in range(wl.H)]
+    ost = {}
+    for b, h in heads:
+        _, Sp = O.gdn_recurrent(x["q"][b, :prefix * P, h], x["k"][b, :prefix * P, h], x["v"][b, :prefix * P, h],
+                                x["a"][b, :prefix * P, h], x["b"][b, :prefix * P, h])
+        s = O.StreamHead(P, wl.swa_frames, wl.dswa_dilation, wl.dswa_taps, wl.gdn_chunk)
+        s.load_prefix(x["k"][b, :, h], x["v"][b, :, h], prefix, Sp)
+        ost[b, h] = s
+    frames = np.full(B, prefix, dtype=np.int64)
+    schedule = [(1, 1, 0), (1, 0, 1), (0, 1, 1), (1, 1, 1), (1, 0, 0), (0, 0, 1), (1, 1, 0)]
+    for mask in schedule:
+        call = np.where(np.array(mask) == 1, frames, -1).astype(np.int64)
+        if np.any(call >= wl.T):
+            break
+        fr = {}
+        for n, t in dev.items():
+            if n == "w":
+                fr[n] = t
+                continue
+            rows = torch.full((B, P) + tuple(t.shape[2:]), float("nan"), dtype=t.dtype, device=t.device)
+            for b in range(B):
+                if call[b] >= 0:
+                    rows[b] = t[b, call[b] * P:(call[b] + 1) * P]
+            fr[n] = rows.contiguous()
+        # an uncommitted evaluation with other inputs leaves every count, ring and state alone
+        before = call.copy()
+        H.hlta_step_frame_rollouts(st, call, fr["q"] * 2, fr["k"], fr["v"] * 3, fr["a"], fr["b"], fr["w"],
+                                   commit=False)
+        assert np.array_equal(call, before)
+        out = H.alloc_outputs(st.cfg, P)
+        for t in out.values():
+            t.fill_(7.0)
+        S_before = st.S.clone()
+        got = H.hlta_step_frame_rollouts(st, call, fr["q"], fr["k"], fr["v"], fr["a"], fr["b"], fr["w"], out=out)
+        torch.cuda.synchronize()
+        assert np.array_equal(call, np.where(before >= 0, before + 1, -1))
+        for b in range(B):
+            if before[b] < 0:
+                for n in BRANCHES:
+                    assert bool(torch.all(got[n][b] == 7.0)), f"rollout {b} sat out but {n} was written"
+                assert torch.equal(st.S[b], S_before[b]), f"rollout {b} sat out but its state moved"
+                continue
+            f = int(before[b])
+            sl = slice(f * P, (f + 1) * P)
+            refs = {n: np.zeros((P, wl.H, wl.d)) for n in BRANCHES}
+            for h in range(wl.H):
+                outs = ost[b, h].step(x["q"][b, sl, h], x["k"][b, sl, h], x["v"][b, sl, h], x["a"][b, sl, h],
+                                      x["b"][b, sl, h], x["w"][h])
+                for n, o in zip(BRANCHES, outs):
+                    refs[n][:, h] = o
+            for n in BRANCHES:
+                g = to64(got[n][b])
+                e = O.rel_l2(g, refs[n])
+                e_full = O.rel_l2(g, to64(full[n][b, sl]))
+                assert e <= tol, f"rollout {b} frame {f} {n}: {e:.2e}"
+                assert e_full <= tol, f"rollout {b} frame {f} {n} vs full: {e_full:.2e}"
+        frames = np.where(before >= 0, before + 1, frames)
+    assert np.all(frames > prefix)
+    Sref = np.stack([np.stack([ost[b, h].S0 for h in range(wl.H)]) for b in range(B)])
+    assert O.rel_l2(to64(st.S), Sref) <= tol
