@@ -22,7 +22,9 @@ Readings taken where the pages are silent (each is listed in the design doc):
   * SWA frame set {f - j : 0 <= j < W}: W counts the current frame;
   * DSWA frame set {f - dil*r : 1 <= r <= taps}; frames below 0 are skipped;
     a query with an empty frame set outputs zeros;
-  * softmax scale 1/sqrt(d) unless given; no bias, no positional term;
+  * softmax scale 1/sqrt(d) unless given; no bias; no positional term unless
+    the optional rotary embedding of the softmax branches is asked for (its
+    variant is not on the pages; the reading is stated at `rope`);
   * the memory follows the gated delta rule, one token at a time in token order
     (raster inside a frame), with per-token per-head gates a (decay) and b
     (write strength) used as given, in-op L2 normalisation of q and k with
@@ -192,13 +194,69 @@ def gdn_chunked(q, k, v, a, b, C, S0=None, l2norm=True):
 
 
 # ---------------------------------------------------------------------------
+# rotary position embedding of the softmax branches (optional)
+# ---------------------------------------------------------------------------
+#
+# The pages say the local branches are sliding windows over latent frames and
+# name no positional scheme. Reading taken for the optional rotary embedding:
+# positions are three-dimensional, (absolute latent frame, row, column) with
+# token p of a frame at row p // grid_w, column p % grid_w; the d/2 coordinate
+# pairs (x[2i], x[2i+1]) are complex numbers rotated by angle pos * theta^(-j/n)
+# where the first d/8 pairs follow the frame, the next half of the rest the
+# row, the others the column, j is the pair's index within its axis and n the
+# number of pairs of that axis. It applies to q and k of SWA and DSWA only; the
+# memory branch reads q and k without positions.
+
+def rope_axis_pairs(d):
+    """Pairs of a head of size d given to the (frame, row, column) axes."""
+    n = d // 2
+    nt = d // 8
+    nh = (n - nt) // 2
+    return nt, nh, n - nt - nh
+
+
+def rope_positions(T, P, grid_w, f0=0):
+    """(frame, row, column) of the T*P tokens of frames f0 .. f0+T-1, [T*P, 3]."""
+    t = np.arange(T * P)
+    p = t % P
+    return np.stack([f0 + t // P, p // grid_w, p % grid_w], axis=1).astype(np.float64)
+
+
+def rope(x, pos, theta):
+    """Rotate each token's coordinate pairs by its position (reading above).
+    x [n_tokens, d], pos [n_tokens, 3]."""
+    x = np.asarray(x, np.float64)
+    d = x.shape[1]
+    nt, nh, nw = rope_axis_pairs(d)
+    out = np.empty_like(x)
+    for i in range(d // 2):
+        if i < nt:
+            axis, j, n = 0, i, nt
+        elif i < nt + nh:
+            axis, j, n = 1, i - nt, nh
+        else:
+            axis, j, n = 2, i - nt - nh, nw
+        ang = pos[:, axis] * float(theta) ** (-j / n)
+        z = (x[:, 2 * i] + 1j * x[:, 2 * i + 1]) * np.exp(1j * ang)
+        out[:, 2 * i] = z.real
+        out[:, 2 * i + 1] = z.imag
+    return out
+
+
+# ---------------------------------------------------------------------------
 # whole operator
 # ---------------------------------------------------------------------------
 
-def hlta_head(q, k, v, a, b, w3, T, P, W, dil, taps, C, scale=None, S0=None, gdn="chunked"):
-    """HLTA forward of one (batch, head): returns o_swa, o_dswa, o_gdn, o_mix, S_out."""
-    o_swa = swa(q, k, v, T, P, W, scale)
-    o_dswa = dswa(q, k, v, T, P, dil, taps, scale)
+def hlta_head(q, k, v, a, b, w3, T, P, W, dil, taps, C, scale=None, S0=None, gdn="chunked", rope_cfg=None):
+    """HLTA forward of one (batch, head): returns o_swa, o_dswa, o_gdn, o_mix, S_out.
+    rope_cfg = (theta, grid_w): rotary embedding of the softmax branches' q, k."""
+    qa, ka = q, k
+    if rope_cfg is not None:
+        theta, grid_w = rope_cfg
+        pos = rope_positions(T, P, grid_w)
+        qa, ka = rope(q, pos, theta), rope(k, pos, theta)
+    o_swa = swa(qa, ka, v, T, P, W, scale)
+    o_dswa = dswa(qa, ka, v, T, P, dil, taps, scale)
     if gdn == "chunked":
         o_gdn, S = gdn_chunked(q, k, v, a, b, C, S0)
     else:
@@ -209,7 +267,7 @@ def hlta_head(q, k, v, a, b, w3, T, P, W, dil, taps, C, scale=None, S0=None, gdn
 
 
 def hlta_forward(q, k, v, a, b, w, T, P, W, dil, taps, C, scale=None, S0=None, gdn="chunked",
-                 heads=None):
+                 heads=None, rope_cfg=None):
     """HLTA forward over [B, L, H, d] inputs; returns float64 arrays in the same
     layout (o_* [B, L, H, d], S_out [B, H, d_v, d_k]). heads: optional list of
     (b, h) to compute (others stay zero)."""
@@ -221,7 +279,7 @@ def hlta_forward(q, k, v, a, b, w, T, P, W, dil, taps, C, scale=None, S0=None, g
     for bi, hi in todo:
         s0 = None if S0 is None else S0[bi, hi]
         res = hlta_head(q[bi, :, hi], k[bi, :, hi], v[bi, :, hi], a[bi, :, hi], b[bi, :, hi],
-                        w[hi], T, P, W, dil, taps, C, scale, s0, gdn)
+                        w[hi], T, P, W, dil, taps, C, scale, s0, gdn, rope_cfg)
         for o, r in zip(outs, res[:4]):
             o[bi, :, hi] = r
         S_out[bi, hi] = res[4]
@@ -239,17 +297,24 @@ class StreamHead:
     incremental generation; long-context page, section 02: a recurrent twin of
     the parallel form for decoding)."""
 
-    def __init__(self, P, W, dil, taps, C, scale=None, S0=None):
+    def __init__(self, P, W, dil, taps, C, scale=None, S0=None, rope_cfg=None):
         self.P, self.W, self.dil, self.taps, self.C = P, W, dil, taps, C
         self.scale = scale
+        self.rope_cfg = rope_cfg   # (theta, grid_w): past keys are kept rotated
         self.S0 = None if S0 is None else np.array(S0, np.float64)
         self.k = {}
         self.v = {}
         self.f = 0
 
+    def _rot(self, x, f):
+        if self.rope_cfg is None:
+            return np.asarray(x, np.float64)
+        theta, grid_w = self.rope_cfg
+        return rope(x, rope_positions(1, self.P, grid_w, f0=f), theta)
+
     def load_prefix(self, k, v, frames, S):
         for j in range(frames):
-            self.k[j] = np.asarray(k[j * self.P:(j + 1) * self.P], np.float64)
+            self.k[j] = self._rot(k[j * self.P:(j + 1) * self.P], j)
             self.v[j] = np.asarray(v[j * self.P:(j + 1) * self.P], np.float64)
         self.f = frames
         self.S0 = np.array(S, np.float64)
@@ -261,12 +326,14 @@ class StreamHead:
         vf = np.asarray(v, np.float64)
         scale = 1.0 / np.sqrt(q.shape[1]) if self.scale is None else self.scale
 
+        qr, kr = self._rot(q, f), self._rot(kf, f)
+
         def attend(frames):
             if not frames:
                 return np.zeros((P, vf.shape[1]))
-            ks = np.concatenate([kf if g == f else self.k[g] for g in frames])
+            ks = np.concatenate([kr if g == f else self.k[g] for g in frames])
             vs = np.concatenate([vf if g == f else self.v[g] for g in frames])
-            z = scale * (q @ ks.T)
+            z = scale * (qr @ ks.T)
             z -= z.max(axis=1, keepdims=True)
             e = np.exp(z)
             return (e @ vs) / e.sum(axis=1, keepdims=True)
@@ -277,7 +344,7 @@ class StreamHead:
         w3 = np.asarray(w3, np.float64)
         o_mix = w3[0] * o_swa + w3[1] * o_dswa + w3[2] * o_gdn
         if commit:
-            self.k[f], self.v[f] = kf, vf
+            self.k[f], self.v[f] = kr, vf
             self.S0 = S
             self.f = f + 1
         return o_swa, o_dswa, o_gdn, o_mix

@@ -374,3 +374,103 @@ def test_inputs_recipe():
     assert 0 < x["b"].min() and x["b"].max() < 1
     y = I.make_clip(wl)
     np.testing.assert_array_equal(x["q"], y["q"])   # seeded
+
+
+# ---------------------------------------------------------------------------
+# rotary embedding of the softmax branches (optional)
+# ---------------------------------------------------------------------------
+
+def test_rope_values_by_hand():
+    """d = 32: pairs 0-3 follow the frame, 4-9 the row, 10-15 the column;
+    pair j of an axis with n pairs turns by pos * 10000^(-j/n). Unit vectors
+    at chosen positions land on cos/sin values worked out by hand."""
+    theta, d = 10000.0, 32
+    assert O.rope_axis_pairs(d) == (4, 6, 6)
+    e = np.eye(d)
+    # frame 1: pair 0 turns by 1 rad, pair 1 by 10000^(-1/4) = 0.1 rad
+    r = O.rope(e[[0, 2, 3]], np.array([[1.0, 0, 0]] * 3), theta)
+    assert np.allclose(r[0, :2], [math.cos(1.0), math.sin(1.0)], atol=1e-15) and np.allclose(r[0, 2:], 0)
+    assert np.allclose(r[1, 2:4], [math.cos(0.1), math.sin(0.1)], atol=1e-15)
+    assert np.allclose(r[2, 2:4], [-math.sin(0.1), math.cos(0.1)], atol=1e-15)   # second coordinate of the pair
+    # row 2: the first row pair (coordinates 8, 9) turns by 2 rad; frame and column pairs stay
+    r = O.rope(e[[8, 0, 20]], np.array([[0.0, 2, 0]] * 3), theta)
+    assert np.allclose(r[0, 8:10], [math.cos(2.0), math.sin(2.0)], atol=1e-15)
+    assert np.allclose(r[1], e[0]) and np.allclose(r[2], e[20])
+    # column 3: first column pair (20, 21) by 3 rad, second (22, 23) by 3 * 10000^(-1/6)
+    r = O.rope(e[[20, 22]], np.array([[0.0, 0, 3]] * 2), theta)
+    assert np.allclose(r[0, 20:22], [math.cos(3.0), math.sin(3.0)], atol=1e-15)
+    a = 3.0 * 10000.0 ** (-1.0 / 6.0)
+    assert np.allclose(r[1, 22:24], [math.cos(a), math.sin(a)], atol=1e-15)
+
+
+def test_rope_identity_norm_and_relative_positions():
+    """Position (0, 0, 0) leaves a vector unchanged; every rotation keeps the
+    norm; the score of a rotated query and key depends only on the difference
+    of their positions (a common shift of both positions changes nothing)."""
+    rng = np.random.default_rng(41)
+    for d in (32, 64, 128):
+        x = rng.standard_normal((50, d))
+        assert np.array_equal(O.rope(x, np.zeros((50, 3)), 500.0), x)
+        pos = rng.integers(0, 60, size=(50, 3)).astype(np.float64)
+        r = O.rope(x, pos, 500.0)
+        assert np.allclose(np.linalg.norm(r, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+        u, w = rng.standard_normal((2, 20, d))
+        p1 = rng.integers(0, 40, size=(20, 3)).astype(np.float64)
+        p2 = rng.integers(0, 40, size=(20, 3)).astype(np.float64)
+        shift = rng.integers(-30, 30, size=(1, 3)).astype(np.float64)
+        s0 = np.sum(O.rope(u, p1, 500.0) * O.rope(w, p2, 500.0), axis=1)
+        s1 = np.sum(O.rope(u, p1 + shift, 500.0) * O.rope(w, p2 + shift, 500.0), axis=1)
+        assert np.allclose(s0, s1, rtol=1e-11, atol=1e-11)
+        # and it does depend on the difference
+        s2 = np.sum(O.rope(u, p1 + shift, 500.0) * O.rope(w, p2, 500.0), axis=1)
+        assert not np.allclose(s0, s2, atol=1e-3)
+
+
+def test_rope_branches_independent_of_frame_origin_and_memory_untouched():
+    """With the rotary embedding on, SWA and DSWA outputs are unchanged when every
+    frame index is shifted (a stream that started earlier), equal plain
+    attention when every position is the same, and the memory branch ignores it."""
+    wl = I.TINY_F32
+    x = I.make_clip(wl)
+    T, P, H = wl.T, wl.P, wl.H
+    grid_w = 4
+    base = O.hlta_forward(x["q"], x["k"], x["v"], x["a"], x["b"], x["w"], T, P, wl.swa_frames,
+                          wl.dswa_dilation, wl.dswa_taps, wl.gdn_chunk)
+    rot = O.hlta_forward(x["q"], x["k"], x["v"], x["a"], x["b"], x["w"], T, P, wl.swa_frames,
+                         wl.dswa_dilation, wl.dswa_taps, wl.gdn_chunk, rope_cfg=(100.0, grid_w))
+    assert np.array_equal(rot[2], base[2]) and np.array_equal(rot[4], base[4])
+    assert O.rel_l2(rot[0], base[0]) > 1e-3
+    # shifting every frame index by 7: apply by hand through positions with f0 = 7
+    for h in range(H):
+        q, k, v = x["q"][0, :, h], x["k"][0, :, h], x["v"][0, :, h]
+        pos = O.rope_positions(T, P, grid_w, f0=7)
+        o = O.swa(O.rope(q, pos, 100.0), O.rope(k, pos, 100.0), v, T, P, wl.swa_frames)
+        assert np.allclose(o, rot[0][0, :, h], rtol=1e-11, atol=1e-12)
+    # all tokens at one position: the rotation cancels in every score
+    q, k, v = x["q"][0, :, 0], x["k"][0, :, 0], x["v"][0, :, 0]
+    same = np.tile([[3.0, 1.0, 2.0]], (T * P, 1))
+    o = O.swa(O.rope(q, same, 100.0), O.rope(k, same, 100.0), v, T, P, wl.swa_frames)
+    assert np.allclose(o, base[0][0, :, 0], rtol=1e-11, atol=1e-12)
+
+
+def test_rope_stream_equals_full_forward():
+    """The streaming oracle with the rotary embedding (past keys kept rotated
+    at their own frames) equals the rows of the full forward."""
+    wl = I.TINY_F32
+    x = I.make_clip(wl)
+    T, P = wl.T, wl.P
+    cfg = (100.0, 4)
+    full = O.hlta_forward(x["q"], x["k"], x["v"], x["a"], x["b"], x["w"], T, P, wl.swa_frames,
+                          wl.dswa_dilation, wl.dswa_taps, wl.gdn_chunk, rope_cfg=cfg)
+    pre = 3
+    for h in range(wl.H):
+        _, Sp = O.gdn_recurrent(x["q"][0, :pre * P, h], x["k"][0, :pre * P, h], x["v"][0, :pre * P, h],
+                                x["a"][0, :pre * P, h], x["b"][0, :pre * P, h])
+        s = O.StreamHead(P, wl.swa_frames, wl.dswa_dilation, wl.dswa_taps, wl.gdn_chunk, rope_cfg=cfg)
+        s.load_prefix(x["k"][0, :, h], x["v"][0, :, h], pre, Sp)
+        for f in range(pre, T):
+            sl = slice(f * P, (f + 1) * P)
+            outs = s.step(x["q"][0, sl, h], x["k"][0, sl, h], x["v"][0, sl, h], x["a"][0, sl, h],
+                          x["b"][0, sl, h], x["w"][h])
+            for i in range(4):
+                assert np.allclose(outs[i], full[i][0, sl, h], rtol=1e-9, atol=1e-11), (f, i)
