@@ -213,6 +213,39 @@ def rollouts_leg(H, st, frames, w, out, steps):
             "half_sitting_out_ms_per_step": ms_half, "half_sitting_out_tokens_per_s": tps_half}
 
 
+# latent token grid of a frame (rows x columns) for the rotary-embedding leg
+LATENT_GRID = {1560: (30, 52), 3600: (45, 80)}
+
+
+def rope_leg(H, wl, dev, out, S_out, steps, impl):
+    """hlta_fwd with the rotary embedding of the softmax branches on (theta
+    10000, the frame's latent grid) against the same call without it, in the
+    same process: whole-forward time per step for both."""
+    import torch
+    stream = torch.cuda.current_stream()
+    res = {"grid": list(LATENT_GRID[wl.P]), "theta": 10000.0, "steps": steps}
+    for tag, kw in (("with", dict(rope_theta=10000.0, rope_grid=LATENT_GRID[wl.P])), ("without", {})):
+        cfg = H.make_config(wl, impl=impl, **kw)
+        ws = H.alloc_workspace(H.hlta_fwd_workspace_bytes(cfg))
+
+        def fwd():
+            H.hlta_fwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], out=out, S_out=S_out,
+                       workspace=ws, stream=stream)
+        fwd()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fwd()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[f"ms_per_step_{tag}"] = e0.elapsed_time(e1) / steps
+        del ws
+    res["tokens_per_s_with"] = wl.B * wl.L / (res["ms_per_step_with"] * 1e-3)
+    res["extra_ms"] = res["ms_per_step_with"] - res["ms_per_step_without"]
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -222,6 +255,8 @@ def main():
     ap.add_argument("--impl", type=int, default=0, help="0 auto, 1 generic, 2 mfma")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stream-steps", type=int, default=64, help="streaming frame steps to time (0: skip)")
+    ap.add_argument("--rope-steps", type=int, default=5,
+                    help="hlta_fwd steps timed with and without the rotary embedding (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB read + 1 GiB write elementwise kernel (3 launches), to scale "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -308,6 +343,9 @@ def main():
                          "bytes_per_token_head": per_th, "avg_ms": gdn_ms},
         "device": torch.cuda.get_device_name(0),
     }
+    if args.rope_steps > 0 and wl.P in LATENT_GRID:
+        print(f"# rotary-embedding leg, {args.rope_steps} steps", file=sys.stderr, flush=True)
+        res["rope"] = rope_leg(H, wl, dev, out, S_out, args.rope_steps, args.impl)
     if args.stream_steps > 0:
         del dev, out, ws
         torch.cuda.empty_cache()

@@ -67,9 +67,6 @@ __device__ __forceinline__ bf16x4 ld_tr(const bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
-__device__ __forceinline__ bf16x4 ld4(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
-
-
 // direct global -> LDS loads, padded-tile helpers
 __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),

@@ -91,6 +91,21 @@ hlta_status run_mix(const hlta_config* cfg, const Plan& plan, const void* o_swa,
   return HLTA_OK;
 }
 
+// Rotary embedding on: rotate q and k of the softmax branches into the
+// workspace (positions from attn.f0 or attn.ro) and point attn at the copies.
+hlta_status run_rope(const hlta_config* cfg, const Plan& plan, AttnParams& attn, void* workspace, hipStream_t st) {
+  if (cfg->rope_theta <= 0.f) return HLTA_OK;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  void* qr = ws + plan.ws_rope_off;
+  void* kr = ws + plan.ws_rope_off + plan.ws_rope_bytes;
+  hipError_t e = launch_rope_qk(attn.q, attn.k, qr, kr, cfg->B, plan.L, cfg->H, cfg->d, cfg->P, cfg->rope_grid_w,
+                                cfg->rope_theta, cfg->in_dtype, attn.f0, attn.per_rollout, attn.ro, st);
+  if (e != hipSuccess) return hip_fail(e, "rotary embedding launch");
+  attn.q = qr;
+  attn.k = kr;
+  return HLTA_OK;
+}
+
 // One layer: the memory branch (GDN over L tokens per row), the softmax
 // branches, then the per-head mix of the three stored outputs, in order on st.
 // Rollouts in attn.ro.skip are left out of all three.
@@ -99,8 +114,9 @@ hlta_status run_mix(const hlta_config* cfg, const Plan& plan, const void* o_swa,
 // share the chip with the attention branches.) attn.* query fields set by caller.
 hlta_status run_layer(const hlta_config* cfg, const Plan& plan, const void* q, const void* k, const void* v,
                       const float* a, const float* b, const float* S0, float* S_out, void* o_gdn,
-                      const float* mix_w, void* o_mix, void* workspace, AttnParams attn, hipStream_t st) {
+                      const float* mix_w, void* o_mix, void* workspace, AttnParams& attn, hipStream_t st) {
   HLTA_TRY(run_gdn(cfg, plan, q, k, v, a, b, S0, S_out, o_gdn, workspace, st, attn.ro.skip));
+  HLTA_TRY(run_rope(cfg, plan, attn, workspace, st));
   HLTA_TRY(run_attn(cfg, plan, attn, st));
   return run_mix(cfg, plan, attn.o_swa, attn.o_dswa, o_gdn, o_mix, mix_w, st, attn.ro.skip);
 }
@@ -213,6 +229,8 @@ hlta_status hlta_attn_fwd(const hlta_config* cfg, const void* q, const void* k, 
   HLTA_TRY(need(o_swa, "o_swa"));
   HLTA_TRY(need(o_dswa, "o_dswa"));
   HLTA_TRY(need(o_mix, "o_mix"));
+  if (cfg->rope_theta > 0.f)
+    return fail(HLTA_E_UNSUPPORTED, "the rotary embedding needs a workspace: use hlta_fwd");
   AttnParams at = full_attn_params(cfg, q, k, v, o_swa, o_dswa);
   hipStream_t st = static_cast<hipStream_t>(stream);
   HLTA_TRY(run_attn(cfg, plan, at, st));
@@ -256,6 +274,9 @@ hlta_status hlta_stream_load_prefix(const hlta_config* cfg, hlta_stream_state* s
   if (e == hipSuccess)
     e = launch_ring_store(v_prefix, prefix_frames, 0, st->ring_v, st->ring_frames, first, keep, cfg->B,
                           frame_elems, elem, s);
+  if (e == hipSuccess && cfg->rope_theta > 0.f && keep > 0)
+    e = launch_rope_ring(st->ring_k, cfg->B, st->ring_frames, first, int(keep), cfg->H, cfg->d, cfg->P,
+                         cfg->rope_grid_w, cfg->rope_theta, cfg->in_dtype, s);
   if (e != hipSuccess) return hip_fail(e, "ring store");
   e = S_prefix ? (S_prefix == st->S ? hipSuccess
                                     : hipMemcpyAsync(st->S, S_prefix, state_bytes(cfg), hipMemcpyDeviceToDevice, s))
@@ -325,13 +346,14 @@ static hlta_status step_frame_impl(const hlta_config* cfg, hlta_stream_state* st
     const long long frame_elems = (long long)cfg->P * cfg->H * cfg->d;
     const int elem = int(dtype_bytes(cfg->in_dtype));
     hipError_t e = hipSuccess;
+    // the ring keeps the keys the attention read (rotated when the rotary embedding is on)
     if (!frames) {
-      e = launch_ring_store(k_f, 1, f, st->ring_k, st->ring_frames, f, 1, cfg->B, frame_elems, elem, s);
+      e = launch_ring_store(at.k, 1, f, st->ring_k, st->ring_frames, f, 1, cfg->B, frame_elems, elem, s);
       if (e == hipSuccess)
         e = launch_ring_store(v_f, 1, f, st->ring_v, st->ring_frames, f, 1, cfg->B, frame_elems, elem, s);
     } else {
       // each rollout that stepped into the slot of its own frame
-      e = launch_ring_store_rollouts(k_f, st->ring_k, st->ring_frames, cfg->B, frame_elems, elem, at.ro, s);
+      e = launch_ring_store_rollouts(at.k, st->ring_k, st->ring_frames, cfg->B, frame_elems, elem, at.ro, s);
       if (e == hipSuccess)
         e = launch_ring_store_rollouts(v_f, st->ring_v, st->ring_frames, cfg->B, frame_elems, elem, at.ro, s);
     }

@@ -49,6 +49,12 @@ hlta_status check_config(const hlta_config* cfg) {
     return fail(HLTA_E_DTYPE, "float32 inputs need float32 outputs");
   if (cfg->impl != HLTA_IMPL_AUTO && cfg->impl != HLTA_IMPL_GENERIC && cfg->impl != HLTA_IMPL_MFMA)
     return fail(HLTA_E_SHAPE, "impl must be HLTA_IMPL_AUTO, _GENERIC or _MFMA");
+  if (!std::isfinite(cfg->rope_theta) || cfg->rope_theta < 0.f)
+    return fail(HLTA_E_SHAPE, "rope_theta must be finite and >= 0");
+  if (cfg->rope_theta > 0.f &&
+      (cfg->rope_grid_h < 1 || cfg->rope_grid_w < 1 || int64_t(cfg->rope_grid_h) * cfg->rope_grid_w != cfg->P))
+    return fail(HLTA_E_SHAPE, "rope_grid_h * rope_grid_w must equal P (" + std::to_string(cfg->rope_grid_h) +
+                                  " x " + std::to_string(cfg->rope_grid_w) + " vs " + std::to_string(cfg->P) + ")");
   // every element offset must fit in int64, and token counts in int32 grids
   int64_t L, n;
   if (!mul_ok(cfg->T, cfg->P, &L) || !mul_ok(L, cfg->B, &n) || !mul_ok(n, cfg->H, &n) ||
@@ -106,6 +112,14 @@ hlta_status make_plan(const hlta_config* cfg, int64_t L, Plan* plan) {
   if (!mul_ok(int64_t(cfg->B) * cfg->H, p.n_chunks, &nrec)) return fail(HLTA_E_SHAPE, "workspace overflow");
   p.ws_gdn = size_t(nrec) * rec;
   p.ws_total = p.ws_gdn;
+  if (cfg->rope_theta > 0.f) {
+    // rotated q and k of the softmax branches, [B, L, H, d] in_dtype each
+    int64_t n = 0;
+    if (!mul_ok(int64_t(cfg->B) * L, int64_t(cfg->H) * cfg->d, &n)) return fail(HLTA_E_SHAPE, "workspace overflow");
+    p.ws_rope_bytes = align_up(size_t(n) * dtype_bytes(cfg->in_dtype), 256);
+    p.ws_rope_off = align_up(p.ws_gdn, 256);
+    p.ws_total = p.ws_rope_off + 2 * p.ws_rope_bytes;
+  }
   *plan = p;
   return HLTA_OK;
 }

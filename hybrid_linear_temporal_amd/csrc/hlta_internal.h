@@ -20,6 +20,8 @@ struct Plan {
   int64_t L = 0;            // tokens per batch row in this call
   int64_t n_chunks = 0;     // ceil(L / C)
   size_t ws_gdn = 0;        // bytes of GDN scratch
+  size_t ws_rope_off = 0;   // rotated q, then rotated k (rotary embedding on), each ws_rope_bytes
+  size_t ws_rope_bytes = 0;
   size_t ws_total = 0;      // bytes the caller must supply
   float scale = 0.f;        // resolved softmax scale
 };

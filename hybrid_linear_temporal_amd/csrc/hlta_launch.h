@@ -30,6 +30,16 @@ hipError_t launch_ring_store(const void* src, long long src_frames, long long sr
                              int R, long long first_frame, long long n_frames, int B, long long frame_elems,
                              int elem, hipStream_t st);
 
+// Rotary embedding of the softmax branches (reading in rope.hip): q, k
+// [B, L, H, d] (dt) -> rotated copies qr, kr; token t of row b sits in frame
+// (per_rollout ? ro.frame[b] : f0) + t / P; rollouts in ro.skip are left alone.
+hipError_t launch_rope_qk(const void* q, const void* k, void* qr, void* kr, int B, long long L, int H, int d, int P,
+                          int grid_w, float theta, int dt, long long f0, int per_rollout, const RolloutFrames& ro,
+                          hipStream_t st);
+// The same in place over the ring slots of frames first .. first+n-1.
+hipError_t launch_rope_ring(void* ring, int B, int R, long long first, int n, int H, int d, int P, int grid_w,
+                            float theta, int dt, hipStream_t st);
+
 // Streaming with a position per rollout: src [B, P, H, d] holds one frame per
 // rollout; rollout b's goes to ring slot sel.frame[b] mod R (rollouts in
 // sel.skip are left alone).

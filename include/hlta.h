@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define HLTA_ABI_VERSION 1
+#define HLTA_ABI_VERSION 2
 
 typedef enum {
   HLTA_OK = 0,
@@ -81,7 +81,25 @@ typedef struct {
   int32_t in_dtype;       /* hlta_dtype of q, k, v and of the ring buffers */
   int32_t out_dtype;      /* hlta_dtype of every output: (f32,f32), (bf16,bf16), (bf16,f32) */
   int32_t impl;           /* hlta_impl */
+  float rope_theta;       /* > 0: rotary embedding of the softmax branches' q and k (below); 0: none */
+  int32_t rope_grid_h;    /* with rope_theta > 0: the token grid of a latent frame, */
+  int32_t rope_grid_w;    /*   rope_grid_h * rope_grid_w == P, token p at (p / grid_w, p % grid_w) */
 } hlta_config;
+
+/*
+ * Rotary embedding of the softmax branches (optional, rope_theta > 0). The
+ * pages give the local branches as windows over latent frames and name no
+ * positional scheme; the reading implemented: a token's position is
+ * (absolute latent frame, row, column); its d/2 coordinate pairs
+ * (x[2i], x[2i+1]) are rotated as complex numbers by pos_axis * theta^(-j/n),
+ * the first d/8 pairs by the frame, the next half of the rest by the row, the
+ * others by the column (j = the pair's index within its axis, n = the axis's
+ * pair count). q and k of SWA and DSWA are rotated (rounded once to
+ * in_dtype); the memory branch reads them unrotated. Streaming rings hold
+ * rotated keys. hlta_fwd and the streaming calls support it (its rotated
+ * copies live in the workspace); hlta_attn_fwd, which has no workspace,
+ * returns HLTA_E_UNSUPPORTED for it.
+ */
 
 /* ABI version of the loaded library (HLTA_ABI_VERSION). */
 int32_t hlta_abi_version(void);

@@ -31,12 +31,12 @@ def test_library_exports_every_header_symbol(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(H.EXPORTS)
-    assert lib.hlta_abi_version() == 1
+    assert lib.hlta_abi_version() == 2
 
 
 def test_struct_layout_matches_header():
-    # 13 int32 fields + 1 float = 56 bytes; stream state: 3 pointers, int32, int64
-    assert ctypes.sizeof(H.hlta_config) == 14 * 4
+    # 15 int32 fields + 2 floats = 68 bytes; stream state: 3 pointers, int32, int64
+    assert ctypes.sizeof(H.hlta_config) == 17 * 4
     assert ctypes.sizeof(H.hlta_stream_state) == 8 * 3 + 8 + 8
 
 
@@ -160,3 +160,23 @@ def test_step_rollouts_argument_errors(lib):
     big = H.make_config(I.STREAM_P480)
     big.B = 65
     assert call(big, np.zeros(65, dtype=np.int64)) == 4
+
+
+def test_rope_config_checks(lib):
+    """The rotary embedding needs a frame grid of exactly P tokens and a finite
+    theta >= 0; it adds two rotated copies of q, k to the workspaces."""
+    base = _cfg()
+    ws0 = H.hlta_fwd_workspace_bytes(base)
+    good = _cfg(rope_theta=10000.0, rope_grid=(30, 52))
+    H.hlta_validate_config(good)
+    n = good.B * good.T * good.P * good.H * good.d * 2
+    assert H.hlta_fwd_workspace_bytes(good) >= ws0 + 2 * n
+    assert H.hlta_step_workspace_bytes(good) > H.hlta_step_workspace_bytes(base)
+    for theta, grid in ((10000.0, (30, 51)), (10000.0, (0, 1560)), (-1.0, (30, 52)), (float("nan"), (30, 52))):
+        with pytest.raises(H.HLTAError) as e:
+            H.hlta_validate_config(_cfg(rope_theta=theta, rope_grid=grid))
+        assert e.value.status == 2 and b"rope" in lib.hlta_last_error()
+    # hlta_attn_fwd has no workspace for the rotated copies
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.hlta_attn_fwd(ctypes.byref(good), *([fake] * 9)) == 4
+    assert b"workspace" in lib.hlta_last_error()

@@ -220,3 +220,23 @@ def test_scores_far_from_zero(side):
     ref = run_oracle(wl, x)
     got = run_gpu(wl, x)
     compare(got, ref, TOL["bf16"], label=f"scores {side}")
+
+
+ROPE_CASES = [
+    (BF16_CASES[0], (7, 10), 10000.0),   # P = 70, MFMA attention
+    (F32_CASES[0], (5, 10), 500.0),      # P = 50, d = 64, generic attention
+]
+
+
+@pytest.mark.parametrize("wl,grid,theta", ROPE_CASES, ids=lambda c: getattr(c, "name", str(c)))
+def test_rope_matches_oracle_and_leaves_memory_alone(wl, grid, theta):
+    """Rotary embedding of the softmax branches: every branch against the
+    float64 oracle with the same embedding; o_gdn and the state are bit for
+    bit those of the call without it."""
+    x = I.make_clip(wl)
+    ref = run_oracle(wl, x, rope_cfg=(theta, grid[1]))
+    got = run_gpu(wl, x, rope_theta=theta, rope_grid=grid)
+    compare(got, ref, TOL[wl.dtype], label=f"rope {wl.name}")
+    plain = run_gpu(wl, x)
+    assert torch.equal(got["o_gdn"], plain["o_gdn"]) and torch.equal(got["S_out"], plain["S_out"])
+    assert O.rel_l2(to64(got["o_swa"]), to64(plain["o_swa"])) > 1e-3

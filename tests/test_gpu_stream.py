@@ -192,3 +192,69 @@ def test_rollouts_at_own_positions(wl, prefix, R):
     assert np.all(frames > prefix)
     Sref = np.stack([np.stack([ost[b, h].S0 for h in range(wl.H)]) for b in range(B)])
     assert O.rel_l2(to64(st.S), Sref) <= tol
+
+
+@pytest.mark.parametrize("wl,prefix,R", STREAM_CASES, ids=lambda c: getattr(c, "name", str(c)))
+def test_rope_stream_matches_full_forward(wl, prefix, R):
+    """With the rotary embedding on, a streamed frame (its keys and the ring's
+    rotated at their own frames) equals the rows of hlta_fwd over the clip and
+    the float64 stream; the same through hlta_step_frame_rollouts with the
+    rollouts at different positions."""
+    grid = {70: (7, 10), 20: (4, 5)}[wl.P]
+    theta = 1000.0
+    x = I.make_clip(wl)
+    P, B = wl.P, wl.B
+    tol = TOL[wl.dtype]
+    dev = H.to_device(x, wl.dtype)
+    kw = dict(rope_theta=theta, rope_grid=grid)
+    full = H.hlta_fwd(H.make_config(wl, **kw), dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"])
+    ref_full = O.hlta_forward(x["q"], x["k"], x["v"], x["a"], x["b"], x["w"], wl.T, P, wl.swa_frames,
+                              wl.dswa_dilation, wl.dswa_taps, wl.gdn_chunk, rope_cfg=(theta, grid[1]))
+    for i, n in enumerate(BRANCHES):
+        assert O.rel_l2(to64(full[n]), ref_full[i]) <= tol, n
+    pre = {n: t[:, :prefix * P].contiguous() if n != "w" else t for n, t in dev.items()}
+    S_pre = torch.empty((B, wl.H, wl.d, wl.d), dtype=torch.float32, device="cuda")
+    H.hlta_fwd(H.make_config(wl, T=prefix, **kw), pre["q"], pre["k"], pre["v"], pre["a"], pre["b"], pre["w"],
+               S_out=S_pre)
+    cfg = H.make_config(wl, T=1, **kw)
+    st = H.Stream(cfg, R)
+    H.hlta_stream_load_prefix(st, pre["k"], pre["v"], prefix, S_pre)
+    st2 = H.Stream(cfg, R)
+    H.hlta_stream_load_prefix(st2, pre["k"], pre["v"], prefix, S_pre)
+    pos = np.full(B, prefix, dtype=np.int64)
+    for f in range(prefix, min(prefix + 4, wl.T)):
+        fr = {n: t[:, f * P:(f + 1) * P].contiguous() if n != "w" else t for n, t in dev.items()}
+        got = H.hlta_step_frame(st, fr["q"], fr["k"], fr["v"], fr["a"], fr["b"], fr["w"])
+        torch.cuda.synchronize()
+        for n in BRANCHES:
+            e = O.rel_l2(to64(got[n]), to64(full[n][:, f * P:(f + 1) * P]))
+            assert e <= tol, f"frame {f} {n}: {e:.2e}"
+    # rollout 0 runs ahead by two frames, then both step together at their own positions
+    def rows(b_frames):
+        out = {}
+        for n, t in dev.items():
+            if n == "w":
+                out[n] = t
+                continue
+            r = torch.zeros((B, P) + tuple(t.shape[2:]), dtype=t.dtype, device=t.device)
+            for b, f in enumerate(b_frames):
+                if f >= 0:
+                    r[b] = t[b, f * P:(f + 1) * P]
+            out[n] = r.contiguous()
+        return out
+    for mask in ((1, 0), (1, 0), (1, 1), (1, 1)):
+        call = np.where(np.array(mask[:B] + (0,) * max(0, B - 2)) == 1, pos, -1).astype(np.int64)
+        if np.any(call >= wl.T):
+            break
+        before = call.copy()
+        fr = rows(before)
+        got = H.hlta_step_frame_rollouts(st2, call, fr["q"], fr["k"], fr["v"], fr["a"], fr["b"], fr["w"])
+        torch.cuda.synchronize()
+        for b in range(B):
+            if before[b] < 0:
+                continue
+            f = int(before[b])
+            for n in BRANCHES:
+                e = O.rel_l2(to64(got[n][b]), to64(full[n][b, f * P:(f + 1) * P]))
+                assert e <= tol, f"rollout {b} frame {f} {n}: {e:.2e}"
+        pos = np.where(before >= 0, before + 1, pos)
