@@ -31,7 +31,9 @@ Readings taken where the pages are silent (each is listed in the design doc):
     eps = 1e-6 inside the square root, and the read o_t = S_t q_t taken after
     the token's own update;
   * the three outputs are combined as o_mix = w0*o_swa + w1*o_dswa + w2*o_gdn
-    with caller weights w[h, :] and nothing else.
+    with caller weights w[h, :] and nothing else;
+  * optionally the gates arrive as logits and the memory uses their logistic
+    function (the pages give no gate parameterization; see `gates_from_logits`).
 """
 from __future__ import annotations
 
@@ -193,6 +195,17 @@ def gdn_chunked(q, k, v, a, b, C, S0=None, l2norm=True):
     return o, S
 
 
+def gates_from_logits(xa, xb):
+    """Decay and write gates from raw logits (optional reading; the pages name
+    the gates but not how a layer produces them): a = sigmoid(x_a),
+    b = sigmoid(x_b), in the form that does not overflow for either sign."""
+    def sig(x):
+        x = np.asarray(x, np.float64)
+        e = np.exp(-np.abs(x))
+        return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+    return sig(xa), sig(xb)
+
+
 # ---------------------------------------------------------------------------
 # rotary position embedding of the softmax branches (optional)
 # ---------------------------------------------------------------------------
@@ -247,9 +260,13 @@ def rope(x, pos, theta):
 # whole operator
 # ---------------------------------------------------------------------------
 
-def hlta_head(q, k, v, a, b, w3, T, P, W, dil, taps, C, scale=None, S0=None, gdn="chunked", rope_cfg=None):
+def hlta_head(q, k, v, a, b, w3, T, P, W, dil, taps, C, scale=None, S0=None, gdn="chunked", rope_cfg=None,
+              gate_logits=False):
     """HLTA forward of one (batch, head): returns o_swa, o_dswa, o_gdn, o_mix, S_out.
-    rope_cfg = (theta, grid_w): rotary embedding of the softmax branches' q, k."""
+    rope_cfg = (theta, grid_w): rotary embedding of the softmax branches' q, k.
+    gate_logits: a and b are logits (the memory uses their logistic function)."""
+    if gate_logits:
+        a, b = gates_from_logits(a, b)
     qa, ka = q, k
     if rope_cfg is not None:
         theta, grid_w = rope_cfg
@@ -267,7 +284,7 @@ def hlta_head(q, k, v, a, b, w3, T, P, W, dil, taps, C, scale=None, S0=None, gdn
 
 
 def hlta_forward(q, k, v, a, b, w, T, P, W, dil, taps, C, scale=None, S0=None, gdn="chunked",
-                 heads=None, rope_cfg=None):
+                 heads=None, rope_cfg=None, gate_logits=False):
     """HLTA forward over [B, L, H, d] inputs; returns float64 arrays in the same
     layout (o_* [B, L, H, d], S_out [B, H, d_v, d_k]). heads: optional list of
     (b, h) to compute (others stay zero)."""
@@ -279,7 +296,7 @@ def hlta_forward(q, k, v, a, b, w, T, P, W, dil, taps, C, scale=None, S0=None, g
     for bi, hi in todo:
         s0 = None if S0 is None else S0[bi, hi]
         res = hlta_head(q[bi, :, hi], k[bi, :, hi], v[bi, :, hi], a[bi, :, hi], b[bi, :, hi],
-                        w[hi], T, P, W, dil, taps, C, scale, s0, gdn, rope_cfg)
+                        w[hi], T, P, W, dil, taps, C, scale, s0, gdn, rope_cfg, gate_logits)
         for o, r in zip(outs, res[:4]):
             o[bi, :, hi] = r
         S_out[bi, hi] = res[4]
@@ -297,10 +314,11 @@ class StreamHead:
     incremental generation; long-context page, section 02: a recurrent twin of
     the parallel form for decoding)."""
 
-    def __init__(self, P, W, dil, taps, C, scale=None, S0=None, rope_cfg=None):
+    def __init__(self, P, W, dil, taps, C, scale=None, S0=None, rope_cfg=None, gate_logits=False):
         self.P, self.W, self.dil, self.taps, self.C = P, W, dil, taps, C
         self.scale = scale
         self.rope_cfg = rope_cfg   # (theta, grid_w): past keys are kept rotated
+        self.gate_logits = gate_logits
         self.S0 = None if S0 is None else np.array(S0, np.float64)
         self.k = {}
         self.v = {}
@@ -340,6 +358,8 @@ class StreamHead:
 
         o_swa = attend(swa_frames(f, self.W))
         o_dswa = attend(dswa_frames(f, self.dil, self.taps))
+        if self.gate_logits:
+            a, b = gates_from_logits(a, b)
         o_gdn, S = gdn_chunked(q, kf, vf, a, b, self.C, self.S0)
         w3 = np.asarray(w3, np.float64)
         o_mix = w3[0] * o_swa + w3[1] * o_dswa + w3[2] * o_gdn

@@ -43,7 +43,8 @@ def run_oracle(wl: I.Workload, x: dict, S0=None, heads=None, gdn="chunked", **ov
     return O.hlta_forward(x["q"], x["k"], x["v"], x["a"], x["b"], x["w"], T, wl.P,
                           over.get("swa_frames", wl.swa_frames), over.get("dswa_dilation", wl.dswa_dilation),
                           over.get("dswa_taps", wl.dswa_taps), over.get("gdn_chunk", wl.gdn_chunk),
-                          S0=S0, gdn=gdn, heads=heads, rope_cfg=over.get("rope_cfg"))
+                          S0=S0, gdn=gdn, heads=heads, rope_cfg=over.get("rope_cfg"),
+                          gate_logits=over.get("gate_logits", False))
 
 
 def compare(gpu: dict, ref, tol: float, heads=None, label=""):

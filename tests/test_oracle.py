@@ -474,3 +474,33 @@ def test_rope_stream_equals_full_forward():
                           x["b"][0, sl, h], x["w"][h])
             for i in range(4):
                 assert np.allclose(outs[i], full[i][0, sl, h], rtol=1e-9, atol=1e-11), (f, i)
+
+
+# ---------------------------------------------------------------------------
+# gates given as logits (optional)
+# ---------------------------------------------------------------------------
+
+def test_gate_logits_are_the_logistic_function():
+    """The oracle's gates from logits are scipy's logistic function, over the
+    whole range (no overflow at either end)."""
+    from scipy.special import expit
+    x = np.concatenate([np.linspace(-800, 800, 4001), [0.0, 1e-9, -1e-9]])
+    a, b = O.gates_from_logits(x, -x)
+    assert np.allclose(a, expit(x), rtol=1e-15, atol=1e-300) and np.allclose(b, expit(-x), rtol=1e-15, atol=1e-300)
+    assert a[-3] == 0.5 and np.all(np.isfinite(a)) and np.all((a >= 0) & (a <= 1))
+
+
+def test_gate_logits_forward_equals_forward_on_the_gates():
+    """Feeding the logits of the generated gates reproduces the forward on the
+    gates themselves (decay to a, write to b: swapping them would not)."""
+    wl = I.TINY_F32
+    x = I.make_clip(wl)
+    a64, b64 = x["a"].astype(np.float64), x["b"].astype(np.float64)
+    xa, xb = np.log(a64 / (1.0 - a64)), np.log(b64 / (1.0 - b64))
+    args = (wl.T, wl.P, wl.swa_frames, wl.dswa_dilation, wl.dswa_taps, wl.gdn_chunk)
+    ref = O.hlta_forward(x["q"], x["k"], x["v"], x["a"], x["b"], x["w"], *args)
+    got = O.hlta_forward(x["q"], x["k"], x["v"], xa, xb, x["w"], *args, gate_logits=True)
+    for r, g in zip(ref, got):
+        assert np.allclose(g, r, rtol=1e-9, atol=1e-12)
+    swapped = O.hlta_forward(x["q"], x["k"], x["v"], xb, xa, x["w"], *args, gate_logits=True)
+    assert O.rel_l2(swapped[2], ref[2]) > 1e-2
