@@ -77,10 +77,7 @@ gdn_prep_generic(GdnParams p) {
     float acc = 0.f;
     for (int i = 0; i < C; ++i) {
       float la = 0.f, bi = 0.f;
-      if (i < n) {
-        la = fmaxf(logf(p.a[gbase + size_t(i) * p.H]), kLogAFloor);
-        bi = p.b[gbase + size_t(i) * p.H];
-      }
+      if (i < n) load_gates(p.a, p.b, gbase + size_t(i) * p.H, p.gate_logits, kLogAFloor, la, bi);
       acc += la;
       g[i] = acc;
       bb[i] = bi;

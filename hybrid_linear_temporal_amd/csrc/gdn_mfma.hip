@@ -168,10 +168,7 @@ gdn_prep_mfma(GdnParams p) {
   if (wave == 0) {
     // gates: inclusive scan of log a over the chunk (one token per lane)
     float la = 0.f, bi = 0.f;
-    if (lane < n) {
-      la = fmaxf(logf(p.a[gbase + size_t(lane) * p.H]), kLogAFloor);
-      bi = p.b[gbase + size_t(lane) * p.H];
-    }
+    if (lane < n) load_gates(p.a, p.b, gbase + size_t(lane) * p.H, p.gate_logits, kLogAFloor, la, bi);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float y = __shfl_up(la, off);

@@ -67,6 +67,7 @@ hlta_status run_gdn(const hlta_config* cfg, const Plan& plan, const void* q, con
   g.L = plan.L;
   g.n_chunks = int(plan.n_chunks);
   g.l2norm = cfg->gdn_l2norm_qk;
+  g.gate_logits = cfg->gate_logits;
   hipError_t e = plan.gdn == Impl::Mfma
                      ? launch_gdn_mfma(g, cfg->out_dtype, st)
                      : launch_gdn_generic(g, cfg->d, cfg->gdn_chunk, cfg->in_dtype, cfg->out_dtype, st);

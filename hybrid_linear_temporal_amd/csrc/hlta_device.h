@@ -75,6 +75,22 @@ __device__ __forceinline__ const T* key_frame_ptr(const T* main, const T* ring, 
   return ring + ((size_t(b) * p.R + slot) * p.P * p.H + h) * D;
 }
 
+// Decay and write gates of one token as the memory uses them: log a (floored)
+// and b, from the given gates or, with logits, from log sigmoid(x_a) and
+// sigmoid(x_b); log sigmoid(x) = min(x, 0) - log1p(exp(-|x|)) has no
+// cancellation for either sign.
+__device__ __forceinline__ void load_gates(const float* a, const float* b, size_t i, int logits, float floor_log_a,
+                                           float& la, float& bi) {
+  const float xa = a[i], xb = b[i];
+  if (logits) {
+    la = fmaxf(fminf(xa, 0.f) - log1pf(expf(-fabsf(xa))), floor_log_a);
+    bi = 1.f / (1.f + expf(-xb));
+  } else {
+    la = fmaxf(logf(xa), floor_log_a);
+    bi = xb;
+  }
+}
+
 // Frame sets of query frame f (absolute): SWA reads frames f-nswa+1 .. f,
 // DSWA reads f - dil*(s+1) for s < ndswa.
 __device__ __forceinline__ int swa_count(long long f, int W) {
@@ -104,6 +120,7 @@ struct GdnParams {
   long long L;
   int n_chunks;
   int l2norm;
+  int gate_logits;           // a, b hold logits: the gates are sigmoid(a), sigmoid(b)
   unsigned long long skip;   // rollouts left out (bit b)
 };
 

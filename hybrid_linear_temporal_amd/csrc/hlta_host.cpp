@@ -49,6 +49,7 @@ hlta_status check_config(const hlta_config* cfg) {
     return fail(HLTA_E_DTYPE, "float32 inputs need float32 outputs");
   if (cfg->impl != HLTA_IMPL_AUTO && cfg->impl != HLTA_IMPL_GENERIC && cfg->impl != HLTA_IMPL_MFMA)
     return fail(HLTA_E_SHAPE, "impl must be HLTA_IMPL_AUTO, _GENERIC or _MFMA");
+  if (cfg->gate_logits != 0 && cfg->gate_logits != 1) return fail(HLTA_E_SHAPE, "gate_logits must be 0 or 1");
   if (!std::isfinite(cfg->rope_theta) || cfg->rope_theta < 0.f)
     return fail(HLTA_E_SHAPE, "rope_theta must be finite and >= 0");
   if (cfg->rope_theta > 0.f &&

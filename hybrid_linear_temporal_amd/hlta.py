@@ -36,7 +36,7 @@ class hlta_config(ctypes.Structure):
                 ("dswa_taps", ctypes.c_int32), ("gdn_chunk", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("gdn_l2norm_qk", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("impl", ctypes.c_int32), ("rope_theta", ctypes.c_float), ("rope_grid_h", ctypes.c_int32),
-                ("rope_grid_w", ctypes.c_int32)]
+                ("rope_grid_w", ctypes.c_int32), ("gate_logits", ctypes.c_int32)]
 
 
 class hlta_stream_state(ctypes.Structure):
@@ -110,7 +110,7 @@ def _tdtype(dt: int):
 
 def make_config(wl: _inputs.Workload | None = None, *, impl: int = HLTA_IMPL_AUTO, out_dtype: str | None = None,
                 softmax_scale: float = 0.0, l2norm: bool = True, rope_theta: float = 0.0, rope_grid=(0, 0),
-                **over) -> hlta_config:
+                gate_logits: bool = False, **over) -> hlta_config:
     """hlta_config from a Workload (fields can be overridden by keyword).
     rope_theta > 0 with rope_grid = (rows, columns) of a frame turns on the
     rotary embedding of the softmax branches."""
@@ -121,7 +121,7 @@ def make_config(wl: _inputs.Workload | None = None, *, impl: int = HLTA_IMPL_AUT
     out_dt = in_dt if out_dtype is None else (HLTA_BF16 if out_dtype == "bf16" else HLTA_F32)
     return hlta_config(f["B"], f["H"], f["T"], f["P"], f["d"], f["swa_frames"], f["dswa_dilation"],
                        f["dswa_taps"], f["gdn_chunk"], softmax_scale, int(l2norm), in_dt, out_dt, impl,
-                       float(rope_theta), int(rope_grid[0]), int(rope_grid[1]))
+                       float(rope_theta), int(rope_grid[0]), int(rope_grid[1]), int(bool(gate_logits)))
 
 
 def hlta_validate_config(cfg: hlta_config) -> None:

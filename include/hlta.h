@@ -31,7 +31,8 @@
  *             returns HLTA_E_HIP. Faults inside kernels surface at the caller's
  *             synchronisation. Gate values are not checked: a in (0, 1] and
  *             b in [0, 1] give the contractive memory; a = 0 is accepted (its
- *             logarithm is floored at -80).
+ *             logarithm is floored at -80). With cfg->gate_logits = 1 they
+ *             are logits instead (below).
  */
 #ifndef HLTA_H
 #define HLTA_H
@@ -84,6 +85,7 @@ typedef struct {
   float rope_theta;       /* > 0: rotary embedding of the softmax branches' q and k (below); 0: none */
   int32_t rope_grid_h;    /* with rope_theta > 0: the token grid of a latent frame, */
   int32_t rope_grid_w;    /*   rope_grid_h * rope_grid_w == P, token p at (p / grid_w, p % grid_w) */
+  int32_t gate_logits;    /* 1: a and b hold logits; the memory uses sigmoid(a) and sigmoid(b) (below) */
 } hlta_config;
 
 /*
@@ -99,6 +101,13 @@ typedef struct {
  * rotated keys. hlta_fwd and the streaming calls support it (its rotated
  * copies live in the workspace); hlta_attn_fwd, which has no workspace,
  * returns HLTA_E_UNSUPPORTED for it.
+ *
+ * Gate logits (optional, gate_logits = 1). The pages give the decay and write
+ * gates but not how a layer produces them; the reading implemented: a and b
+ * arrive as raw per-token logits and the memory branch applies the logistic
+ * function as it loads them (in fp32: log a = log sigmoid(x_a), computed
+ * without cancellation, floored at -80; b = sigmoid(x_b)). Both gates then lie
+ * in (0, 1), the contractive range.
  */
 
 /* ABI version of the loaded library (HLTA_ABI_VERSION). */

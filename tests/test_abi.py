@@ -35,8 +35,8 @@ def test_library_exports_every_header_symbol(lib):
 
 
 def test_struct_layout_matches_header():
-    # 15 int32 fields + 2 floats = 68 bytes; stream state: 3 pointers, int32, int64
-    assert ctypes.sizeof(H.hlta_config) == 17 * 4
+    # 16 int32 fields + 2 floats = 72 bytes; stream state: 3 pointers, int32, int64
+    assert ctypes.sizeof(H.hlta_config) == 18 * 4
     assert ctypes.sizeof(H.hlta_stream_state) == 8 * 3 + 8 + 8
 
 
@@ -52,7 +52,7 @@ def test_valid_configs(lib):
 @pytest.mark.parametrize("field,value,status", [
     ("B", 0, 2), ("H", 0, 2), ("T", -1, 2), ("P", 0, 2), ("d", 96, 4), ("swa_frames", -1, 2),
     ("dswa_dilation", 0, 2), ("dswa_taps", -2, 2), ("gdn_chunk", 48, 4), ("in_dtype", 7, 3),
-    ("impl", 9, 2), ("softmax_scale", float("inf"), 2), ("gdn_l2norm_qk", 2, 2)])
+    ("impl", 9, 2), ("softmax_scale", float("inf"), 2), ("gdn_l2norm_qk", 2, 2), ("gate_logits", 3, 2)])
 def test_invalid_config_codes(lib, field, value, status):
     cfg = _cfg()
     setattr(cfg, field, value)

@@ -240,3 +240,20 @@ def test_rope_matches_oracle_and_leaves_memory_alone(wl, grid, theta):
     plain = run_gpu(wl, x)
     assert torch.equal(got["o_gdn"], plain["o_gdn"]) and torch.equal(got["S_out"], plain["S_out"])
     assert O.rel_l2(to64(got["o_swa"]), to64(plain["o_swa"])) > 1e-3
+
+
+@pytest.mark.parametrize("wl", [BF16_CASES[0], F32_CASES[1]], ids=lambda w: w.name)
+def test_gate_logits_in_kernel(wl):
+    """Gates passed as logits and turned into gates inside the memory branch
+    match the float64 oracle on the gates themselves (the round trip through
+    the logistic function) and the oracle's logit mode."""
+    x = I.make_clip(wl)
+    a64, b64 = x["a"].astype(np.float64), x["b"].astype(np.float64)
+    xl = dict(x)
+    xl["a"] = np.log(a64 / (1.0 - a64)).astype(np.float32)
+    xl["b"] = np.log(b64 / (1.0 - b64)).astype(np.float32)
+    ref = run_oracle(wl, xl, gate_logits=True)
+    got = run_gpu(wl, xl, gate_logits=True)
+    compare(got, ref, TOL[wl.dtype], label=f"gate logits {wl.name}")
+    ref_gates = run_oracle(wl, x)
+    compare(got, ref_gates, TOL[wl.dtype], label=f"gate logits vs gates {wl.name}")
