@@ -371,6 +371,62 @@ class StreamHead:
 
 
 # ---------------------------------------------------------------------------
+# FP8 (e4m3) variant of the softmax branches: input quantisation
+# ---------------------------------------------------------------------------
+#
+# The pages mention low-precision attention without a method. The variant
+# implemented: q, k, v quantised per (batch row, head) to the e4m3 format
+# (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; largest finite
+# value 448; subnormals down to 2^-9) with the scale s = max|x| / 448, codes
+# = e4m3(x / s) rounded to nearest, ties to even, after clamping to +-448;
+# x / s and s itself are taken in float32 (both sides decide the codes in the
+# same precision). The attention then runs on the decoded values times s.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_encode(x):
+    """Nearest e4m3 code (ties to even) of float values already within +-448."""
+    x = np.asarray(x, np.float64)
+    a = np.abs(x)
+    sign = np.where(np.signbit(x), 0x80, 0)
+    code = np.zeros(x.shape, np.int64)
+    sub = a < 2.0 ** -6
+    code[sub] = np.rint(a[sub] / 2.0 ** -9).astype(np.int64)          # 0 .. 8 (8 = smallest normal)
+    nrm = ~sub
+    e = np.floor(np.log2(a[nrm])).astype(np.int64)
+    m = np.rint((a[nrm] / 2.0 ** e - 1.0) * 8.0).astype(np.int64)       # 0 .. 8
+    e = np.where(m == 8, e + 1, e)
+    m = np.where(m == 8, 0, m)
+    code[nrm] = (e + 7) * 8 + m
+    return (code | sign).astype(np.uint8)
+
+
+def e4m3_decode(code):
+    """Value of e4m3 codes (0x7f / 0xff, the NaN codes, are never produced here)."""
+    c = np.asarray(code, np.int64)
+    e, m = (c >> 3) & 15, c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    return np.where(c & 0x80, -mag, mag)
+
+
+def quantize_e4m3(x):
+    """Per-(batch row, head) e4m3 quantisation of x [B, L, H, d]: returns codes
+    (uint8, same shape) and the float32 scales [B, H]."""
+    x32 = np.asarray(x, np.float32)
+    amax = np.abs(x32).max(axis=(1, 3))                                # [B, H]
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    y = (x32 / scale[:, None, :, None]).astype(np.float32)
+    y = np.clip(y, -E4M3_MAX, E4M3_MAX)
+    return e4m3_encode(y), scale
+
+
+def dequantize_e4m3(code, scale):
+    """Decoded values times their (batch row, head) scale, float64."""
+    return e4m3_decode(code) * np.asarray(scale, np.float64)[:, None, :, None]
+
+
+# ---------------------------------------------------------------------------
 # comparison
 # ---------------------------------------------------------------------------
 

@@ -504,3 +504,44 @@ def test_gate_logits_forward_equals_forward_on_the_gates():
         assert np.allclose(g, r, rtol=1e-9, atol=1e-12)
     swapped = O.hlta_forward(x["q"], x["k"], x["v"], xb, xa, x["w"], *args, gate_logits=True)
     assert O.rel_l2(swapped[2], ref[2]) > 1e-2
+
+
+# ---------------------------------------------------------------------------
+# e4m3 quantisation of the FP8 variant
+# ---------------------------------------------------------------------------
+
+def test_e4m3_codes_by_hand_and_against_torch():
+    """Codes worked out from the format (bias 7, 3 mantissa bits, 448 largest,
+    2^-9 smallest) and torch's float8_e4m3fn cast on values spanning every
+    binade, the subnormals and exact ties (round half to even)."""
+    hand = {1.0: 0x38, 448.0: 0x7E, 2.0 ** -9: 0x01, -7.5: 0xCF, 0.0: 0x00, 1.0625: 0x38, 1.1875: 0x3A,
+            2.0 ** -10: 0x00, 3 * 2.0 ** -10: 0x02, 0.015625: 0x08, 240.0: 0x77, 256.0: 0x78}
+    for v, c in hand.items():
+        assert int(O.e4m3_encode(np.array([v]))[0]) == c, (v, hex(c))
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.uniform(-448, 448, 20000), np.exp2(rng.uniform(-12, 8.8, 20000)) * rng.choice([-1, 1], 20000),
+                        (np.arange(1, 2000) * 2.0 ** -10), np.float32(1.0) + np.arange(16) / 16.0])
+    x = np.clip(x, -448, 448).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = O.e4m3_encode(x)
+    assert np.array_equal(got, want)
+    # decoding returns exactly the representable values torch gives back
+    assert np.array_equal(O.e4m3_decode(got), torch.from_numpy(x).to(torch.float8_e4m3fn).double().numpy())
+
+
+def test_quantize_scales_and_error_bound():
+    """Per-(batch row, head) scale = max|x| / 448 (float32); the largest
+    magnitude maps to the code 448; every element is recovered within half a
+    unit of its binade (relative 2^-4), or 2^-10 s in the subnormal range."""
+    x = np.random.default_rng(4).standard_normal((2, 300, 3, 32)).astype(np.float32) * 3
+    x[1, :, 2] = 0.0                                   # an all-zero head: scale 1, codes 0
+    code, s = O.quantize_e4m3(x)
+    amax = np.abs(x).max(axis=(1, 3))
+    assert s.dtype == np.float32 and s[1, 2] == 1.0 and np.all(code[1, :, 2] == 0)
+    assert np.allclose(s[amax > 0], amax[amax > 0] / 448.0, rtol=1e-7)
+    deq = O.dequantize_e4m3(code, s)
+    err = np.abs(deq - x)
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * s[:, None, :, None]) * (1 + 1e-6)
+    assert np.all(err <= bound)
+    for b, h in ((0, 0), (0, 2), (1, 1)):
+        assert np.max(np.abs(O.e4m3_decode(code[b, :, h]))) == 448.0
