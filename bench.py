@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 METRIC = "HLTA fwd tokens/s at 480P 31 latent frames (1 MI355X); % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 
 
 def valid_pairs(T, P, W, dil, taps):
@@ -246,6 +247,34 @@ def rope_leg(H, wl, dev, out, S_out, steps, impl):
     return res
 
 
+def fp8_leg(H, wl, dev, out, steps, impl, attn_ms_bf16):
+    """The FP8 variant of the softmax branches on the same clip: quantisation
+    (per (batch row, head) e4m3 codes and scales) and the attention kernel,
+    each timed with HIP events, against the bf16 attention timed in this run."""
+    import torch
+    stream = torch.cuda.current_stream()
+    cfg = H.make_config(wl, impl=impl)
+    fp8 = H.hlta_quantize_fp8(cfg, dev["q"], dev["k"], dev["v"], stream=stream)
+    H.hlta_attn_fwd_fp8(cfg, fp8, dev["w"], out["o_gdn"], out, stream=stream)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        e[0].record(stream)
+        H.hlta_quantize_fp8(cfg, dev["q"], dev["k"], dev["v"], stream=stream)
+        e[1].record(stream)
+        H.hlta_attn_fwd_fp8(cfg, fp8, dev["w"], out["o_gdn"], out, stream=stream)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    q_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    a_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    flops = work(wl)[0]
+    tf = flops / (a_ms * 1e-3) / 1e12
+    return {"steps": steps, "quantize_ms": q_ms, "attn_ms": a_ms, "attn_tflops": tf,
+            "frac_of_fp8_peak": tf / PEAK_FP8_TFLOPS, "attn_ms_bf16": attn_ms_bf16,
+            "attn_speedup_vs_bf16": attn_ms_bf16 / a_ms,
+            "note": "attn_ms includes the mix kernel, as the bf16 attention time does"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -255,6 +284,8 @@ def main():
     ap.add_argument("--impl", type=int, default=0, help="0 auto, 1 generic, 2 mfma")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stream-steps", type=int, default=64, help="streaming frame steps to time (0: skip)")
+    ap.add_argument("--fp8-steps", type=int, default=5,
+                    help="steps of the FP8 softmax branches timed (0: skip)")
     ap.add_argument("--rope-steps", type=int, default=5,
                     help="hlta_fwd steps timed with and without the rotary embedding (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -343,6 +374,9 @@ def main():
                          "bytes_per_token_head": per_th, "avg_ms": gdn_ms},
         "device": torch.cuda.get_device_name(0),
     }
+    if args.fp8_steps > 0 and wl.d == 128 and wl.P >= 64:
+        print(f"# FP8 leg, {args.fp8_steps} steps", file=sys.stderr, flush=True)
+        res["fp8"] = fp8_leg(H, wl, dev, out, args.fp8_steps, args.impl, attn_ms)
     if args.rope_steps > 0 and wl.P in LATENT_GRID:
         print(f"# rotary-embedding leg, {args.rope_steps} steps", file=sys.stderr, flush=True)
         res["rope"] = rope_leg(H, wl, dev, out, S_out, args.rope_steps, args.impl)

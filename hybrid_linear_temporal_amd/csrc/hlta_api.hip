@@ -238,6 +238,53 @@ hlta_status hlta_attn_fwd(const hlta_config* cfg, const void* q, const void* k, 
   return run_mix(cfg, plan, o_swa, o_dswa, o_gdn, o_mix, mix_w, st);
 }
 
+hlta_status hlta_quantize_fp8(const hlta_config* cfg, const void* q, const void* k, const void* v, void* q8,
+                              void* k8, void* v8, float* scales, void* stream) {
+  clear_error();
+  HLTA_TRY(check_config(cfg));
+  HLTA_TRY(need(q, "q"));
+  HLTA_TRY(need(k, "k"));
+  HLTA_TRY(need(v, "v"));
+  HLTA_TRY(need(q8, "q8"));
+  HLTA_TRY(need(k8, "k8"));
+  HLTA_TRY(need(v8, "v8"));
+  HLTA_TRY(need(scales, "scales"));
+  const long long L = (long long)cfg->T * cfg->P;
+  hipError_t e = launch_quantize_e4m3(q, k, v, q8, k8, v8, scales, cfg->B, L, cfg->H, cfg->d, cfg->in_dtype,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "quantisation launch");
+  return HLTA_OK;
+}
+
+hlta_status hlta_attn_fwd_fp8(const hlta_config* cfg, const void* q8, const void* k8, const void* v8,
+                              const float* scales, const float* mix_w, const void* o_gdn, void* o_swa,
+                              void* o_dswa, void* o_mix, void* stream) {
+  clear_error();
+  Plan plan;
+  HLTA_TRY(check_config(cfg));
+  HLTA_TRY(make_plan(cfg, int64_t(cfg->T) * cfg->P, &plan));
+  if (cfg->d != 128 || cfg->P < 64)
+    return fail(HLTA_E_UNSUPPORTED, "the FP8 softmax branches need d = 128 and P >= 64");
+  if (cfg->rope_theta > 0.f)
+    return fail(HLTA_E_UNSUPPORTED, "the FP8 softmax branches take codes of already rotated q and k");
+  if (plan.L == 0) return HLTA_OK;
+  HLTA_TRY(need(q8, "q8"));
+  HLTA_TRY(need(k8, "k8"));
+  HLTA_TRY(need(v8, "v8"));
+  HLTA_TRY(need(scales, "scales"));
+  HLTA_TRY(need(mix_w, "mix_w"));
+  HLTA_TRY(need(o_gdn, "o_gdn"));
+  HLTA_TRY(need(o_swa, "o_swa"));
+  HLTA_TRY(need(o_dswa, "o_dswa"));
+  HLTA_TRY(need(o_mix, "o_mix"));
+  AttnParams at = full_attn_params(cfg, q8, k8, v8, o_swa, o_dswa);
+  at.scale_log2 = plan.scale * kLog2e;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_attn_fp8(at, scales, cfg->out_dtype, st);
+  if (e != hipSuccess) return hip_fail(e, "FP8 attention launch");
+  return run_mix(cfg, plan, o_swa, o_dswa, o_gdn, o_mix, mix_w, st);
+}
+
 static hlta_status check_stream(const hlta_config* cfg, const hlta_stream_state* st) {
   if (!st) return fail(HLTA_E_NULL, "stream state is NULL");
   HLTA_TRY(need(st->S, "state S"));

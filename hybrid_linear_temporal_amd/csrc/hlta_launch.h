@@ -19,6 +19,13 @@ hipError_t launch_mix(const void* o_swa, const void* o_dswa, const void* o_gdn, 
                       long long ntok, int H, int d, int out_dt, hipStream_t st, unsigned long long skip = 0,
                       long long rollout_tokens = 1);
 
+// FP8 variant of the softmax branches: SWA + DSWA on e4m3 codes (q, k, v of p)
+// with float32 scales [B, H, 3] (q, k, v per head), d = 128, P >= 64.
+hipError_t launch_attn_fp8(const AttnParams& p, const float* scales, int out_dt, hipStream_t st);
+// e4m3 codes of q, k, v [B, L, H, d] (dt) with per-(b, h, tensor) scales.
+hipError_t launch_quantize_e4m3(const void* q, const void* k, const void* v, void* q8, void* k8, void* v8,
+                                float* scales, int B, long long L, int H, int d, int dt, hipStream_t st);
+
 // Gated delta rule, chunked form, fp32 arithmetic (any supported d, C, dtype).
 hipError_t launch_gdn_generic(const GdnParams& p, int d, int C, int in_dt, int out_dt, hipStream_t st);
 // Gated delta rule, chunked form with bf16 MFMA (bf16 inputs, d = 128, C = 64).

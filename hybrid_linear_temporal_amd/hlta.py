@@ -27,7 +27,7 @@ STATUS = {0: "HLTA_OK", 1: "HLTA_E_NULL", 2: "HLTA_E_SHAPE", 3: "HLTA_E_DTYPE", 
 EXPORTS = ("hlta_abi_version", "hlta_status_string", "hlta_last_error", "hlta_validate_config",
            "hlta_fwd_workspace_bytes", "hlta_fwd", "hlta_gdn_fwd", "hlta_attn_fwd", "hlta_stream_ring_bytes",
            "hlta_stream_load_prefix", "hlta_step_workspace_bytes", "hlta_step_frame",
-           "hlta_step_frame_rollouts")
+           "hlta_step_frame_rollouts", "hlta_quantize_fp8", "hlta_attn_fwd_fp8")
 
 
 class hlta_config(ctypes.Structure):
@@ -80,6 +80,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "hlta_step_frame": (I32, [cfgp, stp, P, P, P, P, P, P, P, P, P, P, I32, P, S, P]),
         "hlta_step_frame_rollouts": (I32, [cfgp, stp, ctypes.POINTER(I64), P, P, P, P, P, P, P, P, P, P, I32, P,
                                            S, P]),
+        "hlta_quantize_fp8": (I32, [cfgp, P, P, P, P, P, P, P, P]),
+        "hlta_attn_fwd_fp8": (I32, [cfgp, P, P, P, P, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -184,6 +186,25 @@ def hlta_attn_fwd(cfg: hlta_config, q, k, v, mix_w, o_gdn, out: dict, stream=Non
     _check(load_library().hlta_attn_fwd(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(mix_w), _ptr(o_gdn),
                                         _ptr(out["o_swa"]), _ptr(out["o_dswa"]), _ptr(out["o_mix"]),
                                         _stream(stream)))
+
+
+def hlta_quantize_fp8(cfg: hlta_config, q, k, v, stream=None) -> dict:
+    """e4m3 codes (uint8 tensors) of q, k, v and their [B, H, 3] float32 scales
+    (C: hlta_quantize_fp8)."""
+    q8 = torch.empty(q.shape, dtype=torch.uint8, device=q.device)
+    k8, v8 = torch.empty_like(q8), torch.empty_like(q8)
+    scales = torch.empty((cfg.B, cfg.H, 3), dtype=torch.float32, device=q.device)
+    _check(load_library().hlta_quantize_fp8(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(q8), _ptr(k8),
+                                            _ptr(v8), _ptr(scales), _stream(stream)))
+    return {"q8": q8, "k8": k8, "v8": v8, "scales": scales}
+
+
+def hlta_attn_fwd_fp8(cfg: hlta_config, fp8: dict, mix_w, o_gdn, out: dict, stream=None):
+    """Softmax branches on e4m3 codes and the mix (C: hlta_attn_fwd_fp8)."""
+    _check(load_library().hlta_attn_fwd_fp8(ctypes.byref(cfg), _ptr(fp8["q8"]), _ptr(fp8["k8"]), _ptr(fp8["v8"]),
+                                            _ptr(fp8["scales"]), _ptr(mix_w), _ptr(o_gdn), _ptr(out["o_swa"]),
+                                            _ptr(out["o_dswa"]), _ptr(out["o_mix"]), _stream(stream)))
+    return out
 
 
 class Stream:

@@ -182,6 +182,35 @@ hlta_status hlta_attn_fwd(const hlta_config* cfg,
                           void* o_swa, void* o_dswa, void* o_mix, void* stream);
 
 /*
+ * FP8 variant of the softmax branches. The pages mention low-precision
+ * attention without a method; the variant implemented quantises q, k, v per
+ * (batch row, head) to e4m3 (1 sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; largest finite value 448) and runs SWA and DSWA with 8-bit MFMA
+ * products accumulated in fp32, the softmax in fp32 and P rounded to e4m3.
+ *
+ * hlta_quantize_fp8 - codes and scales: for each (b, h) and tensor,
+ * s = max|x| / 448 (1 when the head is all zero), code = e4m3(x / s) with x / s
+ * in float32 clamped to +-448, rounded to nearest, ties to even.
+ * q, k, v [B, L, H, d] in_dtype (read only); q8, k8, v8 [B, L, H, d] bytes
+ * (written); scales [B, H, 3] float32 (written; s of q, k, v).
+ */
+hlta_status hlta_quantize_fp8(const hlta_config* cfg, const void* q, const void* k, const void* v,
+                              void* q8, void* k8, void* v8, float* scales, void* stream);
+
+/*
+ * hlta_attn_fwd_fp8 - hlta_attn_fwd on e4m3 codes: o_swa, o_dswa equal exact
+ * softmax attention over the dequantised inputs (code x scale) up to the
+ * rounding of P to e4m3 (numerator and denominator both use the rounded P);
+ * o_mix as in hlta_attn_fwd. d = 128 and P >= 64 (HLTA_E_UNSUPPORTED
+ * otherwise); cfg->in_dtype is not used; no rotary embedding (rotate before
+ * quantising). Arguments as in hlta_attn_fwd with q8, k8, v8, scales as
+ * hlta_quantize_fp8 writes them.
+ */
+hlta_status hlta_attn_fwd_fp8(const hlta_config* cfg, const void* q8, const void* k8, const void* v8,
+                              const float* scales, const float* mix_w, const void* o_gdn,
+                              void* o_swa, void* o_dswa, void* o_mix, void* stream);
+
+/*
  * Streaming (Kairos article on zhichai.net, section 2.3: streaming tokens so
  * generation proceeds incrementally without recomputing the sequence).
  *

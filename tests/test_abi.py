@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _header_functions():
     src = open(os.path.join(ROOT, "include", "hlta.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(hlta_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(hlta_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")

@@ -257,3 +257,61 @@ def test_gate_logits_in_kernel(wl):
     compare(got, ref, TOL[wl.dtype], label=f"gate logits {wl.name}")
     ref_gates = run_oracle(wl, x)
     compare(got, ref_gates, TOL[wl.dtype], label=f"gate logits vs gates {wl.name}")
+
+
+# ---------------------------------------------------------------------------
+# FP8 variant of the softmax branches
+# ---------------------------------------------------------------------------
+
+FP8_CASES = [BF16_CASES[0], BF16_CASES[1], BF16_CASES[4]]
+# P is rounded to e4m3 (at most 2^-4 of its binade, uniformly spread: rms
+# about 2^-4/sqrt(3) relative) and the numerator and denominator both use the
+# rounded P. The outputs are themselves averages of v rows, so their relative
+# error stays near the relative error of the weights instead of averaging
+# away: about 1.3e-2 against exact attention over the same dequantised inputs
+# at these sizes, bound 3e-2; the e4m3 rounding of q, k, v (same size per
+# element) brings it to about 3e-2 against the unquantised inputs, bound 5e-2.
+TOL_FP8_SAME_INPUTS = 3e-2
+TOL_FP8_VS_EXACT = 5e-2
+
+
+@pytest.mark.parametrize("wl", [BF16_CASES[0], F32_CASES[1]], ids=lambda w: w.name)
+def test_quantize_fp8_matches_oracle_bit_for_bit(wl):
+    """e4m3 codes and per-(batch row, head) scales equal the oracle's exactly."""
+    x = I.make_clip(wl)
+    dev = H.to_device(x, wl.dtype)
+    cfg = H.make_config(wl)
+    got = H.hlta_quantize_fp8(cfg, dev["q"], dev["k"], dev["v"])
+    torch.cuda.synchronize()
+    for i, n in enumerate("qkv"):
+        code, s = O.quantize_e4m3(x[n])
+        g = got[n + "8"].cpu().numpy()
+        assert np.array_equal(g, code), f"{n}: {int(np.sum(g != code))} codes differ"
+        assert np.array_equal(got["scales"][..., i].cpu().numpy(), s), n
+
+
+@pytest.mark.parametrize("wl", FP8_CASES, ids=lambda w: w.name)
+def test_attn_fp8_matches_attention_over_dequantised_inputs(wl):
+    x = I.make_clip(wl)
+    dev = H.to_device(x, wl.dtype)
+    cfg = H.make_config(wl)
+    fp8 = H.hlta_quantize_fp8(cfg, dev["q"], dev["k"], dev["v"])
+    out = H.alloc_outputs(cfg, wl.L)
+    out["o_gdn"].zero_()
+    H.hlta_attn_fwd_fp8(cfg, fp8, dev["w"], out["o_gdn"], out)
+    torch.cuda.synchronize()
+    deq = {}
+    for n in "qkv":
+        code, s = O.quantize_e4m3(x[n])
+        deq[n] = O.dequantize_e4m3(code, s)
+    args = (wl.T, wl.P, wl.swa_frames, wl.dswa_dilation, wl.dswa_taps, wl.gdn_chunk)
+    ref_q = O.hlta_forward(deq["q"], deq["k"], deq["v"], x["a"], x["b"], x["w"], *args)
+    ref_x = O.hlta_forward(x["q"], x["k"], x["v"], x["a"], x["b"], x["w"], *args)
+    for i, n in enumerate(("o_swa", "o_dswa")):
+        g = to64(out[n])
+        e_q, e_x = O.rel_l2(g, ref_q[i]), O.rel_l2(g, ref_x[i])
+        print(wl.name, n, f"vs dequantised {e_q:.2e}, vs exact {e_x:.2e}", flush=True)
+        assert e_q <= TOL_FP8_SAME_INPUTS and e_x <= TOL_FP8_VS_EXACT, (n, e_q, e_x)
+    w = x["w"].astype(np.float64)
+    mix = w[None, None, :, 0, None] * to64(out["o_swa"]) + w[None, None, :, 1, None] * to64(out["o_dswa"])
+    assert np.all(np.abs(to64(out["o_mix"]) - mix) <= 2.0 ** -8 * np.abs(mix) + 1e-6)
