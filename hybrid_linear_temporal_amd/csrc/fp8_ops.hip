@@ -25,26 +25,35 @@ __global__ void __launch_bounds__(kThreads) clear_kernel(unsigned* p, int n) {
   if (i < n) p[i] = 0u;
 }
 
-template <typename T>
-__device__ __forceinline__ float absf(T x) {
-  return fabsf(static_cast<float>(x));
+// max |x| over the elements of one 16-byte chunk
+__device__ __forceinline__ float chunk_absmax(const bf16*, const uint4& u) {
+  const bf16* e = reinterpret_cast<const bf16*>(&u);
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(static_cast<float>(e[i])));
+  return m;
+}
+__device__ __forceinline__ float chunk_absmax(const float*, const uint4& u) {
+  const float* e = reinterpret_cast<const float*>(&u);
+  return fmaxf(fmaxf(fabsf(e[0]), fabsf(e[1])), fmaxf(fabsf(e[2]), fabsf(e[3])));
 }
 
-// grid: (ceil(L / kTokensPerBlock), H, B * 3); 16 threads per token row of one
-// head (d <= 128: each thread d / 16 values), 16 rows at a time.
+// grid: (ceil(L / kTokensPerBlock), H, B * 3); one 16-byte chunk per thread,
+// cpr chunks per token row of one head (d * sizeof(T) / 16), 256 / cpr rows at a time.
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
 absmax_kernel(const T* q, const T* k, const T* v, unsigned* amax, long long L, int H, int d) {
   const int h = blockIdx.y, b = blockIdx.z / 3, t = blockIdx.z % 3;
   const T* x = t == 0 ? q : (t == 1 ? k : v);
-  const int per = d / 16;   // values per thread
-  const int col = (threadIdx.x & 15) * per;
+  const int cpr = int(d * sizeof(T) / 16);
+  const int rows = kThreads / cpr;
+  const int chunk = threadIdx.x % cpr;
   const long long t0 = (long long)blockIdx.x * kTokensPerBlock;
   const long long t1 = t0 + kTokensPerBlock < L ? t0 + kTokensPerBlock : L;
   float m = 0.f;
-  for (long long tok = t0 + (threadIdx.x >> 4); tok < t1; tok += kThreads / 16) {
-    const T* row = x + ((size_t(b) * L + size_t(tok)) * H + h) * d + col;
-    for (int e = 0; e < per; ++e) m = fmaxf(m, absf(row[e]));
+  for (long long tok = t0 + threadIdx.x / cpr; tok < t1; tok += rows) {
+    const uint4 u = reinterpret_cast<const uint4*>(x + ((size_t(b) * L + size_t(tok)) * H + h) * d)[chunk];
+    m = fmaxf(m, chunk_absmax(x, u));
   }
   // wave maximum, then the block's through LDS
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -88,31 +97,32 @@ struct Load8<float> {
   }
 };
 
-// one thread per 8 consecutive values; grid-stride over the three tensors
+// one workgroup per token (grid-stride): its batch row is wave-uniform; a
+// thread converts 8 consecutive values of one (tensor, head) at a time
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
 quantize_kernel(const T* q, const T* k, const T* v, unsigned char* q8, unsigned char* k8, unsigned char* v8,
-                const unsigned* amax, long long n8, long long L, int H, int d8) {
-  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < 3 * n8;
-       i += (long long)gridDim.x * kThreads) {
-    const int t = int(i / n8);
-    const long long j = i - t * n8;
-    const long long vec = j / d8;          // (b, token, h)
-    const int h = int(vec % H);
-    const int b = int(vec / H / L);
-    const float s = scale_of(amax[(size_t(b) * H + h) * 3 + t]);
-    const T* x = (t == 0 ? q : (t == 1 ? k : v)) + size_t(j) * 8;
-    unsigned char* y = (t == 0 ? q8 : (t == 1 ? k8 : v8)) + size_t(j) * 8;
-    float f[8];
-    Load8<T>::get(x, f);
+                const unsigned* amax, int B, long long L, int H, int d) {
+  const int d8 = d / 8, per_tensor = H * d8;
+  for (long long tok = blockIdx.x; tok < (long long)B * L; tok += gridDim.x) {
+    const int b = int(tok / L);
+    for (int i = threadIdx.x; i < 3 * per_tensor; i += kThreads) {
+      const int t = i / per_tensor, r = i - t * per_tensor, h = r / d8;
+      const float s = scale_of(amax[(size_t(b) * H + h) * 3 + t]);
+      const size_t o = size_t(tok) * per_tensor * 8 + size_t(r) * 8;
+      const T* x = (t == 0 ? q : (t == 1 ? k : v)) + o;
+      unsigned char* y = (t == 0 ? q8 : (t == 1 ? k8 : v8)) + o;
+      float f[8];
+      Load8<T>::get(x, f);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = fminf(fmaxf(f[e] / s, -kE4m3Max), kE4m3Max);
-    int lo = 0, hi = 0;
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], lo, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], hi, false);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
-    *reinterpret_cast<uint2*>(y) = make_uint2(unsigned(lo), unsigned(hi));
+      for (int e = 0; e < 8; ++e) f[e] = fminf(fmaxf(f[e] / s, -kE4m3Max), kE4m3Max);
+      int lo = 0, hi = 0;
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], lo, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], hi, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+      *reinterpret_cast<uint2*>(y) = make_uint2(unsigned(lo), unsigned(hi));
+    }
   }
 }
 
@@ -130,23 +140,22 @@ hipError_t launch_quantize_e4m3(const void* q, const void* k, const void* v, voi
   hipLaunchKernelGGL(clear_kernel, dim3((ns + kThreads - 1) / kThreads), dim3(kThreads), 0, st, amax, ns);
   if (L > 0) {
     const dim3 grid(unsigned((L + kTokensPerBlock - 1) / kTokensPerBlock), unsigned(H), unsigned(B * 3));
-    const long long n8 = (long long)B * L * H * (d / 8);
-    long long blocks = (3 * n8 + kThreads - 1) / kThreads;
-    if (blocks > 16384) blocks = 16384;
+    long long blocks = (long long)B * L;
+    if (blocks > (1 << 20)) blocks = 1 << 20;
     if (dt == HLTA_BF16) {
       hipLaunchKernelGGL(absmax_kernel<bf16>, grid, dim3(kThreads), 0, st, static_cast<const bf16*>(q),
                          static_cast<const bf16*>(k), static_cast<const bf16*>(v), amax, L, H, d);
       hipLaunchKernelGGL(quantize_kernel<bf16>, dim3(unsigned(blocks)), dim3(kThreads), 0, st,
                          static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
                          static_cast<unsigned char*>(q8), static_cast<unsigned char*>(k8),
-                         static_cast<unsigned char*>(v8), amax, n8, L, H, d / 8);
+                         static_cast<unsigned char*>(v8), amax, B, L, H, d);
     } else {
       hipLaunchKernelGGL(absmax_kernel<float>, grid, dim3(kThreads), 0, st, static_cast<const float*>(q),
                          static_cast<const float*>(k), static_cast<const float*>(v), amax, L, H, d);
       hipLaunchKernelGGL(quantize_kernel<float>, dim3(unsigned(blocks)), dim3(kThreads), 0, st,
                          static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
                          static_cast<unsigned char*>(q8), static_cast<unsigned char*>(k8),
-                         static_cast<unsigned char*>(v8), amax, n8, L, H, d / 8);
+                         static_cast<unsigned char*>(v8), amax, B, L, H, d);
     }
   }
   hipLaunchKernelGGL(finalize_kernel, dim3((ns + kThreads - 1) / kThreads), dim3(kThreads), 0, st, amax, ns);
