@@ -29,7 +29,17 @@ def summarise(path: str) -> str:
                                ("14gdn_chain_mfmaIDF16b", "gdn_chain_mfma<bf16>"),
                                ("14gdn_chain_mfmaIf", "gdn_chain_mfma<float>"),
                                ("10mix_kernelIDF16b", "mix_kernel<bf16>"),
-                               ("10mix_kernelIf", "mix_kernel<float>")):
+                               ("10mix_kernelIf", "mix_kernel<float>"),
+                               ("15attn_fp8_kernelIDF16b", "attn_fp8_kernel<bf16>"),
+                               ("15attn_fp8_kernelIf", "attn_fp8_kernel<float>"),
+                               ("15quantize_kernelIDF16b", "quantize_kernel<bf16>"),
+                               ("15quantize_kernelIf", "quantize_kernel<float>"),
+                               ("13absmax_kernelIDF16b", "absmax_kernel<bf16>"),
+                               ("13absmax_kernelIf", "absmax_kernel<float>"),
+                               ("14rope_qk_kernelIDF16b", "rope_qk_kernel<bf16>"),
+                               ("14rope_qk_kernelIf", "rope_qk_kernel<float>"),
+                               ("16rope_ring_kernelIDF16b", "rope_ring_kernel<bf16>"),
+                               ("16rope_ring_kernelIf", "rope_ring_kernel<float>")):
             if mangled in short:
                 short = plain
                 break
