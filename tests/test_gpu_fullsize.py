@@ -98,3 +98,56 @@ def test_stream_full_size_sampled():
     for b, h in pairs:
         err = O.rel_l2(to64(st.S[b, h]), ost[b, h].S0)
         assert err <= TOL["bf16"], f"stream state {err:.3e}"
+
+
+def test_full_size_rope_and_fp8_sampled():
+    """480P / 31 frames at full size: the rotary embedding (the 30 x 52 latent
+    grid) on sampled query frames of two heads against the float64 oracle; the
+    FP8 softmax branches against exact attention over the dequantised inputs
+    and the quantiser's codes bit for bit on those heads."""
+    wl = I.P480_T31
+    grid, theta = (30, 52), 10000.0
+    x = I.make_clip(wl, threads=16)
+    dev = H.to_device(x, wl.dtype)
+    P = wl.P
+    frames = (0, 5, wl.T - 1)
+    heads = ((0, 0), (0, wl.H - 1))
+    # rotary embedding
+    cfg = H.make_config(wl, rope_theta=theta, rope_grid=grid)
+    res = H.hlta_fwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"])
+    torch.cuda.synchronize()
+    pos = O.rope_positions(wl.T, P, grid[1])
+    for b, h in heads:
+        qr, kr = O.rope(x["q"][b, :, h], pos, theta), O.rope(x["k"][b, :, h], pos, theta)
+        v = x["v"][b, :, h]
+        for f in frames:
+            sl = slice(f * P, (f + 1) * P)
+            for name, fr in (("o_swa", O.swa_frames(f, wl.swa_frames)),
+                             ("o_dswa", O.dswa_frames(f, wl.dswa_dilation, wl.dswa_taps))):
+                err = O.rel_l2(to64(res[name][b, sl, h]), O.attend_rows(qr[sl], kr, v, P, fr))
+                print(f"rope (b={b}, h={h}) frame {f} {name} {err:.2e}", flush=True)
+                assert err <= TOL["bf16"], (b, h, f, name, err)
+    del res
+    # FP8 variant
+    cfg = H.make_config(wl)
+    fp8 = H.hlta_quantize_fp8(cfg, dev["q"], dev["k"], dev["v"])
+    out = H.alloc_outputs(cfg, wl.L)
+    out["o_gdn"].zero_()
+    H.hlta_attn_fwd_fp8(cfg, fp8, dev["w"], out["o_gdn"], out)
+    torch.cuda.synchronize()
+    scales = fp8["scales"].cpu().numpy()
+    for b, h in heads:
+        deq = {}
+        for i, n in enumerate("qkv"):
+            code, s = O.quantize_e4m3(x[n][b:b + 1, :, h:h + 1])
+            assert np.array_equal(fp8[n + "8"][b, :, h].cpu().numpy(), code[0, :, 0]), (n, b, h)
+            assert scales[b, h, i] == s[0, 0], (n, b, h)
+            deq[n] = O.dequantize_e4m3(code, s)[0, :, 0]
+        for f in frames:
+            sl = slice(f * P, (f + 1) * P)
+            for name, fr in (("o_swa", O.swa_frames(f, wl.swa_frames)),
+                             ("o_dswa", O.dswa_frames(f, wl.dswa_dilation, wl.dswa_taps))):
+                ref = O.attend_rows(deq["q"][sl], deq["k"], deq["v"], P, fr)
+                err = O.rel_l2(to64(out[name][b, sl, h]), ref)
+                print(f"fp8 (b={b}, h={h}) frame {f} {name} {err:.2e}", flush=True)
+                assert err <= 3e-2, (b, h, f, name, err)
