@@ -371,6 +371,128 @@ class StreamHead:
 
 
 # ---------------------------------------------------------------------------
+# backward: gradients of the operator (the training workload)
+# ---------------------------------------------------------------------------
+#
+# Given the gradient of the mixed output, d_mix [B, L, H, d], the gradients of
+# q, k, v, the gates, the mix weights and the start state. Every formula is the
+# chain rule through the forward definitions above (no approximation); the
+# pins compare them with central differences of those forward functions.
+
+def attention_backward(q, k, v, do, T, P, frames_of, scale=None):
+    """Gradients (dq, dk, dv) of the frame-block softmax attention
+    o = frame_softmax_attention(q, k, v, T, P, frames_of) given do = dL/do.
+    Per query frame f with keys K (its frame set): Z = s q K^T, Pm = softmax(Z),
+    o = Pm V; dV += Pm^T do, dPm = do V^T, dZ = Pm * (dPm - rowsum(dPm * Pm)),
+    dq = s dZ K, dK += s dZ^T q."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    do = np.asarray(do, np.float64)
+    d = q.shape[1]
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for f in range(T):
+        frames = frames_of(f)
+        if not frames:
+            continue
+        rows = slice(f * P, (f + 1) * P)
+        idx = np.concatenate([np.arange(g * P, (g + 1) * P) for g in frames])
+        z = scale * (q[rows] @ k[idx].T)
+        z -= z.max(axis=1, keepdims=True)
+        pm = np.exp(z)
+        pm /= pm.sum(axis=1, keepdims=True)
+        dv[idx] += pm.T @ do[rows]
+        dpm = do[rows] @ v[idx].T
+        dz = pm * (dpm - np.sum(dpm * pm, axis=1, keepdims=True))
+        dq[rows] += scale * (dz @ k[idx])
+        dk[idx] += scale * (dz.T @ q[rows])
+    return dq, dk, dv
+
+
+def gdn_recurrent_backward(q, k, v, a, b, do, S0=None, l2norm=True):
+    """Gradients (dq, dk, dv, da, db, dS0) of the gated delta rule (gdn_recurrent)
+    given do = dL/do_t, by running the recurrence backwards. With k^ = k/n(k),
+    n(x) = sqrt(|x|^2 + eps), u = S_{t-1} k^, X = S_{t-1} - b u k^^T and
+    S_t = a X + b v k^^T, o_t = S_t q^; for G = dL/dS_t (do_t q^^T plus what
+    flows back from later tokens):
+      dq^ = S_t^T do_t, da = <G, X>, dX = a G, dv = b G k^,
+      db = v^T G k^ - u^T dX k^,  dk^ = b G^T v - b (S_{t-1}^T dX + dX^T S_{t-1}) k^,
+      dL/dS_{t-1} = dX - b (dX k^) k^^T,
+    and through the normalisation dx = dx^/n - x (x.dx^)/n^3."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    do = np.asarray(do, np.float64)
+    L, dk_ = k.shape
+    dvd = v.shape[1]
+    qh, kh = (l2norm_rows(q), l2norm_rows(k)) if l2norm else (q, k)
+    S = np.zeros((dvd, dk_)) if S0 is None else np.array(S0, np.float64)
+    states = [S]
+    for t in range(L):
+        u = S @ kh[t]
+        S = a[t] * (S - b[t] * np.outer(u, kh[t])) + b[t] * np.outer(v[t], kh[t])
+        states.append(S)
+    dqh, dkh = np.zeros_like(qh), np.zeros_like(kh)
+    dv, da, db = np.zeros_like(v), np.zeros(L), np.zeros(L)
+    G = np.zeros((dvd, dk_))
+    for t in range(L - 1, -1, -1):
+        St, Sp = states[t + 1], states[t]
+        G = G + np.outer(do[t], qh[t])
+        dqh[t] = St.T @ do[t]
+        u = Sp @ kh[t]
+        X = Sp - b[t] * np.outer(u, kh[t])
+        da[t] = np.sum(G * X)
+        dX = a[t] * G
+        dv[t] = b[t] * (G @ kh[t])
+        db[t] = v[t] @ G @ kh[t] - u @ dX @ kh[t]
+        dkh[t] = b[t] * (G.T @ v[t]) - b[t] * (Sp.T @ dX + dX.T @ Sp) @ kh[t]
+        G = dX - b[t] * np.outer(dX @ kh[t], kh[t])
+    def through_norm(x, dxh):
+        n = np.sqrt(np.sum(x * x, axis=1, keepdims=True) + L2_EPS)
+        return dxh / n - x * np.sum(x * dxh, axis=1, keepdims=True) / n ** 3
+    dq = through_norm(q, dqh) if l2norm else dqh
+    dk = through_norm(k, dkh) if l2norm else dkh
+    return dq, dk, dv, da, db, G
+
+
+def hlta_backward(q, k, v, a, b, w, d_mix, T, P, W, dil, taps, scale=None, S0=None):
+    """Gradients of L = <d_mix, o_mix> for inputs [B, L, H, d]: returns dq, dk,
+    dv [B, L, H, d], da, db [B, L, H], dw [H, 3], dS0 [B, H, d_v, d_k]. The
+    branch gradients are do_i = w[h, i] * d_mix; dw[h, i] = <d_mix, o_i>."""
+    q = np.asarray(q, np.float64)
+    B, Lt, H, d = q.shape
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(q), np.zeros(np.shape(v))
+    da, db = np.zeros((B, Lt, H)), np.zeros((B, Lt, H))
+    dw, dS0 = np.zeros((H, 3)), np.zeros((B, H, np.shape(v)[3], d))
+    for bi in range(B):
+        for hi in range(H):
+            qh, kh, vh = q[bi, :, hi], np.asarray(k[bi, :, hi], np.float64), np.asarray(v[bi, :, hi], np.float64)
+            g = np.asarray(d_mix[bi, :, hi], np.float64)
+            w3 = np.asarray(w[hi], np.float64)
+            s0 = None if S0 is None else S0[bi, hi]
+            o_swa = swa(qh, kh, vh, T, P, W, scale)
+            o_dswa = dswa(qh, kh, vh, T, P, dil, taps, scale)
+            o_gdn, _ = gdn_recurrent(qh, kh, vh, a[bi, :, hi], b[bi, :, hi], s0)
+            dw[hi] += [np.sum(g * o_swa), np.sum(g * o_dswa), np.sum(g * o_gdn)]
+            for wi, fo in ((w3[0], lambda f: swa_frames(f, W)), (w3[1], lambda f: dswa_frames(f, dil, taps))):
+                gq, gk, gv = attention_backward(qh, kh, vh, wi * g, T, P, fo, scale)
+                dq[bi, :, hi] += gq
+                dk[bi, :, hi] += gk
+                dv[bi, :, hi] += gv
+            gq, gk, gv, ga, gb, gS = gdn_recurrent_backward(qh, kh, vh, a[bi, :, hi], b[bi, :, hi], w3[2] * g, s0)
+            dq[bi, :, hi] += gq
+            dk[bi, :, hi] += gk
+            dv[bi, :, hi] += gv
+            da[bi, :, hi] = ga
+            db[bi, :, hi] = gb
+            dS0[bi, hi] = gS
+    return dq, dk, dv, da, db, dw, dS0
+
+
+# ---------------------------------------------------------------------------
 # FP8 (e4m3) variant of the softmax branches: input quantisation
 # ---------------------------------------------------------------------------
 #

@@ -545,3 +545,90 @@ def test_quantize_scales_and_error_bound():
     assert np.all(err <= bound)
     for b, h in ((0, 0), (0, 2), (1, 1)):
         assert np.max(np.abs(O.e4m3_decode(code[b, :, h]))) == 448.0
+
+
+# ---------------------------------------------------------------------------
+# backward: gradients against central differences of the (pinned) forward
+# ---------------------------------------------------------------------------
+
+def _central(f, x, idx, h=1e-6):
+    xp, xm = x.copy(), x.copy()
+    xp[idx] += h
+    xm[idx] -= h
+    return (f(xp) - f(xm)) / (2 * h)
+
+
+def _check_grad(f, x, g, n=40, seed=0, rtol=2e-6, atol=1e-8):
+    """g = analytic gradient of the scalar f at x, checked on n coordinates."""
+    rng = np.random.default_rng(seed)
+    flat = [tuple(i) for i in np.argwhere(np.ones(x.shape, bool))]
+    for j in rng.choice(len(flat), size=min(n, len(flat)), replace=False):
+        idx = flat[j]
+        fd = _central(f, x, idx)
+        assert abs(fd - g[idx]) <= atol + rtol * max(abs(fd), abs(g[idx])), (idx, fd, g[idx])
+
+
+def test_attention_backward_matches_finite_differences():
+    T, P, d, W, dil, taps = 5, 3, 8, 2, 2, 2
+    rng = np.random.default_rng(21)
+    q, k, v, do = (rng.standard_normal((T * P, d)) for _ in range(4))
+    for frames_of in (lambda f: O.swa_frames(f, W), lambda f: O.dswa_frames(f, dil, taps)):
+        gq, gk, gv = O.attention_backward(q, k, v, do, T, P, frames_of)
+        loss = lambda qq, kk, vv: np.sum(do * O.frame_softmax_attention(qq, kk, vv, T, P, frames_of))
+        _check_grad(lambda x: loss(x, k, v), q, gq)
+        _check_grad(lambda x: loss(q, x, v), k, gk)
+        _check_grad(lambda x: loss(q, k, x), v, gv)
+
+
+def test_gdn_backward_matches_finite_differences():
+    L, d = 11, 6
+    rng = np.random.default_rng(22)
+    q, k, v, do = (rng.standard_normal((L, d)) for _ in range(4))
+    a, b = rng.uniform(0.5, 0.99, L), rng.uniform(0.1, 0.9, L)
+    S0 = 0.3 * rng.standard_normal((d, d))
+    gq, gk, gv, ga, gb, gS = O.gdn_recurrent_backward(q, k, v, a, b, do, S0)
+    loss = lambda qq, kk, vv, aa, bb, ss: np.sum(do * O.gdn_recurrent(qq, kk, vv, aa, bb, ss)[0])
+    _check_grad(lambda x: loss(x, k, v, a, b, S0), q, gq)
+    _check_grad(lambda x: loss(q, x, v, a, b, S0), k, gk)
+    _check_grad(lambda x: loss(q, k, x, a, b, S0), v, gv)
+    _check_grad(lambda x: loss(q, k, v, x, b, S0), a, ga, n=L)
+    _check_grad(lambda x: loss(q, k, v, a, x, S0), b, gb, n=L)
+    _check_grad(lambda x: loss(q, k, v, a, b, x), S0, gS)
+
+
+def test_gdn_backward_closed_form_without_writes():
+    """b = 0, a = 1: S_t = S0, o_t = S0 q^_t, so dS0 = sum_t do_t q^_t^T,
+    dv = 0 and the gradient of q^ is S0^T do_t."""
+    L, d = 7, 5
+    rng = np.random.default_rng(23)
+    q, k, v, do = (rng.standard_normal((L, d)) for _ in range(4))
+    S0 = rng.standard_normal((d, d))
+    gq, gk, gv, ga, gb, gS = O.gdn_recurrent_backward(q, k, v, np.ones(L), np.zeros(L), do, S0, l2norm=False)
+    assert np.allclose(gS, do.T @ q) and np.allclose(gv, 0) and np.allclose(gq, do @ S0)
+    # k enters only through the (zero) writes; da_t = <sum_{s>=t} do_s q_s^T, S0>
+    assert np.allclose(gk, 0)
+    assert np.allclose(ga, [np.sum((do[t:, :, None] * q[t:, None, :]).sum(0) * S0) for t in range(L)])
+
+
+def test_hlta_backward_matches_finite_differences():
+    wl = I.TINY_F32
+    x = I.make_clip(wl)
+    T, P = 4, wl.P
+    sub = {n: (arr[:, :T * P] if n != "w" else arr).astype(np.float64) for n, arr in x.items()}
+    rng = np.random.default_rng(24)
+    g = rng.standard_normal(sub["q"].shape)
+    S0 = 0.2 * rng.standard_normal((wl.B, wl.H, wl.d, wl.d))
+    args = (T, P, wl.swa_frames, wl.dswa_dilation, wl.dswa_taps)
+    dq, dk, dv, da, db, dw, dS0 = O.hlta_backward(sub["q"], sub["k"], sub["v"], sub["a"], sub["b"], sub["w"], g,
+                                                  *args, S0=S0)
+
+    def loss(q=sub["q"], k=sub["k"], v=sub["v"], a=sub["a"], b=sub["b"], w=sub["w"], s0=S0):
+        o = O.hlta_forward(q, k, v, a, b, w, *args, wl.gdn_chunk, S0=s0, gdn="recurrent")
+        return np.sum(g * o[3])
+    _check_grad(lambda z: loss(q=z), sub["q"], dq, n=25)
+    _check_grad(lambda z: loss(k=z), sub["k"], dk, n=25)
+    _check_grad(lambda z: loss(v=z), sub["v"], dv, n=25)
+    _check_grad(lambda z: loss(a=z), sub["a"], da, n=15)
+    _check_grad(lambda z: loss(b=z), sub["b"], db, n=15)
+    _check_grad(lambda z: loss(w=z), sub["w"], dw, n=6)
+    _check_grad(lambda z: loss(s0=z), S0, dS0, n=15)
