@@ -1,0 +1,623 @@
+// Backward of the operator (gradients for training): given dL/do_mix, the
+// gradients of q, k, v, the gates, the mix weights and the start state. The
+// branch gradients are do_i = w[h, i] * d_mix (the mix is linear). Plain fp32
+// kernels (any supported d and input dtype), written for clarity first:
+//
+//  * softmax branches (exact attention, so its gradient is the textbook one;
+//    long-context page, section 03 on tiled exact attention): a recompute pass
+//    stores per query row the log2-sum-exp and D = do . o; a query-major pass
+//    accumulates dq = s sum_k P (do . v_k - D) k; a key-major pass walks, for
+//    each key frame, the query frames whose frame set holds it and
+//    accumulates dv = sum_i P do_i and dk = s sum_i P (do_i . v - D_i) q_i;
+//  * gated delta rule (Kairos related-work page, row A; long-context page,
+//    section 06): a forward pass checkpoints S every C tokens, then chunk by
+//    chunk from the end the chunk's states are recomputed and the adjoint
+//    G = dL/dS_t is carried backwards token by token (the formulas are in
+//    gdn_bwd_kernel). One workgroup per (batch row, head); each thread owns an
+//    (d/16) x (d/16) block of S and of G, and row and column reductions go
+//    through LDS;
+//  * mix weights: dw[h, i] = <d_mix, o_i> over the stored branch outputs.
+#include "hlta_device.h"
+#include "hlta_launch.h"
+
+namespace hlta {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kL2Eps = 1e-6f;
+
+template <typename T>
+__device__ __forceinline__ float ld(const T* p, size_t i) {
+  return static_cast<float>(p[i]);
+}
+
+// ---------------------------------------------------------------------------
+// softmax branches
+// ---------------------------------------------------------------------------
+
+constexpr int kRows = 64;   // query (or key) rows per workgroup, 4 threads per row
+constexpr int kTile = 32;   // rows of the other side staged in LDS at a time
+
+// sum over the 4 threads of a row (lanes 4r .. 4r+3)
+__device__ __forceinline__ float row4(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  return x;
+}
+
+// Recompute pass: lse2 (log2 of the softmax denominator, scores in log2 units)
+// and D = do . o of every query row, per branch. grid (tiles of the frame * T, H, B)
+template <typename Tin, typename Tg, int D>
+__global__ void __launch_bounds__(kThreads)
+attn_bwd_stats(AttnParams p, const Tg* d_mix, const float* mix_w, float* lse2, float* dsum) {
+  constexpr int DP = D / 4;
+  __shared__ float Ks[kTile][D + 1], Vs[kTile][D + 1];
+  const int tiles = (p.P + kRows - 1) / kRows;
+  const int fq = blockIdx.x / tiles, row0 = (blockIdx.x % tiles) * kRows;
+  const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x, r = tid >> 2, c = tid & 3;
+  const int prow = row0 + r;
+  const bool ok = prow < p.P;
+  const long long f = fq;
+  const Tin* q = static_cast<const Tin*>(p.q);
+  const Tin* k = static_cast<const Tin*>(p.k);
+  const Tin* v = static_cast<const Tin*>(p.v);
+  const size_t HD = size_t(p.H) * D;
+  const size_t tok = size_t(b) * p.T * p.P + size_t(fq) * p.P + prow;
+  float qr[DP], g[DP];
+#pragma unroll
+  for (int i = 0; i < DP; ++i) {
+    qr[i] = ok ? ld(q, tok * HD + h * D + c * DP + i) * p.scale_log2 : 0.f;
+    g[i] = ok ? ld(d_mix, tok * HD + h * D + c * DP + i) : 0.f;
+  }
+  const int nswa = swa_count(f, p.W), ndswa = dswa_count(f, p.dil, p.taps);
+  for (int branch = 0; branch < 2; ++branch) {
+    const int nfr = branch == 0 ? nswa : ndswa;
+    const long long nk = (long long)nfr * p.P;
+    float m = -INFINITY, l = 0.f, acc[DP];
+#pragma unroll
+    for (int i = 0; i < DP; ++i) acc[i] = 0.f;
+    for (long long t0 = 0; t0 < nk; t0 += kTile) {
+      __syncthreads();
+      for (int e = tid; e < kTile * D; e += kThreads) {
+        const int jj = e / D, col = e % D;
+        const long long j = t0 + jj;
+        float kv = 0.f, vv = 0.f;
+        if (j < nk) {
+          const long long gfr = branch_frame(branch, f, nswa, p.dil, int(j / p.P));
+          const size_t kt = (size_t(b) * p.T * p.P + size_t(gfr) * p.P + size_t(j % p.P)) * HD + h * D + col;
+          kv = ld(k, kt);
+          vv = ld(v, kt);
+        }
+        Ks[jj][col] = kv;
+        Vs[jj][col] = vv;
+      }
+      __syncthreads();
+      const int nj = int(nk - t0 < kTile ? nk - t0 : kTile);
+      for (int jj = 0; jj < nj; ++jj) {
+        float sc = 0.f;
+#pragma unroll
+        for (int i = 0; i < DP; ++i) sc += qr[i] * Ks[jj][c * DP + i];
+        sc = row4(sc);
+        const float mn = fmaxf(m, sc);
+        const float al = exp2f(m - mn), e = exp2f(sc - mn);
+        l = l * al + e;
+#pragma unroll
+        for (int i = 0; i < DP; ++i) acc[i] = acc[i] * al + e * Vs[jj][c * DP + i];
+        m = mn;
+      }
+    }
+    float dd = 0.f;
+    if (nk > 0) {
+#pragma unroll
+      for (int i = 0; i < DP; ++i) dd += g[i] * acc[i];
+      dd = row4(dd) / l;
+    }
+    if (ok && c == 0) {
+      const size_t o = (size_t(branch) * p.B * p.T * p.P + tok) * p.H + h;
+      lse2[o] = nk > 0 ? m + log2f(l) : 0.f;
+      dsum[o] = dd * mix_w[3 * h + branch];   // D of do = w * d_mix
+    }
+  }
+}
+
+// dq, query-major: dq += s * sum_k P (do . v_k - D) k over both branches
+template <typename Tin, typename Tg, int D>
+__global__ void __launch_bounds__(kThreads)
+attn_bwd_dq(AttnParams p, const Tg* d_mix, const float* mix_w, const float* lse2, const float* dsum, float* dq,
+            float scale) {
+  constexpr int DP = D / 4;
+  __shared__ float Ks[kTile][D + 1], Vs[kTile][D + 1];
+  const int tiles = (p.P + kRows - 1) / kRows;
+  const int fq = blockIdx.x / tiles, row0 = (blockIdx.x % tiles) * kRows;
+  const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x, r = tid >> 2, c = tid & 3;
+  const int prow = row0 + r;
+  const bool ok = prow < p.P;
+  const long long f = fq;
+  const Tin* q = static_cast<const Tin*>(p.q);
+  const Tin* k = static_cast<const Tin*>(p.k);
+  const Tin* v = static_cast<const Tin*>(p.v);
+  const size_t HD = size_t(p.H) * D;
+  const size_t tok = size_t(b) * p.T * p.P + size_t(fq) * p.P + prow;
+  float qr[DP], g[DP], dqa[DP];
+#pragma unroll
+  for (int i = 0; i < DP; ++i) {
+    qr[i] = ok ? ld(q, tok * HD + h * D + c * DP + i) * p.scale_log2 : 0.f;
+    g[i] = ok ? ld(d_mix, tok * HD + h * D + c * DP + i) : 0.f;
+    dqa[i] = 0.f;
+  }
+  const int nswa = swa_count(f, p.W), ndswa = dswa_count(f, p.dil, p.taps);
+  for (int branch = 0; branch < 2; ++branch) {
+    const int nfr = branch == 0 ? nswa : ndswa;
+    const long long nk = (long long)nfr * p.P;
+    const float w = mix_w[3 * h + branch];
+    const size_t so = (size_t(branch) * p.B * p.T * p.P + (ok ? tok : 0)) * p.H + h;
+    const float L2 = lse2[so], Dd = dsum[so];
+    for (long long t0 = 0; t0 < nk; t0 += kTile) {
+      __syncthreads();
+      for (int e = tid; e < kTile * D; e += kThreads) {
+        const int jj = e / D, col = e % D;
+        const long long j = t0 + jj;
+        float kv = 0.f, vv = 0.f;
+        if (j < nk) {
+          const long long gfr = branch_frame(branch, f, nswa, p.dil, int(j / p.P));
+          const size_t kt = (size_t(b) * p.T * p.P + size_t(gfr) * p.P + size_t(j % p.P)) * HD + h * D + col;
+          kv = ld(k, kt);
+          vv = ld(v, kt);
+        }
+        Ks[jj][col] = kv;
+        Vs[jj][col] = vv;
+      }
+      __syncthreads();
+      const int nj = int(nk - t0 < kTile ? nk - t0 : kTile);
+      for (int jj = 0; jj < nj; ++jj) {
+        float sc = 0.f, dp = 0.f;
+#pragma unroll
+        for (int i = 0; i < DP; ++i) {
+          sc += qr[i] * Ks[jj][c * DP + i];
+          dp += g[i] * Vs[jj][c * DP + i];
+        }
+        sc = row4(sc);
+        dp = row4(dp) * w;
+        const float pr = exp2f(sc - L2);
+        const float ds = pr * (dp - Dd);
+#pragma unroll
+        for (int i = 0; i < DP; ++i) dqa[i] += ds * Ks[jj][c * DP + i];
+      }
+    }
+  }
+  if (ok) {
+#pragma unroll
+    for (int i = 0; i < DP; ++i) dq[tok * HD + h * D + c * DP + i] = scale * dqa[i];
+  }
+}
+
+// dk, dv, key-major: rows of this workgroup are keys of frame g; the queries
+// that read them are those of frames f with g in their frame set
+template <typename Tin, typename Tg, int D>
+__global__ void __launch_bounds__(kThreads)
+attn_bwd_dkdv(AttnParams p, const Tg* d_mix, const float* mix_w, const float* lse2, const float* dsum, float* dk,
+              float* dv, float scale) {
+  constexpr int DP = D / 4;
+  __shared__ float Qs[kTile][D + 1], Gs[kTile][D + 1];
+  __shared__ float Ls[kTile], Ds[kTile];
+  const int tiles = (p.P + kRows - 1) / kRows;
+  const int gk = blockIdx.x / tiles, row0 = (blockIdx.x % tiles) * kRows;
+  const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x, r = tid >> 2, c = tid & 3;
+  const int krow = row0 + r;
+  const bool ok = krow < p.P;
+  const Tin* q = static_cast<const Tin*>(p.q);
+  const Tin* k = static_cast<const Tin*>(p.k);
+  const Tin* v = static_cast<const Tin*>(p.v);
+  const size_t HD = size_t(p.H) * D;
+  const size_t ktok = size_t(b) * p.T * p.P + size_t(gk) * p.P + krow;
+  float kr[DP], vr[DP], dka[DP], dva[DP];
+#pragma unroll
+  for (int i = 0; i < DP; ++i) {
+    kr[i] = ok ? ld(k, ktok * HD + h * D + c * DP + i) * p.scale_log2 : 0.f;
+    vr[i] = ok ? ld(v, ktok * HD + h * D + c * DP + i) : 0.f;
+    dka[i] = dva[i] = 0.f;
+  }
+  for (int branch = 0; branch < 2; ++branch) {
+    const float w = mix_w[3 * h + branch];
+    // query frames whose branch frame set holds frame gk
+    const int nq = branch == 0 ? p.W : p.taps;
+    for (int qi = 0; qi < nq; ++qi) {
+      const long long f = branch == 0 ? (long long)gk + qi : (long long)gk + (long long)p.dil * (qi + 1);
+      if (f >= p.T) break;
+      for (int t0 = 0; t0 < p.P; t0 += kTile) {
+        __syncthreads();
+        for (int e = tid; e < kTile * D; e += kThreads) {
+          const int ii = e / D, col = e % D;
+          const int i = t0 + ii;
+          float qv = 0.f, gv = 0.f;
+          if (i < p.P) {
+            const size_t qt = (size_t(b) * p.T * p.P + size_t(f) * p.P + i) * HD + h * D + col;
+            qv = ld(q, qt);
+            gv = ld(d_mix, qt) * w;
+          }
+          Qs[ii][col] = qv;
+          Gs[ii][col] = gv;
+        }
+        if (tid < kTile) {
+          const int i = t0 + tid;
+          float L2 = 0.f, Dd = 0.f;
+          if (i < p.P) {
+            const size_t so = (size_t(branch) * p.B * p.T * p.P + size_t(b) * p.T * p.P + size_t(f) * p.P + i) * p.H + h;
+            L2 = lse2[so];
+            Dd = dsum[so];
+          }
+          Ls[tid] = L2;
+          Ds[tid] = Dd;
+        }
+        __syncthreads();
+        const int ni = p.P - t0 < kTile ? p.P - t0 : kTile;
+        for (int ii = 0; ii < ni; ++ii) {
+          float sc = 0.f, dp = 0.f;
+#pragma unroll
+          for (int i = 0; i < DP; ++i) {
+            sc += kr[i] * Qs[ii][c * DP + i];
+            dp += vr[i] * Gs[ii][c * DP + i];
+          }
+          sc = row4(sc);
+          dp = row4(dp);
+          const float pr = exp2f(sc - Ls[ii]);
+          const float ds = pr * (dp - Ds[ii]);
+#pragma unroll
+          for (int i = 0; i < DP; ++i) {
+            dva[i] += pr * Gs[ii][c * DP + i];
+            dka[i] += ds * Qs[ii][c * DP + i];
+          }
+        }
+      }
+    }
+  }
+  if (ok) {
+#pragma unroll
+    for (int i = 0; i < DP; ++i) {
+      dk[ktok * HD + h * D + c * DP + i] = scale * dka[i];
+      dv[ktok * HD + h * D + c * DP + i] = dva[i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// gated delta rule
+// ---------------------------------------------------------------------------
+
+// Block layout: thread t owns rows 16-block t/16 and columns 16-block t%16 of
+// a d x d matrix, BS = d/16 each. Reductions: partial row (or column) sums of
+// the 16 threads sharing a block row (column) meet in LDS.
+template <int D>
+struct GdnBlock {
+  static constexpr int BS = D / 16;
+  float red[16][D];   // partial sums: [thread column-or-row group][index]
+  float vec[12][D];   // small vectors of the current token
+  float scal[16];     // scalars
+};
+
+// y_i = sum_j M_ij x_j (rows == true) or y_j = sum_i M_ij x_i
+template <int D, bool kRows>
+__device__ __forceinline__ void reduce_mv(GdnBlock<D>& sm, const float (&M)[D / 16][D / 16], const float* x,
+                                          float* y) {
+  constexpr int BS = D / 16;
+  const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
+#pragma unroll
+  for (int a = 0; a < BS; ++a) {
+    float s = 0.f;
+#pragma unroll
+    for (int bb = 0; bb < BS; ++bb) s += kRows ? M[a][bb] * x[tc * BS + bb] : M[bb][a] * x[tr * BS + bb];
+    if (kRows) sm.red[tc][tr * BS + a] = s;
+    else sm.red[tr][tc * BS + a] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) s += sm.red[g][threadIdx.x];
+    y[threadIdx.x] = s;
+  }
+  __syncthreads();
+}
+
+// sum of one value per thread (result broadcast through sm.scal[slot])
+template <int D>
+__device__ __forceinline__ float reduce_all(GdnBlock<D>& sm, float x, int slot) {
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  if ((threadIdx.x & 63) == 0) sm.red[0][threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) sm.scal[slot] = sm.red[0][0] + sm.red[0][1] + sm.red[0][2] + sm.red[0][3];
+  __syncthreads();
+  return sm.scal[slot];
+}
+
+// dot product of two LDS vectors (all threads get it)
+template <int D>
+__device__ __forceinline__ float dot(GdnBlock<D>& sm, const float* x, const float* y, int slot) {
+  float s = 0.f;
+  for (int i = threadIdx.x; i < D; i += kThreads) s += x[i] * y[i];
+  return reduce_all(sm, s, slot);
+}
+
+// normalised copy of row x (length D, in LDS) into y; returns the norm n
+template <int D>
+__device__ __forceinline__ float normalise(GdnBlock<D>& sm, const float* x, float* y, int slot, bool on) {
+  const float n2 = dot(sm, x, x, slot);
+  const float n = on ? sqrtf(n2 + kL2Eps) : 1.f;
+  if (threadIdx.x < D) y[threadIdx.x] = x[threadIdx.x] / n;
+  __syncthreads();
+  return n;
+}
+
+// Forward with checkpoints: S before token c*C for every chunk c.
+template <typename Tin, int D>
+__global__ void __launch_bounds__(kThreads)
+gdn_ckpt_kernel(GdnParams p, int C, float* ckpt) {
+  constexpr int BS = D / 16;
+  __shared__ GdnBlock<D> sm;
+  const int h = blockIdx.x % p.H, b = blockIdx.x / p.H;
+  const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
+  const size_t sbase = (size_t(b) * p.H + h) * D * D;
+  float S[BS][BS];
+#pragma unroll
+  for (int i = 0; i < BS; ++i)
+#pragma unroll
+    for (int j = 0; j < BS; ++j) S[i][j] = p.S0 ? p.S0[sbase + size_t(tr * BS + i) * D + tc * BS + j] : 0.f;
+  const Tin* k = static_cast<const Tin*>(p.k);
+  const Tin* v = static_cast<const Tin*>(p.v);
+  const size_t HD = size_t(p.H) * D;
+  float* ck = ckpt + size_t(b * p.H + h) * p.n_chunks * D * D;
+  for (long long t = 0; t < p.L; ++t) {
+    if (t % C == 0) {
+      float* dst = ck + size_t(t / C) * D * D;
+#pragma unroll
+      for (int i = 0; i < BS; ++i)
+#pragma unroll
+        for (int j = 0; j < BS; ++j) dst[size_t(tr * BS + i) * D + tc * BS + j] = S[i][j];
+    }
+    const size_t tok = (size_t(b) * p.L + t) * HD + size_t(h) * D;
+    if (threadIdx.x < D) {
+      sm.vec[0][threadIdx.x] = ld(k, tok + threadIdx.x);
+      sm.vec[1][threadIdx.x] = ld(v, tok + threadIdx.x);
+    }
+    __syncthreads();
+    normalise(sm, sm.vec[0], sm.vec[2], 0, p.l2norm != 0);   // vec[2] = k^
+    reduce_mv<D, true>(sm, S, sm.vec[2], sm.vec[3]);          // vec[3] = u = S k^
+    const size_t g = (size_t(b) * p.L + t) * p.H + h;
+    const float at = p.a[g], bt = p.b[g];
+#pragma unroll
+    for (int i = 0; i < BS; ++i)
+#pragma unroll
+      for (int j = 0; j < BS; ++j) {
+        const float kj = sm.vec[2][tc * BS + j];
+        S[i][j] = at * (S[i][j] - bt * sm.vec[3][tr * BS + i] * kj) + bt * sm.vec[1][tr * BS + i] * kj;
+      }
+    __syncthreads();
+  }
+}
+
+// Backward: per chunk from the last, recompute the chunk's states S_{t-1}
+// into chunk_buf, then run the adjoint backwards over its tokens. With
+// G = dL/dS_t (it gains do_t q^^T at token t), u = S_{t-1} k^:
+//   dq^ = S_t^T do_t = a (S_{t-1}^T do - b k^ (u . do)) + b k^ (v . do)
+//   da = <G, S_{t-1}> - b (u . G k^),  dv = b G k^,
+//   db = v . G k^ - a (u . G k^),
+//   dk^ = b G^T v - a b (S_{t-1}^T G k^ + G^T u),
+//   G <- a (G - b (G k^) k^^T)  (dL/dS_{t-1}),
+// and dx = dx^/n - x (x . dx^)/n^3 through the L2 normalisation.
+template <typename Tin, typename Tg, int D>
+__global__ void __launch_bounds__(kThreads)
+gdn_bwd_kernel(GdnParams p, int C, const float* ckpt, float* chunk_buf, const Tg* d_mix, const float* mix_w,
+               float* dq, float* dk, float* dv, float* da, float* db, float* dS0) {
+  constexpr int BS = D / 16;
+  __shared__ GdnBlock<D> sm;
+  const int h = blockIdx.x % p.H, b = blockIdx.x / p.H;
+  const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
+  const Tin* q = static_cast<const Tin*>(p.q);
+  const Tin* k = static_cast<const Tin*>(p.k);
+  const Tin* v = static_cast<const Tin*>(p.v);
+  const size_t HD = size_t(p.H) * D;
+  const float w2 = mix_w[3 * h + 2];
+  const float* ck = ckpt + size_t(b * p.H + h) * p.n_chunks * D * D;
+  float* cb = chunk_buf + size_t(b * p.H + h) * C * D * D;
+  float G[BS][BS], S[BS][BS];
+#pragma unroll
+  for (int i = 0; i < BS; ++i)
+#pragma unroll
+    for (int j = 0; j < BS; ++j) G[i][j] = 0.f;
+  auto blk = [&](int i, int j) { return size_t(tr * BS + i) * D + tc * BS + j; };
+  for (int c = p.n_chunks - 1; c >= 0; --c) {
+    const long long t0 = (long long)c * C;
+    const int n = int(p.L - t0 < C ? p.L - t0 : C);
+    // recompute the chunk's states before each token
+#pragma unroll
+    for (int i = 0; i < BS; ++i)
+#pragma unroll
+      for (int j = 0; j < BS; ++j) S[i][j] = ck[size_t(c) * D * D + blk(i, j)];
+    for (int s = 0; s < n; ++s) {
+#pragma unroll
+      for (int i = 0; i < BS; ++i)
+#pragma unroll
+        for (int j = 0; j < BS; ++j) cb[size_t(s) * D * D + blk(i, j)] = S[i][j];
+      const long long t = t0 + s;
+      const size_t tok = (size_t(b) * p.L + t) * HD + size_t(h) * D;
+      if (threadIdx.x < D) {
+        sm.vec[0][threadIdx.x] = ld(k, tok + threadIdx.x);
+        sm.vec[1][threadIdx.x] = ld(v, tok + threadIdx.x);
+      }
+      __syncthreads();
+      normalise(sm, sm.vec[0], sm.vec[2], 0, p.l2norm != 0);
+      reduce_mv<D, true>(sm, S, sm.vec[2], sm.vec[3]);
+      const size_t g = (size_t(b) * p.L + t) * p.H + h;
+      const float at = p.a[g], bt = p.b[g];
+#pragma unroll
+      for (int i = 0; i < BS; ++i)
+#pragma unroll
+        for (int j = 0; j < BS; ++j) {
+          const float kj = sm.vec[2][tc * BS + j];
+          S[i][j] = at * (S[i][j] - bt * sm.vec[3][tr * BS + i] * kj) + bt * sm.vec[1][tr * BS + i] * kj;
+        }
+      __syncthreads();
+    }
+    // adjoint over the chunk, last token first
+    for (int s = n - 1; s >= 0; --s) {
+#pragma unroll
+      for (int i = 0; i < BS; ++i)
+#pragma unroll
+        for (int j = 0; j < BS; ++j) S[i][j] = cb[size_t(s) * D * D + blk(i, j)];   // S_{t-1}
+      const long long t = t0 + s;
+      const size_t tok = (size_t(b) * p.L + t) * HD + size_t(h) * D;
+      const size_t g = (size_t(b) * p.L + t) * p.H + h;
+      const float at = p.a[g], bt = p.b[g];
+      // vec: 0 k, 1 v, 2 k^, 3 q, 4 q^, 5 do, 6 u, 7 S^T do, 8 G k^, 9 G^T v, 10 G^T u, 11 S^T G k^
+      if (threadIdx.x < D) {
+        sm.vec[0][threadIdx.x] = ld(k, tok + threadIdx.x);
+        sm.vec[1][threadIdx.x] = ld(v, tok + threadIdx.x);
+        sm.vec[3][threadIdx.x] = ld(q, tok + threadIdx.x);
+        sm.vec[5][threadIdx.x] = w2 * ld(d_mix, tok + threadIdx.x);
+      }
+      __syncthreads();
+      const float nk = normalise(sm, sm.vec[0], sm.vec[2], 0, p.l2norm != 0);
+      const float nq = normalise(sm, sm.vec[3], sm.vec[4], 1, p.l2norm != 0);
+      // G += do q^^T
+#pragma unroll
+      for (int i = 0; i < BS; ++i)
+#pragma unroll
+        for (int j = 0; j < BS; ++j) G[i][j] += sm.vec[5][tr * BS + i] * sm.vec[4][tc * BS + j];
+      reduce_mv<D, true>(sm, S, sm.vec[2], sm.vec[6]);    // u
+      reduce_mv<D, false>(sm, S, sm.vec[5], sm.vec[7]);   // S^T do
+      reduce_mv<D, true>(sm, G, sm.vec[2], sm.vec[8]);    // G k^
+      reduce_mv<D, false>(sm, G, sm.vec[1], sm.vec[9]);   // G^T v
+      reduce_mv<D, false>(sm, G, sm.vec[6], sm.vec[10]);  // G^T u
+      reduce_mv<D, false>(sm, S, sm.vec[8], sm.vec[11]);  // S^T G k^
+      float gs = 0.f;
+#pragma unroll
+      for (int i = 0; i < BS; ++i)
+#pragma unroll
+        for (int j = 0; j < BS; ++j) gs += G[i][j] * S[i][j];
+      const float GS = reduce_all(sm, gs, 2);
+      const float udo = dot(sm, sm.vec[6], sm.vec[5], 3);
+      const float vdo = dot(sm, sm.vec[1], sm.vec[5], 4);
+      const float uGk = dot(sm, sm.vec[6], sm.vec[8], 5);
+      const float vGk = dot(sm, sm.vec[1], sm.vec[8], 6);
+      if (threadIdx.x == 0) {
+        da[g] = GS - bt * uGk;
+        db[g] = vGk - at * uGk;
+      }
+      // dq^ and dk^ into vec[7] and vec[9] (their inputs are no longer needed)
+      if (threadIdx.x < D) {
+        const int i = threadIdx.x;
+        const float kh = sm.vec[2][i];
+        const float dqh = at * (sm.vec[7][i] - bt * kh * udo) + bt * kh * vdo;
+        const float dkh = bt * sm.vec[9][i] - at * bt * (sm.vec[11][i] + sm.vec[10][i]);
+        sm.vec[7][i] = dqh;
+        sm.vec[9][i] = dkh;
+        dv[tok + i] += bt * sm.vec[8][i];
+      }
+      __syncthreads();
+      const float qdq = dot(sm, sm.vec[3], sm.vec[7], 7);
+      const float kdk = dot(sm, sm.vec[0], sm.vec[9], 8);
+      if (threadIdx.x < D) {
+        const int i = threadIdx.x;
+        const float gq = p.l2norm ? sm.vec[7][i] / nq - sm.vec[3][i] * qdq / (nq * nq * nq) : sm.vec[7][i];
+        const float gk = p.l2norm ? sm.vec[9][i] / nk - sm.vec[0][i] * kdk / (nk * nk * nk) : sm.vec[9][i];
+        dq[tok + i] += gq;
+        dk[tok + i] += gk;
+      }
+      // G <- a (G - b (G k^) k^^T)
+#pragma unroll
+      for (int i = 0; i < BS; ++i)
+#pragma unroll
+        for (int j = 0; j < BS; ++j)
+          G[i][j] = at * (G[i][j] - bt * sm.vec[8][tr * BS + i] * sm.vec[2][tc * BS + j]);
+      __syncthreads();
+    }
+  }
+  if (dS0) {
+    const size_t sbase = (size_t(b) * p.H + h) * D * D;
+#pragma unroll
+    for (int i = 0; i < BS; ++i)
+#pragma unroll
+      for (int j = 0; j < BS; ++j) dS0[sbase + blk(i, j)] = G[i][j];
+  }
+}
+
+// dw[h, i] = <d_mix, o_i>: one workgroup per head, atomics across none
+template <typename Tg, typename Tout>
+__global__ void __launch_bounds__(kThreads)
+dmix_kernel(const Tg* d_mix, const Tout* o_swa, const Tout* o_dswa, const Tout* o_gdn, float* dw, long long ntok,
+            int H, int d) {
+  const int h = blockIdx.x;
+  float s[3] = {0.f, 0.f, 0.f};
+  for (long long e = threadIdx.x; e < ntok * d; e += kThreads) {
+    const size_t i = size_t(e / d) * H * d + size_t(h) * d + size_t(e % d);
+    const float g = ld(d_mix, i);
+    s[0] += g * ld(o_swa, i);
+    s[1] += g * ld(o_dswa, i);
+    s[2] += g * ld(o_gdn, i);
+  }
+  __shared__ float red[3][kThreads / 64];
+  for (int j = 0; j < 3; ++j) {
+    float x = s[j];
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    if ((threadIdx.x & 63) == 0) red[j][threadIdx.x >> 6] = x;
+  }
+  __syncthreads();
+  if (threadIdx.x < 3) {
+    float x = 0.f;
+    for (int w = 0; w < kThreads / 64; ++w) x += red[threadIdx.x][w];
+    dw[3 * h + threadIdx.x] = x;
+  }
+}
+
+template <typename Tin, typename Tg, int D>
+hipError_t launch_bwd_t(const BwdArgs& x, hipStream_t st) {
+  const AttnParams& p = x.attn;
+  const int tiles = (p.P + kRows - 1) / kRows;
+  const dim3 grid(unsigned(tiles * p.T), unsigned(p.H), unsigned(p.B));
+  const Tg* g = static_cast<const Tg*>(x.d_mix);
+  hipLaunchKernelGGL((attn_bwd_stats<Tin, Tg, D>), grid, dim3(kThreads), 0, st, p, g, x.mix_w, x.lse2, x.dsum);
+  hipLaunchKernelGGL((attn_bwd_dq<Tin, Tg, D>), grid, dim3(kThreads), 0, st, p, g, x.mix_w, x.lse2, x.dsum, x.dq,
+                     x.scale);
+  hipLaunchKernelGGL((attn_bwd_dkdv<Tin, Tg, D>), grid, dim3(kThreads), 0, st, p, g, x.mix_w, x.lse2, x.dsum,
+                     x.dk, x.dv, x.scale);
+  const unsigned heads = unsigned(x.gdn.B * x.gdn.H);
+  hipLaunchKernelGGL((gdn_ckpt_kernel<Tin, D>), dim3(heads), dim3(kThreads), 0, st, x.gdn, x.C, x.ckpt);
+  hipLaunchKernelGGL((gdn_bwd_kernel<Tin, Tg, D>), dim3(heads), dim3(kThreads), 0, st, x.gdn, x.C, x.ckpt,
+                     x.chunk_buf, g, x.mix_w, x.dq, x.dk, x.dv, x.da, x.db, x.dS0);
+  return hipGetLastError();
+}
+
+template <typename Tin, typename Tg>
+hipError_t launch_bwd_d(const BwdArgs& x, int d, hipStream_t st) {
+  switch (d) {
+    case 32: return launch_bwd_t<Tin, Tg, 32>(x, st);
+    case 64: return launch_bwd_t<Tin, Tg, 64>(x, st);
+    default: return launch_bwd_t<Tin, Tg, 128>(x, st);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& x, int d, int in_dt, int out_dt, hipStream_t st) {
+  hipError_t e;
+  if (in_dt == HLTA_BF16)
+    e = out_dt == HLTA_BF16 ? launch_bwd_d<bf16, bf16>(x, d, st) : launch_bwd_d<bf16, float>(x, d, st);
+  else
+    e = launch_bwd_d<float, float>(x, d, st);
+  if (e != hipSuccess) return e;
+  const long long ntok = (long long)x.attn.B * x.gdn.L;
+  if (out_dt == HLTA_BF16)
+    hipLaunchKernelGGL((dmix_kernel<bf16, bf16>), dim3(unsigned(x.attn.H)), dim3(kThreads), 0, st,
+                       static_cast<const bf16*>(x.d_mix), static_cast<const bf16*>(x.o_swa),
+                       static_cast<const bf16*>(x.o_dswa), static_cast<const bf16*>(x.o_gdn), x.dmix_w, ntok,
+                       x.attn.H, d);
+  else
+    hipLaunchKernelGGL((dmix_kernel<float, float>), dim3(unsigned(x.attn.H)), dim3(kThreads), 0, st,
+                       static_cast<const float*>(x.d_mix), static_cast<const float*>(x.o_swa),
+                       static_cast<const float*>(x.o_dswa), static_cast<const float*>(x.o_gdn), x.dmix_w, ntok,
+                       x.attn.H, d);
+  return hipGetLastError();
+}
+
+}  // namespace hlta

@@ -1,6 +1,7 @@
 // C-ABI entry points that launch work: hlta_fwd, hlta_gdn_fwd, hlta_attn_fwd,
-// hlta_stream_load_prefix, hlta_step_frame. Validation happens on the host before any launch; the
-// library allocates no device memory (scratch is the caller's workspace).
+// the FP8 pair, hlta_bwd, hlta_stream_load_prefix, hlta_step_frame(_rollouts).
+// Validation happens on the host before any launch; the library allocates no
+// device memory (scratch is the caller's workspace).
 #include <string>
 
 #include "hlta_device.h"
@@ -283,6 +284,75 @@ hlta_status hlta_attn_fwd_fp8(const hlta_config* cfg, const void* q8, const void
   hipError_t e = launch_attn_fp8(at, scales, cfg->out_dtype, st);
   if (e != hipSuccess) return hip_fail(e, "FP8 attention launch");
   return run_mix(cfg, plan, o_swa, o_dswa, o_gdn, o_mix, mix_w, st);
+}
+
+hlta_status hlta_bwd(const hlta_config* cfg, const void* q, const void* k, const void* v, const float* a,
+                     const float* b, const float* mix_w, const float* S0, const void* o_swa, const void* o_dswa,
+                     const void* o_gdn, const void* d_mix, float* dq, float* dk, float* dv, float* da, float* db,
+                     float* dmix_w, float* dS0, void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  Plan plan;
+  BwdPlan bp;
+  HLTA_TRY(check_config(cfg));
+  HLTA_TRY(make_plan(cfg, int64_t(cfg->T) * cfg->P, &plan));
+  HLTA_TRY(make_bwd_plan(cfg, &bp));
+  if (cfg->rope_theta > 0.f) return fail(HLTA_E_UNSUPPORTED, "the backward takes no rotary embedding");
+  if (cfg->gate_logits) return fail(HLTA_E_UNSUPPORTED, "the backward takes the gates themselves, not logits");
+  HLTA_TRY(maybe(S0, "S0"));
+  HLTA_TRY(maybe(dS0, "dS0"));
+  HLTA_TRY(need(dmix_w, "dmix_w"));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (plan.L == 0) {
+    // no tokens: every gradient that exists is zero
+    hipError_t e = hipMemsetAsync(dmix_w, 0, size_t(cfg->H) * 3 * sizeof(float), st);
+    if (e == hipSuccess && dS0) e = hipMemsetAsync(dS0, 0, state_bytes(cfg), st);
+    if (e != hipSuccess) return hip_fail(e, "gradient clear");
+    return HLTA_OK;
+  }
+  const void* ins[] = {q, k, v, a, b, mix_w, o_swa, o_dswa, o_gdn, d_mix, dq, dk, dv, da, db};
+  const char* names[] = {"q", "k", "v", "a", "b", "mix_w", "o_swa", "o_dswa", "o_gdn", "d_mix",
+                         "dq", "dk", "dv", "da", "db"};
+  for (int i = 0; i < 15; ++i) HLTA_TRY(need(ins[i], names[i]));
+  HLTA_TRY(need(workspace, "workspace"));
+  if (ws_bytes < bp.total)
+    return fail(HLTA_E_WORKSPACE, "workspace has " + std::to_string(ws_bytes) + " bytes, needs " +
+                                      std::to_string(bp.total));
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  BwdArgs x{};
+  x.attn = full_attn_params(cfg, q, k, v, nullptr, nullptr);
+  x.attn.scale_log2 = plan.scale * kLog2e;
+  x.gdn.q = q;
+  x.gdn.k = k;
+  x.gdn.v = v;
+  x.gdn.a = a;
+  x.gdn.b = b;
+  x.gdn.S0 = S0;
+  x.gdn.B = cfg->B;
+  x.gdn.H = cfg->H;
+  x.gdn.L = plan.L;
+  x.gdn.n_chunks = int(plan.n_chunks);
+  x.gdn.l2norm = cfg->gdn_l2norm_qk;
+  x.d_mix = d_mix;
+  x.mix_w = mix_w;
+  x.o_swa = o_swa;
+  x.o_dswa = o_dswa;
+  x.o_gdn = o_gdn;
+  x.dq = dq;
+  x.dk = dk;
+  x.dv = dv;
+  x.da = da;
+  x.db = db;
+  x.dmix_w = dmix_w;
+  x.dS0 = dS0;
+  x.lse2 = reinterpret_cast<float*>(ws);
+  x.dsum = reinterpret_cast<float*>(ws + bp.stats_bytes);
+  x.ckpt = reinterpret_cast<float*>(ws + bp.ckpt_off);
+  x.chunk_buf = reinterpret_cast<float*>(ws + bp.chunk_off);
+  x.C = cfg->gdn_chunk;
+  x.scale = plan.scale;
+  hipError_t e = launch_bwd(x, cfg->d, cfg->in_dtype, cfg->out_dtype, st);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return HLTA_OK;
 }
 
 static hlta_status check_stream(const hlta_config* cfg, const hlta_stream_state* st) {

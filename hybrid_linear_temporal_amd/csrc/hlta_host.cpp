@@ -125,6 +125,26 @@ hlta_status make_plan(const hlta_config* cfg, int64_t L, Plan* plan) {
   return HLTA_OK;
 }
 
+hlta_status make_bwd_plan(const hlta_config* cfg, BwdPlan* plan) {
+  hlta_status s = check_config(cfg);
+  if (s != HLTA_OK) return s;
+  const int64_t L = int64_t(cfg->T) * cfg->P, C = cfg->gdn_chunk, nch = (L + C - 1) / C;
+  const int64_t dd = int64_t(cfg->d) * cfg->d;
+  int64_t rows = 0, ck = 0, cb = 0;
+  if (!mul_ok(int64_t(cfg->B) * cfg->H, L, &rows) || !mul_ok(int64_t(cfg->B) * cfg->H * nch, dd, &ck) ||
+      !mul_ok(int64_t(cfg->B) * cfg->H * C, dd, &cb))
+    return fail(HLTA_E_SHAPE, "workspace overflow");
+  BwdPlan p;
+  p.stats_bytes = align_up(size_t(rows) * 2 * sizeof(float), 256);
+  p.ckpt_off = 2 * p.stats_bytes;
+  p.ckpt_bytes = align_up(size_t(ck) * sizeof(float), 256);
+  p.chunk_off = p.ckpt_off + p.ckpt_bytes;
+  p.chunk_bytes = align_up(size_t(cb) * sizeof(float), 256);
+  p.total = p.chunk_off + p.chunk_bytes;
+  *plan = p;
+  return HLTA_OK;
+}
+
 }  // namespace hlta
 
 using namespace hlta;
@@ -167,6 +187,13 @@ size_t hlta_step_workspace_bytes(const hlta_config* cfg) {
   Plan p;
   if (!cfg || make_plan(cfg, cfg->P, &p) != HLTA_OK) return 0;
   return p.ws_total;
+}
+
+size_t hlta_bwd_workspace_bytes(const hlta_config* cfg) {
+  clear_error();
+  BwdPlan p;
+  if (!cfg || make_bwd_plan(cfg, &p) != HLTA_OK) return 0;
+  return p.total;
 }
 
 size_t hlta_stream_ring_bytes(const hlta_config* cfg, int32_t ring_frames) {

@@ -36,6 +36,17 @@ hlta_status check_config(const hlta_config* cfg);
 // Kernel selection and workspace layout for a call over L tokens per row.
 hlta_status make_plan(const hlta_config* cfg, int64_t L, Plan* plan);
 
+// Workspace of the backward over L tokens per row: per-row softmax statistics
+// of both branches, then the memory's state checkpoints (one per chunk of C =
+// gdn_chunk tokens) and the states of one chunk, all fp32, 256-byte aligned.
+struct BwdPlan {
+  size_t stats_bytes = 0;   // lse2 and D, each [2, B, L, H]
+  size_t ckpt_off = 0, ckpt_bytes = 0;
+  size_t chunk_off = 0, chunk_bytes = 0;
+  size_t total = 0;
+};
+hlta_status make_bwd_plan(const hlta_config* cfg, BwdPlan* plan);
+
 // Is there an MFMA kernel for this shape?
 bool mfma_attn_supported(const hlta_config* cfg);
 bool mfma_gdn_supported(const hlta_config* cfg);

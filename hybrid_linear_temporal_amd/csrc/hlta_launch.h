@@ -53,4 +53,32 @@ hipError_t launch_rope_ring(void* ring, int B, int R, long long first, int n, in
 hipError_t launch_ring_store_rollouts(const void* src, void* ring, int R, int B, long long frame_elems, int elem,
                                       const RolloutFrames& sel, hipStream_t st);
 
+// Backward of the operator (bwd.hip): fp32 gradients of q, k, v [B, L, H, d],
+// a, b [B, L, H], mix_w [H, 3] and S0 [B, H, d, d] given d_mix (out dtype).
+// attn and gdn describe the forward (attn.scale_log2 set; gdn.n_chunks =
+// ceil(L / C)); the stored forward outputs feed the mix-weight gradient.
+struct BwdArgs {
+  AttnParams attn;
+  GdnParams gdn;
+  const void* d_mix;
+  const float* mix_w;
+  const void* o_swa;
+  const void* o_dswa;
+  const void* o_gdn;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* da;
+  float* db;
+  float* dmix_w;
+  float* dS0;        // or null
+  float* lse2;       // [2, B, L, H] workspace
+  float* dsum;       // [2, B, L, H] workspace
+  float* ckpt;       // [B*H, n_chunks, d, d] workspace
+  float* chunk_buf;  // [B*H, C, d, d] workspace
+  int C;
+  float scale;
+};
+hipError_t launch_bwd(const BwdArgs& x, int d, int in_dt, int out_dt, hipStream_t st);
+
 }  // namespace hlta

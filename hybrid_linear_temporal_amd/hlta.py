@@ -27,7 +27,8 @@ STATUS = {0: "HLTA_OK", 1: "HLTA_E_NULL", 2: "HLTA_E_SHAPE", 3: "HLTA_E_DTYPE", 
 EXPORTS = ("hlta_abi_version", "hlta_status_string", "hlta_last_error", "hlta_validate_config",
            "hlta_fwd_workspace_bytes", "hlta_fwd", "hlta_gdn_fwd", "hlta_attn_fwd", "hlta_stream_ring_bytes",
            "hlta_stream_load_prefix", "hlta_step_workspace_bytes", "hlta_step_frame",
-           "hlta_step_frame_rollouts", "hlta_quantize_fp8", "hlta_attn_fwd_fp8")
+           "hlta_step_frame_rollouts", "hlta_quantize_fp8", "hlta_attn_fwd_fp8", "hlta_bwd_workspace_bytes",
+           "hlta_bwd")
 
 
 class hlta_config(ctypes.Structure):
@@ -82,6 +83,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                            S, P]),
         "hlta_quantize_fp8": (I32, [cfgp, P, P, P, P, P, P, P, P]),
         "hlta_attn_fwd_fp8": (I32, [cfgp, P, P, P, P, P, P, P, P, P, P]),
+        "hlta_bwd_workspace_bytes": (S, [cfgp]),
+        "hlta_bwd": (I32, [cfgp] + [P] * 18 + [P, S, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -186,6 +189,32 @@ def hlta_attn_fwd(cfg: hlta_config, q, k, v, mix_w, o_gdn, out: dict, stream=Non
     _check(load_library().hlta_attn_fwd(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(mix_w), _ptr(o_gdn),
                                         _ptr(out["o_swa"]), _ptr(out["o_dswa"]), _ptr(out["o_mix"]),
                                         _stream(stream)))
+
+
+def hlta_bwd_workspace_bytes(cfg: hlta_config) -> int:
+    return int(load_library().hlta_bwd_workspace_bytes(ctypes.byref(cfg)))
+
+
+def hlta_bwd(cfg: hlta_config, q, k, v, a, b, mix_w, fwd: dict, d_mix, S0=None, want_dS0: bool = True,
+             workspace=None, stream=None) -> dict:
+    """Gradients of <d_mix, o_mix> (C: hlta_bwd). fwd holds the forward's
+    o_swa, o_dswa, o_gdn. Returns float32 dq, dk, dv [B, L, H, d], da, db
+    [B, L, H], dmix_w [H, 3] and dS0 [B, H, d, d] (None unless want_dS0)."""
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {n: torch.empty(q.shape, **f32) for n in ("dq", "dk", "dv")}
+    g["da"] = torch.empty(a.shape, **f32)
+    g["db"] = torch.empty(b.shape, **f32)
+    g["dmix_w"] = torch.empty((cfg.H, 3), **f32)
+    g["dS0"] = torch.empty((cfg.B, cfg.H, cfg.d, cfg.d), **f32) if want_dS0 else None
+    if workspace is None:
+        workspace = alloc_workspace(hlta_bwd_workspace_bytes(cfg), dev)
+    _check(load_library().hlta_bwd(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(mix_w),
+                                   _ptr(S0), _ptr(fwd["o_swa"]), _ptr(fwd["o_dswa"]), _ptr(fwd["o_gdn"]),
+                                   _ptr(d_mix), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["da"]),
+                                   _ptr(g["db"]), _ptr(g["dmix_w"]), _ptr(g["dS0"]), _ptr(workspace),
+                                   workspace.numel(), _stream(stream)))
+    return g
 
 
 def hlta_quantize_fp8(cfg: hlta_config, q, k, v, stream=None) -> dict:

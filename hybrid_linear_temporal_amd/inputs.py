@@ -26,7 +26,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 # field ids inside one stream
-F_Q, F_K, F_V, F_A, F_B, F_W = 0, 1, 2, 3, 4, 5
+F_Q, F_K, F_V, F_A, F_B, F_W, F_DO = 0, 1, 2, 3, 4, 5, 6
 # stream ids: 0 = the clip, 1 = the streaming prefix, 2 + s = streaming step s
 S_CLIP, S_PREFIX, S_STEP0 = 0, 1, 2
 
@@ -159,3 +159,15 @@ def stream_step_inputs(wl: Workload, s: int, threads: int = 8):
     """Inputs of streaming step s: one latent frame per rollout, [B, P, H, d]."""
     step_wl = dataclasses.replace(wl, T=1)
     return make_clip(step_wl, stream=S_STEP0 + s, T=1, threads=threads)
+
+
+def upstream_grad(wl: Workload, dtype: str, T: int | None = None, seed_offset: int = 0) -> np.ndarray:
+    """dL/do_mix for the backward: standard normal [B, L, H, d] values of dtype
+    (stored as float32), one generator per (b, h) as for the inputs."""
+    T = wl.T if T is None else T
+    L = T * wl.P
+    g = np.empty((wl.B, L, wl.H, wl.d), np.float32)
+    for b in range(wl.B):
+        for h in range(wl.H):
+            g[b, :, h] = cast(rng(wl.seed + seed_offset, S_CLIP, F_DO, b, h).standard_normal((L, wl.d)), dtype)
+    return g

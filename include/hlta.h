@@ -211,6 +211,38 @@ hlta_status hlta_attn_fwd_fp8(const hlta_config* cfg, const void* q8, const void
                               void* o_swa, void* o_dswa, void* o_mix, void* stream);
 
 /*
+ * hlta_bwd - gradients of the operator for training: with L = <d_mix, o_mix>,
+ * the branch gradients are do_i = w[h,i] * d_mix (the mix is linear) and
+ *   dmix_w[h,i] = <d_mix, o_i> over the stored branch outputs;
+ *   softmax branches: the exact gradient of softmax attention over each query
+ *     frame's key set (the branches are exact attention: long-context page,
+ *     section 03), recomputed from q, k, v with per-row log-sum-exp;
+ *   memory: the gated delta rule of hlta_fwd run backwards token by token from
+ *     per-chunk state checkpoints (Kairos related-work page, row A; long-context
+ *     page, section 06), through the L2 normalisation of q and k when on.
+ * dq, dk, dv receive the sum over the three branches.
+ *
+ * q, k, v, a, b, mix_w, S0   the forward's inputs (read only)
+ * o_swa, o_dswa, o_gdn       the forward's branch outputs, out_dtype (read only)
+ * d_mix      [B, L, H, d] out_dtype, dL/do_mix (read only)
+ * dq, dk, dv [B, L, H, d] float32 (written)
+ * da, db     [B, L, H] float32, gradients of the gates a and b (written)
+ * dmix_w     [H, 3] float32 (written)
+ * dS0        [B, H, d, d] float32 gradient of the start state, or NULL
+ * workspace  device buffer of at least hlta_bwd_workspace_bytes(cfg) bytes
+ * The gates are taken as given (gate_logits = 1 and the rotary embedding give
+ * HLTA_E_UNSUPPORTED). Gradients are evaluated in fp32 whatever the dtypes.
+ */
+size_t hlta_bwd_workspace_bytes(const hlta_config* cfg);
+hlta_status hlta_bwd(const hlta_config* cfg,
+                     const void* q, const void* k, const void* v,
+                     const float* a, const float* b, const float* mix_w, const float* S0,
+                     const void* o_swa, const void* o_dswa, const void* o_gdn, const void* d_mix,
+                     float* dq, float* dk, float* dv, float* da, float* db,
+                     float* dmix_w, float* dS0,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Streaming (Kairos article on zhichai.net, section 2.3: streaming tokens so
  * generation proceeds incrementally without recomputing the sequence).
  *

@@ -180,3 +180,40 @@ def test_rope_config_checks(lib):
     fake = ctypes.c_void_p(1 << 20)
     assert lib.hlta_attn_fwd(ctypes.byref(good), *([fake] * 9)) == 4
     assert b"workspace" in lib.hlta_last_error()
+
+
+def test_bwd_workspace_and_argument_errors(lib):
+    """Backward: workspace = two [2, B, L, H] fp32 statistics, one d x d state
+    per chunk and per chunk token; argument errors fail before any launch."""
+    cfg = _cfg()
+    L = cfg.T * cfg.P
+    chunks = -(-L // cfg.gdn_chunk)
+
+    def up(x):
+        return -(-x // 256) * 256
+
+    bh, dd = cfg.B * cfg.H, cfg.d * cfg.d * 4
+    want = 2 * up(bh * L * 2 * 4) + up(bh * chunks * dd) + up(bh * cfg.gdn_chunk * dd)
+    ws = H.hlta_bwd_workspace_bytes(cfg)
+    assert ws == want
+    assert H.hlta_bwd_workspace_bytes(_cfg(d=96)) == 0
+    fake = ctypes.c_void_p(1 << 20)
+    args = [fake] * 6 + [None] + [fake] * 10 + [None, fake]   # S0 and dS0 NULL
+
+    def call(c, a, nbytes=ws):
+        return lib.hlta_bwd(ctypes.byref(c), *a, nbytes, None)
+
+    for i, name in ((0, b"q"), (9, b"o_gdn"), (10, b"d_mix"), (15, b"db"), (16, b"dmix_w")):
+        a2 = list(args)
+        a2[i] = None
+        assert call(cfg, a2) == 1 and name + b" is NULL" in lib.hlta_last_error()
+    assert call(cfg, args, ws - 1) == 5
+    a2 = list(args)
+    a2[18] = None
+    assert call(cfg, a2) == 1
+    a2 = list(args)
+    a2[3] = ctypes.c_void_p((1 << 20) + 4)
+    assert call(cfg, a2) == 6
+    assert call(_cfg(gate_logits=1), args) == 4
+    rope = _cfg(rope_theta=10000.0, rope_grid=(30, 52))
+    assert call(rope, args) == 4
