@@ -275,6 +275,40 @@ def fp8_leg(H, wl, dev, out, steps, impl, attn_ms_bf16):
             "note": "attn_ms includes the mix kernel, as the bf16 attention time does"}
 
 
+def bwd_leg(H, wl, dev, out, S_out, steps, impl):
+    """The backward (hlta_bwd) on the same clip with a standard-normal upstream
+    gradient in the output dtype: whole-call time per step with HIP events, and
+    the softmax-branch part priced at the algorithmic backward flops (2.5x the
+    forward's: QK^T, dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    cfg = H.make_config(wl, impl=impl)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.seed + 7)
+    d_mix = torch.randn(out["o_mix"].shape, generator=gen, device="cuda").to(out["o_mix"].dtype)
+    ws = H.alloc_workspace(H.hlta_bwd_workspace_bytes(cfg))
+    S0 = torch.zeros_like(S_out)
+
+    def bwd():
+        return H.hlta_bwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], out, d_mix, S0=S0,
+                          workspace=ws, stream=stream)
+    g = bwd()
+    torch.cuda.synchronize()
+    finite = all(bool(torch.isfinite(t).all()) for t in g.values() if t is not None)
+    del g
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        bwd()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    attn_flops = 2.5 * work(wl)[0]
+    return {"steps": steps, "ms_per_step": ms, "tokens_per_s": wl.B * wl.L / (ms * 1e-3),
+            "attn_bwd_flops": attn_flops, "workspace_bytes": ws.numel(), "grads_finite": finite,
+            "note": "fp32 kernels; per-kernel times in the rocprofv3 summary"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -288,6 +322,8 @@ def main():
                     help="steps of the FP8 softmax branches timed (0: skip)")
     ap.add_argument("--rope-steps", type=int, default=5,
                     help="hlta_fwd steps timed with and without the rotary embedding (0: skip)")
+    ap.add_argument("--bwd-steps", type=int, default=1,
+                    help="steps of the backward (hlta_bwd) timed on the same clip (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB read + 1 GiB write elementwise kernel (3 launches), to scale "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -380,6 +416,9 @@ def main():
     if args.rope_steps > 0 and wl.P in LATENT_GRID:
         print(f"# rotary-embedding leg, {args.rope_steps} steps", file=sys.stderr, flush=True)
         res["rope"] = rope_leg(H, wl, dev, out, S_out, args.rope_steps, args.impl)
+    if args.bwd_steps > 0:
+        print(f"# backward leg, {args.bwd_steps} steps", file=sys.stderr, flush=True)
+        res["bwd"] = bwd_leg(H, wl, dev, out, S_out, args.bwd_steps, args.impl)
     if args.stream_steps > 0:
         del dev, out, ws
         torch.cuda.empty_cache()

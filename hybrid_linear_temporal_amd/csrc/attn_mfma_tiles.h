@@ -1,0 +1,228 @@
+// Tile machinery shared by the bf16 MFMA softmax-branch kernels (forward and
+// backward, d = 128): 64-row tiles of 256-byte rows in LDS with a per-row XOR
+// permutation of the 16-byte chunks, direct global -> LDS loads, the walk over
+// the rows of a branch's frames as one virtual sequence, and the MFMA operand
+// reads (row chunks and transposed reads) of gfx950.
+#pragma once
+
+#include "hlta_device.h"
+
+namespace hlta {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr int D = 128;           // head dim
+constexpr int KT = 64;           // keys per tile
+constexpr int NT = 256;          // threads
+constexpr int kXcds = 8;
+
+// one K or V tile: 64 rows of 256 B, 16-byte chunks permuted per row (swz)
+struct Tile {
+  uint4 row[KT][16];
+};
+
+// 16-byte chunk c of key row r sits at chunk position c ^ f(r mod 16), with f
+// swapping the two 2-bit halves of the row index. A 256-byte row spans all 64
+// LDS banks, so only the position matters: f is a bijection, so the 16 rows of
+// a K column read land on 16 positions, and the 8 rows x 4 chunks of a
+// transposed V read (rows 4*hl + e) reach all 16 positions twice, the minimum
+// two passes. With the plain c ^ (r mod 16) those V reads hit 8 positions
+// only (four-way bank conflicts, measured at 2.8x the time).
+__device__ __forceinline__ int swz(int r, int c) {
+  const int x = r & 15;
+  return c ^ (((x & 3) << 2) | (x >> 2));
+}
+
+// Wave-uniform values kept in scalar registers.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+template <typename T>
+__device__ __forceinline__ const T* uni(const T* ptr) {
+  const unsigned long long u = reinterpret_cast<unsigned long long>(ptr);
+  const unsigned lo = __builtin_amdgcn_readfirstlane(unsigned(u));
+  const unsigned hi = __builtin_amdgcn_readfirstlane(unsigned(u >> 32));
+  return reinterpret_cast<const T*>((static_cast<unsigned long long>(hi) << 32) | lo);
+}
+
+// Walks the virtual key sequence of one branch tile by tile (the key-major
+// backward walks the queries of the frames that read a key frame the same way). A tile of 64
+// keys spans at most two frames (P >= 64); all fields are wave-uniform.
+// Frames of a branch are g, g + step, ...: step 1 for SWA (oldest first),
+// -dil for DSWA. In stream mode the call's own frame f0 comes from the main
+// tensors and earlier frames from ring slot g mod R.
+template <bool kRing>
+struct KeyStream {
+  const bf16* kmain;     // token 0 of frame 0 (full mode) or of the call's frame (stream mode), head h
+  const bf16* vmain;
+  const bf16* kring;     // token 0 of ring slot 0, head h (stream mode)
+  const bf16* vring;
+  size_t fstride;        // elements between consecutive frames: P*H*D
+  long long f0;
+  int R;
+  long long g;           // current frame
+  int step, left, P;     // frame step, frames after the current one, tokens per frame
+  int pk;                // current tile starts at token pk of the current frame
+  const bf16* k0;        // token 0 of the current frame
+  const bf16* v0;
+  const bf16* k1;        // token 0 of the next frame (the current one if none)
+  const bf16* v1;
+
+  __device__ __forceinline__ void frame_ptrs(long long gg, const bf16*& kb, const bf16*& vb) const {
+    if constexpr (!kRing) {
+      const size_t off = size_t(gg) * fstride;
+      kb = uni(kmain + off);
+      vb = uni(vmain + off);
+    } else {
+      if (gg == f0) {
+        kb = kmain;
+        vb = vmain;
+      } else {
+        const size_t off = size_t(unsigned(gg) % unsigned(R)) * fstride;
+        kb = uni(kring + off);
+        vb = uni(vring + off);
+      }
+    }
+  }
+  __device__ __forceinline__ void start(long long g_first, int step_, int nframes) {
+    g = g_first;
+    step = step_;
+    left = nframes - 1;
+    pk = 0;
+    if (nframes > 0) frame_ptrs(g, k0, v0);
+    if (nframes > 1) frame_ptrs(g + step, k1, v1);
+    else {
+      k1 = k0;
+      v1 = v0;
+    }
+  }
+  __device__ __forceinline__ void advance() {
+    pk += KT;
+    if (pk >= P) {
+      pk -= P;
+      g += step;
+      --left;
+      k0 = k1;
+      v0 = v1;
+      if (left > 0) frame_ptrs(g + step, k1, v1);
+    }
+  }
+};
+
+// Buffer resource over [base, base + bytes): 32-bit lane offsets on a scalar base.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+
+// Direct global -> LDS copy of the current tile: wave w moves rows 16w .. 16w+15,
+// four rows (1 KB) per instruction; lane i lands at chunk position i%16 of row
+// 16w + 4j + i/16 and so loads the chunk that the swizzle puts there. A tile
+// inside one frame (the common case) loads through buffer resources with the
+// precomputed lane offsets `off` (no per-lane address arithmetic); a tile
+// across a frame boundary or past the end of the sequence computes each lane's
+// row, and rows past the end re-read the last valid row (finite data; their
+// scores are masked, so they contribute exactly zero).
+template <bool kRing, bool kV = true>
+__device__ __forceinline__ void issue_tile(Tile& Kd, Tile& Vd, const KeyStream<kRing>& ks, int kleft,
+                                           const unsigned (&off)[4], size_t ts, int wave, int lane) {
+  if (ks.pk + KT <= ks.P && kleft >= KT) {
+    const unsigned bytes = unsigned(KT * ts * sizeof(bf16));
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(ks.k0 + size_t(ks.pk) * ts, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(ks.v0 + size_t(ks.pk) * ts, bytes);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r0 = 16 * wave + 4 * j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(&Kd.row[r0][0]), 16,
+                                               off[j], 0, 0, 0);
+      if constexpr (kV)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(&Vd.row[r0][0]),
+                                                 16, off[j], 0, 0, 0);
+    }
+    return;
+  }
+  const int split = ks.P - ks.pk;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r0 = 16 * wave + 4 * j;
+    const int row = r0 + (lane >> 4);
+    const int rr = row < kleft ? row : kleft - 1;
+    const int c = swz(row, lane & 15);
+    const size_t koff = rr < split ? size_t(ks.pk + rr) * ts : size_t(rr - split) * ts;
+    const bf16* ksrc = (rr < split ? ks.k0 : ks.k1) + koff + c * 8;
+    const bf16* vsrc = (rr < split ? ks.v0 : ks.v1) + koff + c * 8;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(ksrc),
+                                     (__attribute__((address_space(3))) void*)(&Kd.row[r0][0]), 16, 0, 0);
+    if constexpr (kV)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vsrc),
+                                       (__attribute__((address_space(3))) void*)(&Vd.row[r0][0]), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+// Lanes l and l ^ 32 combined without LDS: v_permlane32_swap on two copies of
+// x leaves (x[l], x[l^32]) in lanes below 32 and (x[l^32], x[l]) above (lane
+// layout checked on the GPU). The results are copied out of the returned
+// vector before the bit casts: casting the vector elements in place reads
+// element 0 twice with this compiler.
+__device__ __forceinline__ void pair_xor32(float x, float& a, float& b) {
+  const unsigned xa = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(xa, xa, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  float a, b;
+  pair_xor32(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  float a, b;
+  pair_xor32(x, a, b);
+  return a + b;
+}
+
+// Address of (lane part + constant part) inside a tile. The lane part is made
+// provably less than 16 KB, so the compiler folds the constant part and the
+// tile's own LDS address into the instruction's immediate offset: one set of
+// lane address registers serves both buffers and every key block.
+__device__ __forceinline__ const char* at(const Tile& t, int lane_off, int const_off) {
+  return reinterpret_cast<const char*>(&t) + (unsigned(lane_off) & unsigned(sizeof(Tile) - 1)) + const_off;
+}
+
+// 8 consecutive d values (chunk c) of key row kb*32 + l32
+__device__ __forceinline__ bf16x8 ld_chunk(const Tile& t, int kb, int l32, int c) {
+  return *reinterpret_cast<const bf16x8*>(at(t, l32 * 256 + swz(l32, c) * 16, kb * 32 * 256));
+}
+
+// V^T operand of one 32x32x16 MFMA: lane = d row (d0 + l16 inside its 16-lane group),
+// slots 0..3 = keys k0 .. k0+3, slots 4..7 = keys k0+8 .. k0+11 with
+// k0 = kb*32 + 16*m2 + 4*hl, read transposed: lane 4e+q of the group addresses
+// key row k0+e (+8), d columns d0 + 4q .. +3. Rows kb*32 + 16*m2 + x share
+// their swizzle with row x, so only x enters the lane part.
+__device__ __forceinline__ bf16x8 ld_vt(const Tile& t, int kb, int m2, int hl, int d0, int l16) {
+  const int e = l16 >> 2, q = l16 & 3;
+  const int dcol = d0 + 4 * q;
+  const int x0 = 4 * hl + e, x1 = x0 + 8;
+  const int kc = (kb * 32 + 16 * m2) * 256;
+  const char* p0 = at(t, x0 * 256 + swz(x0, dcol >> 3) * 16 + (dcol & 7) * 2, kc);
+  const char* p1 = at(t, x1 * 256 + swz(x1, dcol >> 3) * 16 + (dcol & 7) * 2, kc);
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p1));
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ void store4(bf16* p, const float* v) {
+  bf16x4 x = {static_cast<bf16>(v[0]), static_cast<bf16>(v[1]), static_cast<bf16>(v[2]), static_cast<bf16>(v[3])};
+  *reinterpret_cast<bf16x4*>(p) = x;
+}
+__device__ __forceinline__ void store4(float* p, const float* v) {
+  f32x4 x = {v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<f32x4*>(p) = x;
+}
+
+}  // namespace
+}  // namespace hlta

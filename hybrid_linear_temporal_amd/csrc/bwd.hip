@@ -10,13 +10,19 @@
 //    each key frame, the query frames whose frame set holds it and
 //    accumulates dv = sum_i P do_i and dk = s sum_i P (do_i . v - D_i) q_i;
 //  * gated delta rule (Kairos related-work page, row A; long-context page,
-//    section 06): a forward pass checkpoints S every C tokens, then chunk by
-//    chunk from the end the chunk's states are recomputed and the adjoint
-//    G = dL/dS_t is carried backwards token by token (the formulas are in
-//    gdn_bwd_kernel). One workgroup per (batch row, head); each thread owns an
-//    (d/16) x (d/16) block of S and of G, and row and column reductions go
-//    through LDS;
+//    section 06): with M_t = a_t (I - b_t k^ k^^T) the state obeys
+//    S_t = S_{t-1} M_t + b_t v_t k^_t^T and its adjoint G_{t-1} = G_t M_t +
+//    do_{t-1} q^_{t-1}^T. Per chunk of C tokens, in parallel, the transition
+//    A_c (product of the M_t), the chunk's own state from zero U_c and its own
+//    adjoint from zero X_c; then two short chains over chunks give every
+//    chunk's start state and the adjoint reaching its end; then, per chunk in
+//    parallel again, the states are recomputed token by token and the adjoint
+//    carried back over the chunk, giving the token gradients (formulas at
+//    gdn_bwd_tokens). Exact in fp32 (no approximation beyond rounding);
+//    one workgroup per matrix, each thread owning a (d/16) x (d/16) block;
 //  * mix weights: dw[h, i] = <d_mix, o_i> over the stored branch outputs.
+// With bf16 inputs and outputs, d = 128 and P >= 64 the softmax branches run
+// on the bf16 MFMA kernels of attn_bwd_mfma.hip instead.
 #include "hlta_device.h"
 #include "hlta_launch.h"
 
@@ -349,122 +355,230 @@ __device__ __forceinline__ float normalise(GdnBlock<D>& sm, const float* x, floa
   return n;
 }
 
-// Forward with checkpoints: S before token c*C for every chunk c.
-template <typename Tin, int D>
-__global__ void __launch_bounds__(kThreads)
-gdn_ckpt_kernel(GdnParams p, int C, float* ckpt) {
+// One token of the memory on S (held in blocks): vec[0] = k and vec[1] = v
+// are in LDS; leaves k^ in vec[2] and u = S k^ in vec[3], and applies
+// S <- a (S - b u k^^T) (+ b v k^^T when with_v).
+template <int D>
+__device__ __forceinline__ void fwd_token(GdnBlock<D>& sm, float (&S)[D / 16][D / 16], float at, float bt, bool l2,
+                                          bool with_v) {
   constexpr int BS = D / 16;
-  __shared__ GdnBlock<D> sm;
-  const int h = blockIdx.x % p.H, b = blockIdx.x / p.H;
   const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
-  const size_t sbase = (size_t(b) * p.H + h) * D * D;
-  float S[BS][BS];
+  normalise(sm, sm.vec[0], sm.vec[2], 0, l2);
+  reduce_mv<D, true>(sm, S, sm.vec[2], sm.vec[3]);
 #pragma unroll
   for (int i = 0; i < BS; ++i)
 #pragma unroll
-    for (int j = 0; j < BS; ++j) S[i][j] = p.S0 ? p.S0[sbase + size_t(tr * BS + i) * D + tc * BS + j] : 0.f;
+    for (int j = 0; j < BS; ++j) {
+      const float kj = sm.vec[2][tc * BS + j];
+      const float vt = with_v ? bt * sm.vec[1][tr * BS + i] * kj : 0.f;
+      S[i][j] = at * (S[i][j] - bt * sm.vec[3][tr * BS + i] * kj) + vt;
+    }
+  __syncthreads();
+}
+
+template <int D>
+__device__ __forceinline__ void load_mat(float (&M)[D / 16][D / 16], const float* src) {
+  constexpr int BS = D / 16;
+  const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
+#pragma unroll
+  for (int i = 0; i < BS; ++i)
+#pragma unroll
+    for (int j = 0; j < BS; ++j) M[i][j] = src ? src[size_t(tr * BS + i) * D + tc * BS + j] : 0.f;
+}
+template <int D>
+__device__ __forceinline__ void store_mat(float* dst, const float (&M)[D / 16][D / 16]) {
+  constexpr int BS = D / 16;
+  const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
+#pragma unroll
+  for (int i = 0; i < BS; ++i)
+#pragma unroll
+    for (int j = 0; j < BS; ++j) dst[size_t(tr * BS + i) * D + tc * BS + j] = M[i][j];
+}
+
+// Chunk c of head (b, h) covers tokens [c*C, min(L, (c+1)*C)). With
+// M_t = a_t (I - b_t k^_t k^_t^T) (symmetric), per chunk:
+//   what 0: A_c = M_s M_{s+1} .. M_e            (S_end = S_start A_c + U_c)
+//   what 1: U_c = the chunk's own state from S = 0
+//   what 2: X_c = sum_t do_t q^_t^T M_t M_{t-1} .. M_s
+//           (the chunk's own adjoint carried to its start; G = dL/dS)
+// grid (B*H*n_chunks, 3); one matrix per workgroup.
+template <typename Tin, typename Tg, int D>
+__global__ void __launch_bounds__(kThreads)
+gdn_bwd_prep(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float* Am, float* Um, float* Xm) {
+  constexpr int BS = D / 16;
+  __shared__ GdnBlock<D> sm;
+  const int what = blockIdx.y;
+  const long long job = blockIdx.x;
+  const int c = int(job % p.n_chunks), bh = int(job / p.n_chunks), b = bh / p.H, h = bh % p.H;
+  const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
+  const Tin* q = static_cast<const Tin*>(p.q);
   const Tin* k = static_cast<const Tin*>(p.k);
   const Tin* v = static_cast<const Tin*>(p.v);
   const size_t HD = size_t(p.H) * D;
-  float* ck = ckpt + size_t(b * p.H + h) * p.n_chunks * D * D;
-  for (long long t = 0; t < p.L; ++t) {
-    if (t % C == 0) {
-      float* dst = ck + size_t(t / C) * D * D;
+  const long long t0 = (long long)c * C;
+  const int n = int(p.L - t0 < C ? p.L - t0 : C);
+  const bool l2 = p.l2norm != 0;
+  float M[BS][BS];
+#pragma unroll
+  for (int i = 0; i < BS; ++i)
+#pragma unroll
+    for (int j = 0; j < BS; ++j) M[i][j] = (what == 0 && tr * BS + i == tc * BS + j) ? 1.f : 0.f;
+  if (what < 2) {
+    for (int s = 0; s < n; ++s) {
+      const size_t tok = (size_t(b) * p.L + t0 + s) * HD + size_t(h) * D;
+      if (threadIdx.x < D) {
+        sm.vec[0][threadIdx.x] = ld(k, tok + threadIdx.x);
+        sm.vec[1][threadIdx.x] = ld(v, tok + threadIdx.x);
+      }
+      __syncthreads();
+      const size_t g = (size_t(b) * p.L + t0 + s) * p.H + h;
+      fwd_token(sm, M, p.a[g], p.b[g], l2, what == 1);
+    }
+  } else {
+    const float w2 = mix_w[3 * h + 2];
+    for (int s = n - 1; s >= 0; --s) {
+      const size_t tok = (size_t(b) * p.L + t0 + s) * HD + size_t(h) * D;
+      if (threadIdx.x < D) {
+        sm.vec[0][threadIdx.x] = ld(k, tok + threadIdx.x);
+        sm.vec[5][threadIdx.x] = w2 * ld(d_mix, tok + threadIdx.x);
+        sm.vec[6][threadIdx.x] = ld(q, tok + threadIdx.x);
+      }
+      __syncthreads();
+      normalise(sm, sm.vec[0], sm.vec[2], 0, l2);
+      normalise(sm, sm.vec[6], sm.vec[4], 1, l2);
+      const size_t g = (size_t(b) * p.L + t0 + s) * p.H + h;
+      const float at = p.a[g], bt = p.b[g];
+      // M <- (M + do q^^T) M_t
 #pragma unroll
       for (int i = 0; i < BS; ++i)
 #pragma unroll
-        for (int j = 0; j < BS; ++j) dst[size_t(tr * BS + i) * D + tc * BS + j] = S[i][j];
+        for (int j = 0; j < BS; ++j) M[i][j] += sm.vec[5][tr * BS + i] * sm.vec[4][tc * BS + j];
+      reduce_mv<D, true>(sm, M, sm.vec[2], sm.vec[8]);
+#pragma unroll
+      for (int i = 0; i < BS; ++i)
+#pragma unroll
+        for (int j = 0; j < BS; ++j) M[i][j] = at * (M[i][j] - bt * sm.vec[8][tr * BS + i] * sm.vec[2][tc * BS + j]);
+      __syncthreads();
     }
-    const size_t tok = (size_t(b) * p.L + t) * HD + size_t(h) * D;
-    if (threadIdx.x < D) {
-      sm.vec[0][threadIdx.x] = ld(k, tok + threadIdx.x);
-      sm.vec[1][threadIdx.x] = ld(v, tok + threadIdx.x);
+  }
+  float* dst = what == 0 ? Am : (what == 1 ? Um : Xm);
+  store_mat<D>(dst + size_t(job) * D * D, M);
+}
+
+// The two chains over chunks, rows of the state split over workgroups (rows
+// evolve independently: row i of S A + U only needs row i of S and U):
+//   dir 0: S_start(0) = S0, S_start(c+1) = S_start(c) A_c + U_c
+//   dir 1: R(N-1) = 0,      R(c-1) = R(c) A_c^T + X_c, dS0 = R(-1)
+// R(c) is the adjoint reaching the end of chunk c from later tokens. A_c is
+// staged in LDS (padded rows) per step; a thread owns one row of the group
+// and CPT columns. grid (B*H, D/16, 2).
+constexpr int kChainRows = 16;
+template <int D>
+__global__ void __launch_bounds__(kThreads)
+gdn_bwd_chain(int n_chunks, const float* S0, const float* Am, const float* Um, const float* Xm, float* Sst,
+              float* Rin, float* dS0) {
+  __shared__ float As[D][D + 1];
+  __shared__ float rows[kChainRows][D];
+  constexpr int CPT = D * kChainRows / kThreads;   // columns per thread: 8 (d = 128), 4 (64), 2 (32)
+  const int bh = blockIdx.x, r0 = blockIdx.y * kChainRows, dir = blockIdx.z;
+  const int r = threadIdx.x / (D / CPT), j0 = (threadIdx.x % (D / CPT)) * CPT;
+  const size_t mat = size_t(D) * D;
+  const size_t base = size_t(bh) * n_chunks * mat;
+#pragma unroll
+  for (int jj = 0; jj < CPT; ++jj)
+    rows[r][j0 + jj] = (dir == 0 && S0) ? S0[size_t(bh) * mat + size_t(r0 + r) * D + j0 + jj] : 0.f;
+  for (int step = 0; step < n_chunks; ++step) {
+    const int c = dir == 0 ? step : n_chunks - 1 - step;
+    const float* A = Am + base + size_t(c) * mat;
+    __syncthreads();
+    for (int e = threadIdx.x; e < D * D / 4; e += kThreads) {
+      const float4 x = reinterpret_cast<const float4*>(A)[e];
+      const int i = (e * 4) / D, j = (e * 4) % D;
+      As[i][j] = x.x;
+      As[i][j + 1] = x.y;
+      As[i][j + 2] = x.z;
+      As[i][j + 3] = x.w;
     }
     __syncthreads();
-    normalise(sm, sm.vec[0], sm.vec[2], 0, p.l2norm != 0);   // vec[2] = k^
-    reduce_mv<D, true>(sm, S, sm.vec[2], sm.vec[3]);          // vec[3] = u = S k^
-    const size_t g = (size_t(b) * p.L + t) * p.H + h;
-    const float at = p.a[g], bt = p.b[g];
+    float out[CPT];
+    float* rec = (dir == 0 ? Sst : Rin) + base + size_t(c) * mat + size_t(r0 + r) * D + j0;
 #pragma unroll
-    for (int i = 0; i < BS; ++i)
+    for (int jj = 0; jj < CPT; ++jj) {
+      rec[jj] = rows[r][j0 + jj];
+      out[jj] = 0.f;
+    }
+    for (int kk = 0; kk < D; ++kk) {
+      const float x = rows[r][kk];
 #pragma unroll
-      for (int j = 0; j < BS; ++j) {
-        const float kj = sm.vec[2][tc * BS + j];
-        S[i][j] = at * (S[i][j] - bt * sm.vec[3][tr * BS + i] * kj) + bt * sm.vec[1][tr * BS + i] * kj;
-      }
+      for (int jj = 0; jj < CPT; ++jj) out[jj] += x * (dir == 0 ? As[kk][j0 + jj] : As[j0 + jj][kk]);
+    }
+    const float* add = (dir == 0 ? Um : Xm) + base + size_t(c) * mat + size_t(r0 + r) * D + j0;
+#pragma unroll
+    for (int jj = 0; jj < CPT; ++jj) out[jj] += add[jj];
     __syncthreads();
+#pragma unroll
+    for (int jj = 0; jj < CPT; ++jj) rows[r][j0 + jj] = out[jj];
+  }
+  if (dir == 1 && dS0) {
+#pragma unroll
+    for (int jj = 0; jj < CPT; ++jj) dS0[size_t(bh) * mat + size_t(r0 + r) * D + j0 + jj] = rows[r][j0 + jj];
   }
 }
 
-// Backward: per chunk from the last, recompute the chunk's states S_{t-1}
-// into chunk_buf, then run the adjoint backwards over its tokens. With
-// G = dL/dS_t (it gains do_t q^^T at token t), u = S_{t-1} k^:
+// Gradients of one chunk's tokens from its start state S_start(c) and the
+// adjoint R(c) reaching its end: the chunk's states are recomputed into this
+// workgroup's slot, then the adjoint is carried backwards token by token.
+// With G = dL/dS_t (it gains do_t q^^T at token t), u = S_{t-1} k^:
 //   dq^ = S_t^T do_t = a (S_{t-1}^T do - b k^ (u . do)) + b k^ (v . do)
 //   da = <G, S_{t-1}> - b (u . G k^),  dv = b G k^,
 //   db = v . G k^ - a (u . G k^),
 //   dk^ = b G^T v - a b (S_{t-1}^T G k^ + G^T u),
 //   G <- a (G - b (G k^) k^^T)  (dL/dS_{t-1}),
 // and dx = dx^/n - x (x . dx^)/n^3 through the L2 normalisation.
+// Persistent: workgroup i takes jobs i, i + grid, ... (job = (b*H + h)*N + c).
 template <typename Tin, typename Tg, int D>
 __global__ void __launch_bounds__(kThreads)
-gdn_bwd_kernel(GdnParams p, int C, const float* ckpt, float* chunk_buf, const Tg* d_mix, const float* mix_w,
-               float* dq, float* dk, float* dv, float* da, float* db, float* dS0) {
+gdn_bwd_tokens(GdnParams p, int C, const float* Sst, const float* Rin, float* slots, const Tg* d_mix,
+               const float* mix_w, float* dq, float* dk, float* dv, float* da, float* db) {
   constexpr int BS = D / 16;
   __shared__ GdnBlock<D> sm;
-  const int h = blockIdx.x % p.H, b = blockIdx.x / p.H;
   const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
   const Tin* q = static_cast<const Tin*>(p.q);
   const Tin* k = static_cast<const Tin*>(p.k);
   const Tin* v = static_cast<const Tin*>(p.v);
   const size_t HD = size_t(p.H) * D;
-  const float w2 = mix_w[3 * h + 2];
-  const float* ck = ckpt + size_t(b * p.H + h) * p.n_chunks * D * D;
-  float* cb = chunk_buf + size_t(b * p.H + h) * C * D * D;
-  float G[BS][BS], S[BS][BS];
-#pragma unroll
-  for (int i = 0; i < BS; ++i)
-#pragma unroll
-    for (int j = 0; j < BS; ++j) G[i][j] = 0.f;
+  const size_t mat = size_t(D) * D;
+  float* cb = slots + size_t(blockIdx.x) * C * mat;
+  const long long jobs = (long long)p.B * p.H * p.n_chunks;
+  const bool l2 = p.l2norm != 0;
   auto blk = [&](int i, int j) { return size_t(tr * BS + i) * D + tc * BS + j; };
-  for (int c = p.n_chunks - 1; c >= 0; --c) {
+  for (long long job = blockIdx.x; job < jobs; job += gridDim.x) {
+    const int c = int(job % p.n_chunks), bh = int(job / p.n_chunks), b = bh / p.H, h = bh % p.H;
+    const float w2 = mix_w[3 * h + 2];
     const long long t0 = (long long)c * C;
     const int n = int(p.L - t0 < C ? p.L - t0 : C);
-    // recompute the chunk's states before each token
-#pragma unroll
-    for (int i = 0; i < BS; ++i)
-#pragma unroll
-      for (int j = 0; j < BS; ++j) S[i][j] = ck[size_t(c) * D * D + blk(i, j)];
+    float S[BS][BS], G[BS][BS];
+    load_mat<D>(S, Sst + size_t(job) * mat);
     for (int s = 0; s < n; ++s) {
 #pragma unroll
       for (int i = 0; i < BS; ++i)
 #pragma unroll
-        for (int j = 0; j < BS; ++j) cb[size_t(s) * D * D + blk(i, j)] = S[i][j];
-      const long long t = t0 + s;
-      const size_t tok = (size_t(b) * p.L + t) * HD + size_t(h) * D;
+        for (int j = 0; j < BS; ++j) cb[size_t(s) * mat + blk(i, j)] = S[i][j];
+      const size_t tok = (size_t(b) * p.L + t0 + s) * HD + size_t(h) * D;
       if (threadIdx.x < D) {
         sm.vec[0][threadIdx.x] = ld(k, tok + threadIdx.x);
         sm.vec[1][threadIdx.x] = ld(v, tok + threadIdx.x);
       }
       __syncthreads();
-      normalise(sm, sm.vec[0], sm.vec[2], 0, p.l2norm != 0);
-      reduce_mv<D, true>(sm, S, sm.vec[2], sm.vec[3]);
-      const size_t g = (size_t(b) * p.L + t) * p.H + h;
-      const float at = p.a[g], bt = p.b[g];
-#pragma unroll
-      for (int i = 0; i < BS; ++i)
-#pragma unroll
-        for (int j = 0; j < BS; ++j) {
-          const float kj = sm.vec[2][tc * BS + j];
-          S[i][j] = at * (S[i][j] - bt * sm.vec[3][tr * BS + i] * kj) + bt * sm.vec[1][tr * BS + i] * kj;
-        }
-      __syncthreads();
+      const size_t g = (size_t(b) * p.L + t0 + s) * p.H + h;
+      fwd_token(sm, S, p.a[g], p.b[g], l2, true);
     }
-    // adjoint over the chunk, last token first
+    load_mat<D>(G, Rin + size_t(job) * mat);
     for (int s = n - 1; s >= 0; --s) {
 #pragma unroll
       for (int i = 0; i < BS; ++i)
 #pragma unroll
-        for (int j = 0; j < BS; ++j) S[i][j] = cb[size_t(s) * D * D + blk(i, j)];   // S_{t-1}
+        for (int j = 0; j < BS; ++j) S[i][j] = cb[size_t(s) * mat + blk(i, j)];   // S_{t-1}
       const long long t = t0 + s;
       const size_t tok = (size_t(b) * p.L + t) * HD + size_t(h) * D;
       const size_t g = (size_t(b) * p.L + t) * p.H + h;
@@ -477,9 +591,8 @@ gdn_bwd_kernel(GdnParams p, int C, const float* ckpt, float* chunk_buf, const Tg
         sm.vec[5][threadIdx.x] = w2 * ld(d_mix, tok + threadIdx.x);
       }
       __syncthreads();
-      const float nk = normalise(sm, sm.vec[0], sm.vec[2], 0, p.l2norm != 0);
-      const float nq = normalise(sm, sm.vec[3], sm.vec[4], 1, p.l2norm != 0);
-      // G += do q^^T
+      const float nk = normalise(sm, sm.vec[0], sm.vec[2], 0, l2);
+      const float nq = normalise(sm, sm.vec[3], sm.vec[4], 1, l2);
 #pragma unroll
       for (int i = 0; i < BS; ++i)
 #pragma unroll
@@ -504,7 +617,6 @@ gdn_bwd_kernel(GdnParams p, int C, const float* ckpt, float* chunk_buf, const Tg
         da[g] = GS - bt * uGk;
         db[g] = vGk - at * uGk;
       }
-      // dq^ and dk^ into vec[7] and vec[9] (their inputs are no longer needed)
       if (threadIdx.x < D) {
         const int i = threadIdx.x;
         const float kh = sm.vec[2][i];
@@ -519,12 +631,11 @@ gdn_bwd_kernel(GdnParams p, int C, const float* ckpt, float* chunk_buf, const Tg
       const float kdk = dot(sm, sm.vec[0], sm.vec[9], 8);
       if (threadIdx.x < D) {
         const int i = threadIdx.x;
-        const float gq = p.l2norm ? sm.vec[7][i] / nq - sm.vec[3][i] * qdq / (nq * nq * nq) : sm.vec[7][i];
-        const float gk = p.l2norm ? sm.vec[9][i] / nk - sm.vec[0][i] * kdk / (nk * nk * nk) : sm.vec[9][i];
+        const float gq = l2 ? sm.vec[7][i] / nq - sm.vec[3][i] * qdq / (nq * nq * nq) : sm.vec[7][i];
+        const float gk = l2 ? sm.vec[9][i] / nk - sm.vec[0][i] * kdk / (nk * nk * nk) : sm.vec[9][i];
         dq[tok + i] += gq;
         dk[tok + i] += gk;
       }
-      // G <- a (G - b (G k^) k^^T)
 #pragma unroll
       for (int i = 0; i < BS; ++i)
 #pragma unroll
@@ -533,23 +644,18 @@ gdn_bwd_kernel(GdnParams p, int C, const float* ckpt, float* chunk_buf, const Tg
       __syncthreads();
     }
   }
-  if (dS0) {
-    const size_t sbase = (size_t(b) * p.H + h) * D * D;
-#pragma unroll
-    for (int i = 0; i < BS; ++i)
-#pragma unroll
-      for (int j = 0; j < BS; ++j) dS0[sbase + blk(i, j)] = G[i][j];
-  }
 }
 
-// dw[h, i] = <d_mix, o_i>: one workgroup per head, atomics across none
+// dw[h, i] = <d_mix, o_i> in two deterministic stages: per-head partial sums
+// over grid.y slices (grid (H, slices)), then their sum in a fixed order.
 template <typename Tg, typename Tout>
 __global__ void __launch_bounds__(kThreads)
-dmix_kernel(const Tg* d_mix, const Tout* o_swa, const Tout* o_dswa, const Tout* o_gdn, float* dw, long long ntok,
-            int H, int d) {
+dmix_partial(const Tg* d_mix, const Tout* o_swa, const Tout* o_dswa, const Tout* o_gdn, float* part, long long ntok,
+             int H, int d) {
   const int h = blockIdx.x;
   float s[3] = {0.f, 0.f, 0.f};
-  for (long long e = threadIdx.x; e < ntok * d; e += kThreads) {
+  for (long long e = (long long)blockIdx.y * kThreads + threadIdx.x; e < ntok * d;
+       e += (long long)gridDim.y * kThreads) {
     const size_t i = size_t(e / d) * H * d + size_t(h) * d + size_t(e % d);
     const float g = ld(d_mix, i);
     s[0] += g * ld(o_swa, i);
@@ -566,8 +672,17 @@ dmix_kernel(const Tg* d_mix, const Tout* o_swa, const Tout* o_dswa, const Tout* 
   if (threadIdx.x < 3) {
     float x = 0.f;
     for (int w = 0; w < kThreads / 64; ++w) x += red[threadIdx.x][w];
-    dw[3 * h + threadIdx.x] = x;
+    part[(size_t(h) * gridDim.y + blockIdx.y) * 3 + threadIdx.x] = x;
   }
+}
+
+__global__ void __launch_bounds__(64) dmix_final(const float* part, float* dw, int H, int nblk) {
+  const int i = blockIdx.x * 64 + threadIdx.x;
+  if (i >= 3 * H) return;
+  const int h = i / 3, j = i % 3;
+  float x = 0.f;
+  for (int k = 0; k < nblk; ++k) x += part[(size_t(h) * nblk + k) * 3 + j];
+  dw[i] = x;
 }
 
 template <typename Tin, typename Tg, int D>
@@ -576,15 +691,25 @@ hipError_t launch_bwd_t(const BwdArgs& x, hipStream_t st) {
   const int tiles = (p.P + kRows - 1) / kRows;
   const dim3 grid(unsigned(tiles * p.T), unsigned(p.H), unsigned(p.B));
   const Tg* g = static_cast<const Tg*>(x.d_mix);
-  hipLaunchKernelGGL((attn_bwd_stats<Tin, Tg, D>), grid, dim3(kThreads), 0, st, p, g, x.mix_w, x.lse2, x.dsum);
-  hipLaunchKernelGGL((attn_bwd_dq<Tin, Tg, D>), grid, dim3(kThreads), 0, st, p, g, x.mix_w, x.lse2, x.dsum, x.dq,
-                     x.scale);
-  hipLaunchKernelGGL((attn_bwd_dkdv<Tin, Tg, D>), grid, dim3(kThreads), 0, st, p, g, x.mix_w, x.lse2, x.dsum,
-                     x.dk, x.dv, x.scale);
+  if (x.attn_mfma) {
+    const hipError_t e = launch_attn_bwd_mfma(p, x.d_mix, x.o_swa, x.o_dswa, x.mix_w, x.lse2, x.dsum, x.dq, x.dk,
+                                              x.dv, x.scale, st);
+    if (e != hipSuccess) return e;
+  } else {
+    hipLaunchKernelGGL((attn_bwd_stats<Tin, Tg, D>), grid, dim3(kThreads), 0, st, p, g, x.mix_w, x.lse2, x.dsum);
+    hipLaunchKernelGGL((attn_bwd_dq<Tin, Tg, D>), grid, dim3(kThreads), 0, st, p, g, x.mix_w, x.lse2, x.dsum,
+                       x.dq, x.scale);
+    hipLaunchKernelGGL((attn_bwd_dkdv<Tin, Tg, D>), grid, dim3(kThreads), 0, st, p, g, x.mix_w, x.lse2, x.dsum,
+                       x.dk, x.dv, x.scale);
+  }
   const unsigned heads = unsigned(x.gdn.B * x.gdn.H);
-  hipLaunchKernelGGL((gdn_ckpt_kernel<Tin, D>), dim3(heads), dim3(kThreads), 0, st, x.gdn, x.C, x.ckpt);
-  hipLaunchKernelGGL((gdn_bwd_kernel<Tin, Tg, D>), dim3(heads), dim3(kThreads), 0, st, x.gdn, x.C, x.ckpt,
-                     x.chunk_buf, g, x.mix_w, x.dq, x.dk, x.dv, x.da, x.db, x.dS0);
+  const unsigned jobs = heads * unsigned(x.gdn.n_chunks);
+  hipLaunchKernelGGL((gdn_bwd_prep<Tin, Tg, D>), dim3(jobs, 3), dim3(kThreads), 0, st, x.gdn, x.C, g, x.mix_w, x.Am,
+                     x.Um, x.Xm);
+  hipLaunchKernelGGL((gdn_bwd_chain<D>), dim3(heads, D / kChainRows, 2), dim3(kThreads), 0, st, x.gdn.n_chunks,
+                     x.gdn.S0, x.Am, x.Um, x.Xm, x.Sst, x.Rin, x.dS0);
+  hipLaunchKernelGGL((gdn_bwd_tokens<Tin, Tg, D>), dim3(unsigned(x.n_slots)), dim3(kThreads), 0, st, x.gdn, x.C,
+                     x.Sst, x.Rin, x.slots, g, x.mix_w, x.dq, x.dk, x.dv, x.da, x.db);
   return hipGetLastError();
 }
 
@@ -607,16 +732,17 @@ hipError_t launch_bwd(const BwdArgs& x, int d, int in_dt, int out_dt, hipStream_
     e = launch_bwd_d<float, float>(x, d, st);
   if (e != hipSuccess) return e;
   const long long ntok = (long long)x.attn.B * x.gdn.L;
+  const dim3 pg(unsigned(x.attn.H), unsigned(x.dw_slices));
   if (out_dt == HLTA_BF16)
-    hipLaunchKernelGGL((dmix_kernel<bf16, bf16>), dim3(unsigned(x.attn.H)), dim3(kThreads), 0, st,
-                       static_cast<const bf16*>(x.d_mix), static_cast<const bf16*>(x.o_swa),
-                       static_cast<const bf16*>(x.o_dswa), static_cast<const bf16*>(x.o_gdn), x.dmix_w, ntok,
-                       x.attn.H, d);
+    hipLaunchKernelGGL((dmix_partial<bf16, bf16>), pg, dim3(kThreads), 0, st, static_cast<const bf16*>(x.d_mix),
+                       static_cast<const bf16*>(x.o_swa), static_cast<const bf16*>(x.o_dswa),
+                       static_cast<const bf16*>(x.o_gdn), x.dw_part, ntok, x.attn.H, d);
   else
-    hipLaunchKernelGGL((dmix_kernel<float, float>), dim3(unsigned(x.attn.H)), dim3(kThreads), 0, st,
-                       static_cast<const float*>(x.d_mix), static_cast<const float*>(x.o_swa),
-                       static_cast<const float*>(x.o_dswa), static_cast<const float*>(x.o_gdn), x.dmix_w, ntok,
-                       x.attn.H, d);
+    hipLaunchKernelGGL((dmix_partial<float, float>), pg, dim3(kThreads), 0, st, static_cast<const float*>(x.d_mix),
+                       static_cast<const float*>(x.o_swa), static_cast<const float*>(x.o_dswa),
+                       static_cast<const float*>(x.o_gdn), x.dw_part, ntok, x.attn.H, d);
+  hipLaunchKernelGGL(dmix_final, dim3(unsigned((3 * x.attn.H + 63) / 64)), dim3(64), 0, st, x.dw_part, x.dmix_w,
+                     x.attn.H, x.dw_slices);
   return hipGetLastError();
 }
 

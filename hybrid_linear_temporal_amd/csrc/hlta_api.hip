@@ -346,10 +346,15 @@ hlta_status hlta_bwd(const hlta_config* cfg, const void* q, const void* k, const
   x.dS0 = dS0;
   x.lse2 = reinterpret_cast<float*>(ws);
   x.dsum = reinterpret_cast<float*>(ws + bp.stats_bytes);
-  x.ckpt = reinterpret_cast<float*>(ws + bp.ckpt_off);
-  x.chunk_buf = reinterpret_cast<float*>(ws + bp.chunk_off);
+  float** mats[] = {&x.Am, &x.Um, &x.Xm, &x.Sst, &x.Rin};
+  for (int i = 0; i < 5; ++i) *mats[i] = reinterpret_cast<float*>(ws + bp.mat_off + i * bp.mat_bytes);
+  x.slots = reinterpret_cast<float*>(ws + bp.slot_off);
+  x.n_slots = bp.n_slots;
+  x.dw_part = reinterpret_cast<float*>(ws + bp.part_off);
+  x.dw_slices = kDwSlices;
   x.C = cfg->gdn_chunk;
   x.scale = plan.scale;
+  x.attn_mfma = plan.attn == Impl::Mfma && cfg->out_dtype == HLTA_BF16;
   hipError_t e = launch_bwd(x, cfg->d, cfg->in_dtype, cfg->out_dtype, st);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return HLTA_OK;

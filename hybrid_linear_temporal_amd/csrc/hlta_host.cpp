@@ -1,6 +1,7 @@
 // HIP-free host layer of the HLTA library: status strings, the thread-local
 // error message, config validation, kernel selection and workspace sizing.
 // Built into libhlta.so and, with g++, into a CPU test binary.
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <limits>
@@ -129,18 +130,17 @@ hlta_status make_bwd_plan(const hlta_config* cfg, BwdPlan* plan) {
   hlta_status s = check_config(cfg);
   if (s != HLTA_OK) return s;
   const int64_t L = int64_t(cfg->T) * cfg->P, C = cfg->gdn_chunk, nch = (L + C - 1) / C;
-  const int64_t dd = int64_t(cfg->d) * cfg->d;
-  int64_t rows = 0, ck = 0, cb = 0;
-  if (!mul_ok(int64_t(cfg->B) * cfg->H, L, &rows) || !mul_ok(int64_t(cfg->B) * cfg->H * nch, dd, &ck) ||
-      !mul_ok(int64_t(cfg->B) * cfg->H * C, dd, &cb))
-    return fail(HLTA_E_SHAPE, "workspace overflow");
+  const int64_t dd = int64_t(cfg->d) * cfg->d, bh = int64_t(cfg->B) * cfg->H;
+  int64_t rows = 0, mats = 0;
+  if (!mul_ok(bh, L, &rows) || !mul_ok(bh * nch, dd, &mats)) return fail(HLTA_E_SHAPE, "workspace overflow");
   BwdPlan p;
+  p.n_slots = int(std::min<int64_t>(std::max<int64_t>(bh * nch, 1), kBwdSlots));
   p.stats_bytes = align_up(size_t(rows) * 2 * sizeof(float), 256);
-  p.ckpt_off = 2 * p.stats_bytes;
-  p.ckpt_bytes = align_up(size_t(ck) * sizeof(float), 256);
-  p.chunk_off = p.ckpt_off + p.ckpt_bytes;
-  p.chunk_bytes = align_up(size_t(cb) * sizeof(float), 256);
-  p.total = p.chunk_off + p.chunk_bytes;
+  p.mat_off = 2 * p.stats_bytes;
+  p.mat_bytes = align_up(size_t(mats) * sizeof(float), 256);
+  p.slot_off = p.mat_off + 5 * p.mat_bytes;
+  p.part_off = p.slot_off + align_up(size_t(p.n_slots) * size_t(C) * size_t(dd) * sizeof(float), 256);
+  p.total = p.part_off + align_up(size_t(cfg->H) * kDwSlices * 3 * sizeof(float), 256);
   *plan = p;
   return HLTA_OK;
 }

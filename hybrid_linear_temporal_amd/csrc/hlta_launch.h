@@ -53,6 +53,13 @@ hipError_t launch_rope_ring(void* ring, int B, int R, long long first, int n, in
 hipError_t launch_ring_store_rollouts(const void* src, void* ring, int R, int B, long long frame_elems, int elem,
                                       const RolloutFrames& sel, hipStream_t st);
 
+// Softmax-branch backward with bf16 MFMA (bf16 q, k, v, d_mix and stored
+// outputs, d = 128, P >= 64): lse and dsum are [2, B, H, L] fp32 scratch;
+// dq, dk, dv [B, L, H, d] fp32 are written (not accumulated).
+hipError_t launch_attn_bwd_mfma(const AttnParams& p, const void* d_mix, const void* o_swa, const void* o_dswa,
+                                const float* mix_w, float* lse, float* dsum, float* dq, float* dk, float* dv,
+                                float scale, hipStream_t st);
+
 // Backward of the operator (bwd.hip): fp32 gradients of q, k, v [B, L, H, d],
 // a, b [B, L, H], mix_w [H, 3] and S0 [B, H, d, d] given d_mix (out dtype).
 // attn and gdn describe the forward (attn.scale_log2 set; gdn.n_chunks =
@@ -72,12 +79,20 @@ struct BwdArgs {
   float* db;
   float* dmix_w;
   float* dS0;        // or null
-  float* lse2;       // [2, B, L, H] workspace
-  float* dsum;       // [2, B, L, H] workspace
-  float* ckpt;       // [B*H, n_chunks, d, d] workspace
-  float* chunk_buf;  // [B*H, C, d, d] workspace
+  float* lse2;       // [2, B*L*H] workspace: softmax row statistics
+  float* dsum;       // [2, B*L*H] workspace
+  float* Am;         // [B*H, n_chunks, d, d] workspace: per-chunk transition of the memory
+  float* Um;         //   ... the chunk's own state from zero
+  float* Xm;         //   ... the chunk's own adjoint from zero
+  float* Sst;        //   ... state at the chunk's start
+  float* Rin;        //   ... adjoint reaching the chunk's end
+  float* slots;      // [n_slots, C, d, d] workspace: recomputed states, one slot per workgroup
+  int n_slots;
+  float* dw_part;    // [H, dw_slices, 3] workspace
+  int dw_slices;
   int C;
   float scale;
+  int attn_mfma;     // softmax branches on the bf16 MFMA kernels (bf16 in and out, d = 128, P >= 64)
 };
 hipError_t launch_bwd(const BwdArgs& x, int d, int in_dt, int out_dt, hipStream_t st);
 

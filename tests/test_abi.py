@@ -183,8 +183,10 @@ def test_rope_config_checks(lib):
 
 
 def test_bwd_workspace_and_argument_errors(lib):
-    """Backward: workspace = two [2, B, L, H] fp32 statistics, one d x d state
-    per chunk and per chunk token; argument errors fail before any launch."""
+    """Backward: workspace = two [2, B, L, H] fp32 statistics, five d x d
+    matrices per chunk, the states of one chunk per token-pass slot (at most
+    512 slots) and the mix-weight partial sums; argument errors fail before
+    any launch."""
     cfg = _cfg()
     L = cfg.T * cfg.P
     chunks = -(-L // cfg.gdn_chunk)
@@ -193,7 +195,8 @@ def test_bwd_workspace_and_argument_errors(lib):
         return -(-x // 256) * 256
 
     bh, dd = cfg.B * cfg.H, cfg.d * cfg.d * 4
-    want = 2 * up(bh * L * 2 * 4) + up(bh * chunks * dd) + up(bh * cfg.gdn_chunk * dd)
+    slots = min(bh * chunks, 512)
+    want = 2 * up(bh * L * 2 * 4) + 5 * up(bh * chunks * dd) + up(slots * cfg.gdn_chunk * dd) + up(cfg.H * 128 * 3 * 4)
     ws = H.hlta_bwd_workspace_bytes(cfg)
     assert ws == want
     assert H.hlta_bwd_workspace_bytes(_cfg(d=96)) == 0
