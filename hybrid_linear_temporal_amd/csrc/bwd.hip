@@ -292,20 +292,21 @@ attn_bwd_dkdv(AttnParams p, const Tg* d_mix, const float* mix_w, const float* ls
 // ---------------------------------------------------------------------------
 
 // Block layout: thread t owns rows 16-block t/16 and columns 16-block t%16 of
-// a d x d matrix, BS = d/16 each. Reductions: partial row (or column) sums of
-// the 16 threads sharing a block row (column) meet in LDS.
+// a d x d matrix, BS = d/16 each. Matrix-vector products: each thread writes
+// the partial sums of its block to LDS and, after one barrier, the 16 partials
+// of an entry are added in a fixed order; up to four products share a round.
+// Scalar sums: wave reduction, then the four wave partials from LDS.
 template <int D>
 struct GdnBlock {
   static constexpr int BS = D / 16;
-  float red[16][D];   // partial sums: [thread column-or-row group][index]
-  float vec[12][D];   // small vectors of the current token
-  float scal[16];     // scalars
+  float red[4][16][D];   // partial sums of up to four matrix-vector products
+  float vec[12][D];      // vectors of the current token
+  float wsum[8][8][4];   // wave partials of up to 8 sums, 8 slots
 };
 
-// y_i = sum_j M_ij x_j (rows == true) or y_j = sum_i M_ij x_i
+// partial sums of y = M x (kRows) or y = M^T x into red[slot]
 template <int D, bool kRows>
-__device__ __forceinline__ void reduce_mv(GdnBlock<D>& sm, const float (&M)[D / 16][D / 16], const float* x,
-                                          float* y) {
+__device__ __forceinline__ void mv_part(GdnBlock<D>& sm, const float (&M)[D / 16][D / 16], const float* x, int slot) {
   constexpr int BS = D / 16;
   const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
 #pragma unroll
@@ -313,63 +314,63 @@ __device__ __forceinline__ void reduce_mv(GdnBlock<D>& sm, const float (&M)[D / 
     float s = 0.f;
 #pragma unroll
     for (int bb = 0; bb < BS; ++bb) s += kRows ? M[a][bb] * x[tc * BS + bb] : M[bb][a] * x[tr * BS + bb];
-    if (kRows) sm.red[tc][tr * BS + a] = s;
-    else sm.red[tr][tc * BS + a] = s;
+    if (kRows) sm.red[slot][tc][tr * BS + a] = s;
+    else sm.red[slot][tr][tc * BS + a] = s;
   }
-  __syncthreads();
-  if (threadIdx.x < D) {
+}
+// vec[y[slot]] = f[slot] * (sum of the partials of slot), slots 0 .. n-1 (after a barrier)
+template <int D>
+__device__ __forceinline__ void mv_finish(GdnBlock<D>& sm, int n, const int (&y)[4], const float (&f)[4]) {
+  for (int e = threadIdx.x; e < n * D; e += kThreads) {
+    const int slot = e / D, i = e % D;
     float s = 0.f;
 #pragma unroll
-    for (int g = 0; g < 16; ++g) s += sm.red[g][threadIdx.x];
-    y[threadIdx.x] = s;
+    for (int g = 0; g < 16; ++g) s += sm.red[slot][g][i];
+    sm.vec[y[slot]][i] = s * f[slot];
+  }
+}
+
+// N sums of one value per thread; every thread gets the totals. Slot picks a
+// private LDS area (a slot is reused only after further barriers).
+template <int D, int N>
+__device__ __forceinline__ void sum_n(GdnBlock<D>& sm, float (&x)[N], int slot) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    float v = x[j];
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    x[j] = v;
+  }
+  if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) sm.wsum[slot][j][threadIdx.x >> 6] = x[j];
   }
   __syncthreads();
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] = sm.wsum[slot][j][0] + sm.wsum[slot][j][1] + sm.wsum[slot][j][2] + sm.wsum[slot][j][3];
 }
 
-// sum of one value per thread (result broadcast through sm.scal[slot])
-template <int D>
-__device__ __forceinline__ float reduce_all(GdnBlock<D>& sm, float x, int slot) {
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  if ((threadIdx.x & 63) == 0) sm.red[0][threadIdx.x >> 6] = x;
-  __syncthreads();
-  if (threadIdx.x == 0) sm.scal[slot] = sm.red[0][0] + sm.red[0][1] + sm.red[0][2] + sm.red[0][3];
-  __syncthreads();
-  return sm.scal[slot];
-}
-
-// dot product of two LDS vectors (all threads get it)
-template <int D>
-__device__ __forceinline__ float dot(GdnBlock<D>& sm, const float* x, const float* y, int slot) {
-  float s = 0.f;
-  for (int i = threadIdx.x; i < D; i += kThreads) s += x[i] * y[i];
-  return reduce_all(sm, s, slot);
-}
-
-// normalised copy of row x (length D, in LDS) into y; returns the norm n
-template <int D>
-__device__ __forceinline__ float normalise(GdnBlock<D>& sm, const float* x, float* y, int slot, bool on) {
-  const float n2 = dot(sm, x, x, slot);
-  const float n = on ? sqrtf(n2 + kL2Eps) : 1.f;
-  if (threadIdx.x < D) y[threadIdx.x] = x[threadIdx.x] / n;
-  __syncthreads();
-  return n;
-}
+__device__ __forceinline__ float l2n(float n2, bool on) { return on ? sqrtf(n2 + kL2Eps) : 1.f; }
 
 // One token of the memory on S (held in blocks): vec[0] = k and vec[1] = v
-// are in LDS; leaves k^ in vec[2] and u = S k^ in vec[3], and applies
-// S <- a (S - b u k^^T) (+ b v k^^T when with_v).
+// are in LDS (written before a barrier); applies S <- a (S - b u k^^T)
+// (+ b v k^^T when with_v) with k^ = k / n(k) and u = S k^ (S k and |k|^2 in
+// one round).
 template <int D>
 __device__ __forceinline__ void fwd_token(GdnBlock<D>& sm, float (&S)[D / 16][D / 16], float at, float bt, bool l2,
                                           bool with_v) {
   constexpr int BS = D / 16;
   const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
-  normalise(sm, sm.vec[0], sm.vec[2], 0, l2);
-  reduce_mv<D, true>(sm, S, sm.vec[2], sm.vec[3]);
+  mv_part<D, true>(sm, S, sm.vec[0], 0);
+  float n2[1] = {threadIdx.x < D ? sm.vec[0][threadIdx.x] * sm.vec[0][threadIdx.x] : 0.f};
+  sum_n<D, 1>(sm, n2, 0);   // its barrier also completes the partials
+  const float inv = 1.f / l2n(n2[0], l2);
+  mv_finish<D>(sm, 1, {3, 0, 0, 0}, {inv, 1.f, 1.f, 1.f});   // u = S k / n
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < BS; ++i)
 #pragma unroll
     for (int j = 0; j < BS; ++j) {
-      const float kj = sm.vec[2][tc * BS + j];
+      const float kj = sm.vec[0][tc * BS + j] * inv;
       const float vt = with_v ? bt * sm.vec[1][tr * BS + i] * kj : 0.f;
       S[i][j] = at * (S[i][j] - bt * sm.vec[3][tr * BS + i] * kj) + vt;
     }
@@ -423,41 +424,66 @@ gdn_bwd_prep(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float* Am,
   for (int i = 0; i < BS; ++i)
 #pragma unroll
     for (int j = 0; j < BS; ++j) M[i][j] = (what == 0 && tr * BS + i == tc * BS + j) ? 1.f : 0.f;
+  const size_t tok0 = (size_t(b) * p.L + t0) * HD + size_t(h) * D;
+  const size_t g0 = (size_t(b) * p.L + t0) * p.H + h;
+  const int e = threadIdx.x < D ? threadIdx.x : 0;
   if (what < 2) {
+    // the next token's vectors and gates are loaded while the current one computes
+    float xk = ld(k, tok0 + e), xv = ld(v, tok0 + e), xa = p.a[g0], xb = p.b[g0];
     for (int s = 0; s < n; ++s) {
-      const size_t tok = (size_t(b) * p.L + t0 + s) * HD + size_t(h) * D;
       if (threadIdx.x < D) {
-        sm.vec[0][threadIdx.x] = ld(k, tok + threadIdx.x);
-        sm.vec[1][threadIdx.x] = ld(v, tok + threadIdx.x);
+        sm.vec[0][threadIdx.x] = xk;
+        sm.vec[1][threadIdx.x] = xv;
       }
+      const float at = xa, bt = xb;
       __syncthreads();
-      const size_t g = (size_t(b) * p.L + t0 + s) * p.H + h;
-      fwd_token(sm, M, p.a[g], p.b[g], l2, what == 1);
+      if (s + 1 < n) {
+        xk = ld(k, tok0 + size_t(s + 1) * HD + e);
+        xv = ld(v, tok0 + size_t(s + 1) * HD + e);
+        xa = p.a[g0 + size_t(s + 1) * p.H];
+        xb = p.b[g0 + size_t(s + 1) * p.H];
+      }
+      fwd_token(sm, M, at, bt, l2, what == 1);
     }
   } else {
     const float w2 = mix_w[3 * h + 2];
+    size_t o = tok0 + size_t(n - 1) * HD + e;
+    float xk = ld(k, o), xd = w2 * ld(d_mix, o), xq = ld(q, o);
+    float xa = p.a[g0 + size_t(n - 1) * p.H], xb = p.b[g0 + size_t(n - 1) * p.H];
     for (int s = n - 1; s >= 0; --s) {
-      const size_t tok = (size_t(b) * p.L + t0 + s) * HD + size_t(h) * D;
       if (threadIdx.x < D) {
-        sm.vec[0][threadIdx.x] = ld(k, tok + threadIdx.x);
-        sm.vec[5][threadIdx.x] = w2 * ld(d_mix, tok + threadIdx.x);
-        sm.vec[6][threadIdx.x] = ld(q, tok + threadIdx.x);
+        sm.vec[0][threadIdx.x] = xk;
+        sm.vec[5][threadIdx.x] = xd;
+        sm.vec[6][threadIdx.x] = xq;
       }
+      const float at = xa, bt = xb;
       __syncthreads();
-      normalise(sm, sm.vec[0], sm.vec[2], 0, l2);
-      normalise(sm, sm.vec[6], sm.vec[4], 1, l2);
-      const size_t g = (size_t(b) * p.L + t0 + s) * p.H + h;
-      const float at = p.a[g], bt = p.b[g];
+      if (s > 0) {
+        o = tok0 + size_t(s - 1) * HD + e;
+        xk = ld(k, o), xd = w2 * ld(d_mix, o), xq = ld(q, o);
+        xa = p.a[g0 + size_t(s - 1) * p.H], xb = p.b[g0 + size_t(s - 1) * p.H];
+      }
+      float n2[2] = {0.f, 0.f};
+      if (threadIdx.x < D) {
+        n2[0] = sm.vec[0][threadIdx.x] * sm.vec[0][threadIdx.x];
+        n2[1] = sm.vec[6][threadIdx.x] * sm.vec[6][threadIdx.x];
+      }
+      sum_n<D, 2>(sm, n2, 0);
+      const float ik = 1.f / l2n(n2[0], l2), iq = 1.f / l2n(n2[1], l2);
       // M <- (M + do q^^T) M_t
 #pragma unroll
       for (int i = 0; i < BS; ++i)
 #pragma unroll
-        for (int j = 0; j < BS; ++j) M[i][j] += sm.vec[5][tr * BS + i] * sm.vec[4][tc * BS + j];
-      reduce_mv<D, true>(sm, M, sm.vec[2], sm.vec[8]);
+        for (int j = 0; j < BS; ++j) M[i][j] += sm.vec[5][tr * BS + i] * sm.vec[6][tc * BS + j] * iq;
+      mv_part<D, true>(sm, M, sm.vec[0], 0);
+      __syncthreads();
+      mv_finish<D>(sm, 1, {8, 0, 0, 0}, {ik, 1.f, 1.f, 1.f});   // M k^
+      __syncthreads();
 #pragma unroll
       for (int i = 0; i < BS; ++i)
 #pragma unroll
-        for (int j = 0; j < BS; ++j) M[i][j] = at * (M[i][j] - bt * sm.vec[8][tr * BS + i] * sm.vec[2][tc * BS + j]);
+        for (int j = 0; j < BS; ++j)
+          M[i][j] = at * (M[i][j] - bt * sm.vec[8][tr * BS + i] * sm.vec[0][tc * BS + j] * ik);
       __syncthreads();
     }
   }
@@ -470,8 +496,11 @@ gdn_bwd_prep(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float* Am,
 //   dir 0: S_start(0) = S0, S_start(c+1) = S_start(c) A_c + U_c
 //   dir 1: R(N-1) = 0,      R(c-1) = R(c) A_c^T + X_c, dS0 = R(-1)
 // R(c) is the adjoint reaching the end of chunk c from later tokens. A_c is
-// staged in LDS (padded rows) per step; a thread owns one row of the group
-// and CPT columns. grid (B*H, D/16, 2).
+// staged in LDS (rows padded by one float, so the row and the column walks
+// are both free of bank conflicts); a thread owns one row of the group and
+// CPT columns. The next step's A and U/X rows are loaded into registers while
+// the current step computes (the chain is latency-bound: one dependent
+// 16 x d by d x d product per chunk). grid (B*H, D/16, 2).
 constexpr int kChainRows = 16;
 template <int D>
 __global__ void __launch_bounds__(kThreads)
@@ -480,46 +509,67 @@ gdn_bwd_chain(int n_chunks, const float* S0, const float* Am, const float* Um, c
   __shared__ float As[D][D + 1];
   __shared__ float rows[kChainRows][D];
   constexpr int CPT = D * kChainRows / kThreads;   // columns per thread: 8 (d = 128), 4 (64), 2 (32)
+  constexpr int PER = D * D / 4 / kThreads;        // float4 of A per thread per step
   const int bh = blockIdx.x, r0 = blockIdx.y * kChainRows, dir = blockIdx.z;
   const int r = threadIdx.x / (D / CPT), j0 = (threadIdx.x % (D / CPT)) * CPT;
   const size_t mat = size_t(D) * D;
   const size_t base = size_t(bh) * n_chunks * mat;
+  const float* Bm = dir == 0 ? Um : Xm;
 #pragma unroll
   for (int jj = 0; jj < CPT; ++jj)
     rows[r][j0 + jj] = (dir == 0 && S0) ? S0[size_t(bh) * mat + size_t(r0 + r) * D + j0 + jj] : 0.f;
+  float4 na[PER];
+  float nb[CPT];
+  auto fetch = [&](int c) {
+    const float4* A4 = reinterpret_cast<const float4*>(Am + base + size_t(c) * mat);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) na[i] = A4[threadIdx.x + i * kThreads];
+    const float* add = Bm + base + size_t(c) * mat + size_t(r0 + r) * D + j0;
+#pragma unroll
+    for (int jj = 0; jj < CPT; ++jj) nb[jj] = add[jj];
+  };
+  fetch(dir == 0 ? 0 : n_chunks - 1);
   for (int step = 0; step < n_chunks; ++step) {
     const int c = dir == 0 ? step : n_chunks - 1 - step;
-    const float* A = Am + base + size_t(c) * mat;
-    __syncthreads();
-    for (int e = threadIdx.x; e < D * D / 4; e += kThreads) {
-      const float4 x = reinterpret_cast<const float4*>(A)[e];
-      const int i = (e * 4) / D, j = (e * 4) % D;
-      As[i][j] = x.x;
-      As[i][j + 1] = x.y;
-      As[i][j + 2] = x.z;
-      As[i][j + 3] = x.w;
+    __syncthreads();   // the previous step no longer reads As or rows
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = (threadIdx.x + i * kThreads) * 4;
+      const int ii = e / D, jc = e % D;
+      As[ii][jc] = na[i].x;
+      As[ii][jc + 1] = na[i].y;
+      As[ii][jc + 2] = na[i].z;
+      As[ii][jc + 3] = na[i].w;
     }
-    __syncthreads();
     float out[CPT];
+#pragma unroll
+    for (int jj = 0; jj < CPT; ++jj) out[jj] = nb[jj];
+    if (step + 1 < n_chunks) fetch(dir == 0 ? c + 1 : c - 1);
+    __syncthreads();
     float* rec = (dir == 0 ? Sst : Rin) + base + size_t(c) * mat + size_t(r0 + r) * D + j0;
 #pragma unroll
-    for (int jj = 0; jj < CPT; ++jj) {
-      rec[jj] = rows[r][j0 + jj];
-      out[jj] = 0.f;
-    }
-    for (int kk = 0; kk < D; ++kk) {
-      const float x = rows[r][kk];
+    for (int jj = 0; jj < CPT; ++jj) rec[jj] = rows[r][j0 + jj];
+    if (dir == 0) {
+#pragma unroll 8
+      for (int kk = 0; kk < D; ++kk) {
+        const float x = rows[r][kk];
 #pragma unroll
-      for (int jj = 0; jj < CPT; ++jj) out[jj] += x * (dir == 0 ? As[kk][j0 + jj] : As[j0 + jj][kk]);
-    }
-    const float* add = (dir == 0 ? Um : Xm) + base + size_t(c) * mat + size_t(r0 + r) * D + j0;
+        for (int jj = 0; jj < CPT; ++jj) out[jj] += x * As[kk][j0 + jj];
+      }
+    } else {
+#pragma unroll 8
+      for (int kk = 0; kk < D; ++kk) {
+        const float x = rows[r][kk];
 #pragma unroll
-    for (int jj = 0; jj < CPT; ++jj) out[jj] += add[jj];
+        for (int jj = 0; jj < CPT; ++jj) out[jj] += x * As[j0 + jj][kk];
+      }
+    }
     __syncthreads();
 #pragma unroll
     for (int jj = 0; jj < CPT; ++jj) rows[r][j0 + jj] = out[jj];
   }
   if (dir == 1 && dS0) {
+    __syncthreads();
 #pragma unroll
     for (int jj = 0; jj < CPT; ++jj) dS0[size_t(bh) * mat + size_t(r0 + r) * D + j0 + jj] = rows[r][j0 + jj];
   }
@@ -559,21 +609,37 @@ gdn_bwd_tokens(GdnParams p, int C, const float* Sst, const float* Rin, float* sl
     const int n = int(p.L - t0 < C ? p.L - t0 : C);
     float S[BS][BS], G[BS][BS];
     load_mat<D>(S, Sst + size_t(job) * mat);
+    // the next token's vectors and gates are loaded while the current one computes
+    const size_t tok0 = (size_t(b) * p.L + t0) * HD + size_t(h) * D;
+    const size_t g0 = (size_t(b) * p.L + t0) * p.H + h;
+    const int e = threadIdx.x < D ? threadIdx.x : 0;
+    float xk = ld(k, tok0 + e), xv = ld(v, tok0 + e), xa = p.a[g0], xb = p.b[g0];
     for (int s = 0; s < n; ++s) {
 #pragma unroll
       for (int i = 0; i < BS; ++i)
 #pragma unroll
         for (int j = 0; j < BS; ++j) cb[size_t(s) * mat + blk(i, j)] = S[i][j];
-      const size_t tok = (size_t(b) * p.L + t0 + s) * HD + size_t(h) * D;
       if (threadIdx.x < D) {
-        sm.vec[0][threadIdx.x] = ld(k, tok + threadIdx.x);
-        sm.vec[1][threadIdx.x] = ld(v, tok + threadIdx.x);
+        sm.vec[0][threadIdx.x] = xk;
+        sm.vec[1][threadIdx.x] = xv;
       }
+      const float at = xa, bt = xb;
       __syncthreads();
-      const size_t g = (size_t(b) * p.L + t0 + s) * p.H + h;
-      fwd_token(sm, S, p.a[g], p.b[g], l2, true);
+      if (s + 1 < n) {
+        xk = ld(k, tok0 + size_t(s + 1) * HD + e);
+        xv = ld(v, tok0 + size_t(s + 1) * HD + e);
+        xa = p.a[g0 + size_t(s + 1) * p.H];
+        xb = p.b[g0 + size_t(s + 1) * p.H];
+      }
+      fwd_token(sm, S, at, bt, l2, true);
     }
     load_mat<D>(G, Rin + size_t(job) * mat);
+    float xq = 0.f, xd = 0.f;
+    {
+      const size_t o = tok0 + size_t(n - 1) * HD + e;
+      xk = ld(k, o), xv = ld(v, o), xq = ld(q, o), xd = w2 * ld(d_mix, o);
+      xa = p.a[g0 + size_t(n - 1) * p.H], xb = p.b[g0 + size_t(n - 1) * p.H];
+    }
     for (int s = n - 1; s >= 0; --s) {
 #pragma unroll
       for (int i = 0; i < BS; ++i)
@@ -582,65 +648,85 @@ gdn_bwd_tokens(GdnParams p, int C, const float* Sst, const float* Rin, float* sl
       const long long t = t0 + s;
       const size_t tok = (size_t(b) * p.L + t) * HD + size_t(h) * D;
       const size_t g = (size_t(b) * p.L + t) * p.H + h;
-      const float at = p.a[g], bt = p.b[g];
-      // vec: 0 k, 1 v, 2 k^, 3 q, 4 q^, 5 do, 6 u, 7 S^T do, 8 G k^, 9 G^T v, 10 G^T u, 11 S^T G k^
+      const float at = xa, bt = xb;
+      // vec: 0 k, 1 v, 3 q, 5 do, 6 u = S k^, 7 S^T do, 8 G k^, 9 G^T v, 10 G^T u, 11 S^T G k^
+      // (k^ = k ik and q^ = q iq are formed on the fly)
       if (threadIdx.x < D) {
-        sm.vec[0][threadIdx.x] = ld(k, tok + threadIdx.x);
-        sm.vec[1][threadIdx.x] = ld(v, tok + threadIdx.x);
-        sm.vec[3][threadIdx.x] = ld(q, tok + threadIdx.x);
-        sm.vec[5][threadIdx.x] = w2 * ld(d_mix, tok + threadIdx.x);
+        sm.vec[0][threadIdx.x] = xk;
+        sm.vec[1][threadIdx.x] = xv;
+        sm.vec[3][threadIdx.x] = xq;
+        sm.vec[5][threadIdx.x] = xd;
       }
       __syncthreads();
-      const float nk = normalise(sm, sm.vec[0], sm.vec[2], 0, l2);
-      const float nq = normalise(sm, sm.vec[3], sm.vec[4], 1, l2);
+      if (s > 0) {
+        const size_t o = tok0 + size_t(s - 1) * HD + e;
+        xk = ld(k, o), xv = ld(v, o), xq = ld(q, o), xd = w2 * ld(d_mix, o);
+        xa = p.a[g0 + size_t(s - 1) * p.H], xb = p.b[g0 + size_t(s - 1) * p.H];
+      }
+      float n2[2] = {0.f, 0.f};
+      if (threadIdx.x < D) {
+        n2[0] = sm.vec[0][threadIdx.x] * sm.vec[0][threadIdx.x];
+        n2[1] = sm.vec[3][threadIdx.x] * sm.vec[3][threadIdx.x];
+      }
+      sum_n<D, 2>(sm, n2, 0);
+      const float ik = 1.f / l2n(n2[0], l2), iq = 1.f / l2n(n2[1], l2);
 #pragma unroll
       for (int i = 0; i < BS; ++i)
 #pragma unroll
-        for (int j = 0; j < BS; ++j) G[i][j] += sm.vec[5][tr * BS + i] * sm.vec[4][tc * BS + j];
-      reduce_mv<D, true>(sm, S, sm.vec[2], sm.vec[6]);    // u
-      reduce_mv<D, false>(sm, S, sm.vec[5], sm.vec[7]);   // S^T do
-      reduce_mv<D, true>(sm, G, sm.vec[2], sm.vec[8]);    // G k^
-      reduce_mv<D, false>(sm, G, sm.vec[1], sm.vec[9]);   // G^T v
-      reduce_mv<D, false>(sm, G, sm.vec[6], sm.vec[10]);  // G^T u
-      reduce_mv<D, false>(sm, S, sm.vec[8], sm.vec[11]);  // S^T G k^
-      float gs = 0.f;
+        for (int j = 0; j < BS; ++j) G[i][j] += sm.vec[5][tr * BS + i] * sm.vec[3][tc * BS + j] * iq;
+      mv_part<D, true>(sm, S, sm.vec[0], 0);    // S k
+      mv_part<D, false>(sm, S, sm.vec[5], 1);   // S^T do
+      mv_part<D, true>(sm, G, sm.vec[0], 2);    // G k
+      mv_part<D, false>(sm, G, sm.vec[1], 3);   // G^T v
+      __syncthreads();
+      mv_finish<D>(sm, 4, {6, 7, 8, 9}, {ik, 1.f, ik, 1.f});
+      __syncthreads();
+      mv_part<D, false>(sm, G, sm.vec[6], 0);   // G^T u
+      mv_part<D, false>(sm, S, sm.vec[8], 1);   // S^T G k^
+      float sc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};  // <G, S>, u.do, v.do, u.Gk^, v.Gk^
 #pragma unroll
       for (int i = 0; i < BS; ++i)
 #pragma unroll
-        for (int j = 0; j < BS; ++j) gs += G[i][j] * S[i][j];
-      const float GS = reduce_all(sm, gs, 2);
-      const float udo = dot(sm, sm.vec[6], sm.vec[5], 3);
-      const float vdo = dot(sm, sm.vec[1], sm.vec[5], 4);
-      const float uGk = dot(sm, sm.vec[6], sm.vec[8], 5);
-      const float vGk = dot(sm, sm.vec[1], sm.vec[8], 6);
+        for (int j = 0; j < BS; ++j) sc[0] += G[i][j] * S[i][j];
+      if (threadIdx.x < D) {
+        const int i = threadIdx.x;
+        sc[1] = sm.vec[6][i] * sm.vec[5][i];
+        sc[2] = sm.vec[1][i] * sm.vec[5][i];
+        sc[3] = sm.vec[6][i] * sm.vec[8][i];
+        sc[4] = sm.vec[1][i] * sm.vec[8][i];
+      }
+      sum_n<D, 5>(sm, sc, 1);   // its barrier also completes the second round's partials
+      mv_finish<D>(sm, 2, {10, 11, 0, 0}, {1.f, 1.f, 1.f, 1.f});
+      __syncthreads();
+      const float GS = sc[0], udo = sc[1], vdo = sc[2], uGk = sc[3], vGk = sc[4];
       if (threadIdx.x == 0) {
         da[g] = GS - bt * uGk;
         db[g] = vGk - at * uGk;
       }
+      float dqh = 0.f, dkh = 0.f, qi = 0.f, ki = 0.f;
+      float d2[2] = {0.f, 0.f};
       if (threadIdx.x < D) {
         const int i = threadIdx.x;
-        const float kh = sm.vec[2][i];
-        const float dqh = at * (sm.vec[7][i] - bt * kh * udo) + bt * kh * vdo;
-        const float dkh = bt * sm.vec[9][i] - at * bt * (sm.vec[11][i] + sm.vec[10][i]);
-        sm.vec[7][i] = dqh;
-        sm.vec[9][i] = dkh;
+        ki = sm.vec[0][i];
+        qi = sm.vec[3][i];
+        const float kh = ki * ik;
+        dqh = at * (sm.vec[7][i] - bt * kh * udo) + bt * kh * vdo;
+        dkh = bt * sm.vec[9][i] - at * bt * (sm.vec[11][i] + sm.vec[10][i]);
         dv[tok + i] += bt * sm.vec[8][i];
+        d2[0] = qi * dqh;
+        d2[1] = ki * dkh;
       }
-      __syncthreads();
-      const float qdq = dot(sm, sm.vec[3], sm.vec[7], 7);
-      const float kdk = dot(sm, sm.vec[0], sm.vec[9], 8);
+      sum_n<D, 2>(sm, d2, 2);
       if (threadIdx.x < D) {
         const int i = threadIdx.x;
-        const float gq = l2 ? sm.vec[7][i] / nq - sm.vec[3][i] * qdq / (nq * nq * nq) : sm.vec[7][i];
-        const float gk = l2 ? sm.vec[9][i] / nk - sm.vec[0][i] * kdk / (nk * nk * nk) : sm.vec[9][i];
-        dq[tok + i] += gq;
-        dk[tok + i] += gk;
+        dq[tok + i] += l2 ? dqh * iq - qi * d2[0] * iq * iq * iq : dqh;
+        dk[tok + i] += l2 ? dkh * ik - ki * d2[1] * ik * ik * ik : dkh;
       }
 #pragma unroll
       for (int i = 0; i < BS; ++i)
 #pragma unroll
         for (int j = 0; j < BS; ++j)
-          G[i][j] = at * (G[i][j] - bt * sm.vec[8][tr * BS + i] * sm.vec[2][tc * BS + j]);
+          G[i][j] = at * (G[i][j] - bt * sm.vec[8][tr * BS + i] * sm.vec[0][tc * BS + j] * ik);
       __syncthreads();
     }
   }
