@@ -8,7 +8,9 @@ mix) over one synthetic clip that is already resident in HBM. Prints one JSON
 line: tokens/s over the timed steps, the roofline of the dominant kernel (the
 softmax-branch kernel, priced against the bf16 MFMA peak) measured with HIP
 events on the stream the library launches on, and the float64 CPU oracle timed
-on a bounded sample of the same workload.
+on a bounded sample of the same workload. Extra legs (reported beside, never in
+`value`): the FP8 softmax branches, the rotary embedding, the backward
+(hlta_bwd) and the streaming frame step.
 """
 from __future__ import annotations
 
@@ -393,7 +395,8 @@ def main():
     gdn_gbs = gdn_bytes / (gdn_ms * 1e-3) / 1e9
     mfma = cfg.impl != H.HLTA_IMPL_GENERIC and wl.dtype == "bf16" and wl.d == 128
     attn_src = "attn_mfma.hip" if mfma else "attn_generic.hip"
-    traffic = read_traffic(f"traffic_{attn_src.split('.')[0]}_{wl.name}.txt", source_digest(attn_src))
+    srcs = (attn_src, "attn_mfma_tiles.h") if mfma else (attn_src,)
+    traffic = read_traffic(f"traffic_{attn_src.split('.')[0]}_{wl.name}.txt", source_digest(*srcs))
     res = {
         "metric": METRIC, "value": tokens * args.steps / elapsed, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,

@@ -39,7 +39,19 @@ def summarise(path: str) -> str:
                                ("14rope_qk_kernelIDF16b", "rope_qk_kernel<bf16>"),
                                ("14rope_qk_kernelIf", "rope_qk_kernel<float>"),
                                ("16rope_ring_kernelIDF16b", "rope_ring_kernel<bf16>"),
-                               ("16rope_ring_kernelIf", "rope_ring_kernel<float>")):
+                               ("16rope_ring_kernelIf", "rope_ring_kernel<float>"),
+                               ("16attn_bwd_dq_mfmaE", "attn_bwd_dq_mfma"),
+                               ("18attn_bwd_dkdv_mfmaE", "attn_bwd_dkdv_mfma"),
+                               ("17attn_bwd_lse_mfmaE", "attn_bwd_lse_mfma"),
+                               ("13attn_bwd_dsumE", "attn_bwd_dsum"),
+                               ("14attn_bwd_statsI", "attn_bwd_stats (fp32)"),
+                               ("11attn_bwd_dqI", "attn_bwd_dq (fp32)"),
+                               ("13attn_bwd_dkdvI", "attn_bwd_dkdv (fp32)"),
+                               ("12gdn_bwd_prepI", "gdn_bwd_prep"),
+                               ("13gdn_bwd_chainI", "gdn_bwd_chain"),
+                               ("14gdn_bwd_tokensI", "gdn_bwd_tokens"),
+                               ("12dmix_partialI", "dmix_partial"),
+                               ("10dmix_finalE", "dmix_final")):
             if mangled in short:
                 short = plain
                 break
