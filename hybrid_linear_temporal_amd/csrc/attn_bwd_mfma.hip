@@ -317,10 +317,29 @@ attn_bwd_dq_mfma(AttnParams p, const bf16* g, const float* mix_w, const float* l
 // dk, dv, key-major: the wave's 32 key rows stay in registers; the query rows
 // (and d_mix rows) of the frames that read this key frame stream through LDS
 // ---------------------------------------------------------------------------
+// token index (in the batch row) of query j of the tile at the stream's position
+__device__ __forceinline__ long long tile_token(const KeyStream<false>& qs, int step, int j) {
+  const int split = qs.P - qs.pk;
+  return j < split ? qs.g * qs.P + qs.pk + j : (qs.g + step) * qs.P + (j - split);
+}
+
+// the 64 statistics (lse and D) of a tile's query rows, global -> LDS by
+// direct 4-byte loads (wave 0: lse, wave 1: D); rows past the end re-read the
+// last valid row
+__device__ __forceinline__ void issue_stats(float* Ld, float* Dd, const KeyStream<false>& qs, int step, int qleft,
+                                            const float* lse_b, const float* ds_b, int wave, int lane) {
+  if (wave > 1) return;
+  const int j = lane < qleft ? lane : qleft - 1;
+  const float* src = (wave == 0 ? lse_b : ds_b) + tile_token(qs, step, j);
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
+                                   (__attribute__((address_space(3))) void*)(wave == 0 ? Ld : Dd), 4, 0, 0);
+}
+
 __global__ void __launch_bounds__(NT, 1)
 attn_bwd_dkdv_mfma(AttnParams p, const bf16* g, const float* mix_w, const float* lse, const float* dsum, float* dk,
                    float* dv, float scale) {
   __shared__ Tile sQ0, sG0, sQ1, sG1;
+  __shared__ __attribute__((aligned(16))) float sL0[KT], sD0[KT], sL1[KT], sD1[KT];
   const int tid = threadIdx.x;
   const int wave = uni(tid >> 6), lane = tid & 63, hl = lane >> 5, l32 = lane & 31, l16 = lane & 15;
   Item it;
@@ -370,20 +389,21 @@ attn_bwd_dkdv_mfma(AttnParams p, const bf16* g, const float* mix_w, const float*
       const long long left = nq - (long long)t * KT;
       return int(left < KT ? (left > 0 ? left : 0) : KT);
     };
-    if (ntiles > 0) issue_tile(sQ0, sG0, qs, qleft_of(0), off, HD, wave, lane);
-    auto tile = [&](int t, const Tile& Qt, const Tile& Gt, Tile& Qn, Tile& Gn) __attribute__((always_inline)) {
-      // token index (in the row) of tile query j: frame qs.g from row qs.pk, then the next frame
-      const long long t0 = qs.g * p.P + qs.pk;
-      const long long t1 = (qs.g + step) * p.P - (p.P - qs.pk);
-      const int split = p.P - qs.pk;
-      const int qleft = qleft_of(t);
+    if (ntiles > 0) {
+      issue_tile(sQ0, sG0, qs, qleft_of(0), off, HD, wave, lane);
+      issue_stats(sL0, sD0, qs, step, qleft_of(0), lse_b, ds_b, wave, lane);
+    }
+    auto tile = [&](int t, const Tile& Qt, const Tile& Gt, const float* Lt, const float* Dt, Tile& Qn, Tile& Gn,
+                    float* Ln, float* Dn) __attribute__((always_inline)) {
       wait_vmem();
       __syncthreads();
       if (t + 1 < ntiles) {
         qs.advance();
         issue_tile(Qn, Gn, qs, qleft_of(t + 1), off, HD, wave, lane);
+        issue_stats(Ln, Dn, qs, step, qleft_of(t + 1), lse_b, ds_b, wave, lane);
       }
       if (wave_active) {
+        const int qthr = uni(qleft_of(t)) - 4 * hl;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           f32x16 x, dp;
@@ -396,16 +416,19 @@ attn_bwd_dkdv_mfma(AttnParams p, const bf16* g, const float* mix_w, const float*
           }
           bf16x8 pw[2], dsb[2];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = qb * 32 + (r >> 2) * 8 + 4 * hl + (r & 3);
-            float pr = 0.f, ds = 0.f;
-            if (j < qleft) {
-              const long long tok = j < split ? t0 + j : t1 + j;
-              pr = __builtin_amdgcn_exp2f(fmaf(x[r], c, -lse_b[tok]));
-              ds = pr * fmaf(w, dp[r], -ds_b[tok]);
+          for (int r4 = 0; r4 < 4; ++r4) {
+            // queries qb*32 + 8 r4 + 4 hl + 0..3: their statistics as one 16-byte read each
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lt + qb * 32 + 8 * r4 + 4 * hl);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dt + qb * 32 + 8 * r4 + 4 * hl);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * r4 + e;
+              float pr = __builtin_amdgcn_exp2f(fmaf(x[r], c, -l4[e]));
+              if (qb * 32 + 8 * r4 + e >= qthr) pr = 0.f;
+              const float ds = pr * fmaf(w, dp[r], -d4[e]);
+              pw[r >> 3][r & 7] = static_cast<bf16>(w * pr);
+              dsb[r >> 3][r & 7] = static_cast<bf16>(ds);
             }
-            pw[r >> 3][r & 7] = static_cast<bf16>(w * pr);
-            dsb[r >> 3][r & 7] = static_cast<bf16>(ds);
           }
 #pragma unroll
           for (int db = 0; db < 4; ++db)
@@ -420,8 +443,8 @@ attn_bwd_dkdv_mfma(AttnParams p, const bf16* g, const float* mix_w, const float*
       }
     };
     for (int t = 0; t < ntiles; t += 2) {
-      tile(t, sQ0, sG0, sQ1, sG1);
-      if (t + 1 < ntiles) tile(t + 1, sQ1, sG1, sQ0, sG0);
+      tile(t, sQ0, sG0, sL0, sD0, sQ1, sG1, sL1, sD1);
+      if (t + 1 < ntiles) tile(t + 1, sQ1, sG1, sL1, sD1, sQ0, sG0, sL0, sD0);
     }
   }
   if (kok) {
