@@ -151,3 +151,57 @@ def test_full_size_rope_and_fp8_sampled():
                 err = O.rel_l2(to64(out[name][b, sl, h]), ref)
                 print(f"fp8 (b={b}, h={h}) frame {f} {name} {err:.2e}", flush=True)
                 assert err <= 3e-2, (b, h, f, name, err)
+
+
+def test_full_size_backward_one_head():
+    """hlta_bwd at 480P / 31 frames (all 24 heads, the launch configuration
+    bench.py times) against the float64 oracle's gradients of one whole head:
+    its dq, dk, dv over all 48360 tokens (sums of the three branches), its gate
+    gradients, its start-state gradient, and its mix-weight gradient (B = 1, so
+    dw[h] is a sum over this head alone). Bar: relative L2 1e-2 (bf16 inputs
+    and outputs; the softmax branches round P and dS to bf16 for their products)."""
+    wl = I.P480_T31
+    print(f"generating {wl.name} and its upstream gradient", flush=True)
+    x = I.make_clip(wl, threads=16)
+    g = I.upstream_grad(wl, "bf16")
+    dev = H.to_device(x, wl.dtype)
+    cfg = H.make_config(wl)
+    S0 = (0.1 * np.random.default_rng(wl.seed).standard_normal((wl.B, wl.H, wl.d, wl.d))).astype(np.float32)
+    S0_t = torch.from_numpy(S0).cuda()
+    fwd = H.hlta_fwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], S0=S0_t)
+    g_t = torch.from_numpy(g).cuda().to(torch.bfloat16)
+    got = H.hlta_bwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], fwd, g_t, S0=S0_t)
+    torch.cuda.synchronize()
+    print("GPU backward done; oracle on one head", flush=True)
+    b, h = 0, 7
+    q, k, v = x["q"][b, :, h], x["k"][b, :, h], x["v"][b, :, h]
+    a, bb = x["a"][b, :, h], x["b"][b, :, h]
+    gh = g[b, :, h].astype(np.float64)
+    w3 = x["w"][h].astype(np.float64)
+    P, T = wl.P, wl.T
+    dq = np.zeros(q.shape)
+    dk = np.zeros(q.shape)
+    dv = np.zeros(q.shape)
+    frame_sets = ((w3[0], lambda f: O.swa_frames(f, wl.swa_frames)),
+                  (w3[1], lambda f: O.dswa_frames(f, wl.dswa_dilation, wl.dswa_taps)))
+    for wi, fo in frame_sets:
+        gq, gk, gv = O.attention_backward(q, k, v, wi * gh, T, P, fo)
+        dq += gq
+        dk += gk
+        dv += gv
+    gq, gk, gv, ga, gb, gS = O.gdn_recurrent_backward(q, k, v, a, bb, w3[2] * gh, S0[b, h])
+    dq += gq
+    dk += gk
+    dv += gv
+    o_swa = O.swa(q, k, v, T, P, wl.swa_frames)
+    o_dswa = O.dswa(q, k, v, T, P, wl.dswa_dilation, wl.dswa_taps)
+    o_gdn, _ = O.gdn_recurrent(q, k, v, a, bb, S0[b, h])
+    dw = np.array([np.sum(gh * o_swa), np.sum(gh * o_dswa), np.sum(gh * o_gdn)])
+    checks = (("dq", to64(got["dq"][b, :, h]), dq), ("dk", to64(got["dk"][b, :, h]), dk),
+              ("dv", to64(got["dv"][b, :, h]), dv), ("da", to64(got["da"][b, :, h]), ga),
+              ("db", to64(got["db"][b, :, h]), gb), ("dS0", to64(got["dS0"][b, h]), gS),
+              ("dmix_w", to64(got["dmix_w"][h]), dw))
+    for name, gv_, rv in checks:
+        err = O.rel_l2(gv_, rv)
+        print(f"{wl.name} backward (b={b}, h={h}) {name} {err:.2e}", flush=True)
+        assert err <= TOL["bf16"], f"{name}: {err:.3e}"
