@@ -405,7 +405,8 @@ __device__ __forceinline__ void store_mat(float* dst, const float (&M)[D / 16][D
 // grid (B*H*n_chunks, 3); one matrix per workgroup.
 template <typename Tin, typename Tg, int D>
 __global__ void __launch_bounds__(kThreads)
-gdn_bwd_prep(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float* Am, float* Um, float* Xm) {
+gdn_bwd_prep(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float* Am, float* AmT, float* Um,
+             float* Xm) {
   constexpr int BS = D / 16;
   __shared__ GdnBlock<D> sm;
   const int what = blockIdx.y;
@@ -489,39 +490,51 @@ gdn_bwd_prep(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float* Am,
   }
   float* dst = what == 0 ? Am : (what == 1 ? Um : Xm);
   store_mat<D>(dst + size_t(job) * D * D, M);
+  if (what == 0) {   // A^T too, so both chains run the same row-times-matrix product
+    const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
+    float* t = AmT + size_t(job) * D * D;
+#pragma unroll
+    for (int j = 0; j < BS; ++j)
+#pragma unroll
+      for (int i = 0; i < BS; ++i) t[size_t(tc * BS + j) * D + tr * BS + i] = M[i][j];
+  }
 }
 
 // The two chains over chunks, rows of the state split over workgroups (rows
 // evolve independently: row i of S A + U only needs row i of S and U):
 //   dir 0: S_start(0) = S0, S_start(c+1) = S_start(c) A_c + U_c
 //   dir 1: R(N-1) = 0,      R(c-1) = R(c) A_c^T + X_c, dS0 = R(-1)
-// R(c) is the adjoint reaching the end of chunk c from later tokens. A_c is
-// staged in LDS (rows padded by one float, so the row and the column walks
-// are both free of bank conflicts); a thread owns one row of the group and
-// CPT columns. The next step's A and U/X rows are loaded into registers while
-// the current step computes (the chain is latency-bound: one dependent
-// 16 x d by d x d product per chunk). grid (B*H, D/16, 2).
+// R(c) is the adjoint reaching the end of chunk c from later tokens. The
+// matrix (A_c, or A_c^T as the prep stored it) is staged in LDS rows padded
+// to keep 16-byte alignment; a thread owns one row of the group and CPT
+// consecutive columns, read as float4s, and the row itself is read four
+// values at a time. The next step's matrix and U/X rows are loaded into
+// registers while the current step computes (the chain is latency-bound: one
+// dependent 16 x d by d x d product per chunk). grid (B*H, D/16, 2).
 constexpr int kChainRows = 16;
+typedef float v4f __attribute__((ext_vector_type(4)));
 template <int D>
 __global__ void __launch_bounds__(kThreads)
-gdn_bwd_chain(int n_chunks, const float* S0, const float* Am, const float* Um, const float* Xm, float* Sst,
-              float* Rin, float* dS0) {
-  __shared__ float As[D][D + 1];
-  __shared__ float rows[kChainRows][D];
+gdn_bwd_chain(int n_chunks, const float* S0, const float* Am, const float* AmT, const float* Um, const float* Xm,
+              float* Sst, float* Rin, float* dS0) {
+  constexpr int DP = D + 4;                        // padded row (floats), keeps float4 alignment
+  __shared__ __attribute__((aligned(16))) float As[D * DP];
+  __shared__ __attribute__((aligned(16))) float rows[kChainRows][D];
   constexpr int CPT = D * kChainRows / kThreads;   // columns per thread: 8 (d = 128), 4 (64), 2 (32)
-  constexpr int PER = D * D / 4 / kThreads;        // float4 of A per thread per step
+  constexpr int PER = D * D / 4 / kThreads;        // float4 of the matrix per thread per step
   const int bh = blockIdx.x, r0 = blockIdx.y * kChainRows, dir = blockIdx.z;
   const int r = threadIdx.x / (D / CPT), j0 = (threadIdx.x % (D / CPT)) * CPT;
   const size_t mat = size_t(D) * D;
   const size_t base = size_t(bh) * n_chunks * mat;
+  const float* Mm = dir == 0 ? Am : AmT;
   const float* Bm = dir == 0 ? Um : Xm;
 #pragma unroll
   for (int jj = 0; jj < CPT; ++jj)
     rows[r][j0 + jj] = (dir == 0 && S0) ? S0[size_t(bh) * mat + size_t(r0 + r) * D + j0 + jj] : 0.f;
-  float4 na[PER];
+  v4f na[PER];
   float nb[CPT];
-  auto fetch = [&](int c) {
-    const float4* A4 = reinterpret_cast<const float4*>(Am + base + size_t(c) * mat);
+  auto fetch = [&](int c) __attribute__((always_inline)) {
+    const v4f* A4 = reinterpret_cast<const v4f*>(Mm + base + size_t(c) * mat);
 #pragma unroll
     for (int i = 0; i < PER; ++i) na[i] = A4[threadIdx.x + i * kThreads];
     const float* add = Bm + base + size_t(c) * mat + size_t(r0 + r) * D + j0;
@@ -535,41 +548,47 @@ gdn_bwd_chain(int n_chunks, const float* S0, const float* Am, const float* Um, c
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = (threadIdx.x + i * kThreads) * 4;
-      const int ii = e / D, jc = e % D;
-      As[ii][jc] = na[i].x;
-      As[ii][jc + 1] = na[i].y;
-      As[ii][jc + 2] = na[i].z;
-      As[ii][jc + 3] = na[i].w;
+      *reinterpret_cast<v4f*>(&As[(e / D) * DP + e % D]) = na[i];
     }
     float out[CPT];
 #pragma unroll
     for (int jj = 0; jj < CPT; ++jj) out[jj] = nb[jj];
-    if (step + 1 < n_chunks) fetch(dir == 0 ? c + 1 : c - 1);
+    // unconditional (the last step re-reads its own chunk) so the prefetch buffer stays in registers
+    fetch(dir == 0 ? (c + 1 < n_chunks ? c + 1 : c) : (c > 0 ? c - 1 : 0));
     __syncthreads();
     float* rec = (dir == 0 ? Sst : Rin) + base + size_t(c) * mat + size_t(r0 + r) * D + j0;
 #pragma unroll
     for (int jj = 0; jj < CPT; ++jj) rec[jj] = rows[r][j0 + jj];
-    if (dir == 0) {
-#pragma unroll 8
-      for (int kk = 0; kk < D; ++kk) {
-        const float x = rows[r][kk];
+    // out += x * (row k of the matrix), CPT consecutive columns from j0
+    auto axpy = [&](float x, int k) __attribute__((always_inline)) {
+      const float* arow = &As[k * DP + j0];
+      if constexpr (CPT >= 4) {
 #pragma unroll
-        for (int jj = 0; jj < CPT; ++jj) out[jj] += x * As[kk][j0 + jj];
-      }
-    } else {
-#pragma unroll 8
-      for (int kk = 0; kk < D; ++kk) {
-        const float x = rows[r][kk];
+        for (int j4 = 0; j4 < CPT; j4 += 4) {
+          const v4f a4 = *reinterpret_cast<const v4f*>(arow + j4);
+          out[j4] += x * a4.x;
+          out[j4 + 1] += x * a4.y;
+          out[j4 + 2] += x * a4.z;
+          out[j4 + 3] += x * a4.w;
+        }
+      } else {
 #pragma unroll
-        for (int jj = 0; jj < CPT; ++jj) out[jj] += x * As[j0 + jj][kk];
+        for (int jj = 0; jj < CPT; ++jj) out[jj] += x * arow[jj];
       }
+    };
+#pragma unroll 4
+    for (int k4 = 0; k4 < D; k4 += 4) {
+      const v4f x = *reinterpret_cast<const v4f*>(&rows[r][k4]);
+      axpy(x.x, k4);
+      axpy(x.y, k4 + 1);
+      axpy(x.z, k4 + 2);
+      axpy(x.w, k4 + 3);
     }
     __syncthreads();
 #pragma unroll
     for (int jj = 0; jj < CPT; ++jj) rows[r][j0 + jj] = out[jj];
   }
   if (dir == 1 && dS0) {
-    __syncthreads();
 #pragma unroll
     for (int jj = 0; jj < CPT; ++jj) dS0[size_t(bh) * mat + size_t(r0 + r) * D + j0 + jj] = rows[r][j0 + jj];
   }
@@ -791,9 +810,9 @@ hipError_t launch_bwd_t(const BwdArgs& x, hipStream_t st) {
   const unsigned heads = unsigned(x.gdn.B * x.gdn.H);
   const unsigned jobs = heads * unsigned(x.gdn.n_chunks);
   hipLaunchKernelGGL((gdn_bwd_prep<Tin, Tg, D>), dim3(jobs, 3), dim3(kThreads), 0, st, x.gdn, x.C, g, x.mix_w, x.Am,
-                     x.Um, x.Xm);
+                     x.AmT, x.Um, x.Xm);
   hipLaunchKernelGGL((gdn_bwd_chain<D>), dim3(heads, D / kChainRows, 2), dim3(kThreads), 0, st, x.gdn.n_chunks,
-                     x.gdn.S0, x.Am, x.Um, x.Xm, x.Sst, x.Rin, x.dS0);
+                     x.gdn.S0, x.Am, x.AmT, x.Um, x.Xm, x.Sst, x.Rin, x.dS0);
   hipLaunchKernelGGL((gdn_bwd_tokens<Tin, Tg, D>), dim3(unsigned(x.n_slots)), dim3(kThreads), 0, st, x.gdn, x.C,
                      x.Sst, x.Rin, x.slots, g, x.mix_w, x.dq, x.dk, x.dv, x.da, x.db);
   return hipGetLastError();

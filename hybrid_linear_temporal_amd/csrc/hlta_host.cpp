@@ -138,7 +138,7 @@ hlta_status make_bwd_plan(const hlta_config* cfg, BwdPlan* plan) {
   p.stats_bytes = align_up(size_t(rows) * 2 * sizeof(float), 256);
   p.mat_off = 2 * p.stats_bytes;
   p.mat_bytes = align_up(size_t(mats) * sizeof(float), 256);
-  p.slot_off = p.mat_off + 5 * p.mat_bytes;
+  p.slot_off = p.mat_off + 6 * p.mat_bytes;
   p.part_off = p.slot_off + align_up(size_t(p.n_slots) * size_t(C) * size_t(dd) * sizeof(float), 256);
   p.total = p.part_off + align_up(size_t(cfg->H) * kDwSlices * 3 * sizeof(float), 256);
   *plan = p;

@@ -37,16 +37,16 @@ hlta_status check_config(const hlta_config* cfg);
 hlta_status make_plan(const hlta_config* cfg, int64_t L, Plan* plan);
 
 // Workspace of the backward over L tokens per row, all fp32, 256-byte
-// aligned: per-row softmax statistics of both branches (two arrays); five
-// d x d matrices per chunk of C = gdn_chunk tokens (transition, own state,
-// own adjoint, start state, adjoint at the end); the recomputed states of one
+// aligned: per-row softmax statistics of both branches (two arrays); six
+// d x d matrices per chunk of C = gdn_chunk tokens (transition and its
+// transpose, own state, own adjoint, start state, adjoint at the end); the recomputed states of one
 // chunk per slot (one slot per workgroup of the token pass); partial sums of
 // the mix-weight gradient.
 constexpr int kBwdSlots = 512;
 constexpr int kDwSlices = 128;
 struct BwdPlan {
   size_t stats_bytes = 0;   // each of the two: [2, B*L*H]
-  size_t mat_off = 0, mat_bytes = 0;   // each of the five: [B*H*n_chunks, d, d]
+  size_t mat_off = 0, mat_bytes = 0;   // each of the six: [B*H*n_chunks, d, d]
   size_t slot_off = 0;
   int n_slots = 0;
   size_t part_off = 0;

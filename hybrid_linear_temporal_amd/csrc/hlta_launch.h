@@ -82,6 +82,7 @@ struct BwdArgs {
   float* lse2;       // [2, B*L*H] workspace: softmax row statistics
   float* dsum;       // [2, B*L*H] workspace
   float* Am;         // [B*H, n_chunks, d, d] workspace: per-chunk transition of the memory
+  float* AmT;        //   ... its transpose
   float* Um;         //   ... the chunk's own state from zero
   float* Xm;         //   ... the chunk's own adjoint from zero
   float* Sst;        //   ... state at the chunk's start

@@ -183,7 +183,7 @@ def test_rope_config_checks(lib):
 
 
 def test_bwd_workspace_and_argument_errors(lib):
-    """Backward: workspace = two [2, B, L, H] fp32 statistics, five d x d
+    """Backward: workspace = two [2, B, L, H] fp32 statistics, six d x d
     matrices per chunk, the states of one chunk per token-pass slot (at most
     512 slots) and the mix-weight partial sums; argument errors fail before
     any launch."""
@@ -196,7 +196,7 @@ def test_bwd_workspace_and_argument_errors(lib):
 
     bh, dd = cfg.B * cfg.H, cfg.d * cfg.d * 4
     slots = min(bh * chunks, 512)
-    want = 2 * up(bh * L * 2 * 4) + 5 * up(bh * chunks * dd) + up(slots * cfg.gdn_chunk * dd) + up(cfg.H * 128 * 3 * 4)
+    want = 2 * up(bh * L * 2 * 4) + 6 * up(bh * chunks * dd) + up(slots * cfg.gdn_chunk * dd) + up(cfg.H * 128 * 3 * 4)
     ws = H.hlta_bwd_workspace_bytes(cfg)
     assert ws == want
     assert H.hlta_bwd_workspace_bytes(_cfg(d=96)) == 0
