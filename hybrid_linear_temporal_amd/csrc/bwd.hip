@@ -396,23 +396,61 @@ __device__ __forceinline__ void store_mat(float* dst, const float (&M)[D / 16][D
     for (int j = 0; j < BS; ++j) dst[size_t(tr * BS + i) * D + tc * BS + j] = M[i][j];
 }
 
+// CPL consecutive values of a [.., D] row (bf16 or fp32) as floats
+template <int CPL>
+__device__ __forceinline__ void load_cols(const bf16* p, float (&x)[CPL]) {
+#pragma unroll
+  for (int i = 0; i < CPL; i += 8) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p + i);
+    const bf16* e = reinterpret_cast<const bf16*>(&u);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[i + j] = static_cast<float>(e[j]);
+  }
+}
+template <int CPL>
+__device__ __forceinline__ void load_cols(const float* p, float (&x)[CPL]) {
+#pragma unroll
+  for (int i = 0; i < CPL; i += 4) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p + i);
+    const float* e = reinterpret_cast<const float*>(&u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[i + j] = e[j];
+  }
+}
+
+// sum over the 4 lanes of a row (lanes 4r .. 4r+3)
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  return x;
+}
+
 // Chunk c of head (b, h) covers tokens [c*C, min(L, (c+1)*C)). With
 // M_t = a_t (I - b_t k^_t k^_t^T) (symmetric), per chunk:
-//   what 0: A_c = M_s M_{s+1} .. M_e            (S_end = S_start A_c + U_c)
-//   what 1: U_c = the chunk's own state from S = 0
-//   what 2: X_c = sum_t do_t q^_t^T M_t M_{t-1} .. M_s
-//           (the chunk's own adjoint carried to its start; G = dL/dS)
-// grid (B*H*n_chunks, 3); one matrix per workgroup.
-template <typename Tin, typename Tg, int D>
+//   kWhat 0: A_c = M_s M_{s+1} .. M_e            (S_end = S_start A_c + U_c)
+//   kWhat 1: U_c = the chunk's own state from S = 0
+//   kWhat 2: X_c = sum_t do_t q^_t^T M_t M_{t-1} .. M_s
+//            (the chunk's own adjoint carried to its start; G = dL/dS)
+// Rows of all three evolve independently (row i of A M_t is a (a_i - b
+// (a_i . k^) k^)), so each wave owns 16 rows: lane = (row lane/4, quarter
+// lane%4 of the columns), row dot products by two lane shuffles, no barrier
+// inside the token loop. The workgroup (4 waves, 64 rows) first stages the
+// chunk's k (and q), the rows' v (or d_mix) and the gates in LDS, so a token
+// costs LDS reads only. grid (B*H*n_chunks, ceil(D/64)).
+constexpr int kMaxChunk = 64;
+template <typename Tin, typename Tg, int D, int kWhat>
 __global__ void __launch_bounds__(kThreads)
-gdn_bwd_prep(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float* Am, float* AmT, float* Um,
-             float* Xm) {
-  constexpr int BS = D / 16;
-  __shared__ GdnBlock<D> sm;
-  const int what = blockIdx.y;
+gdn_bwd_prep(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float* out, float* AmT) {
+  constexpr int CPL = D / 4;
+  __shared__ __attribute__((aligned(16))) Tin kS[kMaxChunk][D];
+  __shared__ __attribute__((aligned(16))) Tin qS[kWhat == 2 ? kMaxChunk : 1][D];
+  __shared__ float xS[kWhat >= 1 ? kMaxChunk : 1][64];
+  __shared__ float aS[kMaxChunk], bS[kMaxChunk];
   const long long job = blockIdx.x;
   const int c = int(job % p.n_chunks), bh = int(job / p.n_chunks), b = bh / p.H, h = bh % p.H;
-  const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane >> 2, c0 = (lane & 3) * CPL;
+  const int R0 = blockIdx.y * 64;
+  const int row = R0 + wave * 16 + r;
   const Tin* q = static_cast<const Tin*>(p.q);
   const Tin* k = static_cast<const Tin*>(p.k);
   const Tin* v = static_cast<const Tin*>(p.v);
@@ -420,83 +458,67 @@ gdn_bwd_prep(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float* Am,
   const long long t0 = (long long)c * C;
   const int n = int(p.L - t0 < C ? p.L - t0 : C);
   const bool l2 = p.l2norm != 0;
-  float M[BS][BS];
-#pragma unroll
-  for (int i = 0; i < BS; ++i)
-#pragma unroll
-    for (int j = 0; j < BS; ++j) M[i][j] = (what == 0 && tr * BS + i == tc * BS + j) ? 1.f : 0.f;
   const size_t tok0 = (size_t(b) * p.L + t0) * HD + size_t(h) * D;
   const size_t g0 = (size_t(b) * p.L + t0) * p.H + h;
-  const int e = threadIdx.x < D ? threadIdx.x : 0;
-  if (what < 2) {
-    // the next token's vectors and gates are loaded while the current one computes
-    float xk = ld(k, tok0 + e), xv = ld(v, tok0 + e), xa = p.a[g0], xb = p.b[g0];
-    for (int s = 0; s < n; ++s) {
-      if (threadIdx.x < D) {
-        sm.vec[0][threadIdx.x] = xk;
-        sm.vec[1][threadIdx.x] = xv;
-      }
-      const float at = xa, bt = xb;
-      __syncthreads();
-      if (s + 1 < n) {
-        xk = ld(k, tok0 + size_t(s + 1) * HD + e);
-        xv = ld(v, tok0 + size_t(s + 1) * HD + e);
-        xa = p.a[g0 + size_t(s + 1) * p.H];
-        xb = p.b[g0 + size_t(s + 1) * p.H];
-      }
-      fwd_token(sm, M, at, bt, l2, what == 1);
-    }
-  } else {
+  for (int e = threadIdx.x; e < n * D; e += kThreads) {
+    const int t = e / D, col = e % D;
+    kS[t][col] = k[tok0 + size_t(t) * HD + col];
+    if constexpr (kWhat == 2) qS[t][col] = q[tok0 + size_t(t) * HD + col];
+  }
+  if constexpr (kWhat >= 1) {
     const float w2 = mix_w[3 * h + 2];
-    size_t o = tok0 + size_t(n - 1) * HD + e;
-    float xk = ld(k, o), xd = w2 * ld(d_mix, o), xq = ld(q, o);
-    float xa = p.a[g0 + size_t(n - 1) * p.H], xb = p.b[g0 + size_t(n - 1) * p.H];
-    for (int s = n - 1; s >= 0; --s) {
-      if (threadIdx.x < D) {
-        sm.vec[0][threadIdx.x] = xk;
-        sm.vec[5][threadIdx.x] = xd;
-        sm.vec[6][threadIdx.x] = xq;
-      }
-      const float at = xa, bt = xb;
-      __syncthreads();
-      if (s > 0) {
-        o = tok0 + size_t(s - 1) * HD + e;
-        xk = ld(k, o), xd = w2 * ld(d_mix, o), xq = ld(q, o);
-        xa = p.a[g0 + size_t(s - 1) * p.H], xb = p.b[g0 + size_t(s - 1) * p.H];
-      }
-      float n2[2] = {0.f, 0.f};
-      if (threadIdx.x < D) {
-        n2[0] = sm.vec[0][threadIdx.x] * sm.vec[0][threadIdx.x];
-        n2[1] = sm.vec[6][threadIdx.x] * sm.vec[6][threadIdx.x];
-      }
-      sum_n<D, 2>(sm, n2, 0);
-      const float ik = 1.f / l2n(n2[0], l2), iq = 1.f / l2n(n2[1], l2);
-      // M <- (M + do q^^T) M_t
-#pragma unroll
-      for (int i = 0; i < BS; ++i)
-#pragma unroll
-        for (int j = 0; j < BS; ++j) M[i][j] += sm.vec[5][tr * BS + i] * sm.vec[6][tc * BS + j] * iq;
-      mv_part<D, true>(sm, M, sm.vec[0], 0);
-      __syncthreads();
-      mv_finish<D>(sm, 1, {8, 0, 0, 0}, {ik, 1.f, 1.f, 1.f});   // M k^
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < BS; ++i)
-#pragma unroll
-        for (int j = 0; j < BS; ++j)
-          M[i][j] = at * (M[i][j] - bt * sm.vec[8][tr * BS + i] * sm.vec[0][tc * BS + j] * ik);
-      __syncthreads();
+    for (int e = threadIdx.x; e < n * 64; e += kThreads) {
+      const int t = e / 64, rr = R0 + e % 64;
+      float x = 0.f;
+      if (rr < D) x = kWhat == 1 ? ld(v, tok0 + size_t(t) * HD + rr) : w2 * ld(d_mix, tok0 + size_t(t) * HD + rr);
+      xS[t][e % 64] = x;
     }
   }
-  float* dst = what == 0 ? Am : (what == 1 ? Um : Xm);
-  store_mat<D>(dst + size_t(job) * D * D, M);
-  if (what == 0) {   // A^T too, so both chains run the same row-times-matrix product
-    const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
-    float* t = AmT + size_t(job) * D * D;
+  if (threadIdx.x < n) {
+    aS[threadIdx.x] = p.a[g0 + size_t(threadIdx.x) * p.H];
+    bS[threadIdx.x] = p.b[g0 + size_t(threadIdx.x) * p.H];
+  }
+  __syncthreads();
+  if (R0 + wave * 16 >= D) return;   // d = 32: two waves have no rows
+  float M[CPL];
 #pragma unroll
-    for (int j = 0; j < BS; ++j)
+  for (int j = 0; j < CPL; ++j) M[j] = (kWhat == 0 && c0 + j == row) ? 1.f : 0.f;
+  for (int i = 0; i < n; ++i) {
+    const int s = kWhat == 2 ? n - 1 - i : i;
+    float kx[CPL];
+    load_cols<CPL>(&kS[s][c0], kx);
+    const float at = aS[s], bt = bS[s];
+    float k2 = 0.f;
 #pragma unroll
-      for (int i = 0; i < BS; ++i) t[size_t(tc * BS + j) * D + tr * BS + i] = M[i][j];
+    for (int j = 0; j < CPL; ++j) k2 += kx[j] * kx[j];
+    const float ik = 1.f / l2n(quad_sum(k2), l2);
+    if constexpr (kWhat == 2) {   // M <- M + do q^^T
+      float qx[CPL];
+      load_cols<CPL>(&qS[s][c0], qx);
+      float q2 = 0.f;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) q2 += qx[j] * qx[j];
+      const float f = xS[s][wave * 16 + r] / l2n(quad_sum(q2), l2);
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) M[j] += f * qx[j];
+    }
+    float u = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) u += M[j] * kx[j];
+    u = quad_sum(u) * ik;
+    // M <- a (M - b u k^^T) (+ b v k^^T for the own state)
+    const float cu = at * bt * u * ik;
+    const float cv = kWhat == 1 ? bt * xS[s][wave * 16 + r] * ik : 0.f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) M[j] = at * M[j] + (cv - cu) * kx[j];
+  }
+  float* dst = out + size_t(job) * D * D + size_t(row) * D + c0;
+#pragma unroll
+  for (int j = 0; j < CPL; j += 4) *reinterpret_cast<float4*>(dst + j) = make_float4(M[j], M[j + 1], M[j + 2], M[j + 3]);
+  if constexpr (kWhat == 0) {   // A^T too, so both chains run the same row-times-matrix product
+    float* t = AmT + size_t(job) * D * D + row;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) t[size_t(c0 + j) * D] = M[j];
   }
 }
 
@@ -809,8 +831,10 @@ hipError_t launch_bwd_t(const BwdArgs& x, hipStream_t st) {
   }
   const unsigned heads = unsigned(x.gdn.B * x.gdn.H);
   const unsigned jobs = heads * unsigned(x.gdn.n_chunks);
-  hipLaunchKernelGGL((gdn_bwd_prep<Tin, Tg, D>), dim3(jobs, 3), dim3(kThreads), 0, st, x.gdn, x.C, g, x.mix_w, x.Am,
-                     x.AmT, x.Um, x.Xm);
+  const dim3 pgrid(jobs, (D + 63) / 64);
+  hipLaunchKernelGGL((gdn_bwd_prep<Tin, Tg, D, 0>), pgrid, dim3(kThreads), 0, st, x.gdn, x.C, g, x.mix_w, x.Am, x.AmT);
+  hipLaunchKernelGGL((gdn_bwd_prep<Tin, Tg, D, 1>), pgrid, dim3(kThreads), 0, st, x.gdn, x.C, g, x.mix_w, x.Um, x.AmT);
+  hipLaunchKernelGGL((gdn_bwd_prep<Tin, Tg, D, 2>), pgrid, dim3(kThreads), 0, st, x.gdn, x.C, g, x.mix_w, x.Xm, x.AmT);
   hipLaunchKernelGGL((gdn_bwd_chain<D>), dim3(heads, D / kChainRows, 2), dim3(kThreads), 0, st, x.gdn.n_chunks,
                      x.gdn.S0, x.Am, x.AmT, x.Um, x.Xm, x.Sst, x.Rin, x.dS0);
   hipLaunchKernelGGL((gdn_bwd_tokens<Tin, Tg, D>), dim3(unsigned(x.n_slots)), dim3(kThreads), 0, st, x.gdn, x.C,
