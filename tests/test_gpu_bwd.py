@@ -114,3 +114,20 @@ def test_bwd_empty_clip():
     torch.cuda.synchronize()
     assert torch.count_nonzero(got["dmix_w"]).item() == 0
     assert torch.count_nonzero(got["dS0"]).item() == 0
+
+
+def test_bwd_deterministic():
+    """Two backward calls on the same inputs give bit-identical gradients (no
+    atomics; every reduction runs in a fixed order), on the MFMA path."""
+    wl = CASES[4][1]
+    print(f"case {CASES[4][0]} twice", flush=True)
+    x = I.make_clip(wl)
+    cfg = H.make_config(wl)
+    dev = H.to_device(x, wl.dtype)
+    fwd = H.hlta_fwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"])
+    g_t = torch.from_numpy(I.upstream_grad(wl, "bf16")).cuda().to(torch.bfloat16)
+    r1 = H.hlta_bwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], fwd, g_t)
+    r2 = H.hlta_bwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], fwd, g_t)
+    torch.cuda.synchronize()
+    for n in GRADS:
+        assert torch.equal(r1[n], r2[n]), n
