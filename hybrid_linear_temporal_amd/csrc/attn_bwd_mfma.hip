@@ -335,9 +335,13 @@ __device__ __forceinline__ void issue_stats(float* Ld, float* Dd, const KeyStrea
                                    (__attribute__((address_space(3))) void*)(wave == 0 ? Ld : Dd), 4, 0, 0);
 }
 
-__global__ void __launch_bounds__(NT, 1)
-attn_bwd_dkdv_mfma(AttnParams p, const bf16* g, const float* mix_w, const float* lse, const float* dsum, float* dk,
-                   float* dv, float scale) {
+// kDV: dV^T += dO^T (w P) (scores X = Q K^T only); otherwise dK^T += Q^T dS
+// (X and dP = dO V^T). Two instantiations, so each holds one accumulator set
+// and runs two waves per SIMD.
+template <bool kDV>
+__global__ void __launch_bounds__(NT, 2)
+attn_bwd_dkdv_mfma(AttnParams p, const bf16* g, const float* mix_w, const float* lse, const float* dsum, float* out,
+                   float scale) {
   __shared__ Tile sQ0, sG0, sQ1, sG1;
   __shared__ __attribute__((aligned(16))) float sL0[KT], sD0[KT], sL1[KT], sD1[KT];
   const int tid = threadIdx.x;
@@ -350,9 +354,9 @@ attn_bwd_dkdv_mfma(AttnParams p, const bf16* g, const float* mix_w, const float*
   const bool kok = krow < p.P;
   const bool wave_active = it.rt * RT + wave * 32 < p.P;
   const size_t fbase = ((size_t(it.b) * p.T + it.f) * p.P) * HD + size_t(it.h) * D;
-  bf16x8 kv[8], vv[8];
+  bf16x8 kv[8], vv[kDV ? 1 : 8];
   load_rows(static_cast<const bf16*>(p.k) + fbase, krow, kok, HD, hl, kv);
-  load_rows(static_cast<const bf16*>(p.v) + fbase, krow, kok, HD, hl, vv);
+  if constexpr (!kDV) load_rows(static_cast<const bf16*>(p.v) + fbase, krow, kok, HD, hl, vv);
   unsigned off[4];
   dma_offsets(wave, lane, HD, off);
   KeyStream<false> qst;
@@ -363,11 +367,11 @@ attn_bwd_dkdv_mfma(AttnParams p, const bf16* g, const float* mix_w, const float*
   qst.vmain = uni(g + o);
   const float c = p.scale_log2;
   const size_t L = size_t(p.T) * p.P;
-  f32x16 ak[4], av[4];
+  f32x16 acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) ak[db][r] = av[db][r] = 0.f;
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
   for (int branch = 0; branch < 2; ++branch) {
     // query frames reading key frame gk: gk .. gk+W-1 (SWA), gk + dil*j, j = 1..taps (DSWA)
     const long long first = branch == 0 ? gk : gk + p.dil;
@@ -412,33 +416,30 @@ attn_bwd_dkdv_mfma(AttnParams p, const bf16* g, const float* mix_w, const float*
 #pragma unroll
           for (int k8 = 0; k8 < 8; ++k8) {
             x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_chunk(Qt, qb, l32, 2 * k8 + hl), kv[k8], x, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_chunk(Gt, qb, l32, 2 * k8 + hl), vv[k8], dp, 0, 0, 0);
+            if constexpr (!kDV)
+              dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_chunk(Gt, qb, l32, 2 * k8 + hl), vv[k8], dp, 0, 0, 0);
           }
-          bf16x8 pw[2], dsb[2];
+          bf16x8 ob[2];   // w P (kDV) or dS
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
             // queries qb*32 + 8 r4 + 4 hl + 0..3: their statistics as one 16-byte read each
             const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lt + qb * 32 + 8 * r4 + 4 * hl);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dt + qb * 32 + 8 * r4 + 4 * hl);
+            f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (!kDV) d4 = *reinterpret_cast<const f32x4*>(Dt + qb * 32 + 8 * r4 + 4 * hl);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * r4 + e;
               float pr = __builtin_amdgcn_exp2f(fmaf(x[r], c, -l4[e]));
               if (qb * 32 + 8 * r4 + e >= qthr) pr = 0.f;
-              const float ds = pr * fmaf(w, dp[r], -d4[e]);
-              pw[r >> 3][r & 7] = static_cast<bf16>(w * pr);
-              dsb[r >> 3][r & 7] = static_cast<bf16>(ds);
+              ob[r >> 3][r & 7] = static_cast<bf16>(kDV ? w * pr : pr * fmaf(w, dp[r], -d4[e]));
             }
           }
 #pragma unroll
           for (int db = 0; db < 4; ++db)
 #pragma unroll
-            for (int m2 = 0; m2 < 2; ++m2) {
-              av[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_vt(Gt, qb, m2, hl, db * 32 + (l32 & 16), l16),
-                                                               pw[m2], av[db], 0, 0, 0);
-              ak[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_vt(Qt, qb, m2, hl, db * 32 + (l32 & 16), l16),
-                                                               dsb[m2], ak[db], 0, 0, 0);
-            }
+            for (int m2 = 0; m2 < 2; ++m2)
+              acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  ld_vt(kDV ? Gt : Qt, qb, m2, hl, db * 32 + (l32 & 16), l16), ob[m2], acc[db], 0, 0, 0);
         }
       }
     };
@@ -447,10 +448,7 @@ attn_bwd_dkdv_mfma(AttnParams p, const bf16* g, const float* mix_w, const float*
       if (t + 1 < ntiles) tile(t + 1, sQ1, sG1, sL1, sD1, sQ0, sG0, sL0, sD0);
     }
   }
-  if (kok) {
-    store_rows(dk + fbase + size_t(krow) * HD, ak, scale, hl);
-    store_rows(dv + fbase + size_t(krow) * HD, av, 1.f, hl);
-  }
+  if (kok) store_rows(out + fbase + size_t(krow) * HD, acc, kDV ? 1.f : scale, hl);
 }
 
 }  // namespace
@@ -468,7 +466,8 @@ hipError_t launch_attn_bwd_mfma(const AttnParams& p, const void* d_mix, const vo
   hipLaunchKernelGGL(attn_bwd_dsum, dim3(dgrid), dim3(256), 0, st, g, static_cast<const bf16*>(o_swa),
                      static_cast<const bf16*>(o_dswa), mix_w, dsum, p.B, L, p.H);
   hipLaunchKernelGGL(attn_bwd_dq_mfma, dim3(grid), dim3(NT), 0, st, p, g, mix_w, lse, dsum, dq, scale);
-  hipLaunchKernelGGL(attn_bwd_dkdv_mfma, dim3(grid), dim3(NT), 0, st, p, g, mix_w, lse, dsum, dk, dv, scale);
+  hipLaunchKernelGGL(attn_bwd_dkdv_mfma<false>, dim3(grid), dim3(NT), 0, st, p, g, mix_w, lse, dsum, dk, scale);
+  hipLaunchKernelGGL(attn_bwd_dkdv_mfma<true>, dim3(grid), dim3(NT), 0, st, p, g, mix_w, lse, dsum, dv, scale);
   return hipGetLastError();
 }
 

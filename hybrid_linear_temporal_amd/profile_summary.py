@@ -41,7 +41,8 @@ def summarise(path: str) -> str:
                                ("16rope_ring_kernelIDF16b", "rope_ring_kernel<bf16>"),
                                ("16rope_ring_kernelIf", "rope_ring_kernel<float>"),
                                ("16attn_bwd_dq_mfmaE", "attn_bwd_dq_mfma"),
-                               ("18attn_bwd_dkdv_mfmaE", "attn_bwd_dkdv_mfma"),
+                               ("18attn_bwd_dkdv_mfmaILb0", "attn_bwd_dkdv_mfma<dK>"),
+                               ("18attn_bwd_dkdv_mfmaILb1", "attn_bwd_dkdv_mfma<dV>"),
                                ("17attn_bwd_lse_mfmaE", "attn_bwd_lse_mfma"),
                                ("13attn_bwd_dsumE", "attn_bwd_dsum"),
                                ("14attn_bwd_statsI", "attn_bwd_stats (fp32)"),
