@@ -131,3 +131,38 @@ def test_bwd_deterministic():
     torch.cuda.synchronize()
     for n in GRADS:
         assert torch.equal(r1[n], r2[n]), n
+
+
+def test_bwd_graph_replays_match_eager():
+    """hlta_bwd captured in a HIP graph (MFMA path): every replay, with eager
+    work and synchronisation in between, equals the eager call bit for bit."""
+    wl = CASES[4][1]
+    print(f"case {CASES[4][0]} captured", flush=True)
+    x = I.make_clip(wl)
+    cfg = H.make_config(wl)
+    dev = H.to_device(x, wl.dtype)
+    fwd = H.hlta_fwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"])
+    g_t = torch.from_numpy(I.upstream_grad(wl, "bf16")).cuda().to(torch.bfloat16)
+    ws = H.alloc_workspace(H.hlta_bwd_workspace_bytes(cfg))
+
+    def call():
+        return H.hlta_bwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], fwd, g_t, workspace=ws)
+
+    ref = call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            out = call()
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        for t in out.values():
+            t.fill_(float("nan"))
+        ws.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n in GRADS:
+            assert torch.equal(out[n], ref[n]), (rep, n)
