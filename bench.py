@@ -308,7 +308,8 @@ def bwd_leg(H, wl, dev, out, S_out, steps, impl):
     attn_flops = 2.5 * work(wl)[0]
     return {"steps": steps, "ms_per_step": ms, "tokens_per_s": wl.B * wl.L / (ms * 1e-3),
             "attn_bwd_flops": attn_flops, "workspace_bytes": ws.numel(), "grads_finite": finite,
-            "note": "fp32 kernels; per-kernel times in the rocprofv3 summary"}
+            "note": "softmax branches on bf16 MFMA (fp32 gradients), memory in fp32; per-kernel times in "
+                    "profiles/kernels_bwd_p480_T31_bf16.md"}
 
 
 def main():
