@@ -166,3 +166,75 @@ def test_bwd_graph_replays_match_eager():
         torch.cuda.synchronize()
         for n in GRADS:
             assert torch.equal(out[n], ref[n]), (rep, n)
+
+
+def _oracle_grads(wl, x, g, S0, l2norm):
+    """Gradients of every head from the oracle's per-branch functions, with the
+    memory's L2 normalisation on or off (hlta_backward takes the default)."""
+    B, Lt, Hh, d = x["q"].shape
+    out = {n: np.zeros((B, Lt, Hh, d)) for n in ("dq", "dk", "dv")}
+    out["da"], out["db"] = np.zeros((B, Lt, Hh)), np.zeros((B, Lt, Hh))
+    out["dmix_w"], out["dS0"] = np.zeros((Hh, 3)), np.zeros((B, Hh, d, d))
+    for b in range(B):
+        for h in range(Hh):
+            q, k, v = x["q"][b, :, h], x["k"][b, :, h], x["v"][b, :, h]
+            a, bb = x["a"][b, :, h], x["b"][b, :, h]
+            gh = g[b, :, h].astype(np.float64)
+            w3 = x["w"][h].astype(np.float64)
+            s0 = None if S0 is None else S0[b, h]
+            for i, fo in ((0, lambda f: O.swa_frames(f, wl.swa_frames)),
+                          (1, lambda f: O.dswa_frames(f, wl.dswa_dilation, wl.dswa_taps))):
+                gq, gk, gv = O.attention_backward(q, k, v, w3[i] * gh, wl.T, wl.P, fo)
+                out["dq"][b, :, h] += gq
+                out["dk"][b, :, h] += gk
+                out["dv"][b, :, h] += gv
+            gq, gk, gv, ga, gb, gS = O.gdn_recurrent_backward(q, k, v, a, bb, w3[2] * gh, s0, l2norm=l2norm)
+            out["dq"][b, :, h] += gq
+            out["dk"][b, :, h] += gk
+            out["dv"][b, :, h] += gv
+            out["da"][b, :, h], out["db"][b, :, h], out["dS0"][b, h] = ga, gb, gS
+            o_gdn, _ = O.gdn_recurrent(q, k, v, a, bb, s0, l2norm=l2norm)
+            out["dmix_w"][h] += [np.sum(gh * O.swa(q, k, v, wl.T, wl.P, wl.swa_frames)),
+                                 np.sum(gh * O.dswa(q, k, v, wl.T, wl.P, wl.dswa_dilation, wl.dswa_taps)),
+                                 np.sum(gh * o_gdn)]
+    return out
+
+
+@pytest.mark.parametrize("name,wl,out_dt,l2norm", [
+    ("f32_no_l2norm", small("bwd_nol2", B=1, H=2, T=6, P=20, d=32, swa_frames=2, dswa_dilation=2, dswa_taps=2,
+                            gdn_chunk=16, seed=2105), "f32", False),
+    ("bf16_mfma_chunk32", small("bwd_c32", B=1, H=2, T=5, P=72, d=128, swa_frames=3, dswa_dilation=2,
+                                dswa_taps=2, gdn_chunk=32, dtype="bf16", seed=2106), "bf16", True),
+], ids=["f32_no_l2norm", "bf16_mfma_chunk32"])
+def test_bwd_options(name, wl, out_dt, l2norm):
+    """The memory's L2 normalisation off (q and k halved, so it matters), with
+    the forward's memory output checked too; and the MFMA softmax-branch
+    kernels beside a 32-token memory chunk."""
+    print(f"case {name}", flush=True)
+    x = I.make_clip(wl)
+    x["q"] = (x["q"] * 0.5).astype(np.float32)   # exact in every dtype
+    x["k"] = (x["k"] * 0.5).astype(np.float32)
+    cfg = H.make_config(wl, out_dtype=out_dt, l2norm=l2norm)
+    dev = H.to_device(x, wl.dtype)
+    S0 = _start_state(wl)
+    S0_t = torch.from_numpy(S0).cuda()
+    fwd = H.hlta_fwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], S0=S0_t)
+    g = I.upstream_grad(wl, out_dt)
+    g_t = torch.from_numpy(g).cuda().to(torch.bfloat16 if out_dt == "bf16" else torch.float32)
+    got = H.hlta_bwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], fwd, g_t, S0=S0_t)
+    torch.cuda.synchronize()
+    tol = TOL[out_dt]
+    for b in range(wl.B):
+        for h in range(wl.H):
+            o_ref, _ = O.gdn_recurrent(x["q"][b, :, h], x["k"][b, :, h], x["v"][b, :, h], x["a"][b, :, h],
+                                       x["b"][b, :, h], S0[b, h], l2norm=l2norm)
+            e = O.rel_l2(to64(fwd["o_gdn"][b, :, h]), o_ref)
+            print(f"{name} forward o_gdn (b={b}, h={h}) {e:.2e}", flush=True)
+            assert e <= tol
+    ref = _oracle_grads(wl, x, g, S0, l2norm)
+    mfma = _mfma(wl, out_dt, AUTO)
+    for n in GRADS:
+        e = O.rel_l2(to64(got[n]), ref[n])
+        print(f"{name} {n} {e:.2e}", flush=True)
+        loose = (n == "dmix_w" and out_dt == "bf16") or (mfma and n in ("dq", "dk", "dv"))
+        assert e <= (TOL["bf16"] if loose else TOL["f32"]), f"{name} {n}: {e:.3e}"
