@@ -315,3 +315,23 @@ def test_attn_fp8_matches_attention_over_dequantised_inputs(wl):
     w = x["w"].astype(np.float64)
     mix = w[None, None, :, 0, None] * to64(out["o_swa"]) + w[None, None, :, 1, None] * to64(out["o_dswa"])
     assert np.all(np.abs(to64(out["o_mix"]) - mix) <= 2.0 ** -8 * np.abs(mix) + 1e-6)
+
+
+@pytest.mark.parametrize("dtype,C", [("bf16", 64), ("f32", 16)], ids=["mfma", "generic"])
+def test_gdn_without_l2norm(dtype, C):
+    """gdn_l2norm_qk = 0: q and k are used as given (here halved, so the
+    normalisation would change the result) on both memory kernel families."""
+    wl = small(f"nol2_{dtype}", B=1, H=2, T=5, P=72, d=128 if dtype == "bf16" else 32, swa_frames=3,
+               dswa_dilation=2, dswa_taps=2, gdn_chunk=C, dtype=dtype, seed=2107)
+    print(f"case {wl.name}", flush=True)
+    x = I.make_clip(wl)
+    x["q"] = (x["q"] * 0.5).astype(np.float32)
+    x["k"] = (x["k"] * 0.5).astype(np.float32)
+    got = run_gpu(wl, x, l2norm=False)
+    for h in range(wl.H):
+        o_ref, S_ref = O.gdn_recurrent(x["q"][0, :, h], x["k"][0, :, h], x["v"][0, :, h], x["a"][0, :, h],
+                                       x["b"][0, :, h], l2norm=False)
+        e = O.rel_l2(to64(got["o_gdn"][0, :, h]), o_ref)
+        eS = O.rel_l2(to64(got["S_out"][0, h]), S_ref)
+        print(f"{wl.name} h={h} o_gdn {e:.2e} S_out {eS:.2e}", flush=True)
+        assert e <= TOL[dtype] and eS <= TOL[dtype]
