@@ -238,3 +238,40 @@ def test_bwd_options(name, wl, out_dt, l2norm):
         print(f"{name} {n} {e:.2e}", flush=True)
         loose = (n == "dmix_w" and out_dt == "bf16") or (mfma and n in ("dq", "dk", "dv"))
         assert e <= (TOL["bf16"] if loose else TOL["f32"]), f"{name} {n}: {e:.3e}"
+
+
+@pytest.mark.parametrize("name,wl,out_dt", [
+    ("f32_scale", small("scale_f32", B=1, H=2, T=6, P=20, d=32, swa_frames=2, dswa_dilation=2, dswa_taps=2,
+                        gdn_chunk=16, seed=2108), "f32"),
+    ("bf16_mfma_scale", small("scale_bf16", B=1, H=1, T=5, P=72, d=128, swa_frames=3, dswa_dilation=2,
+                              dswa_taps=2, gdn_chunk=64, dtype="bf16", seed=2109), "bf16"),
+], ids=["f32", "bf16_mfma"])
+def test_softmax_scale_forward_and_backward(name, wl, out_dt):
+    """A caller-set softmax scale (0.3 instead of 1/sqrt(d)) reaches both
+    softmax branches of the forward and their gradients."""
+    scale = 0.3
+    print(f"case {name} scale {scale}", flush=True)
+    x = I.make_clip(wl, q_scale=4.0)   # peaked enough that the scale matters
+    cfg = H.make_config(wl, out_dtype=out_dt, softmax_scale=scale)
+    dev = H.to_device(x, wl.dtype)
+    fwd = H.hlta_fwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"])
+    g = I.upstream_grad(wl, out_dt)
+    g_t = torch.from_numpy(g).cuda().to(torch.bfloat16 if out_dt == "bf16" else torch.float32)
+    got = H.hlta_bwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], fwd, g_t)
+    torch.cuda.synchronize()
+    tol = TOL[out_dt]
+    for h in range(wl.H):
+        q, k, v = x["q"][0, :, h], x["k"][0, :, h], x["v"][0, :, h]
+        for name_o, ref in (("o_swa", O.swa(q, k, v, wl.T, wl.P, wl.swa_frames, scale)),
+                            ("o_dswa", O.dswa(q, k, v, wl.T, wl.P, wl.dswa_dilation, wl.dswa_taps, scale))):
+            e = O.rel_l2(to64(fwd[name_o][0, :, h]), ref)
+            print(f"{name} {name_o} h={h} {e:.2e}", flush=True)
+            assert e <= tol
+    ref = O.hlta_backward(x["q"], x["k"], x["v"], x["a"], x["b"], x["w"], g, wl.T, wl.P, wl.swa_frames,
+                          wl.dswa_dilation, wl.dswa_taps, scale=scale)
+    mfma = _mfma(wl, out_dt, AUTO)
+    for n, r in zip(GRADS, ref):
+        e = O.rel_l2(to64(got[n]), r)
+        print(f"{name} {n} {e:.2e}", flush=True)
+        loose = (n == "dmix_w" and out_dt == "bf16") or (mfma and n in ("dq", "dk", "dv"))
+        assert e <= (TOL["bf16"] if loose else TOL["f32"]), f"{name} {n}: {e:.3e}"
