@@ -332,7 +332,7 @@ def main():
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1 (heads and rollouts shard across GPUs with no exchange, but no multi-GPU path is built)"}))
         sys.exit(2)
 
     import torch

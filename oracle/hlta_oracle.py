@@ -15,7 +15,7 @@ sliding-window softmax attention for local dynamics, dilated sliding windows for
 mid-range dependencies, and gated linear attention with a delta update rule as
 the persistent global memory.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * tokens are frame-major, t = f*P + p; frame(t) = t // P;
   * the softmax branches are frame-block causal: a query of frame f sees every
     token of each frame in its frame set, bidirectional inside a frame;
