@@ -217,9 +217,11 @@ hlta_status hlta_attn_fwd_fp8(const hlta_config* cfg, const void* q8, const void
  *   softmax branches: the exact gradient of softmax attention over each query
  *     frame's key set (the branches are exact attention: long-context page,
  *     section 03), recomputed from q, k, v with per-row log-sum-exp;
- *   memory: the gated delta rule of hlta_fwd run backwards token by token from
- *     per-chunk state checkpoints (Kairos related-work page, row A; long-context
- *     page, section 06), through the L2 normalisation of q and k when on.
+ *   memory: the exact gradient of the gated delta rule of hlta_fwd (Kairos
+ *     related-work page, row A; long-context page, section 06): per chunk its
+ *     transition, own state and own adjoint, chains over chunks for every
+ *     chunk's start state and incoming adjoint, then each chunk's tokens run
+ *     backwards; through the L2 normalisation of q and k when on.
  * dq, dk, dv receive the sum over the three branches.
  *
  * q, k, v, a, b, mix_w, S0   the forward's inputs (read only)
@@ -231,7 +233,13 @@ hlta_status hlta_attn_fwd_fp8(const hlta_config* cfg, const void* q8, const void
  * dS0        [B, H, d, d] float32 gradient of the start state, or NULL
  * workspace  device buffer of at least hlta_bwd_workspace_bytes(cfg) bytes
  * The gates are taken as given (gate_logits = 1 and the rotary embedding give
- * HLTA_E_UNSUPPORTED). Gradients are evaluated in fp32 whatever the dtypes.
+ * HLTA_E_UNSUPPORTED). The memory's gradients are evaluated in fp32. The
+ * softmax branches' are too, except with bf16 inputs and outputs, d = 128 and
+ * P >= 64, where they run on bf16 MFMA (fp32 accumulation; P and dS rounded
+ * to bf16 for their products; D = do . o from the stored outputs).
+ * Validation (NULL, alignment, workspace size, config) happens before any
+ * launch; outputs must not alias inputs; results are deterministic (no
+ * atomics). Work is enqueued on `stream`; nothing is allocated.
  */
 size_t hlta_bwd_workspace_bytes(const hlta_config* cfg);
 hlta_status hlta_bwd(const hlta_config* cfg,
