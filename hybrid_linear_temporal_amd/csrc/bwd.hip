@@ -1,7 +1,7 @@
 // Backward of the operator (gradients for training): given dL/do_mix, the
 // gradients of q, k, v, the gates, the mix weights and the start state. The
-// branch gradients are do_i = w[h, i] * d_mix (the mix is linear). Plain fp32
-// kernels (any supported d and input dtype), written for clarity first:
+// branch gradients are do_i = w[h, i] * d_mix (the mix is linear). fp32
+// kernels (any supported d and input dtype):
 //
 //  * softmax branches (exact attention, so its gradient is the textbook one;
 //    long-context page, section 03 on tiled exact attention): a recompute pass
@@ -18,8 +18,9 @@
 //    chunk's start state and the adjoint reaching its end; then, per chunk in
 //    parallel again, the states are recomputed token by token and the adjoint
 //    carried back over the chunk, giving the token gradients (formulas at
-//    gdn_bwd_tokens). Exact in fp32 (no approximation beyond rounding);
-//    one workgroup per matrix, each thread owning a (d/16) x (d/16) block;
+//    gdn_bwd_tokens). Exact in fp32 (no approximation beyond rounding). The
+//    prep gives each wave 16 rows of one matrix (rows evolve independently);
+//    the token pass keeps S and G as per-thread (d/16) x (d/16) blocks;
 //  * mix weights: dw[h, i] = <d_mix, o_i> over the stored branch outputs.
 // With bf16 inputs and outputs, d = 128 and P >= 64 the softmax branches run
 // on the bf16 MFMA kernels of attn_bwd_mfma.hip instead.
