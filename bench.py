@@ -325,7 +325,7 @@ def main():
                     help="steps of the FP8 softmax branches timed (0: skip)")
     ap.add_argument("--rope-steps", type=int, default=5,
                     help="hlta_fwd steps timed with and without the rotary embedding (0: skip)")
-    ap.add_argument("--bwd-steps", type=int, default=1,
+    ap.add_argument("--bwd-steps", type=int, default=3,
                     help="steps of the backward (hlta_bwd) timed on the same clip (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB read + 1 GiB write elementwise kernel (3 launches), to scale "
