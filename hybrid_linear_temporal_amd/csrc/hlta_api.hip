@@ -172,8 +172,7 @@ hlta_status hlta_fwd(const hlta_config* cfg, const void* q, const void* k, const
   if (plan.L == 0) {
     // empty clip: the state passes through unchanged
     if (S_out && S_out != S0) {
-      hipError_t e = S0 ? hipMemcpyAsync(S_out, S0, state_bytes(cfg), hipMemcpyDeviceToDevice, st)
-                        : hipMemsetAsync(S_out, 0, state_bytes(cfg), st);
+      hipError_t e = launch_copy_or_zero(S_out, S0, state_bytes(cfg), st);
       if (e != hipSuccess) return hip_fail(e, "state copy");
     }
     return HLTA_OK;
@@ -199,8 +198,7 @@ hlta_status hlta_gdn_fwd(const hlta_config* cfg, const void* q, const void* k, c
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (plan.L == 0) {
     if (S_out && S_out != S0) {
-      hipError_t e = S0 ? hipMemcpyAsync(S_out, S0, state_bytes(cfg), hipMemcpyDeviceToDevice, st)
-                        : hipMemsetAsync(S_out, 0, state_bytes(cfg), st);
+      hipError_t e = launch_copy_or_zero(S_out, S0, state_bytes(cfg), st);
       if (e != hipSuccess) return hip_fail(e, "state copy");
     }
     return HLTA_OK;
@@ -304,8 +302,8 @@ hlta_status hlta_bwd(const hlta_config* cfg, const void* q, const void* k, const
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (plan.L == 0) {
     // no tokens: every gradient that exists is zero
-    hipError_t e = hipMemsetAsync(dmix_w, 0, size_t(cfg->H) * 3 * sizeof(float), st);
-    if (e == hipSuccess && dS0) e = hipMemsetAsync(dS0, 0, state_bytes(cfg), st);
+    hipError_t e = launch_copy_or_zero(dmix_w, nullptr, size_t(cfg->H) * 3 * sizeof(float), st);
+    if (e == hipSuccess && dS0) e = launch_copy_or_zero(dS0, nullptr, state_bytes(cfg), st);
     if (e != hipSuccess) return hip_fail(e, "gradient clear");
     return HLTA_OK;
   }
@@ -401,9 +399,7 @@ hlta_status hlta_stream_load_prefix(const hlta_config* cfg, hlta_stream_state* s
     e = launch_rope_ring(st->ring_k, cfg->B, st->ring_frames, first, int(keep), cfg->H, cfg->d, cfg->P,
                          cfg->rope_grid_w, cfg->rope_theta, cfg->in_dtype, s);
   if (e != hipSuccess) return hip_fail(e, "ring store");
-  e = S_prefix ? (S_prefix == st->S ? hipSuccess
-                                    : hipMemcpyAsync(st->S, S_prefix, state_bytes(cfg), hipMemcpyDeviceToDevice, s))
-               : hipMemsetAsync(st->S, 0, state_bytes(cfg), s);
+  e = S_prefix == st->S ? hipSuccess : launch_copy_or_zero(st->S, S_prefix, state_bytes(cfg), s);
   if (e != hipSuccess) return hip_fail(e, "state copy");
   st->frames_done = prefix_frames;
   return HLTA_OK;

@@ -31,6 +31,9 @@ hipError_t launch_gdn_generic(const GdnParams& p, int d, int C, int in_dt, int o
 // Gated delta rule, chunked form with bf16 MFMA (bf16 inputs, d = 128, C = 64).
 hipError_t launch_gdn_mfma(const GdnParams& p, int out_dt, hipStream_t st);
 
+// dst = src (src non-null) or dst = 0, bytes a multiple of 4; one kernel launch.
+hipError_t launch_copy_or_zero(void* dst, const void* src, size_t bytes, hipStream_t st);
+
 // Copy n_frames latent frames [B, frames, P, H, d] from src (frames src_f0..)
 // into ring slots (frame g -> slot g mod R). elem = element bytes.
 hipError_t launch_ring_store(const void* src, long long src_frames, long long src_f0, void* ring,

@@ -92,7 +92,26 @@ mix_kernel(const T* swa, const T* dswa, const T* gdn, T* mix, const float* w, lo
   }
 }
 
+// dst = src, or dst = 0 when src is null, over n 4-byte words (grid-stride).
+// A kernel rather than hipMemcpyAsync / hipMemsetAsync, so that every entry
+// point records only kernel nodes when a caller captures it in a HIP graph.
+__global__ void __launch_bounds__(kThreads)
+copy_words_kernel(unsigned* dst, const unsigned* src, long long n) {
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < n; i += (long long)gridDim.x * kThreads)
+    dst[i] = src ? src[i] : 0u;
+}
+
 }  // namespace
+
+hipError_t launch_copy_or_zero(void* dst, const void* src, size_t bytes, hipStream_t st) {
+  const long long n = (long long)(bytes / 4);
+  if (n <= 0) return hipSuccess;
+  long long blocks = (n + kThreads * 4 - 1) / (kThreads * 4);
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(copy_words_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, st, static_cast<unsigned*>(dst),
+                     static_cast<const unsigned*>(src), n);
+  return hipGetLastError();
+}
 
 hipError_t launch_mix(const void* o_swa, const void* o_dswa, const void* o_gdn, void* o_mix, const float* mix_w,
                       long long ntok, int H, int d, int out_dt, hipStream_t st, unsigned long long skip,

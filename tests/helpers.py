@@ -72,3 +72,15 @@ def compare(gpu: dict, ref, tol: float, heads=None, label=""):
 
 def replace(wl, **kw):
     return dataclasses.replace(wl, **kw)
+
+
+def rescale_qk(x: dict, dtype: str, seed: int, lo: float = 0.3, hi: float = 3.0) -> dict:
+    """Copy of x with every (token, head) row of q and k multiplied by its own
+    factor ~ U[lo, hi], rounded once to dtype: keys and queries of non-unit
+    norm, so the memory's in-op L2 normalisation changes the result."""
+    rng = np.random.default_rng(seed)
+    y = dict(x)
+    for n in ("q", "k"):
+        s = rng.uniform(lo, hi, x[n].shape[:-1])[..., None]
+        y[n] = I.cast(x[n].astype(np.float64) * s, dtype)
+    return y

@@ -275,3 +275,110 @@ def test_softmax_scale_forward_and_backward(name, wl, out_dt):
         print(f"{name} {n} {e:.2e}", flush=True)
         loose = (n == "dmix_w" and out_dt == "bf16") or (mfma and n in ("dq", "dk", "dv"))
         assert e <= (TOL["bf16"] if loose else TOL["f32"]), f"{name} {n}: {e:.3e}"
+
+
+# ---------------------------------------------------------------------------
+# softmax-branch gradients alone: the memory's mix weight is 0, so dq, dk, dv
+# come from the SWA/DSWA backward kernels only and nothing else can hide an
+# error in them
+# ---------------------------------------------------------------------------
+
+def _softmax_only_weights(Hh):
+    """Per head: SWA alone, DSWA alone, then both (memory weight 0 everywhere)."""
+    pattern = np.array([[1.0, 0.0, 0.0], [0.0, 1.0, 0.0], [0.7, 0.4, 0.0]], np.float32)
+    return pattern[np.arange(Hh) % 3]
+
+
+def _softmax_oracle_grads(wl, x, g, scale=None):
+    """dq, dk, dv of w0 * SWA + w1 * DSWA per (row, head), float64."""
+    out = {n: np.zeros(x["q"].shape) for n in ("dq", "dk", "dv")}
+    for b in range(wl.B):
+        for h in range(wl.H):
+            q, k, v = x["q"][b, :, h], x["k"][b, :, h], x["v"][b, :, h]
+            gh = g[b, :, h].astype(np.float64)
+            for i, fo in ((0, lambda f: O.swa_frames(f, wl.swa_frames)),
+                          (1, lambda f: O.dswa_frames(f, wl.dswa_dilation, wl.dswa_taps))):
+                wi = float(x["w"][h, i])
+                if wi == 0.0:
+                    continue
+                gq, gk, gv = O.attention_backward(q, k, v, wi * gh, wl.T, wl.P, fo, scale)
+                out["dq"][b, :, h] += gq
+                out["dk"][b, :, h] += gk
+                out["dv"][b, :, h] += gv
+    return out
+
+
+SOFTMAX_ONLY_CASES = [
+    # name, workload, out dtype, impl. P >= 64 and not a multiple of 64 (ragged
+    # row and key tiles); T below dil * taps, so early frames have partial DSWA
+    # tap sets and frame 0 none; three heads: SWA only, DSWA only, both.
+    ("mfma_P72", small("smx_mfma", B=1, H=3, T=6, P=72, d=128, swa_frames=3, dswa_dilation=2, dswa_taps=3,
+                       gdn_chunk=64, dtype="bf16", seed=2110), "bf16", AUTO),
+    ("mfma_B2_P100", small("smx_mfma_b2", B=2, H=3, T=9, P=100, d=128, swa_frames=3, dswa_dilation=2,
+                           dswa_taps=3, gdn_chunk=64, dtype="bf16", seed=2111), "bf16", AUTO),
+    ("generic_bf16_P72", small("smx_gen", B=1, H=3, T=6, P=72, d=128, swa_frames=3, dswa_dilation=2,
+                               dswa_taps=3, gdn_chunk=64, dtype="bf16", seed=2112), "bf16", GEN),
+    ("generic_f32_d64", small("smx_f32", B=2, H=3, T=7, P=40, d=64, swa_frames=2, dswa_dilation=2, dswa_taps=3,
+                              gdn_chunk=32, seed=2113), "f32", AUTO),
+]
+
+
+@pytest.mark.parametrize("name,wl,out_dt,impl", SOFTMAX_ONLY_CASES, ids=[c[0] for c in SOFTMAX_ONLY_CASES])
+def test_bwd_softmax_branches_alone(name, wl, out_dt, impl):
+    """With the memory's mix weight 0 and peaked queries (q x 8, so the
+    softmax Jacobian term dS carries weight), dq, dk and dv each come only from
+    the softmax-branch backward and are compared with the float64 gradient of
+    exact attention; the memory's own gradients (da, db, dS0) are exactly 0."""
+    print(f"case {name}: B={wl.B} H={wl.H} T={wl.T} P={wl.P} d={wl.d} {wl.dtype}->{out_dt} impl={impl}",
+          flush=True)
+    x = I.make_clip(wl, q_scale=8.0)
+    x["w"] = _softmax_only_weights(wl.H)
+    cfg = H.make_config(wl, out_dtype=out_dt, impl=impl)
+    dev = H.to_device(x, wl.dtype)
+    S0_t = torch.from_numpy(_start_state(wl)).cuda()
+    fwd = H.hlta_fwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], S0=S0_t)
+    g = I.upstream_grad(wl, out_dt)
+    g_t = torch.from_numpy(g).cuda().to(torch.bfloat16 if out_dt == "bf16" else torch.float32)
+    got = H.hlta_bwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], fwd, g_t, S0=S0_t)
+    torch.cuda.synchronize()
+    ref = _softmax_oracle_grads(wl, x, g)
+    mfma = _mfma(wl, out_dt, impl)
+    tol = TOL["bf16"] if mfma else TOL["f32"]
+    for n in ("dq", "dk", "dv"):
+        gv_ = to64(got[n])
+        for h in range(wl.H):
+            e = O.rel_l2(gv_[:, :, h], ref[n][:, :, h])
+            print(f"{name} {n} head {h} (w = {x['w'][h].tolist()}) {e:.2e}", flush=True)
+            assert e <= tol, f"{name} {n} head {h}: rel-L2 {e:.3e} > {tol:.0e}"
+    for n in ("da", "db", "dS0"):
+        assert torch.count_nonzero(got[n]).item() == 0, n
+
+
+@pytest.mark.slow
+def test_full_size_backward_softmax_branches_alone():
+    """hlta_bwd at 480P / 31 frames (all 24 heads) with the memory's mix weight
+    0 and SWA, DSWA weighted (1, 1): dq, dk, dv of one whole head against the
+    float64 gradient of exact attention over both branches."""
+    wl = I.P480_T31
+    print(f"generating {wl.name}, memory weight 0", flush=True)
+    x = I.make_clip(wl, q_scale=8.0, threads=16)
+    x["w"] = np.tile(np.array([[1.0, 1.0, 0.0]], np.float32), (wl.H, 1))
+    g = I.upstream_grad(wl, "bf16")
+    dev = H.to_device(x, wl.dtype)
+    cfg = H.make_config(wl)
+    fwd = H.hlta_fwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"])
+    g_t = torch.from_numpy(g).cuda().to(torch.bfloat16)
+    got = H.hlta_bwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], fwd, g_t)
+    torch.cuda.synchronize()
+    print("GPU backward done; oracle on one head", flush=True)
+    b, h = 0, 11
+    q, k, v = x["q"][b, :, h], x["k"][b, :, h], x["v"][b, :, h]
+    gh = g[b, :, h].astype(np.float64)
+    ref = {n: np.zeros(q.shape) for n in ("dq", "dk", "dv")}
+    for fo in (lambda f: O.swa_frames(f, wl.swa_frames), lambda f: O.dswa_frames(f, wl.dswa_dilation, wl.dswa_taps)):
+        for n, r in zip(("dq", "dk", "dv"), O.attention_backward(q, k, v, gh, wl.T, wl.P, fo)):
+            ref[n] += r
+    for n in ("dq", "dk", "dv"):
+        err = O.rel_l2(to64(got[n][b, :, h]), ref[n])
+        print(f"{wl.name} softmax-only backward (b={b}, h={h}) {n} {err:.2e}", flush=True)
+        assert err <= TOL["bf16"], f"{n}: {err:.3e}"

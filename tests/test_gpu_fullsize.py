@@ -10,7 +10,7 @@ import torch
 from hybrid_linear_temporal_amd import hlta as H
 from hybrid_linear_temporal_amd import inputs as I
 from oracle import hlta_oracle as O
-from tests.helpers import TOL, to64
+from tests.helpers import BRANCHES as BRANCH_NAMES, TOL, to64
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -58,46 +58,89 @@ def test_full_size_sampled(wl):
         _check_head(wl, x, res, b, h, frames, wl.name)
 
 
-def test_stream_full_size_sampled():
-    """8 rollouts of 480P frames: a 16-frame prefix through hlta_fwd, then
-    frame steps; sampled (rollout, head) pairs against the streaming oracle."""
+def _fill_sampled(wl, T, stream, pairs, gen):
+    """Device inputs [B, T*P, H, d] of a streaming workload: the sampled (rollout,
+    head) pairs from the seeded NumPy generator (returned too, for the oracle),
+    every other pair from torch's seeded GPU generator with the same recipe.
+    Rollouts and heads are independent, so the others only have to fill the
+    launch configuration."""
+    B, L, Hh, d = wl.B, T * wl.P, wl.H, wl.d
+    dev = {}
+    for n in ("q", "k"):
+        x = torch.randn((B, L, Hh, d), generator=gen, device="cuda")
+        dev[n] = (x / x.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    dev["v"] = torch.randn((B, L, Hh, d), generator=gen, device="cuda").to(torch.bfloat16)
+    dev["a"] = 0.9 + 0.099 * torch.rand((B, L, Hh), generator=gen, device="cuda")
+    dev["b"] = torch.sigmoid(torch.randn((B, L, Hh), generator=gen, device="cuda"))
+    dev["w"] = torch.from_numpy(I.mix_weights(wl.seed, Hh)).cuda()
+    host = {}
+    for b, h in pairs:
+        q, k, v = I.head_qkv(wl.seed, stream, b, h, L, d, wl.dtype)
+        a, bb = I.head_gates(wl.seed, stream, b, h, L)
+        host[b, h] = dict(q=q, k=k, v=v, a=a, b=bb)
+        for n, arr in host[b, h].items():
+            t = torch.from_numpy(arr).cuda()
+            dev[n][b, :, h] = t.to(dev[n].dtype)
+    return dev, host
+
+
+def test_stream_full_size_all_steps():
+    """8 rollouts of 480P frames, the whole 64-step rollout: a 16-frame prefix
+    through hlta_fwd, then 64 committed frame steps at full size (all 8
+    rollouts, all 24 heads). Three sampled (rollout, head) pairs follow a
+    float64 stream each: o_gdn on every step, all four outputs on every 8th
+    step and the last, and the carried state after step 64."""
     wl = I.STREAM_P480
-    P, R, prefix, steps = wl.P, wl.ring_frames, wl.prefix_frames, 3
+    P, R, prefix, steps = wl.P, wl.ring_frames, wl.prefix_frames, wl.steps
+    pairs = ((0, 0), (3, 11), (wl.B - 1, wl.H - 1))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.seed)
     pre_wl = I.Workload("stream_prefix", B=wl.B, H=wl.H, T=prefix, P=P, d=wl.d, swa_frames=wl.swa_frames,
                         dswa_dilation=wl.dswa_dilation, dswa_taps=wl.dswa_taps, gdn_chunk=wl.gdn_chunk,
                         dtype=wl.dtype, seed=wl.seed)
-    print("generating stream prefix", flush=True)
-    xp = I.make_clip(pre_wl, stream=I.S_PREFIX, threads=16)
-    dev = H.to_device(xp, wl.dtype)
-    cfg_pre = H.make_config(pre_wl)
+    print("stream prefix (16 frames, 8 rollouts) through hlta_fwd", flush=True)
+    dev, host = _fill_sampled(wl, prefix, I.S_PREFIX, pairs, gen)
     S_pre = torch.empty((wl.B, wl.H, wl.d, wl.d), dtype=torch.float32, device="cuda")
-    H.hlta_fwd(cfg_pre, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], S_out=S_pre)
+    H.hlta_fwd(H.make_config(pre_wl), dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], S_out=S_pre)
     st = H.Stream(H.make_config(wl), R)
     H.hlta_stream_load_prefix(st, dev["k"], dev["v"], prefix, S_pre)
+    torch.cuda.synchronize()
     del dev
-    pairs = ((0, 0), (wl.B - 1, wl.H - 1))
+    w = I.mix_weights(wl.seed, wl.H)
     ost = {}
     for b, h in pairs:
-        _, Sp = O.gdn_chunked(xp["q"][b, :, h], xp["k"][b, :, h], xp["v"][b, :, h], xp["a"][b, :, h],
-                              xp["b"][b, :, h], wl.gdn_chunk)
+        x = host[b, h]
+        _, Sp = O.gdn_chunked(x["q"], x["k"], x["v"], x["a"], x["b"], wl.gdn_chunk)
         s = O.StreamHead(P, wl.swa_frames, wl.dswa_dilation, wl.dswa_taps, wl.gdn_chunk)
-        s.load_prefix(xp["k"][b, :, h], xp["v"][b, :, h], prefix, Sp)
+        s.load_prefix(x["k"], x["v"], prefix, Sp)
         ost[b, h] = s
     for s_i in range(steps):
-        xs = I.stream_step_inputs(wl, s_i, threads=16)
-        d = H.to_device(xs, wl.dtype)
-        got = H.hlta_step_frame(st, d["q"], d["k"], d["v"], d["a"], d["b"], d["w"])
+        dev, host = _fill_sampled(wl, 1, I.S_STEP0 + s_i, pairs, gen)
+        got = H.hlta_step_frame(st, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"])
         torch.cuda.synchronize()
+        full_check = s_i % 8 == 0 or s_i == steps - 1
         for b, h in pairs:
-            refs = ost[b, h].step(xs["q"][b, :, h], xs["k"][b, :, h], xs["v"][b, :, h], xs["a"][b, :, h],
-                                  xs["b"][b, :, h], xs["w"][h])
-            for name, ref in zip(("o_swa", "o_dswa", "o_gdn", "o_mix"), refs):
+            x, s = host[b, h], ost[b, h]
+            f = s.f
+            if full_check:
+                refs = s.step(x["q"], x["k"], x["v"], x["a"], x["b"], w[h])
+                names = BRANCH_NAMES
+            else:
+                # the memory only: advance the float64 stream exactly as its
+                # step does (the keys of frame f join its store unrotated)
+                o_gdn, S = O.gdn_chunked(x["q"], x["k"], x["v"], x["a"], x["b"], wl.gdn_chunk, s.S0)
+                s.k[f], s.v[f] = np.asarray(x["k"], np.float64), np.asarray(x["v"], np.float64)
+                s.S0, s.f = S, f + 1
+                refs, names = (o_gdn,), ("o_gdn",)
+            for name, ref in zip(names, refs):
                 err = O.rel_l2(to64(got[name][b, :, h]), ref)
-                print(f"stream step {s_i} (b={b}, h={h}) {name} {err:.2e}", flush=True)
-                assert err <= TOL["bf16"], f"step {s_i} {name}: {err:.3e}"
+                print(f"stream step {s_i} (frame {f}, b={b}, h={h}) {name} {err:.2e}", flush=True)
+                assert err <= TOL["bf16"], f"step {s_i} (b={b}, h={h}) {name}: {err:.3e}"
+    assert st.frames_done == prefix + steps
     for b, h in pairs:
         err = O.rel_l2(to64(st.S[b, h]), ost[b, h].S0)
-        assert err <= TOL["bf16"], f"stream state {err:.3e}"
+        print(f"stream state after {steps} steps (b={b}, h={h}) {err:.2e}", flush=True)
+        assert err <= TOL["bf16"], f"stream state (b={b}, h={h}) {err:.3e}"
 
 
 def test_full_size_rope_and_fp8_sampled():

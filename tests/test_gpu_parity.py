@@ -335,3 +335,36 @@ def test_gdn_without_l2norm(dtype, C):
         eS = O.rel_l2(to64(got["S_out"][0, h]), S_ref)
         print(f"{wl.name} h={h} o_gdn {e:.2e} S_out {eS:.2e}", flush=True)
         assert e <= TOL[dtype] and eS <= TOL[dtype]
+
+
+NONUNIT_CASES = [
+    # the chunk-64 MFMA memory kernels (bf16, d = 128), ragged last chunk, (b, h) pairs not a multiple of 8
+    (small("nonunit_mfma", B=2, H=3, T=7, P=70, d=128, swa_frames=3, dswa_dilation=2, dswa_taps=3, gdn_chunk=64,
+           dtype="bf16", seed=2120), H.HLTA_IMPL_AUTO),
+    # the generic memory kernels on the same bf16 inputs, and on float32 with another chunk length
+    (small("nonunit_generic_bf16", B=2, H=3, T=7, P=70, d=128, swa_frames=3, dswa_dilation=2, dswa_taps=3,
+           gdn_chunk=64, dtype="bf16", seed=2120), H.HLTA_IMPL_GENERIC),
+    (small("nonunit_generic_f32", B=1, H=2, T=9, P=30, d=64, swa_frames=2, dswa_dilation=2, dswa_taps=2,
+           gdn_chunk=32, seed=2121), H.HLTA_IMPL_AUTO),
+]
+
+
+@pytest.mark.parametrize("wl,impl", NONUNIT_CASES, ids=lambda c: getattr(c, "name", str(c)))
+def test_memory_normalises_nonunit_keys(wl, impl):
+    """q and k rows of norm ~U[0.3, 3] per (token, head) with the in-op L2
+    normalisation on: the memory must normalise both before every use (the
+    Gram matrices, the write and the state update), so o_gdn and S_out match
+    the float64 token recurrence, and every branch matches the oracle."""
+    from tests.helpers import rescale_qk
+    print(f"case {wl.name} impl={impl}", flush=True)
+    x = rescale_qk(I.make_clip(wl), wl.dtype, seed=wl.seed)
+    kn = np.linalg.norm(x["k"], axis=-1)
+    assert kn.min() < 0.5 and kn.max() > 2.5   # the normalisation matters
+    S0 = (0.1 * np.random.default_rng(wl.seed).standard_normal((wl.B, wl.H, wl.d, wl.d))).astype(np.float32)
+    got = run_gpu(wl, x, impl=impl, S0=S0)
+    ref = run_oracle(wl, x, S0=S0, gdn="recurrent")
+    compare(got, ref, TOL[wl.dtype], label=f"{wl.name} impl={impl}")
+    # without the normalisation the memory's result is far from it
+    o_raw, _ = O.gdn_recurrent(x["q"][0, :, 0], x["k"][0, :, 0], x["v"][0, :, 0], x["a"][0, :, 0], x["b"][0, :, 0],
+                               S0[0, 0], l2norm=False)
+    assert O.rel_l2(to64(got["o_gdn"][0, :, 0]), o_raw) > 0.1

@@ -7,7 +7,7 @@ import torch
 from hybrid_linear_temporal_amd import hlta as H
 from hybrid_linear_temporal_amd import inputs as I
 from oracle import hlta_oracle as O
-from tests.helpers import BRANCHES, TOL, small, to64
+from tests.helpers import BRANCHES, TOL, rescale_qk, small, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -28,13 +28,20 @@ STREAM_CASES = [
     (small("stream_f32", B=2, H=2, T=14, P=20, d=32, swa_frames=2, dswa_dilation=2, dswa_taps=2,
            gdn_chunk=16, dtype="f32", seed=3001), 3, 5),
 ]
+# q and k rows of norm ~U[0.3, 3]: the memory's in-op L2 normalisation on the
+# streaming path (MFMA memory kernels, 70 tokens per frame = one full and one
+# ragged chunk per step)
+NONUNIT_STREAM = (small("stream_bf16_nonunit", B=2, H=2, T=20, P=70, d=128, swa_frames=3, dswa_dilation=4,
+                        dswa_taps=4, gdn_chunk=64, dtype="bf16", seed=3002), 16, 16)
 
 
-@pytest.mark.parametrize("wl,prefix,R", STREAM_CASES, ids=lambda c: getattr(c, "name", str(c)))
+@pytest.mark.parametrize("wl,prefix,R", STREAM_CASES + [NONUNIT_STREAM], ids=lambda c: getattr(c, "name", str(c)))
 def test_stream_steps_match_oracle_and_full_forward(wl, prefix, R):
     """Prefix through hlta_fwd, then one hlta_step_frame per remaining frame
     (with an uncommitted evaluation before each committed one)."""
     x = I.make_clip(wl)
+    if wl.name.endswith("_nonunit"):
+        x = rescale_qk(x, wl.dtype, seed=wl.seed)
     P = wl.P
     tol = TOL[wl.dtype]
     dev = H.to_device(x, wl.dtype)

@@ -380,6 +380,18 @@ def test_inputs_recipe():
 # rotary embedding of the softmax branches (optional)
 # ---------------------------------------------------------------------------
 
+def test_rope_positions_by_hand():
+    """Token positions of two 2 x 3 latent frames starting at frame 5, written
+    out by hand: raster order, row = p // 3 (3 columns per row), column =
+    p % 3. The grid is not square, so exchanging rows and columns, or taking
+    the frame from the wrong counter, changes the table."""
+    want = [(5, 0, 0), (5, 0, 1), (5, 0, 2), (5, 1, 0), (5, 1, 1), (5, 1, 2),
+            (6, 0, 0), (6, 0, 1), (6, 0, 2), (6, 1, 0), (6, 1, 1), (6, 1, 2)]
+    np.testing.assert_array_equal(O.rope_positions(2, 6, 3, f0=5), np.array(want, np.float64))
+    # one 4 x 2 frame: token 5 sits in row 2, column 1
+    np.testing.assert_array_equal(O.rope_positions(1, 8, 2)[5], [0.0, 2.0, 1.0])
+
+
 def test_rope_values_by_hand():
     """d = 32: pairs 0-3 follow the frame, 4-9 the row, 10-15 the column;
     pair j of an axis with n pairs turns by pos * 10000^(-j/n). Unit vectors
