@@ -1,7 +1,10 @@
-// C-ABI entry points that launch work: hlta_fwd, hlta_gdn_fwd, hlta_attn_fwd,
-// the FP8 pair, hlta_bwd, hlta_stream_load_prefix, hlta_step_frame(_rollouts).
-// Validation happens on the host before any launch; the library allocates no
-// device memory (scratch is the caller's workspace).
+// C-ABI entry points that launch work: hlta_fwd (and its allocation-free
+// variant hlta_fwd_noalloc), hlta_gdn_fwd, hlta_attn_fwd, the FP8 pair,
+// hlta_bwd, hlta_stream_load_prefix, hlta_step_frame(_rollouts). Validation
+// happens on the host before any launch; the library allocates no device
+// memory (scratch is the caller's workspace, or for hlta_fwd_noalloc a fixed
+// device array).
+#include <mutex>
 #include <string>
 
 #include "hlta_device.h"
@@ -155,6 +158,41 @@ hlta_status check_workspace(const Plan& plan, const void* workspace, size_t ws_b
 
 size_t state_bytes(const hlta_config* cfg) { return size_t(cfg->B) * cfg->H * cfg->d * cfg->d * sizeof(float); }
 
+hlta_status fwd_body(const hlta_config* cfg, const Plan& plan, const void* q, const void* k, const void* v,
+                     const float* a, const float* b, const float* mix_w, const float* S0, void* o_swa,
+                     void* o_dswa, void* o_gdn, void* o_mix, float* S_out, void* workspace, size_t ws_bytes,
+                     hipStream_t st);
+
+// Scratch of hlta_fwd_noalloc: a fixed device array, one copy per GPU, held
+// until the process ends. Host code never passes the array's name to a kernel
+// (on the host it is only a stand-in for the symbol): the device address of
+// each GPU's copy is looked up once, with that device current, and kept.
+constexpr size_t kScratchBytes = HLTA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on first use).
+hlta_status device_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(HLTA_E_UNSUPPORTED, "device " + std::to_string(dev) + " is beyond the " +
+                                        std::to_string(kMaxDevices) + " devices the scratch table holds");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "scratch address lookup");
+    if (!ptr) return fail(HLTA_E_HIP, "scratch address lookup returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return HLTA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -166,9 +204,39 @@ hlta_status hlta_fwd(const hlta_config* cfg, const void* q, const void* k, const
   Plan plan;
   HLTA_TRY(check_config(cfg));
   HLTA_TRY(make_plan(cfg, int64_t(cfg->T) * cfg->P, &plan));
+  return fwd_body(cfg, plan, q, k, v, a, b, mix_w, S0, o_swa, o_dswa, o_gdn, o_mix, S_out, workspace, ws_bytes,
+                  static_cast<hipStream_t>(stream));
+}
+
+hlta_status hlta_fwd_noalloc(const hlta_config* cfg, const void* q, const void* k, const void* v, const float* a,
+                             const float* b, const float* mix_w, const float* S0, void* o_swa, void* o_dswa,
+                             void* o_gdn, void* o_mix, float* S_out, void* stream) {
+  clear_error();
+  Plan plan;
+  HLTA_TRY(check_config(cfg));
+  HLTA_TRY(make_plan(cfg, int64_t(cfg->T) * cfg->P, &plan));
+  if (plan.ws_total > kScratchBytes)
+    return fail(HLTA_E_WORKSPACE, "this call needs " + std::to_string(plan.ws_total) +
+                                      " bytes of scratch; the allocation-free entry point holds at most " +
+                                      std::to_string(kScratchBytes) + " (use hlta_fwd with a workspace)");
+  void* scratch_ptr = nullptr;
+  if (plan.L > 0 && plan.ws_total > 0) HLTA_TRY(device_scratch(&scratch_ptr));
+  return fwd_body(cfg, plan, q, k, v, a, b, mix_w, S0, o_swa, o_dswa, o_gdn, o_mix, S_out, scratch_ptr,
+                  kScratchBytes, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// hlta_fwd after the config is checked and planned: argument checks, then the
+// launches (shared by hlta_fwd and hlta_fwd_noalloc).
+hlta_status fwd_body(const hlta_config* cfg, const Plan& plan, const void* q, const void* k, const void* v,
+                     const float* a, const float* b, const float* mix_w, const float* S0, void* o_swa,
+                     void* o_dswa, void* o_gdn, void* o_mix, float* S_out, void* workspace, size_t ws_bytes,
+                     hipStream_t st) {
   HLTA_TRY(maybe(S0, "S0"));
   HLTA_TRY(maybe(S_out, "S_out"));
-  hipStream_t st = static_cast<hipStream_t>(stream);
   if (plan.L == 0) {
     // empty clip: the state passes through unchanged
     if (S_out && S_out != S0) {
@@ -185,6 +253,10 @@ hlta_status hlta_fwd(const hlta_config* cfg, const void* q, const void* k, const
   AttnParams at = full_attn_params(cfg, q, k, v, o_swa, o_dswa);
   return run_layer(cfg, plan, q, k, v, a, b, S0, S_out, o_gdn, mix_w, o_mix, workspace, at, st);
 }
+
+}  // namespace
+
+extern "C" {
 
 hlta_status hlta_gdn_fwd(const hlta_config* cfg, const void* q, const void* k, const void* v, const float* a,
                          const float* b, const float* S0, void* o_gdn, float* S_out, void* workspace,

@@ -28,7 +28,7 @@ EXPORTS = ("hlta_abi_version", "hlta_status_string", "hlta_last_error", "hlta_va
            "hlta_fwd_workspace_bytes", "hlta_fwd", "hlta_gdn_fwd", "hlta_attn_fwd", "hlta_stream_ring_bytes",
            "hlta_stream_load_prefix", "hlta_step_workspace_bytes", "hlta_step_frame",
            "hlta_step_frame_rollouts", "hlta_quantize_fp8", "hlta_attn_fwd_fp8", "hlta_bwd_workspace_bytes",
-           "hlta_bwd")
+           "hlta_bwd", "hlta_fwd_noalloc")
 
 
 class hlta_config(ctypes.Structure):
@@ -73,6 +73,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "hlta_validate_config": (I32, [cfgp]),
         "hlta_fwd_workspace_bytes": (S, [cfgp]),
         "hlta_fwd": (I32, [cfgp, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]),
+        "hlta_fwd_noalloc": (I32, [cfgp, P, P, P, P, P, P, P, P, P, P, P, P, P]),
         "hlta_gdn_fwd": (I32, [cfgp, P, P, P, P, P, P, P, P, P, S, P]),
         "hlta_attn_fwd": (I32, [cfgp, P, P, P, P, P, P, P, P, P]),
         "hlta_stream_ring_bytes": (S, [cfgp, I32]),
@@ -170,6 +171,20 @@ def hlta_fwd(cfg: hlta_config, q, k, v, a, b, mix_w, S0=None, out=None, S_out=No
     _check(lib.hlta_fwd(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(mix_w), _ptr(S0),
                         _ptr(out["o_swa"]), _ptr(out["o_dswa"]), _ptr(out["o_gdn"]), _ptr(out["o_mix"]),
                         _ptr(S_out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    res = dict(out)
+    res["S_out"] = S_out
+    return res
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # HLTA_NOALLOC_SCRATCH_BYTES
+
+
+def hlta_fwd_noalloc(cfg: hlta_config, q, k, v, a, b, mix_w, out: dict, S0=None, S_out=None, stream=None) -> dict:
+    """HLTA forward on the library's fixed per-GPU scratch (C: hlta_fwd_noalloc);
+    out holds the four preallocated outputs."""
+    _check(load_library().hlta_fwd_noalloc(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                           _ptr(mix_w), _ptr(S0), _ptr(out["o_swa"]), _ptr(out["o_dswa"]),
+                                           _ptr(out["o_gdn"]), _ptr(out["o_mix"]), _ptr(S_out), _stream(stream)))
     res = dict(out)
     res["S_out"] = S_out
     return res

@@ -158,6 +158,30 @@ hlta_status hlta_fwd(const hlta_config* cfg,
                      void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * hlta_fwd_noalloc - hlta_fwd without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation. It calls no allocating routine; its
+ * scratch is a fixed device array of HLTA_NOALLOC_SCRATCH_BYTES per GPU,
+ * reserved when the library's code is loaded on that GPU and held until the
+ * process ends. Results equal hlta_fwd's bit for bit (the same kernels).
+ *
+ * A call whose hlta_fwd_workspace_bytes(cfg) exceeds the array returns
+ * HLTA_E_WORKSPACE before anything is launched. Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (different streams, or
+ * different host threads) race on it and must be ordered by the caller. The
+ * array keeps the last call's contents; a call reads only scratch it has
+ * written itself. The stream must belong to the current device. Other
+ * arguments and errors as in hlta_fwd.
+ */
+#define HLTA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+hlta_status hlta_fwd_noalloc(const hlta_config* cfg,
+                             const void* q, const void* k, const void* v,
+                             const float* a, const float* b, const float* mix_w,
+                             const float* S0,
+                             void* o_swa, void* o_dswa, void* o_gdn, void* o_mix,
+                             float* S_out, void* stream);
+
+/*
  * hlta_gdn_fwd - the memory branch alone: o_gdn and S_out exactly as hlta_fwd
  * computes them (the gated delta rule of the Kairos related-work page, row A,
  * and of the long-context page, section 06). Arguments as in hlta_fwd.
