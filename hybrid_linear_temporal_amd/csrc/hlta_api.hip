@@ -64,8 +64,7 @@ hlta_status run_gdn(const hlta_config* cfg, const Plan& plan, const void* q, con
   g.S_out = S_out;
   g.o = o_gdn;
   g.ws = static_cast<unsigned char*>(workspace);
-  g.rec_bytes = plan.gdn == Impl::Mfma ? gdn_mfma_record_bytes(cfg->gdn_chunk, cfg->d)
-                                       : gdn_generic_record_bytes(cfg->gdn_chunk, cfg->d);
+  g.rec_bytes = plan.gdn == Impl::Mfma ? 0 : gdn_generic_record_bytes(cfg->gdn_chunk, cfg->d);
   g.B = cfg->B;
   g.H = cfg->H;
   g.L = plan.L;
@@ -73,7 +72,7 @@ hlta_status run_gdn(const hlta_config* cfg, const Plan& plan, const void* q, con
   g.l2norm = cfg->gdn_l2norm_qk;
   g.gate_logits = cfg->gate_logits;
   hipError_t e = plan.gdn == Impl::Mfma
-                     ? launch_gdn_mfma(g, cfg->out_dtype, st)
+                     ? launch_gdn_seg(g, plan.gdn_G, plan.gdn_seg_chunks, workspace, cfg->out_dtype, st)
                      : launch_gdn_generic(g, cfg->d, cfg->gdn_chunk, cfg->in_dtype, cfg->out_dtype, st);
   if (e != hipSuccess) return hip_fail(e, "gated delta rule launch");
   return HLTA_OK;

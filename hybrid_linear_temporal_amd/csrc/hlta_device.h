@@ -79,9 +79,8 @@ __device__ __forceinline__ const T* key_frame_ptr(const T* main, const T* ring, 
 // and b, from the given gates or, with logits, from log sigmoid(x_a) and
 // sigmoid(x_b); log sigmoid(x) = min(x, 0) - log1p(exp(-|x|)) has no
 // cancellation for either sign.
-__device__ __forceinline__ void load_gates(const float* a, const float* b, size_t i, int logits, float floor_log_a,
-                                           float& la, float& bi) {
-  const float xa = a[i], xb = b[i];
+__device__ __forceinline__ void gate_values(float xa, float xb, int logits, float floor_log_a, float& la,
+                                            float& bi) {
   if (logits) {
     la = fmaxf(fminf(xa, 0.f) - log1pf(expf(-fabsf(xa))), floor_log_a);
     bi = 1.f / (1.f + expf(-xb));
@@ -89,6 +88,10 @@ __device__ __forceinline__ void load_gates(const float* a, const float* b, size_
     la = fmaxf(logf(xa), floor_log_a);
     bi = xb;
   }
+}
+__device__ __forceinline__ void load_gates(const float* a, const float* b, size_t i, int logits, float floor_log_a,
+                                           float& la, float& bi) {
+  gate_values(a[i], b[i], logits, floor_log_a, la, bi);
 }
 
 // Frame sets of query frame f (absolute): SWA reads frames f-nswa+1 .. f,

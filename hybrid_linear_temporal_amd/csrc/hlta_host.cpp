@@ -82,8 +82,22 @@ size_t gdn_generic_record_bytes(int C, int d) {
   return align_up(sizeof(float) * (4 * size_t(C) * d + size_t(C) * C + 1), 256);
 }
 
-size_t gdn_mfma_record_bytes(int C, int d) {
-  return (C == int(GdnMfmaRec::C) && d == int(GdnMfmaRec::D)) ? GdnMfmaRec::BYTES : 0;
+// one record per chunk: T'' and T' as six 1 KB operand tiles each, then 3 x 64 fp32 per-token values
+size_t gdn_seg_record_bytes(int B, int H, long long n_chunks) { return size_t(B) * H * size_t(n_chunks) * 13056; }
+
+size_t gdn_seg_map_bytes(int B, int H, int G, int d) {
+  return G > 1 ? size_t(B) * H * (2 * size_t(G) - 1) * d * d * sizeof(float) : 0;
+}
+
+// Segments per (batch row, head) for the MFMA memory kernels: enough that the
+// passes fill two workgroups on each of the 256 compute units, with at least
+// four chunks per segment; one segment when the heads alone fill the chip.
+static void gdn_segments(int64_t bh, int64_t n_chunks, int* G, int* seg_chunks) {
+  int64_t g = 1;
+  if (bh < 128) g = std::max<int64_t>(1, std::min<int64_t>(512 / bh, n_chunks / 4));
+  const int64_t s = n_chunks > 0 ? (n_chunks + g - 1) / g : 1;
+  *seg_chunks = int(s);
+  *G = n_chunks > 0 ? int((n_chunks + s - 1) / s) : 1;
 }
 
 hlta_status make_plan(const hlta_config* cfg, int64_t L, Plan* plan) {
@@ -108,11 +122,21 @@ hlta_status make_plan(const hlta_config* cfg, int64_t L, Plan* plan) {
       p.attn = ma ? Impl::Mfma : Impl::Generic;
       p.gdn = mg ? Impl::Mfma : Impl::Generic;
   }
-  const size_t rec = p.gdn == Impl::Mfma ? gdn_mfma_record_bytes(cfg->gdn_chunk, cfg->d)
-                                         : gdn_generic_record_bytes(cfg->gdn_chunk, cfg->d);
-  int64_t nrec = 0;
-  if (!mul_ok(int64_t(cfg->B) * cfg->H, p.n_chunks, &nrec)) return fail(HLTA_E_SHAPE, "workspace overflow");
-  p.ws_gdn = size_t(nrec) * rec;
+  // the MFMA memory kernels address one batch row of q, k, v and the outputs
+  // with 32-bit offsets
+  if (p.gdn == Impl::Mfma && L * int64_t(cfg->H) * cfg->d * 4 > int64_t(0xFFFFFFFF)) {
+    if (cfg->impl == HLTA_IMPL_MFMA)
+      return fail(HLTA_E_UNSUPPORTED, "the MFMA memory kernels need L*H*d*4 < 2^32 bytes per batch row");
+    p.gdn = Impl::Generic;
+  }
+  if (p.gdn == Impl::Mfma) {
+    gdn_segments(int64_t(cfg->B) * cfg->H, p.n_chunks, &p.gdn_G, &p.gdn_seg_chunks);
+    p.ws_gdn = gdn_seg_record_bytes(cfg->B, cfg->H, p.n_chunks) + gdn_seg_map_bytes(cfg->B, cfg->H, p.gdn_G, cfg->d);
+  } else {
+    int64_t nrec = 0;
+    if (!mul_ok(int64_t(cfg->B) * cfg->H, p.n_chunks, &nrec)) return fail(HLTA_E_SHAPE, "workspace overflow");
+    p.ws_gdn = size_t(nrec) * gdn_generic_record_bytes(cfg->gdn_chunk, cfg->d);
+  }
   p.ws_total = p.ws_gdn;
   if (cfg->rope_theta > 0.f) {
     // rotated q and k of the softmax branches, [B, L, H, d] in_dtype each

@@ -20,6 +20,8 @@ struct Plan {
   int64_t L = 0;            // tokens per batch row in this call
   int64_t n_chunks = 0;     // ceil(L / C)
   size_t ws_gdn = 0;        // bytes of GDN scratch
+  int gdn_G = 1;            // MFMA memory: segments per (batch row, head) run side by side
+  int gdn_seg_chunks = 0;   //   and chunks per segment (the last may have fewer)
   size_t ws_rope_off = 0;   // rotated q, then rotated k (rotary embedding on), each ws_rope_bytes
   size_t ws_rope_bytes = 0;
   size_t ws_total = 0;      // bytes the caller must supply
@@ -61,24 +63,13 @@ bool mfma_gdn_supported(const hlta_config* cfg);
 // Per-chunk record sizes of the GDN scratch (in bytes).
 size_t gdn_generic_record_bytes(int C, int d);
 
-// Record of one chunk for the MFMA gated-delta-rule kernels (C = 64, d = 128):
-//   Wn   bf16 [C][d]  -W = -T diag(b gamma) K^   (row per token)
-//   UpT  bf16 [d][C]  U'^T = (T diag(b) V)^T     (row per value channel)
-//   Aqk  bf16 [C][C]  exp(g_i - g_j) q^_i.k^_j, j <= i
-//   sq   f32  [C]     gamma_i / ||q_i||          (scales rows of Q S^T)
-//   sk   f32  [C]     gamma_C / (gamma_i ||k_i||) (scales rows of U in the state update)
-//   gC   f32          gamma_C
-struct GdnMfmaRec {
-  static constexpr size_t C = 64, D = 128;
-  static constexpr size_t WN = 0;
-  static constexpr size_t UPT = WN + 2 * C * D;
-  static constexpr size_t AQK = UPT + 2 * D * C;
-  static constexpr size_t SQ = AQK + 2 * C * C;
-  static constexpr size_t SK = SQ + 4 * C;
-  static constexpr size_t GC = SK + 4 * C;
-  static constexpr size_t BYTES = (GC + 16 + 255) / 256 * 256;
-};
-size_t gdn_mfma_record_bytes(int C, int d);
+// Scratch of the MFMA memory kernels: one 6 KB record per chunk (the chunk's
+// T'' = T diag(b) in bf16 operand order), then, when G > 1, the segment maps:
+// 2G - 1 d x d fp32 matrices per (batch row, head) (per segment but the last
+// its N and M, and a copy of the start state).
+size_t gdn_seg_record_bytes(int B, int H, long long n_chunks);
+size_t gdn_seg_map_bytes(int B, int H, int G, int d);
+
 
 // 16-byte alignment check of a device pointer (NULL passes; checked elsewhere).
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

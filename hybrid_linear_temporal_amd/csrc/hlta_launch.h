@@ -28,8 +28,10 @@ hipError_t launch_quantize_e4m3(const void* q, const void* k, const void* v, voi
 
 // Gated delta rule, chunked form, fp32 arithmetic (any supported d, C, dtype).
 hipError_t launch_gdn_generic(const GdnParams& p, int d, int C, int in_dt, int out_dt, hipStream_t st);
-// Gated delta rule, chunked form with bf16 MFMA (bf16 inputs, d = 128, C = 64).
-hipError_t launch_gdn_mfma(const GdnParams& p, int out_dt, hipStream_t st);
+// Gated delta rule, chunked form with bf16 MFMA (bf16 inputs, d = 128, C = 64),
+// G segments of seg_chunks chunks per (batch row, head) run side by side;
+// workspace: gdn_seg_record_bytes(B, H, n_chunks) + gdn_seg_map_bytes(B, H, G, 128) bytes.
+hipError_t launch_gdn_seg(const GdnParams& p, int G, int seg_chunks, void* workspace, int out_dt, hipStream_t st);
 
 // dst = src (src non-null) or dst = 0, bytes a multiple of 4; one kernel launch.
 hipError_t launch_copy_or_zero(void* dst, const void* src, size_t bytes, hipStream_t st);

@@ -79,8 +79,17 @@ def test_workspace_sizes(lib):
     cfg = _cfg()
     ws = H.hlta_fwd_workspace_bytes(cfg)
     assert ws > 0
+    # bf16, d = 128, chunk 64: a 13056-byte record per chunk, then the memory's
+    # segment maps, 2G - 1 fp32 d x d matrices per (batch row, head) for G
+    # segments side by side
     chunks = -(-cfg.T * cfg.P // cfg.gdn_chunk)
-    assert ws % (cfg.B * cfg.H * chunks) == 0
+    maps = ws - cfg.B * cfg.H * chunks * 13056
+    per = cfg.B * cfg.H * cfg.d * cfg.d * 4
+    assert maps > 0 and maps % per == 0 and (maps // per) % 2 == 1
+    # float32: the generic kernels' per-chunk records
+    f32 = H.make_config(I.TINY_F32)
+    chunks = -(-f32.T * f32.P // f32.gdn_chunk)
+    assert H.hlta_fwd_workspace_bytes(f32) % (f32.B * f32.H * chunks) == 0
     bad = _cfg(d=96)
     assert H.hlta_fwd_workspace_bytes(bad) == 0
     assert H.hlta_step_workspace_bytes(cfg) > 0
