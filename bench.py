@@ -88,6 +88,7 @@ def cpu_baseline(wl, budget_s=12.0):
     w = I.mix_weights(wl.seed, wl.H)
     done = []
     t_total = 0.0
+    cpu0 = os.times()
     for b in range(wl.B):
         for h in range(wl.H):
             q, k, v = I.head_qkv(wl.seed, I.S_CLIP, b, h, wl.L, wl.d, wl.dtype)
@@ -101,13 +102,45 @@ def cpu_baseline(wl, budget_s=12.0):
                 break
         if t_total >= budget_s:
             break
+    cpu1 = os.times()
     frac = len(done) / (wl.B * wl.H)
     blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
-    return {"value": wl.B * wl.L * frac / t_total, "unit": "tokens/s", "cores": int(max(blas) if blas else 1),
+    host = host_cpu()
+    busy = ((cpu1.user - cpu0.user) + (cpu1.system - cpu0.system)) / t_total
+    return {"value": wl.B * wl.L * frac / t_total, "unit": "tokens/s", "cores": host["cores"],
             "kind": "oracle",
             "sample": f"float64 oracle (SWA, DSWA, chunked GDN, mix) on {len(done)} of {wl.B * wl.H} "
-                      f"(batch, head) pairs of {wl.name}, {t_total:.1f} s; tokens/s scaled by that fraction; "
-                      f"host CPUs available: {len(os.sched_getaffinity(0))}"}
+                      f"(batch, head) pairs of {wl.name}, {t_total:.1f} s; tokens/s scaled by that fraction",
+            "cpu_model": host["model"], "logical_cpus": host["logical"],
+            "blas_threads": int(max(blas) if blas else 1), "busy_cores_avg": round(busy, 2)}
+
+
+def host_cpu():
+    """The host CPUs this process may run on: model name, physical cores
+    (distinct (package, core) pairs) and logical CPUs, from /proc/cpuinfo."""
+    allowed = os.sched_getaffinity(0)
+    model, cores, cpu, phys, core = "unknown", set(), None, None, None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f.read().splitlines() + [""]:
+                if not line.strip():
+                    if cpu in allowed:
+                        cores.add((phys, core if core is not None else cpu))
+                    cpu, phys, core = None, None, None
+                    continue
+                k, _, v = line.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "processor":
+                    cpu = int(v)
+                elif k == "physical id":
+                    phys = v
+                elif k == "core id":
+                    core = v
+                elif k == "model name" and model == "unknown":
+                    model = v
+    except OSError:
+        pass
+    return {"model": model, "cores": len(cores) or len(allowed), "logical": len(allowed)}
 
 
 def torch_recipe(shape, dtype, gen, device="cuda"):

@@ -23,10 +23,8 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-result",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# Per-file additions. The GDN state pass keeps its fp32 state in MFMA
-# accumulators that VALU code also scales and converts every chunk; the VGPR
-# form of MFMA keeps them out of the AGPR file (no copies back and forth).
-EXTRA = {"gdn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-file additions to the flags above (none at present).
+EXTRA: dict[str, list[str]] = {}
 
 
 def sources() -> list[str]:

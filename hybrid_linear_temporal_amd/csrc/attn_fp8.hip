@@ -30,7 +30,7 @@
 //    byte t byte u%8 of the 8 bytes addressed by lane 2t + u/8 (probed), so
 //    lane v of a 16-lane group addresses the key of byte t = v/2 and the
 //    columns 8(v%2) .. of its group's 16-column block.
-#include "hlta_device.h"
+#include "attn_mfma_tiles.h"
 #include "hlta_launch.h"
 
 namespace hlta {
@@ -39,152 +39,21 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v2i __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 typedef unsigned char u8;
 
-constexpr int D = 128;           // head dim (bytes per token row)
 constexpr int QT = 128;          // query rows per workgroup: 4 waves x 32
-constexpr int KT = 64;           // keys per tile
-constexpr int NT = 256;
-constexpr int kXcds = 8;
 constexpr float kLazy = 8.f;     // raise the running max only past this margin (log2 units); P <= 2^8 < 448
 constexpr int kScaleOne = 127;   // E8M0 block scale 2^0 of the MFMA
-
-struct Tile {
-  uint4 row[KT][8];
-};
-
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
-
-__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
-template <typename T>
-__device__ __forceinline__ const T* uni(const T* ptr) {
-  const unsigned long long u = reinterpret_cast<unsigned long long>(ptr);
-  const unsigned lo = __builtin_amdgcn_readfirstlane(unsigned(u));
-  const unsigned hi = __builtin_amdgcn_readfirstlane(unsigned(u >> 32));
-  return reinterpret_cast<const T*>((static_cast<unsigned long long>(hi) << 32) | lo);
-}
-
-// Key stream of one branch (frames g, g + step, ...), wave-uniform fields.
-struct KeyStream {
-  const u8* kmain;   // token 0 of frame 0, head h
-  const u8* vmain;
-  size_t fstride;    // bytes between frames: P*H*D
-  long long g;
-  int step, left, P, pk;
-  const u8* k0;
-  const u8* v0;
-  const u8* k1;
-  const u8* v1;
-  __device__ __forceinline__ void start(long long g_first, int step_, int nframes) {
-    g = g_first;
-    step = step_;
-    left = nframes - 1;
-    pk = 0;
-    if (nframes > 0) {
-      k0 = uni(kmain + size_t(g) * fstride);
-      v0 = uni(vmain + size_t(g) * fstride);
-    }
-    if (nframes > 1) {
-      k1 = uni(kmain + size_t(g + step) * fstride);
-      v1 = uni(vmain + size_t(g + step) * fstride);
-    } else {
-      k1 = k0;
-      v1 = v0;
-    }
-  }
-  __device__ __forceinline__ void advance() {
-    pk += KT;
-    if (pk >= P) {
-      pk -= P;
-      g += step;
-      --left;
-      k0 = k1;
-      v0 = v1;
-      if (left > 0) {
-        k1 = uni(kmain + size_t(g + step) * fstride);
-        v1 = uni(vmain + size_t(g + step) * fstride);
-      }
-    }
-  }
-};
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
-}
-
-// Direct loads of one tile: wave w moves rows 16w .. 16w+15, 8 rows (1 KB) per
-// instruction; lane i lands at chunk position i%8 of row 16w + 8j + i/8 and
-// loads the chunk the permutation puts there. Rows past the end re-read the
-// last valid row (finite codes; their scores are masked).
-__device__ __forceinline__ void issue_tile(Tile& Kd, Tile& Vd, const KeyStream& ks, int kleft,
-                                           const unsigned (&off)[2], size_t ts, int wave, int lane) {
-  if (ks.pk + KT <= ks.P && kleft >= KT) {
-    const unsigned bytes = unsigned(KT * ts);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(ks.k0 + size_t(ks.pk) * ts, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(ks.v0 + size_t(ks.pk) * ts, bytes);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r0 = 16 * wave + 8 * j;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(&Kd.row[r0][0]), 16,
-                                               off[j], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(&Vd.row[r0][0]), 16,
-                                               off[j], 0, 0, 0);
-    }
-    return;
-  }
-  const int split = ks.P - ks.pk;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r0 = 16 * wave + 8 * j;
-    const int row = r0 + (lane >> 3);
-    const int rr = row < kleft ? row : kleft - 1;
-    const int c = swz(row, lane & 7);
-    const size_t koff = rr < split ? size_t(ks.pk + rr) * ts : size_t(rr - split) * ts;
-    const u8* ksrc = (rr < split ? ks.k0 : ks.k1) + koff + c * 16;
-    const u8* vsrc = (rr < split ? ks.v0 : ks.v1) + koff + c * 16;
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(ksrc),
-                                     (__attribute__((address_space(3))) void*)(&Kd.row[r0][0]), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vsrc),
-                                     (__attribute__((address_space(3))) void*)(&Vd.row[r0][0]), 16, 0, 0);
-  }
-}
-
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
-
-__device__ __forceinline__ float max_xor32(float x) {
-  const unsigned xa = __builtin_bit_cast(unsigned, x);
-  const auto r = __builtin_amdgcn_permlane32_swap(xa, xa, false, false);
-  const unsigned r0 = r[0], r1 = r[1];
-  return fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
-}
-
-// LDS address of (lane part + constant part) inside a tile; the lane part is
-// provably below the tile size so the constant folds into the offset field.
-__device__ __forceinline__ const char* at(const Tile& t, int lane_off, int const_off) {
-  return reinterpret_cast<const char*>(&t) + (unsigned(lane_off) & unsigned(sizeof(Tile) - 1)) + const_off;
-}
 
 __device__ __forceinline__ f32x16 mfma8(const v8i& a, const v8i& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kScaleOne, 0, kScaleOne);
 }
 
-__device__ __forceinline__ void store4(bf16* p, const float* v) {
-  bf16x4 x = {static_cast<bf16>(v[0]), static_cast<bf16>(v[1]), static_cast<bf16>(v[2]), static_cast<bf16>(v[3])};
-  *reinterpret_cast<bf16x4*>(p) = x;
-}
-__device__ __forceinline__ void store4(float* p, const float* v) {
-  f32x4 x = {v[0], v[1], v[2], v[3]};
-  *reinterpret_cast<f32x4*>(p) = x;
-}
-
 template <typename Tout>
 __global__ void __launch_bounds__(NT, 2)
 attn_fp8_kernel(AttnParams p, const float* scales) {
-  __shared__ Tile sK0, sV0, sK1, sV1;
+  __shared__ Tile8 sK0, sV0, sK1, sV1;
   const int tid = threadIdx.x;
   const int wave = uni(tid >> 6), lane = tid & 63, g = lane >> 5, l32 = lane & 31;
 
@@ -227,20 +96,20 @@ attn_fp8_kernel(AttnParams p, const float* scales) {
   const int one4 = 0x38383838;
   const v8i ones = {one4, one4, one4, one4, one4, one4, one4, one4};
 
-  // direct-load lane offsets: row 16w + 8j + lane/8, source chunk swz(row, lane%8)
+  // direct-load lane offsets: row 16w + 8j + lane/8, source chunk swz8(row, lane%8)
   const size_t ts = HD;
   unsigned off[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int row = 16 * wave + 8 * j + (lane >> 3);
-    off[j] = unsigned(row) * unsigned(ts) + unsigned(swz(row, lane & 7)) * 16u;
+    off[j] = unsigned(row) * unsigned(ts) + unsigned(swz8(row, lane & 7)) * 16u;
   }
   // K operand addresses: row kb*32 + l32, logical chunks 4ks + 2g + e (kb adds 4096 bytes)
   int koff[2][2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int e = 0; e < 2; ++e) koff[ks][e] = l32 * 128 + swz(l32, 4 * ks + 2 * g + e) * 16;
+    for (int e = 0; e < 2; ++e) koff[ks][e] = l32 * 128 + swz8(l32, 4 * ks + 2 * g + e) * 16;
   // V^T addresses: lane v of its 16-lane group reads key 16 q + R (q = 0..3 adds 2048
   // bytes), R = 8 (t/4) + 4 g + t%4 with t = v/2, columns 32 db + 16 G' + 8 (v%2)
   int voff[4];
@@ -248,10 +117,10 @@ attn_fp8_kernel(AttnParams p, const float* scales) {
     const int v = lane & 15, t = v >> 1, gp = (lane >> 4) & 1;
     const int R = 8 * (t >> 2) + 4 * g + (t & 3);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) voff[db] = R * 128 + swz(R, 2 * db + gp) * 16 + 8 * (v & 1);
+    for (int db = 0; db < 4; ++db) voff[db] = R * 128 + swz8(R, 2 * db + gp) * 16 + 8 * (v & 1);
   }
 
-  KeyStream kst;
+  KeyStream<false, u8> kst;
   kst.fstride = size_t(p.P) * HD;
   kst.P = p.P;
   {
@@ -275,7 +144,7 @@ attn_fp8_kernel(AttnParams p, const float* scales) {
       for (int db = 0; db < 4; ++db) acc[db][r] = 0.f;
     }
 
-    KeyStream ks = kst;
+    KeyStream<false, u8> ks = kst;
     ks.start(branch == 0 ? f - nswa + 1 : f - p.dil, branch == 0 ? 1 : -p.dil, nframes);
     __syncthreads();   // the previous branch's last tile is no longer read
     auto kleft_of = [&](int t) {
@@ -283,7 +152,7 @@ attn_fp8_kernel(AttnParams p, const float* scales) {
       return int(left < KT ? (left > 0 ? left : 0) : KT);
     };
     if (ntiles > 0) issue_tile(sK0, sV0, ks, kleft_of(0), off, ts, wave, lane);
-    auto tile = [&](int t, const Tile& Kt, const Tile& Vt, Tile& Kn, Tile& Vn) __attribute__((always_inline)) {
+    auto tile = [&](int t, const Tile8& Kt, const Tile8& Vt, Tile8& Kn, Tile8& Vn) __attribute__((always_inline)) {
       wait_vmem();
       __syncthreads();   // tile t is in LDS; nobody reads Kn/Vn any more
       if (t + 1 < ntiles) {

@@ -1,8 +1,9 @@
-// Tile machinery shared by the bf16 MFMA softmax-branch kernels (forward and
-// backward, d = 128): 64-row tiles of 256-byte rows in LDS with a per-row XOR
-// permutation of the 16-byte chunks, direct global -> LDS loads, the walk over
-// the rows of a branch's frames as one virtual sequence, and the MFMA operand
-// reads (row chunks and transposed reads) of gfx950.
+// Tile machinery shared by the MFMA softmax-branch kernels (bf16 forward and
+// backward, e4m3 forward; d = 128): 64-row tiles in LDS (256-byte rows of
+// bf16, 128-byte rows of e4m3) with a per-row XOR permutation of the 16-byte
+// chunks, direct global -> LDS loads, the walk over the rows of a branch's
+// frames as one virtual sequence, and the bf16 MFMA operand reads (row chunks
+// and transposed reads) of gfx950.
 #pragma once
 
 #include "hlta_device.h"
@@ -21,10 +22,13 @@ constexpr int KT = 64;           // keys per tile
 constexpr int NT = 256;          // threads
 constexpr int kXcds = 8;
 
-// one K or V tile: 64 rows of 256 B, 16-byte chunks permuted per row (swz)
-struct Tile {
-  uint4 row[KT][16];
+// one K or V tile: 64 rows of kRowBytes, 16-byte chunks permuted per row
+template <int kRowBytes>
+struct TileOf {
+  uint4 row[KT][kRowBytes / 16];
 };
+using Tile = TileOf<256>;    // bf16 rows (swz)
+using Tile8 = TileOf<128>;   // e4m3 rows (swz8)
 
 // 16-byte chunk c of key row r sits at chunk position c ^ f(r mod 16), with f
 // swapping the two 2-bit halves of the row index. A 256-byte row spans all 64
@@ -36,6 +40,18 @@ struct Tile {
 __device__ __forceinline__ int swz(int r, int c) {
   const int x = r & 15;
   return c ^ (((x & 3) << 2) | (x >> 2));
+}
+
+// 128-byte rows (8 chunks, half the banks): chunk c of row r at position
+// c ^ ((r / 2) mod 8), which spreads both 16-row operand reads (two rows per
+// bank set) and the 8-bit transposed reads over all banks.
+__device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+template <int kRowBytes>
+__device__ __forceinline__ int swz_row(int r, int c) {
+  static_assert(kRowBytes == 256 || kRowBytes == 128, "tile rows are 256 or 128 bytes");
+  if constexpr (kRowBytes == 256) return swz(r, c);
+  else return swz8(r, c);
 }
 
 // Wave-uniform values kept in scalar registers.
@@ -53,25 +69,26 @@ __device__ __forceinline__ const T* uni(const T* ptr) {
 // keys spans at most two frames (P >= 64); all fields are wave-uniform.
 // Frames of a branch are g, g + step, ...: step 1 for SWA (oldest first),
 // -dil for DSWA. In stream mode the call's own frame f0 comes from the main
-// tensors and earlier frames from ring slot g mod R.
-template <bool kRing>
+// tensors and earlier frames from ring slot g mod R. E is the element type
+// (bf16, or unsigned char for e4m3 codes); strides count elements.
+template <bool kRing, typename E = bf16>
 struct KeyStream {
-  const bf16* kmain;     // token 0 of frame 0 (full mode) or of the call's frame (stream mode), head h
-  const bf16* vmain;
-  const bf16* kring;     // token 0 of ring slot 0, head h (stream mode)
-  const bf16* vring;
+  const E* kmain;        // token 0 of frame 0 (full mode) or of the call's frame (stream mode), head h
+  const E* vmain;
+  const E* kring;        // token 0 of ring slot 0, head h (stream mode)
+  const E* vring;
   size_t fstride;        // elements between consecutive frames: P*H*D
   long long f0;
   int R;
   long long g;           // current frame
   int step, left, P;     // frame step, frames after the current one, tokens per frame
   int pk;                // current tile starts at token pk of the current frame
-  const bf16* k0;        // token 0 of the current frame
-  const bf16* v0;
-  const bf16* k1;        // token 0 of the next frame (the current one if none)
-  const bf16* v1;
+  const E* k0;           // token 0 of the current frame
+  const E* v0;
+  const E* k1;           // token 0 of the next frame (the current one if none)
+  const E* v1;
 
-  __device__ __forceinline__ void frame_ptrs(long long gg, const bf16*& kb, const bf16*& vb) const {
+  __device__ __forceinline__ void frame_ptrs(long long gg, const E*& kb, const E*& vb) const {
     if constexpr (!kRing) {
       const size_t off = size_t(gg) * fstride;
       kb = uni(kmain + off);
@@ -118,23 +135,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
 }
 
 // Direct global -> LDS copy of the current tile: wave w moves rows 16w .. 16w+15,
-// four rows (1 KB) per instruction; lane i lands at chunk position i%16 of row
-// 16w + 4j + i/16 and so loads the chunk that the swizzle puts there. A tile
+// 1 KB per instruction (four 256-byte or eight 128-byte rows); lane i lands at
+// chunk position i % n of row 16w + (64/n) j + i/n (n chunks per row) and so
+// loads the chunk that the swizzle puts there. A tile
 // inside one frame (the common case) loads through buffer resources with the
-// precomputed lane offsets `off` (no per-lane address arithmetic); a tile
+// precomputed lane offsets `off` (kRowBytes / 64 of them, no per-lane
+// address arithmetic); a tile
 // across a frame boundary or past the end of the sequence computes each lane's
 // row, and rows past the end re-read the last valid row (finite data; their
 // scores are masked, so they contribute exactly zero).
-template <bool kRing, bool kV = true>
-__device__ __forceinline__ void issue_tile(Tile& Kd, Tile& Vd, const KeyStream<kRing>& ks, int kleft,
-                                           const unsigned (&off)[4], size_t ts, int wave, int lane) {
+template <bool kRing, bool kV = true, typename E = bf16, int kRowBytes = 256>
+__device__ __forceinline__ void issue_tile(TileOf<kRowBytes>& Kd, TileOf<kRowBytes>& Vd,
+                                           const KeyStream<kRing, E>& ks, int kleft,
+                                           const unsigned* off, size_t ts, int wave, int lane) {
+  constexpr int kChunks = kRowBytes / 16;   // 16-byte chunks per row
+  constexpr int kRows = 64 / kChunks;       // rows per instruction
+  constexpr int kInst = 16 / kRows;         // instructions per wave
   if (ks.pk + KT <= ks.P && kleft >= KT) {
-    const unsigned bytes = unsigned(KT * ts * sizeof(bf16));
+    const unsigned bytes = unsigned(KT * ts * sizeof(E));
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(ks.k0 + size_t(ks.pk) * ts, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(ks.v0 + size_t(ks.pk) * ts, bytes);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r0 = 16 * wave + 4 * j;
+    for (int j = 0; j < kInst; ++j) {
+      const int r0 = 16 * wave + kRows * j;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(&Kd.row[r0][0]), 16,
                                                off[j], 0, 0, 0);
       if constexpr (kV)
@@ -145,14 +168,14 @@ __device__ __forceinline__ void issue_tile(Tile& Kd, Tile& Vd, const KeyStream<k
   }
   const int split = ks.P - ks.pk;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r0 = 16 * wave + 4 * j;
-    const int row = r0 + (lane >> 4);
+  for (int j = 0; j < kInst; ++j) {
+    const int r0 = 16 * wave + kRows * j;
+    const int row = r0 + lane / kChunks;
     const int rr = row < kleft ? row : kleft - 1;
-    const int c = swz(row, lane & 15);
+    const int c = swz_row<kRowBytes>(row, lane % kChunks);
     const size_t koff = rr < split ? size_t(ks.pk + rr) * ts : size_t(rr - split) * ts;
-    const bf16* ksrc = (rr < split ? ks.k0 : ks.k1) + koff + c * 8;
-    const bf16* vsrc = (rr < split ? ks.v0 : ks.v1) + koff + c * 8;
+    const E* ksrc = (rr < split ? ks.k0 : ks.k1) + koff + c * int(16 / sizeof(E));
+    const E* vsrc = (rr < split ? ks.v0 : ks.v1) + koff + c * int(16 / sizeof(E));
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(ksrc),
                                      (__attribute__((address_space(3))) void*)(&Kd.row[r0][0]), 16, 0, 0);
     if constexpr (kV)
@@ -189,8 +212,10 @@ __device__ __forceinline__ float sum_xor32(float x) {
 // provably less than 16 KB, so the compiler folds the constant part and the
 // tile's own LDS address into the instruction's immediate offset: one set of
 // lane address registers serves both buffers and every key block.
-__device__ __forceinline__ const char* at(const Tile& t, int lane_off, int const_off) {
-  return reinterpret_cast<const char*>(&t) + (unsigned(lane_off) & unsigned(sizeof(Tile) - 1)) + const_off;
+template <int kRowBytes>
+__device__ __forceinline__ const char* at(const TileOf<kRowBytes>& t, int lane_off, int const_off) {
+  return reinterpret_cast<const char*>(&t) + (unsigned(lane_off) & unsigned(sizeof(TileOf<kRowBytes>) - 1)) +
+         const_off;
 }
 
 // 8 consecutive d values (chunk c) of key row kb*32 + l32

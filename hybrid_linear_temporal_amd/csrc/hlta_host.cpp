@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <initializer_list>
 #include <limits>
 #include <string>
 
@@ -24,6 +25,28 @@ static bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   if (a < 0 || b < 0) return false;
   if (a != 0 && b > std::numeric_limits<int64_t>::max() / a) return false;
   *out = a * b;
+  return true;
+}
+
+// product of non-negative factors, false if it leaves int64
+static bool prod_ok(std::initializer_list<int64_t> f, int64_t* out) {
+  int64_t x = 1;
+  for (int64_t v : f)
+    if (!mul_ok(x, v, &x)) return false;
+  *out = x;
+  return true;
+}
+
+static bool add_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0 || a > std::numeric_limits<int64_t>::max() - b) return false;
+  *out = a + b;
+  return true;
+}
+
+// x rounded up to a multiple of 256, false if it leaves int64
+static bool align256_ok(int64_t x, int64_t* out) {
+  if (x < 0 || x > std::numeric_limits<int64_t>::max() - 255) return false;
+  *out = (x + 255) / 256 * 256;
   return true;
 }
 
@@ -129,22 +152,33 @@ hlta_status make_plan(const hlta_config* cfg, int64_t L, Plan* plan) {
       return fail(HLTA_E_UNSUPPORTED, "the MFMA memory kernels need L*H*d*4 < 2^32 bytes per batch row");
     p.gdn = Impl::Generic;
   }
+  const int64_t bh = int64_t(cfg->B) * cfg->H;
+  int64_t gdn = 0;
   if (p.gdn == Impl::Mfma) {
-    gdn_segments(int64_t(cfg->B) * cfg->H, p.n_chunks, &p.gdn_G, &p.gdn_seg_chunks);
-    p.ws_gdn = gdn_seg_record_bytes(cfg->B, cfg->H, p.n_chunks) + gdn_seg_map_bytes(cfg->B, cfg->H, p.gdn_G, cfg->d);
+    gdn_segments(bh, p.n_chunks, &p.gdn_G, &p.gdn_seg_chunks);
+    int64_t recs = 0, maps = 0;
+    if (!prod_ok({bh, p.n_chunks, 13056}, &recs) ||
+        !prod_ok({bh, p.gdn_G > 1 ? 2 * int64_t(p.gdn_G) - 1 : 0, int64_t(cfg->d) * cfg->d, 4}, &maps) ||
+        !add_ok(recs, maps, &gdn))
+      return fail(HLTA_E_SHAPE, "workspace size overflows int64");
+    if (size_t(recs) != gdn_seg_record_bytes(cfg->B, cfg->H, p.n_chunks) ||
+        size_t(maps) != gdn_seg_map_bytes(cfg->B, cfg->H, p.gdn_G, cfg->d))
+      return fail(HLTA_E_SHAPE, "internal: memory workspace layout mismatch");
   } else {
-    int64_t nrec = 0;
-    if (!mul_ok(int64_t(cfg->B) * cfg->H, p.n_chunks, &nrec)) return fail(HLTA_E_SHAPE, "workspace overflow");
-    p.ws_gdn = size_t(nrec) * gdn_generic_record_bytes(cfg->gdn_chunk, cfg->d);
+    if (!prod_ok({bh, p.n_chunks, int64_t(gdn_generic_record_bytes(cfg->gdn_chunk, cfg->d))}, &gdn))
+      return fail(HLTA_E_SHAPE, "workspace size overflows int64");
   }
+  p.ws_gdn = size_t(gdn);
   p.ws_total = p.ws_gdn;
   if (cfg->rope_theta > 0.f) {
     // rotated q and k of the softmax branches, [B, L, H, d] in_dtype each
-    int64_t n = 0;
-    if (!mul_ok(int64_t(cfg->B) * L, int64_t(cfg->H) * cfg->d, &n)) return fail(HLTA_E_SHAPE, "workspace overflow");
-    p.ws_rope_bytes = align_up(size_t(n) * dtype_bytes(cfg->in_dtype), 256);
-    p.ws_rope_off = align_up(p.ws_gdn, 256);
-    p.ws_total = p.ws_rope_off + 2 * p.ws_rope_bytes;
+    int64_t n = 0, off = 0, total = 0;
+    if (!prod_ok({bh, L, cfg->d, int64_t(dtype_bytes(cfg->in_dtype))}, &n) || !align256_ok(n, &n) ||
+        !align256_ok(gdn, &off) || !add_ok(off, n, &total) || !add_ok(total, n, &total))
+      return fail(HLTA_E_SHAPE, "workspace size overflows int64");
+    p.ws_rope_bytes = size_t(n);
+    p.ws_rope_off = size_t(off);
+    p.ws_total = size_t(total);
   }
   *plan = p;
   return HLTA_OK;
@@ -155,16 +189,21 @@ hlta_status make_bwd_plan(const hlta_config* cfg, BwdPlan* plan) {
   if (s != HLTA_OK) return s;
   const int64_t L = int64_t(cfg->T) * cfg->P, C = cfg->gdn_chunk, nch = (L + C - 1) / C;
   const int64_t dd = int64_t(cfg->d) * cfg->d, bh = int64_t(cfg->B) * cfg->H;
-  int64_t rows = 0, mats = 0;
-  if (!mul_ok(bh, L, &rows) || !mul_ok(bh * nch, dd, &mats)) return fail(HLTA_E_SHAPE, "workspace overflow");
   BwdPlan p;
   p.n_slots = int(std::min<int64_t>(std::max<int64_t>(bh * nch, 1), kBwdSlots));
-  p.stats_bytes = align_up(size_t(rows) * 2 * sizeof(float), 256);
+  int64_t stats = 0, mats = 0, mats6 = 0, slots = 0, part = 0, off = 0, total = 0;
+  if (!prod_ok({bh, L, 2, 4}, &stats) || !align256_ok(stats, &stats) ||
+      !prod_ok({bh, nch, dd, 4}, &mats) || !align256_ok(mats, &mats) || !mul_ok(mats, 6, &mats6) ||
+      !prod_ok({p.n_slots, C, dd, 4}, &slots) || !align256_ok(slots, &slots) ||
+      !prod_ok({cfg->H, kDwSlices, 3, 4}, &part) || !align256_ok(part, &part) ||
+      !add_ok(stats, stats, &off) || !add_ok(off, mats6, &off) || !add_ok(off, slots, &total) || !add_ok(total, part, &total))
+    return fail(HLTA_E_SHAPE, "workspace size overflows int64");
+  p.stats_bytes = size_t(stats);
   p.mat_off = 2 * p.stats_bytes;
-  p.mat_bytes = align_up(size_t(mats) * sizeof(float), 256);
+  p.mat_bytes = size_t(mats);
   p.slot_off = p.mat_off + 6 * p.mat_bytes;
-  p.part_off = p.slot_off + align_up(size_t(p.n_slots) * size_t(C) * size_t(dd) * sizeof(float), 256);
-  p.total = p.part_off + align_up(size_t(cfg->H) * kDwSlices * 3 * sizeof(float), 256);
+  p.part_off = p.slot_off + size_t(slots);
+  p.total = size_t(total);
   *plan = p;
   return HLTA_OK;
 }
@@ -222,8 +261,17 @@ size_t hlta_bwd_workspace_bytes(const hlta_config* cfg) {
 
 size_t hlta_stream_ring_bytes(const hlta_config* cfg, int32_t ring_frames) {
   clear_error();
-  if (check_config(cfg) != HLTA_OK || ring_frames < 1) return 0;
-  return size_t(cfg->B) * ring_frames * cfg->P * cfg->H * cfg->d * dtype_bytes(cfg->in_dtype);
+  if (check_config(cfg) != HLTA_OK) return 0;
+  if (ring_frames < 1) {
+    fail(HLTA_E_SHAPE, "ring_frames must be >= 1");
+    return 0;
+  }
+  int64_t n = 0;
+  if (!prod_ok({cfg->B, ring_frames, cfg->P, cfg->H, cfg->d, int64_t(dtype_bytes(cfg->in_dtype))}, &n)) {
+    fail(HLTA_E_SHAPE, "ring size overflows int64");
+    return 0;
+  }
+  return size_t(n);
 }
 
 }  // extern "C"

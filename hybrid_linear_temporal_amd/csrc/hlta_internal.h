@@ -63,8 +63,10 @@ bool mfma_gdn_supported(const hlta_config* cfg);
 // Per-chunk record sizes of the GDN scratch (in bytes).
 size_t gdn_generic_record_bytes(int C, int d);
 
-// Scratch of the MFMA memory kernels: one 6 KB record per chunk (the chunk's
-// T'' = T diag(b) in bf16 operand order), then, when G > 1, the segment maps:
+// Scratch of the MFMA memory kernels: one 13,056-byte record per chunk (the
+// chunk's T'' = T diag(b) and T' = T diag(b gamma / ||k||) in bf16 operand
+// order, then its gate prefix sums, b and inverse key norms), then, when G > 1,
+// the segment maps:
 // 2G - 1 d x d fp32 matrices per (batch row, head) (per segment but the last
 // its N and M, and a copy of the start state).
 size_t gdn_seg_record_bytes(int B, int H, long long n_chunks);
