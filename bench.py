@@ -360,9 +360,12 @@ def main():
                     help="hlta_fwd steps timed with and without the rotary embedding (0: skip)")
     ap.add_argument("--bwd-steps", type=int, default=3,
                     help="steps of the backward (hlta_bwd) timed on the same clip (0: skip)")
+    ap.add_argument("--ceiling-reps", type=int, default=5,
+                    help="timed calls of each measured-ceiling microbenchmark (dense bf16 MFMA loop, HBM copy); "
+                         "0: skip")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB read + 1 GiB write elementwise kernel (3 launches), to scale "
-                         "rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
+                    help="only run the library's streaming copy over 1 GiB (1 GiB read + 1 GiB written, 3 "
+                         "launches), to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1 (heads and rollouts shard across GPUs with no exchange, but no multi-GPU path is built)"}))
@@ -376,7 +379,7 @@ def main():
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
-            torch.mul(src, 1.0, out=dst)
+            H.hlta_ceiling_copy(src, dst)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration": {"read_bytes": src.numel() * 4, "write_bytes": dst.numel() * 4,
                                                "launches": 3}}))
@@ -447,6 +450,12 @@ def main():
                          "bytes_per_token_head": per_th, "avg_ms": gdn_ms},
         "device": torch.cuda.get_device_name(0),
     }
+    if args.ceiling_reps > 0:
+        print("# measured ceilings (bf16 MFMA loop, HBM copy)", file=sys.stderr, flush=True)
+        ceil = H.measure_ceilings(reps=args.ceiling_reps)
+        res["ceilings"] = ceil
+        res["roofline"]["frac_of_measured"] = attn_tflops / ceil["mfma_bf16_tflops"]
+        res["gdn_roofline"]["frac_of_measured"] = gdn_gbs / ceil["hbm_copy_gbs"]
     if args.fp8_steps > 0 and wl.d == 128 and wl.P >= 64:
         print(f"# FP8 leg, {args.fp8_steps} steps", file=sys.stderr, flush=True)
         res["fp8"] = fp8_leg(H, wl, dev, out, args.fp8_steps, args.impl, attn_ms)

@@ -577,4 +577,25 @@ hlta_status hlta_step_frame_rollouts(const hlta_config* cfg, hlta_stream_state* 
                          workspace, ws_bytes, stream);
 }
 
+hlta_status hlta_ceiling_mfma_bf16(float* sink, uint64_t* clocks, int32_t workgroups, int32_t iters, void* stream) {
+  clear_error();
+  HLTA_TRY(need(sink, "sink"));
+  HLTA_TRY(maybe(clocks, "clocks"));
+  if (workgroups < 1 || iters < 1) return fail(HLTA_E_SHAPE, "workgroups and iters must be >= 1");
+  const hipError_t e = launch_ceiling_mfma(sink, reinterpret_cast<unsigned long long*>(clocks), workgroups, iters,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "MFMA ceiling launch");
+  return HLTA_OK;
+}
+
+hlta_status hlta_ceiling_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  clear_error();
+  HLTA_TRY(need(src, "src"));
+  HLTA_TRY(need(dst, "dst"));
+  if (bytes % 16 != 0) return fail(HLTA_E_SHAPE, "bytes must be a multiple of 16");
+  const hipError_t e = launch_ceiling_copy(src, dst, bytes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "copy ceiling launch");
+  return HLTA_OK;
+}
+
 }  // extern "C"

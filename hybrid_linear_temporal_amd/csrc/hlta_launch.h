@@ -36,6 +36,11 @@ hipError_t launch_gdn_seg(const GdnParams& p, int G, int seg_chunks, void* works
 // dst = src (src non-null) or dst = 0, bytes a multiple of 4; one kernel launch.
 hipError_t launch_copy_or_zero(void* dst, const void* src, size_t bytes, hipStream_t st);
 
+// Measured ceilings: a dense bf16 MFMA loop (workgroups x 4 waves, iters x 8
+// MFMA 32x32x16 per wave) and a 16-byte streaming copy of bytes (multiple of 16).
+hipError_t launch_ceiling_mfma(float* sink, unsigned long long* clocks, int workgroups, int iters, hipStream_t st);
+hipError_t launch_ceiling_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
+
 // Copy n_frames latent frames [B, frames, P, H, d] from src (frames src_f0..)
 // into ring slots (frame g -> slot g mod R). elem = element bytes.
 hipError_t launch_ring_store(const void* src, long long src_frames, long long src_f0, void* ring,

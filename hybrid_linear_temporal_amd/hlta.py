@@ -28,7 +28,7 @@ EXPORTS = ("hlta_abi_version", "hlta_status_string", "hlta_last_error", "hlta_va
            "hlta_fwd_workspace_bytes", "hlta_fwd", "hlta_gdn_fwd", "hlta_attn_fwd", "hlta_stream_ring_bytes",
            "hlta_stream_load_prefix", "hlta_step_workspace_bytes", "hlta_step_frame",
            "hlta_step_frame_rollouts", "hlta_quantize_fp8", "hlta_attn_fwd_fp8", "hlta_bwd_workspace_bytes",
-           "hlta_bwd", "hlta_fwd_noalloc")
+           "hlta_bwd", "hlta_fwd_noalloc", "hlta_ceiling_mfma_bf16", "hlta_ceiling_copy")
 
 
 class hlta_config(ctypes.Structure):
@@ -86,6 +86,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "hlta_attn_fwd_fp8": (I32, [cfgp, P, P, P, P, P, P, P, P, P, P]),
         "hlta_bwd_workspace_bytes": (S, [cfgp]),
         "hlta_bwd": (I32, [cfgp] + [P] * 18 + [P, S, P]),
+        "hlta_ceiling_mfma_bf16": (I32, [P, P, I32, I32, P]),
+        "hlta_ceiling_copy": (I32, [P, P, S, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -306,6 +308,64 @@ def hlta_step_frame_rollouts(st: Stream, frames, q_f, k_f, v_f, a_f, b_f, mix_w,
         _ptr(out["o_dswa"]), _ptr(out["o_gdn"]), _ptr(out["o_mix"]), int(bool(commit)), _ptr(st.workspace),
         st.workspace.numel(), _stream(stream)))
     return out
+
+
+MFMA_CEILING_FLOP_PER_WAVE_ITER = 8 * 32 * 32 * 16 * 2
+
+
+def hlta_ceiling_mfma_bf16(sink, clocks, workgroups: int, iters: int, stream=None):
+    """Dense bf16 MFMA loop, workgroups * 4 * iters * 8 * 32768 flop
+    (C: hlta_ceiling_mfma_bf16). sink: float32 [workgroups * 256]; clocks:
+    int64 [2] or None."""
+    _check(load_library().hlta_ceiling_mfma_bf16(_ptr(sink), _ptr(clocks), int(workgroups), int(iters),
+                                                 _stream(stream)))
+
+
+def hlta_ceiling_copy(src, dst, stream=None):
+    """dst = src with 16-byte loads and stores (C: hlta_ceiling_copy)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst is smaller than src")
+    _check(load_library().hlta_ceiling_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+
+
+def measure_ceilings(reps: int = 5, copy_bytes: int = 2 << 30, device="cuda") -> dict:
+    """Best of `reps` timed calls of each ceiling microbenchmark (after one
+    untimed call), with HIP events on the launch stream: bf16 MFMA TFLOP/s at
+    two workgroups per compute unit, the clock held meanwhile, and streaming
+    copy GB/s (read + write bytes over time)."""
+    props = torch.cuda.get_device_properties(device)
+    wgs, iters = 2 * props.multi_processor_count, 4096
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device=device)
+    clocks = torch.zeros(2, dtype=torch.int64, device=device)
+    stream = torch.cuda.current_stream(device)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    flop = wgs * 4 * iters * MFMA_CEILING_FLOP_PER_WAVE_ITER
+    best_mfma, ghz = 0.0, None
+    for r in range(reps + 1):
+        e0.record(stream)
+        hlta_ceiling_mfma_bf16(sink, clocks, wgs, iters, stream)
+        e1.record(stream)
+        e1.synchronize()
+        if r:
+            tf = flop / (e0.elapsed_time(e1) * 1e-3) / 1e12
+            if tf > best_mfma:
+                best_mfma = tf
+                c = clocks.cpu().tolist()
+                ghz = c[0] / c[1] * 0.1 if c[1] > 0 else None
+    src = torch.empty(copy_bytes // 4, dtype=torch.float32, device=device).fill_(1.0)
+    dst = torch.empty_like(src)
+    best_copy = 0.0
+    for r in range(reps + 1):
+        e0.record(stream)
+        hlta_ceiling_copy(src, dst, stream)
+        e1.record(stream)
+        e1.synchronize()
+        if r:
+            best_copy = max(best_copy, 2 * copy_bytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src, dst
+    return {"mfma_bf16_tflops": best_mfma, "mfma_clock_ghz": ghz, "mfma_workgroups": wgs, "mfma_iters": iters,
+            "hbm_copy_gbs": best_copy, "copy_bytes": copy_bytes, "reps": reps}
 
 
 def to_device(x: dict, dtype: str, device="cuda") -> dict:

@@ -355,6 +355,33 @@ hlta_status hlta_step_frame_rollouts(const hlta_config* cfg, hlta_stream_state* 
                                      void* o_swa, void* o_dswa, void* o_gdn, void* o_mix,
                                      int32_t commit, void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * Measured ceilings (not part of the operator): microbenchmarks of the GPU the
+ * library runs on, so that a kernel's roofline fraction can be stated against
+ * what the chip sustains beside its published peak. The caller times them
+ * (e.g. with events on `stream`).
+ *
+ * hlta_ceiling_mfma_bf16 - dense bf16 matrix-core loop: `workgroups`
+ * workgroups of 4 waves; every wave issues iters x 8 independent
+ * v_mfma_f32_32x32x16_bf16 on register operands (32 x 32 x 16 x 2 = 32768 flop
+ * each), so one call performs workgroups * 4 * iters * 8 * 32768 flop.
+ * sink: device float[workgroups * 256], written (keeps the products live).
+ * clocks: device uint64[2] or NULL: core-clock ticks and 100 MHz
+ * reference-clock ticks that workgroup 0 spent in its loop (their ratio times
+ * 100 MHz is the clock the chip held). workgroups, iters >= 1, else
+ * HLTA_E_SHAPE; sink NULL is HLTA_E_NULL; pointers must be 16-byte aligned.
+ */
+hlta_status hlta_ceiling_mfma_bf16(float* sink, uint64_t* clocks, int32_t workgroups, int32_t iters,
+                                   void* stream);
+
+/*
+ * hlta_ceiling_copy - HBM streaming copy: dst[0 .. bytes) = src[0 .. bytes)
+ * with 16-byte loads and stores (2 * bytes of traffic per call). Device
+ * buffers, 16-byte aligned, not overlapping; bytes a multiple of 16, else
+ * HLTA_E_SHAPE.
+ */
+hlta_status hlta_ceiling_copy(const void* src, void* dst, size_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
