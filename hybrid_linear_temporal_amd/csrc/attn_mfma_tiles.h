@@ -209,18 +209,21 @@ __device__ __forceinline__ float sum_xor32(float x) {
 }
 
 // Address of (lane part + constant part) inside a tile. The lane part is made
-// provably less than 16 KB, so the compiler folds the constant part and the
-// tile's own LDS address into the instruction's immediate offset: one set of
-// lane address registers serves both buffers and every key block.
-template <int kRowBytes>
+// provably less than kLaneBound bytes (a power of two no smaller than the
+// largest lane part of the caller), and the constant part is added to the
+// tile's own LDS address first, so the compiler can fold both into the
+// instruction's 16-bit immediate offset and one set of lane address registers
+// serves the buffers and key blocks. (With the lane part added first it kept
+// a register per buffer and lane part, and the forward kernel spilled.)
+template <int kLaneBound = 0, int kRowBytes>
 __device__ __forceinline__ const char* at(const TileOf<kRowBytes>& t, int lane_off, int const_off) {
-  return reinterpret_cast<const char*>(&t) + (unsigned(lane_off) & unsigned(sizeof(TileOf<kRowBytes>) - 1)) +
-         const_off;
+  constexpr unsigned kMask = (kLaneBound ? unsigned(kLaneBound) : unsigned(sizeof(TileOf<kRowBytes>))) - 1u;
+  return (reinterpret_cast<const char*>(&t) + const_off) + (unsigned(lane_off) & kMask);
 }
 
 // 8 consecutive d values (chunk c) of key row kb*32 + l32
 __device__ __forceinline__ bf16x8 ld_chunk(const Tile& t, int kb, int l32, int c) {
-  return *reinterpret_cast<const bf16x8*>(at(t, l32 * 256 + swz(l32, c) * 16, kb * 32 * 256));
+  return *reinterpret_cast<const bf16x8*>(at<32 * 256>(t, l32 * 256 + swz(l32, c) * 16, kb * 32 * 256));
 }
 
 // V^T operand of one 32x32x16 MFMA: lane = d row (d0 + l16 inside its 16-lane group),
@@ -233,8 +236,8 @@ __device__ __forceinline__ bf16x8 ld_vt(const Tile& t, int kb, int m2, int hl, i
   const int dcol = d0 + 4 * q;
   const int x0 = 4 * hl + e, x1 = x0 + 8;
   const int kc = (kb * 32 + 16 * m2) * 256;
-  const char* p0 = at(t, x0 * 256 + swz(x0, dcol >> 3) * 16 + (dcol & 7) * 2, kc);
-  const char* p1 = at(t, x1 * 256 + swz(x1, dcol >> 3) * 16 + (dcol & 7) * 2, kc);
+  const char* p0 = at<16 * 256>(t, x0 * 256 + swz(x0, dcol >> 3) * 16 + (dcol & 7) * 2, kc);
+  const char* p1 = at<16 * 256>(t, x1 * 256 + swz(x1, dcol >> 3) * 16 + (dcol & 7) * 2, kc);
   const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
   const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p1));
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};

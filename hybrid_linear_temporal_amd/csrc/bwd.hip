@@ -1,7 +1,7 @@
 // Backward of the operator (gradients for training): given dL/do_mix, the
 // gradients of q, k, v, the gates, the mix weights and the start state. The
-// branch gradients are do_i = w[h, i] * d_mix (the mix is linear). fp32
-// kernels (any supported d and input dtype):
+// branch gradients are do_i = w[h, i] * d_mix (the mix is linear). Kernels
+// for any supported d and input dtype, accumulating in fp32:
 //
 //  * softmax branches (exact attention, so its gradient is the textbook one;
 //    long-context page, section 03 on tiled exact attention): a recompute pass
@@ -10,20 +10,19 @@
 //    each key frame, the query frames whose frame set holds it and
 //    accumulates dv = sum_i P do_i and dk = s sum_i P (do_i . v - D_i) q_i;
 //  * gated delta rule (Kairos related-work page, row A; long-context page,
-//    section 06): with M_t = a_t (I - b_t k^ k^^T) the state obeys
-//    S_t = S_{t-1} M_t + b_t v_t k^_t^T and its adjoint G_{t-1} = G_t M_t +
-//    do_{t-1} q^_{t-1}^T. Per chunk of C tokens, in parallel, the transition
-//    A_c (product of the M_t), the chunk's own state from zero U_c and its own
-//    adjoint from zero X_c; then two short chains over chunks give every
+//    section 06): per chunk of C tokens, in parallel, the chunk's affine map
+//    S_end = S_start A_c + U_c and its own adjoint from zero X_c (matrix form,
+//    gdn_bwd_mat.hip); then two short chains over chunks here give every
 //    chunk's start state and the adjoint reaching its end; then, per chunk in
-//    parallel again, the states are recomputed token by token and the adjoint
-//    carried back over the chunk, giving the token gradients (formulas at
-//    gdn_bwd_tokens). Exact in fp32 (no approximation beyond rounding). The
-//    prep gives each wave 16 rows of one matrix (rows evolve independently);
-//    the token pass keeps S and G as per-thread (d/16) x (d/16) blocks;
+//    parallel again, the token gradients in matrix form (gdn_bwd_mat.hip).
+//    The chunk products there run on bf16 MFMA with each fp32 operand split
+//    into a bf16 head and a bf16 remainder (three products), which keeps
+//    them close to fp32 accuracy;
 //  * mix weights: dw[h, i] = <d_mix, o_i> over the stored branch outputs.
 // With bf16 inputs and outputs, d = 128 and P >= 64 the softmax branches run
 // on the bf16 MFMA kernels of attn_bwd_mfma.hip instead.
+#include <type_traits>
+
 #include "hlta_device.h"
 #include "hlta_launch.h"
 
@@ -32,7 +31,6 @@ namespace hlta {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr float kL2Eps = 1e-6f;
 
 template <typename T>
 __device__ __forceinline__ float ld(const T* p, size_t i) {
@@ -292,237 +290,6 @@ attn_bwd_dkdv(AttnParams p, const Tg* d_mix, const float* mix_w, const float* ls
 // gated delta rule
 // ---------------------------------------------------------------------------
 
-// Block layout: thread t owns rows 16-block t/16 and columns 16-block t%16 of
-// a d x d matrix, BS = d/16 each. Matrix-vector products: each thread writes
-// the partial sums of its block to LDS and, after one barrier, the 16 partials
-// of an entry are added in a fixed order; up to four products share a round.
-// Scalar sums: wave reduction, then the four wave partials from LDS.
-template <int D>
-struct GdnBlock {
-  static constexpr int BS = D / 16;
-  float red[4][16][D];   // partial sums of up to four matrix-vector products
-  float vec[12][D];      // vectors of the current token
-  float wsum[8][8][4];   // wave partials of up to 8 sums, 8 slots
-};
-
-// partial sums of y = M x (kRows) or y = M^T x into red[slot]
-template <int D, bool kRows>
-__device__ __forceinline__ void mv_part(GdnBlock<D>& sm, const float (&M)[D / 16][D / 16], const float* x, int slot) {
-  constexpr int BS = D / 16;
-  const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
-#pragma unroll
-  for (int a = 0; a < BS; ++a) {
-    float s = 0.f;
-#pragma unroll
-    for (int bb = 0; bb < BS; ++bb) s += kRows ? M[a][bb] * x[tc * BS + bb] : M[bb][a] * x[tr * BS + bb];
-    if (kRows) sm.red[slot][tc][tr * BS + a] = s;
-    else sm.red[slot][tr][tc * BS + a] = s;
-  }
-}
-// vec[y[slot]] = f[slot] * (sum of the partials of slot), slots 0 .. n-1 (after a barrier)
-template <int D>
-__device__ __forceinline__ void mv_finish(GdnBlock<D>& sm, int n, const int (&y)[4], const float (&f)[4]) {
-  for (int e = threadIdx.x; e < n * D; e += kThreads) {
-    const int slot = e / D, i = e % D;
-    float s = 0.f;
-#pragma unroll
-    for (int g = 0; g < 16; ++g) s += sm.red[slot][g][i];
-    sm.vec[y[slot]][i] = s * f[slot];
-  }
-}
-
-// N sums of one value per thread; every thread gets the totals. Slot picks a
-// private LDS area (a slot is reused only after further barriers).
-template <int D, int N>
-__device__ __forceinline__ void sum_n(GdnBlock<D>& sm, float (&x)[N], int slot) {
-#pragma unroll
-  for (int j = 0; j < N; ++j) {
-    float v = x[j];
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    x[j] = v;
-  }
-  if ((threadIdx.x & 63) == 0) {
-#pragma unroll
-    for (int j = 0; j < N; ++j) sm.wsum[slot][j][threadIdx.x >> 6] = x[j];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < N; ++j) x[j] = sm.wsum[slot][j][0] + sm.wsum[slot][j][1] + sm.wsum[slot][j][2] + sm.wsum[slot][j][3];
-}
-
-__device__ __forceinline__ float l2n(float n2, bool on) { return on ? sqrtf(n2 + kL2Eps) : 1.f; }
-
-// One token of the memory on S (held in blocks): vec[0] = k and vec[1] = v
-// are in LDS (written before a barrier); applies S <- a (S - b u k^^T)
-// (+ b v k^^T when with_v) with k^ = k / n(k) and u = S k^ (S k and |k|^2 in
-// one round).
-template <int D>
-__device__ __forceinline__ void fwd_token(GdnBlock<D>& sm, float (&S)[D / 16][D / 16], float at, float bt, bool l2,
-                                          bool with_v) {
-  constexpr int BS = D / 16;
-  const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
-  mv_part<D, true>(sm, S, sm.vec[0], 0);
-  float n2[1] = {threadIdx.x < D ? sm.vec[0][threadIdx.x] * sm.vec[0][threadIdx.x] : 0.f};
-  sum_n<D, 1>(sm, n2, 0);   // its barrier also completes the partials
-  const float inv = 1.f / l2n(n2[0], l2);
-  mv_finish<D>(sm, 1, {3, 0, 0, 0}, {inv, 1.f, 1.f, 1.f});   // u = S k / n
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < BS; ++i)
-#pragma unroll
-    for (int j = 0; j < BS; ++j) {
-      const float kj = sm.vec[0][tc * BS + j] * inv;
-      const float vt = with_v ? bt * sm.vec[1][tr * BS + i] * kj : 0.f;
-      S[i][j] = at * (S[i][j] - bt * sm.vec[3][tr * BS + i] * kj) + vt;
-    }
-  __syncthreads();
-}
-
-template <int D>
-__device__ __forceinline__ void load_mat(float (&M)[D / 16][D / 16], const float* src) {
-  constexpr int BS = D / 16;
-  const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
-#pragma unroll
-  for (int i = 0; i < BS; ++i)
-#pragma unroll
-    for (int j = 0; j < BS; ++j) M[i][j] = src ? src[size_t(tr * BS + i) * D + tc * BS + j] : 0.f;
-}
-template <int D>
-__device__ __forceinline__ void store_mat(float* dst, const float (&M)[D / 16][D / 16]) {
-  constexpr int BS = D / 16;
-  const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
-#pragma unroll
-  for (int i = 0; i < BS; ++i)
-#pragma unroll
-    for (int j = 0; j < BS; ++j) dst[size_t(tr * BS + i) * D + tc * BS + j] = M[i][j];
-}
-
-// CPL consecutive values of a [.., D] row (bf16 or fp32) as floats
-template <int CPL>
-__device__ __forceinline__ void load_cols(const bf16* p, float (&x)[CPL]) {
-#pragma unroll
-  for (int i = 0; i < CPL; i += 8) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p + i);
-    const bf16* e = reinterpret_cast<const bf16*>(&u);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[i + j] = static_cast<float>(e[j]);
-  }
-}
-template <int CPL>
-__device__ __forceinline__ void load_cols(const float* p, float (&x)[CPL]) {
-#pragma unroll
-  for (int i = 0; i < CPL; i += 4) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p + i);
-    const float* e = reinterpret_cast<const float*>(&u);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) x[i + j] = e[j];
-  }
-}
-
-// sum over the 4 lanes of a row (lanes 4r .. 4r+3)
-__device__ __forceinline__ float quad_sum(float x) {
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  return x;
-}
-
-// Chunk c of head (b, h) covers tokens [c*C, min(L, (c+1)*C)). With
-// M_t = a_t (I - b_t k^_t k^_t^T) (symmetric), per chunk:
-//   kWhat 0: A_c = M_s M_{s+1} .. M_e            (S_end = S_start A_c + U_c)
-//   kWhat 1: U_c = the chunk's own state from S = 0
-//   kWhat 2: X_c = sum_t do_t q^_t^T M_t M_{t-1} .. M_s
-//            (the chunk's own adjoint carried to its start; G = dL/dS)
-// Rows of all three evolve independently (row i of A M_t is a (a_i - b
-// (a_i . k^) k^)), so each wave owns 16 rows: lane = (row lane/4, quarter
-// lane%4 of the columns), row dot products by two lane shuffles, no barrier
-// inside the token loop. The workgroup (4 waves, 64 rows) first stages the
-// chunk's k (and q), the rows' v (or d_mix) and the gates in LDS, so a token
-// costs LDS reads only. grid (B*H*n_chunks, ceil(D/64)).
-constexpr int kMaxChunk = 64;
-template <typename Tin, typename Tg, int D, int kWhat>
-__global__ void __launch_bounds__(kThreads)
-gdn_bwd_prep(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float* out, float* AmT) {
-  constexpr int CPL = D / 4;
-  __shared__ __attribute__((aligned(16))) Tin kS[kMaxChunk][D];
-  __shared__ __attribute__((aligned(16))) Tin qS[kWhat == 2 ? kMaxChunk : 1][D];
-  __shared__ float xS[kWhat >= 1 ? kMaxChunk : 1][64];
-  __shared__ float aS[kMaxChunk], bS[kMaxChunk];
-  const long long job = blockIdx.x;
-  const int c = int(job % p.n_chunks), bh = int(job / p.n_chunks), b = bh / p.H, h = bh % p.H;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane >> 2, c0 = (lane & 3) * CPL;
-  const int R0 = blockIdx.y * 64;
-  const int row = R0 + wave * 16 + r;
-  const Tin* q = static_cast<const Tin*>(p.q);
-  const Tin* k = static_cast<const Tin*>(p.k);
-  const Tin* v = static_cast<const Tin*>(p.v);
-  const size_t HD = size_t(p.H) * D;
-  const long long t0 = (long long)c * C;
-  const int n = int(p.L - t0 < C ? p.L - t0 : C);
-  const bool l2 = p.l2norm != 0;
-  const size_t tok0 = (size_t(b) * p.L + t0) * HD + size_t(h) * D;
-  const size_t g0 = (size_t(b) * p.L + t0) * p.H + h;
-  for (int e = threadIdx.x; e < n * D; e += kThreads) {
-    const int t = e / D, col = e % D;
-    kS[t][col] = k[tok0 + size_t(t) * HD + col];
-    if constexpr (kWhat == 2) qS[t][col] = q[tok0 + size_t(t) * HD + col];
-  }
-  if constexpr (kWhat >= 1) {
-    const float w2 = mix_w[3 * h + 2];
-    for (int e = threadIdx.x; e < n * 64; e += kThreads) {
-      const int t = e / 64, rr = R0 + e % 64;
-      float x = 0.f;
-      if (rr < D) x = kWhat == 1 ? ld(v, tok0 + size_t(t) * HD + rr) : w2 * ld(d_mix, tok0 + size_t(t) * HD + rr);
-      xS[t][e % 64] = x;
-    }
-  }
-  if (threadIdx.x < n) {
-    aS[threadIdx.x] = p.a[g0 + size_t(threadIdx.x) * p.H];
-    bS[threadIdx.x] = p.b[g0 + size_t(threadIdx.x) * p.H];
-  }
-  __syncthreads();
-  if (R0 + wave * 16 >= D) return;   // d = 32: two waves have no rows
-  float M[CPL];
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) M[j] = (kWhat == 0 && c0 + j == row) ? 1.f : 0.f;
-  for (int i = 0; i < n; ++i) {
-    const int s = kWhat == 2 ? n - 1 - i : i;
-    float kx[CPL];
-    load_cols<CPL>(&kS[s][c0], kx);
-    const float at = aS[s], bt = bS[s];
-    float k2 = 0.f;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) k2 += kx[j] * kx[j];
-    const float ik = 1.f / l2n(quad_sum(k2), l2);
-    if constexpr (kWhat == 2) {   // M <- M + do q^^T
-      float qx[CPL];
-      load_cols<CPL>(&qS[s][c0], qx);
-      float q2 = 0.f;
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) q2 += qx[j] * qx[j];
-      const float f = xS[s][wave * 16 + r] / l2n(quad_sum(q2), l2);
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) M[j] += f * qx[j];
-    }
-    float u = 0.f;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) u += M[j] * kx[j];
-    u = quad_sum(u) * ik;
-    // M <- a (M - b u k^^T) (+ b v k^^T for the own state)
-    const float cu = at * bt * u * ik;
-    const float cv = kWhat == 1 ? bt * xS[s][wave * 16 + r] * ik : 0.f;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) M[j] = at * M[j] + (cv - cu) * kx[j];
-  }
-  float* dst = out + size_t(job) * D * D + size_t(row) * D + c0;
-#pragma unroll
-  for (int j = 0; j < CPL; j += 4) *reinterpret_cast<float4*>(dst + j) = make_float4(M[j], M[j + 1], M[j + 2], M[j + 3]);
-  if constexpr (kWhat == 0) {   // A^T too, so both chains run the same row-times-matrix product
-    float* t = AmT + size_t(job) * D * D + row;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) t[size_t(c0 + j) * D] = M[j];
-  }
-}
-
 // The two chains over chunks, rows of the state split over workgroups (rows
 // evolve independently: row i of S A + U only needs row i of S and U):
 //   dir 0: S_start(0) = S0, S_start(c+1) = S_start(c) A_c + U_c
@@ -617,163 +384,6 @@ gdn_bwd_chain(int n_chunks, const float* S0, const float* Am, const float* AmT, 
   }
 }
 
-// Gradients of one chunk's tokens from its start state S_start(c) and the
-// adjoint R(c) reaching its end: the chunk's states are recomputed into this
-// workgroup's slot, then the adjoint is carried backwards token by token.
-// With G = dL/dS_t (it gains do_t q^^T at token t), u = S_{t-1} k^:
-//   dq^ = S_t^T do_t = a (S_{t-1}^T do - b k^ (u . do)) + b k^ (v . do)
-//   da = <G, S_{t-1}> - b (u . G k^),  dv = b G k^,
-//   db = v . G k^ - a (u . G k^),
-//   dk^ = b G^T v - a b (S_{t-1}^T G k^ + G^T u),
-//   G <- a (G - b (G k^) k^^T)  (dL/dS_{t-1}),
-// and dx = dx^/n - x (x . dx^)/n^3 through the L2 normalisation.
-// Persistent: workgroup i takes jobs i, i + grid, ... (job = (b*H + h)*N + c).
-template <typename Tin, typename Tg, int D>
-__global__ void __launch_bounds__(kThreads)
-gdn_bwd_tokens(GdnParams p, int C, const float* Sst, const float* Rin, float* slots, const Tg* d_mix,
-               const float* mix_w, float* dq, float* dk, float* dv, float* da, float* db) {
-  constexpr int BS = D / 16;
-  __shared__ GdnBlock<D> sm;
-  const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
-  const Tin* q = static_cast<const Tin*>(p.q);
-  const Tin* k = static_cast<const Tin*>(p.k);
-  const Tin* v = static_cast<const Tin*>(p.v);
-  const size_t HD = size_t(p.H) * D;
-  const size_t mat = size_t(D) * D;
-  float* cb = slots + size_t(blockIdx.x) * C * mat;
-  const long long jobs = (long long)p.B * p.H * p.n_chunks;
-  const bool l2 = p.l2norm != 0;
-  auto blk = [&](int i, int j) { return size_t(tr * BS + i) * D + tc * BS + j; };
-  for (long long job = blockIdx.x; job < jobs; job += gridDim.x) {
-    const int c = int(job % p.n_chunks), bh = int(job / p.n_chunks), b = bh / p.H, h = bh % p.H;
-    const float w2 = mix_w[3 * h + 2];
-    const long long t0 = (long long)c * C;
-    const int n = int(p.L - t0 < C ? p.L - t0 : C);
-    float S[BS][BS], G[BS][BS];
-    load_mat<D>(S, Sst + size_t(job) * mat);
-    // the next token's vectors and gates are loaded while the current one computes
-    const size_t tok0 = (size_t(b) * p.L + t0) * HD + size_t(h) * D;
-    const size_t g0 = (size_t(b) * p.L + t0) * p.H + h;
-    const int e = threadIdx.x < D ? threadIdx.x : 0;
-    float xk = ld(k, tok0 + e), xv = ld(v, tok0 + e), xa = p.a[g0], xb = p.b[g0];
-    for (int s = 0; s < n; ++s) {
-#pragma unroll
-      for (int i = 0; i < BS; ++i)
-#pragma unroll
-        for (int j = 0; j < BS; ++j) cb[size_t(s) * mat + blk(i, j)] = S[i][j];
-      if (threadIdx.x < D) {
-        sm.vec[0][threadIdx.x] = xk;
-        sm.vec[1][threadIdx.x] = xv;
-      }
-      const float at = xa, bt = xb;
-      __syncthreads();
-      if (s + 1 < n) {
-        xk = ld(k, tok0 + size_t(s + 1) * HD + e);
-        xv = ld(v, tok0 + size_t(s + 1) * HD + e);
-        xa = p.a[g0 + size_t(s + 1) * p.H];
-        xb = p.b[g0 + size_t(s + 1) * p.H];
-      }
-      fwd_token(sm, S, at, bt, l2, true);
-    }
-    load_mat<D>(G, Rin + size_t(job) * mat);
-    float xq = 0.f, xd = 0.f;
-    {
-      const size_t o = tok0 + size_t(n - 1) * HD + e;
-      xk = ld(k, o), xv = ld(v, o), xq = ld(q, o), xd = w2 * ld(d_mix, o);
-      xa = p.a[g0 + size_t(n - 1) * p.H], xb = p.b[g0 + size_t(n - 1) * p.H];
-    }
-    for (int s = n - 1; s >= 0; --s) {
-#pragma unroll
-      for (int i = 0; i < BS; ++i)
-#pragma unroll
-        for (int j = 0; j < BS; ++j) S[i][j] = cb[size_t(s) * mat + blk(i, j)];   // S_{t-1}
-      const long long t = t0 + s;
-      const size_t tok = (size_t(b) * p.L + t) * HD + size_t(h) * D;
-      const size_t g = (size_t(b) * p.L + t) * p.H + h;
-      const float at = xa, bt = xb;
-      // vec: 0 k, 1 v, 3 q, 5 do, 6 u = S k^, 7 S^T do, 8 G k^, 9 G^T v, 10 G^T u, 11 S^T G k^
-      // (k^ = k ik and q^ = q iq are formed on the fly)
-      if (threadIdx.x < D) {
-        sm.vec[0][threadIdx.x] = xk;
-        sm.vec[1][threadIdx.x] = xv;
-        sm.vec[3][threadIdx.x] = xq;
-        sm.vec[5][threadIdx.x] = xd;
-      }
-      __syncthreads();
-      if (s > 0) {
-        const size_t o = tok0 + size_t(s - 1) * HD + e;
-        xk = ld(k, o), xv = ld(v, o), xq = ld(q, o), xd = w2 * ld(d_mix, o);
-        xa = p.a[g0 + size_t(s - 1) * p.H], xb = p.b[g0 + size_t(s - 1) * p.H];
-      }
-      float n2[2] = {0.f, 0.f};
-      if (threadIdx.x < D) {
-        n2[0] = sm.vec[0][threadIdx.x] * sm.vec[0][threadIdx.x];
-        n2[1] = sm.vec[3][threadIdx.x] * sm.vec[3][threadIdx.x];
-      }
-      sum_n<D, 2>(sm, n2, 0);
-      const float ik = 1.f / l2n(n2[0], l2), iq = 1.f / l2n(n2[1], l2);
-#pragma unroll
-      for (int i = 0; i < BS; ++i)
-#pragma unroll
-        for (int j = 0; j < BS; ++j) G[i][j] += sm.vec[5][tr * BS + i] * sm.vec[3][tc * BS + j] * iq;
-      mv_part<D, true>(sm, S, sm.vec[0], 0);    // S k
-      mv_part<D, false>(sm, S, sm.vec[5], 1);   // S^T do
-      mv_part<D, true>(sm, G, sm.vec[0], 2);    // G k
-      mv_part<D, false>(sm, G, sm.vec[1], 3);   // G^T v
-      __syncthreads();
-      mv_finish<D>(sm, 4, {6, 7, 8, 9}, {ik, 1.f, ik, 1.f});
-      __syncthreads();
-      mv_part<D, false>(sm, G, sm.vec[6], 0);   // G^T u
-      mv_part<D, false>(sm, S, sm.vec[8], 1);   // S^T G k^
-      float sc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};  // <G, S>, u.do, v.do, u.Gk^, v.Gk^
-#pragma unroll
-      for (int i = 0; i < BS; ++i)
-#pragma unroll
-        for (int j = 0; j < BS; ++j) sc[0] += G[i][j] * S[i][j];
-      if (threadIdx.x < D) {
-        const int i = threadIdx.x;
-        sc[1] = sm.vec[6][i] * sm.vec[5][i];
-        sc[2] = sm.vec[1][i] * sm.vec[5][i];
-        sc[3] = sm.vec[6][i] * sm.vec[8][i];
-        sc[4] = sm.vec[1][i] * sm.vec[8][i];
-      }
-      sum_n<D, 5>(sm, sc, 1);   // its barrier also completes the second round's partials
-      mv_finish<D>(sm, 2, {10, 11, 0, 0}, {1.f, 1.f, 1.f, 1.f});
-      __syncthreads();
-      const float GS = sc[0], udo = sc[1], vdo = sc[2], uGk = sc[3], vGk = sc[4];
-      if (threadIdx.x == 0) {
-        da[g] = GS - bt * uGk;
-        db[g] = vGk - at * uGk;
-      }
-      float dqh = 0.f, dkh = 0.f, qi = 0.f, ki = 0.f;
-      float d2[2] = {0.f, 0.f};
-      if (threadIdx.x < D) {
-        const int i = threadIdx.x;
-        ki = sm.vec[0][i];
-        qi = sm.vec[3][i];
-        const float kh = ki * ik;
-        dqh = at * (sm.vec[7][i] - bt * kh * udo) + bt * kh * vdo;
-        dkh = bt * sm.vec[9][i] - at * bt * (sm.vec[11][i] + sm.vec[10][i]);
-        dv[tok + i] += bt * sm.vec[8][i];
-        d2[0] = qi * dqh;
-        d2[1] = ki * dkh;
-      }
-      sum_n<D, 2>(sm, d2, 2);
-      if (threadIdx.x < D) {
-        const int i = threadIdx.x;
-        dq[tok + i] += l2 ? dqh * iq - qi * d2[0] * iq * iq * iq : dqh;
-        dk[tok + i] += l2 ? dkh * ik - ki * d2[1] * ik * ik * ik : dkh;
-      }
-#pragma unroll
-      for (int i = 0; i < BS; ++i)
-#pragma unroll
-        for (int j = 0; j < BS; ++j)
-          G[i][j] = at * (G[i][j] - bt * sm.vec[8][tr * BS + i] * sm.vec[0][tc * BS + j] * ik);
-      __syncthreads();
-    }
-  }
-}
-
 // dw[h, i] = <d_mix, o_i> in two deterministic stages: per-head partial sums
 // over grid.y slices (grid (H, slices)), then their sum in a fixed order.
 template <typename Tg, typename Tout>
@@ -831,16 +441,15 @@ hipError_t launch_bwd_t(const BwdArgs& x, hipStream_t st) {
                        x.dk, x.dv, x.scale);
   }
   const unsigned heads = unsigned(x.gdn.B * x.gdn.H);
-  const unsigned jobs = heads * unsigned(x.gdn.n_chunks);
-  const dim3 pgrid(jobs, (D + 63) / 64);
-  hipLaunchKernelGGL((gdn_bwd_prep<Tin, Tg, D, 0>), pgrid, dim3(kThreads), 0, st, x.gdn, x.C, g, x.mix_w, x.Am, x.AmT);
-  hipLaunchKernelGGL((gdn_bwd_prep<Tin, Tg, D, 1>), pgrid, dim3(kThreads), 0, st, x.gdn, x.C, g, x.mix_w, x.Um, x.AmT);
-  hipLaunchKernelGGL((gdn_bwd_prep<Tin, Tg, D, 2>), pgrid, dim3(kThreads), 0, st, x.gdn, x.C, g, x.mix_w, x.Xm, x.AmT);
+  const int in_dt = std::is_same<Tin, bf16>::value ? HLTA_BF16 : HLTA_F32;
+  const int out_dt = std::is_same<Tg, bf16>::value ? HLTA_BF16 : HLTA_F32;
+  hipError_t e = launch_gdn_bwd_mat(x, D, in_dt, out_dt, 0, st);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((gdn_bwd_chain<D>), dim3(heads, D / kChainRows, 2), dim3(kThreads), 0, st, x.gdn.n_chunks,
                      x.gdn.S0, x.Am, x.AmT, x.Um, x.Xm, x.Sst, x.Rin, x.dS0);
-  hipLaunchKernelGGL((gdn_bwd_tokens<Tin, Tg, D>), dim3(unsigned(x.n_slots)), dim3(kThreads), 0, st, x.gdn, x.C,
-                     x.Sst, x.Rin, x.slots, g, x.mix_w, x.dq, x.dk, x.dv, x.da, x.db);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_gdn_bwd_mat(x, D, in_dt, out_dt, 1, st);
 }
 
 template <typename Tin, typename Tg>

@@ -419,6 +419,7 @@ hlta_status hlta_bwd(const hlta_config* cfg, const void* q, const void* k, const
   for (int i = 0; i < 6; ++i) *mats[i] = reinterpret_cast<float*>(ws + bp.mat_off + i * bp.mat_bytes);
   x.slots = reinterpret_cast<float*>(ws + bp.slot_off);
   x.n_slots = bp.n_slots;
+  x.slot_floats = bp.slot_floats;
   x.dw_part = reinterpret_cast<float*>(ws + bp.part_off);
   x.dw_slices = kDwSlices;
   x.C = cfg->gdn_chunk;

@@ -194,7 +194,7 @@ hlta_status make_bwd_plan(const hlta_config* cfg, BwdPlan* plan) {
   int64_t stats = 0, mats = 0, mats6 = 0, slots = 0, part = 0, off = 0, total = 0;
   if (!prod_ok({bh, L, 2, 4}, &stats) || !align256_ok(stats, &stats) ||
       !prod_ok({bh, nch, dd, 4}, &mats) || !align256_ok(mats, &mats) || !mul_ok(mats, 6, &mats6) ||
-      !prod_ok({p.n_slots, C, dd, 4}, &slots) || !align256_ok(slots, &slots) ||
+      !prod_ok({p.n_slots, int64_t(bwd_slot_floats(cfg->d)), 4}, &slots) || !align256_ok(slots, &slots) ||
       !prod_ok({cfg->H, kDwSlices, 3, 4}, &part) || !align256_ok(part, &part) ||
       !add_ok(stats, stats, &off) || !add_ok(off, mats6, &off) || !add_ok(off, slots, &total) || !add_ok(total, part, &total))
     return fail(HLTA_E_SHAPE, "workspace size overflows int64");
@@ -202,6 +202,7 @@ hlta_status make_bwd_plan(const hlta_config* cfg, BwdPlan* plan) {
   p.mat_off = 2 * p.stats_bytes;
   p.mat_bytes = size_t(mats);
   p.slot_off = p.mat_off + 6 * p.mat_bytes;
+  p.slot_floats = bwd_slot_floats(cfg->d);
   p.part_off = p.slot_off + size_t(slots);
   p.total = size_t(total);
   *plan = p;

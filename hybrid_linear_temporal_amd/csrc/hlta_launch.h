@@ -97,14 +97,19 @@ struct BwdArgs {
   float* Xm;         //   ... the chunk's own adjoint from zero
   float* Sst;        //   ... state at the chunk's start
   float* Rin;        //   ... adjoint reaching the chunk's end
-  float* slots;      // [n_slots, C, d, d] workspace: recomputed states, one slot per workgroup
+  float* slots;      // [n_slots, slot_floats] workspace: per-workgroup scratch of the memory's backward
   int n_slots;
+  size_t slot_floats;
   float* dw_part;    // [H, dw_slices, 3] workspace
   int dw_slices;
   int C;
   float scale;
   int attn_mfma;     // softmax branches on the bf16 MFMA kernels (bf16 in and out, d = 128, P >= 64)
 };
+
+// The gated delta rule's backward in matrix form (per chunk): phase 0 the
+// chunk maps Am, AmT, Um, Xm; phase 1 (after the chains) the token gradients.
+hipError_t launch_gdn_bwd_mat(const BwdArgs& x, int d, int in_dt, int out_dt, int phase, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& x, int d, int in_dt, int out_dt, hipStream_t st);
 
 }  // namespace hlta

@@ -64,9 +64,9 @@ def short_name(name: str) -> str | None:
                            ("14attn_bwd_statsI", "attn_bwd_stats (fp32)"),
                            ("11attn_bwd_dqI", "attn_bwd_dq (fp32)"),
                            ("13attn_bwd_dkdvI", "attn_bwd_dkdv (fp32)"),
-                           ("12gdn_bwd_prepI", "gdn_bwd_prep"),
+                           ("16gdn_bwd_mat_prepI", "gdn_bwd_mat_prep"),
                            ("13gdn_bwd_chainI", "gdn_bwd_chain"),
-                           ("14gdn_bwd_tokensI", "gdn_bwd_tokens"),
+                           ("16gdn_bwd_mat_gradI", "gdn_bwd_mat_grad"),
                            ("12dmix_partialI", "dmix_partial"),
                            ("10dmix_finalE", "dmix_final")):
         if mangled in short:
