@@ -57,32 +57,39 @@ __device__ __forceinline__ float4 ld4f(const bf16* p) {
                      static_cast<float>(x[3]));
 }
 
-// C = alpha op(A) op(B) (+ C when acc): op(A) M x K, op(B) K x N, row-major
+// C = alpha op(A) op(B) (+ Z when Z is given; Z may be C itself): op(A)
+// M x K, op(B) K x N, Z M x N, row-major
 // with leading dimensions (multiples of 4, 16-byte aligned rows); TA: A is
 // stored K x M, TB: B is stored N x K. Products on bf16 MFMA with each factor
 // split into a high and a low bf16 part (x = hi + lo, about 16 significant
 // bits): hi*hi + hi*lo + lo*hi in fp32 accumulation, so the result keeps
-// close to fp32 accuracy. K goes through LDS in slices of 64, staged as the
-// split parts in rows of 72 bf16 (k contiguous, 16-byte reads free of bank
-// conflicts); wave w computes the 32 x 32 output tiles w, w + 4, .. with
+// close to fp32 accuracy. K goes through LDS in slices of up to 64; a slice's
+// fp32 operands are loaded in batches of eight 16-byte loads per thread (all
+// in flight together), split, and staged in the layout they are stored in,
+// so every staging store writes four consecutive values:
+//  * an operand stored with k contiguous (A: M x K, B: N x K) as rows of 72
+//    bf16 (one row per output row or column; 16-byte reads of 8 consecutive
+//    k, free of bank conflicts);
+//  * an operand stored with k as its rows (A: K x M, B: K x N) as k-major rows
+//    of M (N) bf16, read with ds_read_b64_tr_b16, which gives each lane four
+//    consecutive k of its own column; the 8-byte chunks of a row are
+//    XOR-permuted by the row's index mod 4 so the four rows of one read hit
+//    distinct banks.
+// Wave w computes the 32 x 32 output tiles w, w + 4, .. with
 // v_mfma_f32_32x32x16_bf16 (A: lane = row l%32, k 8(l/32) ..; B: lane =
 // column l%32, same k; C: lane = column l%32, rows 8(r/4) + 4(l/32) + r%4).
 // Ends with a barrier, so C is visible to the whole workgroup (C must not
 // alias A or B).
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kKS = 64;   // k per slice
 constexpr int kRow = 72;  // bf16 per staged row (64 + pad)
 constexpr int kLdsFloats = 4 * 128 * kRow / 2;   // hi and lo of A and B, up to 128 rows each
 
-__device__ __forceinline__ void split_store(bf16* hi, bf16* lo, float x) {
-  const bf16 h = static_cast<bf16>(x);
-  *hi = h;
-  *lo = static_cast<bf16>(x - static_cast<float>(h));
-}
-// four consecutive k of one row: one 8-byte store each for hi and lo
+// four consecutive values: one 8-byte store each for hi and lo
 __device__ __forceinline__ void split_store4(bf16* hi, bf16* lo, const float4& x) {
-  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
   const bf16x4_t h = {static_cast<bf16>(x.x), static_cast<bf16>(x.y), static_cast<bf16>(x.z), static_cast<bf16>(x.w)};
   const bf16x4_t l = {static_cast<bf16>(x.x - static_cast<float>(h[0])), static_cast<bf16>(x.y - static_cast<float>(h[1])),
                       static_cast<bf16>(x.z - static_cast<float>(h[2])), static_cast<bf16>(x.w - static_cast<float>(h[3]))};
@@ -90,65 +97,132 @@ __device__ __forceinline__ void split_store4(bf16* hi, bf16* lo, const float4& x
   *reinterpret_cast<bf16x4_t*>(lo) = l;
 }
 
+// k-major staging of an operand with W columns: element (k, m) of the slice
+// sits in row k at 8-byte chunk (m / 4) ^ kmaj_sw(k), value m % 4.
+template <int W>
+__device__ __forceinline__ int kmaj_sw(int k) {
+  return W == 128 ? 8 * (k & 3) : (W == 64 ? 8 * ((k & 3) >> 1) : 0);
+}
+template <int W>
+__device__ __forceinline__ int kmaj_off(int k, int m) {   // bf16 offset of chunk start
+  return k * W + 4 * ((m >> 2) ^ kmaj_sw<W>(k));
+}
+// Operand of one MFMA from k-major staging: lane l gets column c0 + l%32 and
+// k = k0 + 8 (l / 32) .. + 7 (two transposed 8-byte reads of four k each).
+template <int W>
+__device__ __forceinline__ bf16x8_t ld_kmaj(const bf16* st, int k0, int c0, int lane) {
+  const int j = lane & 15, e = j >> 2, q = j & 3;
+  const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * q;   // first of this lane's four addressed columns
+  const int kb = k0 + 8 * (lane >> 5);
+  const bf16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(st + kmaj_off<W>(kb + e, col)));
+  const bf16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(st + kmaj_off<W>(kb + 4 + e, col)));
+  return bf16x8_t{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+}
+
 template <int M, int N, int K, bool TA, bool TB>
 __device__ __attribute__((noinline)) void mm(float* C, int ldc, const float* A, int lda, const float* B, int ldb,
-                                             float alpha, bool acc, float* lds) {
+                                             float alpha, const float* Z, float* lds) {
   constexpr int KS = K < kKS ? K : kKS;   // k of one slice
   static_assert(M % 32 == 0 && N % 32 == 0 && K % KS == 0 && KS % 16 == 0 && M <= 128 && N <= 128, "aligned shapes");
   constexpr int NT = (M / 32) * (N / 32), TPW = (NT + 3) / 4;   // tiles, tiles per wave
+  constexpr int NA = M * KS / 4 / kNT, NB = N * KS / 4 / kNT;   // float4 of A and B per thread per slice
+  static_assert(NA * kNT * 4 == M * KS && NB * kNT * 4 == N * KS, "slices split evenly over the threads");
+  constexpr int SA = TA ? KS * M : M * kRow, SB = TB ? N * kRow : KS * N;   // bf16 per staged part
+  static_assert(2 * (SA + SB) <= 2 * kLdsFloats, "staging fits");
   bf16* Ahi = reinterpret_cast<bf16*>(lds);
-  bf16* Alo = Ahi + M * kRow;
-  bf16* Bhi = Alo + M * kRow;
-  bf16* Blo = Bhi + N * kRow;
+  bf16* Alo = Ahi + SA;
+  bf16* Bhi = Alo + SA;
+  bf16* Blo = Bhi + SB;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   f32x16_t c[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u)
 #pragma unroll
     for (int r = 0; r < 16; ++r) c[u][r] = 0.f;
+  // staging in rounds of at most 8 float4 per thread (A's first, then B's),
+  // each round's loads in flight together
+  constexpr int kBatch = 8;
+#pragma unroll 1
   for (int k0 = 0; k0 < K; k0 += KS) {
-    __syncthreads();
-    for (int e = tid; e < M * KS / 4; e += kNT) {
-      if (TA) {
-        const int kk = e / (M / 4), i4 = e % (M / 4);
-        const float4 x = *reinterpret_cast<const float4*>(A + size_t(k0 + kk) * lda + 4 * i4);
-        split_store(Ahi + (4 * i4 + 0) * kRow + kk, Alo + (4 * i4 + 0) * kRow + kk, x.x);
-        split_store(Ahi + (4 * i4 + 1) * kRow + kk, Alo + (4 * i4 + 1) * kRow + kk, x.y);
-        split_store(Ahi + (4 * i4 + 2) * kRow + kk, Alo + (4 * i4 + 2) * kRow + kk, x.z);
-        split_store(Ahi + (4 * i4 + 3) * kRow + kk, Alo + (4 * i4 + 3) * kRow + kk, x.w);
-      } else {
-        const int i = e / (KS / 4), k4 = e % (KS / 4);
-        const float4 x = *reinterpret_cast<const float4*>(A + size_t(i) * lda + k0 + 4 * k4);
-        split_store4(Ahi + i * kRow + 4 * k4, Alo + i * kRow + 4 * k4, x);
+    __syncthreads();   // the previous slice's products are done with the staging area
+#pragma unroll
+    for (int u0 = 0; u0 < NA + NB; u0 += kBatch) {
+      float4 x[kBatch];
+#pragma unroll
+      for (int v = 0; v < kBatch; ++v) {
+        const int u = u0 + v;
+        if (u < NA) {
+          const int e = tid + u * kNT;
+          if (TA) {
+            const int kk = e / (M / 4), i4 = e % (M / 4);
+            x[v] = *reinterpret_cast<const float4*>(A + size_t(k0 + kk) * lda + 4 * i4);
+          } else {
+            const int i = e / (KS / 4), k4 = e % (KS / 4);
+            x[v] = *reinterpret_cast<const float4*>(A + size_t(i) * lda + k0 + 4 * k4);
+          }
+        } else if (u < NA + NB) {
+          const int e = tid + (u - NA) * kNT;
+          if (TB) {
+            const int j = e / (KS / 4), k4 = e % (KS / 4);
+            x[v] = *reinterpret_cast<const float4*>(B + size_t(j) * ldb + k0 + 4 * k4);
+          } else {
+            const int kk = e / (N / 4), j4 = e % (N / 4);
+            x[v] = *reinterpret_cast<const float4*>(B + size_t(k0 + kk) * ldb + 4 * j4);
+          }
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < kBatch; ++v) {
+        const int u = u0 + v;
+        if (u < NA) {
+          const int e = tid + u * kNT;
+          if (TA) {
+            const int kk = e / (M / 4), i4 = e % (M / 4);
+            const int o = kmaj_off<M>(kk, 4 * i4);
+            split_store4(Ahi + o, Alo + o, x[v]);
+          } else {
+            const int i = e / (KS / 4), k4 = e % (KS / 4);
+            split_store4(Ahi + i * kRow + 4 * k4, Alo + i * kRow + 4 * k4, x[v]);
+          }
+        } else if (u < NA + NB) {
+          const int e = tid + (u - NA) * kNT;
+          if (TB) {
+            const int j = e / (KS / 4), k4 = e % (KS / 4);
+            split_store4(Bhi + j * kRow + 4 * k4, Blo + j * kRow + 4 * k4, x[v]);
+          } else {
+            const int kk = e / (N / 4), j4 = e % (N / 4);
+            const int o = kmaj_off<N>(kk, 4 * j4);
+            split_store4(Bhi + o, Blo + o, x[v]);
+          }
+        }
       }
     }
-    for (int e = tid; e < N * KS / 4; e += kNT) {
-      if (TB) {
-        const int j = e / (KS / 4), k4 = e % (KS / 4);
-        const float4 x = *reinterpret_cast<const float4*>(B + size_t(j) * ldb + k0 + 4 * k4);
-        split_store4(Bhi + j * kRow + 4 * k4, Blo + j * kRow + 4 * k4, x);
-      } else {
-        const int kk = e / (N / 4), j4 = e % (N / 4);
-        const float4 x = *reinterpret_cast<const float4*>(B + size_t(k0 + kk) * ldb + 4 * j4);
-        split_store(Bhi + (4 * j4 + 0) * kRow + kk, Blo + (4 * j4 + 0) * kRow + kk, x.x);
-        split_store(Bhi + (4 * j4 + 1) * kRow + kk, Blo + (4 * j4 + 1) * kRow + kk, x.y);
-        split_store(Bhi + (4 * j4 + 2) * kRow + kk, Blo + (4 * j4 + 2) * kRow + kk, x.z);
-        split_store(Bhi + (4 * j4 + 3) * kRow + kk, Blo + (4 * j4 + 3) * kRow + kk, x.w);
-      }
-    }
     __syncthreads();
+    // k steps outermost and only partly unrolled, so the operand reads of a
+    // step are not all hoisted at once (the register file holds two workgroups)
+#pragma unroll 2
+    for (int ks = 0; ks < KS / 16; ++ks) {
+      const int ko = 16 * ks + 8 * hl;
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int t = wave + 4 * u;
-      if (t < NT) {
-        const int tm = t / (N / 32), tn = t % (N / 32);
-#pragma unroll
-        for (int ks = 0; ks < KS / 16; ++ks) {
-          const int ko = 16 * ks + 8 * hl;
-          const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(Ahi + (32 * tm + l32) * kRow + ko);
-          const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(Alo + (32 * tm + l32) * kRow + ko);
-          const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(Bhi + (32 * tn + l32) * kRow + ko);
-          const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(Blo + (32 * tn + l32) * kRow + ko);
+      for (int u = 0; u < TPW; ++u) {
+        const int t = wave + 4 * u;
+        if (t < NT) {
+          const int tm = t / (N / 32), tn = t % (N / 32);
+          bf16x8_t ah, al, bh, bl;
+          if (TA) {
+            ah = ld_kmaj<M>(Ahi, 16 * ks, 32 * tm, lane);
+            al = ld_kmaj<M>(Alo, 16 * ks, 32 * tm, lane);
+          } else {
+            ah = *reinterpret_cast<const bf16x8_t*>(Ahi + (32 * tm + l32) * kRow + ko);
+            al = *reinterpret_cast<const bf16x8_t*>(Alo + (32 * tm + l32) * kRow + ko);
+          }
+          if (TB) {
+            bh = *reinterpret_cast<const bf16x8_t*>(Bhi + (32 * tn + l32) * kRow + ko);
+            bl = *reinterpret_cast<const bf16x8_t*>(Blo + (32 * tn + l32) * kRow + ko);
+          } else {
+            bh = ld_kmaj<N>(Bhi, 16 * ks, 32 * tn, lane);
+            bl = ld_kmaj<N>(Blo, 16 * ks, 32 * tn, lane);
+          }
           c[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, c[u], 0, 0, 0);
           c[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, c[u], 0, 0, 0);
           c[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, c[u], 0, 0, 0);
@@ -161,27 +235,85 @@ __device__ __attribute__((noinline)) void mm(float* C, int ldc, const float* A, 
     const int t = wave + 4 * u;
     if (t < NT) {
       const int tm = t / (N / 32), tn = t % (N / 32);
+      const size_t c0 = size_t(32 * tm + 4 * hl) * ldc + 32 * tn + l32;
+      auto at = [&](int r) { return c0 + size_t(8 * (r >> 2) + (r & 3)) * ldc; };
+      float z[16];   // all 16 addends in flight before the first store
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 32 * tm + 8 * (r >> 2) + 4 * hl + (r & 3), col = 32 * tn + l32;
-        float* cp = C + size_t(row) * ldc + col;
-        *cp = alpha * c[u][r] + (acc ? *cp : 0.f);
-      }
+      for (int r = 0; r < 16; ++r) z[r] = Z ? Z[at(r)] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) C[at(r)] = alpha * c[u][r] + z[r];
     }
   }
   __syncthreads();
 }
 
-// out[t] = sum_j X[t][j] Y[t][j], t < CM (a wave per row, lanes over columns)
-template <int D>
-__device__ void rowdot(float* out, const float* X, const float* Y) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int t = wave; t < CM; t += kNT / 64) {
-    float s = 0.f;
-    for (int j = lane; j < D; j += 64) s += X[size_t(t) * D + j] * Y[size_t(t) * D + j];
+// Elementwise passes over the chunk's arrays as 16-byte vectors: ld(e)
+// gathers what position e needs (returns a small struct), st(e, x) writes the
+// results; each thread takes positions tid, tid + 256, .. and issues the
+// loads of kBatch positions before the first store, so their latencies
+// overlap (the arrays live in the workspace, mostly beyond the caches).
+template <int N4, int kBatch, typename LD, typename ST>
+__device__ __forceinline__ void ew(LD ld, ST st) {
+  static_assert(N4 % kNT == 0, "whole passes");
+  constexpr int PER = N4 / kNT;
+  using X = decltype(ld(0));
+  // an opaque copy of the thread index: addresses are formed here, not shared
+  // with (and kept live from) other passes
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == 0) out[t] = s;
+  for (int u0 = 0; u0 < PER; u0 += kBatch) {
+    X x[kBatch];
+#pragma unroll
+    for (int v = 0; v < kBatch; ++v)
+      if (u0 + v < PER) x[v] = ld(tid + (u0 + v) * kNT);
+#pragma unroll
+    for (int v = 0; v < kBatch; ++v)
+      if (u0 + v < PER) st(tid + (u0 + v) * kNT, x[v]);
+    __builtin_amdgcn_sched_barrier(0);   // the next batch's loads stay behind these stores
+  }
+}
+struct F4x2 { float4 a, b; };
+struct F4x3 { float4 a, b, c; };
+struct F4x4 { float4 a, b, c, d; };
+__device__ __forceinline__ float4 operator*(float s, const float4& x) { return make_float4(s * x.x, s * x.y, s * x.z, s * x.w); }
+__device__ __forceinline__ float4 operator+(const float4& x, const float4& y) {
+  return make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
+}
+__device__ __forceinline__ float4 operator-(const float4& x, const float4& y) {
+  return make_float4(x.x - y.x, x.y - y.y, x.z - y.z, x.w - y.w);
+}
+__device__ __forceinline__ float dot4(const float4& x, const float4& y) {
+  return x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+}
+__device__ __forceinline__ float4* f4(float* p) { return reinterpret_cast<float4*>(p); }
+__device__ __forceinline__ const float4* f4(const float* p) { return reinterpret_cast<const float4*>(p); }
+
+// out[t] = sum_j X[t][j] Y[t][j] for the W-wide rows t < CM: row t's W/4
+// vectors go to W/4 consecutive lanes, all of a thread's loads in flight
+// together, the partial sums joined by shuffles.
+template <int W>
+__device__ void rowdot(float* out, const float* X, const float* Y) {
+  constexpr int LPR = W / 4, RPP = kNT / LPR, PASSES = CM / RPP, HALF = PASSES > 4 ? PASSES / 2 : PASSES;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));   // addresses formed here (see ew)
+  const int c4 = tid % LPR, r0 = tid / LPR;
+#pragma unroll
+  for (int q0 = 0; q0 < PASSES; q0 += HALF) {
+    float4 x[HALF], y[HALF];
+#pragma unroll
+    for (int q = 0; q < HALF; ++q) {
+      x[q] = f4(X)[(r0 + (q0 + q) * RPP) * LPR + c4];
+      y[q] = f4(Y)[(r0 + (q0 + q) * RPP) * LPR + c4];
+    }
+#pragma unroll
+    for (int q = 0; q < HALF; ++q) {
+      float d = dot4(x[q], y[q]);
+#pragma unroll
+      for (int off = 1; off < LPR; off <<= 1) d += __shfl_xor(d, off);
+      if (c4 == 0) out[r0 + (q0 + q) * RPP] = d;
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
 }
@@ -190,8 +322,7 @@ __device__ void rowdot(float* out, const float* X, const float* Y) {
 // LDS; four lanes per column j (lane q holds t_m for m = q mod 4) solve it by
 // forward substitution, the partial dot products joined by two shuffles.
 __device__ __attribute__((noinline)) void tri_inverse(float* Tm, const float* L, const float* b, float* lds) {
-  for (int e = threadIdx.x; e < CM * CM / 4; e += kNT)
-    reinterpret_cast<float4*>(lds)[e] = reinterpret_cast<const float4*>(L)[e];
+  ew<CM * CM / 4, 2>([&](int e) { return f4(L)[e]; }, [&](int e, const float4& x) { f4(lds)[e] = x; });
   __syncthreads();
   const int j = threadIdx.x >> 2, q = threadIdx.x & 3;
   float t[CM / 4];
@@ -235,10 +366,30 @@ enum { sGK = 0, sT, sP, sDP, sDPG, sE1, sE2 };
 // Chunk vectors in LDS
 struct ChunkVec {
   float g[CM], gam[CM], De[CM], b[CM], a[CM], rk[CM], rq[CM];
-  float v0[CM], v1[CM], v2[CM], v3[CM], v4[CM];
+  float v0[CM], v1[CM], v2[CM], v3[CM], v4[CM], gs[CM];
+  float cpart[kNT / 64][CM];   // per-wave partial column sums
   float red[kNT / 64];
   float gC;
 };
+
+// [CM][CM] masked by the causal pattern: strict (j < i) or inclusive (j <= i),
+// each kept entry scaled by exp(g_i - g_j)
+template <bool kStrict>
+__device__ void gam_mask(float* X, const ChunkVec& v) {
+  ew<CM * CM / 4, 2>([&](int e) { return f4(X)[e]; },
+                     [&](int e, float4 x) {
+                       const int i = (4 * e) / CM, j0 = (4 * e) % CM;
+                       float* xs = reinterpret_cast<float*>(&x);
+#pragma unroll
+                       for (int q = 0; q < 4; ++q) {
+                         const int j = j0 + q;
+                         const bool keep = kStrict ? j < i : j <= i;
+                         xs[q] = keep ? expf(v.g[i] - v.g[j]) * xs[q] : 0.f;
+                       }
+                       f4(X)[e] = x;
+                     });
+  __syncthreads();
+}
 
 // Loads chunk c of head (b, h): K, Q (normalised), V, dO = w2 d_mix, gates,
 // then forms diag(b gamma) K, De K, diag(b) V, strict_lower(Gam . K K^T), T,
@@ -255,22 +406,26 @@ __device__ void chunk_forward(const GdnParams& p, int C, const Tg* d_mix, float 
   const Tin* k = static_cast<const Tin*>(p.k);
   const Tin* vv = static_cast<const Tin*>(p.v);
   float *K = s.cd(sK), *Q = s.cd(sQ), *V = s.cd(sV), *dO = s.cd(sDO);
-  for (int e = threadIdx.x; e < CM * D / 4; e += kNT) {
-    const int t = (4 * e) / D, j = (4 * e) % D;
-    float4 xk = {0.f, 0.f, 0.f, 0.f}, xq = xk, xv = xk, xd = xk;
-    if (t < n) {
-      const size_t o = tok0 + size_t(t) * HD + j;
-      xk = ld4f(k + o);
-      xq = ld4f(q + o);
-      xv = ld4f(vv + o);
-      xd = ld4f(d_mix + o);
-      xd = make_float4(w2 * xd.x, w2 * xd.y, w2 * xd.z, w2 * xd.w);
-    }
-    reinterpret_cast<float4*>(K)[e] = xk;
-    reinterpret_cast<float4*>(Q)[e] = xq;
-    reinterpret_cast<float4*>(V)[e] = xv;
-    reinterpret_cast<float4*>(dO)[e] = xd;
-  }
+  ew<CM * D / 4, 2>(
+      [&](int e) {
+        const int t = (4 * e) / D, j = (4 * e) % D;
+        F4x4 x;
+        x.a = x.b = x.c = x.d = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (t < n) {
+          const size_t o = tok0 + size_t(t) * HD + j;
+          x.a = ld4f(k + o);
+          x.b = ld4f(q + o);
+          x.c = ld4f(vv + o);
+          x.d = ld4f(d_mix + o);
+        }
+        return x;
+      },
+      [&](int e, const F4x4& x) {
+        f4(K)[e] = x.a;
+        f4(Q)[e] = x.b;
+        f4(V)[e] = x.c;
+        f4(dO)[e] = w2 * x.d;
+      });
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (wave == 0) {
     const int t = lane;
@@ -289,100 +444,93 @@ __device__ void chunk_forward(const GdnParams& p, int C, const Tg* d_mix, float 
     v.b[t] = bt;
   }
   __syncthreads();   // K, Q written; gates
-  {
-    // norms: a wave per row, lanes over columns
-    for (int t = wave; t < CM; t += kNT / 64) {
-      float sk = 0.f, sq = 0.f;
-      for (int j = lane; j < D; j += 64) {
-        const float kx = K[size_t(t) * D + j], qx = Q[size_t(t) * D + j];
-        sk += kx * kx;
-        sq += qx * qx;
-      }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        sk += __shfl_xor(sk, off);
-        sq += __shfl_xor(sq, off);
-      }
-      if (lane == 0) {
-        v.rk[t] = p.l2norm ? 1.f / sqrtf(sk + kEps) : 1.f;
-        v.rq[t] = p.l2norm ? 1.f / sqrtf(sq + kEps) : 1.f;
-        v.De[t] = expf(v.g[CM - 1] - v.g[t]);
-      }
-    }
-    if (threadIdx.x == 0) v.gC = v.gam[CM - 1];
+  rowdot<D>(v.v0, K, K);
+  rowdot<D>(v.v1, Q, Q);
+  if (threadIdx.x < CM) {
+    const int t = threadIdx.x;
+    v.rk[t] = p.l2norm ? 1.f / sqrtf(v.v0[t] + kEps) : 1.f;
+    v.rq[t] = p.l2norm ? 1.f / sqrtf(v.v1[t] + kEps) : 1.f;
+    v.De[t] = expf(v.g[CM - 1] - v.g[t]);
   }
+  if (threadIdx.x == 0) v.gC = v.gam[CM - 1];
   __syncthreads();
   float *BK = s.cd(sBK), *DK = s.cd(sDK), *BV = s.cd(sBV);
-  for (int e = threadIdx.x; e < CM * D; e += kNT) {
-    const int t = e / D;
-    const float kx = K[e] * v.rk[t];
-    K[e] = kx;
-    Q[e] *= v.rq[t];
-    BK[e] = v.b[t] * v.gam[t] * kx;
-    DK[e] = v.De[t] * kx;
-    BV[e] = v.b[t] * V[e];
-  }
+  ew<CM * D / 4, 2>(
+      [&](int e) {
+        F4x3 x;
+        x.a = f4(K)[e];
+        x.b = f4(Q)[e];
+        x.c = f4(V)[e];
+        return x;
+      },
+      [&](int e, const F4x3& x) {
+        const int t = (4 * e) / D;
+        const float4 kx = v.rk[t] * x.a;
+        f4(K)[e] = kx;
+        f4(Q)[e] = v.rq[t] * x.b;
+        f4(BK)[e] = (v.b[t] * v.gam[t]) * kx;
+        f4(DK)[e] = v.De[t] * kx;
+        f4(BV)[e] = v.b[t] * x.c;
+      });
   __syncthreads();
   // GK = strict_lower(Gam . K K^T), T = (I + diag(b) GK)^-1
   float *GK = s.cc(sGK), *Tm = s.cc(sT), *P = s.cc(sP);
-  mm<CM, CM, D, false, true>(GK, CM, K, D, K, D, 1.f, false, lds);
-  for (int e = threadIdx.x; e < CM * CM; e += kNT) {
-    const int i = e / CM, j = e % CM;
-    GK[e] = j < i ? expf(v.g[i] - v.g[j]) * GK[e] : 0.f;
-  }
-  __syncthreads();
+  mm<CM, CM, D, false, true>(GK, CM, K, D, K, D, 1.f, nullptr, lds);
+  gam_mask<true>(GK, v);
   tri_inverse(Tm, GK, v.b, lds);
-  mm<CM, D, CM, false, false>(s.cd(sW), D, Tm, CM, BK, D, 1.f, false, lds);
-  mm<CM, D, CM, false, false>(s.cd(sUp), D, Tm, CM, BV, D, 1.f, false, lds);
+  mm<CM, D, CM, false, false>(s.cd(sW), D, Tm, CM, BK, D, 1.f, nullptr, lds);
+  mm<CM, D, CM, false, false>(s.cd(sUp), D, Tm, CM, BV, D, 1.f, nullptr, lds);
   // P = lower(Gam . Q K^T)
-  mm<CM, CM, D, false, true>(P, CM, Q, D, K, D, 1.f, false, lds);
-  for (int e = threadIdx.x; e < CM * CM; e += kNT) {
-    const int i = e / CM, j = e % CM;
-    P[e] = j <= i ? expf(v.g[i] - v.g[j]) * P[e] : 0.f;
-  }
-  __syncthreads();
+  mm<CM, CM, D, false, true>(P, CM, Q, D, K, D, 1.f, nullptr, lds);
+  gam_mask<false>(P, v);
 }
 
 // Per chunk: M (Am), M^T (AmT), N (Um) and the chunk's own adjoint X (Xm).
 template <typename Tin, typename Tg, int D>
-__global__ void __launch_bounds__(kNT)
+__global__ void __launch_bounds__(kNT, 2)
 gdn_bwd_mat_prep(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float* slots, size_t slot_floats,
                  float* Am, float* AmT, float* Um, float* Xm) {
   __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];   // product staging or the inverse
   __shared__ ChunkVec v;
-  const Slot<D> s{slots + size_t(blockIdx.x) * slot_floats};
+  float* const slot = slots + size_t(blockIdx.x) * slot_floats;
   const long long jobs = (long long)p.B * p.H * p.n_chunks;
   const size_t mat = size_t(D) * D;
   for (long long job = blockIdx.x; job < jobs; job += gridDim.x) {
     const int c = int(job % p.n_chunks), bh = int(job / p.n_chunks), b = bh / p.H, h = bh % p.H;
+    // the slot's address is opaque to the compiler inside the loop, so it does
+    // not hoist every per-thread address of the chunk's arrays out of it
+    float* sb = slot;
+    asm volatile("" : "+s"(sb));
+    const Slot<D> s{sb};
     chunk_forward<Tin, Tg, D>(p, C, d_mix, mix_w[3 * h + 2], c, b, h, s, v, lds);
     float *W = s.cd(sW), *Up = s.cd(sUp), *DK = s.cd(sDK), *Q = s.cd(sQ), *dO = s.cd(sDO), *Y = s.cd(sX1);
     float* am = Am + size_t(job) * mat;
     float* amt = AmT + size_t(job) * mat;
-    mm<D, D, CM, true, false>(am, D, W, D, DK, D, -1.f, false, lds);    // -W^T De K
-    mm<D, D, CM, true, false>(amt, D, DK, D, W, D, -1.f, false, lds);   // -K^T De W
-    mm<D, D, CM, true, false>(Um + size_t(job) * mat, D, Up, D, DK, D, 1.f, false, lds);
+    mm<D, D, CM, true, false>(am, D, W, D, DK, D, -1.f, nullptr, lds);    // -W^T De K
+    mm<D, D, CM, true, false>(amt, D, DK, D, W, D, -1.f, nullptr, lds);   // -K^T De W
+    mm<D, D, CM, true, false>(Um + size_t(job) * mat, D, Up, D, DK, D, 1.f, nullptr, lds);
     for (int i = threadIdx.x; i < D; i += kNT) {
       am[size_t(i) * D + i] += v.gC;
       amt[size_t(i) * D + i] += v.gC;
     }
-    // X = dO^T (diag(gamma) Q - P W)
-    mm<CM, D, CM, false, false>(Y, D, s.cc(sP), CM, W, D, -1.f, false, lds);
-    for (int e = threadIdx.x; e < CM * D; e += kNT) Y[e] += v.gam[e / D] * Q[e];
+    // X = dO^T (diag(gamma) Q - P W): Y = diag(gamma) Q first, then Y -= P W
+    ew<CM * D / 4, 2>([&](int e) { return f4(Q)[e]; },
+                      [&](int e, const float4& x) { f4(Y)[e] = v.gam[(4 * e) / D] * x; });
     __syncthreads();
-    mm<D, D, CM, true, false>(Xm + size_t(job) * mat, D, dO, D, Y, D, 1.f, false, lds);
+    mm<CM, D, CM, false, false>(Y, D, s.cc(sP), CM, W, D, -1.f, Y, lds);
+    mm<D, D, CM, true, false>(Xm + size_t(job) * mat, D, dO, D, Y, D, 1.f, nullptr, lds);
   }
 }
 
 // Per chunk, given its start state S (Sst) and the adjoint G reaching its end
 // (Rin): dq, dk, dv (added to what the softmax branches wrote), da, db.
 template <typename Tin, typename Tg, int D>
-__global__ void __launch_bounds__(kNT)
+__global__ void __launch_bounds__(kNT, 2)
 gdn_bwd_mat_grad(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float* slots, size_t slot_floats,
                  const float* Sst, const float* Rin, float* dq, float* dk, float* dv, float* da, float* db) {
   __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];
   __shared__ ChunkVec v;
-  const Slot<D> s{slots + size_t(blockIdx.x) * slot_floats};
+  float* const slot = slots + size_t(blockIdx.x) * slot_floats;
   const long long jobs = (long long)p.B * p.H * p.n_chunks;
   const size_t mat = size_t(D) * D;
   const size_t HD = size_t(p.H) * D;
@@ -393,6 +541,9 @@ gdn_bwd_mat_grad(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float*
     const int n = int(p.L - t0 < C ? p.L - t0 : C);
     const size_t tok0 = (size_t(b) * p.L + t0) * HD + size_t(h) * D;
     const size_t g0 = (size_t(b) * p.L + t0) * p.H + h;
+    float* sb = slot;   // opaque inside the loop (see gdn_bwd_mat_prep)
+    asm volatile("" : "+s"(sb));
+    const Slot<D> s{sb};
     chunk_forward<Tin, Tg, D>(p, C, d_mix, mix_w[3 * h + 2], c, b, h, s, v, lds);
     const float* S = Sst + size_t(job) * mat;
     const float* G = Rin + size_t(job) * mat;
@@ -401,81 +552,152 @@ gdn_bwd_mat_grad(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float*
     float *X1 = s.cd(sX1), *X2 = s.cd(sX2), *X3 = s.cd(sX3), *BV = s.cd(sBV);
     float *GK = s.cc(sGK), *Tm = s.cc(sT), *P = s.cc(sP), *dP = s.cc(sDP), *dPG = s.cc(sDPG);
     float *E1 = s.cc(sE1), *E2 = s.cc(sE2);
+    // scatter-add of a [CM][D] array into a gradient (rows t < n), optionally
+    // through the L2 normalisation's Jacobian (x^ the normalised rows, r the
+    // inverse norms, pr[t] = x^_t . dx^_t)
+    auto add_rows = [&](float* grad, const float* X, const float* Xh, const float* pr, const float* rn, bool norm) {
+      ew<CM * D / 4, 2>(
+          [&](int e) {
+            const int t = (4 * e) / D, j = (4 * e) % D;
+            F4x3 x;
+            x.a = f4(X)[e];
+            x.b = Xh ? f4(Xh)[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+            x.c = t < n ? f4(grad)[(tok0 + size_t(t) * HD + j) / 4] : make_float4(0.f, 0.f, 0.f, 0.f);
+            return x;
+          },
+          [&](int e, const F4x3& x) {
+            const int t = (4 * e) / D, j = (4 * e) % D;
+            if (t >= n) return;
+            const float4 d = norm ? rn[t] * (x.a - pr[t] * x.b) : (rn ? rn[t] * x.a : x.a);
+            f4(grad)[(tok0 + size_t(t) * HD + j) / 4] = x.c + d;
+          });
+    };
 
     // U = U' - W S^T;  De K G^T;  t_i = U_i . (De K G^T)_i
-    for (int e = threadIdx.x; e < CM * D; e += kNT) U[e] = Up[e];
-    mm<CM, D, D, false, true>(U, D, W, D, S, D, -1.f, true, lds);
-    mm<CM, D, D, false, true>(DKG, D, DK, D, G, D, 1.f, false, lds);
+    mm<CM, D, D, false, true>(U, D, W, D, S, D, -1.f, Up, lds);
+    mm<CM, D, D, false, true>(DKG, D, DK, D, G, D, 1.f, nullptr, lds);
     rowdot<D>(v.v0, U, DKG);   // t_i
     // dU = P^T dO + De K G^T
-    for (int e = threadIdx.x; e < CM * D; e += kNT) dU[e] = DKG[e];
-    mm<CM, D, CM, true, false>(dU, D, P, CM, dO, D, 1.f, true, lds);
+    mm<CM, D, CM, true, false>(dU, D, P, CM, dO, D, 1.f, DKG, lds);
     // dP = lower(dO U^T), dPG = dP . Gam
-    mm<CM, CM, D, false, true>(dP, CM, dO, D, U, D, 1.f, false, lds);
-    for (int e = threadIdx.x; e < CM * CM; e += kNT) {
-      const int i = e / CM, j = e % CM;
-      const float x = j <= i ? dP[e] : 0.f;
-      dP[e] = x;
-      dPG[e] = j <= i ? x * expf(v.g[i] - v.g[j]) : 0.f;
-    }
+    mm<CM, CM, D, false, true>(dP, CM, dO, D, U, D, 1.f, nullptr, lds);
+    ew<CM * CM / 4, 2>([&](int e) { return f4(dP)[e]; },
+                       [&](int e, float4 x) {
+                         const int i = (4 * e) / CM, j0 = (4 * e) % CM;
+                         float* xs = reinterpret_cast<float*>(&x);
+                         float4 y;
+                         float* ys = reinterpret_cast<float*>(&y);
+#pragma unroll
+                         for (int q = 0; q < 4; ++q) {
+                           const int j = j0 + q;
+                           xs[q] = j <= i ? xs[q] : 0.f;
+                           ys[q] = j <= i ? xs[q] * expf(v.g[i] - v.g[j]) : 0.f;
+                         }
+                         f4(dP)[e] = x;
+                         f4(dPG)[e] = y;
+                       });
     __syncthreads();
     // dq^ = diag(gamma) dO S + dPG K (the row dots q_i . (dO S)_i first)
-    mm<CM, D, D, false, false>(X1, D, dO, D, S, D, 1.f, false, lds);
+    mm<CM, D, D, false, false>(X1, D, dO, D, S, D, 1.f, nullptr, lds);
     rowdot<D>(v.v1, X1, Q);   // q_i . (dO S)_i
-    for (int e = threadIdx.x; e < CM * D; e += kNT) X1[e] *= v.gam[e / D];
+    ew<CM * D / 4, 2>([&](int e) { return f4(X1)[e]; },
+                      [&](int e, const float4& x) { f4(X1)[e] = v.gam[(4 * e) / D] * x; });
     __syncthreads();
-    mm<CM, D, CM, false, false>(X1, D, dPG, CM, K, D, 1.f, true, lds);
+    mm<CM, D, CM, false, false>(X1, D, dPG, CM, K, D, 1.f, X1, lds);
     // through the normalisation, into dq
     rowdot<D>(v.v2, X1, Q);   // q^ . dq^
-    for (int e = threadIdx.x; e < n * D; e += kNT) {
-      const int t = e / D, j = e % D;
-      const float x = p.l2norm ? (X1[e] - Q[e] * v.v2[t]) * v.rq[t] : X1[e];
-      dq[tok0 + size_t(t) * HD + j] += x;
-    }
+    add_rows(dq, X1, Q, v.v2, v.rq, p.l2norm != 0);
     __syncthreads();
     // dW = -dU S (X2), T^T dW (X3), dT = dW (diag(b gamma) K)^T (E1)
-    mm<CM, D, D, false, false>(X2, D, dU, D, S, D, -1.f, false, lds);
-    mm<CM, D, CM, true, false>(X3, D, Tm, CM, X2, D, 1.f, false, lds);
-    mm<CM, CM, D, false, true>(E1, CM, X2, D, BK, D, 1.f, false, lds);
+    mm<CM, D, D, false, false>(X2, D, dU, D, S, D, -1.f, nullptr, lds);
+    mm<CM, D, CM, true, false>(X3, D, Tm, CM, X2, D, 1.f, nullptr, lds);
+    mm<CM, CM, D, false, true>(E1, CM, X2, D, BK, D, 1.f, nullptr, lds);
     // T^T dU (X2), dT += dU (diag(b) V)^T
-    mm<CM, D, CM, true, false>(X2, D, Tm, CM, dU, D, 1.f, false, lds);
-    mm<CM, CM, D, false, true>(E1, CM, dU, D, BV, D, 1.f, true, lds);
+    mm<CM, D, CM, true, false>(X2, D, Tm, CM, dU, D, 1.f, nullptr, lds);
+    mm<CM, CM, D, false, true>(E1, CM, dU, D, BV, D, 1.f, E1, lds);
     // dv = diag(b) T^T dU; row dots for db
-    for (int e = threadIdx.x; e < n * D; e += kNT) {
-      const int t = e / D, j = e % D;
-      dv[tok0 + size_t(t) * HD + j] += v.b[t] * X2[e];
-    }
+    add_rows(dv, X2, nullptr, nullptr, v.b, false);
     rowdot<D>(v.v2, X2, V);   // (T^T dU)_i . v_i
     rowdot<D>(v.v3, X3, K);   // (T^T dW)_i . k_i
     // dA = strict_lower(-T^T dT T^T) (E1), via E2 = dT T^T
-    mm<CM, CM, CM, false, true>(E2, CM, E1, CM, Tm, CM, 1.f, false, lds);
-    mm<CM, CM, CM, true, false>(E1, CM, Tm, CM, E2, CM, -1.f, false, lds);
-    // E2 = dKK = dA . (b_i Gam_ij); E (into dP) = dA . A + dP . P; db part sum_j dA GK
-    for (int e = threadIdx.x; e < CM * CM; e += kNT) {
-      const int i = e / CM, j = e % CM;
-      const float dA = j < i ? E1[e] : 0.f;
-      E1[e] = dA * GK[e];   // dA . (Gam . KK), row sums feed db
-      E2[e] = j < i ? dA * v.b[i] * expf(v.g[i] - v.g[j]) : 0.f;
-      dP[e] = dA * v.b[i] * GK[e] + dP[e] * P[e];
-    }
+    mm<CM, CM, CM, false, true>(E2, CM, E1, CM, Tm, CM, 1.f, nullptr, lds);
+    mm<CM, CM, CM, true, false>(E1, CM, Tm, CM, E2, CM, -1.f, nullptr, lds);
+    // E2 = dKK = dA . (b_i Gam_ij); E (into dP) = dA . A + dP . P; E1 = dA . GK (row sums feed db)
+    ew<CM * CM / 4, 2>(
+        [&](int e) {
+          F4x4 x;
+          x.a = f4(E1)[e];
+          x.b = f4(GK)[e];
+          x.c = f4(dP)[e];
+          x.d = f4(P)[e];
+          return x;
+        },
+        [&](int e, F4x4 x) {
+          const int i = (4 * e) / CM, j0 = (4 * e) % CM;
+          float *e1 = reinterpret_cast<float*>(&x.a), *gk = reinterpret_cast<float*>(&x.b);
+          float *dp = reinterpret_cast<float*>(&x.c), *pp = reinterpret_cast<float*>(&x.d);
+          float4 y;
+          float* e2 = reinterpret_cast<float*>(&y);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int j = j0 + q;
+            const float dA = j < i ? e1[q] : 0.f;
+            e2[q] = j < i ? dA * v.b[i] * expf(v.g[i] - v.g[j]) : 0.f;
+            dp[q] = dA * v.b[i] * gk[q] + dp[q] * pp[q];
+            e1[q] = dA * gk[q];
+          }
+          f4(E1)[e] = x.a;
+          f4(E2)[e] = y;
+          f4(dP)[e] = x.c;
+        });
     __syncthreads();
-    // gates: row and column sums of E, the db row sums of dA . GK
-    if (wave == 0) {
-      float rs = 0.f, cs = 0.f, gs = 0.f;
-      for (int j = 0; j < CM; ++j) {
-        rs += dP[lane * CM + j];
-        cs += dP[j * CM + lane];
-        gs += E1[lane * CM + j];
+    // gates: row sums minus column sums of E (in dP), row sums of dA . GK (in E1)
+    {
+      constexpr int LPR = CM / 4, RPP = kNT / LPR, PASSES = CM / RPP;   // 16 lanes per row, 4 passes
+      const int c4 = threadIdx.x % LPR, r0 = threadIdx.x / LPR;
+      float4 xe[PASSES], xg[PASSES];
+#pragma unroll
+      for (int q = 0; q < PASSES; ++q) {
+        xe[q] = f4(dP)[(r0 + q * RPP) * LPR + c4];
+        xg[q] = f4(E1)[(r0 + q * RPP) * LPR + c4];
       }
-      v.v4[lane] = rs - cs;
-      // db (before the gates' own terms overwrite the scratch)
-      const float dbt = v.gam[lane] * v.v3[lane] + v.v2[lane] + gs;
-      if (lane < n) db[g0 + size_t(lane) * p.H] = dbt;
+      float4 col = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int q = 0; q < PASSES; ++q) {
+        float rs = xe[q].x + xe[q].y + xe[q].z + xe[q].w;
+        float gs = xg[q].x + xg[q].y + xg[q].z + xg[q].w;
+#pragma unroll
+        for (int off = 1; off < LPR; off <<= 1) {
+          rs += __shfl_xor(rs, off);
+          gs += __shfl_xor(gs, off);
+        }
+        if (c4 == 0) {
+          v.v4[r0 + q * RPP] = rs;
+          v.gs[r0 + q * RPP] = gs;
+        }
+        col = col + xe[q];
+      }
+      // column partials: the lanes of a wave with the same c4 hold the same columns
+#pragma unroll
+      for (int off = LPR; off < 64; off <<= 1) {
+        col.x += __shfl_xor(col.x, off);
+        col.y += __shfl_xor(col.y, off);
+        col.z += __shfl_xor(col.z, off);
+        col.w += __shfl_xor(col.w, off);
+      }
+      if (lane < LPR) f4(v.cpart[wave])[c4] = col;
     }
     // <G, S>
     {
       float x = 0.f;
-      for (size_t e = threadIdx.x; e < mat; e += kNT) x += G[e] * S[e];
+      ew<D * D / 4, 8>(
+          [&](int e) {
+            F4x2 y;
+            y.a = f4(G)[e];
+            y.b = f4(S)[e];
+            return y;
+          },
+          [&](int, const F4x2& y) { x += dot4(y.a, y.b); });
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
       if (lane == 0) v.red[wave] = x;
@@ -483,12 +705,18 @@ gdn_bwd_mat_grad(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float*
     __syncthreads();
     if (wave == 0) {
       const int i = lane;
+      float cs = 0.f;
+#pragma unroll
+      for (int w = 0; w < kNT / 64; ++w) cs += v.cpart[w][i];
+      const float dbt = v.gam[i] * v.v3[i] + v.v2[i] + v.gs[i];
+      if (i < n) db[g0 + size_t(i) * p.H] = dbt;
       float tsum = v.v0[i];
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) tsum += __shfl_xor(tsum, off);
       float GS = 0.f;
+#pragma unroll
       for (int w = 0; w < kNT / 64; ++w) GS += v.red[w];
-      float dg = v.v4[i] + v.b[i] * v.gam[i] * v.v3[i] + v.gam[i] * v.v1[i] - v.v0[i];
+      float dg = v.v4[i] - cs + v.b[i] * v.gam[i] * v.v3[i] + v.gam[i] * v.v1[i] - v.v0[i];
       if (i == CM - 1) dg += v.gC * GS + tsum;
       // d(log a_t) = sum_{i >= t} dg_i
 #pragma unroll
@@ -499,21 +727,24 @@ gdn_bwd_mat_grad(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float*
       if (i < n) da[g0 + size_t(i) * p.H] = v.a[i] > 0.f ? dg / v.a[i] : 0.f;
     }
     // dk^ = De U G + diag(b gamma) T^T dW + dPG^T Q + dKK K + dKK^T K
-    mm<CM, D, D, false, false>(X1, D, U, D, G, D, 1.f, false, lds);
-    for (int e = threadIdx.x; e < CM * D; e += kNT) {
-      const int t = e / D;
-      X1[e] = v.De[t] * X1[e] + v.b[t] * v.gam[t] * X3[e];
-    }
+    mm<CM, D, D, false, false>(X1, D, U, D, G, D, 1.f, nullptr, lds);
+    ew<CM * D / 4, 2>(
+        [&](int e) {
+          F4x2 y;
+          y.a = f4(X1)[e];
+          y.b = f4(X3)[e];
+          return y;
+        },
+        [&](int e, const F4x2& y) {
+          const int t = (4 * e) / D;
+          f4(X1)[e] = v.De[t] * y.a + (v.b[t] * v.gam[t]) * y.b;
+        });
     __syncthreads();
-    mm<CM, D, CM, true, false>(X1, D, dPG, CM, Q, D, 1.f, true, lds);
-    mm<CM, D, CM, false, false>(X1, D, E2, CM, K, D, 1.f, true, lds);
-    mm<CM, D, CM, true, false>(X1, D, E2, CM, K, D, 1.f, true, lds);
+    mm<CM, D, CM, true, false>(X1, D, dPG, CM, Q, D, 1.f, X1, lds);
+    mm<CM, D, CM, false, false>(X1, D, E2, CM, K, D, 1.f, X1, lds);
+    mm<CM, D, CM, true, false>(X1, D, E2, CM, K, D, 1.f, X1, lds);
     rowdot<D>(v.v2, X1, K);   // k^ . dk^
-    for (int e = threadIdx.x; e < n * D; e += kNT) {
-      const int t = e / D, j = e % D;
-      const float x = p.l2norm ? (X1[e] - K[e] * v.v2[t]) * v.rk[t] : X1[e];
-      dk[tok0 + size_t(t) * HD + j] += x;
-    }
+    add_rows(dk, X1, K, v.v2, v.rk, p.l2norm != 0);
     __syncthreads();
   }
 }
