@@ -12,9 +12,10 @@
 //  * gated delta rule (Kairos related-work page, row A; long-context page,
 //    section 06): per chunk of C tokens, in parallel, the chunk's affine map
 //    S_end = S_start A_c + U_c and its own adjoint from zero X_c (matrix form,
-//    gdn_bwd_mat.hip); then two short chains over chunks here give every
-//    chunk's start state and the adjoint reaching its end; then, per chunk in
-//    parallel again, the token gradients in matrix form (gdn_bwd_mat.hip).
+//    gdn_bwd_mat.hip); then two short chains over chunks give every chunk's
+//    start state and the adjoint reaching its end; then, per chunk in
+//    parallel again, the token gradients in matrix form (all in
+//    gdn_bwd_mat.hip).
 //    The chunk products there run on bf16 MFMA with each fp32 operand split
 //    into a bf16 head and a bf16 remainder (three products), which keeps
 //    them close to fp32 accuracy;
@@ -290,100 +291,6 @@ attn_bwd_dkdv(AttnParams p, const Tg* d_mix, const float* mix_w, const float* ls
 // gated delta rule
 // ---------------------------------------------------------------------------
 
-// The two chains over chunks, rows of the state split over workgroups (rows
-// evolve independently: row i of S A + U only needs row i of S and U):
-//   dir 0: S_start(0) = S0, S_start(c+1) = S_start(c) A_c + U_c
-//   dir 1: R(N-1) = 0,      R(c-1) = R(c) A_c^T + X_c, dS0 = R(-1)
-// R(c) is the adjoint reaching the end of chunk c from later tokens. The
-// matrix (A_c, or A_c^T as the prep stored it) is staged in LDS rows padded
-// to keep 16-byte alignment; a thread owns one row of the group and CPT
-// consecutive columns, read as float4s, and the row itself is read four
-// values at a time. The next step's matrix and U/X rows are loaded into
-// registers while the current step computes (the chain is latency-bound: one
-// dependent 16 x d by d x d product per chunk). grid (B*H, D/16, 2).
-constexpr int kChainRows = 16;
-typedef float v4f __attribute__((ext_vector_type(4)));
-template <int D>
-__global__ void __launch_bounds__(kThreads)
-gdn_bwd_chain(int n_chunks, const float* S0, const float* Am, const float* AmT, const float* Um, const float* Xm,
-              float* Sst, float* Rin, float* dS0) {
-  constexpr int DP = D + 4;                        // padded row (floats), keeps float4 alignment
-  __shared__ __attribute__((aligned(16))) float As[D * DP];
-  __shared__ __attribute__((aligned(16))) float rows[kChainRows][D];
-  constexpr int CPT = D * kChainRows / kThreads;   // columns per thread: 8 (d = 128), 4 (64), 2 (32)
-  constexpr int PER = D * D / 4 / kThreads;        // float4 of the matrix per thread per step
-  const int bh = blockIdx.x, r0 = blockIdx.y * kChainRows, dir = blockIdx.z;
-  const int r = threadIdx.x / (D / CPT), j0 = (threadIdx.x % (D / CPT)) * CPT;
-  const size_t mat = size_t(D) * D;
-  const size_t base = size_t(bh) * n_chunks * mat;
-  const float* Mm = dir == 0 ? Am : AmT;
-  const float* Bm = dir == 0 ? Um : Xm;
-#pragma unroll
-  for (int jj = 0; jj < CPT; ++jj)
-    rows[r][j0 + jj] = (dir == 0 && S0) ? S0[size_t(bh) * mat + size_t(r0 + r) * D + j0 + jj] : 0.f;
-  v4f na[PER];
-  float nb[CPT];
-  auto fetch = [&](int c) __attribute__((always_inline)) {
-    const v4f* A4 = reinterpret_cast<const v4f*>(Mm + base + size_t(c) * mat);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) na[i] = A4[threadIdx.x + i * kThreads];
-    const float* add = Bm + base + size_t(c) * mat + size_t(r0 + r) * D + j0;
-#pragma unroll
-    for (int jj = 0; jj < CPT; ++jj) nb[jj] = add[jj];
-  };
-  fetch(dir == 0 ? 0 : n_chunks - 1);
-  for (int step = 0; step < n_chunks; ++step) {
-    const int c = dir == 0 ? step : n_chunks - 1 - step;
-    __syncthreads();   // the previous step no longer reads As or rows
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = (threadIdx.x + i * kThreads) * 4;
-      *reinterpret_cast<v4f*>(&As[(e / D) * DP + e % D]) = na[i];
-    }
-    float out[CPT];
-#pragma unroll
-    for (int jj = 0; jj < CPT; ++jj) out[jj] = nb[jj];
-    // unconditional (the last step re-reads its own chunk) so the prefetch buffer stays in registers
-    fetch(dir == 0 ? (c + 1 < n_chunks ? c + 1 : c) : (c > 0 ? c - 1 : 0));
-    __syncthreads();
-    float* rec = (dir == 0 ? Sst : Rin) + base + size_t(c) * mat + size_t(r0 + r) * D + j0;
-#pragma unroll
-    for (int jj = 0; jj < CPT; ++jj) rec[jj] = rows[r][j0 + jj];
-    // out += x * (row k of the matrix), CPT consecutive columns from j0
-    auto axpy = [&](float x, int k) __attribute__((always_inline)) {
-      const float* arow = &As[k * DP + j0];
-      if constexpr (CPT >= 4) {
-#pragma unroll
-        for (int j4 = 0; j4 < CPT; j4 += 4) {
-          const v4f a4 = *reinterpret_cast<const v4f*>(arow + j4);
-          out[j4] += x * a4.x;
-          out[j4 + 1] += x * a4.y;
-          out[j4 + 2] += x * a4.z;
-          out[j4 + 3] += x * a4.w;
-        }
-      } else {
-#pragma unroll
-        for (int jj = 0; jj < CPT; ++jj) out[jj] += x * arow[jj];
-      }
-    };
-#pragma unroll 4
-    for (int k4 = 0; k4 < D; k4 += 4) {
-      const v4f x = *reinterpret_cast<const v4f*>(&rows[r][k4]);
-      axpy(x.x, k4);
-      axpy(x.y, k4 + 1);
-      axpy(x.z, k4 + 2);
-      axpy(x.w, k4 + 3);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int jj = 0; jj < CPT; ++jj) rows[r][j0 + jj] = out[jj];
-  }
-  if (dir == 1 && dS0) {
-#pragma unroll
-    for (int jj = 0; jj < CPT; ++jj) dS0[size_t(bh) * mat + size_t(r0 + r) * D + j0 + jj] = rows[r][j0 + jj];
-  }
-}
-
 // dw[h, i] = <d_mix, o_i> in two deterministic stages: per-head partial sums
 // over grid.y slices (grid (H, slices)), then their sum in a fixed order.
 template <typename Tg, typename Tout>
@@ -440,14 +347,11 @@ hipError_t launch_bwd_t(const BwdArgs& x, hipStream_t st) {
     hipLaunchKernelGGL((attn_bwd_dkdv<Tin, Tg, D>), grid, dim3(kThreads), 0, st, p, g, x.mix_w, x.lse2, x.dsum,
                        x.dk, x.dv, x.scale);
   }
-  const unsigned heads = unsigned(x.gdn.B * x.gdn.H);
   const int in_dt = std::is_same<Tin, bf16>::value ? HLTA_BF16 : HLTA_F32;
   const int out_dt = std::is_same<Tg, bf16>::value ? HLTA_BF16 : HLTA_F32;
   hipError_t e = launch_gdn_bwd_mat(x, D, in_dt, out_dt, 0, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gdn_bwd_chain<D>), dim3(heads, D / kChainRows, 2), dim3(kThreads), 0, st, x.gdn.n_chunks,
-                     x.gdn.S0, x.Am, x.AmT, x.Um, x.Xm, x.Sst, x.Rin, x.dS0);
-  e = hipGetLastError();
+  e = launch_gdn_bwd_mat(x, D, in_dt, out_dt, 2, st);
   if (e != hipSuccess) return e;
   return launch_gdn_bwd_mat(x, D, in_dt, out_dt, 1, st);
 }

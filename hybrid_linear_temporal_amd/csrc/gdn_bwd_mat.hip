@@ -749,6 +749,164 @@ gdn_bwd_mat_grad(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float*
   }
 }
 
+// The two chains over chunks: S(c+1) = S(c) M_c + N_c forward from S(0) = S0
+// (the start states, into Sst) and R(c-1) = R(c) M_c^T + X_c backward from
+// R(n-1) = 0 (the adjoints reaching each chunk's end, into Rin; dS0 = R(-1)).
+// A workgroup carries RW rows of the state through all chunks of one head and
+// direction (grid (B*H, D/RW, 2)); each step is one RW x D by D x D product on
+// split-bf16 MFMA, computed transposed, out^T = M^T S^T: the state stays in
+// registers in the MFMA accumulator layout (lane = state row, values = 16
+// state columns per 32 x 32 tile), which is also the B-operand layout of the
+// next step once the reduction index is permuted the same way in both
+// operands: B value i of lane l in k-step (tm, h) is column
+// 32 tm + 16 h + 8 (i / 4) + 4 (l / 32) + i % 4, and the A operand reads those
+// rows of M (k-major in LDS, two transposing reads of four rows each). Each
+// step hands its tiles to the other waves through LDS (one 16-byte chunk per
+// lane and half-tile) and loads the next step's matrix and addend rows into
+// registers while it multiplies.
+template <int D>
+__global__ void __launch_bounds__(kNT)
+gdn_bwd_chain_mfma(int n_chunks, const float* S0, const float* Am, const float* AmT, const float* Um,
+                   const float* Xm, float* Sst, float* Rin, float* dS0) {
+  constexpr int RW = D < 64 ? D : 64;                  // state rows per workgroup
+  constexpr int TMO = D / 32, TN = RW / 32;            // output tiles: state columns x state rows
+  constexpr int NTILE = TMO * TN, TPW = (NTILE + 3) / 4;
+  constexpr int PM = D * D / 4 / kNT;                  // float4 of the matrix per thread per step
+  static_assert(PM * kNT * 4 == D * D, "the matrix splits evenly over the threads");
+  __shared__ __attribute__((aligned(16))) bf16 Mhi[D * D], Mlo[D * D];
+  __shared__ __attribute__((aligned(16))) bf16x8_t Xhi[NTILE * 2 * 64], Xlo[NTILE * 2 * 64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
+  const int bh = blockIdx.x, r0 = blockIdx.y * RW, dir = blockIdx.z;
+  const size_t mat = size_t(D) * D;
+  const size_t base = size_t(bh) * n_chunks * mat;
+  const float* Mm = dir == 0 ? Am : AmT;
+  const float* Nm = dir == 0 ? Um : Xm;
+  float* rec = dir == 0 ? Sst : Rin;
+  // this lane's place in tile u: state row r0 + 32 tn + l32, columns 32 tm + 8 j + 4 hl .. + 3
+  auto tile_of = [&](int u, int& tm, int& tn) {
+    const int t = wave + 4 * u;
+    tm = t / TN;
+    tn = t % TN;
+    return t < NTILE;
+  };
+  auto off4 = [&](int tm, int tn, int j) { return size_t(r0 + 32 * tn + l32) * D + 32 * tm + 8 * j + 4 * hl; };
+  f32x16_t acc[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    int tm, tn;
+    const bool own = tile_of(u, tm, tn);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (own && dir == 0 && S0) x = f4(S0 + size_t(bh) * mat)[off4(tm, tn, j) / 4];
+      acc[u][4 * j] = x.x;
+      acc[u][4 * j + 1] = x.y;
+      acc[u][4 * j + 2] = x.z;
+      acc[u][4 * j + 3] = x.w;
+    }
+  }
+  float4 nm[PM];          // the next step's matrix
+  float4 nn[TPW][4];      // the next step's addend rows
+  auto fetch = [&](int c) __attribute__((always_inline)) {
+    const float4* M4 = f4(Mm + base + size_t(c) * mat);
+#pragma unroll
+    for (int i = 0; i < PM; ++i) nm[i] = M4[tid + i * kNT];
+    const float* N = Nm + base + size_t(c) * mat;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      int tm, tn;
+      const bool own = tile_of(u, tm, tn);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) nn[u][j] = own ? f4(N)[off4(tm, tn, j) / 4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  fetch(dir == 0 ? 0 : n_chunks - 1);
+  for (int step = 0; step < n_chunks; ++step) {
+    const int c = dir == 0 ? step : n_chunks - 1 - step;
+    __syncthreads();   // the previous step's operand reads are done
+    // record the state entering this step; hand it to the other waves as split operands
+    float* rc = rec + base + size_t(c) * mat;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      int tm, tn;
+      if (!tile_of(u, tm, tn)) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        f4(rc)[off4(tm, tn, j) / 4] = make_float4(acc[u][4 * j], acc[u][4 * j + 1], acc[u][4 * j + 2], acc[u][4 * j + 3]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bf16x8_t xh, xl;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float x = acc[u][8 * h + i];
+          xh[i] = static_cast<bf16>(x);
+          xl[i] = static_cast<bf16>(x - static_cast<float>(xh[i]));
+        }
+        Xhi[((tm * TN + tn) * 2 + h) * 64 + lane] = xh;
+        Xlo[((tm * TN + tn) * 2 + h) * 64 + lane] = xl;
+      }
+    }
+    // this step's matrix, split, k-major (row k of M holds its D columns)
+#pragma unroll
+    for (int i = 0; i < PM; ++i) {
+      const int e = tid + i * kNT;
+      const int o = kmaj_off<D>(e / (D / 4), 4 * (e % (D / 4)));
+      split_store4(Mhi + o, Mlo + o, nm[i]);
+    }
+    float4 add[TPW][4];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) add[u][j] = nn[u][j];
+    __syncthreads();
+    // the next step's operands, in flight during the products (the last step re-reads its own)
+    fetch(dir == 0 ? (c + 1 < n_chunks ? c + 1 : c) : (c > 0 ? c - 1 : 0));
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      int tm, tn;
+      if (!tile_of(u, tm, tn)) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[u][4 * j] = add[u][j].x;
+        acc[u][4 * j + 1] = add[u][j].y;
+        acc[u][4 * j + 2] = add[u][j].z;
+        acc[u][4 * j + 3] = add[u][j].w;
+      }
+      // out^T tile (rows: state columns 32 tm .., columns: state rows 32 tn ..)
+      const int j16 = lane & 15, e = j16 >> 2, q = j16 & 3;
+      const int col = 32 * tm + 16 * ((lane >> 4) & 1) + 4 * q;
+#pragma unroll
+      for (int km = 0; km < TMO; ++km)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int kb = 32 * km + 16 * h + 4 * hl + e;
+          const bf16x4_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(Mhi + kmaj_off<D>(kb, col)));
+          const bf16x4_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(Mhi + kmaj_off<D>(kb + 8, col)));
+          const bf16x4_t b0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(Mlo + kmaj_off<D>(kb, col)));
+          const bf16x4_t b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(Mlo + kmaj_off<D>(kb + 8, col)));
+          const bf16x8_t ah = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+          const bf16x8_t al = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+          const bf16x8_t bh = Xhi[((km * TN + tn) * 2 + h) * 64 + lane];
+          const bf16x8_t bl = Xlo[((km * TN + tn) * 2 + h) * 64 + lane];
+          acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc[u], 0, 0, 0);
+          acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[u], 0, 0, 0);
+          acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[u], 0, 0, 0);
+        }
+    }
+  }
+  if (dir == 1 && dS0) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      int tm, tn;
+      if (!tile_of(u, tm, tn)) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        f4(dS0 + size_t(bh) * mat)[off4(tm, tn, j) / 4] =
+            make_float4(acc[u][4 * j], acc[u][4 * j + 1], acc[u][4 * j + 2], acc[u][4 * j + 3]);
+    }
+  }
+}
+
 template <typename Tin, typename Tg, int D>
 hipError_t launch_t(const BwdArgs& x, int phase, hipStream_t st) {
   const Tg* g = static_cast<const Tg*>(x.d_mix);
@@ -756,6 +914,9 @@ hipError_t launch_t(const BwdArgs& x, int phase, hipStream_t st) {
   if (phase == 0)
     hipLaunchKernelGGL((gdn_bwd_mat_prep<Tin, Tg, D>), grid, dim3(kNT), 0, st, x.gdn, x.C, g, x.mix_w, x.slots,
                        x.slot_floats, x.Am, x.AmT, x.Um, x.Xm);
+  else if (phase == 2)
+    hipLaunchKernelGGL((gdn_bwd_chain_mfma<D>), dim3(unsigned(x.gdn.B * x.gdn.H), unsigned(D / (D < 64 ? D : 64)), 2),
+                       dim3(kNT), 0, st, x.gdn.n_chunks, x.gdn.S0, x.Am, x.AmT, x.Um, x.Xm, x.Sst, x.Rin, x.dS0);
   else
     hipLaunchKernelGGL((gdn_bwd_mat_grad<Tin, Tg, D>), grid, dim3(kNT), 0, st, x.gdn, x.C, g, x.mix_w, x.slots,
                        x.slot_floats, x.Sst, x.Rin, x.dq, x.dk, x.dv, x.da, x.db);

@@ -108,7 +108,8 @@ struct BwdArgs {
 };
 
 // The gated delta rule's backward in matrix form (per chunk): phase 0 the
-// chunk maps Am, AmT, Um, Xm; phase 1 (after the chains) the token gradients.
+// chunk maps Am, AmT, Um, Xm; phase 2 the two chains over chunks (Sst, Rin,
+// dS0); phase 1 (after the chains) the token gradients.
 hipError_t launch_gdn_bwd_mat(const BwdArgs& x, int d, int in_dt, int out_dt, int phase, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& x, int d, int in_dt, int out_dt, hipStream_t st);
 
