@@ -30,7 +30,7 @@
 // through the L2 normalisation: dx = (dx^ - x^ (x^ . dx^)) / n(x).
 //
 // Two kernels replace a token-by-token walk: gdn_bwd_mat_prep (per chunk: M,
-// M^T, N, X for the chains over chunks) and gdn_bwd_mat_grad (per chunk, after
+// N, X for the chains over chunks) and gdn_bwd_mat_grad (per chunk, after
 // the chains: the token gradients). Each is a persistent grid, one workgroup
 // per scratch slot of the workspace; the chunk's matrices live in that slot
 // (global memory, resident in the caches) and every product goes through LDS
@@ -485,11 +485,11 @@ __device__ void chunk_forward(const GdnParams& p, int C, const Tg* d_mix, float 
   gam_mask<false>(P, v);
 }
 
-// Per chunk: M (Am), M^T (AmT), N (Um) and the chunk's own adjoint X (Xm).
+// Per chunk: M (Am), N (Um) and the chunk's own adjoint X (Xm).
 template <typename Tin, typename Tg, int D>
 __global__ void __launch_bounds__(kNT, 2)
 gdn_bwd_mat_prep(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float* slots, size_t slot_floats,
-                 float* Am, float* AmT, float* Um, float* Xm) {
+                 float* Am, float* Um, float* Xm) {
   __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];   // product staging or the inverse
   __shared__ ChunkVec v;
   float* const slot = slots + size_t(blockIdx.x) * slot_floats;
@@ -505,14 +505,9 @@ gdn_bwd_mat_prep(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float*
     chunk_forward<Tin, Tg, D>(p, C, d_mix, mix_w[3 * h + 2], c, b, h, s, v, lds);
     float *W = s.cd(sW), *Up = s.cd(sUp), *DK = s.cd(sDK), *Q = s.cd(sQ), *dO = s.cd(sDO), *Y = s.cd(sX1);
     float* am = Am + size_t(job) * mat;
-    float* amt = AmT + size_t(job) * mat;
     mm<D, D, CM, true, false>(am, D, W, D, DK, D, -1.f, nullptr, lds);    // -W^T De K
-    mm<D, D, CM, true, false>(amt, D, DK, D, W, D, -1.f, nullptr, lds);   // -K^T De W
     mm<D, D, CM, true, false>(Um + size_t(job) * mat, D, Up, D, DK, D, 1.f, nullptr, lds);
-    for (int i = threadIdx.x; i < D; i += kNT) {
-      am[size_t(i) * D + i] += v.gC;
-      amt[size_t(i) * D + i] += v.gC;
-    }
+    for (int i = threadIdx.x; i < D; i += kNT) am[size_t(i) * D + i] += v.gC;
     // X = dO^T (diag(gamma) Q - P W): Y = diag(gamma) Q first, then Y -= P W
     ew<CM * D / 4, 2>([&](int e) { return f4(Q)[e]; },
                       [&](int e, const float4& x) { f4(Y)[e] = v.gam[(4 * e) / D] * x; });
@@ -751,7 +746,9 @@ gdn_bwd_mat_grad(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float*
 
 // The two chains over chunks: S(c+1) = S(c) M_c + N_c forward from S(0) = S0
 // (the start states, into Sst) and R(c-1) = R(c) M_c^T + X_c backward from
-// R(n-1) = 0 (the adjoints reaching each chunk's end, into Rin; dS0 = R(-1)).
+// R(n-1) = 0 (the adjoints reaching each chunk's end, into Rin; dS0 = R(-1)),
+// both from the one stored M_c: the forward chain stages it k-major and reads
+// it transposed, the backward one stages its rows as they are.
 // A workgroup carries RW rows of the state through all chunks of one head and
 // direction (grid (B*H, D/RW, 2)); each step is one RW x D by D x D product on
 // split-bf16 MFMA, computed transposed, out^T = M^T S^T: the state stays in
@@ -762,29 +759,35 @@ gdn_bwd_mat_grad(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float*
 // 32 tm + 16 h + 8 (i / 4) + 4 (l / 32) + i % 4, and the A operand reads those
 // rows of M (k-major in LDS, two transposing reads of four rows each). Each
 // step hands its tiles to the other waves through LDS (one 16-byte chunk per
-// lane and half-tile) and loads the next step's matrix and addend rows into
-// registers while it multiplies.
+// lane and half-tile); the matrices and addend rows are loaded into registers
+// two steps ahead of their use.
 template <int D>
-__global__ void __launch_bounds__(kNT)
-gdn_bwd_chain_mfma(int n_chunks, const float* S0, const float* Am, const float* AmT, const float* Um,
-                   const float* Xm, float* Sst, float* Rin, float* dS0) {
+constexpr int chain_threads() { return D == 128 ? 512 : 256; }   // two waves per SIMD at d = 128
+// bf16 row pitch of the row-major staging: D + 4 puts consecutive rows two of
+// the 64 four-byte banks apart, so the 32 rows of one 8-byte read are spread
+// over all banks
+template <int D>
+constexpr int chain_row() { return D + 4; }
+template <int D, int DIR>
+__device__ __forceinline__ void chain_body(int n_chunks, const float* S0, const float* Am, const float* Um,
+                                           const float* Xm, float* Sst, float* Rin, float* dS0, bf16* Mhi,
+                                           bf16* Mlo, bf16x8_t* Xhi, bf16x8_t* Xlo) {
+  constexpr int NTC = chain_threads<D>(), NW = NTC / 64;
   constexpr int RW = D < 64 ? D : 64;                  // state rows per workgroup
   constexpr int TMO = D / 32, TN = RW / 32;            // output tiles: state columns x state rows
-  constexpr int NTILE = TMO * TN, TPW = (NTILE + 3) / 4;
-  constexpr int PM = D * D / 4 / kNT;                  // float4 of the matrix per thread per step
-  static_assert(PM * kNT * 4 == D * D, "the matrix splits evenly over the threads");
-  __shared__ __attribute__((aligned(16))) bf16 Mhi[D * D], Mlo[D * D];
-  __shared__ __attribute__((aligned(16))) bf16x8_t Xhi[NTILE * 2 * 64], Xlo[NTILE * 2 * 64];
+  constexpr int NTILE = TMO * TN, TPW = (NTILE + NW - 1) / NW;
+  constexpr int PM = D * D / 4 / NTC;                  // float4 of the matrix per thread per step
+  static_assert(PM * NTC * 4 == D * D, "the matrix splits evenly over the threads");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
-  const int bh = blockIdx.x, r0 = blockIdx.y * RW, dir = blockIdx.z;
+  const int bh = blockIdx.x, r0 = blockIdx.y * RW, dir = DIR;
   const size_t mat = size_t(D) * D;
   const size_t base = size_t(bh) * n_chunks * mat;
-  const float* Mm = dir == 0 ? Am : AmT;
+  const float* Mm = Am;
   const float* Nm = dir == 0 ? Um : Xm;
   float* rec = dir == 0 ? Sst : Rin;
   // this lane's place in tile u: state row r0 + 32 tn + l32, columns 32 tm + 8 j + 4 hl .. + 3
   auto tile_of = [&](int u, int& tm, int& tn) {
-    const int t = wave + 4 * u;
+    const int t = wave + NW * u;
     tm = t / TN;
     tn = t % TN;
     return t < NTILE;
@@ -805,12 +808,15 @@ gdn_bwd_chain_mfma(int n_chunks, const float* S0, const float* Am, const float* 
       acc[u][4 * j + 3] = x.w;
     }
   }
-  float4 nm[PM];          // the next step's matrix
-  float4 nn[TPW][4];      // the next step's addend rows
-  auto fetch = [&](int c) __attribute__((always_inline)) {
+  // two register sets of a step's matrix and addend rows, each refilled two
+  // steps ahead, so a load has two steps' products to arrive
+  float4 nm0[PM], nm1[PM];
+  float4 nn0[TPW][4], nn1[TPW][4];
+  auto chunk_of = [&](int step) { return dir == 0 ? step : n_chunks - 1 - step; };
+  auto fetch = [&](float4 (&nm)[PM], float4 (&nn)[TPW][4], int c) __attribute__((always_inline)) {
     const float4* M4 = f4(Mm + base + size_t(c) * mat);
 #pragma unroll
-    for (int i = 0; i < PM; ++i) nm[i] = M4[tid + i * kNT];
+    for (int i = 0; i < PM; ++i) nm[i] = M4[tid + i * NTC];
     const float* N = Nm + base + size_t(c) * mat;
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
@@ -820,9 +826,8 @@ gdn_bwd_chain_mfma(int n_chunks, const float* S0, const float* Am, const float* 
       for (int j = 0; j < 4; ++j) nn[u][j] = own ? f4(N)[off4(tm, tn, j) / 4] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
-  fetch(dir == 0 ? 0 : n_chunks - 1);
-  for (int step = 0; step < n_chunks; ++step) {
-    const int c = dir == 0 ? step : n_chunks - 1 - step;
+  auto body = [&](int step, float4 (&nm)[PM], float4 (&nn)[TPW][4]) __attribute__((always_inline)) {
+    const int c = chunk_of(step);
     __syncthreads();   // the previous step's operand reads are done
     // record the state entering this step; hand it to the other waves as split operands
     float* rc = rec + base + size_t(c) * mat;
@@ -846,32 +851,31 @@ gdn_bwd_chain_mfma(int n_chunks, const float* S0, const float* Am, const float* 
         Xlo[((tm * TN + tn) * 2 + h) * 64 + lane] = xl;
       }
     }
-    // this step's matrix, split, k-major (row k of M holds its D columns)
+    // this step's matrix M, split: k-major for the forward chain (A = M^T, row
+    // k of M holds its D columns), row-major rows of CRP for the backward one (A = M)
 #pragma unroll
     for (int i = 0; i < PM; ++i) {
-      const int e = tid + i * kNT;
-      const int o = kmaj_off<D>(e / (D / 4), 4 * (e % (D / 4)));
+      const int e = tid + i * NTC;
+      const int a = e / (D / 4), b4 = 4 * (e % (D / 4));
+      const int o = DIR == 0 ? kmaj_off<D>(a, b4) : a * chain_row<D>() + b4;
       split_store4(Mhi + o, Mlo + o, nm[i]);
     }
-    float4 add[TPW][4];
 #pragma unroll
     for (int u = 0; u < TPW; ++u)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) add[u][j] = nn[u][j];
+      for (int j = 0; j < 4; ++j) {
+        acc[u][4 * j] = nn[u][j].x;
+        acc[u][4 * j + 1] = nn[u][j].y;
+        acc[u][4 * j + 2] = nn[u][j].z;
+        acc[u][4 * j + 3] = nn[u][j].w;
+      }
     __syncthreads();
-    // the next step's operands, in flight during the products (the last step re-reads its own)
-    fetch(dir == 0 ? (c + 1 < n_chunks ? c + 1 : c) : (c > 0 ? c - 1 : 0));
+    // refill this set for two steps ahead (past the end it re-reads this step's chunk)
+    fetch(nm, nn, chunk_of(step + 2 < n_chunks ? step + 2 : step));
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       int tm, tn;
       if (!tile_of(u, tm, tn)) continue;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[u][4 * j] = add[u][j].x;
-        acc[u][4 * j + 1] = add[u][j].y;
-        acc[u][4 * j + 2] = add[u][j].z;
-        acc[u][4 * j + 3] = add[u][j].w;
-      }
       // out^T tile (rows: state columns 32 tm .., columns: state rows 32 tn ..)
       const int j16 = lane & 15, e = j16 >> 2, q = j16 & 3;
       const int col = 32 * tm + 16 * ((lane >> 4) & 1) + 4 * q;
@@ -879,11 +883,21 @@ gdn_bwd_chain_mfma(int n_chunks, const float* S0, const float* Am, const float* 
       for (int km = 0; km < TMO; ++km)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int kb = 32 * km + 16 * h + 4 * hl + e;
-          const bf16x4_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(Mhi + kmaj_off<D>(kb, col)));
-          const bf16x4_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(Mhi + kmaj_off<D>(kb + 8, col)));
-          const bf16x4_t b0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(Mlo + kmaj_off<D>(kb, col)));
-          const bf16x4_t b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(Mlo + kmaj_off<D>(kb + 8, col)));
+          bf16x4_t a0, a1, b0, b1;
+          if constexpr (DIR == 0) {
+            const int kb = 32 * km + 16 * h + 4 * hl + e;
+            a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(Mhi + kmaj_off<D>(kb, col)));
+            a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(Mhi + kmaj_off<D>(kb + 8, col)));
+            b0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(Mlo + kmaj_off<D>(kb, col)));
+            b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(Mlo + kmaj_off<D>(kb + 8, col)));
+          } else {
+            // row 32 tm + l32 of M, reduction columns kb .. kb+3 and kb+8 .. kb+11
+            const int o = (32 * tm + l32) * chain_row<D>() + 32 * km + 16 * h + 4 * hl;
+            a0 = *reinterpret_cast<const bf16x4_t*>(Mhi + o);
+            a1 = *reinterpret_cast<const bf16x4_t*>(Mhi + o + 8);
+            b0 = *reinterpret_cast<const bf16x4_t*>(Mlo + o);
+            b1 = *reinterpret_cast<const bf16x4_t*>(Mlo + o + 8);
+          }
           const bf16x8_t ah = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
           const bf16x8_t al = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
           const bf16x8_t bh = Xhi[((km * TN + tn) * 2 + h) * 64 + lane];
@@ -893,6 +907,12 @@ gdn_bwd_chain_mfma(int n_chunks, const float* S0, const float* Am, const float* 
           acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[u], 0, 0, 0);
         }
     }
+  };
+  fetch(nm0, nn0, chunk_of(0));
+  fetch(nm1, nn1, chunk_of(n_chunks > 1 ? 1 : 0));
+  for (int step = 0; step < n_chunks; step += 2) {
+    body(step, nm0, nn0);
+    if (step + 1 < n_chunks) body(step + 1, nm1, nn1);
   }
   if (dir == 1 && dS0) {
 #pragma unroll
@@ -907,16 +927,28 @@ gdn_bwd_chain_mfma(int n_chunks, const float* S0, const float* Am, const float* 
   }
 }
 
+template <int D>
+__global__ void __launch_bounds__(chain_threads<D>())
+gdn_bwd_chain_mfma(int n_chunks, const float* S0, const float* Am, const float* Um, const float* Xm, float* Sst,
+                   float* Rin, float* dS0) {
+  __shared__ __attribute__((aligned(16))) bf16 Mhi[D * chain_row<D>()], Mlo[D * chain_row<D>()];
+  constexpr int NT2 = (D / 32) * ((D < 64 ? D : 64) / 32) * 2 * 64;
+  __shared__ __attribute__((aligned(16))) bf16x8_t Xhi[NT2], Xlo[NT2];
+  if (blockIdx.z == 0) chain_body<D, 0>(n_chunks, S0, Am, Um, Xm, Sst, Rin, dS0, Mhi, Mlo, Xhi, Xlo);
+  else chain_body<D, 1>(n_chunks, S0, Am, Um, Xm, Sst, Rin, dS0, Mhi, Mlo, Xhi, Xlo);
+}
+
 template <typename Tin, typename Tg, int D>
 hipError_t launch_t(const BwdArgs& x, int phase, hipStream_t st) {
   const Tg* g = static_cast<const Tg*>(x.d_mix);
   const dim3 grid(unsigned(x.n_slots));
   if (phase == 0)
     hipLaunchKernelGGL((gdn_bwd_mat_prep<Tin, Tg, D>), grid, dim3(kNT), 0, st, x.gdn, x.C, g, x.mix_w, x.slots,
-                       x.slot_floats, x.Am, x.AmT, x.Um, x.Xm);
+                       x.slot_floats, x.Am, x.Um, x.Xm);
   else if (phase == 2)
     hipLaunchKernelGGL((gdn_bwd_chain_mfma<D>), dim3(unsigned(x.gdn.B * x.gdn.H), unsigned(D / (D < 64 ? D : 64)), 2),
-                       dim3(kNT), 0, st, x.gdn.n_chunks, x.gdn.S0, x.Am, x.AmT, x.Um, x.Xm, x.Sst, x.Rin, x.dS0);
+                       dim3(chain_threads<D>()), 0, st, x.gdn.n_chunks, x.gdn.S0, x.Am, x.Um, x.Xm, x.Sst, x.Rin,
+                       x.dS0);
   else
     hipLaunchKernelGGL((gdn_bwd_mat_grad<Tin, Tg, D>), grid, dim3(kNT), 0, st, x.gdn, x.C, g, x.mix_w, x.slots,
                        x.slot_floats, x.Sst, x.Rin, x.dq, x.dk, x.dv, x.da, x.db);

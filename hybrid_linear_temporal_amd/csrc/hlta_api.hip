@@ -415,8 +415,8 @@ hlta_status hlta_bwd(const hlta_config* cfg, const void* q, const void* k, const
   x.dS0 = dS0;
   x.lse2 = reinterpret_cast<float*>(ws);
   x.dsum = reinterpret_cast<float*>(ws + bp.stats_bytes);
-  float** mats[] = {&x.Am, &x.AmT, &x.Um, &x.Xm, &x.Sst, &x.Rin};
-  for (int i = 0; i < 6; ++i) *mats[i] = reinterpret_cast<float*>(ws + bp.mat_off + i * bp.mat_bytes);
+  float** mats[] = {&x.Am, &x.Um, &x.Xm, &x.Sst, &x.Rin};
+  for (int i = 0; i < 5; ++i) *mats[i] = reinterpret_cast<float*>(ws + bp.mat_off + i * bp.mat_bytes);
   x.slots = reinterpret_cast<float*>(ws + bp.slot_off);
   x.n_slots = bp.n_slots;
   x.slot_floats = bp.slot_floats;

@@ -191,17 +191,17 @@ hlta_status make_bwd_plan(const hlta_config* cfg, BwdPlan* plan) {
   const int64_t dd = int64_t(cfg->d) * cfg->d, bh = int64_t(cfg->B) * cfg->H;
   BwdPlan p;
   p.n_slots = int(std::min<int64_t>(std::max<int64_t>(bh * nch, 1), kBwdSlots));
-  int64_t stats = 0, mats = 0, mats6 = 0, slots = 0, part = 0, off = 0, total = 0;
+  int64_t stats = 0, mats = 0, mats5 = 0, slots = 0, part = 0, off = 0, total = 0;
   if (!prod_ok({bh, L, 2, 4}, &stats) || !align256_ok(stats, &stats) ||
-      !prod_ok({bh, nch, dd, 4}, &mats) || !align256_ok(mats, &mats) || !mul_ok(mats, 6, &mats6) ||
+      !prod_ok({bh, nch, dd, 4}, &mats) || !align256_ok(mats, &mats) || !mul_ok(mats, 5, &mats5) ||
       !prod_ok({p.n_slots, int64_t(bwd_slot_floats(cfg->d)), 4}, &slots) || !align256_ok(slots, &slots) ||
       !prod_ok({cfg->H, kDwSlices, 3, 4}, &part) || !align256_ok(part, &part) ||
-      !add_ok(stats, stats, &off) || !add_ok(off, mats6, &off) || !add_ok(off, slots, &total) || !add_ok(total, part, &total))
+      !add_ok(stats, stats, &off) || !add_ok(off, mats5, &off) || !add_ok(off, slots, &total) || !add_ok(total, part, &total))
     return fail(HLTA_E_SHAPE, "workspace size overflows int64");
   p.stats_bytes = size_t(stats);
   p.mat_off = 2 * p.stats_bytes;
   p.mat_bytes = size_t(mats);
-  p.slot_off = p.mat_off + 6 * p.mat_bytes;
+  p.slot_off = p.mat_off + 5 * p.mat_bytes;
   p.slot_floats = bwd_slot_floats(cfg->d);
   p.part_off = p.slot_off + size_t(slots);
   p.total = size_t(total);

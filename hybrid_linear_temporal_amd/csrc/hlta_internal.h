@@ -39,9 +39,9 @@ hlta_status check_config(const hlta_config* cfg);
 hlta_status make_plan(const hlta_config* cfg, int64_t L, Plan* plan);
 
 // Workspace of the backward over L tokens per row, all fp32, 256-byte
-// aligned: per-row softmax statistics of both branches (two arrays); six
-// d x d matrices per chunk of C = gdn_chunk tokens (transition and its
-// transpose, own state, own adjoint, start state, adjoint at the end); one
+// aligned: per-row softmax statistics of both branches (two arrays); five
+// d x d matrices per chunk of C = gdn_chunk tokens (transition, own state,
+// own adjoint, start state, adjoint at the end); one
 // scratch slot per workgroup of the memory's per-chunk kernels (the chunk's
 // 64-row matrices, bwd_slot_floats(d) floats); partial sums of the
 // mix-weight gradient.
@@ -51,7 +51,7 @@ constexpr size_t bwd_slot_floats(int d) { return 16 * size_t(64) * size_t(d) + 8
 constexpr int kDwSlices = 128;
 struct BwdPlan {
   size_t stats_bytes = 0;   // each of the two: [2, B*L*H]
-  size_t mat_off = 0, mat_bytes = 0;   // each of the six: [B*H*n_chunks, d, d]
+  size_t mat_off = 0, mat_bytes = 0;   // each of the five: [B*H*n_chunks, d, d]
   size_t slot_off = 0;
   int n_slots = 0;
   size_t slot_floats = 0;   // floats of one slot (scratch of one workgroup of the memory's backward)

@@ -92,7 +92,6 @@ struct BwdArgs {
   float* lse2;       // [2, B*L*H] workspace: softmax row statistics
   float* dsum;       // [2, B*L*H] workspace
   float* Am;         // [B*H, n_chunks, d, d] workspace: per-chunk transition of the memory
-  float* AmT;        //   ... its transpose
   float* Um;         //   ... the chunk's own state from zero
   float* Xm;         //   ... the chunk's own adjoint from zero
   float* Sst;        //   ... state at the chunk's start
@@ -108,7 +107,7 @@ struct BwdArgs {
 };
 
 // The gated delta rule's backward in matrix form (per chunk): phase 0 the
-// chunk maps Am, AmT, Um, Xm; phase 2 the two chains over chunks (Sst, Rin,
+// chunk maps Am, Um, Xm; phase 2 the two chains over chunks (Sst, Rin,
 // dS0); phase 1 (after the chains) the token gradients.
 hipError_t launch_gdn_bwd_mat(const BwdArgs& x, int d, int in_dt, int out_dt, int phase, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& x, int d, int in_dt, int out_dt, hipStream_t st);

@@ -125,7 +125,7 @@ static bool check_bwd_plan(const hlta_config& c, const BwdPlan& p) {
   CHECK(p.stats_bytes >= size_t(c.B) * c.H * size_t(L) * 8, "%s", cs.c_str());
   CHECK(p.mat_bytes >= size_t(c.B) * c.H * size_t(nch) * c.d * c.d * 4, "%s", cs.c_str());
   CHECK(p.mat_off == 2 * p.stats_bytes, "%s", cs.c_str());
-  CHECK(p.slot_off == p.mat_off + 6 * p.mat_bytes, "%s", cs.c_str());
+  CHECK(p.slot_off == p.mat_off + 5 * p.mat_bytes, "%s", cs.c_str());
   CHECK(p.slot_floats >= 16 * size_t(64) * c.d + 7 * size_t(64) * 64, "%s", cs.c_str());
   CHECK(p.part_off >= p.slot_off + size_t(p.n_slots) * p.slot_floats * 4, "%s", cs.c_str());
   CHECK(p.total >= p.part_off + size_t(c.H) * kDwSlices * 3 * 4 && p.total % 256 == 0, "%s", cs.c_str());
