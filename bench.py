@@ -338,11 +338,28 @@ def bwd_leg(H, wl, dev, out, S_out, steps, impl):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    # the same with the forward's softmax statistics handed over (hlta_attn_fwd_lse
+    # then hlta_bwd_lse, as a training step would call them)
+    lse = H.hlta_attn_fwd_lse(cfg, dev["q"], dev["k"], dev["v"], dev["w"], out["o_gdn"], out, stream=stream)
+    torch.cuda.synchronize()
+
+    def bwd_lse():
+        return H.hlta_bwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], out, d_mix, S0=S0,
+                          workspace=ws, stream=stream, lse=lse)
+    bwd_lse()
+    e0.record(stream)
+    for _ in range(steps):
+        bwd_lse()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_lse = e0.elapsed_time(e1) / steps
     attn_flops = 2.5 * work(wl)[0]
     return {"steps": steps, "ms_per_step": ms, "tokens_per_s": wl.B * wl.L / (ms * 1e-3),
+            "ms_per_step_lse_given": ms_lse, "tokens_per_s_lse_given": wl.B * wl.L / (ms_lse * 1e-3),
             "attn_bwd_flops": attn_flops, "workspace_bytes": ws.numel(), "grads_finite": finite,
-            "note": "softmax branches on bf16 MFMA (fp32 gradients), memory on split-bf16 MFMA (fp32 accumulation); per-kernel times in "
-                    "profiles/kernels_bwd_p480_T31_bf16.md"}
+            "note": "softmax branches on bf16 MFMA (fp32 gradients), memory on split-bf16 MFMA (fp32 "
+                    "accumulation); _lse_given: the forward's softmax statistics passed in (hlta_bwd_lse); "
+                    "per-kernel times in profiles/kernels_bwd_p480_T31_bf16.md"}
 
 
 def main():

@@ -454,15 +454,15 @@ attn_bwd_dkdv_mfma(AttnParams p, const bf16* g, const float* mix_w, const float*
 }  // namespace
 
 hipError_t launch_attn_bwd_mfma(const AttnParams& p, const void* d_mix, const void* o_swa, const void* o_dswa,
-                                const float* mix_w, float* lse, float* dsum, float* dq, float* dk, float* dv,
-                                float scale, hipStream_t st) {
+                                const float* mix_w, float* lse, bool lse_given, float* dsum, float* dq, float* dk,
+                                float* dv, float scale, hipStream_t st) {
   const unsigned grid = grid_of(p);
   if (grid == 0) return hipSuccess;
   const bf16* g = static_cast<const bf16*>(d_mix);
   const long long L = (long long)p.T * p.P;
   const long long rows = (long long)p.B * L * p.H;
   const unsigned dgrid = unsigned(rows / 16 + 1 < 65536 ? rows / 16 + 1 : 65536);
-  hipLaunchKernelGGL(attn_bwd_lse_mfma, dim3(grid), dim3(NT), 0, st, p, lse);
+  if (!lse_given) hipLaunchKernelGGL(attn_bwd_lse_mfma, dim3(grid), dim3(NT), 0, st, p, lse);
   hipLaunchKernelGGL(attn_bwd_dsum, dim3(dgrid), dim3(256), 0, st, g, static_cast<const bf16*>(o_swa),
                      static_cast<const bf16*>(o_dswa), mix_w, dsum, p.B, L, p.H);
   hipLaunchKernelGGL(attn_bwd_dq_mfma, dim3(grid), dim3(NT), 0, st, p, g, mix_w, lse, dsum, dq, scale);

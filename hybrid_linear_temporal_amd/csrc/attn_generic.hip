@@ -109,6 +109,9 @@ attn_generic_kernel(AttnParams p) {
 
     const float inv = l > 0.f ? 1.f / l : 0.f;
     Tout* out = static_cast<Tout*>(branch == 0 ? p.o_swa : p.o_dswa);
+    if (p.R == 0 && p.lse && row_ok && c == 0)
+      p.lse[((size_t(branch) * p.B + b) * p.H + h) * (size_t(p.T) * p.P) + size_t(fq) * p.P + prow] =
+          nk > 0 ? m + log2f(l) : 0.f;
     if (row_ok) {
 #pragma unroll
       for (int i = 0; i < DP; ++i) out[qoff + i] = from_f32<Tout>(acc[i] * inv);

@@ -43,7 +43,7 @@ constexpr int RB = 1;            // 32-row query blocks per wave
 constexpr int QT = 4 * 32 * RB;  // query rows per workgroup (128)
 constexpr float kLazy = 8.f;     // raise the running max only past this margin (log2 units)
 
-template <typename Tout, bool kRing>
+template <typename Tout, bool kRing, bool kLse = false>
 __global__ void __launch_bounds__(NT, 2)
 attn_mfma_kernel(AttnParams p) {
   // The two buffers are four separate LDS objects addressed only by name (the
@@ -266,6 +266,9 @@ attn_mfma_kernel(AttnParams p) {
         const int qrow = wrow0 + rb * 32 + l32;
         const float ltot = sum_xor32(lsum[rb]);
         const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+        if (kLse && hl == 0 && qrow < p.P)
+          p.lse[((size_t(branch) * p.B + b) * p.H + h) * (size_t(p.T) * p.P) + size_t(fq) * p.P + qrow] =
+              ntiles > 0 ? m[rb] + log2f(ltot) : 0.f;
         if (qrow < p.P) {
           const size_t qbase = fbase + size_t(qrow) * HD;
 #pragma unroll
@@ -290,7 +293,9 @@ hipError_t launch_t(const AttnParams& p, hipStream_t st) {
   const long long grid = (total + kXcds - 1) / kXcds * kXcds;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (p.R == 0)
+  if (p.R == 0 && p.lse)   // whole clip, softmax statistics wanted (a separate instantiation)
+    hipLaunchKernelGGL((attn_mfma_kernel<Tout, false, true>), dim3(unsigned(grid)), dim3(NT), 0, st, p);
+  else if (p.R == 0)
     hipLaunchKernelGGL((attn_mfma_kernel<Tout, false>), dim3(unsigned(grid)), dim3(NT), 0, st, p);
   else
     hipLaunchKernelGGL((attn_mfma_kernel<Tout, true>), dim3(unsigned(grid)), dim3(NT), 0, st, p);

@@ -337,8 +337,8 @@ hipError_t launch_bwd_t(const BwdArgs& x, hipStream_t st) {
   const dim3 grid(unsigned(tiles * p.T), unsigned(p.H), unsigned(p.B));
   const Tg* g = static_cast<const Tg*>(x.d_mix);
   if (x.attn_mfma) {
-    const hipError_t e = launch_attn_bwd_mfma(p, x.d_mix, x.o_swa, x.o_dswa, x.mix_w, x.lse2, x.dsum, x.dq, x.dk,
-                                              x.dv, x.scale, st);
+    const hipError_t e = launch_attn_bwd_mfma(p, x.d_mix, x.o_swa, x.o_dswa, x.mix_w, x.lse2, x.lse_given != 0,
+                                              x.dsum, x.dq, x.dk, x.dv, x.scale, st);
     if (e != hipSuccess) return e;
   } else {
     hipLaunchKernelGGL((attn_bwd_stats<Tin, Tg, D>), grid, dim3(kThreads), 0, st, p, g, x.mix_w, x.lse2, x.dsum);

@@ -308,6 +308,32 @@ hlta_status hlta_attn_fwd(const hlta_config* cfg, const void* q, const void* k, 
   return run_mix(cfg, plan, o_swa, o_dswa, o_gdn, o_mix, mix_w, st);
 }
 
+hlta_status hlta_attn_fwd_lse(const hlta_config* cfg, const void* q, const void* k, const void* v,
+                              const float* mix_w, const void* o_gdn, void* o_swa, void* o_dswa, void* o_mix,
+                              float* lse, void* stream) {
+  clear_error();
+  Plan plan;
+  HLTA_TRY(check_config(cfg));
+  HLTA_TRY(make_plan(cfg, int64_t(cfg->T) * cfg->P, &plan));
+  if (plan.L == 0) return HLTA_OK;
+  HLTA_TRY(need(q, "q"));
+  HLTA_TRY(need(k, "k"));
+  HLTA_TRY(need(v, "v"));
+  HLTA_TRY(need(mix_w, "mix_w"));
+  HLTA_TRY(need(o_gdn, "o_gdn"));
+  HLTA_TRY(need(o_swa, "o_swa"));
+  HLTA_TRY(need(o_dswa, "o_dswa"));
+  HLTA_TRY(need(o_mix, "o_mix"));
+  HLTA_TRY(need(lse, "lse"));
+  if (cfg->rope_theta > 0.f)
+    return fail(HLTA_E_UNSUPPORTED, "the rotary embedding needs a workspace: use hlta_fwd");
+  AttnParams at = full_attn_params(cfg, q, k, v, o_swa, o_dswa);
+  at.lse = lse;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  HLTA_TRY(run_attn(cfg, plan, at, st));
+  return run_mix(cfg, plan, o_swa, o_dswa, o_gdn, o_mix, mix_w, st);
+}
+
 hlta_status hlta_quantize_fp8(const hlta_config* cfg, const void* q, const void* k, const void* v, void* q8,
                               void* k8, void* v8, float* scales, void* stream) {
   clear_error();
@@ -355,11 +381,15 @@ hlta_status hlta_attn_fwd_fp8(const hlta_config* cfg, const void* q8, const void
   return run_mix(cfg, plan, o_swa, o_dswa, o_gdn, o_mix, mix_w, st);
 }
 
-hlta_status hlta_bwd(const hlta_config* cfg, const void* q, const void* k, const void* v, const float* a,
-                     const float* b, const float* mix_w, const float* S0, const void* o_swa, const void* o_dswa,
-                     const void* o_gdn, const void* d_mix, float* dq, float* dk, float* dv, float* da, float* db,
-                     float* dmix_w, float* dS0, void* workspace, size_t ws_bytes, void* stream) {
-  clear_error();
+}  // extern "C"
+
+// hlta_bwd, with the softmax row statistics given (lse, from
+// hlta_attn_fwd_lse) or recomputed (lse NULL).
+static hlta_status bwd_impl(const hlta_config* cfg, const void* q, const void* k, const void* v, const float* a,
+                            const float* b, const float* mix_w, const float* S0, const void* o_swa,
+                            const void* o_dswa, const void* o_gdn, const void* d_mix, float* dq, float* dk,
+                            float* dv, float* da, float* db, float* dmix_w, float* dS0, const float* lse,
+                            void* workspace, size_t ws_bytes, void* stream) {
   Plan plan;
   BwdPlan bp;
   HLTA_TRY(check_config(cfg));
@@ -425,9 +455,35 @@ hlta_status hlta_bwd(const hlta_config* cfg, const void* q, const void* k, const
   x.C = cfg->gdn_chunk;
   x.scale = plan.scale;
   x.attn_mfma = plan.attn == Impl::Mfma && cfg->out_dtype == HLTA_BF16;
+  if (lse && x.attn_mfma) {
+    x.lse2 = const_cast<float*>(lse);   // read only: the statistics kernel is skipped
+    x.lse_given = 1;
+  }
   hipError_t e = launch_bwd(x, cfg->d, cfg->in_dtype, cfg->out_dtype, st);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return HLTA_OK;
+}
+
+extern "C" {
+
+hlta_status hlta_bwd(const hlta_config* cfg, const void* q, const void* k, const void* v, const float* a,
+                     const float* b, const float* mix_w, const float* S0, const void* o_swa, const void* o_dswa,
+                     const void* o_gdn, const void* d_mix, float* dq, float* dk, float* dv, float* da, float* db,
+                     float* dmix_w, float* dS0, void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  return bwd_impl(cfg, q, k, v, a, b, mix_w, S0, o_swa, o_dswa, o_gdn, d_mix, dq, dk, dv, da, db, dmix_w, dS0,
+                  nullptr, workspace, ws_bytes, stream);
+}
+
+hlta_status hlta_bwd_lse(const hlta_config* cfg, const void* q, const void* k, const void* v, const float* a,
+                         const float* b, const float* mix_w, const float* S0, const void* o_swa, const void* o_dswa,
+                         const void* o_gdn, const void* d_mix, const float* lse, float* dq, float* dk, float* dv,
+                         float* da, float* db, float* dmix_w, float* dS0, void* workspace, size_t ws_bytes,
+                         void* stream) {
+  clear_error();
+  if (cfg && int64_t(cfg->T) * cfg->P > 0) HLTA_TRY(need(lse, "lse"));
+  return bwd_impl(cfg, q, k, v, a, b, mix_w, S0, o_swa, o_dswa, o_gdn, d_mix, dq, dk, dv, da, db, dmix_w, dS0,
+                  lse, workspace, ws_bytes, stream);
 }
 
 static hlta_status check_stream(const hlta_config* cfg, const hlta_stream_state* st) {

@@ -55,6 +55,10 @@ struct AttnParams {
   // ro.frame[b]; rollouts in ro.skip are left out entirely (also without it).
   int per_rollout;
   RolloutFrames ro;
+  // Optional (whole-clip calls): per query row and branch, the log2 of the
+  // softmax denominator with scores in log2 units, [2, B, H, T*P]; 0 for a
+  // row with no keys.
+  float* lse;
 };
 
 // Absolute index of the call's first query frame for rollout b.

@@ -64,11 +64,12 @@ hipError_t launch_ring_store_rollouts(const void* src, void* ring, int R, int B,
                                       const RolloutFrames& sel, hipStream_t st);
 
 // Softmax-branch backward with bf16 MFMA (bf16 q, k, v, d_mix and stored
-// outputs, d = 128, P >= 64): lse and dsum are [2, B, H, L] fp32 scratch;
-// dq, dk, dv [B, L, H, d] fp32 are written (not accumulated).
+// outputs, d = 128, P >= 64): lse and dsum are [2, B, H, L] fp32 scratch
+// (lse given: filled by the forward already, not recomputed); dq, dk, dv
+// [B, L, H, d] fp32 are written (not accumulated).
 hipError_t launch_attn_bwd_mfma(const AttnParams& p, const void* d_mix, const void* o_swa, const void* o_dswa,
-                                const float* mix_w, float* lse, float* dsum, float* dq, float* dk, float* dv,
-                                float scale, hipStream_t st);
+                                const float* mix_w, float* lse, bool lse_given, float* dsum, float* dq, float* dk,
+                                float* dv, float scale, hipStream_t st);
 
 // Backward of the operator (bwd.hip): fp32 gradients of q, k, v [B, L, H, d],
 // a, b [B, L, H], mix_w [H, 3] and S0 [B, H, d, d] given d_mix (out dtype).
@@ -104,6 +105,7 @@ struct BwdArgs {
   int C;
   float scale;
   int attn_mfma;     // softmax branches on the bf16 MFMA kernels (bf16 in and out, d = 128, P >= 64)
+  int lse_given;     // lse2 holds the forward's statistics (MFMA path only)
 };
 
 // The gated delta rule's backward in matrix form (per chunk): phase 0 the

@@ -28,7 +28,8 @@ EXPORTS = ("hlta_abi_version", "hlta_status_string", "hlta_last_error", "hlta_va
            "hlta_fwd_workspace_bytes", "hlta_fwd", "hlta_gdn_fwd", "hlta_attn_fwd", "hlta_stream_ring_bytes",
            "hlta_stream_load_prefix", "hlta_step_workspace_bytes", "hlta_step_frame",
            "hlta_step_frame_rollouts", "hlta_quantize_fp8", "hlta_attn_fwd_fp8", "hlta_bwd_workspace_bytes",
-           "hlta_bwd", "hlta_fwd_noalloc", "hlta_ceiling_mfma_bf16", "hlta_ceiling_copy")
+           "hlta_bwd", "hlta_fwd_noalloc", "hlta_ceiling_mfma_bf16", "hlta_ceiling_copy", "hlta_attn_fwd_lse",
+           "hlta_bwd_lse")
 
 
 class hlta_config(ctypes.Structure):
@@ -76,6 +77,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "hlta_fwd_noalloc": (I32, [cfgp, P, P, P, P, P, P, P, P, P, P, P, P, P]),
         "hlta_gdn_fwd": (I32, [cfgp, P, P, P, P, P, P, P, P, P, S, P]),
         "hlta_attn_fwd": (I32, [cfgp, P, P, P, P, P, P, P, P, P]),
+        "hlta_attn_fwd_lse": (I32, [cfgp, P, P, P, P, P, P, P, P, P, P]),
         "hlta_stream_ring_bytes": (S, [cfgp, I32]),
         "hlta_stream_load_prefix": (I32, [cfgp, stp, P, P, I32, P, P]),
         "hlta_step_workspace_bytes": (S, [cfgp]),
@@ -86,6 +88,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "hlta_attn_fwd_fp8": (I32, [cfgp, P, P, P, P, P, P, P, P, P, P]),
         "hlta_bwd_workspace_bytes": (S, [cfgp]),
         "hlta_bwd": (I32, [cfgp] + [P] * 18 + [P, S, P]),
+        "hlta_bwd_lse": (I32, [cfgp] + [P] * 19 + [P, S, P]),
         "hlta_ceiling_mfma_bf16": (I32, [P, P, I32, I32, P]),
         "hlta_ceiling_copy": (I32, [P, P, S, P]),
     }
@@ -212,9 +215,21 @@ def hlta_bwd_workspace_bytes(cfg: hlta_config) -> int:
     return int(load_library().hlta_bwd_workspace_bytes(ctypes.byref(cfg)))
 
 
+def hlta_attn_fwd_lse(cfg: hlta_config, q, k, v, mix_w, o_gdn, out: dict, lse=None, stream=None):
+    """hlta_attn_fwd that also writes the softmax row statistics (C:
+    hlta_attn_fwd_lse); returns lse [2, B, H, L] float32 (allocated when None)."""
+    if lse is None:
+        lse = torch.empty((2, cfg.B, cfg.H, q.shape[1]), dtype=torch.float32, device=q.device)
+    _check(load_library().hlta_attn_fwd_lse(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(mix_w), _ptr(o_gdn),
+                                            _ptr(out["o_swa"]), _ptr(out["o_dswa"]), _ptr(out["o_mix"]), _ptr(lse),
+                                            _stream(stream)))
+    return lse
+
+
 def hlta_bwd(cfg: hlta_config, q, k, v, a, b, mix_w, fwd: dict, d_mix, S0=None, want_dS0: bool = True,
-             workspace=None, stream=None) -> dict:
-    """Gradients of <d_mix, o_mix> (C: hlta_bwd). fwd holds the forward's
+             workspace=None, stream=None, lse=None) -> dict:
+    """Gradients of <d_mix, o_mix> (C: hlta_bwd, or hlta_bwd_lse when the
+    forward's softmax statistics lse are given). fwd holds the forward's
     o_swa, o_dswa, o_gdn. Returns float32 dq, dk, dv [B, L, H, d], da, db
     [B, L, H], dmix_w [H, 3] and dS0 [B, H, d, d] (None unless want_dS0)."""
     dev = q.device
@@ -226,11 +241,15 @@ def hlta_bwd(cfg: hlta_config, q, k, v, a, b, mix_w, fwd: dict, d_mix, S0=None, 
     g["dS0"] = torch.empty((cfg.B, cfg.H, cfg.d, cfg.d), **f32) if want_dS0 else None
     if workspace is None:
         workspace = alloc_workspace(hlta_bwd_workspace_bytes(cfg), dev)
-    _check(load_library().hlta_bwd(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(mix_w),
-                                   _ptr(S0), _ptr(fwd["o_swa"]), _ptr(fwd["o_dswa"]), _ptr(fwd["o_gdn"]),
-                                   _ptr(d_mix), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["da"]),
-                                   _ptr(g["db"]), _ptr(g["dmix_w"]), _ptr(g["dS0"]), _ptr(workspace),
-                                   workspace.numel(), _stream(stream)))
+    lib = load_library()
+    head = [ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(mix_w), _ptr(S0),
+            _ptr(fwd["o_swa"]), _ptr(fwd["o_dswa"]), _ptr(fwd["o_gdn"]), _ptr(d_mix)]
+    tail = [_ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["da"]), _ptr(g["db"]), _ptr(g["dmix_w"]),
+            _ptr(g["dS0"]), _ptr(workspace), workspace.numel(), _stream(stream)]
+    if lse is None:
+        _check(lib.hlta_bwd(*head, *tail))
+    else:
+        _check(lib.hlta_bwd_lse(*head, _ptr(lse), *tail))
     return g
 
 

@@ -39,6 +39,8 @@ def short_name(name: str) -> str | None:
     short = short.split("(")[0]
     for mangled, plain in (("16attn_mfma_kernelIDF16bLb1", "attn_mfma_kernel<bf16, ring>"),
                            ("16attn_mfma_kernelIfLb1", "attn_mfma_kernel<float, ring>"),
+                           ("16attn_mfma_kernelIDF16bLb0ELb1", "attn_mfma_kernel<bf16, lse>"),
+                           ("16attn_mfma_kernelIfLb0ELb1", "attn_mfma_kernel<float, lse>"),
                            ("16attn_mfma_kernelIDF16b", "attn_mfma_kernel<bf16>"),
                            ("16attn_mfma_kernelIf", "attn_mfma_kernel<float>"),
                            ("14gdn_seg_kernelILb0E", "gdn_seg_kernel<maps>"),

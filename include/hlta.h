@@ -206,6 +206,24 @@ hlta_status hlta_attn_fwd(const hlta_config* cfg,
                           void* o_swa, void* o_dswa, void* o_mix, void* stream);
 
 /*
+ * hlta_attn_fwd_lse - hlta_attn_fwd that also writes the softmax row
+ * statistics the backward needs (each query row's log-sum-exp, which the
+ * tiled exact attention of the long-context page, section 03, carries
+ * anyway), so that hlta_bwd_lse does not recompute them:
+ * lse  [2, B, H, L] float32 (branch SWA then DSWA, batch row, head, token):
+ *      log2 of the row's softmax denominator with scores in log2 units,
+ *      log2 sum_j exp(scale * q . k_j); 0 for a row whose branch has no key
+ *      (written; the caller owns it).
+ * Outputs o_swa, o_dswa, o_mix are bit for bit those of hlta_attn_fwd. Other
+ * arguments and errors as hlta_attn_fwd; lse NULL gives HLTA_E_NULL.
+ */
+hlta_status hlta_attn_fwd_lse(const hlta_config* cfg,
+                              const void* q, const void* k, const void* v,
+                              const float* mix_w, const void* o_gdn,
+                              void* o_swa, void* o_dswa, void* o_mix,
+                              float* lse, void* stream);
+
+/*
  * FP8 variant of the softmax branches. The pages mention low-precision
  * attention without a method; the variant implemented quantises q, k, v per
  * (batch row, head) to e4m3 (1 sign, 4 exponent bits with bias 7, 3 mantissa
@@ -244,8 +262,9 @@ hlta_status hlta_attn_fwd_fp8(const hlta_config* cfg, const void* q8, const void
  *   memory: the exact gradient of the gated delta rule of hlta_fwd (Kairos
  *     related-work page, row A; long-context page, section 06): per chunk its
  *     transition, own state and own adjoint, chains over chunks for every
- *     chunk's start state and incoming adjoint, then each chunk's tokens run
- *     backwards; through the L2 normalisation of q and k when on.
+ *     chunk's start state and incoming adjoint, then each chunk's token
+ *     gradients in the chunk's matrix (UT / WY) form; through the L2
+ *     normalisation of q and k when on.
  * dq, dk, dv receive the sum over the three branches.
  *
  * q, k, v, a, b, mix_w, S0   the forward's inputs (read only)
@@ -257,8 +276,10 @@ hlta_status hlta_attn_fwd_fp8(const hlta_config* cfg, const void* q8, const void
  * dS0        [B, H, d, d] float32 gradient of the start state, or NULL
  * workspace  device buffer of at least hlta_bwd_workspace_bytes(cfg) bytes
  * The gates are taken as given (gate_logits = 1 and the rotary embedding give
- * HLTA_E_UNSUPPORTED). The memory's gradients are evaluated in fp32. The
- * softmax branches' are too, except with bf16 inputs and outputs, d = 128 and
+ * HLTA_E_UNSUPPORTED). The memory's gradients are evaluated with fp32
+ * accumulation, their matrix products on bf16 MFMA with each fp32 factor split
+ * into two bf16 parts (close to fp32 accuracy). The softmax branches' are in
+ * fp32, except with bf16 inputs and outputs, d = 128 and
  * P >= 64, where they run on bf16 MFMA (fp32 accumulation; P and dS rounded
  * to bf16 for their products; D = do . o from the stored outputs).
  * Validation (NULL, alignment, workspace size, config) happens before any
@@ -273,6 +294,23 @@ hlta_status hlta_bwd(const hlta_config* cfg,
                      float* dq, float* dk, float* dv, float* da, float* db,
                      float* dmix_w, float* dS0,
                      void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * hlta_bwd_lse - hlta_bwd with the softmax row statistics given: lse as
+ * hlta_attn_fwd_lse wrote it for the same cfg, q and k (read only). Where the
+ * softmax branches run on bf16 MFMA (see above) their statistics pass is
+ * skipped; elsewhere the statistics are recomputed and lse is not read. Other
+ * arguments, results and errors as hlta_bwd (same workspace size); lse NULL
+ * with L > 0 gives HLTA_E_NULL.
+ */
+hlta_status hlta_bwd_lse(const hlta_config* cfg,
+                         const void* q, const void* k, const void* v,
+                         const float* a, const float* b, const float* mix_w, const float* S0,
+                         const void* o_swa, const void* o_dswa, const void* o_gdn, const void* d_mix,
+                         const float* lse,
+                         float* dq, float* dk, float* dv, float* da, float* db,
+                         float* dmix_w, float* dS0,
+                         void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Streaming (Kairos article on zhichai.net, section 2.3: streaming tokens so

@@ -98,6 +98,29 @@ def attend_rows(q_rows, k, v, P, frames, scale=None):
     return (e @ vv) / e.sum(axis=1, keepdims=True)
 
 
+def frame_softmax_lse2(q, k, T, P, frames_of, scale=None):
+    """Per query row, the log2 of its softmax denominator,
+    log2 sum_j exp(scale q_i . k_j), over the keys of its frame set (the
+    log-sum-exp that tiled exact attention carries per row, long-context page,
+    section 03, here in log2 units); 0 for a row with no key frame.
+
+    q, k: [T*P, d] float64 of one (batch, head); frames_of as in
+    frame_softmax_attention. Returns [T*P]."""
+    q = np.asarray(q, np.float64)
+    d = q.shape[1]
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    out = np.zeros(T * P)
+    for f in range(T):
+        frames = frames_of(f)
+        if not frames:
+            continue
+        idx = np.concatenate([np.arange(g * P, (g + 1) * P) for g in frames])
+        z = scale * (q[f * P:(f + 1) * P] @ np.asarray(k[idx], np.float64).T)
+        zm = z.max(axis=1)
+        out[f * P:(f + 1) * P] = (zm + np.log(np.exp(z - zm[:, None]).sum(axis=1))) / np.log(2.0)
+    return out
+
+
 def swa(q, k, v, T, P, W, scale=None):
     return frame_softmax_attention(q, k, v, T, P, lambda f: swa_frames(f, W), scale)
 

@@ -231,3 +231,31 @@ def test_bwd_workspace_and_argument_errors(lib):
     assert call(_cfg(gate_logits=1), args) == 4
     rope = _cfg(rope_theta=10000.0, rope_grid=(30, 52))
     assert call(rope, args) == 4
+    # hlta_bwd_lse: the same checks, and the statistics themselves are required
+    args_lse = args[:11] + [fake] + args[11:]   # lse after d_mix
+
+    def call_lse(c, a, nbytes=ws):
+        return lib.hlta_bwd_lse(ctypes.byref(c), *a, nbytes, None)
+
+    a2 = list(args_lse)
+    a2[11] = None
+    assert call_lse(cfg, a2) == 1 and b"lse is NULL" in lib.hlta_last_error()
+    a2 = list(args_lse)
+    a2[0] = None
+    assert call_lse(cfg, a2) == 1 and b"q is NULL" in lib.hlta_last_error()
+    assert call_lse(cfg, args_lse, ws - 1) == 5
+
+
+def test_attn_fwd_lse_argument_errors(lib):
+    """hlta_attn_fwd_lse checks what hlta_attn_fwd checks, and its lse output."""
+    cfg = _cfg()
+    fake = ctypes.c_void_p(1 << 20)
+    args = [fake] * 8   # q, k, v, mix_w, o_gdn, o_swa, o_dswa, o_mix
+    assert lib.hlta_attn_fwd_lse(ctypes.byref(cfg), *args, None, None) == 1
+    assert b"lse is NULL" in lib.hlta_last_error()
+    a2 = list(args)
+    a2[0] = None
+    assert lib.hlta_attn_fwd_lse(ctypes.byref(cfg), *a2, fake, None) == 1
+    assert lib.hlta_attn_fwd_lse(ctypes.byref(cfg), *args, ctypes.c_void_p((1 << 20) + 4), None) == 6
+    rope = _cfg(rope_theta=10000.0, rope_grid=(30, 52))
+    assert lib.hlta_attn_fwd_lse(ctypes.byref(rope), *args, fake, None) == 4

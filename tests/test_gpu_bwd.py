@@ -81,6 +81,59 @@ def test_bwd_matches_oracle(name, wl, out_dt, impl):
         assert e <= tol, f"{name} {n}: rel-L2 {e:.3e} > {tol:.0e}"
 
 
+LSE_CASES = [("bf16_mfma_B2_P100", CASES[4][1], "bf16", AUTO), ("tiny_f32", CASES[0][1], "f32", AUTO)]
+
+
+@pytest.mark.parametrize("name,wl,out_dt,impl", LSE_CASES, ids=[c[0] for c in LSE_CASES])
+def test_forward_statistics_and_backward_with_them(name, wl, out_dt, impl):
+    """hlta_attn_fwd_lse leaves the outputs of hlta_attn_fwd unchanged (bit for
+    bit) and writes each row's log-sum-exp (log2 units) as the oracle's
+    frame_softmax_lse2 gives it, 0 for rows without keys; hlta_bwd_lse with
+    those statistics gives hlta_bwd's gradients (to the rounding of the
+    statistics) and the oracle's, to the same bar as test_bwd_matches_oracle."""
+    print(f"case {name} with forward statistics", flush=True)
+    x = I.make_clip(wl)
+    cfg = H.make_config(wl, out_dtype=out_dt, impl=impl)
+    dev = H.to_device(x, wl.dtype)
+    S0 = _start_state(wl)
+    S0_t = torch.from_numpy(S0).cuda()
+    fwd = H.hlta_fwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], S0=S0_t)
+    out2 = H.alloc_outputs(cfg, wl.L)
+    lse = H.hlta_attn_fwd_lse(cfg, dev["q"], dev["k"], dev["v"], dev["w"], fwd["o_gdn"], out2)
+    torch.cuda.synchronize()
+    for n in ("o_swa", "o_dswa", "o_mix"):
+        assert torch.equal(out2[n], fwd[n]), n
+    got_lse = lse.double().cpu().numpy()
+    worst = 0.0
+    for b in range(wl.B):
+        for h in range(wl.H):
+            qb, kb = x["q"][b, :, h].astype(np.float64), x["k"][b, :, h].astype(np.float64)
+            sets = (lambda f: O.swa_frames(f, wl.swa_frames),
+                    lambda f: O.dswa_frames(f, wl.dswa_dilation, wl.dswa_taps))
+            for br, frames_of in enumerate(sets):
+                ref = O.frame_softmax_lse2(qb, kb, wl.T, wl.P, frames_of)
+                worst = max(worst, float(np.abs(got_lse[br, b, h] - ref).max()))
+    print(f"{name} lse max abs error (log2 units) {worst:.2e}", flush=True)
+    assert worst <= (1e-3 if out_dt == "bf16" else 1e-5)
+    g = I.upstream_grad(wl, out_dt)
+    g_t = torch.from_numpy(g).cuda().to(torch.bfloat16 if out_dt == "bf16" else torch.float32)
+    plain = H.hlta_bwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], fwd, g_t, S0=S0_t)
+    given = H.hlta_bwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], fwd, g_t, S0=S0_t,
+                       lse=lse)
+    torch.cuda.synchronize()
+    ref = dict(zip(GRADS, O.hlta_backward(x["q"], x["k"], x["v"], x["a"], x["b"], x["w"], g, wl.T, wl.P,
+                                          wl.swa_frames, wl.dswa_dilation, wl.dswa_taps, S0=S0)))
+    mfma = _mfma(wl, out_dt, impl)
+    for n in GRADS:
+        same = O.rel_l2(to64(given[n]), to64(plain[n]))
+        e = O.rel_l2(to64(given[n]), ref[n])
+        print(f"{name} {n}: vs hlta_bwd {same:.1e}, vs oracle {e:.2e}", flush=True)
+        # the generic kernels recompute the statistics, so they match exactly
+        assert same <= (1e-3 if mfma else 0.0), n
+        loose = (n == "dmix_w" and out_dt == "bf16") or (mfma and n in ("dq", "dk", "dv"))
+        assert e <= (TOL["bf16"] if loose else TOL["f32"]), n
+
+
 def test_bwd_without_start_state_gradient():
     """dS0 = NULL is allowed; the other gradients are unchanged, and a NULL S0
     means the zero start state."""

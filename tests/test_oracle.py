@@ -145,6 +145,33 @@ def test_softmax_branch_invariants():
     np.testing.assert_allclose(moved[2 * P:], base[2 * P:], rtol=1e-12)
 
 
+def test_row_lse_closed_forms_and_library():
+    """frame_softmax_lse2: zero queries give log2 of the key count; adding
+    c q_i / |q_i|^2 to every key shifts row i by c log2(e) (and no other row of
+    another frame); rows with no key frame are 0; on one frame it equals
+    torch.logsumexp of the scaled scores divided by ln 2."""
+    T, P, d = 5, 7, 8
+    q, k = _rand(30, T * P, d), _rand(31, T * P, d)
+    sw = lambda f: O.swa_frames(f, 2)
+    ds = lambda f: O.dswa_frames(f, 2, 2)
+    z = O.frame_softmax_lse2(np.zeros_like(q), k, T, P, sw)
+    counts = np.repeat([len(sw(f)) * P for f in range(T)], P)
+    np.testing.assert_allclose(z, np.log2(counts), rtol=0, atol=1e-13)
+    lz = O.frame_softmax_lse2(q, k, T, P, ds)
+    np.testing.assert_array_equal(lz[:2 * P], 0.0)   # frames 0, 1 have no dilated frame
+    # one query row, shifted keys
+    i, c = 3 * P + 2, 0.7
+    qi = q[i]
+    k2 = k + c * qi / (qi @ qi) * np.sqrt(d)   # scale 1/sqrt(d) cancels the sqrt(d)
+    base = O.frame_softmax_lse2(q, k, T, P, sw)
+    moved = O.frame_softmax_lse2(q, k2, T, P, sw)
+    assert abs((moved[i] - base[i]) - c / math.log(2.0)) < 1e-12
+    # single frame against the library
+    s1 = O.frame_softmax_lse2(q[:P], k[:P], 1, P, lambda f: [0])
+    ref = torch.logsumexp(torch.from_numpy(q[:P] @ k[:P].T / np.sqrt(d)), dim=1).numpy() / math.log(2.0)
+    np.testing.assert_allclose(s1, ref, rtol=1e-13, atol=1e-13)
+
+
 # ---------------------------------------------------------------------------
 # gated delta rule: closed forms and invariants
 # ---------------------------------------------------------------------------
