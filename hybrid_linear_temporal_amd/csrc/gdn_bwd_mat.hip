@@ -119,12 +119,19 @@ __device__ __forceinline__ bf16x8_t ld_kmaj(const bf16* st, int k0, int c0, int 
   return bf16x8_t{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
 }
 
+template <int M, int N>
+constexpr int mm_tpw() { return ((M / 32) * (N / 32) + 3) / 4; }   // 32 x 32 output tiles per wave
+
+__device__ __forceinline__ float4 operator*(float s, const float4& x) { return make_float4(s * x.x, s * x.y, s * x.z, s * x.w); }
+
+// Accumulates sa op(A) op(B) into the wave's output tiles c (sa = +-1, applied
+// to A's values as they are staged, so exactly).
 template <int M, int N, int K, bool TA, bool TB>
-__device__ __attribute__((noinline)) void mm(float* C, int ldc, const float* A, int lda, const float* B, int ldb,
-                                             float alpha, const float* Z, float* lds) {
+__device__ __forceinline__ void mm_term(f32x16_t (&c)[((M / 32) * (N / 32) + 3) / 4], const float* A, int lda, const float* B,
+                                        int ldb, float sa, float* lds) {
   constexpr int KS = K < kKS ? K : kKS;   // k of one slice
   static_assert(M % 32 == 0 && N % 32 == 0 && K % KS == 0 && KS % 16 == 0 && M <= 128 && N <= 128, "aligned shapes");
-  constexpr int NT = (M / 32) * (N / 32), TPW = (NT + 3) / 4;   // tiles, tiles per wave
+  constexpr int NT = (M / 32) * (N / 32), TPW = mm_tpw<M, N>();
   constexpr int NA = M * KS / 4 / kNT, NB = N * KS / 4 / kNT;   // float4 of A and B per thread per slice
   static_assert(NA * kNT * 4 == M * KS && NB * kNT * 4 == N * KS, "slices split evenly over the threads");
   constexpr int SA = TA ? KS * M : M * kRow, SB = TB ? N * kRow : KS * N;   // bf16 per staged part
@@ -134,11 +141,6 @@ __device__ __attribute__((noinline)) void mm(float* C, int ldc, const float* A, 
   bf16* Bhi = Alo + SA;
   bf16* Blo = Bhi + SB;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
-  f32x16_t c[TPW];
-#pragma unroll
-  for (int u = 0; u < TPW; ++u)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) c[u][r] = 0.f;
   // staging in rounds of at most 8 float4 per thread (A's first, then B's),
   // each round's loads in flight together
   constexpr int kBatch = 8;
@@ -179,10 +181,10 @@ __device__ __attribute__((noinline)) void mm(float* C, int ldc, const float* A, 
           if (TA) {
             const int kk = e / (M / 4), i4 = e % (M / 4);
             const int o = kmaj_off<M>(kk, 4 * i4);
-            split_store4(Ahi + o, Alo + o, x[v]);
+            split_store4(Ahi + o, Alo + o, sa * x[v]);
           } else {
             const int i = e / (KS / 4), k4 = e % (KS / 4);
-            split_store4(Ahi + i * kRow + 4 * k4, Alo + i * kRow + 4 * k4, x[v]);
+            split_store4(Ahi + i * kRow + 4 * k4, Alo + i * kRow + 4 * k4, sa * x[v]);
           }
         } else if (u < NA + NB) {
           const int e = tid + (u - NA) * kNT;
@@ -230,6 +232,14 @@ __device__ __attribute__((noinline)) void mm(float* C, int ldc, const float* A, 
       }
     }
   }
+}
+
+// C = alpha c + Z (Z may be C itself or null), then a barrier
+template <int M, int N>
+__device__ __forceinline__ void mm_store(const f32x16_t (&c)[((M / 32) * (N / 32) + 3) / 4], float* C, int ldc, float alpha,
+                                         const float* Z) {
+  constexpr int NT = (M / 32) * (N / 32), TPW = mm_tpw<M, N>();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hl = lane >> 5;
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     const int t = wave + 4 * u;
@@ -245,6 +255,35 @@ __device__ __attribute__((noinline)) void mm(float* C, int ldc, const float* A, 
     }
   }
   __syncthreads();
+}
+
+
+template <int M, int N, int K, bool TA, bool TB>
+__device__ __attribute__((noinline)) void mm(float* C, int ldc, const float* A, int lda, const float* B, int ldb,
+                                             float alpha, const float* Z, float* lds) {
+  f32x16_t c[mm_tpw<M, N>()];
+#pragma unroll
+  for (int u = 0; u < mm_tpw<M, N>(); ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[u][r] = 0.f;
+  mm_term<M, N, K, TA, TB>(c, A, lda, B, ldb, 1.f, lds);
+  mm_store<M, N>(c, C, ldc, alpha, Z);
+}
+
+// C = sa1 op(A1) op(B1) + sa2 op(A2) op(B2) (+ Z): two products summed in the
+// accumulators (one pass over C instead of two); sa1, sa2 = +-1.
+template <int M, int N, int K1, bool TA1, bool TB1, int K2, bool TA2, bool TB2>
+__device__ __attribute__((noinline)) void mm2(float* C, int ldc, const float* A1, int lda1, const float* B1, int ldb1,
+                                              float sa1, const float* A2, int lda2, const float* B2, int ldb2,
+                                              float sa2, const float* Z, float* lds) {
+  f32x16_t c[mm_tpw<M, N>()];
+#pragma unroll
+  for (int u = 0; u < mm_tpw<M, N>(); ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[u][r] = 0.f;
+  mm_term<M, N, K1, TA1, TB1>(c, A1, lda1, B1, ldb1, sa1, lds);
+  mm_term<M, N, K2, TA2, TB2>(c, A2, lda2, B2, ldb2, sa2, lds);
+  mm_store<M, N>(c, C, ldc, 1.f, Z);
 }
 
 // Elementwise passes over the chunk's arrays as 16-byte vectors: ld(e)
@@ -276,7 +315,6 @@ __device__ __forceinline__ void ew(LD ld, ST st) {
 struct F4x2 { float4 a, b; };
 struct F4x3 { float4 a, b, c; };
 struct F4x4 { float4 a, b, c, d; };
-__device__ __forceinline__ float4 operator*(float s, const float4& x) { return make_float4(s * x.x, s * x.y, s * x.z, s * x.w); }
 __device__ __forceinline__ float4 operator+(const float4& x, const float4& y) {
   return make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
 }
@@ -359,9 +397,11 @@ struct Slot {
   __device__ float* cc(int i) const { return base + 16 * CD + i * CC; }  // [CM][CM] matrices 0 ..
 };
 // [CM][D] slots
-enum { sK = 0, sQ, sV, sDO, sBK, sDK, sW, sUp, sU, sDU, sX1, sX2, sX3, sDKG, sBV };
+// (K, Q adjacent: one product forms K K^T and Q K^T; dO, dU adjacent and X1, X2
+// adjacent: one product forms dO S and dU S)
+enum { sK = 0, sQ, sV, sDO, sDU, sBK, sDK, sW, sUp, sU, sX1, sX2, sX3, sDKG, sBV };
 // [CM][CM] slots
-enum { sGK = 0, sT, sP, sDP, sDPG, sE1, sE2 };
+enum { sGK = 0, sP, sT, sDP, sDPG, sE1, sE2 };   // GK, P adjacent
 
 // Chunk vectors in LDS
 struct ChunkVec {
@@ -473,16 +513,16 @@ __device__ void chunk_forward(const GdnParams& p, int C, const Tg* d_mix, float 
         f4(BV)[e] = v.b[t] * x.c;
       });
   __syncthreads();
-  // GK = strict_lower(Gam . K K^T), T = (I + diag(b) GK)^-1
+  // [GK; P] = [K; Q] K^T in one product; GK = strict_lower(Gam . K K^T),
+  // P = lower(Gam . Q K^T), T = (I + diag(b) GK)^-1
   float *GK = s.cc(sGK), *Tm = s.cc(sT), *P = s.cc(sP);
-  mm<CM, CM, D, false, true>(GK, CM, K, D, K, D, 1.f, nullptr, lds);
+  static_assert(sQ == sK + 1 && sP == sGK + 1, "K, Q and GK, P adjacent");
+  mm<2 * CM, CM, D, false, true>(GK, CM, K, D, K, D, 1.f, nullptr, lds);
   gam_mask<true>(GK, v);
+  gam_mask<false>(P, v);
   tri_inverse(Tm, GK, v.b, lds);
   mm<CM, D, CM, false, false>(s.cd(sW), D, Tm, CM, BK, D, 1.f, nullptr, lds);
   mm<CM, D, CM, false, false>(s.cd(sUp), D, Tm, CM, BV, D, 1.f, nullptr, lds);
-  // P = lower(Gam . Q K^T)
-  mm<CM, CM, D, false, true>(P, CM, Q, D, K, D, 1.f, nullptr, lds);
-  gam_mask<false>(P, v);
 }
 
 // Per chunk: M (Am), N (Um) and the chunk's own adjoint X (Xm).
@@ -592,8 +632,10 @@ gdn_bwd_mat_grad(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float*
                          f4(dPG)[e] = y;
                        });
     __syncthreads();
+    // [X1; X2] = [dO; dU] S in one product (X2 = dU S = -dW)
+    static_assert(sDU == sDO + 1 && sX2 == sX1 + 1, "dO, dU and X1, X2 adjacent");
+    mm<2 * CM, D, D, false, false>(X1, D, dO, D, S, D, 1.f, nullptr, lds);
     // dq^ = diag(gamma) dO S + dPG K (the row dots q_i . (dO S)_i first)
-    mm<CM, D, D, false, false>(X1, D, dO, D, S, D, 1.f, nullptr, lds);
     rowdot<D>(v.v1, X1, Q);   // q_i . (dO S)_i
     ew<CM * D / 4, 2>([&](int e) { return f4(X1)[e]; },
                       [&](int e, const float4& x) { f4(X1)[e] = v.gam[(4 * e) / D] * x; });
@@ -603,13 +645,11 @@ gdn_bwd_mat_grad(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float*
     rowdot<D>(v.v2, X1, Q);   // q^ . dq^
     add_rows(dq, X1, Q, v.v2, v.rq, p.l2norm != 0);
     __syncthreads();
-    // dW = -dU S (X2), T^T dW (X3), dT = dW (diag(b gamma) K)^T (E1)
-    mm<CM, D, D, false, false>(X2, D, dU, D, S, D, -1.f, nullptr, lds);
-    mm<CM, D, CM, true, false>(X3, D, Tm, CM, X2, D, 1.f, nullptr, lds);
-    mm<CM, CM, D, false, true>(E1, CM, X2, D, BK, D, 1.f, nullptr, lds);
-    // T^T dU (X2), dT += dU (diag(b) V)^T
+    // dW = -X2: T^T dW (X3), dT = dW (diag(b gamma) K)^T + dU (diag(b) V)^T (E1, one pass)
+    mm<CM, D, CM, true, false>(X3, D, Tm, CM, X2, D, -1.f, nullptr, lds);
+    mm2<CM, CM, D, false, true, D, false, true>(E1, CM, X2, D, BK, D, -1.f, dU, D, BV, D, 1.f, nullptr, lds);
+    // T^T dU (X2)
     mm<CM, D, CM, true, false>(X2, D, Tm, CM, dU, D, 1.f, nullptr, lds);
-    mm<CM, CM, D, false, true>(E1, CM, dU, D, BV, D, 1.f, E1, lds);
     // dv = diag(b) T^T dU; row dots for db
     add_rows(dv, X2, nullptr, nullptr, v.b, false);
     rowdot<D>(v.v2, X2, V);   // (T^T dU)_i . v_i
@@ -721,7 +761,17 @@ gdn_bwd_mat_grad(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float*
       }
       if (i < n) da[g0 + size_t(i) * p.H] = v.a[i] > 0.f ? dg / v.a[i] : 0.f;
     }
-    // dk^ = De U G + diag(b gamma) T^T dW + dPG^T Q + dKK K + dKK^T K
+    // dk^ = De U G + diag(b gamma) T^T dW + dPG^T Q + (dKK + dKK^T) K; the
+    // symmetric part of dKK into E1 (free after the gate sums)
+    ew<CM * CM / 4, 4>(
+        [&](int e) {
+          const int i = (4 * e) / CM, j0 = (4 * e) % CM;
+          F4x2 y;
+          y.a = f4(E2)[e];
+          y.b = make_float4(E2[(j0 + 0) * CM + i], E2[(j0 + 1) * CM + i], E2[(j0 + 2) * CM + i], E2[(j0 + 3) * CM + i]);
+          return y;
+        },
+        [&](int e, const F4x2& y) { f4(E1)[e] = y.a + y.b; });
     mm<CM, D, D, false, false>(X1, D, U, D, G, D, 1.f, nullptr, lds);
     ew<CM * D / 4, 2>(
         [&](int e) {
@@ -735,9 +785,7 @@ gdn_bwd_mat_grad(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float*
           f4(X1)[e] = v.De[t] * y.a + (v.b[t] * v.gam[t]) * y.b;
         });
     __syncthreads();
-    mm<CM, D, CM, true, false>(X1, D, dPG, CM, Q, D, 1.f, X1, lds);
-    mm<CM, D, CM, false, false>(X1, D, E2, CM, K, D, 1.f, X1, lds);
-    mm<CM, D, CM, true, false>(X1, D, E2, CM, K, D, 1.f, X1, lds);
+    mm2<CM, D, CM, true, false, CM, false, false>(X1, D, dPG, CM, Q, D, 1.f, E1, CM, K, D, 1.f, X1, lds);
     rowdot<D>(v.v2, X1, K);   // k^ . dk^
     add_rows(dk, X1, K, v.v2, v.rk, p.l2norm != 0);
     __syncthreads();
