@@ -270,6 +270,42 @@ __device__ __attribute__((noinline)) void mm(float* C, int ldc, const float* A, 
   mm_store<M, N>(c, C, ldc, alpha, Z);
 }
 
+// [GK; P] = [K; Q] K^T with the causal gate factors applied as they are
+// stored: GK_ij = exp(g_i - g_j) (K K^T)_ij for j < i, P_ij = exp(g_i - g_j)
+// (Q K^T)_ij for j <= i, 0 elsewhere; GK also goes to LDS (at lds, CM x CM)
+// for the triangular solve that follows. K and Q are adjacent [CM][D] arrays.
+template <int D>
+__device__ __attribute__((noinline)) void gk_p(float* GKP, const float* KQ, const float* g, float* lds) {
+  constexpr int M = 2 * CM, N = CM;
+  f32x16_t c[mm_tpw<M, N>()];
+#pragma unroll
+  for (int u = 0; u < mm_tpw<M, N>(); ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[u][r] = 0.f;
+  mm_term<M, N, D, false, true>(c, KQ, D, KQ, D, 1.f, lds);
+  __syncthreads();   // the staging area becomes the solve's copy of GK
+  constexpr int NT = (M / 32) * (N / 32);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hl = lane >> 5;
+#pragma unroll
+  for (int u = 0; u < mm_tpw<M, N>(); ++u) {
+    const int t = wave + 4 * u;
+    if (t < NT) {
+      const int tm = t / (N / 32), tn = t % (N / 32);
+      const int j = 32 * tn + l32;
+      const float gj = g[j];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * tm + 8 * (r >> 2) + 4 * hl + (r & 3), i = row % CM;
+        const bool keep = row < CM ? j < i : j <= i;
+        const float x = keep ? expf(g[i] - gj) * c[u][r] : 0.f;
+        GKP[size_t(row) * N + j] = x;
+        if (row < CM) lds[row * CM + j] = x;
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // C = sa1 op(A1) op(B1) + sa2 op(A2) op(B2) (+ Z): two products summed in the
 // accumulators (one pass over C instead of two); sa1, sa2 = +-1.
 template <int M, int N, int K1, bool TA1, bool TB1, int K2, bool TA2, bool TB2>
@@ -356,12 +392,10 @@ __device__ void rowdot(float* out, const float* X, const float* Y) {
   __syncthreads();
 }
 
-// T = (I + diag(b) L)^-1 for strictly lower L [CM][CM] (global): L goes to
-// LDS; four lanes per column j (lane q holds t_m for m = q mod 4) solve it by
-// forward substitution, the partial dot products joined by two shuffles.
-__device__ __attribute__((noinline)) void tri_inverse(float* Tm, const float* L, const float* b, float* lds) {
-  ew<CM * CM / 4, 2>([&](int e) { return f4(L)[e]; }, [&](int e, const float4& x) { f4(lds)[e] = x; });
-  __syncthreads();
+// T = (I + diag(b) L)^-1 for strictly lower L [CM][CM] (in LDS): four lanes
+// per column j (lane q holds t_m for m = q mod 4) solve it by forward
+// substitution, the partial dot products joined by two shuffles.
+__device__ __attribute__((noinline)) void tri_inverse(float* Tm, const float* b, const float* lds) {
   const int j = threadIdx.x >> 2, q = threadIdx.x & 3;
   float t[CM / 4];
 #pragma unroll
@@ -412,25 +446,6 @@ struct ChunkVec {
   float gC;
 };
 
-// [CM][CM] masked by the causal pattern: strict (j < i) or inclusive (j <= i),
-// each kept entry scaled by exp(g_i - g_j)
-template <bool kStrict>
-__device__ void gam_mask(float* X, const ChunkVec& v) {
-  ew<CM * CM / 4, 2>([&](int e) { return f4(X)[e]; },
-                     [&](int e, float4 x) {
-                       const int i = (4 * e) / CM, j0 = (4 * e) % CM;
-                       float* xs = reinterpret_cast<float*>(&x);
-#pragma unroll
-                       for (int q = 0; q < 4; ++q) {
-                         const int j = j0 + q;
-                         const bool keep = kStrict ? j < i : j <= i;
-                         xs[q] = keep ? expf(v.g[i] - v.g[j]) * xs[q] : 0.f;
-                       }
-                       f4(X)[e] = x;
-                     });
-  __syncthreads();
-}
-
 // Loads chunk c of head (b, h): K, Q (normalised), V, dO = w2 d_mix, gates,
 // then forms diag(b gamma) K, De K, diag(b) V, strict_lower(Gam . K K^T), T,
 // W, U' and P. Rows t >= n are zero (gates a = 1, b = 0).
@@ -446,6 +461,32 @@ __device__ void chunk_forward(const GdnParams& p, int C, const Tg* d_mix, float 
   const Tin* k = static_cast<const Tin*>(p.k);
   const Tin* vv = static_cast<const Tin*>(p.v);
   float *K = s.cd(sK), *Q = s.cd(sQ), *V = s.cd(sV), *dO = s.cd(sDO);
+  float *BK = s.cd(sBK), *DK = s.cd(sDK), *BV = s.cd(sBV);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // gates first: prefix sums g of log a, gamma, b, De = gamma_C / gamma
+  if (wave == 0) {
+    const int t = lane;
+    const float at = t < n ? p.a[g0 + size_t(t) * p.H] : 1.f;
+    const float bt = t < n ? p.b[g0 + size_t(t) * p.H] : 0.f;
+    float la = at > 0.f ? fmaxf(logf(at), kLogFloor) : kLogFloor;
+    if (t >= n) la = 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(la, off);
+      if (lane >= off) la += y;
+    }
+    const float gl = __shfl(la, CM - 1);
+    v.g[t] = la;
+    v.gam[t] = expf(la);
+    v.a[t] = at;
+    v.b[t] = bt;
+    v.De[t] = expf(gl - la);
+    if (t == 0) v.gC = expf(gl);
+  }
+  __syncthreads();
+  // the inputs in one pass: K^, Q^ (each row's squared norm joined over the
+  // D/4 consecutive lanes that hold the row), V, dO = w2 d_mix, and from them
+  // diag(b gamma) K^, De K^, diag(b) V
   ew<CM * D / 4, 2>(
       [&](int e) {
         const int t = (4 * e) / D, j = (4 * e) % D;
@@ -461,66 +502,36 @@ __device__ void chunk_forward(const GdnParams& p, int C, const Tg* d_mix, float 
         return x;
       },
       [&](int e, const F4x4& x) {
-        f4(K)[e] = x.a;
-        f4(Q)[e] = x.b;
+        const int t = (4 * e) / D;
+        float sk = dot4(x.a, x.a), sq = dot4(x.b, x.b);
+#pragma unroll
+        for (int off = 1; off < D / 4; off <<= 1) {
+          sk += __shfl_xor(sk, off);
+          sq += __shfl_xor(sq, off);
+        }
+        const float rk = p.l2norm ? 1.f / sqrtf(sk + kEps) : 1.f;
+        const float rq = p.l2norm ? 1.f / sqrtf(sq + kEps) : 1.f;
+        if (e % (D / 4) == 0) {
+          v.rk[t] = rk;
+          v.rq[t] = rq;
+        }
+        const float4 kx = rk * x.a;
+        f4(K)[e] = kx;
+        f4(Q)[e] = rq * x.b;
         f4(V)[e] = x.c;
         f4(dO)[e] = w2 * x.d;
-      });
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (wave == 0) {
-    const int t = lane;
-    const float at = t < n ? p.a[g0 + size_t(t) * p.H] : 1.f;
-    const float bt = t < n ? p.b[g0 + size_t(t) * p.H] : 0.f;
-    float la = at > 0.f ? fmaxf(logf(at), kLogFloor) : kLogFloor;
-    if (t >= n) la = 0.f;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_up(la, off);
-      if (lane >= off) la += y;
-    }
-    v.g[t] = la;
-    v.gam[t] = expf(la);
-    v.a[t] = at;
-    v.b[t] = bt;
-  }
-  __syncthreads();   // K, Q written; gates
-  rowdot<D>(v.v0, K, K);
-  rowdot<D>(v.v1, Q, Q);
-  if (threadIdx.x < CM) {
-    const int t = threadIdx.x;
-    v.rk[t] = p.l2norm ? 1.f / sqrtf(v.v0[t] + kEps) : 1.f;
-    v.rq[t] = p.l2norm ? 1.f / sqrtf(v.v1[t] + kEps) : 1.f;
-    v.De[t] = expf(v.g[CM - 1] - v.g[t]);
-  }
-  if (threadIdx.x == 0) v.gC = v.gam[CM - 1];
-  __syncthreads();
-  float *BK = s.cd(sBK), *DK = s.cd(sDK), *BV = s.cd(sBV);
-  ew<CM * D / 4, 2>(
-      [&](int e) {
-        F4x3 x;
-        x.a = f4(K)[e];
-        x.b = f4(Q)[e];
-        x.c = f4(V)[e];
-        return x;
-      },
-      [&](int e, const F4x3& x) {
-        const int t = (4 * e) / D;
-        const float4 kx = v.rk[t] * x.a;
-        f4(K)[e] = kx;
-        f4(Q)[e] = v.rq[t] * x.b;
         f4(BK)[e] = (v.b[t] * v.gam[t]) * kx;
         f4(DK)[e] = v.De[t] * kx;
         f4(BV)[e] = v.b[t] * x.c;
       });
   __syncthreads();
-  // [GK; P] = [K; Q] K^T in one product; GK = strict_lower(Gam . K K^T),
-  // P = lower(Gam . Q K^T), T = (I + diag(b) GK)^-1
-  float *GK = s.cc(sGK), *Tm = s.cc(sT), *P = s.cc(sP);
+  // [GK; P] = [K; Q] K^T with masks and gate factors applied as stored
+  // (GK = strict_lower(Gam . K K^T), P = lower(Gam . Q K^T)), then
+  // T = (I + diag(b) GK)^-1 from GK's copy in LDS
+  float *GK = s.cc(sGK), *Tm = s.cc(sT);
   static_assert(sQ == sK + 1 && sP == sGK + 1, "K, Q and GK, P adjacent");
-  mm<2 * CM, CM, D, false, true>(GK, CM, K, D, K, D, 1.f, nullptr, lds);
-  gam_mask<true>(GK, v);
-  gam_mask<false>(P, v);
-  tri_inverse(Tm, GK, v.b, lds);
+  gk_p<D>(GK, K, v.g, lds);
+  tri_inverse(Tm, v.b, lds);
   mm<CM, D, CM, false, false>(s.cd(sW), D, Tm, CM, BK, D, 1.f, nullptr, lds);
   mm<CM, D, CM, false, false>(s.cd(sUp), D, Tm, CM, BV, D, 1.f, nullptr, lds);
 }
