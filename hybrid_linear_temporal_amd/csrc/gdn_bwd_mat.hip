@@ -392,31 +392,33 @@ __device__ void rowdot(float* out, const float* X, const float* Y) {
   __syncthreads();
 }
 
-// T = (I + diag(b) L)^-1 for strictly lower L [CM][CM] (in LDS): four lanes
-// per column j (lane q holds t_m for m = q mod 4) solve it by forward
-// substitution, the partial dot products joined by two shuffles.
+// T = (I + diag(b) L)^-1 for strictly lower L [CM][CM] (in LDS), by forward
+// substitution down the rows: one wave, lane j holding column j of T in
+// registers; row i's L entries are read as broadcast 16-byte vectors (the
+// zeros on and above the diagonal included, against t's not-yet-formed zeros)
+// and summed in four chains, the newest t entering last.
 __device__ __attribute__((noinline)) void tri_inverse(float* Tm, const float* b, const float* lds) {
-  const int j = threadIdx.x >> 2, q = threadIdx.x & 3;
-  float t[CM / 4];
+  if (threadIdx.x < 64) {
+    const int j = threadIdx.x;
+    float t[CM];
 #pragma unroll
-  for (int r = 0; r < CM / 4; ++r) t[r] = 0.f;
+    for (int i = 0; i < CM; ++i) t[i] = 0.f;
 #pragma unroll
-  for (int i = 0; i < CM; ++i) {
-    float s0 = 0.f, s1 = 0.f;
+    for (int i = 0; i < CM; ++i) {
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
-    for (int r = 0; r < (i + 3) / 4; ++r) {
-      const float l = 4 * r + q < i ? lds[i * CM + 4 * r + q] : 0.f;
-      if (r & 1) s1 = fmaf(l, t[r], s1);
-      else s0 = fmaf(l, t[r], s0);
+      for (int r = 0; r < (i + 3) / 4; ++r) {
+        const float4 l = f4(lds + i * CM)[r];
+        s0 = fmaf(l.x, t[4 * r], s0);
+        s1 = fmaf(l.y, t[4 * r + 1], s1);
+        s2 = fmaf(l.z, t[4 * r + 2], s2);
+        s3 = fmaf(l.w, t[4 * r + 3], s3);
+      }
+      t[i] = (i == j ? 1.f : 0.f) - b[i] * ((s0 + s1) + (s2 + s3));
     }
-    float s = s0 + s1;
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    const float ti = (i == j ? 1.f : 0.f) - b[i] * s;
-    if ((i & 3) == q) t[i >> 2] = ti;
-  }
 #pragma unroll
-  for (int r = 0; r < CM / 4; ++r) Tm[size_t(4 * r + q) * CM + j] = t[r];
+    for (int i = 0; i < CM; ++i) Tm[size_t(i) * CM + j] = t[i];
+  }
   __syncthreads();
 }
 
