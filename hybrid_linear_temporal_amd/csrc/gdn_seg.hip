@@ -396,21 +396,19 @@ __device__ __forceinline__ void dma16r(__amdgpu_buffer_rsrc_t r, unsigned voff, 
 // ---------------------------------------------------------------------------
 // passes 1 and 3
 // ---------------------------------------------------------------------------
-// LDS (about 80 KB, two workgroups per CU), per chunk:
+// LDS (about 80 KB in pass 3, two workgroups per CU), per chunk:
 //   Kt   k rows (raw)
 //   Qt   q rows (raw, pass 3 only)
 //   Vt   v rows (raw), then U' (rows = tokens)
 //   R1   the chunk's record, then -W (rows = tokens)
 //   XA   Aqk (bf16, pass 3 only)
-struct SegSmem {
-  uint4 Kt[TILE];
-  uint4 Vt[TILE];
-  uint4 R1[TILE];
-  uint4 Qt[TILE];
-  uint4 XA[C * QP * 2 / 16];
+// and the per-token scales below. They are separate arrays, not members of
+// one struct, so the compiler can tell a direct load into one of them from
+// reads of the others: the next chunk's tiles are loaded while this chunk's
+// last products still read the other tiles, with no wait for those loads.
+struct __attribute__((aligned(16))) SegVec {
   float sq[C], sk[C], rq[C];
   float gC;
-  unsigned pf_scratch[64];   // target of the L2 prefetch loads (one word per lane; never read)
 };
 
 // State columns per wave: S^T is d_k (128 rows) x 128 columns, wave w owns
@@ -488,7 +486,12 @@ __device__ __forceinline__ void tproduct(const uint4* X, const unsigned char* ti
 template <bool OUT, typename Tout>
 __global__ void __launch_bounds__(NT, 2)
 gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned char* recs) {
-  __shared__ __attribute__((aligned(16))) SegSmem sm;
+  __shared__ __attribute__((aligned(16))) uint4 Kt[TILE];
+  __shared__ __attribute__((aligned(16))) uint4 Vt[TILE];
+  __shared__ __attribute__((aligned(16))) uint4 R1[TILE];
+  __shared__ __attribute__((aligned(16))) uint4 Qt[OUT ? TILE : 1];
+  __shared__ __attribute__((aligned(16))) uint4 XA[OUT ? C * QP * 2 / 16 : 1];
+  __shared__ SegVec sv;
   const int h = blockIdx.y, b = blockIdx.z;
   if (skipped(p.skip, b)) return;
   const int seg = OUT ? int(blockIdx.x) : int(blockIdx.x) >> 1;
@@ -501,7 +504,7 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
   const unsigned tok_bytes = unsigned(HD * sizeof(bf16));
   int c0, c1;
   seg_range(seg, seg_chunks, p.n_chunks, c0, c1);
-  bf16 (*aqk)[QP] = reinterpret_cast<bf16 (*)[QP]>(sm.XA);
+  bf16 (*aqk)[QP] = reinterpret_cast<bf16 (*)[QP]>(XA);
 
   // ---- start state ----
   State S;
@@ -539,20 +542,6 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
                                rsv = make_rsrc(vg + org, span);
   const __amdgpu_buffer_rsrc_t rsr = make_rsrc(recs + size_t(bh) * p.n_chunks * kRecBytes,
                                                size_t(p.n_chunks) * kRecBytes);
-  unsigned voff[5], pfoff[2];
-  {
-    const int lane = int(threadIdx.x) & 63;
-#pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      const int P = 64 * (wave + 4 * i) + lane, row = P / PQ, ch = P - row * PQ;
-      voff[i] = unsigned(row) * tok_bytes + unsigned(ch > 15 ? 15 : ch) * 16u;
-    }
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int line = 64 * r + lane;   // line = token * 2 + half
-      pfoff[r] = unsigned(line >> 1) * tok_bytes + 128u * unsigned(line & 1);
-    }
-  }
   // Each chunk's outputs are stored after the next chunk's loads have been
   // waited for: the wait counts stores too, and a store just issued would
   // hold it up. out_pend holds them meanwhile (rows < pend_n of token pend_t0 ..).
@@ -576,6 +565,43 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
     pend_n = 0;
   };
 
+  // direct loads of chunk ch's rows of one tensor into a tile, and of its
+  // record into R1 (each wave its share of the 16-byte slots)
+  // (the per-lane source offsets are formed at each use from a lane index
+  // the compiler cannot carry across the loop, rather than kept live in
+  // registers beside the state)
+  auto load_rows = [&](__amdgpu_buffer_rsrc_t rs, uint4* tile, int ch) __attribute__((always_inline)) {
+    const unsigned soff = unsigned((long long)ch * C) * tok_bytes;
+    int lane = int(threadIdx.x) & 63;
+    asm volatile("" : "+v"(lane));
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const int j = wave + 4 * i;
+      if (j < PQ) {
+        const int P = 64 * j + lane, row = P / PQ, c16 = P - row * PQ;   // tile slot P: row, 16-byte column
+        dma16r(rs, unsigned(row) * tok_bytes + unsigned(c16 > 15 ? 15 : c16) * 16u, soff, &tile[64 * j]);
+      }
+    }
+  };
+  auto load_record = [&](int ch) __attribute__((always_inline)) {
+    const int lane = int(threadIdx.x) & 63;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = wave + 4 * i;   // 1 KB piece k of the record
+      if (k < (kRecBytes + 1023) / 1024)
+        dma16r(rsr, unsigned(lane) * 16u, unsigned(ch) * kRecBytes + 1024u * k, &R1[64 * k]);
+    }
+  };
+  // The first chunk's tiles; every later chunk's are issued during the chunk
+  // before it, each as soon as that chunk is done with the tile: V and the
+  // record after U, Q after the outputs, K after the state update.
+  if (c0 < c1) {
+    load_rows(rsk, Kt, c0);
+    if (OUT) load_rows(rsq, Qt, c0);
+    if (vterm) load_rows(rsv, Vt, c0);
+    load_record(c0);
+  }
+  int pf = 0;   // value of the L2 prefetch load (never used)
   for (int chunk = c0; chunk < c1; ++chunk) {
     // The thread index passes through an empty asm each chunk, so per-lane
     // addresses are recomputed here instead of being hoisted out of the loop
@@ -586,52 +612,22 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
     const long long t0 = (long long)chunk * C;
     const int n = int(p.L - t0 < C ? p.L - t0 : C);
 
-    lds_barrier();   // the previous chunk's chain is done with every region
-    // ---- loads: K, Q, V tiles and the chunk's record (into R1) by direct loads ----
-    {
-      const unsigned soff = unsigned(t0) * tok_bytes;
-#pragma unroll
-      for (int i = 0; i < 5; ++i) {
-        const int j = wave + 4 * i;
-        if (j < PQ) {
-          dma16r(rsk, voff[i], soff, &sm.Kt[64 * j]);
-          if (OUT) dma16r(rsq, voff[i], soff, &sm.Qt[64 * j]);
-          if (vterm) dma16r(rsv, voff[i], soff, &sm.Vt[64 * j]);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int k = wave + 4 * i;   // 1 KB piece k of the record
-        if (k < (kRecBytes + 1023) / 1024)
-          dma16r(rsr, unsigned(lane) * 16u, unsigned(chunk) * kRecBytes + 1024u * k, &sm.R1[64 * k]);
-      }
-    }
-    wait_vmem();
+    wait_vmem();   // this chunk's tiles (and the previous chunk's stores and prefetch)
+    // the prefetch value is consumed here, where the wait above has covered
+    // it, so the compiler adds no wait of its own for it
+    asm volatile("" ::"v"(pf));
     if (OUT) store_pending(l16, g);
-    // L2 prefetch of the next chunk's rows and record (one 4-byte direct load
-    // per 128-byte line), waited for only by the next chunk's loads
-    if (chunk + 1 < c1) {
-      const unsigned soff = unsigned(t0 + C) * tok_bytes;
-      const int ntens = 1 + int(OUT) + int(vterm);   // k, then q (pass 3), then v
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int idx = wave + 4 * r;
-        if (idx < 2 * ntens) {
-          const int tensor = idx >> 1;
-          const __amdgpu_buffer_rsrc_t rs = tensor == 0 ? rsk : (tensor == 1 && OUT ? rsq : rsv);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(sm.pf_scratch), 4,
-                                                   pfoff[idx & 1], soff, 0, 0);
-        }
-        if (wave == 3 && 64 * r + lane < kRecBytes / 128)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsr, (__attribute__((address_space(3))) void*)(sm.pf_scratch), 4,
-                                                   128u * unsigned(64 * r + lane), unsigned(chunk + 1) * kRecBytes,
-                                                   0, 0);
-      }
-    }
-    lds_barrier();
+    // L2 prefetch of the next chunk's k rows (one 4-byte load per 128-byte
+    // line into a register): their tile is loaded last, after this chunk's
+    // state update
+    if (chunk + 1 < c1 && wave < 2)
+      pf = __builtin_amdgcn_raw_buffer_load_b32(   // line 64 wave + lane = token * 2 + half
+          rsk, unsigned(32 * wave + (lane >> 1)) * tok_bytes + 128u * unsigned(lane & 1), unsigned(t0 + C) * tok_bytes,
+          0);
+    lds_barrier();   // every wave's share of the tiles is in
     // ---- per-token scales from the record (and, pass 3, the query norms: 4 threads per row) ----
-    const float* rec_g = reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(sm.R1) + kRecG);
-    const float* rec_rk = reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(sm.R1) + kRecRk);
+    const float* rec_g = reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(R1) + kRecG);
+    const float* rec_rk = reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(R1) + kRecRk);
     {
       const int row = tid >> 2, part = tid & 3;
       float rq = 1.f;
@@ -639,7 +635,7 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
         float s2q = 0.f;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const bf16x8 qv = ld8(sm.Qt, row, 32 * part + 8 * c);
+          const bf16x8 qv = ld8(Qt, row, 32 * part + 8 * c);
 #pragma unroll
           for (int e = 0; e < 8; ++e) s2q += static_cast<float>(qv[e]) * static_cast<float>(qv[e]);
         }
@@ -650,11 +646,11 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
       if (part == 0) {
         const float gi = rec_g[row], gl = rec_g[C - 1];
         if (OUT) {
-          sm.rq[row] = rq;
-          sm.sq[row] = row < n ? __expf(gi) * rq : 0.f;             // rows of Q S^T
+          sv.rq[row] = rq;
+          sv.sq[row] = row < n ? __expf(gi) * rq : 0.f;             // rows of Q S^T
         }
-        sm.sk[row] = row < n ? __expf(gl - gi) * rec_rk[row] : 0.f;  // rows of U in the update
-        if (row == 0) sm.gC = __expf(gl);
+        sv.sk[row] = row < n ? __expf(gl - gi) * rec_rk[row] : 0.f;  // rows of U in the update
+        if (row == 0) sv.gC = __expf(gl);
       }
     }
     lds_barrier();
@@ -662,13 +658,13 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
     if (OUT) {
       bf16x8 aq[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) aq[ks] = ld8(sm.Qt, 16 * wave + l16, 32 * ks + 8 * g);
+      for (int ks = 0; ks < 4; ++ks) aq[ks] = ld8(Qt, 16 * wave + l16, 32 * ks + 8 * g);
       float gi[4], rqi[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 16 * wave + 4 * g + e;
         gi[e] = rec_g[i];
-        rqi[e] = sm.rq[i];
+        rqi[e] = sv.rq[i];
       }
       // all four column blocks (the ones above the diagonal are masked to 0):
       // four independent product chains instead of up to four in sequence
@@ -678,7 +674,7 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) qkb[jb] = mfma16(aq[ks], ld8(sm.Kt, 16 * jb + l16, 32 * ks + 8 * g), qkb[jb]);
+        for (int jb = 0; jb < 4; ++jb) qkb[jb] = mfma16(aq[ks], ld8(Kt, 16 * jb + l16, 32 * ks + 8 * g), qkb[jb]);
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb) {
         const f32x4 qk = qkb[jb];
@@ -694,9 +690,9 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
     // ---- -W^T = -K^T T'^T and U'^T = V^T T''^T (wave w: channel blocks 2w, 2w+1) ----
     bf16x4 wkeep[2][4], ukeep[2][4];
     {
-      const unsigned char* rec = reinterpret_cast<const unsigned char*>(sm.R1);
-      tproduct(sm.Kt, rec + kRecTp, true, wave, lane, g, l16, wkeep);
-      if (vterm) tproduct(sm.Vt, rec + kRecTpp, false, wave, lane, g, l16, ukeep);
+      const unsigned char* rec = reinterpret_cast<const unsigned char*>(R1);
+      tproduct(Kt, rec + kRecTp, true, wave, lane, g, l16, wkeep);
+      if (vterm) tproduct(Vt, rec + kRecTpp, false, wave, lane, g, l16, ukeep);
     }
     lds_barrier();   // V is read: -W goes to R1, U' over V
 #pragma unroll
@@ -705,8 +701,8 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
       for (int ib = 0; ib < 4; ++ib) {
         // C layout: column = token 16ib + l16, rows = channels 16(2w + mi) + 4g + e
         const int tok = 16 * ib + l16, ch = 16 * (2 * wave + mi) + 4 * g;
-        st4(sm.R1, tok, ch, wkeep[mi][ib]);
-        if (vterm) st4(sm.Vt, tok, ch, ukeep[mi][ib]);
+        st4(R1, tok, ch, wkeep[mi][ib]);
+        if (vterm) st4(Vt, tok, ch, ukeep[mi][ib]);
       }
     lds_barrier();
 
@@ -719,7 +715,7 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         if (vterm) {
-          const bf16x4 up = ld4_tr(sm.Vt, 16 * tb + 4 * g + (l16 >> 2), col0 + 16 * nb + 4 * (l16 & 3));
+          const bf16x4 up = ld4_tr(Vt, 16 * tb + 4 * g + (l16 >> 2), col0 + 16 * nb + 4 * (l16 & 3));
           u[tb][nb] = f32x4{static_cast<float>(up[0]), static_cast<float>(up[1]), static_cast<float>(up[2]),
                             static_cast<float>(up[3])};
         } else {
@@ -731,11 +727,16 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
       bf16x8 aw[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        aw[ks] = join(ld4(sm.R1, 16 * tb + l16, 32 * ks + 4 * g), ld4(sm.R1, 16 * tb + l16, 32 * ks + 16 + 4 * g));
+        aw[ks] = join(ld4(R1, 16 * tb + l16, 32 * ks + 4 * g), ld4(R1, 16 * tb + l16, 32 * ks + 16 + 4 * g));
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) u[tb][nb] = mfma16(aw[ks], sb[nb][ks], u[tb][nb]);
+    }
+    lds_barrier();   // every wave has read U' (over V) and -W (in R1)
+    if (chunk + 1 < c1) {
+      if (vterm) load_rows(rsv, Vt, chunk + 1);
+      load_record(chunk + 1);
     }
     if (OUT) {
       // O^T = S Q^T diag(sq) + U^T Aqk^T: lane holds channels col0 + 16nb + 4g + e of token 16tb + l16
@@ -750,12 +751,12 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
         bf16x8 aq[4], aa[2];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          aq[ks] = join(ld4(sm.Qt, row, 32 * ks + 4 * g), ld4(sm.Qt, row, 32 * ks + 16 + 4 * g));
+          aq[ks] = join(ld4(Qt, row, 32 * ks + 4 * g), ld4(Qt, row, 32 * ks + 16 + 4 * g));
 #pragma unroll
         for (int js = 0; js < 2; ++js)
           aa[js] = join(*reinterpret_cast<const bf16x4*>(&aqk[row][32 * js + 4 * g]),
                         *reinterpret_cast<const bf16x4*>(&aqk[row][32 * js + 16 + 4 * g]));
-        const float sqv = sm.sq[row];
+        const float sqv = sv.sq[row];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
           f32x4 x = {0.f, 0.f, 0.f, 0.f};
@@ -776,26 +777,30 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
         }
       }
     }
+    if (OUT) {
+      lds_barrier();   // every wave has read Q and Aqk
+      if (chunk + 1 < c1) load_rows(rsq, Qt, chunk + 1);
+    }
     // S^T <- gamma_C S^T + K^T diag(sk) U
     {
       bf16x8 usb[2][2];
 #pragma unroll
       for (int js = 0; js < 2; ++js) {
-        const f32x4 s0 = *reinterpret_cast<const f32x4*>(&sm.sk[32 * js + 4 * g]);
-        const f32x4 s1 = *reinterpret_cast<const f32x4*>(&sm.sk[32 * js + 16 + 4 * g]);
+        const f32x4 s0 = *reinterpret_cast<const f32x4*>(&sv.sk[32 * js + 4 * g]);
+        const f32x4 s1 = *reinterpret_cast<const f32x4*>(&sv.sk[32 * js + 16 + 4 * g]);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
           usb[nb][js] = join(to_bf16x4(u[2 * js][nb] * s0), to_bf16x4(u[2 * js + 1][nb] * s1));
       }
-      const float gc = sm.gC;
+      const float gc = sv.gC;
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
         bf16x8 ak[2];
 #pragma unroll
         for (int js = 0; js < 2; ++js) {
           const int col = 16 * mb + 4 * (l16 & 3);
-          ak[js] = join(ld4_tr(sm.Kt, 32 * js + 4 * g + (l16 >> 2), col),
-                        ld4_tr(sm.Kt, 32 * js + 16 + 4 * g + (l16 >> 2), col));
+          ak[js] = join(ld4_tr(Kt, 32 * js + 4 * g + (l16 >> 2), col),
+                        ld4_tr(Kt, 32 * js + 16 + 4 * g + (l16 >> 2), col));
         }
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
@@ -806,6 +811,8 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
         }
       }
     }
+    lds_barrier();   // every wave has read K
+    if (chunk + 1 < c1) load_rows(rsk, Kt, chunk + 1);
   }
 
   if (OUT) {
