@@ -31,10 +31,12 @@
 //
 // Two kernels replace a token-by-token walk: gdn_bwd_mat_prep (per chunk: M,
 // N, X for the chains over chunks) and gdn_bwd_mat_grad (per chunk, after
-// the chains: the token gradients). Each is a persistent grid, one workgroup
-// per scratch slot of the workspace; the chunk's matrices live in that slot
-// (global memory, resident in the caches) and every product goes through LDS
-// to the matrix cores.
+// the chains: the token gradients). Each is a persistent grid walking the
+// chunks; every chunk has a slot of the workspace (global memory) for its
+// matrices: the prep kernel forms the chunk's forward ones there (normalised
+// K and Q, V, dO, the gated copies, W, U', GK, P, T and the inverse norms),
+// the gradient kernel reads them back and adds its own. Every product goes
+// through LDS to the matrix cores.
 #include "hlta_device.h"
 #include "hlta_internal.h"
 #include "hlta_launch.h"
@@ -422,11 +424,11 @@ __device__ __attribute__((noinline)) void tri_inverse(float* Tm, const float* b,
   __syncthreads();
 }
 
-// Per-workgroup scratch (floats, in its slot of the workspace)
+// A chunk's matrices (floats, in its slot of the workspace)
 template <int D>
 struct Slot {
   static constexpr size_t CD = size_t(CM) * D, CC = size_t(CM) * CM;
-  static_assert(16 * CD + 7 * CC <= bwd_slot_floats(D), "the slot holds the chunk's matrices");
+  static_assert(16 * CD + 7 * CC <= bwd_slot_floats(D) && 2 * CM <= CD, "the slot holds the chunk's matrices");
   static_assert(kLdsFloats >= CC, "the inverse's LDS fits the product staging");
   float* base;
   __device__ float* cd(int i) const { return base + i * CD; }            // [CM][D] matrices 0 ..
@@ -435,7 +437,8 @@ struct Slot {
 // [CM][D] slots
 // (K, Q adjacent: one product forms K K^T and Q K^T; dO, dU adjacent and X1, X2
 // adjacent: one product forms dO S and dU S)
-enum { sK = 0, sQ, sV, sDO, sDU, sBK, sDK, sW, sUp, sU, sX1, sX2, sX3, sDKG, sBV };
+// (sRN: the inverse norms of k and q, 2 x CM floats)
+enum { sK = 0, sQ, sV, sDO, sDU, sBK, sDK, sW, sUp, sU, sX1, sX2, sX3, sDKG, sBV, sRN };
 // [CM][CM] slots
 enum { sGK = 0, sP, sT, sDP, sDPG, sE1, sE2 };   // GK, P adjacent
 
@@ -448,9 +451,35 @@ struct ChunkVec {
   float gC;
 };
 
-// Loads chunk c of head (b, h): K, Q (normalised), V, dO = w2 d_mix, gates,
+// The chunk's gate vectors (wave 0): prefix sums g of log a, gamma, a, b,
+// De = gamma_C / gamma and gamma_C; rows t >= n get a = 1, b = 0.
+__device__ void chunk_gates(const GdnParams& p, int C, int c, int b, int h, ChunkVec& v) {
+  if (threadIdx.x >= 64) return;
+  const long long t0 = (long long)c * C;
+  const int n = int(p.L - t0 < C ? p.L - t0 : C);
+  const size_t g0 = (size_t(b) * p.L + t0) * p.H + h;
+  const int t = threadIdx.x;
+  const float at = t < n ? p.a[g0 + size_t(t) * p.H] : 1.f;
+  const float bt = t < n ? p.b[g0 + size_t(t) * p.H] : 0.f;
+  float la = at > 0.f ? fmaxf(logf(at), kLogFloor) : kLogFloor;
+  if (t >= n) la = 0.f;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(la, off);
+    if (t >= off) la += y;
+  }
+  const float gl = __shfl(la, CM - 1);
+  v.g[t] = la;
+  v.gam[t] = expf(la);
+  v.a[t] = at;
+  v.b[t] = bt;
+  v.De[t] = expf(gl - la);
+  if (t == 0) v.gC = expf(gl);
+}
+
+// Loads chunk c of head (b, h) into its slot: K, Q (normalised), V, dO = w2 d_mix, gates,
 // then forms diag(b gamma) K, De K, diag(b) V, strict_lower(Gam . K K^T), T,
-// W, U' and P. Rows t >= n are zero (gates a = 1, b = 0).
+// W, U', P and the inverse norms. Rows t >= n are zero (gates a = 1, b = 0).
 template <typename Tin, typename Tg, int D>
 __device__ void chunk_forward(const GdnParams& p, int C, const Tg* d_mix, float w2, int c, int b, int h,
                               const Slot<D>& s, ChunkVec& v, float* lds) {
@@ -458,33 +487,12 @@ __device__ void chunk_forward(const GdnParams& p, int C, const Tg* d_mix, float 
   const long long t0 = (long long)c * C;
   const int n = int(p.L - t0 < C ? p.L - t0 : C);
   const size_t tok0 = (size_t(b) * p.L + t0) * HD + size_t(h) * D;
-  const size_t g0 = (size_t(b) * p.L + t0) * p.H + h;
   const Tin* q = static_cast<const Tin*>(p.q);
   const Tin* k = static_cast<const Tin*>(p.k);
   const Tin* vv = static_cast<const Tin*>(p.v);
   float *K = s.cd(sK), *Q = s.cd(sQ), *V = s.cd(sV), *dO = s.cd(sDO);
   float *BK = s.cd(sBK), *DK = s.cd(sDK), *BV = s.cd(sBV);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  // gates first: prefix sums g of log a, gamma, b, De = gamma_C / gamma
-  if (wave == 0) {
-    const int t = lane;
-    const float at = t < n ? p.a[g0 + size_t(t) * p.H] : 1.f;
-    const float bt = t < n ? p.b[g0 + size_t(t) * p.H] : 0.f;
-    float la = at > 0.f ? fmaxf(logf(at), kLogFloor) : kLogFloor;
-    if (t >= n) la = 0.f;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_up(la, off);
-      if (lane >= off) la += y;
-    }
-    const float gl = __shfl(la, CM - 1);
-    v.g[t] = la;
-    v.gam[t] = expf(la);
-    v.a[t] = at;
-    v.b[t] = bt;
-    v.De[t] = expf(gl - la);
-    if (t == 0) v.gC = expf(gl);
-  }
+  chunk_gates(p, C, c, b, h, v);
   __syncthreads();
   // the inputs in one pass: K^, Q^ (each row's squared norm joined over the
   // D/4 consecutive lanes that hold the row), V, dO = w2 d_mix, and from them
@@ -527,6 +535,11 @@ __device__ void chunk_forward(const GdnParams& p, int C, const Tg* d_mix, float 
         f4(BV)[e] = v.b[t] * x.c;
       });
   __syncthreads();
+  if (threadIdx.x < CM) {   // kept with the chunk's matrices for the gradient kernel
+    float* rn = s.cd(sRN);
+    rn[threadIdx.x] = v.rk[threadIdx.x];
+    rn[CM + threadIdx.x] = v.rq[threadIdx.x];
+  }
   // [GK; P] = [K; Q] K^T with masks and gate factors applied as stored
   // (GK = strict_lower(Gam . K K^T), P = lower(Gam . Q K^T)), then
   // T = (I + diag(b) GK)^-1 from GK's copy in LDS
@@ -545,14 +558,13 @@ gdn_bwd_mat_prep(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float*
                  float* Am, float* Um, float* Xm) {
   __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];   // product staging or the inverse
   __shared__ ChunkVec v;
-  float* const slot = slots + size_t(blockIdx.x) * slot_floats;
   const long long jobs = (long long)p.B * p.H * p.n_chunks;
   const size_t mat = size_t(D) * D;
   for (long long job = blockIdx.x; job < jobs; job += gridDim.x) {
     const int c = int(job % p.n_chunks), bh = int(job / p.n_chunks), b = bh / p.H, h = bh % p.H;
-    // the slot's address is opaque to the compiler inside the loop, so it does
-    // not hoist every per-thread address of the chunk's arrays out of it
-    float* sb = slot;
+    // the chunk's slot, its address opaque to the compiler, so it does not
+    // hoist every per-thread address of the chunk's arrays out of the loop
+    float* sb = slots + size_t(job) * slot_floats;
     asm volatile("" : "+s"(sb));
     const Slot<D> s{sb};
     chunk_forward<Tin, Tg, D>(p, C, d_mix, mix_w[3 * h + 2], c, b, h, s, v, lds);
@@ -578,7 +590,6 @@ gdn_bwd_mat_grad(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float*
                  const float* Sst, const float* Rin, float* dq, float* dk, float* dv, float* da, float* db) {
   __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];
   __shared__ ChunkVec v;
-  float* const slot = slots + size_t(blockIdx.x) * slot_floats;
   const long long jobs = (long long)p.B * p.H * p.n_chunks;
   const size_t mat = size_t(D) * D;
   const size_t HD = size_t(p.H) * D;
@@ -589,10 +600,18 @@ gdn_bwd_mat_grad(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float*
     const int n = int(p.L - t0 < C ? p.L - t0 : C);
     const size_t tok0 = (size_t(b) * p.L + t0) * HD + size_t(h) * D;
     const size_t g0 = (size_t(b) * p.L + t0) * p.H + h;
-    float* sb = slot;   // opaque inside the loop (see gdn_bwd_mat_prep)
+    float* sb = slots + size_t(job) * slot_floats;   // opaque (see gdn_bwd_mat_prep)
     asm volatile("" : "+s"(sb));
     const Slot<D> s{sb};
-    chunk_forward<Tin, Tg, D>(p, C, d_mix, mix_w[3 * h + 2], c, b, h, s, v, lds);
+    // the chunk's forward matrices are in its slot (formed by the prep
+    // kernel); only the gate vectors and inverse norms come to LDS again
+    chunk_gates(p, C, c, b, h, v);
+    if (threadIdx.x < CM) {
+      const float* rn = s.cd(sRN);
+      v.rk[threadIdx.x] = rn[threadIdx.x];
+      v.rq[threadIdx.x] = rn[CM + threadIdx.x];
+    }
+    __syncthreads();
     const float* S = Sst + size_t(job) * mat;
     const float* G = Rin + size_t(job) * mat;
     float *K = s.cd(sK), *Q = s.cd(sQ), *V = s.cd(sV), *dO = s.cd(sDO), *DK = s.cd(sDK), *BK = s.cd(sBK);
@@ -1002,7 +1021,7 @@ gdn_bwd_chain_mfma(int n_chunks, const float* S0, const float* Am, const float* 
 template <typename Tin, typename Tg, int D>
 hipError_t launch_t(const BwdArgs& x, int phase, hipStream_t st) {
   const Tg* g = static_cast<const Tg*>(x.d_mix);
-  const dim3 grid(unsigned(x.n_slots));
+  const dim3 grid(unsigned(x.n_slots < kBwdWorkgroups ? x.n_slots : kBwdWorkgroups));
   if (phase == 0)
     hipLaunchKernelGGL((gdn_bwd_mat_prep<Tin, Tg, D>), grid, dim3(kNT), 0, st, x.gdn, x.C, g, x.mix_w, x.slots,
                        x.slot_floats, x.Am, x.Um, x.Xm);

@@ -190,7 +190,8 @@ hlta_status make_bwd_plan(const hlta_config* cfg, BwdPlan* plan) {
   const int64_t L = int64_t(cfg->T) * cfg->P, C = cfg->gdn_chunk, nch = (L + C - 1) / C;
   const int64_t dd = int64_t(cfg->d) * cfg->d, bh = int64_t(cfg->B) * cfg->H;
   BwdPlan p;
-  p.n_slots = int(std::min<int64_t>(std::max<int64_t>(bh * nch, 1), kBwdSlots));
+  if (bh * nch > std::numeric_limits<int>::max()) return fail(HLTA_E_SHAPE, "more than 2^31 - 1 chunks");
+  p.n_slots = int(std::max<int64_t>(bh * nch, 1));
   int64_t stats = 0, mats = 0, mats5 = 0, slots = 0, part = 0, off = 0, total = 0;
   if (!prod_ok({bh, L, 2, 4}, &stats) || !align256_ok(stats, &stats) ||
       !prod_ok({bh, nch, dd, 4}, &mats) || !align256_ok(mats, &mats) || !mul_ok(mats, 5, &mats5) ||

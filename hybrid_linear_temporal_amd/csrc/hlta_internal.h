@@ -42,10 +42,11 @@ hlta_status make_plan(const hlta_config* cfg, int64_t L, Plan* plan);
 // aligned: per-row softmax statistics of both branches (two arrays); five
 // d x d matrices per chunk of C = gdn_chunk tokens (transition, own state,
 // own adjoint, start state, adjoint at the end); one
-// scratch slot per workgroup of the memory's per-chunk kernels (the chunk's
-// 64-row matrices, bwd_slot_floats(d) floats); partial sums of the
+// slot per chunk for the memory's per-chunk kernels (the chunk's 64-row
+// matrices, bwd_slot_floats(d) floats: those of the chunk's forward are formed
+// once, by the first kernel, and read again by the last); partial sums of the
 // mix-weight gradient.
-constexpr int kBwdSlots = 512;
+constexpr int kBwdWorkgroups = 512;   // persistent grid of the memory's per-chunk kernels
 // sixteen 64 x d and eight 64 x 64 fp32 matrices
 constexpr size_t bwd_slot_floats(int d) { return 16 * size_t(64) * size_t(d) + 8 * size_t(64) * 64; }
 constexpr int kDwSlices = 128;
@@ -54,7 +55,7 @@ struct BwdPlan {
   size_t mat_off = 0, mat_bytes = 0;   // each of the five: [B*H*n_chunks, d, d]
   size_t slot_off = 0;
   int n_slots = 0;
-  size_t slot_floats = 0;   // floats of one slot (scratch of one workgroup of the memory's backward)
+  size_t slot_floats = 0;   // floats of one slot (one chunk's matrices in the memory's backward)
   size_t part_off = 0;
   size_t total = 0;
 };

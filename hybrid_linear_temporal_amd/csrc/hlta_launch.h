@@ -97,7 +97,7 @@ struct BwdArgs {
   float* Xm;         //   ... the chunk's own adjoint from zero
   float* Sst;        //   ... state at the chunk's start
   float* Rin;        //   ... adjoint reaching the chunk's end
-  float* slots;      // [n_slots, slot_floats] workspace: per-workgroup scratch of the memory's backward
+  float* slots;      // [n_slots, slot_floats] workspace: one slot per chunk of the memory's backward
   int n_slots;
   size_t slot_floats;
   float* dw_part;    // [H, dw_slices, 3] workspace

@@ -275,6 +275,9 @@ hlta_status hlta_attn_fwd_fp8(const hlta_config* cfg, const void* q8, const void
  * dmix_w     [H, 3] float32 (written)
  * dS0        [B, H, d, d] float32 gradient of the start state, or NULL
  * workspace  device buffer of at least hlta_bwd_workspace_bytes(cfg) bytes
+ *            (per chunk of gdn_chunk tokens of each batch row and head: five
+ *            d x d fp32 matrices and the chunk's own 64-row matrices, about
+ *            0.94 MB at d = 128; plus the softmax statistics)
  * The gates are taken as given (gate_logits = 1 and the rotary embedding give
  * HLTA_E_UNSUPPORTED). The memory's gradients are evaluated with fp32
  * accumulation, their matrix products on bf16 MFMA with each fp32 factor split

@@ -14,6 +14,7 @@
 //
 // Prints "host checks passed: <n> configs" and exits 0, or prints the first
 // failure and exits 1.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -120,7 +121,7 @@ static bool check_plan(const hlta_config& c, int64_t L, const Plan& p) {
 static bool check_bwd_plan(const hlta_config& c, const BwdPlan& p) {
   const std::string cs = describe(c);
   const int64_t L = int64_t(c.T) * c.P, nch = (L + c.gdn_chunk - 1) / c.gdn_chunk;
-  CHECK(p.n_slots >= 1 && p.n_slots <= kBwdSlots, "%s", cs.c_str());
+  CHECK(p.n_slots == std::max<int64_t>(int64_t(c.B) * c.H * nch, 1), "%s", cs.c_str());
   CHECK(p.stats_bytes % 256 == 0 && p.mat_bytes % 256 == 0, "%s", cs.c_str());
   CHECK(p.stats_bytes >= size_t(c.B) * c.H * size_t(L) * 8, "%s", cs.c_str());
   CHECK(p.mat_bytes >= size_t(c.B) * c.H * size_t(nch) * c.d * c.d * 4, "%s", cs.c_str());

@@ -193,10 +193,9 @@ def test_rope_config_checks(lib):
 
 def test_bwd_workspace_and_argument_errors(lib):
     """Backward: workspace = two [2, B, L, H] fp32 statistics, five d x d
-    matrices per chunk, one scratch slot per workgroup of the memory's
-    per-chunk kernels (at most 512; sixteen 64 x d and eight 64 x 64 fp32
-    matrices each) and the mix-weight partial sums; argument errors fail
-    before any launch."""
+    matrices per chunk, one slot per chunk for the memory's per-chunk
+    kernels (sixteen 64 x d and eight 64 x 64 fp32 matrices each) and the
+    mix-weight partial sums; argument errors fail before any launch."""
     cfg = _cfg()
     L = cfg.T * cfg.P
     chunks = -(-L // cfg.gdn_chunk)
@@ -205,7 +204,7 @@ def test_bwd_workspace_and_argument_errors(lib):
         return -(-x // 256) * 256
 
     bh, dd = cfg.B * cfg.H, cfg.d * cfg.d * 4
-    slots = min(bh * chunks, 512)
+    slots = bh * chunks
     slot = (16 * 64 * cfg.d + 8 * 64 * 64) * 4
     want = 2 * up(bh * L * 2 * 4) + 5 * up(bh * chunks * dd) + up(slots * slot) + up(cfg.H * 128 * 3 * 4)
     ws = H.hlta_bwd_workspace_bytes(cfg)
