@@ -486,7 +486,8 @@ __device__ __forceinline__ void tproduct(const uint4* X, const unsigned char* ti
 template <bool OUT, typename Tout>
 __global__ void __launch_bounds__(NT, 2)
 gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned char* recs) {
-  __shared__ __attribute__((aligned(16))) uint4 Kt[TILE];
+  __shared__ __attribute__((aligned(16))) uint4 K0[TILE];
+  __shared__ __attribute__((aligned(16))) uint4 K1[OUT ? 1 : TILE];   // pass 1: K double-buffered
   __shared__ __attribute__((aligned(16))) uint4 Vt[TILE];
   __shared__ __attribute__((aligned(16))) uint4 R1[TILE];
   __shared__ __attribute__((aligned(16))) uint4 Qt[OUT ? TILE : 1];
@@ -594,15 +595,20 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
   };
   // The first chunk's tiles; every later chunk's are issued during the chunk
   // before it, each as soon as that chunk is done with the tile: V and the
-  // record after U, Q after the outputs, K after the state update.
+  // record after U, Q after the outputs, K after the state update (pass 3;
+  // pass 1 has LDS to spare for a second K tile, so there the next chunk's K
+  // is issued before this one's chain).
   if (c0 < c1) {
-    load_rows(rsk, Kt, c0);
+    load_rows(rsk, K0, c0);
     if (OUT) load_rows(rsq, Qt, c0);
     if (vterm) load_rows(rsv, Vt, c0);
     load_record(c0);
   }
   int pf = 0;   // value of the L2 prefetch load (never used)
-  for (int chunk = c0; chunk < c1; ++chunk) {
+  // One chunk with its K in Kt (pass 1: the next chunk's K goes to Kn). The
+  // loop below is unrolled by two for pass 1 so that each step names its
+  // buffers directly (the compiler tracks the loads into each by name).
+  auto chunk_step = [&](int chunk, uint4* Kt, uint4* Kn) __attribute__((always_inline)) {
     // The thread index passes through an empty asm each chunk, so per-lane
     // addresses are recomputed here instead of being hoisted out of the loop
     // (dozens of them would stay live across it, beside the state).
@@ -620,7 +626,7 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
     // L2 prefetch of the next chunk's k rows (one 4-byte load per 128-byte
     // line into a register): their tile is loaded last, after this chunk's
     // state update
-    if (chunk + 1 < c1 && wave < 2)
+    if (OUT && chunk + 1 < c1 && wave < 2)
       pf = __builtin_amdgcn_raw_buffer_load_b32(   // line 64 wave + lane = token * 2 + half
           rsk, unsigned(32 * wave + (lane >> 1)) * tok_bytes + 128u * unsigned(lane & 1), unsigned(t0 + C) * tok_bytes,
           0);
@@ -705,6 +711,10 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
         if (vterm) st4(Vt, tok, ch, ukeep[mi][ib]);
       }
     lds_barrier();
+    // pass 1: the next chunk's K into the other buffer (it held the previous
+    // chunk's K; issued after this chunk's LDS stores, which the compiler
+    // would otherwise hold behind it)
+    if (!OUT && chunk + 1 < c1) load_rows(rsk, Kn, chunk + 1);
 
     // ---- chain: U = U' - W S^T, outputs, state update (wave w: state columns 32w ..) ----
     bf16x8 sb[2][4];
@@ -811,8 +821,18 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
         }
       }
     }
-    lds_barrier();   // every wave has read K
-    if (chunk + 1 < c1) load_rows(rsk, Kt, chunk + 1);
+    if (OUT) {
+      lds_barrier();   // every wave has read K
+      if (chunk + 1 < c1) load_rows(rsk, Kt, chunk + 1);
+    }
+  };
+  if constexpr (OUT) {
+    for (int chunk = c0; chunk < c1; ++chunk) chunk_step(chunk, K0, K0);
+  } else {
+    for (int chunk = c0; chunk < c1; chunk += 2) {
+      chunk_step(chunk, K0, K1);
+      if (chunk + 1 < c1) chunk_step(chunk + 1, K1, K0);
+    }
   }
 
   if (OUT) {
