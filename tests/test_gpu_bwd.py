@@ -33,6 +33,11 @@ CASES = [
                                 dswa_taps=3, gdn_chunk=64, dtype="bf16", seed=2104), "bf16", AUTO),
     ("bf16_in_f32_out", small("bwd_bf16f", B=1, H=1, T=6, P=24, d=128, swa_frames=2, dswa_dilation=3,
                               dswa_taps=2, gdn_chunk=16, dtype="bf16", seed=2103), "f32", AUTO),
+    # 16 heads x 35 chunks (the last one ragged): more chunk jobs than the
+    # memory's persistent grid of 512 workgroups, so some walk a second chunk
+    # and its slot; the forward runs 7 segments of 5 chunks
+    ("bf16_mfma_560_chunks", small("bwd_bf16w", B=1, H=16, T=10, P=220, d=128, swa_frames=3, dswa_dilation=2,
+                                   dswa_taps=3, gdn_chunk=64, dtype="bf16", seed=2105), "bf16", AUTO),
 ]
 
 
