@@ -843,6 +843,11 @@ gdn_bwd_mat_grad(GdnParams p, int C, const Tg* d_mix, const float* mix_w, float*
 // two steps ahead of their use.
 template <int D>
 constexpr int chain_threads() { return D == 128 ? 512 : 256; }   // two waves per SIMD at d = 128
+// state rows per workgroup: 32 at d = 128 (four row blocks per head and
+// direction; a step's matrix loads and record stores, not its products, set
+// its time, so spreading the rows over more compute units shortens it)
+template <int D>
+constexpr int chain_rw() { return D == 128 ? 32 : D; }
 // bf16 row pitch of the row-major staging: D + 4 puts consecutive rows two of
 // the 64 four-byte banks apart, so the 32 rows of one 8-byte read are spread
 // over all banks
@@ -853,7 +858,7 @@ __device__ __forceinline__ void chain_body(int n_chunks, const float* S0, const 
                                            const float* Xm, float* Sst, float* Rin, float* dS0, bf16* Mhi,
                                            bf16* Mlo, bf16x8_t* Xhi, bf16x8_t* Xlo) {
   constexpr int NTC = chain_threads<D>(), NW = NTC / 64;
-  constexpr int RW = D < 64 ? D : 64;                  // state rows per workgroup
+  constexpr int RW = chain_rw<D>();                     // state rows per workgroup
   constexpr int TMO = D / 32, TN = RW / 32;            // output tiles: state columns x state rows
   constexpr int NTILE = TMO * TN, TPW = (NTILE + NW - 1) / NW;
   constexpr int PM = D * D / 4 / NTC;                  // float4 of the matrix per thread per step
@@ -1012,7 +1017,7 @@ __global__ void __launch_bounds__(chain_threads<D>())
 gdn_bwd_chain_mfma(int n_chunks, const float* S0, const float* Am, const float* Um, const float* Xm, float* Sst,
                    float* Rin, float* dS0) {
   __shared__ __attribute__((aligned(16))) bf16 Mhi[D * chain_row<D>()], Mlo[D * chain_row<D>()];
-  constexpr int NT2 = (D / 32) * ((D < 64 ? D : 64) / 32) * 2 * 64;
+  constexpr int NT2 = (D / 32) * (chain_rw<D>() / 32) * 2 * 64;
   __shared__ __attribute__((aligned(16))) bf16x8_t Xhi[NT2], Xlo[NT2];
   if (blockIdx.z == 0) chain_body<D, 0>(n_chunks, S0, Am, Um, Xm, Sst, Rin, dS0, Mhi, Mlo, Xhi, Xlo);
   else chain_body<D, 1>(n_chunks, S0, Am, Um, Xm, Sst, Rin, dS0, Mhi, Mlo, Xhi, Xlo);
@@ -1026,7 +1031,7 @@ hipError_t launch_t(const BwdArgs& x, int phase, hipStream_t st) {
     hipLaunchKernelGGL((gdn_bwd_mat_prep<Tin, Tg, D>), grid, dim3(kNT), 0, st, x.gdn, x.C, g, x.mix_w, x.slots,
                        x.slot_floats, x.Am, x.Um, x.Xm);
   else if (phase == 2)
-    hipLaunchKernelGGL((gdn_bwd_chain_mfma<D>), dim3(unsigned(x.gdn.B * x.gdn.H), unsigned(D / (D < 64 ? D : 64)), 2),
+    hipLaunchKernelGGL((gdn_bwd_chain_mfma<D>), dim3(unsigned(x.gdn.B * x.gdn.H), unsigned(D / chain_rw<D>()), 2),
                        dim3(chain_threads<D>()), 0, st, x.gdn.n_chunks, x.gdn.S0, x.Am, x.Um, x.Xm, x.Sst, x.Rin,
                        x.dS0);
   else
