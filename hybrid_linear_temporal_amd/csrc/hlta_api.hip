@@ -50,9 +50,22 @@ hlta_status check_outputs(const float* a, const float* b, const float* mix_w, vo
   return HLTA_OK;
 }
 
+// The mix's operands when it follows the memory branch (o_swa, o_dswa as
+// already stored by the softmax branches).
+struct MixOut {
+  const void* swa;
+  const void* dswa;
+  void* out;
+  const float* w;
+};
+
+// The memory branch; with mix set, the mix kernel after it. (Forming the mix
+// in the memory's output pass instead was slower: its scattered 8-byte loads
+// and stores of the branch outputs cost that pass more than the mix kernel's
+// 16-byte streams take.)
 hlta_status run_gdn(const hlta_config* cfg, const Plan& plan, const void* q, const void* k, const void* v,
                     const float* a, const float* b, const float* S0, float* S_out, void* o_gdn, void* workspace,
-                    hipStream_t st, unsigned long long skip = 0) {
+                    hipStream_t st, unsigned long long skip = 0, const MixOut* mix = nullptr) {
   GdnParams g{};
   g.skip = skip;
   g.q = q;
@@ -75,6 +88,11 @@ hlta_status run_gdn(const hlta_config* cfg, const Plan& plan, const void* q, con
                      ? launch_gdn_seg(g, plan.gdn_G, plan.gdn_seg_chunks, workspace, cfg->out_dtype, st)
                      : launch_gdn_generic(g, cfg->d, cfg->gdn_chunk, cfg->in_dtype, cfg->out_dtype, st);
   if (e != hipSuccess) return hip_fail(e, "gated delta rule launch");
+  if (mix) {
+    e = launch_mix(mix->swa, mix->dswa, o_gdn, mix->out, mix->w, (long long)cfg->B * plan.L, cfg->H, cfg->d,
+                   cfg->out_dtype, st, skip, plan.L);
+    if (e != hipSuccess) return hip_fail(e, "mix launch");
+  }
   return HLTA_OK;
 }
 
@@ -110,19 +128,19 @@ hlta_status run_rope(const hlta_config* cfg, const Plan& plan, AttnParams& attn,
   return HLTA_OK;
 }
 
-// One layer: the memory branch (GDN over L tokens per row), the softmax
-// branches, then the per-head mix of the three stored outputs, in order on st.
-// Rollouts in attn.ro.skip are left out of all three.
-// (Running the memory branch on a second stream gains nothing here: its state
-// pass needs one compute unit per workgroup for its LDS buffers, so it cannot
+// One layer: the softmax branches, then the memory branch (GDN over L tokens
+// per row) and the per-head mix of the three outputs, in order on st.
+// Rollouts in attn.ro.skip are left out of all of it.
+// (Running the two halves on two streams gains nothing here: the memory's
+// passes need most of a compute unit's LDS per workgroup, so they cannot
 // share the chip with the attention branches.) attn.* query fields set by caller.
 hlta_status run_layer(const hlta_config* cfg, const Plan& plan, const void* q, const void* k, const void* v,
                       const float* a, const float* b, const float* S0, float* S_out, void* o_gdn,
                       const float* mix_w, void* o_mix, void* workspace, AttnParams& attn, hipStream_t st) {
-  HLTA_TRY(run_gdn(cfg, plan, q, k, v, a, b, S0, S_out, o_gdn, workspace, st, attn.ro.skip));
   HLTA_TRY(run_rope(cfg, plan, attn, workspace, st));
   HLTA_TRY(run_attn(cfg, plan, attn, st));
-  return run_mix(cfg, plan, attn.o_swa, attn.o_dswa, o_gdn, o_mix, mix_w, st, attn.ro.skip);
+  const MixOut mix{attn.o_swa, attn.o_dswa, o_mix, mix_w};
+  return run_gdn(cfg, plan, q, k, v, a, b, S0, S_out, o_gdn, workspace, st, attn.ro.skip, &mix);
 }
 
 AttnParams full_attn_params(const hlta_config* cfg, const void* q, const void* k, const void* v, void* o_swa,
@@ -306,6 +324,57 @@ hlta_status hlta_attn_fwd(const hlta_config* cfg, const void* q, const void* k, 
   hipStream_t st = static_cast<hipStream_t>(stream);
   HLTA_TRY(run_attn(cfg, plan, at, st));
   return run_mix(cfg, plan, o_swa, o_dswa, o_gdn, o_mix, mix_w, st);
+}
+
+hlta_status hlta_attn_branches(const hlta_config* cfg, const void* q, const void* k, const void* v, void* o_swa,
+                               void* o_dswa, void* stream) {
+  clear_error();
+  Plan plan;
+  HLTA_TRY(check_config(cfg));
+  HLTA_TRY(make_plan(cfg, int64_t(cfg->T) * cfg->P, &plan));
+  if (plan.L == 0) return HLTA_OK;
+  HLTA_TRY(need(q, "q"));
+  HLTA_TRY(need(k, "k"));
+  HLTA_TRY(need(v, "v"));
+  HLTA_TRY(need(o_swa, "o_swa"));
+  HLTA_TRY(need(o_dswa, "o_dswa"));
+  if (cfg->rope_theta > 0.f)
+    return fail(HLTA_E_UNSUPPORTED, "the rotary embedding needs a workspace: use hlta_fwd");
+  AttnParams at = full_attn_params(cfg, q, k, v, o_swa, o_dswa);
+  return run_attn(cfg, plan, at, static_cast<hipStream_t>(stream));
+}
+
+hlta_status hlta_gdn_mix_fwd(const hlta_config* cfg, const void* q, const void* k, const void* v, const float* a,
+                             const float* b, const float* mix_w, const float* S0, const void* o_swa,
+                             const void* o_dswa, void* o_gdn, void* o_mix, float* S_out, void* workspace,
+                             size_t ws_bytes, void* stream) {
+  clear_error();
+  Plan plan;
+  HLTA_TRY(check_config(cfg));
+  HLTA_TRY(make_plan(cfg, int64_t(cfg->T) * cfg->P, &plan));
+  HLTA_TRY(maybe(S0, "S0"));
+  HLTA_TRY(maybe(S_out, "S_out"));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (plan.L == 0) {
+    if (S_out && S_out != S0) {
+      hipError_t e = launch_copy_or_zero(S_out, S0, state_bytes(cfg), st);
+      if (e != hipSuccess) return hip_fail(e, "state copy");
+    }
+    return HLTA_OK;
+  }
+  HLTA_TRY(need(q, "q"));
+  HLTA_TRY(need(k, "k"));
+  HLTA_TRY(need(v, "v"));
+  HLTA_TRY(need(a, "a"));
+  HLTA_TRY(need(b, "b"));
+  HLTA_TRY(need(mix_w, "mix_w"));
+  HLTA_TRY(need(o_swa, "o_swa"));
+  HLTA_TRY(need(o_dswa, "o_dswa"));
+  HLTA_TRY(need(o_gdn, "o_gdn"));
+  HLTA_TRY(need(o_mix, "o_mix"));
+  HLTA_TRY(check_workspace(plan, workspace, ws_bytes));
+  const MixOut mix{o_swa, o_dswa, o_mix, mix_w};
+  return run_gdn(cfg, plan, q, k, v, a, b, S0, S_out, o_gdn, workspace, st, 0, &mix);
 }
 
 hlta_status hlta_attn_fwd_lse(const hlta_config* cfg, const void* q, const void* k, const void* v,

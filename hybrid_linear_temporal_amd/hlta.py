@@ -29,7 +29,7 @@ EXPORTS = ("hlta_abi_version", "hlta_status_string", "hlta_last_error", "hlta_va
            "hlta_stream_load_prefix", "hlta_step_workspace_bytes", "hlta_step_frame",
            "hlta_step_frame_rollouts", "hlta_quantize_fp8", "hlta_attn_fwd_fp8", "hlta_bwd_workspace_bytes",
            "hlta_bwd", "hlta_fwd_noalloc", "hlta_ceiling_mfma_bf16", "hlta_ceiling_copy", "hlta_attn_fwd_lse",
-           "hlta_bwd_lse")
+           "hlta_bwd_lse", "hlta_attn_branches", "hlta_gdn_mix_fwd")
 
 
 class hlta_config(ctypes.Structure):
@@ -77,6 +77,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "hlta_fwd_noalloc": (I32, [cfgp, P, P, P, P, P, P, P, P, P, P, P, P, P]),
         "hlta_gdn_fwd": (I32, [cfgp, P, P, P, P, P, P, P, P, P, S, P]),
         "hlta_attn_fwd": (I32, [cfgp, P, P, P, P, P, P, P, P, P]),
+        "hlta_attn_branches": (I32, [cfgp, P, P, P, P, P, P]),
+        "hlta_gdn_mix_fwd": (I32, [cfgp] + [P] * 13 + [S, P]),
         "hlta_attn_fwd_lse": (I32, [cfgp, P, P, P, P, P, P, P, P, P, P]),
         "hlta_stream_ring_bytes": (S, [cfgp, I32]),
         "hlta_stream_load_prefix": (I32, [cfgp, stp, P, P, I32, P, P]),
@@ -209,6 +211,24 @@ def hlta_attn_fwd(cfg: hlta_config, q, k, v, mix_w, o_gdn, out: dict, stream=Non
     _check(load_library().hlta_attn_fwd(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(mix_w), _ptr(o_gdn),
                                         _ptr(out["o_swa"]), _ptr(out["o_dswa"]), _ptr(out["o_mix"]),
                                         _stream(stream)))
+
+
+def hlta_attn_branches(cfg: hlta_config, q, k, v, out: dict, stream=None):
+    """Softmax branches alone (C: hlta_attn_branches); out holds o_swa, o_dswa."""
+    _check(load_library().hlta_attn_branches(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(out["o_swa"]),
+                                             _ptr(out["o_dswa"]), _stream(stream)))
+
+
+def hlta_gdn_mix_fwd(cfg: hlta_config, q, k, v, a, b, mix_w, out: dict, S0=None, S_out=None, workspace=None,
+                     stream=None):
+    """Memory branch and the mix (C: hlta_gdn_mix_fwd) from out's o_swa, o_dswa;
+    writes out's o_gdn, o_mix."""
+    if workspace is None:
+        workspace = alloc_workspace(hlta_fwd_workspace_bytes(cfg), q.device)
+    _check(load_library().hlta_gdn_mix_fwd(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                           _ptr(mix_w), _ptr(S0), _ptr(out["o_swa"]), _ptr(out["o_dswa"]),
+                                           _ptr(out["o_gdn"]), _ptr(out["o_mix"]), _ptr(S_out),
+                                           _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 def hlta_bwd_workspace_bytes(cfg: hlta_config) -> int:

@@ -206,6 +206,34 @@ hlta_status hlta_attn_fwd(const hlta_config* cfg,
                           void* o_swa, void* o_dswa, void* o_mix, void* stream);
 
 /*
+ * The other split of hlta_fwd, in its own order: hlta_attn_branches followed
+ * by hlta_gdn_mix_fwd on one stream equals hlta_fwd bit for bit, and equals
+ * hlta_gdn_fwd followed by hlta_attn_fwd.
+ *
+ * hlta_attn_branches - the two softmax branches alone (Kairos abstract,
+ * point (2)): o_swa and o_dswa. Needs no workspace; HLTA_E_UNSUPPORTED with
+ * the rotary embedding on. Arguments as in hlta_fwd.
+ */
+hlta_status hlta_attn_branches(const hlta_config* cfg,
+                               const void* q, const void* k, const void* v,
+                               void* o_swa, void* o_dswa, void* stream);
+
+/*
+ * hlta_gdn_mix_fwd - the memory branch (Kairos related-work page, row A;
+ * long-context page, section 06) and the mix (Kairos page, HLTA section):
+ * o_gdn, S_out and o_mix = w_swa o_swa + w_dswa o_dswa + w_gdn o_gdn per
+ * head, from the o_swa, o_dswa given (read only, as stored by a previous
+ * hlta_attn_branches on the same stream). Arguments and errors as in
+ * hlta_fwd.
+ */
+hlta_status hlta_gdn_mix_fwd(const hlta_config* cfg,
+                             const void* q, const void* k, const void* v,
+                             const float* a, const float* b, const float* mix_w,
+                             const float* S0, const void* o_swa, const void* o_dswa,
+                             void* o_gdn, void* o_mix, float* S_out,
+                             void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * hlta_attn_fwd_lse - hlta_attn_fwd that also writes the softmax row
  * statistics the backward needs (each query row's log-sum-exp, which the
  * tiled exact attention of the long-context page, section 03, carries

@@ -258,3 +258,37 @@ def test_attn_fwd_lse_argument_errors(lib):
     assert lib.hlta_attn_fwd_lse(ctypes.byref(cfg), *args, ctypes.c_void_p((1 << 20) + 4), None) == 6
     rope = _cfg(rope_theta=10000.0, rope_grid=(30, 52))
     assert lib.hlta_attn_fwd_lse(ctypes.byref(rope), *args, fake, None) == 4
+
+
+def test_split_entry_points_argument_errors(lib):
+    """hlta_attn_branches and hlta_gdn_mix_fwd check their arguments before any
+    launch: NULL and misaligned pointers, the workspace size, and the rotary
+    embedding for hlta_attn_branches (which has no workspace for it)."""
+    cfg = _cfg()
+    fake = ctypes.c_void_p(1 << 20)
+    br = [fake] * 5   # q, k, v, o_swa, o_dswa
+    for i, name in ((0, b"q"), (3, b"o_swa"), (4, b"o_dswa")):
+        a2 = list(br)
+        a2[i] = None
+        assert lib.hlta_attn_branches(ctypes.byref(cfg), *a2, None) == 1
+        assert name + b" is NULL" in lib.hlta_last_error()
+    a2 = list(br)
+    a2[3] = ctypes.c_void_p((1 << 20) + 4)
+    assert lib.hlta_attn_branches(ctypes.byref(cfg), *a2, None) == 6
+    rope = _cfg(rope_theta=10000.0, rope_grid=(30, 52))
+    assert lib.hlta_attn_branches(ctypes.byref(rope), *br, None) == 4
+    ws = H.hlta_fwd_workspace_bytes(cfg)
+    # q, k, v, a, b, mix_w, S0 (NULL), o_swa, o_dswa, o_gdn, o_mix, S_out (NULL), workspace
+    gm = [fake] * 6 + [None] + [fake] * 4 + [None, fake]
+
+    def call(a, nbytes=ws):
+        return lib.hlta_gdn_mix_fwd(ctypes.byref(cfg), *a, nbytes, None)
+
+    for i, name in ((0, b"q"), (5, b"mix_w"), (7, b"o_swa"), (8, b"o_dswa"), (9, b"o_gdn"), (10, b"o_mix")):
+        a2 = list(gm)
+        a2[i] = None
+        assert call(a2) == 1 and name + b" is NULL" in lib.hlta_last_error()
+    a2 = list(gm)
+    a2[8] = ctypes.c_void_p((1 << 20) + 4)
+    assert call(a2) == 6
+    assert call(gm, ws - 1) == 5

@@ -106,22 +106,29 @@ def test_mix_is_weighted_sum_of_stored_branches():
 
 
 def test_split_calls_equal_fwd():
-    """hlta_gdn_fwd then hlta_attn_fwd on one stream equal hlta_fwd bit for bit."""
+    """hlta_gdn_fwd then hlta_attn_fwd, and hlta_attn_branches then
+    hlta_gdn_mix_fwd, on one stream equal hlta_fwd bit for bit."""
     for wl in (BF16_CASES[0], F32_CASES[0]):
         x = I.make_clip(wl)
         ref = run_gpu(wl, x)
         cfg = H.make_config(wl)
         dev = H.to_device(x, wl.dtype)
-        out = H.alloc_outputs(cfg, wl.L)
-        S_out = torch.empty((wl.B, wl.H, wl.d, wl.d), device="cuda")
         ws = H.alloc_workspace(H.hlta_fwd_workspace_bytes(cfg))
-        H.hlta_gdn_fwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], out["o_gdn"], S_out=S_out,
-                       workspace=ws)
-        H.hlta_attn_fwd(cfg, dev["q"], dev["k"], dev["v"], dev["w"], out["o_gdn"], out)
-        torch.cuda.synchronize()
-        for n in ("o_swa", "o_dswa", "o_gdn", "o_mix"):
-            assert torch.equal(out[n], ref[n]), (wl.name, n)
-        assert torch.equal(S_out, ref["S_out"]), wl.name
+        for order in ("gdn, attn", "branches, gdn+mix"):
+            out = H.alloc_outputs(cfg, wl.L)
+            S_out = torch.empty((wl.B, wl.H, wl.d, wl.d), device="cuda")
+            if order == "gdn, attn":
+                H.hlta_gdn_fwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], out["o_gdn"], S_out=S_out,
+                               workspace=ws)
+                H.hlta_attn_fwd(cfg, dev["q"], dev["k"], dev["v"], dev["w"], out["o_gdn"], out)
+            else:
+                H.hlta_attn_branches(cfg, dev["q"], dev["k"], dev["v"], out)
+                H.hlta_gdn_mix_fwd(cfg, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], dev["w"], out,
+                                   S_out=S_out, workspace=ws)
+            torch.cuda.synchronize()
+            for n in ("o_swa", "o_dswa", "o_gdn", "o_mix"):
+                assert torch.equal(out[n], ref[n]), (wl.name, order, n)
+            assert torch.equal(S_out, ref["S_out"]), (wl.name, order)
 
 
 def test_fwd_graph_replays_match_eager():
