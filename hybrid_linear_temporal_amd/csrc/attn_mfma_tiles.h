@@ -166,21 +166,35 @@ __device__ __forceinline__ void issue_tile(TileOf<kRowBytes>& Kd, TileOf<kRowByt
     }
     return;
   }
+  // Rows 0 .. split-1 of the tile lie in the current frame, the rest in the
+  // next one: one buffer resource per frame, each lane loading under the
+  // exec mask of its frame. (Buffer loads only: with a FLAT-encoded
+  // global_load_lds anywhere in the loop the compiler cannot tell LDS reads
+  // from those loads in the LDS counter and waits for every outstanding LDS
+  // read before the first product that needs one of them.)
   const int split = ks.P - ks.pk;
+  const unsigned bytes = unsigned(KT * ts * sizeof(E));
+  const __amdgpu_buffer_rsrc_t rka = make_rsrc(ks.k0 + size_t(ks.pk) * ts, bytes);
+  const __amdgpu_buffer_rsrc_t rva = make_rsrc(ks.v0 + size_t(ks.pk) * ts, bytes);
+  const __amdgpu_buffer_rsrc_t rkb = make_rsrc(ks.k1, bytes);
+  const __amdgpu_buffer_rsrc_t rvb = make_rsrc(ks.v1, bytes);
 #pragma unroll
   for (int j = 0; j < kInst; ++j) {
     const int r0 = 16 * wave + kRows * j;
     const int row = r0 + lane / kChunks;
     const int rr = row < kleft ? row : kleft - 1;
     const int c = swz_row<kRowBytes>(row, lane % kChunks);
-    const size_t koff = rr < split ? size_t(ks.pk + rr) * ts : size_t(rr - split) * ts;
-    const E* ksrc = (rr < split ? ks.k0 : ks.k1) + koff + c * int(16 / sizeof(E));
-    const E* vsrc = (rr < split ? ks.v0 : ks.v1) + koff + c * int(16 / sizeof(E));
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(ksrc),
-                                     (__attribute__((address_space(3))) void*)(&Kd.row[r0][0]), 16, 0, 0);
-    if constexpr (kV)
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vsrc),
-                                       (__attribute__((address_space(3))) void*)(&Vd.row[r0][0]), 16, 0, 0);
+    const bool here = rr < split;
+    const unsigned o = unsigned((here ? rr : rr - split) * ts * sizeof(E)) + unsigned(c) * 16u;
+    auto* kd = (__attribute__((address_space(3))) void*)(&Kd.row[r0][0]);
+    auto* vd = (__attribute__((address_space(3))) void*)(&Vd.row[r0][0]);
+    if (here) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rka, kd, 16, o, 0, 0, 0);
+      if constexpr (kV) __builtin_amdgcn_raw_ptr_buffer_load_lds(rva, vd, 16, o, 0, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rkb, kd, 16, o, 0, 0, 0);
+      if constexpr (kV) __builtin_amdgcn_raw_ptr_buffer_load_lds(rvb, vd, 16, o, 0, 0, 0);
+    }
   }
 }
 

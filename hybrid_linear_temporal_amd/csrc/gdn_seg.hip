@@ -159,19 +159,22 @@ __device__ __forceinline__ int rec_tile(int js, int ib) { return ib < 2 ? ib : 2
 // ---------------------------------------------------------------------------
 // kernel T: per chunk, T = (I + A)^-1 and its record
 // ---------------------------------------------------------------------------
-// LDS 40 KB, so four workgroups share a CU and the long dependent chains of
-// the inverse of one chunk overlap with the others'. R1 holds A in its
-// strictly lower 16x16 blocks (fp32) and T transposed in the rest: element
-// (m, n) with n at or right of m's diagonal block is T[n][m]. XA first holds
-// the diagonal blocks of A transposed (for the column-oriented solve), then
-// per-wave 16x16 scratch.
+// LDS 23.5 KB, so six workgroups share a CU and the long dependent chains of
+// the inverse of one chunk overlap with the others'. Kt holds the chunk's k
+// rows until the Gram products have read them; the same bytes (R1) then hold
+// A in its strictly lower 16x16 blocks (fp32) and T transposed in the rest:
+// element (m, n) with n at or right of m's diagonal block is T[n][m]. XA first
+// holds the diagonal blocks of A transposed (for the column-oriented solve),
+// then per-wave 16x16 scratch.
 struct TinvSmem {
-  uint4 Kt[TILE];
-  uint4 R1[TILE];
+  union {
+    uint4 Kt[TILE];
+    uint4 R1[TILE];
+  };
   float XA[4 * 16 * 20];
   float g[C], bb[C], rk[C], sc[C];
 };
-static_assert(sizeof(TinvSmem) <= 40960, "four workgroups per CU");
+static_assert(sizeof(TinvSmem) <= 160 * 1024 / 6, "six workgroups per CU");
 
 // x = hi + lo with hi, lo in bf16 (about 16 significant bits together)
 __device__ __forceinline__ void split_bf16(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
@@ -192,7 +195,7 @@ __device__ __forceinline__ f32x4 mfma_split(const float (&a)[8], const float (&b
   return mfma16(al, bh, c);
 }
 
-__global__ void __launch_bounds__(NT, 4)
+__global__ void __launch_bounds__(NT, 6)
 gdn_tinv_kernel(GdnParams p, unsigned char* recs) {
   __shared__ __attribute__((aligned(16))) TinvSmem sm;
   const int chunk = int(blockIdx.x), h = blockIdx.y, b = blockIdx.z;
@@ -254,6 +257,7 @@ gdn_tinv_kernel(GdnParams p, unsigned char* recs) {
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb) kk[jb] = mfma16(ak[ks], ld8(sm.Kt, 16 * jb + l16, 32 * ks + 8 * g), kk[jb]);
+    lds_barrier();   // every wave has read Kt, whose bytes R now takes over
     float gi[4], bri[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
