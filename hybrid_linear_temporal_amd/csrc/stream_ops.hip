@@ -45,19 +45,27 @@ ring_store_rollouts_kernel(const uint4* src, uint4* ring, int R, long long frame
 // stored branch outputs (Kairos abstract, point (2): the three branches are
 // mixed per head), with one fp32 rounding order for every caller:
 // fma(w2, gdn, fma(w1, dswa, w0 * swa)), then one rounding to the output type.
-// One thread per 8 consecutive values of one (token, head); 16-byte vectors.
+// One thread per 8 consecutive values of one (token, head); 16-byte vectors,
+// loaded and stored non-temporally since the mix streams each value once
+// (bf16: 0.221 -> 0.205 ms per 480P call against plain ones, same results).
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 template <typename T>
 struct Vec8;
 template <>
 struct Vec8<bf16> {
   uint4 u;
-  __device__ __forceinline__ void load(const bf16* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void load(const bf16* p) {
+    const v4u x = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    u = make_uint4(x[0], x[1], x[2], x[3]);
+  }
   __device__ __forceinline__ float get(int i) const {
     const bf16* e = reinterpret_cast<const bf16*>(&u);
     return static_cast<float>(e[i]);
   }
   __device__ __forceinline__ void set(int i, float x) { reinterpret_cast<bf16*>(&u)[i] = static_cast<bf16>(x); }
-  __device__ __forceinline__ void store(bf16* p) const { *reinterpret_cast<uint4*>(p) = u; }
+  __device__ __forceinline__ void store(bf16* p) const {
+    __builtin_nontemporal_store(v4u{u.x, u.y, u.z, u.w}, reinterpret_cast<v4u*>(p));
+  }
 };
 template <>
 struct Vec8<float> {
