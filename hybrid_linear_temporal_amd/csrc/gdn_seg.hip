@@ -23,16 +23,18 @@
 //     a 13,056-byte record in the exact MFMA operand order the later passes
 //     read (so no pass repeats the inverse, the part of a chunk with the
 //     longest dependent chains);
-//   gdn_seg_kernel<false> (pass 1): every segment but the last, two
-//     workgroups: one runs the chain from S = 0 (its end state is N), the
-//     other from S = I with the value term dropped (its end state is M);
+//   gdn_seg_kernel<false> (pass 1): every segment but the last, one
+//     workgroup running two chains over the same tiles: from S = 0 (its end
+//     state is N) and from S = I with the value term dropped (its end state
+//     is M);
 //   gdn_seg_scan (pass 2): per head and 16 state rows, S_{g+1} = S_g M_g + N_g
 //     over the segments in order (fp32 accuracy from split bf16 products);
 //   gdn_seg_kernel<true> (pass 3): every segment from its true start state,
 //     writing o_gdn (and S_out from the last segment).
 //
 // In passes 1 and 3 a workgroup owns the whole 128 x 128 state of its segment
-// (wave w: 32 columns of S^T in MFMA accumulator layout), so a chunk's q, k, v
+// (pass 1: both states; wave w: 32 columns of S^T in MFMA accumulator layout,
+// fp32 in registers), so a chunk's q, k, v
 // are loaded once and W, U' and the causal q.k matrix are formed on chip from
 // the record; nothing per chunk but the record goes through memory.
 #include <type_traits>
@@ -484,9 +486,12 @@ __device__ __forceinline__ void tproduct(const uint4* X, const unsigned char* ti
 }
 
 // OUT = true: pass 3 (outputs, from the segment's true start state).
-// OUT = false: pass 1; blockIdx.x = 2g + m: m = 0 runs the chain from S = 0
-// with the value term (end state N_g), m = 1 from S = I without it (end state
-// M_g, each state row r being row r of the product of the chunks' M_c).
+// OUT = false: pass 1; blockIdx.x = g: the workgroup runs two chains over the
+// segment's chunks, from S = 0 with the value term (end state N_g) and from
+// S = I without it (end state M_g, each state row r being row r of the product
+// of the chunks' M_c). Both read the same tiles, W and K^T operands, so one
+// workgroup holding both states (one round of workgroups on the chip instead
+// of two) forms those once per chunk.
 template <bool OUT, typename Tout>
 __global__ void __launch_bounds__(NT, 2)
 gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned char* recs) {
@@ -499,9 +504,8 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
   __shared__ SegVec sv;
   const int h = blockIdx.y, b = blockIdx.z;
   if (skipped(p.skip, b)) return;
-  const int seg = OUT ? int(blockIdx.x) : int(blockIdx.x) >> 1;
-  const bool mrows = !OUT && (blockIdx.x & 1);   // pass 1, the M half
-  const bool vterm = !mrows;                     // U' (values) takes part
+  const int seg = int(blockIdx.x);
+  constexpr bool vterm = true;   // U' (values) takes part (pass 1: in the N chain)
   const int bh = b * p.H + h;
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
   const int col0 = 32 * wave;   // this wave's state columns
@@ -511,8 +515,8 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
   seg_range(seg, seg_chunks, p.n_chunks, c0, c1);
   bf16 (*aqk)[QP] = reinterpret_cast<bf16 (*)[QP]>(XA);
 
-  // ---- start state ----
-  State S;
+  // ---- start state (pass 1: S the N chain's, SM the M chain's) ----
+  State S, SM;
   {
     const int lane = int(threadIdx.x) & 63, g = lane >> 4, l16 = lane & 15;
     const float* src = nullptr;
@@ -523,15 +527,17 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const int col = col0 + 16 * nb + l16, row = 16 * mb + 4 * g;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        f32x4 v = {0.f, 0.f, 0.f, 0.f}, vm = {0.f, 0.f, 0.f, 0.f};
         if (src) {
           const float4 x = *reinterpret_cast<const float4*>(src + sbase + size_t(col) * D + row);
           v = f32x4{x.x, x.y, x.z, x.w};
-        } else if (mrows) {
+        }
+        if (!OUT) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = row + e == col ? 1.f : 0.f;
+          for (int e = 0; e < 4; ++e) vm[e] = row + e == col ? 1.f : 0.f;
         }
         S.st[mb][nb] = v;
+        SM.st[mb][nb] = vm;
       }
   }
   const unsigned char* kg = static_cast<const unsigned char*>(p.k);
@@ -721,31 +727,74 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
     if (!OUT && chunk + 1 < c1) load_rows(rsk, Kn, chunk + 1);
 
     // ---- chain: U = U' - W S^T, outputs, state update (wave w: state columns 32w ..) ----
-    bf16x8 sb[2][4];
-    state_bf16(S, sb);
-    f32x4 u[4][2];
+    // U of one state (with U' when the value term takes part); sb its bf16 copy
+    auto chain_u = [&](const State& St, bool values, bf16x8 (&sb)[2][4], f32x4 (&u)[4][2])
+        __attribute__((always_inline)) {
+      state_bf16(St, sb);
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+      for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        if (vterm) {
-          const bf16x4 up = ld4_tr(Vt, 16 * tb + 4 * g + (l16 >> 2), col0 + 16 * nb + 4 * (l16 & 3));
-          u[tb][nb] = f32x4{static_cast<float>(up[0]), static_cast<float>(up[1]), static_cast<float>(up[2]),
-                            static_cast<float>(up[3])};
-        } else {
-          u[tb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < 2; ++nb) {
+          if (values) {
+            const bf16x4 up = ld4_tr(Vt, 16 * tb + 4 * g + (l16 >> 2), col0 + 16 * nb + 4 * (l16 & 3));
+            u[tb][nb] = f32x4{static_cast<float>(up[0]), static_cast<float>(up[1]), static_cast<float>(up[2]),
+                              static_cast<float>(up[3])};
+          } else {
+            u[tb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        bf16x8 aw[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          aw[ks] = join(ld4(R1, 16 * tb + l16, 32 * ks + 4 * g), ld4(R1, 16 * tb + l16, 32 * ks + 16 + 4 * g));
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) u[tb][nb] = mfma16(aw[ks], sb[nb][ks], u[tb][nb]);
+      }
+    };
+    // S^T <- gamma_C S^T + K^T diag(sk) U
+    auto chain_update = [&](State& St, const f32x4 (&u)[4][2]) __attribute__((always_inline)) {
+      bf16x8 usb[2][2];
+#pragma unroll
+      for (int js = 0; js < 2; ++js) {
+        const f32x4 s0 = *reinterpret_cast<const f32x4*>(&sv.sk[32 * js + 4 * g]);
+        const f32x4 s1 = *reinterpret_cast<const f32x4*>(&sv.sk[32 * js + 16 + 4 * g]);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          usb[nb][js] = join(to_bf16x4(u[2 * js][nb] * s0), to_bf16x4(u[2 * js + 1][nb] * s1));
+      }
+      const float gc = sv.gC;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        bf16x8 ak[2];
+#pragma unroll
+        for (int js = 0; js < 2; ++js) {
+          const int col = 16 * mb + 4 * (l16 & 3);
+          ak[js] = join(ld4_tr(Kt, 32 * js + 4 * g + (l16 >> 2), col),
+                        ld4_tr(Kt, 32 * js + 16 + 4 * g + (l16 >> 2), col));
+        }
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) St.st[mb][nb][e] *= gc;
+#pragma unroll
+          for (int js = 0; js < 2; ++js) St.st[mb][nb] = mfma16(ak[js], usb[nb][js], St.st[mb][nb]);
         }
       }
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      bf16x8 aw[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        aw[ks] = join(ld4(R1, 16 * tb + l16, 32 * ks + 4 * g), ld4(R1, 16 * tb + l16, 32 * ks + 16 + 4 * g));
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) u[tb][nb] = mfma16(aw[ks], sb[nb][ks], u[tb][nb]);
+    };
+    bf16x8 sb[2][4];
+    f32x4 u[4][2];
+    if constexpr (!OUT) {
+      // the N chain's whole step, then the M chain's U (K stays in its
+      // buffer for the whole chunk: the next chunk's K went to the other one)
+      chain_u(S, true, sb, u);
+      chain_update(S, u);
+      chain_u(SM, false, sb, u);
+    } else {
+      chain_u(S, true, sb, u);
     }
     lds_barrier();   // every wave has read U' (over V) and -W (in R1)
     if (chunk + 1 < c1) {
@@ -795,36 +844,7 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
       lds_barrier();   // every wave has read Q and Aqk
       if (chunk + 1 < c1) load_rows(rsq, Qt, chunk + 1);
     }
-    // S^T <- gamma_C S^T + K^T diag(sk) U
-    {
-      bf16x8 usb[2][2];
-#pragma unroll
-      for (int js = 0; js < 2; ++js) {
-        const f32x4 s0 = *reinterpret_cast<const f32x4*>(&sv.sk[32 * js + 4 * g]);
-        const f32x4 s1 = *reinterpret_cast<const f32x4*>(&sv.sk[32 * js + 16 + 4 * g]);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          usb[nb][js] = join(to_bf16x4(u[2 * js][nb] * s0), to_bf16x4(u[2 * js + 1][nb] * s1));
-      }
-      const float gc = sv.gC;
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        bf16x8 ak[2];
-#pragma unroll
-        for (int js = 0; js < 2; ++js) {
-          const int col = 16 * mb + 4 * (l16 & 3);
-          ak[js] = join(ld4_tr(Kt, 32 * js + 4 * g + (l16 >> 2), col),
-                        ld4_tr(Kt, 32 * js + 16 + 4 * g + (l16 >> 2), col));
-        }
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) S.st[mb][nb][e] *= gc;
-#pragma unroll
-          for (int js = 0; js < 2; ++js) S.st[mb][nb] = mfma16(ak[js], usb[nb][js], S.st[mb][nb]);
-        }
-      }
-    }
+    chain_update(OUT ? S : SM, u);
     if (OUT) {
       lds_barrier();   // every wave has read K
       if (chunk + 1 < c1) load_rows(rsk, Kt, chunk + 1);
@@ -844,15 +864,7 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
     store_pending(lane & 15, lane >> 4);
   }
   // ---- end state: S^T tile (mb, nb) holds rows d_k 16mb + 4g + e of state row col0 + 16nb + l16 ----
-  float* dst = nullptr;
-  bool transposed = false;
-  if (OUT) {
-    if (seg == G - 1 && p.S_out) dst = p.S_out + size_t(bh) * D * D;
-  } else {
-    dst = map_slot(maps, bh, G, 2 * seg + (mrows ? 1 : 0));
-    transposed = mrows;
-  }
-  if (dst) {
+  auto store_state = [&](const State& St, float* dst, bool transposed) {
     const int lane = int(threadIdx.x) & 63, g = lane >> 4, l16 = lane & 15;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
@@ -861,12 +873,18 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
         const int r = col0 + 16 * nb + l16, j = 16 * mb + 4 * g;
         if (!transposed) {
           *reinterpret_cast<float4*>(dst + size_t(r) * D + j) =
-              make_float4(S.st[mb][nb][0], S.st[mb][nb][1], S.st[mb][nb][2], S.st[mb][nb][3]);
+              make_float4(St.st[mb][nb][0], St.st[mb][nb][1], St.st[mb][nb][2], St.st[mb][nb][3]);
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dst[size_t(j + e) * D + r] = S.st[mb][nb][e];
+          for (int e = 0; e < 4; ++e) dst[size_t(j + e) * D + r] = St.st[mb][nb][e];
         }
       }
+  };
+  if (OUT) {
+    if (seg == G - 1 && p.S_out) store_state(S, p.S_out + size_t(bh) * D * D, false);
+  } else {
+    store_state(S, map_slot(maps, bh, G, 2 * seg), false);
+    store_state(SM, map_slot(maps, bh, G, 2 * seg + 1), true);
   }
 }
 
@@ -984,7 +1002,7 @@ hipError_t launch_gdn_seg(const GdnParams& p, int G, int seg_chunks, void* works
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (G > 1) {
-    hipLaunchKernelGGL((gdn_seg_kernel<false, bf16>), dim3(2 * (G - 1), p.H, p.B), dim3(NT), 0, st, p, G,
+    hipLaunchKernelGGL((gdn_seg_kernel<false, bf16>), dim3(G - 1, p.H, p.B), dim3(NT), 0, st, p, G,
                        seg_chunks, maps, recs);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
