@@ -47,9 +47,21 @@ def run_oracle(wl: I.Workload, x: dict, S0=None, heads=None, gdn="chunked", **ov
                           gate_logits=over.get("gate_logits", False))
 
 
-def compare(gpu: dict, ref, tol: float, heads=None, label=""):
-    """rel-L2 per branch (and state) over the given heads; asserts <= tol."""
+def frame_diagnostics(g: np.ndarray, r: np.ndarray, P: int) -> tuple[int, float, float]:
+    """Worst latent frame of one branch ([B, L, H, d], L = T P): its index, its
+    rel-L2 and the largest absolute difference anywhere (diagnostics only)."""
+    T = g.shape[1] // P
+    per = [O.rel_l2(g[:, f * P:(f + 1) * P], r[:, f * P:(f + 1) * P]) for f in range(T)]
+    worst = int(np.argmax(per)) if per else 0
+    return worst, (per[worst] if per else 0.0), float(np.max(np.abs(g - r))) if g.size else 0.0
+
+
+def compare(gpu: dict, ref, tol: float, heads=None, label="", P=None):
+    """rel-L2 per branch (and state) over the given heads; asserts <= tol.
+    With P (tokens per frame) it also prints, per branch, the worst frame's
+    rel-L2 and the largest absolute difference (not asserted)."""
     errs = {}
+    diag = {}
     for i, n in enumerate(BRANCHES):
         g = to64(gpu[n])
         r = ref[i]
@@ -57,6 +69,9 @@ def compare(gpu: dict, ref, tol: float, heads=None, label=""):
             g = np.stack([g[b, :, h] for b, h in heads])
             r = np.stack([r[b, :, h] for b, h in heads])
         errs[n] = O.rel_l2(g, r)
+        if P and heads is None and g.shape[1] % P == 0:
+            f, e, m = frame_diagnostics(g, r, P)
+            diag[n] = f"frame {f}: {e:.2e}, max-abs {m:.2e}"
     if gpu.get("S_out") is not None:
         g = to64(gpu["S_out"])
         r = ref[4]
@@ -65,6 +80,8 @@ def compare(gpu: dict, ref, tol: float, heads=None, label=""):
             r = np.stack([r[b, h] for b, h in heads])
         errs["S_out"] = O.rel_l2(g, r)
     print(label, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    if diag:
+        print(label, "worst frame per branch:", diag, flush=True)
     for n, e in errs.items():
         assert e <= tol, f"{label} {n}: rel-L2 {e:.3e} > {tol:.0e}"
     return errs

@@ -29,7 +29,7 @@ def test_tiny_f32(impl):
     S0 = S0.astype(np.float32)
     ref = run_oracle(wl, x, S0=S0, gdn="recurrent")
     got = run_gpu(wl, x, impl=impl, S0=S0)
-    compare(got, ref, TOL["f32"], label=f"tiny impl={impl}")
+    compare(got, ref, TOL["f32"], label=f"tiny impl={impl}", P=wl.P)
 
 
 F32_CASES = [
@@ -46,7 +46,7 @@ def test_f32_shapes(wl):
     x = I.make_clip(wl)
     ref = run_oracle(wl, x, gdn="recurrent")
     got = run_gpu(wl, x)
-    compare(got, ref, TOL["f32"], label=wl.name)
+    compare(got, ref, TOL["f32"], label=wl.name, P=wl.P)
 
 
 BF16_CASES = [
@@ -71,7 +71,7 @@ def test_bf16_shapes(wl, impl):
     x = I.make_clip(wl)
     ref = run_oracle(wl, x)
     got = run_gpu(wl, x, impl=impl)
-    compare(got, ref, TOL["bf16"], label=f"{wl.name} impl={impl}")
+    compare(got, ref, TOL["bf16"], label=f"{wl.name} impl={impl}", P=wl.P)
 
 
 def test_bf16_in_f32_out():
