@@ -505,7 +505,6 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
   const int h = blockIdx.y, b = blockIdx.z;
   if (skipped(p.skip, b)) return;
   const int seg = int(blockIdx.x);
-  constexpr bool vterm = true;   // U' (values) takes part (pass 1: in the N chain)
   const int bh = b * p.H + h;
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
   const int col0 = 32 * wave;   // this wave's state columns
@@ -611,7 +610,7 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
   if (c0 < c1) {
     load_rows(rsk, K0, c0);
     if (OUT) load_rows(rsq, Qt, c0);
-    if (vterm) load_rows(rsv, Vt, c0);
+    load_rows(rsv, Vt, c0);
     load_record(c0);
   }
   int pf = 0;   // value of the L2 prefetch load (never used)
@@ -708,7 +707,7 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
     {
       const unsigned char* rec = reinterpret_cast<const unsigned char*>(R1);
       tproduct(Kt, rec + kRecTp, true, wave, lane, g, l16, wkeep);
-      if (vterm) tproduct(Vt, rec + kRecTpp, false, wave, lane, g, l16, ukeep);
+      tproduct(Vt, rec + kRecTpp, false, wave, lane, g, l16, ukeep);
     }
     lds_barrier();   // V is read: -W goes to R1, U' over V
 #pragma unroll
@@ -718,7 +717,7 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
         // C layout: column = token 16ib + l16, rows = channels 16(2w + mi) + 4g + e
         const int tok = 16 * ib + l16, ch = 16 * (2 * wave + mi) + 4 * g;
         st4(R1, tok, ch, wkeep[mi][ib]);
-        if (vterm) st4(Vt, tok, ch, ukeep[mi][ib]);
+        st4(Vt, tok, ch, ukeep[mi][ib]);
       }
     lds_barrier();
     // pass 1: the next chunk's K into the other buffer (it held the previous
@@ -798,7 +797,7 @@ gdn_seg_kernel(GdnParams p, int G, int seg_chunks, float* maps, const unsigned c
     }
     lds_barrier();   // every wave has read U' (over V) and -W (in R1)
     if (chunk + 1 < c1) {
-      if (vterm) load_rows(rsv, Vt, chunk + 1);
+      load_rows(rsv, Vt, chunk + 1);
       load_record(chunk + 1);
     }
     if (OUT) {
